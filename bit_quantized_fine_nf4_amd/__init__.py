@@ -1,0 +1,217 @@
+"""Python binding of libqlora_nf4.so — the MI355X (gfx950) NF4 + LoRA linear layer.
+
+Argument marshalling only: every step runs in the library's HIP kernels.
+PyTorch provides device memory and the current stream.  The functions carry
+the C ABI's names (include/qlora_nf4.h).  Importing this module loads the
+library; if it has not been built, the import raises (there is no fallback).
+"""
+from __future__ import annotations
+
+import ctypes
+import dataclasses
+import os
+from typing import Optional, Tuple
+
+import torch  # noqa: F401  (loads the HIP runtime the library then shares)
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libqlora_nf4.so")
+
+QLORA_OK, QLORA_ERR_INVALID_VALUE, QLORA_ERR_UNSUPPORTED, QLORA_ERR_LAUNCH, QLORA_ERR_INTERNAL = range(5)
+QLORA_F32, QLORA_BF16 = 0, 1
+QLORA_OP_DOUBLE_QUANT, QLORA_OP_LINEAR_FWD, QLORA_OP_LINEAR_BWD = 0, 1, 2
+BLOCK, CHUNK, MAX_RANK = 64, 256, 128
+
+EXPORTED = ("qlora_quantize", "qlora_double_quant", "qlora_dequantize", "qlora_linear_fwd",
+            "qlora_linear_bwd", "qlora_workspace_size", "qlora_status_string", "qlora_nf4_levels")
+
+
+class QloraError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        super().__init__(f"{where}: {lib.qlora_status_string(status).decode()} (status {status})")
+        self.status = status
+
+
+class NF4WeightT(ctypes.Structure):
+    _fields_ = [("codes", ctypes.c_void_p), ("qabsmax", ctypes.c_void_p), ("scale2", ctypes.c_void_p),
+                ("mean", ctypes.c_void_p), ("h", ctypes.c_int64), ("o", ctypes.c_int64)]
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with `python -m bit_quantized_fine_nf4_amd.build`")
+    L = ctypes.CDLL(LIB_PATH)
+    vp, i64, i32, f32, st = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_float, ctypes.c_int
+    sz = ctypes.c_size_t
+    L.qlora_quantize.argtypes = [vp, st, i64, vp, vp, vp]
+    L.qlora_double_quant.argtypes = [vp, i64, vp, vp, vp, vp, sz, vp]
+    L.qlora_dequantize.argtypes = [vp, vp, vp, vp, i64, vp, st, vp]
+    L.qlora_linear_fwd.argtypes = [ctypes.POINTER(NF4WeightT), vp, i64, vp, vp, i32, f32, vp, vp, vp, sz, vp]
+    L.qlora_linear_bwd.argtypes = [ctypes.POINTER(NF4WeightT), vp, vp, vp, i64, vp, vp, i32, f32, vp, vp, vp,
+                                   vp, sz, vp]
+    L.qlora_workspace_size.argtypes = [st, i64, i64, i64, i32, ctypes.POINTER(sz)]
+    L.qlora_status_string.argtypes = [st]
+    L.qlora_status_string.restype = ctypes.c_char_p
+    L.qlora_nf4_levels.argtypes = [ctypes.POINTER(ctypes.c_float)]
+    for name in EXPORTED:
+        if name != "qlora_status_string":
+            getattr(L, name).restype = ctypes.c_int
+    return L
+
+
+lib = _load()
+
+
+def _check(status: int, where: str):
+    if status != QLORA_OK:
+        raise QloraError(status, where)
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _dev_check(*ts):
+    for t in ts:
+        if t is not None and (not t.is_cuda or not t.is_contiguous()):
+            raise ValueError("tensors must be contiguous and on the GPU")
+
+
+def nf4_levels() -> list:
+    buf = (ctypes.c_float * 16)()
+    _check(lib.qlora_nf4_levels(buf), "qlora_nf4_levels")
+    return list(buf)
+
+
+def workspace_size(op: int, a: int, b: int = 0, c: int = 0, r: int = 0) -> int:
+    out = ctypes.c_size_t(0)
+    _check(lib.qlora_workspace_size(op, a, b, c, r, ctypes.byref(out)), "qlora_workspace_size")
+    return out.value
+
+
+@dataclasses.dataclass
+class NF4Weight:
+    """A frozen NF4 weight with double-quantized scales, logical shape h x o,
+    stored in [o][h] order (PyTorch Linear.weight)."""
+    codes: torch.Tensor    # uint8 [o*h/2]
+    qabsmax: torch.Tensor  # int8 [o*h/64]
+    scale2: torch.Tensor   # float32 [ceil(o*h/64/256)]
+    mean: torch.Tensor     # float32 [1]
+    h: int
+    o: int
+
+    def as_ctypes(self) -> NF4WeightT:
+        return NF4WeightT(self.codes.data_ptr(), self.qabsmax.data_ptr(), self.scale2.data_ptr(),
+                          self.mean.data_ptr(), self.h, self.o)
+
+
+# ---------------------------------------------------------------------------
+# The five entry points
+# ---------------------------------------------------------------------------
+
+def qlora_quantize(w: torch.Tensor, codes: Optional[torch.Tensor] = None,
+                   absmax: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Blockwise NF4 quantization of any float32/bf16 GPU tensor (flattened)."""
+    _dev_check(w)
+    n = w.numel()
+    dtype = {torch.float32: QLORA_F32, torch.bfloat16: QLORA_BF16}[w.dtype]
+    if codes is None:
+        codes = torch.empty((n + 1) // 2, dtype=torch.uint8, device=w.device)
+    if absmax is None:
+        absmax = torch.empty((n + BLOCK - 1) // BLOCK, dtype=torch.float32, device=w.device)
+    _check(lib.qlora_quantize(_ptr(w), dtype, n, _ptr(codes), _ptr(absmax), _stream(w.device)), "qlora_quantize")
+    return codes, absmax
+
+
+def qlora_double_quant(absmax: torch.Tensor, qabsmax: Optional[torch.Tensor] = None,
+                       scale2: Optional[torch.Tensor] = None, mean: Optional[torch.Tensor] = None,
+                       workspace: Optional[torch.Tensor] = None):
+    """Double quantization of the float32 block scales -> (qabsmax int8, scale2 f32, mean f32[1])."""
+    _dev_check(absmax)
+    nb = absmax.numel()
+    dev = absmax.device
+    if qabsmax is None:
+        qabsmax = torch.empty(nb, dtype=torch.int8, device=dev)
+    if scale2 is None:
+        scale2 = torch.empty((nb + CHUNK - 1) // CHUNK, dtype=torch.float32, device=dev)
+    if mean is None:
+        mean = torch.empty(1, dtype=torch.float32, device=dev)
+    ws_bytes = workspace_size(QLORA_OP_DOUBLE_QUANT, nb)
+    if workspace is None:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    _check(lib.qlora_double_quant(_ptr(absmax), nb, _ptr(qabsmax), _ptr(scale2), _ptr(mean), _ptr(workspace),
+                                  workspace.numel(), _stream(dev)), "qlora_double_quant")
+    return qabsmax, scale2, mean
+
+
+def qlora_dequantize(codes: torch.Tensor, qabsmax: torch.Tensor, scale2: torch.Tensor, mean: torch.Tensor,
+                     n: int, out_dtype: torch.dtype = torch.bfloat16,
+                     out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Rebuild n weights as float32 or bf16."""
+    _dev_check(codes, qabsmax, scale2, mean)
+    dt = {torch.float32: QLORA_F32, torch.bfloat16: QLORA_BF16}[out_dtype]
+    if out is None:
+        out = torch.empty(n, dtype=out_dtype, device=codes.device)
+    _check(lib.qlora_dequantize(_ptr(codes), _ptr(qabsmax), _ptr(scale2), _ptr(mean), n, _ptr(out), dt,
+                                _stream(codes.device)), "qlora_dequantize")
+    return out
+
+
+def quantize_weight(w_oh: torch.Tensor) -> NF4Weight:
+    """quantize + double_quant of a [o][h] float32/bf16 weight."""
+    o, h = w_oh.shape
+    codes, absmax = qlora_quantize(w_oh)
+    qa, s2, mean = qlora_double_quant(absmax)
+    return NF4Weight(codes, qa, s2, mean, h, o)
+
+
+def qlora_linear_fwd(W: NF4Weight, X: torch.Tensor, L1: Optional[torch.Tensor], L2: Optional[torch.Tensor],
+                     s: float, Y: Optional[torch.Tensor] = None, T: Optional[torch.Tensor] = None,
+                     workspace: Optional[torch.Tensor] = None):
+    """Y = X·W_hat + s·(X·L1)·L2 -> (Y bf16 [M][o], T bf16 [M][r] or None)."""
+    _dev_check(X, L1, L2)
+    M = X.shape[0]
+    r = 0 if L1 is None else L1.shape[1]
+    dev = X.device
+    if Y is None:
+        Y = torch.empty(M, W.o, dtype=torch.bfloat16, device=dev)
+    if T is None and r:
+        T = torch.empty(M, r, dtype=torch.bfloat16, device=dev)
+    ws_bytes = workspace_size(QLORA_OP_LINEAR_FWD, M, W.h, W.o, r)
+    if workspace is None and ws_bytes:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    wt = W.as_ctypes()
+    _check(lib.qlora_linear_fwd(ctypes.byref(wt), _ptr(X), M, _ptr(L1), _ptr(L2), r, float(s), _ptr(Y), _ptr(T),
+                                _ptr(workspace), 0 if workspace is None else workspace.numel(), _stream(dev)),
+           "qlora_linear_fwd")
+    return Y, T
+
+
+def qlora_linear_bwd(W: NF4Weight, X: Optional[torch.Tensor], T: Optional[torch.Tensor], dY: torch.Tensor,
+                     L1: Optional[torch.Tensor], L2: Optional[torch.Tensor], s: float,
+                     dX: Optional[torch.Tensor] = None, dL1: Optional[torch.Tensor] = None,
+                     dL2: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None):
+    """Backward through the frozen NF4 weight -> (dX bf16 [M][h], dL1 f32 [h][r], dL2 f32 [r][o])."""
+    _dev_check(X, T, dY, L1, L2)
+    M = dY.shape[0]
+    r = 0 if L1 is None else L1.shape[1]
+    dev = dY.device
+    if dX is None:
+        dX = torch.empty(M, W.h, dtype=torch.bfloat16, device=dev)
+    if r and dL1 is None:
+        dL1 = torch.empty(W.h, r, dtype=torch.float32, device=dev)
+    if r and dL2 is None:
+        dL2 = torch.empty(r, W.o, dtype=torch.float32, device=dev)
+    ws_bytes = workspace_size(QLORA_OP_LINEAR_BWD, M, W.h, W.o, r)
+    if workspace is None and ws_bytes:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    wt = W.as_ctypes()
+    _check(lib.qlora_linear_bwd(ctypes.byref(wt), _ptr(X), _ptr(T), _ptr(dY), M, _ptr(L1), _ptr(L2), r, float(s),
+                                _ptr(dX), _ptr(dL1), _ptr(dL2), _ptr(workspace),
+                                0 if workspace is None else workspace.numel(), _stream(dev)),
+           "qlora_linear_bwd")
+    return dX, dL1, dL2

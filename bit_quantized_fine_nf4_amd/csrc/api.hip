@@ -1,0 +1,147 @@
+// C ABI: argument validation, workspace sizing and dispatch to the kernels.
+// Every check happens before anything is enqueued, so a rejected call leaves
+// all outputs untouched.
+
+#include "../../include/qlora_nf4.h"
+#include "codec.h"
+#include "linear.h"
+
+using namespace ql;
+
+namespace {
+
+inline bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+inline qlora_status_t launch_status(hipError_t e) { return e == hipSuccess ? QLORA_OK : QLORA_ERR_LAUNCH; }
+
+inline size_t round256(size_t b) { return (b + 255) / 256 * 256; }
+
+bool valid_weight(const qlora_nf4_weight_t *W) {
+  if (!W || !W->codes || !W->qabsmax || !W->scale2 || !W->mean) return false;
+  if (W->h <= 0 || W->o <= 0 || W->h % 64 || W->o % 64) return false;
+  if (W->h > (int64_t(1) << 31) || W->o > (int64_t(1) << 31)) return false;
+  if (W->h * W->o / 64 >= (int64_t(1) << 32)) return false;
+  return aligned(W->codes, 16) && aligned(W->qabsmax, 4) && aligned(W->scale2, 4) && aligned(W->mean, 4);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *qlora_status_string(qlora_status_t s) {
+  switch (s) {
+    case QLORA_OK: return "success";
+    case QLORA_ERR_INVALID_VALUE: return "invalid argument (pointer, size, alignment, rank or workspace)";
+    case QLORA_ERR_UNSUPPORTED: return "unsupported request";
+    case QLORA_ERR_LAUNCH: return "kernel launch failed";
+    case QLORA_ERR_INTERNAL: return "NF4 tables could not be built";
+  }
+  return "unknown status";
+}
+
+qlora_status_t qlora_nf4_levels(float out[16]) {
+  if (!out) return QLORA_ERR_INVALID_VALUE;
+  const Nf4Tables *t = host_tables();
+  if (!t) return QLORA_ERR_INTERNAL;
+  for (int i = 0; i < 16; ++i) out[i] = t->level[i];
+  return QLORA_OK;
+}
+
+qlora_status_t qlora_workspace_size(qlora_op_t op, int64_t a, int64_t b, int64_t c, int32_t r,
+                                    size_t *bytes) {
+  if (!bytes) return QLORA_ERR_INVALID_VALUE;
+  switch (op) {
+    case QLORA_OP_DOUBLE_QUANT:
+      if (a < 1) return QLORA_ERR_INVALID_VALUE;
+      *bytes = dq_workspace_bytes();
+      return QLORA_OK;
+    case QLORA_OP_LINEAR_FWD:
+    case QLORA_OP_LINEAR_BWD:
+      if (a < 1 || b < 64 || c < 64 || r < 0 || r > QLORA_MAX_RANK) return QLORA_ERR_INVALID_VALUE;
+      *bytes = round256(op == QLORA_OP_LINEAR_FWD ? linear_fwd_workspace(a, b, c, r)
+                                                  : linear_bwd_workspace(a, b, c, r));
+      return QLORA_OK;
+  }
+  return QLORA_ERR_INVALID_VALUE;
+}
+
+qlora_status_t qlora_quantize(const void *w, qlora_dtype_t w_dtype, int64_t n, uint8_t *codes,
+                              float *absmax, void *stream) {
+  if (!w || !codes || !absmax || n < 1) return QLORA_ERR_INVALID_VALUE;
+  if (w_dtype != QLORA_F32 && w_dtype != QLORA_BF16) return QLORA_ERR_INVALID_VALUE;
+  if (!aligned(w, 16) || !aligned(codes, 4) || !aligned(absmax, 4)) return QLORA_ERR_INVALID_VALUE;
+  const Nf4Tables *t = host_tables();
+  if (!t) return QLORA_ERR_INTERNAL;
+  (void)hipGetLastError();
+  return launch_status(launch_quantize(w, w_dtype == QLORA_BF16, n, codes, absmax, *t,
+                                       reinterpret_cast<hipStream_t>(stream)));
+}
+
+qlora_status_t qlora_double_quant(const float *absmax, int64_t nblocks, int8_t *qabsmax, float *scale2,
+                                  float *mean, void *workspace, size_t ws_bytes, void *stream) {
+  if (!absmax || !qabsmax || !scale2 || !mean || !workspace) return QLORA_ERR_INVALID_VALUE;
+  if (nblocks < 1 || nblocks >= (int64_t(1) << 32)) return QLORA_ERR_INVALID_VALUE;
+  if (!aligned(absmax, 16) || !aligned(qabsmax, 4) || !aligned(scale2, 4) || !aligned(mean, 4) ||
+      !aligned(workspace, 256))
+    return QLORA_ERR_INVALID_VALUE;
+  if (ws_bytes < dq_workspace_bytes()) return QLORA_ERR_INVALID_VALUE;
+  (void)hipGetLastError();
+  return launch_status(launch_double_quant(absmax, nblocks, qabsmax, scale2, mean, workspace,
+                                           reinterpret_cast<hipStream_t>(stream)));
+}
+
+qlora_status_t qlora_dequantize(const uint8_t *codes, const int8_t *qabsmax, const float *scale2,
+                                const float *mean, int64_t n, void *out, qlora_dtype_t out_dtype,
+                                void *stream) {
+  if (!codes || !qabsmax || !scale2 || !mean || !out || n < 1) return QLORA_ERR_INVALID_VALUE;
+  if (out_dtype != QLORA_F32 && out_dtype != QLORA_BF16) return QLORA_ERR_INVALID_VALUE;
+  if (!aligned(codes, 16) || !aligned(out, 16) || !aligned(scale2, 4) || !aligned(mean, 4))
+    return QLORA_ERR_INVALID_VALUE;
+  const Nf4Tables *t = host_tables();
+  if (!t) return QLORA_ERR_INTERNAL;
+  (void)hipGetLastError();
+  return launch_status(launch_dequantize(codes, qabsmax, scale2, mean, n, out, out_dtype == QLORA_BF16,
+                                         *t, reinterpret_cast<hipStream_t>(stream)));
+}
+
+qlora_status_t qlora_linear_fwd(const qlora_nf4_weight_t *W, const uint16_t *X, int64_t M,
+                                const uint16_t *L1, const uint16_t *L2, int32_t r, float s,
+                                uint16_t *Y, uint16_t *T, void *workspace, size_t ws_bytes,
+                                void *stream) {
+  if (!valid_weight(W) || !X || !Y || M < 1 || M > (int64_t(1) << 31)) return QLORA_ERR_INVALID_VALUE;
+  if (r < 0 || r > QLORA_MAX_RANK) return QLORA_ERR_INVALID_VALUE;
+  if (r > 0 && (!L1 || !L2 || !T)) return QLORA_ERR_INVALID_VALUE;
+  if (!aligned(X, 16) || !aligned(Y, 16)) return QLORA_ERR_INVALID_VALUE;
+  if (r > 0 && (!aligned(L1, 16) || !aligned(L2, 16) || !aligned(T, 16))) return QLORA_ERR_INVALID_VALUE;
+  const size_t need = round256(linear_fwd_workspace(M, W->h, W->o, r));
+  if (need && (!workspace || ws_bytes < need || !aligned(workspace, 256))) return QLORA_ERR_INVALID_VALUE;
+  const Nf4Tables *t = host_tables();
+  if (!t) return QLORA_ERR_INTERNAL;
+  (void)hipGetLastError();
+  LinearArgs a{W->codes, W->qabsmax, W->scale2, W->mean, W->h, W->o, M, r, s};
+  return launch_status(launch_linear_fwd(a, X, L1, L2, Y, T, workspace, *t,
+                                         reinterpret_cast<hipStream_t>(stream)));
+}
+
+qlora_status_t qlora_linear_bwd(const qlora_nf4_weight_t *W, const uint16_t *X, const uint16_t *T,
+                                const uint16_t *dY, int64_t M, const uint16_t *L1, const uint16_t *L2,
+                                int32_t r, float s, uint16_t *dX, float *dL1, float *dL2,
+                                void *workspace, size_t ws_bytes, void *stream) {
+  if (!valid_weight(W) || !dY || !dX || M < 1 || M > (int64_t(1) << 31)) return QLORA_ERR_INVALID_VALUE;
+  if (r < 0 || r > QLORA_MAX_RANK) return QLORA_ERR_INVALID_VALUE;
+  if (r > 0 && (!X || !T || !L1 || !L2 || !dL1 || !dL2)) return QLORA_ERR_INVALID_VALUE;
+  if (!aligned(dY, 16) || !aligned(dX, 16)) return QLORA_ERR_INVALID_VALUE;
+  if (r > 0 && (!aligned(X, 16) || !aligned(T, 16) || !aligned(L1, 16) || !aligned(L2, 16) ||
+                !aligned(dL1, 16) || !aligned(dL2, 16)))
+    return QLORA_ERR_INVALID_VALUE;
+  const size_t need = round256(linear_bwd_workspace(M, W->h, W->o, r));
+  if (need && (!workspace || ws_bytes < need || !aligned(workspace, 256))) return QLORA_ERR_INVALID_VALUE;
+  const Nf4Tables *t = host_tables();
+  if (!t) return QLORA_ERR_INTERNAL;
+  (void)hipGetLastError();
+  LinearArgs a{W->codes, W->qabsmax, W->scale2, W->mean, W->h, W->o, M, r, s};
+  return launch_status(launch_linear_bwd(a, X, T, dY, L1, L2, dX, dL1, dL2, workspace, *t,
+                                         reinterpret_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

@@ -1,0 +1,17 @@
+// Host-side launchers of the codec and linear-layer kernels.
+#pragma once
+
+#include "common.h"
+
+namespace ql {
+
+hipError_t launch_quantize(const void *w, bool bf16, int64_t n, uint8_t *codes, float *absmax,
+                           const Nf4Tables &tab, hipStream_t st);
+size_t dq_workspace_bytes();
+hipError_t launch_double_quant(const float *absmax, int64_t nb, int8_t *qabsmax, float *scale2,
+                               float *mean, void *ws, hipStream_t st);
+hipError_t launch_dequantize(const uint8_t *codes, const int8_t *qabsmax, const float *scale2,
+                             const float *mean, int64_t n, void *out, bool bf16, const Nf4Tables &tab,
+                             hipStream_t st);
+
+}  // namespace ql

@@ -1,0 +1,27 @@
+// Host-side launchers of the NF4 + LoRA linear-layer kernels.
+#pragma once
+
+#include "common.h"
+
+namespace ql {
+
+struct LinearArgs {
+  const uint8_t *codes;   // [o][h] packed NF4 codes
+  const int8_t *qabsmax;  // [o][h/64]
+  const float *scale2;    // per 256 block scales
+  const float *mean;      // 1 value
+  int64_t h, o, M;
+  int r;
+  float s;
+};
+
+size_t linear_fwd_workspace(int64_t M, int64_t h, int64_t o, int r);
+size_t linear_bwd_workspace(int64_t M, int64_t h, int64_t o, int r);
+
+hipError_t launch_linear_fwd(const LinearArgs &a, const uint16_t *X, const uint16_t *L1, const uint16_t *L2,
+                             uint16_t *Y, uint16_t *T, void *ws, const Nf4Tables &tab, hipStream_t st);
+hipError_t launch_linear_bwd(const LinearArgs &a, const uint16_t *X, const uint16_t *T, const uint16_t *dY,
+                             const uint16_t *L1, const uint16_t *L2, uint16_t *dX, float *dL1, float *dL2,
+                             void *ws, const Nf4Tables &tab, hipStream_t st);
+
+}  // namespace ql

@@ -1,0 +1,734 @@
+// NF4 + LoRA linear layer for gfx950: Y = X·W_hat + s·(X·L1)·L2 and its
+// backward into dX, dL1, dL2 ([MC] "The algebra", Eq. 3 and Figure 1;
+// [TT] §3-§4).  W_hat is never materialised in HBM: every kernel that needs
+// it decodes the 4-bit codes in registers, rescales by the double-quantized
+// block scale and hands bf16 values to the matrix cores.
+//
+// Kernels
+//   relayout_kernel      tiny bf16 transposes / zero padding of L1, L2
+//   skinny_kernel        P = A·Bt^T for a narrow Bt (the rank-r products
+//                        X·L1 and dY·L2^T), MFMA 16x16x32, split-K partials
+//   skinny_finish        sums the partials, rounds to bf16 (T or U) and
+//                        writes the s-scaled copy the GEMM epilogue uses
+//   nf4_gemm_kernel      fused dequant-GEMM, MFMA 32x32x16: forward
+//                        (B = W_hat, K along h) and dX (B = W_hat^T, K
+//                        along o); the rank-r LoRA product is added as extra
+//                        K steps on the same accumulators
+//   nf4_gemv_kernel      M <= 16 forward: streams the codes once, decodes a
+//                        byte (two codes) per LDS lookup, applies the block
+//                        scale after each 64-wide MFMA pair
+//   lora_grad_kernel     dL1 = s·X^T·U and dL2 = s·T^T·dY: reduction over
+//                        tokens, LDS-transposed operands, split over tokens
+//   lora_grad_finish     sums the token splits, scales by s, stores dL1
+//                        [h][r] or dL2 [r][o]
+
+#include "linear.h"
+
+namespace ql {
+
+namespace {
+
+inline int64_t rup(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
+inline int64_t cdiv(int64_t x, int64_t m) { return (x + m - 1) / m; }
+
+QL_DEV bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+QL_DEV f32x4 mfma16(u32x4 a, u32x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), as_bf16x8(b), c, 0, 0, 0);
+}
+QL_DEV f32x16 mfma32(u32x4 a, u32x4 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(b), c, 0, 0, 0);
+}
+
+QL_DEV uint16_t to_bf16(float v) { return (uint16_t)(pack_bf16x2(v, 0.0f) & 0xFFFFu); }
+
+}  // namespace
+
+// ---------------------------------------------------------------------------
+// dst[a][b] = (a < av && b < bv) ? (trans ? src[b*lds + a] : src[a*lds + b]) : 0
+// ---------------------------------------------------------------------------
+__global__ void relayout_kernel(const uint16_t *__restrict__ src, int64_t lds, bool trans, int64_t A,
+                                int64_t B, int64_t av, int64_t bv, uint16_t *__restrict__ dst) {
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= A * B) return;
+  const int64_t a = idx / B, b = idx % B;
+  uint16_t v = 0;
+  if (a < av && b < bv) v = trans ? src[b * lds + a] : src[a * lds + b];
+  dst[idx] = v;
+}
+
+// ---------------------------------------------------------------------------
+// Rank-r products.  part[s][m][q] = sum over split s of A[m][k] * Bt[q][k].
+// A wave owns 16 rows and all NT*16 columns; operands come straight from
+// global memory in MFMA fragment order (16 B per lane per K step).
+// ---------------------------------------------------------------------------
+template <int NT>
+__global__ __launch_bounds__(256) void skinny_kernel(const uint16_t *__restrict__ A, int64_t lda, int64_t M,
+                                                     int64_t K, const uint16_t *__restrict__ Bt, int64_t ldb,
+                                                     int rvalid, int64_t kchunk, float *__restrict__ part) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t m0 = (int64_t)blockIdx.x * 64 + wave * 16;
+  const int64_t kb = (int64_t)blockIdx.y * kchunk;
+  const int64_t ke = kb + kchunk < K ? kb + kchunk : K;
+  const int g = lane >> 4, r16 = lane & 15;
+  const int64_t m = m0 + r16;
+  const bool mok = m < M;
+  f32x4 acc[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) acc[t] = f32x4{0, 0, 0, 0};
+  const uint16_t *arow = A + (mok ? m : 0) * lda + 8 * g;
+#pragma unroll 2
+  for (int64_t k = kb; k < ke; k += 32) {
+    u32x4 a = mok ? *reinterpret_cast<const u32x4 *>(arow + k) : u32x4{0, 0, 0, 0};
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      const int q = t * 16 + r16;
+      u32x4 b = q < rvalid ? *reinterpret_cast<const u32x4 *>(Bt + (int64_t)q * ldb + k + 8 * g)
+                           : u32x4{0, 0, 0, 0};
+      acc[t] = mfma16(a, b, acc[t]);
+    }
+  }
+  constexpr int RP = NT * 16;
+  float *out = part + (int64_t)blockIdx.y * M * RP;
+#pragma unroll
+  for (int t = 0; t < NT; ++t)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int64_t row = m0 + 4 * g + v;
+      if (row < M) out[row * RP + t * 16 + r16] = acc[t][v];
+    }
+}
+
+// out1[m][q] = bf16(sum) for q < n1 (row stride ld1; zero for r <= q < n1)
+// out2[m][q] = bf16(s * sum) for q < ld2 (zero for q >= r)
+__global__ void skinny_finish_kernel(const float *__restrict__ part, int S, int64_t M, int RP, int r, float s,
+                                     uint16_t *__restrict__ out1, int ld1, uint16_t *__restrict__ out2, int ld2) {
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t W = ld2 > ld1 ? ld2 : ld1;
+  if (idx >= M * W) return;
+  const int64_t m = idx / W;
+  const int q = (int)(idx % W);
+  float acc = 0.0f;
+  if (q < r)
+    for (int i = 0; i < S; ++i) acc += part[((int64_t)i * M + m) * RP + q];
+  if (out1 && q < ld1) out1[m * ld1 + q] = q < r ? to_bf16(acc) : (uint16_t)0;
+  if (out2 && q < ld2) out2[m * ld2 + q] = q < r ? to_bf16(s * acc) : (uint16_t)0;
+}
+
+// ---------------------------------------------------------------------------
+// Fused dequant-GEMM.  C[M][N] = A[M][K]·B[K][N] (+ A2[M][K2]·B2[N][K2]^T)
+//   forward (TRANS = false): A = X, B[k][n] = W_hat^T: codes row n, K along h
+//   dX      (TRANS = true) : A = dY, B[k][n] = codes row k (o index), N along h
+// 256 threads = 2x2 waves; workgroup tile BM x BN, K step 64 (one quantization
+// block per weight row per step in the forward).  Register-staged double
+// buffering: the next tile's global loads are in flight while the matrix
+// cores work on the current LDS buffer; the codes are decoded to bf16 while
+// being written to LDS (k-contiguous [n][k] rows in both directions, so the
+// MFMA B fragments are plain 16-byte LDS reads).
+// ---------------------------------------------------------------------------
+struct GemmParams {
+  const uint16_t *A;
+  int64_t lda;
+  const uint8_t *codes;
+  const int8_t *qabsmax;
+  const float *scale2;
+  const float *mean;
+  int64_t ldw;  // weights per codes row (h)
+  const uint16_t *A2;
+  int64_t lda2;
+  const uint16_t *B2;
+  int64_t ldb2;
+  int ksteps;   // 64-wide K steps over the dequantized weight
+  int ksteps2;  // 64-wide K steps over the LoRA operands
+  int64_t M, N;
+  uint16_t *C;
+  int64_t ldc;
+  int tiles_m, tiles_n;
+  float level[16];
+};
+
+template <int BM, int BN, bool TRANS>
+__global__ __launch_bounds__(256) void nf4_gemm_kernel(GemmParams p) {
+  constexpr int BK = 64, LDK = BK + 8;
+  constexpr int WTM = BM / 2, WTN = BN / 2, TM = WTM / 32, TN = WTN / 32;
+  constexpr int A_CH = BM * 8 / 256;                       // 16-B A chunks per thread
+  constexpr int WU = TRANS ? (BN + 255) / 256 : BN * 2 / 256;  // weight units per thread
+  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * (BM + BN) * LDK];
+  __shared__ float lut[64];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  if (tid < 64) lut[tid] = p.level[tid >> 2];
+
+  int bid = blockIdx.x;
+  const int ntiles = p.tiles_m * p.tiles_n;
+  if ((ntiles & 7) == 0) bid = (bid & 7) * (ntiles >> 3) + (bid >> 3);  // one XCD -> contiguous tiles
+  const int tn = bid % p.tiles_n, tm = bid / p.tiles_n;
+  const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
+  const float mu = *p.mean;
+
+  f32x16 acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
+
+  auto As = [&](int buf) { return smem + buf * (BM + BN) * LDK; };
+  auto Bs = [&](int buf) { return smem + buf * (BM + BN) * LDK + BM * LDK; };
+
+  u32x4 ra[A_CH];
+  // weight staging: forward = 16 B of codes per unit; dX = 8 rows x 4 B per unit
+  u32x4 rc[WU][TRANS ? 2 : 1];
+  int8_t rq[WU][TRANS ? 8 : 1];
+  float rs[WU][TRANS ? 8 : 1];
+
+  auto load_tile = [&](int kt) {
+#pragma unroll
+    for (int c = 0; c < A_CH; ++c) {
+      const int chunk = tid + 256 * c, row = chunk >> 3, col8 = chunk & 7;
+      const int64_t m = m0 + row;
+      ra[c] = m < p.M ? *reinterpret_cast<const u32x4 *>(p.A + m * p.lda + (int64_t)kt * BK + col8 * 8)
+                      : u32x4{0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int u = 0; u < WU; ++u) {
+      const int unit = tid + 256 * u;
+      if (!TRANS) {
+        const int row = unit >> 1, half = unit & 1;
+        const int64_t n = n0 + row;
+        if (n < p.N) {
+          const int64_t blk = n * (p.ldw >> 6) + kt;
+          rc[u][0] = *reinterpret_cast<const u32x4 *>(p.codes + ((n * p.ldw) >> 1) + kt * 32 + half * 16);
+          rq[u][0] = p.qabsmax[blk];
+          rs[u][0] = p.scale2[blk >> 8];
+        } else {
+          rc[u][0] = u32x4{0x77777777u, 0x77777777u, 0x77777777u, 0x77777777u};
+          rq[u][0] = 0;
+          rs[u][0] = 0.0f;
+        }
+      } else {
+        const int c8 = unit % (BN / 8), g8 = unit / (BN / 8);
+        const int64_t n = n0 + c8 * 8;
+        const bool ok = unit < BN && n < p.N;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const int64_t krow = (int64_t)kt * BK + g8 * 8 + j;
+          uint32_t w = 0x77777777u;
+          int8_t q = 0;
+          float s2 = 0.0f;
+          if (ok) {
+            w = *reinterpret_cast<const uint32_t *>(p.codes + ((krow * p.ldw) >> 1) + (n >> 1));
+            const int64_t blk = krow * (p.ldw >> 6) + (n >> 6);
+            q = p.qabsmax[blk];
+            s2 = p.scale2[blk >> 8];
+          }
+          rc[u][j >> 2][j & 3] = w;
+          rq[u][j] = q;
+          rs[u][j] = s2;
+        }
+      }
+    }
+  };
+
+  auto lut_at = [&](uint32_t off16) -> float {
+    return *reinterpret_cast<const float *>(reinterpret_cast<const char *>(lut) + off16);
+  };
+
+  auto store_tile = [&](int buf) {
+    uint16_t *as = As(buf);
+    uint16_t *bs = Bs(buf);
+#pragma unroll
+    for (int c = 0; c < A_CH; ++c) {
+      const int chunk = tid + 256 * c, row = chunk >> 3, col8 = chunk & 7;
+      *reinterpret_cast<u32x4 *>(as + row * LDK + col8 * 8) = ra[c];
+    }
+#pragma unroll
+    for (int u = 0; u < WU; ++u) {
+      const int unit = tid + 256 * u;
+      if (!TRANS) {
+        const int row = unit >> 1, half = unit & 1;
+        const float ah = scale_hat(rq[u][0], rs[u][0], mu);
+        uint32_t o[16];
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+          const uint32_t hi = rc[u][0][d] & 0xF0F0F0F0u;
+          const uint32_t lo = (rc[u][0][d] << 4) & 0xF0F0F0F0u;
+#pragma unroll
+          for (int b = 0; b < 4; ++b)
+            o[4 * d + b] = pack_bf16x2(lut_at((hi >> (8 * b)) & 0xFF) * ah, lut_at((lo >> (8 * b)) & 0xFF) * ah);
+        }
+        u32x4 *dst = reinterpret_cast<u32x4 *>(bs + row * LDK + half * 32);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) dst[q] = u32x4{o[4 * q], o[4 * q + 1], o[4 * q + 2], o[4 * q + 3]};
+      } else {
+        if (unit < BN) {
+          const int c8 = unit % (BN / 8), g8 = unit / (BN / 8);
+          float w[8][8];
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            const float ah = scale_hat(rq[u][j], rs[u][j], mu);
+            const uint32_t word = rc[u][j >> 2][j & 3];
+            const uint32_t hi = word & 0xF0F0F0F0u;
+            const uint32_t lo = (word << 4) & 0xF0F0F0F0u;
+#pragma unroll
+            for (int b = 0; b < 4; ++b) {
+              w[j][2 * b] = lut_at((hi >> (8 * b)) & 0xFF) * ah;
+              w[j][2 * b + 1] = lut_at((lo >> (8 * b)) & 0xFF) * ah;
+            }
+          }
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            *reinterpret_cast<u32x4 *>(bs + (c8 * 8 + e) * LDK + g8 * 8) =
+                u32x4{pack_bf16x2(w[0][e], w[1][e]), pack_bf16x2(w[2][e], w[3][e]),
+                      pack_bf16x2(w[4][e], w[5][e]), pack_bf16x2(w[6][e], w[7][e])};
+        }
+      }
+    }
+  };
+
+  auto compute = [&](int buf) {
+    const uint16_t *as = As(buf) + (wm * WTM + (lane & 31)) * LDK + (lane >> 5) * 8;
+    const uint16_t *bs = Bs(buf) + (wn * WTN + (lane & 31)) * LDK + (lane >> 5) * 8;
+#pragma unroll
+    for (int kk = 0; kk < BK / 16; ++kk) {
+      u32x4 af[TM], bf[TN];
+#pragma unroll
+      for (int i = 0; i < TM; ++i) af[i] = *reinterpret_cast<const u32x4 *>(as + i * 32 * LDK + kk * 16);
+#pragma unroll
+      for (int j = 0; j < TN; ++j) bf[j] = *reinterpret_cast<const u32x4 *>(bs + j * 32 * LDK + kk * 16);
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j) acc[i][j] = mfma32(af[i], bf[j], acc[i][j]);
+    }
+  };
+
+  __syncthreads();  // lut ready
+  load_tile(0);
+  store_tile(0);
+  __syncthreads();
+  for (int kt = 0; kt < p.ksteps; ++kt) {
+    const bool more = kt + 1 < p.ksteps;
+    if (more) load_tile(kt + 1);
+    compute(kt & 1);
+    if (more) store_tile((kt + 1) & 1);
+    __syncthreads();
+  }
+
+  // LoRA: extra K steps over (A2, B2), both bf16 and k-contiguous
+  for (int k2 = 0; k2 < p.ksteps2; ++k2) {
+    uint16_t *as = As(0);
+    uint16_t *bs = Bs(0);
+#pragma unroll
+    for (int c = 0; c < A_CH; ++c) {
+      const int chunk = tid + 256 * c, row = chunk >> 3, col8 = chunk & 7;
+      const int64_t m = m0 + row;
+      *reinterpret_cast<u32x4 *>(as + row * LDK + col8 * 8) =
+          m < p.M ? *reinterpret_cast<const u32x4 *>(p.A2 + m * p.lda2 + (int64_t)k2 * BK + col8 * 8)
+                  : u32x4{0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int c = 0; c < BN * 8 / 256; ++c) {
+      const int chunk = tid + 256 * c, row = chunk >> 3, col8 = chunk & 7;
+      const int64_t n = n0 + row;
+      *reinterpret_cast<u32x4 *>(bs + row * LDK + col8 * 8) =
+          n < p.N ? *reinterpret_cast<const u32x4 *>(p.B2 + n * p.ldb2 + (int64_t)k2 * BK + col8 * 8)
+                  : u32x4{0, 0, 0, 0};
+    }
+    __syncthreads();
+    compute(0);
+    __syncthreads();
+  }
+
+  // Epilogue: fp32 -> bf16 through LDS, then coalesced 16-B stores.
+  constexpr int LDC = BN + 8;
+  uint16_t *cs = smem;
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int row = wm * WTM + 32 * i + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+        const int col = wn * WTN + 32 * j + (lane & 31);
+        cs[row * LDC + col] = to_bf16(acc[i][j][v]);
+      }
+  __syncthreads();
+  for (int chunk = tid; chunk < BM * BN / 8; chunk += 256) {
+    const int row = chunk / (BN / 8), c8 = chunk % (BN / 8);
+    const int64_t m = m0 + row, n = n0 + c8 * 8;
+    if (m < p.M && n < p.N)
+      *reinterpret_cast<u32x4 *>(p.C + m * p.ldc + n) = *reinterpret_cast<const u32x4 *>(cs + row * LDC + c8 * 8);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Few-token forward (M <= 16).  Workgroup = 16 output rows; its 4 waves split
+// the K range and reduce through LDS.  Lane l decodes 8 bytes (16 codes) of
+// row n0 + l%16 per 64-block; a byte indexes a 256-entry LDS table holding
+// the bf16 pair (level[high nibble], level[low nibble]).  The bf16 levels go
+// through the matrix core against the tokens and the block scale a_hat is
+// applied to the float32 MFMA result of each 64-block.
+// ---------------------------------------------------------------------------
+struct GemvParams {
+  const uint16_t *X;
+  int64_t ldx;
+  int M;
+  const uint8_t *codes;
+  const int8_t *qabsmax;
+  const float *scale2;
+  const float *mean;
+  int64_t K, N;
+  const uint16_t *sT;  // [M][ldt] bf16, s already applied (r > 0)
+  int ldt;
+  int r;
+  const uint16_t *L2;  // [r][N] bf16
+  uint16_t *Y;
+  int64_t ldy;
+  float level[16];
+};
+
+__global__ __launch_bounds__(256) void nf4_gemv_kernel(GemvParams p) {
+  __shared__ uint32_t lut2[256];
+  __shared__ float red[4][16][17];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  lut2[tid] = pack_bf16x2(p.level[tid >> 4], p.level[tid & 15]);
+  __syncthreads();
+
+  const int64_t n0 = (int64_t)blockIdx.x * 16;
+  const int g = lane >> 4, r16 = lane & 15;
+  const int64_t n = n0 + r16;
+  const int m = r16;
+  const bool mok = m < p.M;
+  const int64_t nblk = p.K >> 6;
+  const int64_t b0 = wave * nblk / 4, b1 = (wave + 1) * nblk / 4;
+  const float mu = *p.mean;
+  const uint8_t *crow = p.codes + n * (p.K >> 1) + 8 * g;
+  const int8_t *qrow = p.qabsmax + n * nblk;
+  const uint16_t *xrow = p.X + (int64_t)(mok ? m : 0) * p.ldx + 16 * g;
+  f32x4 acc = {0, 0, 0, 0};
+#pragma unroll 4
+  for (int64_t b = b0; b < b1; ++b) {
+    const u32x2 cw = *reinterpret_cast<const u32x2 *>(crow + b * 32);
+    const float ah = scale_hat(qrow[b], p.scale2[(n * nblk + b) >> 8], mu);
+    const u32x4 x0 = mok ? *reinterpret_cast<const u32x4 *>(xrow + b * 64) : u32x4{0, 0, 0, 0};
+    const u32x4 x1 = mok ? *reinterpret_cast<const u32x4 *>(xrow + b * 64 + 8) : u32x4{0, 0, 0, 0};
+    const u32x4 w0 = {lut2[cw[0] & 0xFF], lut2[(cw[0] >> 8) & 0xFF], lut2[(cw[0] >> 16) & 0xFF], lut2[cw[0] >> 24]};
+    const u32x4 w1 = {lut2[cw[1] & 0xFF], lut2[(cw[1] >> 8) & 0xFF], lut2[(cw[1] >> 16) & 0xFF], lut2[cw[1] >> 24]};
+    f32x4 t = mfma16(x0, w0, f32x4{0, 0, 0, 0});
+    t = mfma16(x1, w1, t);
+#pragma unroll
+    for (int v = 0; v < 4; ++v) acc[v] = __builtin_fmaf(ah, t[v], acc[v]);
+  }
+  // acc[v] = partial Y[token 4g + v][n]
+#pragma unroll
+  for (int v = 0; v < 4; ++v) red[wave][4 * g + v][r16] = acc[v];
+  __syncthreads();
+  if (wave == 0) {
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int tok = 4 * g + v;
+      float y = red[0][tok][r16] + red[1][tok][r16] + red[2][tok][r16] + red[3][tok][r16];
+      if (tok < p.M) {
+        for (int q = 0; q < p.r; ++q)
+          y = __builtin_fmaf(bf16_lo(p.sT[(int64_t)tok * p.ldt + q]), bf16_lo(p.L2[(int64_t)q * p.N + n]), y);
+        p.Y[(int64_t)tok * p.ldy + n] = to_bf16(y);
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Adapter gradients: part[s][i][q] = sum over tokens m of split s of
+// P[m][i] * Q[m][q].  Both operands are token-major in HBM; a workgroup
+// transposes a 64-token slab of each into LDS ([i][m] and [q][m]) so the
+// MFMA fragments are 16-byte LDS reads.  Workgroup = 64 values of i, all q.
+// ---------------------------------------------------------------------------
+template <int NT>
+__global__ __launch_bounds__(256) void lora_grad_kernel(const uint16_t *__restrict__ P, int64_t ldp, int64_t I,
+                                                        const uint16_t *__restrict__ Q, int64_t ldq, int rq,
+                                                        int64_t M, int64_t mchunk, float *__restrict__ part) {
+  constexpr int RP = NT * 16, LDT = 64 + 8;
+  __shared__ __attribute__((aligned(16))) uint16_t Pt[64 * LDT];
+  __shared__ __attribute__((aligned(16))) uint16_t Qt[RP * LDT];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t i0 = (int64_t)blockIdx.x * 64;
+  const int64_t ms = (int64_t)blockIdx.y * mchunk;
+  const int64_t me = ms + mchunk < M ? ms + mchunk : M;
+  const bool qvec = (ldq % 8) == 0;
+  f32x4 acc[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) acc[t] = f32x4{0, 0, 0, 0};
+  for (int64_t mb = ms; mb < me; mb += 64) {
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      const int chunk = tid + 256 * c, mm = chunk >> 3, i8 = chunk & 7;
+      const int64_t m = mb + mm;
+      const u32x4 v = m < me ? *reinterpret_cast<const u32x4 *>(P + m * ldp + i0 + i8 * 8) : u32x4{0, 0, 0, 0};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) Pt[(i8 * 8 + e) * LDT + mm] = (uint16_t)(v[e >> 1] >> (16 * (e & 1)));
+    }
+    for (int chunk = tid; chunk < 64 * (RP / 8); chunk += 256) {
+      const int mm = chunk / (RP / 8), q8 = chunk % (RP / 8);
+      const int64_t m = mb + mm;
+      uint16_t vals[8];
+      if (m < me && qvec && q8 * 8 + 8 <= rq) {
+        const u32x4 v = *reinterpret_cast<const u32x4 *>(Q + m * ldq + q8 * 8);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) vals[e] = (uint16_t)(v[e >> 1] >> (16 * (e & 1)));
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) vals[e] = (m < me && q8 * 8 + e < rq) ? Q[m * ldq + q8 * 8 + e] : (uint16_t)0;
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) Qt[(q8 * 8 + e) * LDT + mm] = vals[e];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      const u32x4 af = *reinterpret_cast<const u32x4 *>(Pt + (wave * 16 + (lane & 15)) * LDT + kk * 32 + (lane >> 4) * 8);
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        const u32x4 bq = *reinterpret_cast<const u32x4 *>(Qt + (t * 16 + (lane & 15)) * LDT + kk * 32 + (lane >> 4) * 8);
+        acc[t] = mfma16(af, bq, acc[t]);
+      }
+    }
+    __syncthreads();
+  }
+  float *out = part + (int64_t)blockIdx.y * I * RP;
+#pragma unroll
+  for (int t = 0; t < NT; ++t)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int64_t i = i0 + wave * 16 + 4 * (lane >> 4) + v;
+      out[i * RP + t * 16 + (lane & 15)] = acc[t][v];
+    }
+}
+
+// dL[i][q] (trans = false, stride r) or dL[q][i] (trans = true, stride I) = s * sum_s part
+__global__ void lora_grad_finish_kernel(const float *__restrict__ part, int S, int64_t I, int RP, int r, float s,
+                                        bool trans, float *__restrict__ out) {
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= I * r) return;
+  int64_t i, q;
+  if (trans) { q = idx / I; i = idx % I; } else { i = idx / r; q = idx % r; }
+  float acc = 0.0f;
+  for (int k = 0; k < S; ++k) acc += part[((int64_t)k * I + i) * RP + q];
+  out[idx] = s * acc;
+}
+
+// ---------------------------------------------------------------------------
+// Host side: split choices (shared by workspace sizing and launches), launches.
+// ---------------------------------------------------------------------------
+namespace {
+
+constexpr int kTargetGroups = 512;
+
+struct Split {
+  int S;
+  int64_t chunk;
+};
+
+Split skinny_split(int64_t M, int64_t K) {
+  const int64_t mt = cdiv(M, 64);
+  int64_t S = cdiv(kTargetGroups, mt);
+  S = S < 1 ? 1 : S;
+  S = S > K / 64 ? K / 64 : S;
+  int64_t chunk = rup(cdiv(K, S), 64);
+  return {(int)cdiv(K, chunk), chunk};
+}
+
+Split grad_split(int64_t M, int64_t I) {
+  const int64_t it = I / 64;
+  int64_t S = cdiv(kTargetGroups, it);
+  const int64_t msteps = cdiv(M, 64);
+  S = S < 1 ? 1 : S;
+  S = S > msteps ? msteps : S;
+  int64_t chunk = rup(cdiv(M, S), 64);
+  return {(int)cdiv(M, chunk), chunk};
+}
+
+struct FwdLayout {
+  int RP16, RP64;
+  Split sk;
+  size_t off_l1t, off_part, off_st, off_l2t, total;
+};
+
+FwdLayout fwd_layout(int64_t M, int64_t h, int64_t o, int r) {
+  FwdLayout L{};
+  if (r == 0) return L;
+  L.RP16 = (int)rup(r, 16);
+  L.RP64 = (int)rup(r, 64);
+  L.sk = skinny_split(M, h);
+  size_t off = 0;
+  auto take = [&](size_t bytes) { size_t at = off; off += rup((int64_t)bytes, 256); return at; };
+  L.off_l1t = take((size_t)L.RP16 * h * 2);
+  L.off_part = take((size_t)L.sk.S * M * L.RP16 * 4);
+  L.off_st = take((size_t)M * L.RP64 * 2);
+  L.off_l2t = take((size_t)o * L.RP64 * 2);
+  L.total = off;
+  return L;
+}
+
+struct BwdLayout {
+  int RP16, RP64;
+  Split sk, g1, g2;
+  size_t off_part, off_u, off_su, off_l1p, off_g1, off_g2, total;
+};
+
+BwdLayout bwd_layout(int64_t M, int64_t h, int64_t o, int r) {
+  BwdLayout L{};
+  if (r == 0) return L;
+  L.RP16 = (int)rup(r, 16);
+  L.RP64 = (int)rup(r, 64);
+  L.sk = skinny_split(M, o);
+  L.g1 = grad_split(M, h);
+  L.g2 = grad_split(M, o);
+  size_t off = 0;
+  auto take = [&](size_t bytes) { size_t at = off; off += rup((int64_t)bytes, 256); return at; };
+  L.off_part = take((size_t)L.sk.S * M * L.RP16 * 4);
+  L.off_u = take((size_t)M * L.RP16 * 2);
+  L.off_su = take((size_t)M * L.RP64 * 2);
+  L.off_l1p = take((size_t)h * L.RP64 * 2);
+  L.off_g1 = take((size_t)L.g1.S * h * L.RP16 * 4);
+  L.off_g2 = take((size_t)L.g2.S * o * L.RP16 * 4);
+  L.total = off;
+  return L;
+}
+
+template <typename T>
+T *at(void *ws, size_t off) { return reinterpret_cast<T *>(reinterpret_cast<char *>(ws) + off); }
+
+void relayout(const uint16_t *src, int64_t lds, bool trans, int64_t A, int64_t B, int64_t av, int64_t bv,
+              uint16_t *dst, hipStream_t st) {
+  const int64_t n = A * B;
+  relayout_kernel<<<(unsigned)cdiv(n, 256), 256, 0, st>>>(src, lds, trans, A, B, av, bv, dst);
+}
+
+void skinny(const uint16_t *A, int64_t lda, int64_t M, int64_t K, const uint16_t *Bt, int64_t ldb, int r, int RP16,
+            const Split &sp, float *part, hipStream_t st) {
+  dim3 grid((unsigned)cdiv(M, 64), (unsigned)sp.S);
+  switch (RP16 / 16) {
+#define QL_SK(NT) case NT: skinny_kernel<NT><<<grid, 256, 0, st>>>(A, lda, M, K, Bt, ldb, r, sp.chunk, part); break;
+    QL_SK(1) QL_SK(2) QL_SK(3) QL_SK(4) QL_SK(5) QL_SK(6) QL_SK(7) QL_SK(8)
+#undef QL_SK
+  }
+}
+
+void lora_grad(const uint16_t *P, int64_t ldp, int64_t I, const uint16_t *Q, int64_t ldq, int r, int RP16,
+               int64_t M, const Split &sp, float *part, hipStream_t st) {
+  dim3 grid((unsigned)(I / 64), (unsigned)sp.S);
+  switch (RP16 / 16) {
+#define QL_LG(NT) case NT: lora_grad_kernel<NT><<<grid, 256, 0, st>>>(P, ldp, I, Q, ldq, r, M, sp.chunk, part); break;
+    QL_LG(1) QL_LG(2) QL_LG(3) QL_LG(4) QL_LG(5) QL_LG(6) QL_LG(7) QL_LG(8)
+#undef QL_LG
+  }
+}
+
+template <int BM, int BN, bool TRANS>
+void gemm_launch(GemmParams &gp, hipStream_t st) {
+  gp.tiles_m = (int)cdiv(gp.M, BM);
+  gp.tiles_n = (int)cdiv(gp.N, BN);
+  nf4_gemm_kernel<BM, BN, TRANS><<<gp.tiles_m * gp.tiles_n, 256, 0, st>>>(gp);
+}
+
+template <bool TRANS>
+void gemm(GemmParams &gp, hipStream_t st) {
+  const int64_t t256 = cdiv(gp.M, 256) * cdiv(gp.N, 256);
+  const int64_t t256x128 = cdiv(gp.M, 256) * cdiv(gp.N, 128);
+  if (gp.M >= 256 && t256 >= 240) gemm_launch<256, 256, TRANS>(gp, st);
+  else if (gp.M >= 256 && t256x128 >= 200) gemm_launch<256, 128, TRANS>(gp, st);
+  else gemm_launch<128, 128, TRANS>(gp, st);
+}
+
+void fill_levels(float *dst, const Nf4Tables &tab) {
+  for (int i = 0; i < 16; ++i) dst[i] = tab.level[i];
+}
+
+}  // namespace
+
+size_t linear_fwd_workspace(int64_t M, int64_t h, int64_t o, int r) { return fwd_layout(M, h, o, r).total; }
+size_t linear_bwd_workspace(int64_t M, int64_t h, int64_t o, int r) { return bwd_layout(M, h, o, r).total; }
+
+hipError_t launch_linear_fwd(const LinearArgs &a, const uint16_t *X, const uint16_t *L1, const uint16_t *L2,
+                             uint16_t *Y, uint16_t *T, void *ws, const Nf4Tables &tab, hipStream_t st) {
+  const FwdLayout L = fwd_layout(a.M, a.h, a.o, a.r);
+  uint16_t *sT = nullptr, *L2t = nullptr;
+  if (a.r > 0) {
+    // T = X·L1 (rank r): L1 [h][r] -> L1t [RP16][h]
+    uint16_t *L1t = at<uint16_t>(ws, L.off_l1t);
+    relayout(L1, a.r, true, L.RP16, a.h, a.r, a.h, L1t, st);
+    float *part = at<float>(ws, L.off_part);
+    skinny(X, a.h, a.M, a.h, L1t, a.h, a.r, L.RP16, L.sk, part, st);
+    sT = at<uint16_t>(ws, L.off_st);
+    skinny_finish_kernel<<<(unsigned)cdiv(a.M * (L.RP64 > a.r ? L.RP64 : a.r), 256), 256, 0, st>>>(
+        part, L.sk.S, a.M, L.RP16, a.r, a.s, T, a.r, sT, L.RP64);
+    L2t = at<uint16_t>(ws, L.off_l2t);
+    relayout(L2, a.o, true, a.o, L.RP64, a.o, a.r, L2t, st);  // L2 [r][o] -> L2t [o][RP64]
+  }
+  if (a.M <= 16) {
+    GemvParams gp{};
+    gp.X = X; gp.ldx = a.h; gp.M = (int)a.M;
+    gp.codes = a.codes; gp.qabsmax = a.qabsmax; gp.scale2 = a.scale2; gp.mean = a.mean;
+    gp.K = a.h; gp.N = a.o;
+    gp.sT = sT; gp.ldt = L.RP64; gp.r = a.r; gp.L2 = L2;
+    gp.Y = Y; gp.ldy = a.o;
+    fill_levels(gp.level, tab);
+    nf4_gemv_kernel<<<(unsigned)(a.o / 16), 256, 0, st>>>(gp);
+    return hipGetLastError();
+  }
+  GemmParams gp{};
+  gp.A = X; gp.lda = a.h;
+  gp.codes = a.codes; gp.qabsmax = a.qabsmax; gp.scale2 = a.scale2; gp.mean = a.mean; gp.ldw = a.h;
+  gp.A2 = sT; gp.lda2 = L.RP64; gp.B2 = L2t; gp.ldb2 = L.RP64;
+  gp.ksteps = (int)(a.h / 64);
+  gp.ksteps2 = a.r > 0 ? L.RP64 / 64 : 0;
+  gp.M = a.M; gp.N = a.o;
+  gp.C = Y; gp.ldc = a.o;
+  fill_levels(gp.level, tab);
+  gemm<false>(gp, st);
+  return hipGetLastError();
+}
+
+hipError_t launch_linear_bwd(const LinearArgs &a, const uint16_t *X, const uint16_t *T, const uint16_t *dY,
+                             const uint16_t *L1, const uint16_t *L2, uint16_t *dX, float *dL1, float *dL2,
+                             void *ws, const Nf4Tables &tab, hipStream_t st) {
+  const BwdLayout L = bwd_layout(a.M, a.h, a.o, a.r);
+  uint16_t *sU = nullptr, *L1p = nullptr;
+  if (a.r > 0) {
+    // U = dY·L2^T: Bt = L2 [r][o] is already k-contiguous
+    float *part = at<float>(ws, L.off_part);
+    skinny(dY, a.o, a.M, a.o, L2, a.o, a.r, L.RP16, L.sk, part, st);
+    uint16_t *U = at<uint16_t>(ws, L.off_u);
+    sU = at<uint16_t>(ws, L.off_su);
+    skinny_finish_kernel<<<(unsigned)cdiv(a.M * L.RP64, 256), 256, 0, st>>>(part, L.sk.S, a.M, L.RP16, a.r, a.s, U,
+                                                                           L.RP16, sU, L.RP64);
+    L1p = at<uint16_t>(ws, L.off_l1p);
+    relayout(L1, a.r, false, a.h, L.RP64, a.h, a.r, L1p, st);  // L1 [h][r] -> [h][RP64]
+    // dL1 = s·X^T·U   (P = X [M][h], Q = U [M][RP16])
+    float *g1 = at<float>(ws, L.off_g1);
+    lora_grad(X, a.h, a.h, U, L.RP16, a.r, L.RP16, a.M, L.g1, g1, st);
+    lora_grad_finish_kernel<<<(unsigned)cdiv(a.h * a.r, 256), 256, 0, st>>>(g1, L.g1.S, a.h, L.RP16, a.r, a.s, false,
+                                                                            dL1);
+    // dL2 = s·T^T·dY  (P = dY [M][o], Q = T [M][r]); stored [r][o]
+    float *g2 = at<float>(ws, L.off_g2);
+    lora_grad(dY, a.o, a.o, T, a.r, a.r, L.RP16, a.M, L.g2, g2, st);
+    lora_grad_finish_kernel<<<(unsigned)cdiv(a.o * a.r, 256), 256, 0, st>>>(g2, L.g2.S, a.o, L.RP16, a.r, a.s, true,
+                                                                            dL2);
+  }
+  GemmParams gp{};
+  gp.A = dY; gp.lda = a.o;
+  gp.codes = a.codes; gp.qabsmax = a.qabsmax; gp.scale2 = a.scale2; gp.mean = a.mean; gp.ldw = a.h;
+  gp.A2 = sU; gp.lda2 = L.RP64; gp.B2 = L1p; gp.ldb2 = L.RP64;
+  gp.ksteps = (int)(a.o / 64);
+  gp.ksteps2 = a.r > 0 ? L.RP64 / 64 : 0;
+  gp.M = a.M; gp.N = a.h;
+  gp.C = dX; gp.ldc = a.h;
+  fill_levels(gp.level, tab);
+  gemm<true>(gp, st);
+  return hipGetLastError();
+}
+
+}  // namespace ql

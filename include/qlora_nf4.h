@@ -1,0 +1,168 @@
+/*
+ * qlora_nf4.h — C ABI of the MI355X (gfx950) NF4 + LoRA linear-layer library.
+ *
+ * The operations are those of QLoRA as described by
+ *   [MC] "QLoRA: Efficient Finetuning of Quantized LLMs" (Michał Chromiak's blog),
+ *   [TT] "QLoRA in LLMs" (TensorTonic),
+ *   [GO] "QLoRA: the paper that put large-model fine-tuning on a desk" (Good Omens).
+ *
+ * Conventions shared by every entry point
+ *  - Tensor pointers are DEVICE pointers owned by the caller; the library never
+ *    allocates, frees or retains them.  Where an entry point needs temporary
+ *    device memory the caller passes a workspace sized by qlora_workspace_size().
+ *  - `stream` is a hipStream_t (NULL = the default stream).  Every call only
+ *    enqueues work on that stream and returns without synchronizing.  Calls on
+ *    different streams are safe when their buffers are disjoint.
+ *  - bf16 tensors are passed as uint16_t bit patterns (bfloat16: 1 sign, 8
+ *    exponent, 7 fraction bits).  All matrices are row-major.
+ *  - Pointers must be 16-byte aligned unless stated otherwise.
+ *  - Errors: arguments are validated before anything is enqueued; on
+ *    QLORA_ERR_INVALID_VALUE nothing is launched and no output is touched.
+ *    A failed kernel launch returns QLORA_ERR_LAUNCH.  No exception crosses
+ *    the ABI.  Non-finite inputs give unspecified (but memory-safe) results.
+ *  - Thread safety: the library holds no mutable state after its one-time
+ *    initialisation of the NF4 tables (done under a lock on first use).
+ */
+#ifndef QLORA_NF4_H_
+#define QLORA_NF4_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  QLORA_OK = 0,
+  QLORA_ERR_INVALID_VALUE = 1, /* bad pointer, size, alignment, rank or workspace */
+  QLORA_ERR_UNSUPPORTED = 2,   /* valid request outside what this build supports */
+  QLORA_ERR_LAUNCH = 3,        /* the HIP runtime rejected a kernel launch */
+  QLORA_ERR_INTERNAL = 4       /* the NF4 tables could not be built */
+} qlora_status_t;
+
+typedef enum { QLORA_F32 = 0, QLORA_BF16 = 1 } qlora_dtype_t;
+
+/* Workspace queries (qlora_workspace_size `op`). */
+typedef enum {
+  QLORA_OP_DOUBLE_QUANT = 0, /* a = number of block scales */
+  QLORA_OP_LINEAR_FWD = 1,   /* a = M tokens, b = h, c = o */
+  QLORA_OP_LINEAR_BWD = 2    /* a = M tokens, b = h, c = o */
+} qlora_op_t;
+
+#define QLORA_BLOCK 64      /* weights per first-level scale ([MC] "2. Double quantization") */
+#define QLORA_CHUNK 256     /* first-level scales per second-level scale ([MC] "A worked memory budget") */
+#define QLORA_MAX_RANK 128  /* largest LoRA rank r accepted */
+
+/*
+ * One frozen NF4 weight with double-quantized scales.  Logical shape h x o
+ * (the pages' W: h inputs, o outputs, [MC] "The algebra").  Stored in
+ * PyTorch's Linear.weight order [o][h]: row n holds output n's h weights, so
+ * each 64-weight block runs along h.  Produced by qlora_quantize on the
+ * [o][h] buffer followed by qlora_double_quant.  This struct is a host
+ * object; the pointers in it are device pointers.
+ */
+typedef struct {
+  const uint8_t *codes;   /* h*o/2 bytes: two 4-bit codes per byte, first in the high nibble */
+  const int8_t *qabsmax;  /* h*o/64 int8 block scales (mean-centred) */
+  const float *scale2;    /* ceil(h*o/64/256) float32 steps, one per 256 block scales */
+  const float *mean;      /* 1 float32: the mean of the float32 block scales */
+  int64_t h;              /* input width, a positive multiple of 64 */
+  int64_t o;              /* output width, a positive multiple of 64 */
+} qlora_nf4_weight_t;
+
+/*
+ * qlora_quantize — blockwise NF4 quantization ([MC] "1. NormalFloat";
+ * [TT] §2 "Choose a scale, then round", §3, §5).
+ *  w       n weights, float32 or bf16 (w_dtype), any 1-D buffer.
+ *  codes   out, ceil(n/2) bytes: code of element 2k in the high nibble of byte k.
+ *  absmax  out, ceil(n/64) float32: the largest magnitude of each 64-block.
+ * Each weight is divided by its block's largest magnitude (IEEE float32
+ * division) and mapped to the nearest of the 16 NF4 levels, ties to the lower
+ * level.  A short last block is zero-padded; an odd n pads the last low nibble
+ * with code 7 (the zero level); an all-zero block gets code 7 everywhere.
+ * Alignment: w, codes and absmax need only their natural alignment.
+ */
+qlora_status_t qlora_quantize(const void *w, qlora_dtype_t w_dtype, int64_t n, uint8_t *codes,
+                              float *absmax, void *stream);
+
+/*
+ * qlora_double_quant — quantization of the block scales ([MC] "2. Double
+ * quantization"; [TT] §6; [GO] "Idea two").
+ *  absmax   nblocks float32 block scales (from qlora_quantize), all >= 0.
+ *  qabsmax  out, nblocks int8.
+ *  scale2   out, ceil(nblocks/256) float32 steps.
+ *  mean     out, 1 float32 (device).
+ *  workspace/ws_bytes  device scratch of at least
+ *           qlora_workspace_size(QLORA_OP_DOUBLE_QUANT, nblocks, ...) bytes.
+ * mean = the exact mean of all scales rounded once to float32 (independent of
+ * summation order).  Each chunk j of 256 consecutive centred scales
+ * c = fp32(a - mean) gets step s2_j = fp32(max|c| / 127) and codes
+ * q = rint(fp32(c / s2_j)) in [-127, 127] ([TT] §2's symmetric int8 scheme;
+ * step 0 gives codes 0).  Requires 1 <= nblocks < 2^32.
+ */
+qlora_status_t qlora_double_quant(const float *absmax, int64_t nblocks, int8_t *qabsmax, float *scale2,
+                                  float *mean, void *workspace, size_t ws_bytes, void *stream);
+
+/*
+ * qlora_dequantize — rebuild n weights ([MC] "1. NormalFloat": codes are
+ * dequantized to BF16 for computation; [GO] "The core move").
+ *  a_hat = fp32(fp32(qabsmax * scale2) + mean)      (no fused multiply-add)
+ *  w_hat = fp32(level[code] * a_hat)                 (out_dtype QLORA_F32)
+ *        = bf16 round-to-nearest-even of that value  (out_dtype QLORA_BF16)
+ *  out   n float32 or bf16 values.  Alignment: natural alignment only.
+ */
+qlora_status_t qlora_dequantize(const uint8_t *codes, const int8_t *qabsmax, const float *scale2,
+                                const float *mean, int64_t n, void *out, qlora_dtype_t out_dtype,
+                                void *stream);
+
+/*
+ * qlora_linear_fwd — Y = X·W_hat + s·(X·L1)·L2 ([MC] "The algebra", Eq. 3;
+ * [TT] §3), with W_hat the bf16 dequantization of W computed on the fly.
+ *  X   [M][h] bf16.     L1 [h][r] bf16.    L2 [r][o] bf16.
+ *  Y   out [M][o] bf16.
+ *  T   out [M][r] bf16 = X·L1 (float32 accumulation, rounded once), kept for
+ *      the backward pass.
+ *  r = 0 means no adapter: L1, L2 and T may be NULL.  1 <= M, 0 <= r <= 128.
+ *  workspace: qlora_workspace_size(QLORA_OP_LINEAR_FWD, M, h, o, r) bytes.
+ * Products accumulate in float32 on bf16 operands; outputs round once to bf16.
+ */
+qlora_status_t qlora_linear_fwd(const qlora_nf4_weight_t *W, const uint16_t *X, int64_t M,
+                                const uint16_t *L1, const uint16_t *L2, int32_t r, float s,
+                                uint16_t *Y, uint16_t *T, void *workspace, size_t ws_bytes,
+                                void *stream);
+
+/*
+ * qlora_linear_bwd — gradients through the frozen dequantized weight into the
+ * adapters ([MC] Figure 1 and "One training step"; [TT] §4; [GO] "The core
+ * move": no gradient ever updates the 4-bit weights, so there is no dW).
+ *  With U = dY·L2^T:
+ *   dX  = dY·W_hat^T + s·U·L1^T   out [M][h] bf16
+ *   dL1 = s·X^T·U                 out [h][r] float32
+ *   dL2 = s·T^T·dY                out [r][o] float32
+ *  T is the forward's saved [M][r] bf16 product X·L1.  r = 0: only dX is
+ *  computed and X, T, L1, L2, dL1, dL2 may be NULL.
+ *  workspace: qlora_workspace_size(QLORA_OP_LINEAR_BWD, M, h, o, r) bytes.
+ */
+qlora_status_t qlora_linear_bwd(const qlora_nf4_weight_t *W, const uint16_t *X, const uint16_t *T,
+                                const uint16_t *dY, int64_t M, const uint16_t *L1, const uint16_t *L2,
+                                int32_t r, float s, uint16_t *dX, float *dL1, float *dL2,
+                                void *workspace, size_t ws_bytes, void *stream);
+
+/* Workspace bytes an entry point needs (always a multiple of 256; may be 0). */
+qlora_status_t qlora_workspace_size(qlora_op_t op, int64_t a, int64_t b, int64_t c, int32_t r,
+                                    size_t *bytes);
+
+/* Static description of a status code (never NULL). */
+const char *qlora_status_string(qlora_status_t status);
+
+/* Host copy of the 16 float32 NF4 levels the kernels use, ascending
+ * (code 0 = -1, code 7 = 0, code 15 = +1).  Returns QLORA_ERR_INTERNAL if the
+ * tables could not be built. */
+qlora_status_t qlora_nf4_levels(float out[16]);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QLORA_NF4_H_ */

@@ -1,0 +1,124 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function the
+header declares, builds the same NF4 codebook as the oracle (independently),
+sizes workspaces, and rejects bad arguments before touching the GPU."""
+import ctypes
+import os
+import re
+import subprocess
+
+import numpy as np
+import pytest
+
+import oracle
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "qlora_nf4.h")
+
+nf4 = pytest.importorskip("bit_quantized_fine_nf4_amd")
+lib = nf4.lib
+
+FAKE = ctypes.c_void_p(0x100000)        # 16-byte aligned, never dereferenced (calls fail validation first)
+ODD = ctypes.c_void_p(0x100002)         # misaligned
+
+
+def header_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(qlora_\w+)\s*\(", text, re.M)))
+
+
+def test_header_functions_are_exported():
+    declared = header_functions()
+    assert {"qlora_quantize", "qlora_double_quant", "qlora_dequantize", "qlora_linear_fwd",
+            "qlora_linear_bwd"} <= set(declared)
+    out = subprocess.run(["nm", "-D", "--defined-only", nf4.LIB_PATH], capture_output=True, text=True).stdout
+    exported = set(re.findall(r"\bT (qlora_\w+)", out))
+    assert set(declared) <= exported
+    for name in declared:
+        assert hasattr(lib, name)
+    assert set(nf4.EXPORTED) == set(declared)
+
+
+def test_library_codebook_matches_oracle_bitwise():
+    lv = np.array(nf4.nf4_levels(), dtype=np.float32)
+    assert np.array_equal(lv.view(np.uint32), oracle.nf4_levels().view(np.uint32))
+
+
+def test_status_strings():
+    for s in range(5):
+        assert lib.qlora_status_string(s)
+    assert b"invalid" in lib.qlora_status_string(1)
+
+
+def test_workspace_sizes():
+    assert nf4.workspace_size(nf4.QLORA_OP_DOUBLE_QUANT, 1000) % 256 == 0
+    assert nf4.workspace_size(nf4.QLORA_OP_LINEAR_FWD, 16, 1024, 1024, 0) == 0
+    for op in (nf4.QLORA_OP_LINEAR_FWD, nf4.QLORA_OP_LINEAR_BWD):
+        b = nf4.workspace_size(op, 2048, 4096, 4096, 16)
+        assert b > 0 and b % 256 == 0
+    with pytest.raises(nf4.QloraError):
+        nf4.workspace_size(nf4.QLORA_OP_LINEAR_FWD, 0, 64, 64, 8)
+    with pytest.raises(nf4.QloraError):
+        nf4.workspace_size(nf4.QLORA_OP_LINEAR_FWD, 8, 64, 64, 129)
+    assert lib.qlora_workspace_size(7, 1, 1, 1, 0, ctypes.byref(ctypes.c_size_t())) == nf4.QLORA_ERR_INVALID_VALUE
+
+
+INV = nf4.QLORA_ERR_INVALID_VALUE
+
+
+def test_quantize_rejects_bad_arguments():
+    q = lib.qlora_quantize
+    assert q(None, 0, 10, FAKE, FAKE, None) == INV
+    assert q(FAKE, 0, 0, FAKE, FAKE, None) == INV
+    assert q(FAKE, 0, -5, FAKE, FAKE, None) == INV
+    assert q(FAKE, 2, 10, FAKE, FAKE, None) == INV
+    assert q(ODD, 0, 10, FAKE, FAKE, None) == INV
+    assert q(FAKE, 1, 10, None, FAKE, None) == INV
+    assert q(FAKE, 1, 10, FAKE, None, None) == INV
+
+
+def test_double_quant_and_dequant_reject_bad_arguments():
+    dq = lib.qlora_double_quant
+    assert dq(FAKE, 0, FAKE, FAKE, FAKE, FAKE, 4096, None) == INV
+    assert dq(FAKE, 1 << 32, FAKE, FAKE, FAKE, FAKE, 4096, None) == INV
+    assert dq(FAKE, 100, FAKE, FAKE, FAKE, FAKE, 8, None) == INV          # workspace too small
+    assert dq(FAKE, 100, FAKE, FAKE, FAKE, None, 4096, None) == INV
+    assert dq(ODD, 100, FAKE, FAKE, FAKE, FAKE, 4096, None) == INV
+    de = lib.qlora_dequantize
+    assert de(FAKE, FAKE, FAKE, FAKE, 0, FAKE, 0, None) == INV
+    assert de(FAKE, FAKE, FAKE, FAKE, 10, FAKE, 5, None) == INV
+    assert de(FAKE, FAKE, FAKE, None, 10, FAKE, 0, None) == INV
+    assert de(FAKE, FAKE, FAKE, FAKE, 10, ODD, 1, None) == INV
+
+
+def weight(h=128, o=64, codes=FAKE):
+    return nf4.NF4WeightT(codes.value if codes is not None else None, FAKE.value, FAKE.value, FAKE.value, h, o)
+
+
+def test_linear_rejects_bad_arguments():
+    fwd, bwd = lib.qlora_linear_fwd, lib.qlora_linear_bwd
+    ok = weight()
+    ws = 1 << 30
+    args = lambda W, X=FAKE, M=4, L1=FAKE, L2=FAKE, r=8, Y=FAKE, T=FAKE, w=FAKE: \
+        fwd(ctypes.byref(W), X, M, L1, L2, r, 2.0, Y, T, w, ws, None)
+    assert args(weight(h=100)) == INV                   # h not a multiple of 64
+    assert args(weight(o=0)) == INV
+    assert args(weight(codes=None)) == INV
+    assert args(weight(codes=ODD)) == INV
+    assert args(ok, M=0) == INV
+    assert args(ok, r=-1) == INV
+    assert args(ok, r=129) == INV
+    assert args(ok, L1=None) == INV
+    assert args(ok, T=None) == INV
+    assert args(ok, X=None) == INV
+    assert args(ok, X=ODD) == INV
+    assert args(ok, w=None) == INV                      # r > 0 needs a workspace
+    assert fwd(ctypes.byref(ok), FAKE, 4, FAKE, FAKE, 8, 2.0, FAKE, FAKE, FAKE, 16, None) == INV
+    b = lambda W=ok, X=FAKE, T=FAKE, dY=FAKE, M=4, r=8, dX=FAKE, dL1=FAKE: \
+        bwd(ctypes.byref(W), X, T, dY, M, FAKE, FAKE, r, 2.0, dX, dL1, FAKE, FAKE, ws, None)
+    assert b(dY=None) == INV
+    assert b(dX=None) == INV
+    assert b(X=None) == INV
+    assert b(T=None) == INV
+    assert b(dL1=None) == INV
+    assert b(M=-1) == INV
+    assert b(W=weight(h=64, o=65)) == INV

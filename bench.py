@@ -1,0 +1,415 @@
+#!/usr/bin/env python3
+"""Benchmark of the NF4 + LoRA linear layer hot path on one MI355X.
+
+Default workload: the LLaMA-7B-shaped attention projection (h = o = 4096,
+2048 tokens, LoRA rank 16, s = 2.0; base weight N(0, 0.02) with 0.1% x10
+outliers).  One step is one pass of the whole hot path on one batch:
+quantize the float32 weight to NF4, double-quantize its block scales,
+dequantize it to bf16, run the forward Y = X·W_hat + s·X·L1·L2 and the backward
+(dX, dL1, dL2).  All inputs are resident in HBM before timing starts.
+
+`value` is the algorithmic forward+backward FLOP of the linear layer divided
+by the whole step's time (the codec stages are inside the step).  Per-stage
+times come from HIP events on the stream the kernels run on; the `roofline`
+object reports the dominant kernel (the slower of the two fused dequant-GEMMs)
+timed with events recorded by the library right around that kernel's launch.
+`cpu_baseline` times the CPU oracle on the same workload.
+
+Other workloads (not the default line): --workload codec (quantize + double
+quant + dequantize of 4e9 bf16 weights), gemv (few-token forward on an
+8192 x 28672 weight at 1, 4 and 16 tokens), small (1024 x 1024, 16 tokens).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "QLoRA linear fwd+bwd TFLOP/s & quantize/dequant GB/s, % of MI355X roofline"
+PEAK_HBM_GBS = 8000.0
+PEAK_BF16_TFLOPS = 2500.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.txt")
+
+
+def parse_args():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="attn_proj", choices=["attn_proj", "codec", "gemv", "small"])
+    ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the CPU oracle timing")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0, help="target CPU work for the oracle baseline")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="first run one plain 1 GiB device-to-device copy (a known-size kernel whose "
+                         "FETCH_SIZE / WRITE_SIZE counters calibrate the HBM traffic figures)")
+    return ap.parse_args()
+
+
+def linear_flops(M, h, o, r):
+    fwd = 2 * M * h * o + 2 * M * r * (h + o)
+    bwd = 2 * M * h * o + 4 * M * r * (h + o)
+    return fwd, bwd
+
+
+def codec_bytes(n, src_bytes, out_bytes):
+    nb = (n + 63) // 64
+    nch = (nb + 255) // 256
+    quant = n * src_bytes + (n + 1) // 2 + 4 * nb
+    dq = 4 * nb + nb + 4 * nch + 4
+    deq = (n + 1) // 2 + nb + 4 * nch + 4 + n * out_bytes
+    return quant, dq, deq
+
+
+class HipEvents:
+    """hipEvent_t handles from the HIP runtime PyTorch already loaded.  The library
+    records them around a kernel launch; torch.cuda.Event refuses to time events it
+    did not record itself, so they are created and read here directly."""
+
+    def __init__(self, torch):
+        import ctypes
+        self.ct = ctypes
+        path = None
+        for line in open("/proc/self/maps"):
+            if "libamdhip64" in line:
+                path = line.split()[-1]
+                break
+        self.hip = ctypes.CDLL(path or os.path.join(os.path.dirname(torch.__file__), "lib", "libamdhip64.so"))
+        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.live = []
+
+    def create(self):
+        ev = self.ct.c_void_p()
+        rc = self.hip.hipEventCreate(self.ct.byref(ev))
+        if rc != 0:
+            raise RuntimeError(f"hipEventCreate failed ({rc})")
+        self.live.append(ev)
+        return ev
+
+    def elapsed_ms(self, a, b) -> float:
+        ms = self.ct.c_float()
+        rc = self.hip.hipEventElapsedTime(self.ct.byref(ms), a, b)
+        if rc != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed ({rc})")
+        return ms.value
+
+    def close(self):
+        for ev in self.live:
+            self.hip.hipEventDestroy(ev)
+        self.live = []
+
+
+def read_traffic(kernel: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, or None
+    when absent or when the kernel source changed since the counters were taken."""
+    import hashlib
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    rec = {}
+    for line in open(TRAFFIC_FILE):
+        line = line.strip()
+        if not line or line.startswith("#") or ":" not in line:
+            continue
+        k, v = line.split(":", 1)
+        rec[k.strip()] = v.strip()
+    src = os.path.join(ROOT, "bit_quantized_fine_nf4_amd", "csrc", rec.get("source", "linear.hip"))
+    if not os.path.exists(src):
+        return None
+    sha = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+    if rec.get("source_sha256_16") != sha:
+        return None
+    key = f"{kernel}.bytes_per_launch"
+    return float(rec[key]) if key in rec else None
+
+
+def cpu_oracle_attn_proj(wl_mod, target_s):
+    """Time the oracle on the whole default workload, repeated until target_s of work."""
+    import numpy as np
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = os.cpu_count() or 1
+    c = wl_mod.C2
+    ls = c.linears[0]
+    w = wl_mod.base_weight(c, 0).numpy().ravel()
+    l1, l2 = wl_mod.lora_factors(c, 0)
+    L1, L2 = l1.float().numpy(), l2.float().numpy()
+    X = wl_mod.activations(c, 0).float().numpy().astype(np.float64)
+    DY = wl_mod.activations(c, 0, tensor=wl_mod.TENSOR_DY).float().numpy().astype(np.float64)
+    reps, t_total = 0, 0.0
+    while t_total < target_s and reps < 50:
+        t0 = time.perf_counter()
+        p, a = oracle.quantize(w)
+        q, s2, mean = oracle.double_quant(a)
+        oracle.dequantize(p, q, s2, mean, w.size, out="bf16")
+        wh = oracle.dequantized_weight(p, q, s2, mean, ls.h, ls.o)
+        oracle.linear_fwd(wh, X, L1, L2, ls.s)
+        oracle.linear_bwd(wh, X, DY, L1, L2, ls.s)
+        t_total += time.perf_counter() - t0
+        reps += 1
+    fwd, bwd = linear_flops(c.tokens, ls.h, ls.o, ls.r)
+    return {"value": round((fwd + bwd) * reps / t_total / 1e12, 6), "unit": "TFLOP/s",
+            "cores": int(threads), "kind": "oracle",
+            "sample": f"whole workload (one full step: quantize, double quant, dequant, fp64 fwd+bwd) x {reps} "
+                      f"reps, {t_total:.1f} s; codec single-threaded NumPy, fp64 GEMMs on {threads} BLAS threads",
+            "s_per_step": round(t_total / reps, 4)}
+
+
+def bench_attn_proj(args, torch, nf4, wl):
+    dev = "cuda:0"
+    c = wl.C2
+    ls = c.linears[0]
+    M, h, o, r, s = c.tokens, ls.h, ls.o, ls.r, ls.s
+    n = h * o
+    w = wl.base_weight(c, 0).to(dev)
+    l1, l2 = (t.to(dev) for t in wl.lora_factors(c, 0))
+    X = wl.activations(c, 0).to(dev)
+    dY = wl.activations(c, 0, tensor=wl.TENSOR_DY).to(dev)
+    codes = torch.empty(n // 2, dtype=torch.uint8, device=dev)
+    absmax = torch.empty(n // 64, dtype=torch.float32, device=dev)
+    qa = torch.empty(n // 64, dtype=torch.int8, device=dev)
+    s2 = torch.empty((n // 64 + 255) // 256, dtype=torch.float32, device=dev)
+    mean = torch.empty(1, dtype=torch.float32, device=dev)
+    dq_ws = torch.empty(nf4.workspace_size(nf4.QLORA_OP_DOUBLE_QUANT, n // 64), dtype=torch.uint8, device=dev)
+    wdeq = torch.empty(n, dtype=torch.bfloat16, device=dev)
+    Y = torch.empty(M, o, dtype=torch.bfloat16, device=dev)
+    T = torch.empty(M, r, dtype=torch.bfloat16, device=dev)
+    dX = torch.empty(M, h, dtype=torch.bfloat16, device=dev)
+    dL1 = torch.empty(h, r, dtype=torch.float32, device=dev)
+    dL2 = torch.empty(r, o, dtype=torch.float32, device=dev)
+    fws = torch.empty(nf4.workspace_size(nf4.QLORA_OP_LINEAR_FWD, M, h, o, r), dtype=torch.uint8, device=dev)
+    bws = torch.empty(nf4.workspace_size(nf4.QLORA_OP_LINEAR_BWD, M, h, o, r), dtype=torch.uint8, device=dev)
+    W = nf4.NF4Weight(codes, qa, s2, mean, h, o)
+    stages = ["quantize", "double_quant", "dequantize", "fwd", "bwd"]
+    E = torch.cuda.Event
+
+    def step(ev=None, kev=None):
+        if kev is not None:
+            nf4.qlora_set_timing_events(nf4.TIMED_GEMM_FWD, kev[0], kev[1])
+            nf4.qlora_set_timing_events(nf4.TIMED_GEMM_DX, kev[2], kev[3])
+        rec = (lambda i: ev[i].record()) if ev is not None else (lambda i: None)
+        rec(0)
+        nf4.qlora_quantize(w, codes, absmax)
+        rec(1)
+        nf4.qlora_double_quant(absmax, qa, s2, mean, dq_ws)
+        rec(2)
+        nf4.qlora_dequantize(codes, qa, s2, mean, n, torch.bfloat16, out=wdeq)
+        rec(3)
+        nf4.qlora_linear_fwd(W, X, l1, l2, s, Y, T, fws)
+        rec(4)
+        nf4.qlora_linear_bwd(W, X, T, dY, l1, l2, s, dX, dL1, dL2, bws)
+        rec(5)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    hev = HipEvents(torch)
+    evs = [[E(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
+    kevs = [[hev.create() for _ in range(4)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i], kevs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    nf4.qlora_set_timing_events(nf4.TIMED_GEMM_FWD, None, None)
+    nf4.qlora_set_timing_events(nf4.TIMED_GEMM_DX, None, None)
+
+    ms_per_step = wall * 1e3 / args.steps
+    st_ms = {k: statistics.mean(e[i].elapsed_time(e[i + 1]) for e in evs) for i, k in enumerate(stages)}
+    gemm_fwd_ms = statistics.mean(hev.elapsed_ms(k[0], k[1]) for k in kevs)
+    gemm_dx_ms = statistics.mean(hev.elapsed_ms(k[2], k[3]) for k in kevs)
+    hev.close()
+    fwd_f, bwd_f = linear_flops(M, h, o, r)
+    qb, dqb, deqb = codec_bytes(n, 4, 2)
+    stages_out = {
+        "quantize": {"ms": st_ms["quantize"], "GB/s": qb / st_ms["quantize"] / 1e6},
+        "double_quant": {"ms": st_ms["double_quant"], "GB/s": dqb / st_ms["double_quant"] / 1e6},
+        "dequantize_bf16": {"ms": st_ms["dequantize"], "GB/s": deqb / st_ms["dequantize"] / 1e6},
+        "linear_fwd": {"ms": st_ms["fwd"], "TFLOP/s": fwd_f / st_ms["fwd"] / 1e9},
+        "linear_bwd": {"ms": st_ms["bwd"], "TFLOP/s": bwd_f / st_ms["bwd"] / 1e9},
+        "gemm_fwd_kernel": {"ms": gemm_fwd_ms, "TFLOP/s": (2 * M * h * o + 2 * M * r * o) / gemm_fwd_ms / 1e9},
+        "gemm_dx_kernel": {"ms": gemm_dx_ms, "TFLOP/s": (2 * M * h * o + 2 * M * r * h) / gemm_dx_ms / 1e9},
+    }
+    for v in stages_out.values():
+        for k in list(v):
+            v[k] = round(v[k], 4)
+    if gemm_dx_ms >= gemm_fwd_ms:
+        dom, dom_ms, dom_flops = "nf4_gemm_kernel<dX>", gemm_dx_ms, 2 * M * h * o + 2 * M * r * h
+        tkey = "gemm_dx"
+    else:
+        dom, dom_ms, dom_flops = "nf4_gemm_kernel<fwd>", gemm_fwd_ms, 2 * M * h * o + 2 * M * r * o
+        tkey = "gemm_fwd"
+    achieved = dom_flops / dom_ms / 1e9
+    roofline = {"bound": "mfma", "achieved": round(achieved, 3), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": read_traffic(tkey),
+                "kernel": dom, "kernel_ms": round(dom_ms, 5), "flop_per_launch": dom_flops}
+    value = (fwd_f + bwd_f) / (ms_per_step * 1e-3) / 1e12
+    line = {"metric": METRIC, "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+            "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True,
+            "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+            "config": {"workload": c.name, "h": h, "o": o, "tokens": M, "r": r, "s": s,
+                       "step": "quantize(fp32 W) + double_quant + dequantize(bf16) + linear_fwd + linear_bwd"},
+            "tokens_per_s": round(M / (ms_per_step * 1e-3), 1), "roofline": roofline, "stages": stages_out}
+    return line
+
+
+def bench_codec(args, torch, nf4, wl):
+    dev = "cuda:0"
+    n = wl.C4_CODEC_N
+    w = wl.codec_weights_device(n, seed=0, device=dev)
+    nb = n // 64
+    codes = torch.empty(n // 2, dtype=torch.uint8, device=dev)
+    absmax = torch.empty(nb, dtype=torch.float32, device=dev)
+    qa = torch.empty(nb, dtype=torch.int8, device=dev)
+    s2 = torch.empty((nb + 255) // 256, dtype=torch.float32, device=dev)
+    mean = torch.empty(1, dtype=torch.float32, device=dev)
+    ws = torch.empty(nf4.workspace_size(nf4.QLORA_OP_DOUBLE_QUANT, nb), dtype=torch.uint8, device=dev)
+    out = torch.empty(n, dtype=torch.bfloat16, device=dev)
+    E = torch.cuda.Event
+
+    def step(ev=None):
+        rec = (lambda i: ev[i].record()) if ev is not None else (lambda i: None)
+        rec(0)
+        nf4.qlora_quantize(w, codes, absmax)
+        rec(1)
+        nf4.qlora_double_quant(absmax, qa, s2, mean, ws)
+        rec(2)
+        nf4.qlora_dequantize(codes, qa, s2, mean, n, torch.bfloat16, out=out)
+        rec(3)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[E(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = [statistics.mean(e[i].elapsed_time(e[i + 1]) for e in evs) for i in range(3)]
+    qb, dqb, deqb = codec_bytes(n, 2, 2)
+    gbs = [qb / ms[0] / 1e6, dqb / ms[1] / 1e6, deqb / ms[2] / 1e6]
+    dom = max(range(3), key=lambda i: ms[i])
+    names = ["quantize_kernel<bf16>", "double_quant", "dequantize_kernel<bf16>"]
+    total_bytes = qb + dqb + deqb
+    ms_step = wall * 1e3 / args.steps
+    return {"metric": METRIC, "value": round(total_bytes / (ms_step * 1e-3) / 1e9, 2), "unit": "GB/s", "n_gpus": 1,
+            "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True,
+            "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+            "config": {"workload": "codec_4e9_bf16", "n": n, "step": "quantize(bf16) + double_quant + dequantize(bf16)"},
+            "roofline": {"bound": "hbm", "achieved": round(gbs[dom], 2), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                         "frac": round(gbs[dom] / PEAK_HBM_GBS, 4), "traffic": None, "kernel": names[dom]},
+            "stages": {"quantize": {"ms": round(ms[0], 4), "GB/s": round(gbs[0], 2),
+                                    "frac_hbm": round(gbs[0] / PEAK_HBM_GBS, 4)},
+                       "double_quant": {"ms": round(ms[1], 4), "GB/s": round(gbs[1], 2)},
+                       "dequantize_bf16": {"ms": round(ms[2], 4), "GB/s": round(gbs[2], 2),
+                                           "frac_hbm": round(gbs[2] / PEAK_HBM_GBS, 4)}}}
+
+
+def bench_gemv(args, torch, nf4, wl):
+    dev = "cuda:0"
+    c = wl.C4_GEMV
+    ls = c.linears[0]
+    h, o = ls.h, ls.o
+    copies = 4  # 4 x 121 MB > the 256 MB last-level cache: every launch streams from HBM
+    w = wl.base_weight(c, 0).to(dev)
+    Ws = [nf4.quantize_weight(w) for _ in range(copies)]
+    del w
+    res = {}
+    hev = HipEvents(torch)
+    for m in wl.C4_GEMV_TOKENS:
+        X = wl.activations(c, 0, tokens=m).to(dev)
+        Y = torch.empty(m, o, dtype=torch.bfloat16, device=dev)
+        for i in range(args.warmup):
+            nf4.qlora_linear_fwd(Ws[i % copies], X, None, None, 1.0, Y)
+        torch.cuda.synchronize()
+        reps = max(args.steps, 8)
+        kev = [[hev.create(), hev.create()] for _ in range(reps)]
+        for i in range(reps):
+            nf4.qlora_set_timing_events(nf4.TIMED_GEMV, kev[i][0], kev[i][1])
+            nf4.qlora_linear_fwd(Ws[i % copies], X, None, None, 1.0, Y)
+        torch.cuda.synchronize()
+        nf4.qlora_set_timing_events(nf4.TIMED_GEMV, None, None)
+        ms = statistics.median(hev.elapsed_ms(k[0], k[1]) for k in kev)
+        nb = h * o // 64
+        bytes_ = h * o // 2 + nb + 4 * ((nb + 255) // 256) + 2 * m * h + 2 * m * o
+        res[m] = {"ms": round(ms, 5), "GB/s": round(bytes_ / ms / 1e6, 2),
+                  "frac_hbm": round(bytes_ / ms / 1e6 / PEAK_HBM_GBS, 4), "bytes": bytes_}
+    worst = min(res, key=lambda k: res[k]["GB/s"])
+    return {"metric": METRIC, "value": res[16]["GB/s"], "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+            "warmup": args.warmup, "ms_per_step": res[16]["ms"], "higher_is_better": True, "scaling": "weak",
+            "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+            "config": {"workload": c.name, "h": h, "o": o, "tokens": list(wl.C4_GEMV_TOKENS), "weight_copies": copies},
+            "roofline": {"bound": "hbm", "achieved": res[worst]["GB/s"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                         "frac": res[worst]["frac_hbm"], "traffic": None, "kernel": f"nf4_gemv_kernel (M={worst})"},
+            "stages": {f"M={k}": v for k, v in res.items()}}
+
+
+def bench_small(args, torch, nf4, wl):
+    dev = "cuda:0"
+    c = wl.C1
+    ls = c.linears[0]
+    M, h, o, r, s = c.tokens, ls.h, ls.o, ls.r, ls.s
+    W = nf4.quantize_weight(wl.base_weight(c, 0).to(dev))
+    l1, l2 = (t.to(dev) for t in wl.lora_factors(c, 0))
+    X = wl.activations(c, 0).to(dev)
+    dY = wl.activations(c, 0, tensor=wl.TENSOR_DY).to(dev)
+    Y, T = nf4.qlora_linear_fwd(W, X, l1, l2, s)
+    for _ in range(args.warmup):
+        nf4.qlora_linear_fwd(W, X, l1, l2, s, Y, T)
+        nf4.qlora_linear_bwd(W, X, T, dY, l1, l2, s)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        nf4.qlora_linear_fwd(W, X, l1, l2, s, Y, T)
+        nf4.qlora_linear_bwd(W, X, T, dY, l1, l2, s)
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    fwd_f, bwd_f = linear_flops(M, h, o, r)
+    return {"metric": METRIC, "value": round((fwd_f + bwd_f) / ms / 1e9, 4), "unit": "TFLOP/s", "n_gpus": 1,
+            "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True,
+            "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+            "config": {"workload": c.name, "h": h, "o": o, "tokens": M, "r": r, "s": s, "step": "linear_fwd + linear_bwd"},
+            "roofline": None}
+
+
+def main():
+    args = parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: this build has no multi-GPU path (asked for --gpus {args.gpus}); "
+              "run with --gpus 1", file=sys.stderr)
+        return 2
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs an MI355X GPU (torch.cuda.is_available() is False)", file=sys.stderr)
+        return 1
+    import bit_quantized_fine_nf4_amd as nf4
+    import workloads as wl
+    if args.copy_calibration:
+        src = torch.ones(1 << 28, dtype=torch.float32, device="cuda:0")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+    fn = {"attn_proj": bench_attn_proj, "codec": bench_codec, "gemv": bench_gemv, "small": bench_small}[args.workload]
+    line = fn(args, torch, nf4, wl)
+    if args.workload == "attn_proj" and not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_oracle_attn_proj(wl, args.cpu_seconds)
+    else:
+        line["cpu_baseline"] = None
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -23,7 +23,8 @@ QLORA_OP_DOUBLE_QUANT, QLORA_OP_LINEAR_FWD, QLORA_OP_LINEAR_BWD = 0, 1, 2
 BLOCK, CHUNK, MAX_RANK = 64, 256, 128
 
 EXPORTED = ("qlora_quantize", "qlora_double_quant", "qlora_dequantize", "qlora_linear_fwd",
-            "qlora_linear_bwd", "qlora_workspace_size", "qlora_status_string", "qlora_nf4_levels")
+            "qlora_linear_bwd", "qlora_workspace_size", "qlora_status_string", "qlora_nf4_levels",
+            "qlora_set_timing_events")
 
 
 class QloraError(RuntimeError):
@@ -39,7 +40,7 @@ class NF4WeightT(ctypes.Structure):
 
 def _load():
     if not os.path.exists(LIB_PATH):
-        raise ImportError(f"{LIB_PATH} is missing: build it with `python -m bit_quantized_fine_nf4_amd.build`")
+        raise ImportError(f"{LIB_PATH} is missing: build it with `python bit_quantized_fine_nf4_amd/build.py`")
     L = ctypes.CDLL(LIB_PATH)
     vp, i64, i32, f32, st = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_float, ctypes.c_int
     sz = ctypes.c_size_t
@@ -53,6 +54,7 @@ def _load():
     L.qlora_status_string.argtypes = [st]
     L.qlora_status_string.restype = ctypes.c_char_p
     L.qlora_nf4_levels.argtypes = [ctypes.POINTER(ctypes.c_float)]
+    L.qlora_set_timing_events.argtypes = [i32, vp, vp]
     for name in EXPORTED:
         if name != "qlora_status_string":
             getattr(L, name).restype = ctypes.c_int
@@ -85,6 +87,24 @@ def nf4_levels() -> list:
     buf = (ctypes.c_float * 16)()
     _check(lib.qlora_nf4_levels(buf), "qlora_nf4_levels")
     return list(buf)
+
+
+TIMED_GEMM_FWD, TIMED_GEMM_DX, TIMED_GEMV = 0, 1, 2
+
+
+def _event_handle(ev):
+    if ev is None:
+        return None
+    if hasattr(ev, "cuda_event"):          # torch.cuda.Event (recorded by the library, so read it
+        return ctypes.c_void_p(ev.cuda_event)  # back with hipEventElapsedTime, not torch)
+    return ctypes.c_void_p(ev.value if isinstance(ev, ctypes.c_void_p) else int(ev))
+
+
+def qlora_set_timing_events(kernel: int, start=None, stop=None):
+    """Record the hipEvent_t pair (start, stop) around later launches of `kernel`
+    by this thread (None, None switches the hook off)."""
+    _check(lib.qlora_set_timing_events(kernel, _event_handle(start), _event_handle(stop)),
+           "qlora_set_timing_events")
 
 
 def workspace_size(op: int, a: int, b: int = 0, c: int = 0, r: int = 0) -> int:

@@ -1,6 +1,7 @@
 """Build libqlora_nf4.so (gfx950) in-tree with hipcc.
 
-Usage: python -m bit_quantized_fine_nf4_amd.build [--jobs N]
+Usage: python bit_quantized_fine_nf4_amd/build.py [--jobs N]   (run by path: importing the
+package loads the library this script builds)
 Every HIP source is compiled for gfx950 with float contraction disabled (the
 codec reproduces the method's separately rounded float32 steps) and with the
 packed-fp32 instructions disabled.
@@ -18,7 +19,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libqlora_nf4.so")
-SOURCES = ["nf4_tables.hip", "codec.hip", "linear.hip", "api.hip"]
+SOURCES = ["nf4_tables.hip", "codec.hip", "linear.hip", "nf4_gemm.hip", "api.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

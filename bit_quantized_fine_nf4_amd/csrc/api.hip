@@ -19,7 +19,7 @@ inline size_t round256(size_t b) { return (b + 255) / 256 * 256; }
 bool valid_weight(const qlora_nf4_weight_t *W) {
   if (!W || !W->codes || !W->qabsmax || !W->scale2 || !W->mean) return false;
   if (W->h <= 0 || W->o <= 0 || W->h % 64 || W->o % 64) return false;
-  if (W->h > (int64_t(1) << 31) || W->o > (int64_t(1) << 31)) return false;
+  if (W->h > (int64_t(1) << 20) || W->o > (int64_t(1) << 20)) return false;
   if (W->h * W->o / 64 >= (int64_t(1) << 32)) return false;
   return aligned(W->codes, 16) && aligned(W->qabsmax, 4) && aligned(W->scale2, 4) && aligned(W->mean, 4);
 }
@@ -44,6 +44,12 @@ qlora_status_t qlora_nf4_levels(float out[16]) {
   const Nf4Tables *t = host_tables();
   if (!t) return QLORA_ERR_INTERNAL;
   for (int i = 0; i < 16; ++i) out[i] = t->level[i];
+  return QLORA_OK;
+}
+
+qlora_status_t qlora_set_timing_events(int32_t kernel, void *start, void *stop) {
+  if (kernel < 0 || kernel > 2) return QLORA_ERR_INVALID_VALUE;
+  set_timing_events(kernel, reinterpret_cast<hipEvent_t>(start), reinterpret_cast<hipEvent_t>(stop));
   return QLORA_OK;
 }
 

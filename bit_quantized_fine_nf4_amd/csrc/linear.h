@@ -15,6 +15,10 @@ struct LinearArgs {
   float s;
 };
 
+// Optional per-thread events recorded around the fused GEMM / GEMV launches
+// (0 = forward GEMM, 1 = dX GEMM, 2 = few-token forward).
+void set_timing_events(int kernel, hipEvent_t start, hipEvent_t stop);
+
 size_t linear_fwd_workspace(int64_t M, int64_t h, int64_t o, int r);
 size_t linear_bwd_workspace(int64_t M, int64_t h, int64_t o, int r);
 

@@ -23,6 +23,7 @@
 //                        [h][r] or dL2 [r][o]
 
 #include "linear.h"
+#include "gemm.h"
 
 namespace ql {
 
@@ -35,9 +36,6 @@ QL_DEV bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
 QL_DEV f32x4 mfma16(u32x4 a, u32x4 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), as_bf16x8(b), c, 0, 0, 0);
-}
-QL_DEV f32x16 mfma32(u32x4 a, u32x4 b, f32x16 c) {
-  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(b), c, 0, 0, 0);
 }
 
 QL_DEV uint16_t to_bf16(float v) { return (uint16_t)(pack_bf16x2(v, 0.0f) & 0xFFFFu); }
@@ -113,255 +111,6 @@ __global__ void skinny_finish_kernel(const float *__restrict__ part, int S, int6
     for (int i = 0; i < S; ++i) acc += part[((int64_t)i * M + m) * RP + q];
   if (out1 && q < ld1) out1[m * ld1 + q] = q < r ? to_bf16(acc) : (uint16_t)0;
   if (out2 && q < ld2) out2[m * ld2 + q] = q < r ? to_bf16(s * acc) : (uint16_t)0;
-}
-
-// ---------------------------------------------------------------------------
-// Fused dequant-GEMM.  C[M][N] = A[M][K]·B[K][N] (+ A2[M][K2]·B2[N][K2]^T)
-//   forward (TRANS = false): A = X, B[k][n] = W_hat^T: codes row n, K along h
-//   dX      (TRANS = true) : A = dY, B[k][n] = codes row k (o index), N along h
-// 256 threads = 2x2 waves; workgroup tile BM x BN, K step 64 (one quantization
-// block per weight row per step in the forward).  Register-staged double
-// buffering: the next tile's global loads are in flight while the matrix
-// cores work on the current LDS buffer; the codes are decoded to bf16 while
-// being written to LDS (k-contiguous [n][k] rows in both directions, so the
-// MFMA B fragments are plain 16-byte LDS reads).
-// ---------------------------------------------------------------------------
-struct GemmParams {
-  const uint16_t *A;
-  int64_t lda;
-  const uint8_t *codes;
-  const int8_t *qabsmax;
-  const float *scale2;
-  const float *mean;
-  int64_t ldw;  // weights per codes row (h)
-  const uint16_t *A2;
-  int64_t lda2;
-  const uint16_t *B2;
-  int64_t ldb2;
-  int ksteps;   // 64-wide K steps over the dequantized weight
-  int ksteps2;  // 64-wide K steps over the LoRA operands
-  int64_t M, N;
-  uint16_t *C;
-  int64_t ldc;
-  int tiles_m, tiles_n;
-  float level[16];
-};
-
-template <int BM, int BN, bool TRANS>
-__global__ __launch_bounds__(256) void nf4_gemm_kernel(GemmParams p) {
-  constexpr int BK = 64, LDK = BK + 8;
-  constexpr int WTM = BM / 2, WTN = BN / 2, TM = WTM / 32, TN = WTN / 32;
-  constexpr int A_CH = BM * 8 / 256;                       // 16-B A chunks per thread
-  constexpr int WU = TRANS ? (BN + 255) / 256 : BN * 2 / 256;  // weight units per thread
-  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * (BM + BN) * LDK];
-  __shared__ float lut[64];
-
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
-  if (tid < 64) lut[tid] = p.level[tid >> 2];
-
-  int bid = blockIdx.x;
-  const int ntiles = p.tiles_m * p.tiles_n;
-  if ((ntiles & 7) == 0) bid = (bid & 7) * (ntiles >> 3) + (bid >> 3);  // one XCD -> contiguous tiles
-  const int tn = bid % p.tiles_n, tm = bid / p.tiles_n;
-  const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
-  const float mu = *p.mean;
-
-  f32x16 acc[TM][TN];
-#pragma unroll
-  for (int i = 0; i < TM; ++i)
-#pragma unroll
-    for (int j = 0; j < TN; ++j)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
-
-  auto As = [&](int buf) { return smem + buf * (BM + BN) * LDK; };
-  auto Bs = [&](int buf) { return smem + buf * (BM + BN) * LDK + BM * LDK; };
-
-  u32x4 ra[A_CH];
-  // weight staging: forward = 16 B of codes per unit; dX = 8 rows x 4 B per unit
-  u32x4 rc[WU][TRANS ? 2 : 1];
-  int8_t rq[WU][TRANS ? 8 : 1];
-  float rs[WU][TRANS ? 8 : 1];
-
-  auto load_tile = [&](int kt) {
-#pragma unroll
-    for (int c = 0; c < A_CH; ++c) {
-      const int chunk = tid + 256 * c, row = chunk >> 3, col8 = chunk & 7;
-      const int64_t m = m0 + row;
-      ra[c] = m < p.M ? *reinterpret_cast<const u32x4 *>(p.A + m * p.lda + (int64_t)kt * BK + col8 * 8)
-                      : u32x4{0, 0, 0, 0};
-    }
-#pragma unroll
-    for (int u = 0; u < WU; ++u) {
-      const int unit = tid + 256 * u;
-      if (!TRANS) {
-        const int row = unit >> 1, half = unit & 1;
-        const int64_t n = n0 + row;
-        if (n < p.N) {
-          const int64_t blk = n * (p.ldw >> 6) + kt;
-          rc[u][0] = *reinterpret_cast<const u32x4 *>(p.codes + ((n * p.ldw) >> 1) + kt * 32 + half * 16);
-          rq[u][0] = p.qabsmax[blk];
-          rs[u][0] = p.scale2[blk >> 8];
-        } else {
-          rc[u][0] = u32x4{0x77777777u, 0x77777777u, 0x77777777u, 0x77777777u};
-          rq[u][0] = 0;
-          rs[u][0] = 0.0f;
-        }
-      } else {
-        const int c8 = unit % (BN / 8), g8 = unit / (BN / 8);
-        const int64_t n = n0 + c8 * 8;
-        const bool ok = unit < BN && n < p.N;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const int64_t krow = (int64_t)kt * BK + g8 * 8 + j;
-          uint32_t w = 0x77777777u;
-          int8_t q = 0;
-          float s2 = 0.0f;
-          if (ok) {
-            w = *reinterpret_cast<const uint32_t *>(p.codes + ((krow * p.ldw) >> 1) + (n >> 1));
-            const int64_t blk = krow * (p.ldw >> 6) + (n >> 6);
-            q = p.qabsmax[blk];
-            s2 = p.scale2[blk >> 8];
-          }
-          rc[u][j >> 2][j & 3] = w;
-          rq[u][j] = q;
-          rs[u][j] = s2;
-        }
-      }
-    }
-  };
-
-  auto lut_at = [&](uint32_t off16) -> float {
-    return *reinterpret_cast<const float *>(reinterpret_cast<const char *>(lut) + off16);
-  };
-
-  auto store_tile = [&](int buf) {
-    uint16_t *as = As(buf);
-    uint16_t *bs = Bs(buf);
-#pragma unroll
-    for (int c = 0; c < A_CH; ++c) {
-      const int chunk = tid + 256 * c, row = chunk >> 3, col8 = chunk & 7;
-      *reinterpret_cast<u32x4 *>(as + row * LDK + col8 * 8) = ra[c];
-    }
-#pragma unroll
-    for (int u = 0; u < WU; ++u) {
-      const int unit = tid + 256 * u;
-      if (!TRANS) {
-        const int row = unit >> 1, half = unit & 1;
-        const float ah = scale_hat(rq[u][0], rs[u][0], mu);
-        uint32_t o[16];
-#pragma unroll
-        for (int d = 0; d < 4; ++d) {
-          const uint32_t hi = rc[u][0][d] & 0xF0F0F0F0u;
-          const uint32_t lo = (rc[u][0][d] << 4) & 0xF0F0F0F0u;
-#pragma unroll
-          for (int b = 0; b < 4; ++b)
-            o[4 * d + b] = pack_bf16x2(lut_at((hi >> (8 * b)) & 0xFF) * ah, lut_at((lo >> (8 * b)) & 0xFF) * ah);
-        }
-        u32x4 *dst = reinterpret_cast<u32x4 *>(bs + row * LDK + half * 32);
-#pragma unroll
-        for (int q = 0; q < 4; ++q) dst[q] = u32x4{o[4 * q], o[4 * q + 1], o[4 * q + 2], o[4 * q + 3]};
-      } else {
-        if (unit < BN) {
-          const int c8 = unit % (BN / 8), g8 = unit / (BN / 8);
-          float w[8][8];
-#pragma unroll
-          for (int j = 0; j < 8; ++j) {
-            const float ah = scale_hat(rq[u][j], rs[u][j], mu);
-            const uint32_t word = rc[u][j >> 2][j & 3];
-            const uint32_t hi = word & 0xF0F0F0F0u;
-            const uint32_t lo = (word << 4) & 0xF0F0F0F0u;
-#pragma unroll
-            for (int b = 0; b < 4; ++b) {
-              w[j][2 * b] = lut_at((hi >> (8 * b)) & 0xFF) * ah;
-              w[j][2 * b + 1] = lut_at((lo >> (8 * b)) & 0xFF) * ah;
-            }
-          }
-#pragma unroll
-          for (int e = 0; e < 8; ++e)
-            *reinterpret_cast<u32x4 *>(bs + (c8 * 8 + e) * LDK + g8 * 8) =
-                u32x4{pack_bf16x2(w[0][e], w[1][e]), pack_bf16x2(w[2][e], w[3][e]),
-                      pack_bf16x2(w[4][e], w[5][e]), pack_bf16x2(w[6][e], w[7][e])};
-        }
-      }
-    }
-  };
-
-  auto compute = [&](int buf) {
-    const uint16_t *as = As(buf) + (wm * WTM + (lane & 31)) * LDK + (lane >> 5) * 8;
-    const uint16_t *bs = Bs(buf) + (wn * WTN + (lane & 31)) * LDK + (lane >> 5) * 8;
-#pragma unroll
-    for (int kk = 0; kk < BK / 16; ++kk) {
-      u32x4 af[TM], bf[TN];
-#pragma unroll
-      for (int i = 0; i < TM; ++i) af[i] = *reinterpret_cast<const u32x4 *>(as + i * 32 * LDK + kk * 16);
-#pragma unroll
-      for (int j = 0; j < TN; ++j) bf[j] = *reinterpret_cast<const u32x4 *>(bs + j * 32 * LDK + kk * 16);
-#pragma unroll
-      for (int i = 0; i < TM; ++i)
-#pragma unroll
-        for (int j = 0; j < TN; ++j) acc[i][j] = mfma32(af[i], bf[j], acc[i][j]);
-    }
-  };
-
-  __syncthreads();  // lut ready
-  load_tile(0);
-  store_tile(0);
-  __syncthreads();
-  for (int kt = 0; kt < p.ksteps; ++kt) {
-    const bool more = kt + 1 < p.ksteps;
-    if (more) load_tile(kt + 1);
-    compute(kt & 1);
-    if (more) store_tile((kt + 1) & 1);
-    __syncthreads();
-  }
-
-  // LoRA: extra K steps over (A2, B2), both bf16 and k-contiguous
-  for (int k2 = 0; k2 < p.ksteps2; ++k2) {
-    uint16_t *as = As(0);
-    uint16_t *bs = Bs(0);
-#pragma unroll
-    for (int c = 0; c < A_CH; ++c) {
-      const int chunk = tid + 256 * c, row = chunk >> 3, col8 = chunk & 7;
-      const int64_t m = m0 + row;
-      *reinterpret_cast<u32x4 *>(as + row * LDK + col8 * 8) =
-          m < p.M ? *reinterpret_cast<const u32x4 *>(p.A2 + m * p.lda2 + (int64_t)k2 * BK + col8 * 8)
-                  : u32x4{0, 0, 0, 0};
-    }
-#pragma unroll
-    for (int c = 0; c < BN * 8 / 256; ++c) {
-      const int chunk = tid + 256 * c, row = chunk >> 3, col8 = chunk & 7;
-      const int64_t n = n0 + row;
-      *reinterpret_cast<u32x4 *>(bs + row * LDK + col8 * 8) =
-          n < p.N ? *reinterpret_cast<const u32x4 *>(p.B2 + n * p.ldb2 + (int64_t)k2 * BK + col8 * 8)
-                  : u32x4{0, 0, 0, 0};
-    }
-    __syncthreads();
-    compute(0);
-    __syncthreads();
-  }
-
-  // Epilogue: fp32 -> bf16 through LDS, then coalesced 16-B stores.
-  constexpr int LDC = BN + 8;
-  uint16_t *cs = smem;
-#pragma unroll
-  for (int i = 0; i < TM; ++i)
-#pragma unroll
-    for (int j = 0; j < TN; ++j)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int row = wm * WTM + 32 * i + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-        const int col = wn * WTN + 32 * j + (lane & 31);
-        cs[row * LDC + col] = to_bf16(acc[i][j][v]);
-      }
-  __syncthreads();
-  for (int chunk = tid; chunk < BM * BN / 8; chunk += 256) {
-    const int row = chunk / (BN / 8), c8 = chunk % (BN / 8);
-    const int64_t m = m0 + row, n = n0 + c8 * 8;
-    if (m < p.M && n < p.N)
-      *reinterpret_cast<u32x4 *>(p.C + m * p.ldc + n) = *reinterpret_cast<const u32x4 *>(cs + row * LDC + c8 * 8);
-  }
 }
 
 // ---------------------------------------------------------------------------
@@ -553,7 +302,7 @@ Split grad_split(int64_t M, int64_t I) {
 struct FwdLayout {
   int RP16, RP64;
   Split sk;
-  size_t off_l1t, off_part, off_st, off_l2t, total;
+  size_t off_l1t, off_part, off_st, total;
 };
 
 FwdLayout fwd_layout(int64_t M, int64_t h, int64_t o, int r) {
@@ -567,7 +316,6 @@ FwdLayout fwd_layout(int64_t M, int64_t h, int64_t o, int r) {
   L.off_l1t = take((size_t)L.RP16 * h * 2);
   L.off_part = take((size_t)L.sk.S * M * L.RP16 * 4);
   L.off_st = take((size_t)M * L.RP64 * 2);
-  L.off_l2t = take((size_t)o * L.RP64 * 2);
   L.total = off;
   return L;
 }
@@ -627,21 +375,18 @@ void lora_grad(const uint16_t *P, int64_t ldp, int64_t I, const uint16_t *Q, int
   }
 }
 
-template <int BM, int BN, bool TRANS>
-void gemm_launch(GemmParams &gp, hipStream_t st) {
-  gp.tiles_m = (int)cdiv(gp.M, BM);
-  gp.tiles_n = (int)cdiv(gp.N, BN);
-  nf4_gemm_kernel<BM, BN, TRANS><<<gp.tiles_m * gp.tiles_n, 256, 0, st>>>(gp);
-}
+thread_local hipEvent_t t_ev[3][2] = {};
 
-template <bool TRANS>
-void gemm(GemmParams &gp, hipStream_t st) {
-  const int64_t t256 = cdiv(gp.M, 256) * cdiv(gp.N, 256);
-  const int64_t t256x128 = cdiv(gp.M, 256) * cdiv(gp.N, 128);
-  if (gp.M >= 256 && t256 >= 240) gemm_launch<256, 256, TRANS>(gp, st);
-  else if (gp.M >= 256 && t256x128 >= 200) gemm_launch<256, 128, TRANS>(gp, st);
-  else gemm_launch<128, 128, TRANS>(gp, st);
-}
+struct TimedLaunch {
+  int k;
+  hipStream_t st;
+  TimedLaunch(int kernel, hipStream_t s) : k(kernel), st(s) {
+    if (t_ev[k][0]) (void)hipEventRecord(t_ev[k][0], st);
+  }
+  ~TimedLaunch() {
+    if (t_ev[k][1]) (void)hipEventRecord(t_ev[k][1], st);
+  }
+};
 
 void fill_levels(float *dst, const Nf4Tables &tab) {
   for (int i = 0; i < 16; ++i) dst[i] = tab.level[i];
@@ -649,13 +394,18 @@ void fill_levels(float *dst, const Nf4Tables &tab) {
 
 }  // namespace
 
+void set_timing_events(int kernel, hipEvent_t start, hipEvent_t stop) {
+  t_ev[kernel][0] = start;
+  t_ev[kernel][1] = stop;
+}
+
 size_t linear_fwd_workspace(int64_t M, int64_t h, int64_t o, int r) { return fwd_layout(M, h, o, r).total; }
 size_t linear_bwd_workspace(int64_t M, int64_t h, int64_t o, int r) { return bwd_layout(M, h, o, r).total; }
 
 hipError_t launch_linear_fwd(const LinearArgs &a, const uint16_t *X, const uint16_t *L1, const uint16_t *L2,
                              uint16_t *Y, uint16_t *T, void *ws, const Nf4Tables &tab, hipStream_t st) {
   const FwdLayout L = fwd_layout(a.M, a.h, a.o, a.r);
-  uint16_t *sT = nullptr, *L2t = nullptr;
+  uint16_t *sT = nullptr;
   if (a.r > 0) {
     // T = X·L1 (rank r): L1 [h][r] -> L1t [RP16][h]
     uint16_t *L1t = at<uint16_t>(ws, L.off_l1t);
@@ -665,8 +415,6 @@ hipError_t launch_linear_fwd(const LinearArgs &a, const uint16_t *X, const uint1
     sT = at<uint16_t>(ws, L.off_st);
     skinny_finish_kernel<<<(unsigned)cdiv(a.M * (L.RP64 > a.r ? L.RP64 : a.r), 256), 256, 0, st>>>(
         part, L.sk.S, a.M, L.RP16, a.r, a.s, T, a.r, sT, L.RP64);
-    L2t = at<uint16_t>(ws, L.off_l2t);
-    relayout(L2, a.o, true, a.o, L.RP64, a.o, a.r, L2t, st);  // L2 [r][o] -> L2t [o][RP64]
   }
   if (a.M <= 16) {
     GemvParams gp{};
@@ -676,19 +424,26 @@ hipError_t launch_linear_fwd(const LinearArgs &a, const uint16_t *X, const uint1
     gp.sT = sT; gp.ldt = L.RP64; gp.r = a.r; gp.L2 = L2;
     gp.Y = Y; gp.ldy = a.o;
     fill_levels(gp.level, tab);
-    nf4_gemv_kernel<<<(unsigned)(a.o / 16), 256, 0, st>>>(gp);
+    {
+      TimedLaunch tl(2, st);
+      nf4_gemv_kernel<<<(unsigned)(a.o / 16), 256, 0, st>>>(gp);
+    }
     return hipGetLastError();
   }
   GemmParams gp{};
   gp.A = X; gp.lda = a.h;
-  gp.codes = a.codes; gp.qabsmax = a.qabsmax; gp.scale2 = a.scale2; gp.mean = a.mean; gp.ldw = a.h;
-  gp.A2 = sT; gp.lda2 = L.RP64; gp.B2 = L2t; gp.ldb2 = L.RP64;
+  gp.codes = a.codes; gp.qabsmax = a.qabsmax; gp.scale2 = a.scale2; gp.mean = a.mean;
+  gp.ldw = a.h; gp.wrows = a.o;
+  gp.A2 = sT; gp.lda2 = L.RP64; gp.B2 = L2; gp.ldb2 = a.o; gp.b2rows = a.r;
   gp.ksteps = (int)(a.h / 64);
   gp.ksteps2 = a.r > 0 ? L.RP64 / 64 : 0;
   gp.M = a.M; gp.N = a.o;
   gp.C = Y; gp.ldc = a.o;
   fill_levels(gp.level, tab);
-  gemm<false>(gp, st);
+  {
+    TimedLaunch tl(0, st);
+    launch_nf4_gemm(gp, false, st);
+  }
   return hipGetLastError();
 }
 
@@ -720,14 +475,18 @@ hipError_t launch_linear_bwd(const LinearArgs &a, const uint16_t *X, const uint1
   }
   GemmParams gp{};
   gp.A = dY; gp.lda = a.o;
-  gp.codes = a.codes; gp.qabsmax = a.qabsmax; gp.scale2 = a.scale2; gp.mean = a.mean; gp.ldw = a.h;
-  gp.A2 = sU; gp.lda2 = L.RP64; gp.B2 = L1p; gp.ldb2 = L.RP64;
+  gp.codes = a.codes; gp.qabsmax = a.qabsmax; gp.scale2 = a.scale2; gp.mean = a.mean;
+  gp.ldw = a.h; gp.wrows = a.o;
+  gp.A2 = sU; gp.lda2 = L.RP64; gp.B2 = L1p; gp.ldb2 = L.RP64; gp.b2rows = (int)a.h;
   gp.ksteps = (int)(a.o / 64);
   gp.ksteps2 = a.r > 0 ? L.RP64 / 64 : 0;
   gp.M = a.M; gp.N = a.h;
   gp.C = dX; gp.ldc = a.h;
   fill_levels(gp.level, tab);
-  gemm<true>(gp, st);
+  {
+    TimedLaunch tl(1, st);
+    launch_nf4_gemm(gp, true, st);
+  }
   return hipGetLastError();
 }
 

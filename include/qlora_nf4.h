@@ -67,8 +67,8 @@ typedef struct {
   const int8_t *qabsmax;  /* h*o/64 int8 block scales (mean-centred) */
   const float *scale2;    /* ceil(h*o/64/256) float32 steps, one per 256 block scales */
   const float *mean;      /* 1 float32: the mean of the float32 block scales */
-  int64_t h;              /* input width, a positive multiple of 64 */
-  int64_t o;              /* output width, a positive multiple of 64 */
+  int64_t h;              /* input width, a positive multiple of 64, at most 2^20 */
+  int64_t o;              /* output width, a positive multiple of 64, at most 2^20 */
 } qlora_nf4_weight_t;
 
 /*
@@ -152,6 +152,16 @@ qlora_status_t qlora_linear_bwd(const qlora_nf4_weight_t *W, const uint16_t *X, 
 /* Workspace bytes an entry point needs (always a multiple of 256; may be 0). */
 qlora_status_t qlora_workspace_size(qlora_op_t op, int64_t a, int64_t b, int64_t c, int32_t r,
                                     size_t *bytes);
+
+/*
+ * Timing hook for benchmarks and profilers.  `kernel` 0 = the forward fused
+ * dequant-GEMM, 1 = the dX fused dequant-GEMM, 2 = the few-token forward
+ * (M <= 16).  When `start`/`stop` (hipEvent_t handles) are non-NULL, every
+ * later launch of that kernel by the calling thread records `start` just
+ * before and `stop` just after itself on the call's stream.  NULL/NULL turns
+ * the hook off.  Per thread; the library only records, never synchronizes.
+ */
+qlora_status_t qlora_set_timing_events(int32_t kernel, void *start, void *stop);
 
 /* Static description of a status code (never NULL). */
 const char *qlora_status_string(qlora_status_t status);

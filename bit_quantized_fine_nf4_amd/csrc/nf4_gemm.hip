@@ -2,30 +2,40 @@
 //
 // [MC] "1. NormalFloat" / [GO] "The core move": the 4-bit weights are
 // dequantized to BF16 on the fly for the matrix multiplication and never
-// stored in wider form.  Here every workgroup decodes the codes of its weight
-// tile straight into LDS as bf16(level[code] * a_hat) and feeds bf16 MFMA
+// stored in wider form.  Every workgroup decodes the codes of its weight tile
+// straight into LDS as bf16(level[code] * a_hat) and feeds bf16 MFMA
 // (v_mfma_f32_32x32x16_bf16) with float32 accumulation.
 //
-// Layout.  256 threads = 2 x 2 waves, workgroup tile BM x BN, K step 64.
-//  A tile  [m][k] in LDS (row stride 72 bf16), read as 16-byte fragments.
-//  Forward B tile [n][k] (row stride 72): each 32-weight unit is one half of
-//   one 64-weight block of codes row n, i.e. one scale per unit.
-//  dX B tile [k][n] (row stride BN + 16): the codes are contiguous along n
-//   (h), so each unit is 32 consecutive n of one row k — again one scale per
-//   unit — and the MFMA B fragments (8 consecutive k of one n) come from two
-//   transposing LDS reads (ds_read_b64_tr_b16).  A 16-lane group of that
-//   instruction returns, to lane i, element i%4 of the 8-byte chunks named by
-//   lanes i/4, 4+i/4, 8+i/4, 12+i/4; lane 4j+q names row k0+j, column n0+4q,
-//   so lane i receives rows k0..k0+3 of column n0+i.
-// Decoding.  A 256-entry table at LDS offset 0 maps a code byte to the pair
+// Workgroup: 512 threads = 4 x 2 waves (two waves per SIMD, so one wave's
+// matrix-core work overlaps the other's LDS and decode work), tile BM x BN,
+// K step 64, wave tile (BM/4) x (BN/2).  Both operands are staged through
+// double-buffered LDS; the next K step's global loads are in flight while the
+// matrix cores work on the current buffers.  Within a K step, lane group
+// g = lane/32 owns k in [32g, 32g+32) and MFMA kk takes k = 32g + 8kk + 0..7
+// (the contraction may visit k in any order as long as A and B agree).
+//  A operand (X or dY, k-contiguous): tile [m][k] (row stride 72), loaded with
+//   16-byte loads, 8 lanes per 128-byte row.
+//  B operand is decoded into LDS:
+//   Every thread decodes one unit of BN/8 consecutive weights of one codes row
+//   per K step (16 or 32: inside one 64-weight block, so one scale per unit).
+//   forward: tile [n][k] (row stride 72), units along k of codes row n;
+//    fragments are 16-byte LDS reads.
+//   dX: tile [k][n] (row stride BN + 16); codes are contiguous along n (h),
+//    units run along n of one row k; fragments
+//    (8 consecutive k of one n) come from two transposing LDS reads
+//    (ds_read_b64_tr_b16).  In each 16-lane group that instruction returns to
+//    lane i element i%4 of the 8-byte chunks named by lanes i/4, 4+i/4, 8+i/4,
+//    12+i/4; lane 4j+q names row k0+j, column n0+4q, so lane i receives rows
+//    k0..k0+3 of column n0+i.
+// Decoding: a 256-entry table at LDS offset 0 maps a code byte to the pair
 //  (level[high nibble], level[low nibble]); one shifted byte gives the table
 //  address, one 8-byte LDS read gives both levels, two multiplies by a_hat and
 //  one packed convert give the two bf16 weights.
-// Loads.  All global reads are raw buffer loads with per-tile descriptors:
-//  rows past the end of a matrix read as zero, so there are no branches and
-//  no 64-bit address arithmetic in the K loop.
-// LoRA.  The rank-r term s·(X·L1)·L2 (forward) or s·(dY·L2^T)·L1^T (dX) is
-//  added by extra K steps over (A2, B2) on the same accumulators.
+// Loads: raw buffer loads with per-tile descriptors — rows past the end of a
+//  matrix read as zero, so the K loop has no branches and no 64-bit address
+//  arithmetic.
+// LoRA: the rank-r term s·(X·L1)·L2 (forward) or s·(dY·L2^T)·L1^T (dX) is added
+//  by extra K steps over (A2, B2) on the same accumulators.
 
 #include "gemm.h"
 
@@ -61,29 +71,35 @@ QL_DEV u32x4 tr_pair(const uint16_t *lo, const uint16_t *hi) {
 }
 QL_DEV uint16_t to_bf16(float v) { return (uint16_t)(pack_bf16x2(v, 0.0f) & 0xFFFFu); }
 
+constexpr int cmax(int a, int b) { return a > b ? a : b; }
+
 }  // namespace
 
 template <int BM, int BN, bool TRANS>
-__global__ __launch_bounds__(256) void nf4_gemm_kernel(GemmParams p) {
-  constexpr int BK = 64;
-  constexpr int LDA = BK + 8;    // A [m][k]
+__global__ __launch_bounds__(512) void nf4_gemm_kernel(GemmParams p) {
+  constexpr int NT = 512, BK = 64;
+  constexpr int WTM = BM / 4, WTN = BN / 2, TM = WTM / 32, TN = WTN / 32;
+  constexpr int LDA = BK + 8;     // A [m][k]
   constexpr int LDNK = BK + 8;   // B [n][k]
   constexpr int LDKN = BN + 16;  // B [k][n]
-  constexpr int B_ELEMS = (BN * LDNK > BK * LDKN) ? BN * LDNK : BK * LDKN;
-  constexpr int STAGE = BM * LDA + B_ELEMS;
-  constexpr int WTM = BM / 2, WTN = BN / 2, TM = WTM / 32, TN = WTN / 32;
-  constexpr int A_CH = BM * 8 / 256;   // 16-byte A chunks per thread per K step
-  constexpr int WU = BN / 128;         // 32-weight units per thread per K step
-  constexpr int B2_CH = BN * 8 / 256;  // 16-byte LoRA-B chunks per thread
+  constexpr int B_ELEMS = cmax(BN * LDNK, BK * LDKN);
+  constexpr int STAGE = BM * LDA + B_ELEMS;  // elements per LDS stage (A then B)
+  constexpr int UW = 64 * BN / NT;  // weights per decode unit: every thread decodes one unit
+  constexpr int UB = UW / 2;        // code bytes per unit (8 or 16)
+  constexpr int A_CH = BM * 8 / NT;  // 16-byte A chunks per thread per K step
   constexpr int LUT_BYTES = 256 * 8;
-  static_assert(2 * STAGE >= BM * (BN + 8), "epilogue staging must fit");
-  __shared__ __attribute__((aligned(16))) char lds[LUT_BYTES + 2 * STAGE * 2];
+  constexpr int LDC = BN + 8;
+  constexpr int LDS_BYTES = cmax(LUT_BYTES + 2 * STAGE * 2, BM * LDC * 2);
+  static_assert(UW == 16 || UW == 32, "decode unit of 16 or 32 weights");
+  static_assert(A_CH >= 1, "A tile too small");
+  __shared__ __attribute__((aligned(16))) char lds[LDS_BYTES];
   const f32x2 *lut = reinterpret_cast<const f32x2 *>(lds);
-  uint16_t *smem = reinterpret_cast<uint16_t *>(lds + LUT_BYTES);
+  uint16_t *sm = reinterpret_cast<uint16_t *>(lds + LUT_BYTES);
+  uint16_t *bsm = sm + BM * LDA;  // B tile of stage 0 (stage 1 is STAGE elements further)
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
-  reinterpret_cast<f32x2 *>(lds)[tid] = f32x2{p.level[tid >> 4], p.level[tid & 15]};
+  if (tid < 256) reinterpret_cast<f32x2 *>(lds)[tid] = f32x2{p.level[tid >> 4], p.level[tid & 15]};
 
   int bid = blockIdx.x;
   const int ntiles = p.tiles_m * p.tiles_n;
@@ -94,34 +110,37 @@ __global__ __launch_bounds__(256) void nf4_gemm_kernel(GemmParams p) {
   const int64_t nrows = p.N - n0 < BN ? p.N - n0 : BN;
   const float mu = *p.mean;
   const int64_t bpr = p.ldw >> 6;  // 64-blocks per codes row
+  const int g = lane >> 5, l32 = lane & 31;
 
+  // ---- A tile: 16-byte chunks, 8 lanes per 128-byte row ----
   const auto rA = make_rsrc(p.A + m0 * p.lda, mrows * p.lda * 2);
-  const auto rS2 = make_rsrc(p.scale2, ((p.wrows * bpr + 255) >> 8) * 4);
-
-  // per-thread constant offsets
   int voffA[A_CH];
 #pragma unroll
   for (int c = 0; c < A_CH; ++c) {
-    const int chunk = tid + 256 * c;
+    const int chunk = tid + NT * c;
     voffA[c] = (int)(((chunk >> 3) * p.lda + (chunk & 7) * 8) * 2);
   }
-  int voffC[WU], voffQ[WU];
-  int64_t blk0[WU];
-#pragma unroll
-  for (int u = 0; u < WU; ++u) {
-    const int unit = tid + 256 * u;
-    if (!TRANS) {
-      const int row = unit >> 1, half = unit & 1;
-      voffC[u] = (int)(row * (p.ldw >> 1) + half * 16);
-      voffQ[u] = (int)(row * bpr);
-      blk0[u] = (n0 + row) * bpr;
-    } else {
-      const int krow = unit / (BN / 32), part = unit % (BN / 32);
-      voffC[u] = (int)(krow * (p.ldw >> 1) + part * 16);
-      voffQ[u] = (int)(krow * bpr + (part >> 1));
-      blk0[u] = krow * bpr + ((n0 + part * 32) >> 6);
-    }
+
+  // ---- B decode unit of this thread: UW consecutive weights of one codes row ----
+  int voffC = 0, voffQ = 0;
+  int64_t blk0 = 0;
+  uint16_t *bdst0;  // LDS destination of the unit (buffer 0)
+  if (!TRANS) {
+    constexpr int PER_ROW = 64 / UW;  // units per 64-weight block
+    const int row = tid / PER_ROW, part = tid % PER_ROW;
+    voffC = (int)(row * (p.ldw >> 1) + part * UB);
+    voffQ = (int)(row * bpr);
+    blk0 = (n0 + row) * bpr;
+    bdst0 = bsm + row * LDNK + part * UW;
+  } else {
+    constexpr int PER_ROW = BN / UW;  // units per tile row
+    const int krow = tid / PER_ROW, part = tid % PER_ROW;
+    voffC = (int)(krow * (p.ldw >> 1) + part * UB);
+    voffQ = (int)(krow * bpr + ((part * UW) >> 6));
+    blk0 = krow * bpr + ((n0 + part * UW) >> 6);
+    bdst0 = bsm + krow * LDKN + part * UW;
   }
+  const auto rS2 = make_rsrc(p.scale2, ((p.wrows * bpr + 255) >> 8) * 4);
   const auto rCf = make_rsrc(p.codes + n0 * (p.ldw >> 1), nrows * (p.ldw >> 1));
   const auto rQf = make_rsrc(p.qabsmax + n0 * bpr, nrows * bpr);
 
@@ -133,90 +152,73 @@ __global__ __launch_bounds__(256) void nf4_gemm_kernel(GemmParams p) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
 
-  auto As = [&](int buf) { return smem + buf * STAGE; };
-  auto Bs = [&](int buf) { return smem + buf * STAGE + BM * LDA; };
-
-  u32x4 ra[A_CH];
-  u32x4 rc[WU];
-  int8_t rq[WU];
-  float rs[WU];
-
-  auto load_tile = [&](int kt) {
+  auto load_a = [&](int kt, u32x4 (&ra)[A_CH]) {
 #pragma unroll
     for (int c = 0; c < A_CH; ++c) ra[c] = bload128(rA, voffA[c], kt * BK * 2);
-    if (!TRANS) {
+  };
+  auto store_a = [&](int buf, const u32x4 (&ra)[A_CH]) {
 #pragma unroll
-      for (int u = 0; u < WU; ++u) {
-        rc[u] = bload128(rCf, voffC[u], kt * 32);
-        rq[u] = bload_i8(rQf, voffQ[u], kt);
-        rs[u] = bload_f32(rS2, (int)(((blk0[u] + kt) >> 8) * 4), 0);
-      }
+    for (int c = 0; c < A_CH; ++c) {
+      const int chunk = tid + NT * c;
+      *reinterpret_cast<u32x4 *>(sm + buf * STAGE + (chunk >> 3) * LDA + (chunk & 7) * 8) = ra[c];
+    }
+  };
+  auto load_codes = [&](__amdgpu_buffer_rsrc_t r, int voff, int soff) -> u32x4 {
+    if (UB == 16) return bload128(r, voff, soff);
+    const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0);
+    return u32x4{v[0], v[1], 0u, 0u};
+  };
+  auto load_b = [&](int kt, u32x4 &rc, int8_t &rq, float &rs) {
+    if (!TRANS) {
+      rc = load_codes(rCf, voffC, kt * 32);
+      rq = bload_i8(rQf, voffQ, kt);
+      rs = bload_f32(rS2, (int)(((blk0 + kt) >> 8) * 4), 0);
     } else {
       const int64_t krow0 = (int64_t)kt * BK;
       const auto rC = make_rsrc(p.codes + krow0 * (p.ldw >> 1) + (n0 >> 1),
                                 (p.wrows - krow0) * (p.ldw >> 1) - (n0 >> 1));
       const auto rQ = make_rsrc(p.qabsmax + krow0 * bpr + (n0 >> 6), (p.wrows - krow0) * bpr - (n0 >> 6));
-#pragma unroll
-      for (int u = 0; u < WU; ++u) {
-        rc[u] = bload128(rC, voffC[u], 0);
-        rq[u] = bload_i8(rQ, voffQ[u], 0);
-        rs[u] = bload_f32(rS2, (int)(((blk0[u] + krow0 * bpr) >> 8) * 4), 0);
-      }
+      rc = load_codes(rC, voffC, 0);
+      rq = bload_i8(rQ, voffQ, 0);
+      rs = bload_f32(rS2, (int)(((blk0 + krow0 * bpr) >> 8) * 4), 0);
     }
   };
-
-  auto store_tile = [&](int buf) {
-    uint16_t *as = As(buf);
-    uint16_t *bs = Bs(buf);
+  auto decode_b = [&](int buf, const u32x4 &rc, int8_t rq, float rs) {
+    const float ah = scale_hat(rq, rs, mu);
+    uint32_t o[UB];
 #pragma unroll
-    for (int c = 0; c < A_CH; ++c) {
-      const int chunk = tid + 256 * c;
-      *reinterpret_cast<u32x4 *>(as + (chunk >> 3) * LDA + (chunk & 7) * 8) = ra[c];
-    }
+    for (int d = 0; d < UB / 4; ++d)
 #pragma unroll
-    for (int u = 0; u < WU; ++u) {
-      const int unit = tid + 256 * u;
-      const float ah = scale_hat(rq[u], rs[u], mu);
-      uint32_t o[16];
-#pragma unroll
-      for (int d = 0; d < 4; ++d)
-#pragma unroll
-        for (int b = 0; b < 4; ++b) {
-          const f32x2 l = lut[(rc[u][d] >> (8 * b)) & 0xFF];
-          o[4 * d + b] = pack_bf16x2(l[0] * ah, l[1] * ah);
-        }
-      uint16_t *dst;
-      if (!TRANS) {
-        dst = bs + (unit >> 1) * LDNK + (unit & 1) * 32;
-      } else {
-        dst = bs + (unit / (BN / 32)) * LDKN + (unit % (BN / 32)) * 32;
+      for (int b = 0; b < 4; ++b) {
+        const f32x2 l = lut[(rc[d] >> (8 * b)) & 0xFF];
+        o[4 * d + b] = pack_bf16x2(l[0] * ah, l[1] * ah);
       }
+    u32x4 *dst = reinterpret_cast<u32x4 *>(bdst0 + buf * STAGE);
 #pragma unroll
-      for (int q = 0; q < 4; ++q)
-        reinterpret_cast<u32x4 *>(dst)[q] = u32x4{o[4 * q], o[4 * q + 1], o[4 * q + 2], o[4 * q + 3]};
+    for (int q = 0; q < UB / 4; ++q) dst[q] = u32x4{o[4 * q], o[4 * q + 1], o[4 * q + 2], o[4 * q + 3]};
+  };
+  // B fragments of MFMA step kk from an LDS tile; kn: tile is [k][n] (transposing reads)
+  auto load_bfrag = [&](const uint16_t *bs, bool kn, int kk, u32x4 (&bf)[TN]) {
+    if (!kn) {
+      const uint16_t *b0 = bs + (wn * WTN + l32) * LDNK + 32 * g + 8 * kk;
+#pragma unroll
+      for (int j = 0; j < TN; ++j) bf[j] = *reinterpret_cast<const u32x4 *>(b0 + j * 32 * LDNK);
+    } else {
+      const int c = lane & 15;
+      const uint16_t *b0 = bs + (32 * g + 8 * kk + (c >> 2)) * LDKN + wn * WTN + ((lane >> 4) & 1) * 16 + (c & 3) * 4;
+#pragma unroll
+      for (int j = 0; j < TN; ++j) bf[j] = tr_pair(b0 + j * 32, b0 + 4 * LDKN + j * 32);
     }
   };
-
-  // kn = true: B tile is [k][n] (transposing reads); false: [n][k] (plain 16-byte reads)
-  auto compute = [&](int buf, bool kn) {
-    const uint16_t *as = As(buf) + (wm * WTM + (lane & 31)) * LDA + (lane >> 5) * 8;
-    const uint16_t *bsb = Bs(buf);
+  auto mma_step = [&](int buf, bool kn) {
+    const uint16_t *as = sm + buf * STAGE + (wm * WTM + l32) * LDA + 32 * g;
+    const uint16_t *bs = bsm + buf * STAGE;
 #pragma unroll
-    for (int kk = 0; kk < BK / 16; ++kk) {
+    for (int kk = 0; kk < 4; ++kk) {
       u32x4 af[TM], bf[TN];
 #pragma unroll
-      for (int i = 0; i < TM; ++i) af[i] = *reinterpret_cast<const u32x4 *>(as + i * 32 * LDA + kk * 16);
-      if (!kn) {
-        const uint16_t *bs = bsb + (wn * WTN + (lane & 31)) * LDNK + (lane >> 5) * 8 + kk * 16;
-#pragma unroll
-        for (int j = 0; j < TN; ++j) bf[j] = *reinterpret_cast<const u32x4 *>(bs + j * 32 * LDNK);
-      } else {
-        const int c = lane & 15;
-        const int kb = kk * 16 + (lane >> 5) * 8 + (c >> 2);
-        const uint16_t *bs = bsb + kb * LDKN + wn * WTN + ((lane >> 4) & 1) * 16 + (c & 3) * 4;
-#pragma unroll
-        for (int j = 0; j < TN; ++j) bf[j] = tr_pair(bs + j * 32, bs + 4 * LDKN + j * 32);
-      }
+      for (int i = 0; i < TM; ++i) af[i] = *reinterpret_cast<const u32x4 *>(as + i * 32 * LDA + 8 * kk);
+      load_bfrag(bs, kn, kk, bf);
 #pragma unroll
       for (int i = 0; i < TM; ++i)
 #pragma unroll
@@ -224,15 +226,41 @@ __global__ __launch_bounds__(256) void nf4_gemm_kernel(GemmParams p) {
     }
   };
 
+  u32x4 ra[A_CH];
+  u32x4 rc = {0, 0, 0, 0};
+  int8_t rq = 0;
+  float rs = 0.0f;
+
   __syncthreads();  // decode table ready
-  load_tile(0);
-  store_tile(0);
+  load_a(0, ra);
+  load_b(0, rc, rq, rs);
+  store_a(0, ra);
+  decode_b(0, rc, rq, rs);
   __syncthreads();
-  for (int kt = 0; kt < p.ksteps; ++kt) {
-    const bool more = kt + 1 < p.ksteps;
-    if (more) load_tile(kt + 1);
-    compute(kt & 1, TRANS);
-    if (more) store_tile((kt + 1) & 1);
+  const int nk = p.ksteps;
+  for (int kt = 0; kt < nk; kt += 2) {
+    // even step: compute on buffer 0 while step kt+1 loads into registers, then into buffer 1
+    if (kt + 1 < nk) {
+      load_a(kt + 1, ra);
+      load_b(kt + 1, rc, rq, rs);
+    }
+    mma_step(0, TRANS);
+    if (kt + 1 < nk) {
+      store_a(1, ra);
+      decode_b(1, rc, rq, rs);
+    }
+    __syncthreads();
+    if (kt + 1 >= nk) break;
+    // odd step
+    if (kt + 2 < nk) {
+      load_a(kt + 2, ra);
+      load_b(kt + 2, rc, rq, rs);
+    }
+    mma_step(1, TRANS);
+    if (kt + 2 < nk) {
+      store_a(0, ra);
+      decode_b(0, rc, rq, rs);
+    }
     __syncthreads();
   }
 
@@ -243,48 +271,43 @@ __global__ __launch_bounds__(256) void nf4_gemm_kernel(GemmParams p) {
     const auto rB2 = TRANS ? make_rsrc(p.B2 + n0 * p.ldb2, nrows * p.ldb2 * 2)
                            : make_rsrc(p.B2 + n0, ((int64_t)p.b2rows * p.ldb2 - n0) * 2);
     for (int k2 = 0; k2 < p.ksteps2; ++k2) {
-      uint16_t *as = As(0);
-      uint16_t *bs = Bs(0);
 #pragma unroll
       for (int c = 0; c < A_CH; ++c) {
-        const int chunk = tid + 256 * c, row = chunk >> 3, col8 = chunk & 7;
-        *reinterpret_cast<u32x4 *>(as + row * LDA + col8 * 8) =
+        const int chunk = tid + NT * c, row = chunk >> 3, col8 = chunk & 7;
+        *reinterpret_cast<u32x4 *>(sm + row * LDA + col8 * 8) =
             bload128(rA2, (int)((row * p.lda2 + col8 * 8) * 2), k2 * BK * 2);
       }
-#pragma unroll
-      for (int c = 0; c < B2_CH; ++c) {
-        const int chunk = tid + 256 * c;
+      for (int chunk = tid; chunk < BN * 8; chunk += NT) {
         if (TRANS) {  // [n][k] tile: BN rows of 8 chunks
           const int row = chunk >> 3, col8 = chunk & 7;
-          *reinterpret_cast<u32x4 *>(bs + row * LDNK + col8 * 8) =
+          *reinterpret_cast<u32x4 *>(bsm + row * LDNK + col8 * 8) =
               bload128(rB2, (int)((row * p.ldb2 + col8 * 8) * 2), k2 * BK * 2);
         } else {  // [k][n] tile: 64 rows of BN/8 chunks
           const int krow = chunk / (BN / 8), col8 = chunk % (BN / 8);
-          *reinterpret_cast<u32x4 *>(bs + krow * LDKN + col8 * 8) =
+          *reinterpret_cast<u32x4 *>(bsm + krow * LDKN + col8 * 8) =
               bload128(rB2, (int)(((int64_t)(k2 * BK + krow) * p.ldb2 + col8 * 8) * 2), 0);
         }
       }
       __syncthreads();
-      compute(0, !TRANS);
+      mma_step(0, !TRANS);
       __syncthreads();
     }
   }
 
   // Epilogue: fp32 -> bf16 through LDS, then coalesced 16-byte stores.
-  constexpr int LDC = BN + 8;
-  uint16_t *cs = smem;
+  uint16_t *cs = reinterpret_cast<uint16_t *>(lds);
 #pragma unroll
   for (int i = 0; i < TM; ++i)
 #pragma unroll
     for (int j = 0; j < TN; ++j)
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        const int row = wm * WTM + 32 * i + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-        const int col = wn * WTN + 32 * j + (lane & 31);
+        const int row = wm * WTM + 32 * i + 8 * (v >> 2) + 4 * g + (v & 3);
+        const int col = wn * WTN + 32 * j + l32;
         cs[row * LDC + col] = to_bf16(acc[i][j][v]);
       }
   __syncthreads();
-  for (int chunk = tid; chunk < BM * BN / 8; chunk += 256) {
+  for (int chunk = tid; chunk < BM * BN / 8; chunk += NT) {
     const int row = chunk / (BN / 8), c8 = chunk % (BN / 8);
     const int64_t m = m0 + row, n = n0 + c8 * 8;
     if (m < p.M && n < p.N)
@@ -300,7 +323,7 @@ template <int BM, int BN, bool TRANS>
 void gemm_launch(GemmParams &gp, hipStream_t st) {
   gp.tiles_m = (int)cdiv(gp.M, BM);
   gp.tiles_n = (int)cdiv(gp.N, BN);
-  nf4_gemm_kernel<BM, BN, TRANS><<<gp.tiles_m * gp.tiles_n, 256, 0, st>>>(gp);
+  nf4_gemm_kernel<BM, BN, TRANS><<<gp.tiles_m * gp.tiles_n, 512, 0, st>>>(gp);
 }
 
 template <bool TRANS>
@@ -308,7 +331,7 @@ void gemm_select(GemmParams &gp, hipStream_t st) {
   const int64_t t256 = cdiv(gp.M, 256) * cdiv(gp.N, 256);
   const int64_t t256x128 = cdiv(gp.M, 256) * cdiv(gp.N, 128);
   if (gp.M >= 256 && t256 >= 240) gemm_launch<256, 256, TRANS>(gp, st);
-  else if (gp.M >= 256 && t256x128 >= 200) gemm_launch<256, 128, TRANS>(gp, st);
+  else if (gp.M >= 192 && t256x128 >= 160) gemm_launch<256, 128, TRANS>(gp, st);
   else gemm_launch<128, 128, TRANS>(gp, st);
 }
 

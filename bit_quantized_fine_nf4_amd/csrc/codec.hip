@@ -89,10 +89,7 @@ __global__ __launch_bounds__(256) void quantize_kernel(const void *__restrict__ 
   const int64_t nwaves = (int64_t)gridDim.x * (blockDim.x / 64);
   const int64_t ncodes = (n + 1) >> 1;
 
-  for (int64_t base = wave * 512; base < n; base += nwaves * 512) {
-    const int64_t e0 = base + lane * 8;
-    float v[8];
-    load8<kBf16>(w, e0, n, v);
+  auto encode = [&](const float (&v)[8], int64_t e0) {
     float m = fmaxf(fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3]))),
                     fmaxf(fmaxf(fabsf(v[4]), fabsf(v[5])), fmaxf(fabsf(v[6]), fabsf(v[7]))));
     const float a = dpp_max8(m);
@@ -132,6 +129,17 @@ __global__ __launch_bounds__(256) void quantize_kernel(const void *__restrict__ 
         if (c0 + b < ncodes) codes[c0 + b] = (uint8_t)(word >> (8 * b));
     }
     if ((lane & 7) == 0 && e0 < n) absmax[e0 >> 6] = a;
+  };
+
+  // Two 512-weight chunks per wave iteration, both loads issued before either is encoded.
+  const int64_t stride = nwaves * 512;
+  for (int64_t base = wave * 512; base < n; base += 2 * stride) {
+    const int64_t e0 = base + lane * 8, e1 = base + stride + lane * 8;
+    float v0[8], v1[8];
+    load8<kBf16>(w, e0, n, v0);
+    load8<kBf16>(w, e1, n, v1);
+    encode(v0, e0);
+    if (base + stride < n) encode(v1, e1);
   }
 }
 
@@ -142,7 +150,7 @@ __global__ __launch_bounds__(256) void quantize_kernel(const void *__restrict__ 
 // The mean of the block scales is computed exactly: every float32 is an
 // integer multiple of 2^-149, so the sum is an integer that the kernels
 // accumulate without rounding, binned by exponent, and the one rounding
-// happens at the very end (dq_mean_finish).  Each lane keeps a private 64-bit
+// happens at the very end (mean_from_bins, run by the last workgroup).  Each lane keeps a private 64-bit
 // accumulator for an 8-exponent window anchored at its first value; a value
 // outside the window goes straight to its exponent bin.  Bins live in LDS per
 // workgroup and are flushed to a global array of uint64 bins with atomics.
@@ -150,6 +158,7 @@ __global__ __launch_bounds__(256) void quantize_kernel(const void *__restrict__ 
 // ---------------------------------------------------------------------------
 
 constexpr int kNumBins = 264;  // bin s holds integers in units of 2^(s-149)
+constexpr int kLimbs = 12;     // the exact sum is below 2^(64+263): 11 32-bit limbs suffice
 
 __global__ void zero_u64_kernel(unsigned long long *p, int n) {
   int i = blockIdx.x * blockDim.x + threadIdx.x;
@@ -163,9 +172,89 @@ QL_DEV void split_f32(float a, uint32_t &mant, int &shift) {
   shift = e ? (int)e - 1 : 0;  // value = mant * 2^(shift - 149)
 }
 
+// mean = RNE_f32(S / nb) with S = sum_s bins[s] * 2^(s-149), computed by one workgroup.
+QL_DEV void mean_from_bins(const unsigned long long *b /* LDS, kNumBins */, int64_t nb, float *mean_out) {
+  __shared__ unsigned long long csum[kLimbs];
+  const int tid = threadIdx.x;
+  if (tid < kLimbs) {
+    // limb tid collects the bits of every bins[s] << s that fall in [32*tid, 32*tid + 32)
+    const int j = tid;
+    unsigned long long c = 0;
+    const int s_lo = 32 * j - 63 > 0 ? 32 * j - 63 : 0;
+    const int s_hi = 32 * j + 31 < kNumBins - 1 ? 32 * j + 31 : kNumBins - 1;
+    for (int sidx = s_lo; sidx <= s_hi; ++sidx) {
+      const unsigned long long v = b[sidx];
+      const int sh = sidx - 32 * j;
+      c += (uint32_t)(sh >= 0 ? (v << sh) : (v >> -sh));
+    }
+    csum[j] = c;
+  }
+  __syncthreads();
+  if (tid != 0) return;
+  uint32_t S[kLimbs];
+  unsigned long long carry = 0;
+  for (int j = 0; j < kLimbs; ++j) {
+    const unsigned long long t = csum[j] + carry;
+    S[j] = (uint32_t)t;
+    carry = t >> 32;
+  }
+  int top = kLimbs - 1;
+  while (top >= 0 && S[top] == 0) --top;
+  if (top < 0) { *mean_out = 0.0f; return; }
+  const int bitsS = 32 * top + 32 - __builtin_clz(S[top]);
+  // W = S >> e keeps the top 96 bits; sticky0 records whether anything below was dropped
+  const int e = bitsS > 96 ? bitsS - 96 : 0;
+  const int q = e >> 5, r = e & 31;
+  uint32_t W[3];
+  for (int k = 0; k < 3; ++k) {
+    const uint32_t lo = (k + q < kLimbs) ? S[k + q] : 0u;
+    const uint32_t hi = (k + q + 1 < kLimbs) ? S[k + q + 1] : 0u;
+    W[k] = r ? ((lo >> r) | (hi << (32 - r))) : lo;
+  }
+  bool sticky0 = r ? (S[q] & ((1u << r) - 1u)) != 0u : false;
+  for (int k = 0; k < q; ++k) sticky0 = sticky0 || S[k] != 0u;
+  // Q = W / nb, rem = W % nb (96-bit by 32-bit long division)
+  const uint32_t den = (uint32_t)nb;
+  uint32_t Q[3];
+  unsigned long long rem = 0;
+  for (int k = 2; k >= 0; --k) {
+    const unsigned long long cur = (rem << 32) | W[k];
+    Q[k] = (uint32_t)(cur / den);
+    rem = cur % den;
+  }
+  const unsigned __int128 Qv = ((unsigned __int128)Q[2] << 64) | ((unsigned __int128)Q[1] << 32) | Q[0];
+  int bitsQ = 0;
+  for (int k = 2; k >= 0; --k)
+    if (Q[k]) { bitsQ = 32 * k + 32 - __builtin_clz(Q[k]); break; }
+  if (bitsQ == 0) {  // S/nb < 2^-149 * 1: rounds to 0 or the smallest denormal
+    const bool up = 2 * rem > den || (2 * rem == den && sticky0);
+    *mean_out = up ? ldexpf(1.0f, -149) : 0.0f;
+    return;
+  }
+  // value = (Q + frac) * 2^(e - 149); leading bit exponent E, float32 quantum 2^qe
+  const int E = bitsQ - 1 + e - 149;
+  const int qe = E - 23 > -149 ? E - 23 : -149;
+  const int drop = qe - (e - 149);  // >= 0: bits of Q below the quantum
+  unsigned long long mant = (unsigned long long)(Qv >> drop);
+  bool up;
+  if (drop == 0) {  // only when e == 0, so nothing below the remainder
+    up = 2 * rem > den || (2 * rem == den && (mant & 1ull));
+  } else {
+    const bool half = (Qv >> (drop - 1)) & 1;
+    const bool lower = (drop > 1 && (Qv & (((unsigned __int128)1 << (drop - 1)) - 1)) != 0) || rem != 0 || sticky0;
+    up = half && (lower || (mant & 1ull));
+  }
+  if (up) ++mant;
+  *mean_out = ldexpf((float)mant, qe);
+}
+
+// Exact sum of the block scales into exponent bins; the last workgroup to finish turns
+// the bins into the rounded mean.  gbins[kNumBins] doubles as the completion counter.
 __global__ __launch_bounds__(256) void dq_bins_kernel(const float *__restrict__ absmax, int64_t nb,
-                                                      unsigned long long *__restrict__ gbins) {
+                                                      unsigned long long *__restrict__ gbins,
+                                                      float *__restrict__ mean_out) {
   __shared__ unsigned long long bins[kNumBins];
+  __shared__ bool last;
   for (int i = threadIdx.x; i < kNumBins; i += blockDim.x) bins[i] = 0ull;
   __syncthreads();
 
@@ -173,93 +262,46 @@ __global__ __launch_bounds__(256) void dq_bins_kernel(const float *__restrict__ 
   const int64_t nthr = (int64_t)gridDim.x * blockDim.x;
   int anchor = -1;
   unsigned long long acc = 0ull;
-  for (int64_t i = tid; i < nb; i += nthr) {
+  auto add = [&](float a) {
+    if (a == 0.0f) return;  // contributes nothing; keeps padding from anchoring the window
     uint32_t m;
-    int s;
-    split_f32(absmax[i], m, s);
-    if (anchor < 0) anchor = s > 3 ? s - 3 : 0;
-    const int d = s - anchor;
+    int sh;
+    split_f32(a, m, sh);
+    if (anchor < 0) anchor = sh > 3 ? sh - 3 : 0;
+    const int d = sh - anchor;
     if (d >= 0 && d < 8) {
       acc += (unsigned long long)(m << d);
     } else {
-      atomicAdd(&bins[s], (unsigned long long)m);
+      atomicAdd(&bins[sh], (unsigned long long)m);
     }
+  };
+  // 16-byte loads, four in flight per thread
+  const int64_t nvec = nb >> 2;
+  const f32x4 *v4 = reinterpret_cast<const f32x4 *>(absmax);
+  for (int64_t i = tid; i < nvec; i += 4 * nthr) {
+    f32x4 x[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) x[u] = (i + u * nthr < nvec) ? v4[i + u * nthr] : f32x4{0, 0, 0, 0};
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int k = 0; k < 4; ++k) add(x[u][k]);  // zero padding adds nothing
   }
+  for (int64_t i = (nvec << 2) + tid; i < nb; i += nthr) add(absmax[i]);
   if (anchor >= 0 && acc) atomicAdd(&bins[anchor], acc);
   __syncthreads();
   for (int i = threadIdx.x; i < kNumBins; i += blockDim.x)
     if (bins[i]) atomicAdd(&gbins[i], bins[i]);
-}
-
-// One thread: mean = RNE_f32( (sum_s bins[s] * 2^(s-149)) / nb ).
-__global__ void dq_mean_finish_kernel(const unsigned long long *__restrict__ gbins, int64_t nb,
-                                      float *__restrict__ mean_out) {
-  if (threadIdx.x != 0 || blockIdx.x != 0) return;
-  // S in units of 2^-149 as little-endian 32-bit limbs; S < 2^32 * 2^31 * 2^263 < 2^326.
-  constexpr int NL = 14;
-  uint32_t S[NL];
-  for (int i = 0; i < NL; ++i) S[i] = 0;
-  for (int s = 0; s < kNumBins; ++s) {
-    unsigned long long v = gbins[s];
-    if (!v) continue;
-    int limb = s >> 5, sh = s & 31;
-    // add v << sh (up to 96 bits) at limb
-    unsigned long long lo = (v << sh) & 0xFFFFFFFFull;
-    unsigned long long mid = (sh ? (v >> (32 - sh)) : (v >> 32)) & 0xFFFFFFFFull;
-    unsigned long long hi = sh ? (v >> (64 - sh)) : 0ull;
-    unsigned long long carry = 0;
-    unsigned long long parts[3] = {lo, mid, hi};
-    for (int k = 0; limb + k < NL; ++k) {
-      unsigned long long add = (k < 3 ? parts[k] : 0ull) + carry;
-      if (k >= 3 && add == 0) break;
-      unsigned long long t = (unsigned long long)S[limb + k] + add;
-      S[limb + k] = (uint32_t)t;
-      carry = t >> 32;
-    }
-  }
-  int top = NL - 1;
-  while (top >= 0 && S[top] == 0) --top;
-  if (top < 0) { *mean_out = 0.0f; return; }
-  const int bitsS = top * 32 + (32 - __builtin_clz(S[top]));
-  const uint32_t den = (uint32_t)nb;
-  const int bitsD = 32 - __builtin_clz(den);
-  // scale S by 2^k so the quotient has at least 27 bits
-  int k = 27 + bitsD - bitsS;
-  if (k < 0) k = 0;
-  uint32_t X[NL + 3];
-  for (int i = 0; i < NL + 3; ++i) X[i] = 0;
-  {
-    const int limb = k >> 5, sh = k & 31;
-    for (int i = 0; i < NL; ++i) {
-      unsigned long long v = (unsigned long long)S[i] << sh;
-      if (i + limb < NL + 3) X[i + limb] |= (uint32_t)v;
-      if (i + limb + 1 < NL + 3) X[i + limb + 1] |= (uint32_t)(v >> 32);
-    }
-  }
-  // long division X / den
-  uint32_t Q[NL + 3];
-  unsigned long long rem = 0;
-  for (int i = NL + 2; i >= 0; --i) {
-    unsigned long long cur = (rem << 32) | X[i];
-    Q[i] = (uint32_t)(cur / den);
-    rem = cur % den;
-  }
-  int qt = NL + 2;
-  while (qt > 0 && Q[qt] == 0) --qt;
-  const int bitsQ = qt * 32 + (32 - __builtin_clz(Q[qt]));
-  // value = Q * 2^(-k-149) (+ fraction rem/den); exponent E with 2^E <= value
-  const int E = bitsQ - 1 - k - 149;
-  int qe = E - 23;
-  if (qe < -149) qe = -149;
-  const int drop = qe + k + 149;  // bits of Q below the float32 quantum (>= 3 by choice of k)
-  auto bit = [&](int p) -> uint32_t { return (p < 0) ? 0u : ((Q[p >> 5] >> (p & 31)) & 1u); };
-  unsigned long long mant = 0;
-  for (int p = bitsQ - 1; p >= drop; --p) mant = (mant << 1) | bit(p);
-  const uint32_t half = bit(drop - 1);
-  bool sticky = rem != 0;
-  for (int p = drop - 2; p >= 0 && !sticky; --p) sticky = bit(p) != 0;
-  if (half && (sticky || (mant & 1ull))) ++mant;
-  *mean_out = ldexpf((float)mant, qe);
+  __threadfence();
+  __syncthreads();
+  if (threadIdx.x == 0) last = atomicAdd(&gbins[kNumBins], 1ull) == (unsigned long long)(gridDim.x - 1);
+  __syncthreads();
+  if (!last) return;
+  __threadfence();
+  for (int i = threadIdx.x; i < kNumBins; i += blockDim.x)
+    bins[i] = __hip_atomic_load(&gbins[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __syncthreads();
+  mean_from_bins(bins, nb, mean_out);
 }
 
 // One wave per chunk of 256 scales: c = fp32(a - mean); s2 = fp32(max|c| / 127);
@@ -309,12 +351,45 @@ __global__ __launch_bounds__(256) void dq_chunks_kernel(const float *__restrict_
 
 // ---------------------------------------------------------------------------
 // Dequantization ([MC] "1. NormalFloat": dequantize to BF16 before the
-// matmul; [GO] "The core move").  Each lane turns 16 bytes of codes (32
-// weights, all in one 64-block) into 32 float32 or bf16 values.  The 16
-// levels sit in LDS at a 16-byte stride, so the high nibble of a byte,
-// masked in place, is already its table offset; different codes hit
-// different banks and equal codes broadcast.
+// matmul; [GO] "The core move").  A unit is one 32-bit word of codes = 8
+// weights (inside one 64-block, so one a_hat).  Consecutive lanes take
+// consecutive units, so each wave's code loads read 256 contiguous bytes and
+// its 16-byte bf16 stores (or pairs of 16-byte float32 stores) write
+// contiguous memory.  Each thread handles kDeqUnroll units per pass with all
+// loads issued first.  A 256-entry LDS table at offset 0 maps a code byte to
+// (level[high nibble], level[low nibble]): one shifted byte is the address and
+// one 8-byte read returns both levels.
 // ---------------------------------------------------------------------------
+
+constexpr int kDeqUnroll = 8;
+
+template <bool kOutBf16>
+QL_DEV void dequant_unit(const f32x2 *lut, uint32_t cw, float ah, int64_t e0, int64_t n, void *__restrict__ out) {
+  float wv[8];
+#pragma unroll
+  for (int b = 0; b < 4; ++b) {
+    const f32x2 l = lut[(cw >> (8 * b)) & 0xFF];
+    wv[2 * b] = l[0] * ah;
+    wv[2 * b + 1] = l[1] * ah;
+  }
+  if (e0 + 8 <= n) {
+    if (kOutBf16) {
+      *reinterpret_cast<u32x4 *>(reinterpret_cast<uint16_t *>(out) + e0) =
+          u32x4{pack_bf16x2(wv[0], wv[1]), pack_bf16x2(wv[2], wv[3]), pack_bf16x2(wv[4], wv[5]),
+                pack_bf16x2(wv[6], wv[7])};
+    } else {
+      f32x4 *o = reinterpret_cast<f32x4 *>(reinterpret_cast<float *>(out) + e0);
+      o[0] = f32x4{wv[0], wv[1], wv[2], wv[3]};
+      o[1] = f32x4{wv[4], wv[5], wv[6], wv[7]};
+    }
+  } else {
+    for (int i = 0; i < 8; ++i) {
+      if (e0 + i >= n) break;
+      if (kOutBf16) reinterpret_cast<uint16_t *>(out)[e0 + i] = (uint16_t)(pack_bf16x2(wv[i], 0.0f) & 0xFFFF);
+      else reinterpret_cast<float *>(out)[e0 + i] = wv[i];
+    }
+  }
+}
 
 template <bool kOutBf16>
 __global__ __launch_bounds__(256) void dequantize_kernel(const uint8_t *__restrict__ codes,
@@ -322,61 +397,43 @@ __global__ __launch_bounds__(256) void dequantize_kernel(const uint8_t *__restri
                                                          const float *__restrict__ scale2,
                                                          const float *__restrict__ mean_in, int64_t n,
                                                          void *__restrict__ out, Nf4Tables tab) {
-  __shared__ float lut[16 * 4];
-  if (threadIdx.x < 64) lut[threadIdx.x] = tab.level[threadIdx.x >> 2];
+  __shared__ f32x2 lut[256];
+  lut[threadIdx.x] = f32x2{tab.level[threadIdx.x >> 4], tab.level[threadIdx.x & 15]};
   __syncthreads();
   const float mu = *mean_in;
-  const int64_t ngroups = (n + 31) / 32;
-  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-  for (int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; g < ngroups; g += stride) {
-    const int64_t e0 = g * 32;
-    const int64_t blk = e0 >> 6;
-    const float ah = scale_hat(qabsmax[blk], scale2[blk / kChunk], mu);
-    u32x4 cw;
-    if (e0 + 32 <= n) {
-      cw = *reinterpret_cast<const u32x4 *>(codes + (e0 >> 1));
-    } else {
-      const int64_t nbytes = (n + 1) / 2;
-      uint32_t t[4] = {0x77777777u, 0x77777777u, 0x77777777u, 0x77777777u};
-      for (int b = 0; b < 16; ++b)
-        if ((e0 >> 1) + b < nbytes)
-          t[b >> 2] = (t[b >> 2] & ~(0xFFu << (8 * (b & 3)))) | ((uint32_t)codes[(e0 >> 1) + b] << (8 * (b & 3)));
-      cw = u32x4{t[0], t[1], t[2], t[3]};
-    }
-    float wv[32];
+  const int64_t nunits = (n + 7) / 8;
+  const int64_t nbytes = (n + 1) / 2;
+  const int64_t per_block = (int64_t)kDeqUnroll * blockDim.x;
+  for (int64_t base = (int64_t)blockIdx.x * per_block; base < nunits; base += (int64_t)gridDim.x * per_block) {
+    uint32_t cw[kDeqUnroll];
+    int8_t q[kDeqUnroll];
+    float s2[kDeqUnroll];
 #pragma unroll
-    for (int d = 0; d < 4; ++d) {
-      const uint32_t hi = cw[d] & 0xF0F0F0F0u;        // high nibbles * 16
-      const uint32_t lo = (cw[d] << 4) & 0xF0F0F0F0u; // low nibbles * 16
-#pragma unroll
-      for (int b = 0; b < 4; ++b) {
-        const float l_hi = *reinterpret_cast<const float *>(reinterpret_cast<const char *>(lut) + ((hi >> (8 * b)) & 0xFF));
-        const float l_lo = *reinterpret_cast<const float *>(reinterpret_cast<const char *>(lut) + ((lo >> (8 * b)) & 0xFF));
-        wv[8 * d + 2 * b] = l_hi * ah;
-        wv[8 * d + 2 * b + 1] = l_lo * ah;
-      }
-    }
-    if (e0 + 32 <= n) {
-      if (kOutBf16) {
-        u32x4 *o = reinterpret_cast<u32x4 *>(reinterpret_cast<uint16_t *>(out) + e0);
-#pragma unroll
-        for (int q = 0; q < 4; ++q)
-          o[q] = u32x4{pack_bf16x2(wv[8 * q], wv[8 * q + 1]), pack_bf16x2(wv[8 * q + 2], wv[8 * q + 3]),
-                       pack_bf16x2(wv[8 * q + 4], wv[8 * q + 5]), pack_bf16x2(wv[8 * q + 6], wv[8 * q + 7])};
-      } else {
-        f32x4 *o = reinterpret_cast<f32x4 *>(reinterpret_cast<float *>(out) + e0);
-#pragma unroll
-        for (int q = 0; q < 8; ++q) o[q] = f32x4{wv[4 * q], wv[4 * q + 1], wv[4 * q + 2], wv[4 * q + 3]};
-      }
-    } else {
-      for (int i = 0; i < 32; ++i) {
-        if (e0 + i >= n) break;
-        if (kOutBf16) {
-          reinterpret_cast<uint16_t *>(out)[e0 + i] = (uint16_t)(pack_bf16x2(wv[i], 0.0f) & 0xFFFF);
+    for (int u = 0; u < kDeqUnroll; ++u) {
+      const int64_t unit = base + u * blockDim.x + threadIdx.x;
+      const int64_t e0 = unit * 8;
+      cw[u] = 0x77777777u;
+      q[u] = 0;
+      s2[u] = 0.0f;
+      if (unit < nunits) {
+        const int64_t blk = e0 >> 6;
+        q[u] = qabsmax[blk];
+        s2[u] = scale2[blk / kChunk];
+        if (e0 + 8 <= n) {
+          cw[u] = *reinterpret_cast<const uint32_t *>(codes + (e0 >> 1));
         } else {
-          reinterpret_cast<float *>(out)[e0 + i] = wv[i];
+          uint32_t t = 0x77777777u;
+          for (int bb = 0; bb < 4; ++bb)
+            if ((e0 >> 1) + bb < nbytes)
+              t = (t & ~(0xFFu << (8 * bb))) | ((uint32_t)codes[(e0 >> 1) + bb] << (8 * bb));
+          cw[u] = t;
         }
       }
+    }
+#pragma unroll
+    for (int u = 0; u < kDeqUnroll; ++u) {
+      const int64_t unit = base + u * blockDim.x + threadIdx.x;
+      if (unit < nunits) dequant_unit<kOutBf16>(lut, cw[u], scale_hat(q[u], s2[u], mu), unit * 8, n, out);
     }
   }
 }
@@ -403,15 +460,14 @@ hipError_t launch_quantize(const void *w, bool bf16, int64_t n, uint8_t *codes, 
   return hipGetLastError();
 }
 
-size_t dq_workspace_bytes() { return ((size_t)kNumBins * 8 + 255) / 256 * 256; }
+size_t dq_workspace_bytes() { return ((size_t)(kNumBins + 1) * 8 + 255) / 256 * 256; }
 
 hipError_t launch_double_quant(const float *absmax, int64_t nb, int8_t *qabsmax, float *scale2,
                                float *mean, void *ws, hipStream_t st) {
   auto *bins = reinterpret_cast<unsigned long long *>(ws);
-  zero_u64_kernel<<<(kNumBins + 255) / 256, 256, 0, st>>>(bins, kNumBins);
-  const int grid = grid_for(nb, 256 * 16, 1024);
-  dq_bins_kernel<<<grid, 256, 0, st>>>(absmax, nb, bins);
-  dq_mean_finish_kernel<<<1, 64, 0, st>>>(bins, nb, mean);
+  zero_u64_kernel<<<(kNumBins + 1 + 255) / 256, 256, 0, st>>>(bins, kNumBins + 1);
+  const int grid = grid_for(nb, 256 * 16, 4096);
+  dq_bins_kernel<<<grid, 256, 0, st>>>(absmax, nb, bins, mean);
   const int64_t nch = (nb + kChunk - 1) / kChunk;
   dq_chunks_kernel<<<(int)((nch + 3) / 4), 256, 0, st>>>(absmax, nb, mean, qabsmax, scale2);
   return hipGetLastError();
@@ -420,7 +476,7 @@ hipError_t launch_double_quant(const float *absmax, int64_t nb, int8_t *qabsmax,
 hipError_t launch_dequantize(const uint8_t *codes, const int8_t *qabsmax, const float *scale2,
                              const float *mean, int64_t n, void *out, bool bf16, const Nf4Tables &tab,
                              hipStream_t st) {
-  const int grid = grid_for((n + 31) / 32, 256, 256 * 64);
+  const int grid = grid_for((n + 7) / 8, 256 * kDeqUnroll, 256 * 16);
   if (bf16)
     dequantize_kernel<true><<<grid, 256, 0, st>>>(codes, qabsmax, scale2, mean, n, out, tab);
   else

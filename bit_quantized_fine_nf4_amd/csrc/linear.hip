@@ -34,6 +34,9 @@ inline int64_t cdiv(int64_t x, int64_t m) { return (x + m - 1) / m; }
 
 QL_DEV bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
+QL_DEV f32x16 mfma32(u32x4 a, u32x4 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(b), c, 0, 0, 0);
+}
 QL_DEV f32x4 mfma16(u32x4 a, u32x4 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), as_bf16x8(b), c, 0, 0, 0);
 }
@@ -114,12 +117,17 @@ __global__ void skinny_finish_kernel(const float *__restrict__ part, int S, int6
 }
 
 // ---------------------------------------------------------------------------
-// Few-token forward (M <= 16).  Workgroup = 16 output rows; its 4 waves split
-// the K range and reduce through LDS.  Lane l decodes 8 bytes (16 codes) of
-// row n0 + l%16 per 64-block; a byte indexes a 256-entry LDS table holding
-// the bf16 pair (level[high nibble], level[low nibble]).  The bf16 levels go
-// through the matrix core against the tokens and the block scale a_hat is
-// applied to the float32 MFMA result of each 64-block.
+// Few-token forward (M <= 16): Y = X·W_hat (+ s·T·L2), bandwidth-bound on the
+// packed codes.  Matrix-core formulation with the weights as the B operand of
+// v_mfma_f32_32x32x16_bf16: lane l owns output row n = n0 + l%32 and lane group
+// g = l/32 owns k in [32g, 32g+32) of a 64-block, so one 16-byte code load per
+// lane per block feeds four MFMAs (MFMA j takes k = 32g + 8j + 0..7) that span
+// exactly one block.  The MFMAs see bf16(level[code]) (a 256-entry LDS table
+// maps a code byte to the bf16 pair of its two levels) and the block scale
+// a_hat is applied once to the float32 block partial.  Tokens are the MFMA
+// rows (rows >= M are zero; only the 16 lowest rows are kept).
+// Workgroup: 512 threads = 8 waves over 64 output rows (two 32-row groups that
+// share the token fragments); the waves split K and reduce through LDS.
 // ---------------------------------------------------------------------------
 struct GemvParams {
   const uint16_t *X;
@@ -139,53 +147,94 @@ struct GemvParams {
   float level[16];
 };
 
-__global__ __launch_bounds__(256) void nf4_gemv_kernel(GemvParams p) {
+constexpr int kGemvRows = 64, kGemvWaves = 8, kGemvUnroll = 4;
+
+__global__ __launch_bounds__(512) void nf4_gemv_kernel(GemvParams p) {
   __shared__ uint32_t lut2[256];
-  __shared__ float red[4][16][17];
+  __shared__ float red[kGemvWaves][2][16][33];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  lut2[tid] = pack_bf16x2(p.level[tid >> 4], p.level[tid & 15]);
+  if (tid < 256) lut2[tid] = pack_bf16x2(p.level[tid >> 4], p.level[tid & 15]);
   __syncthreads();
 
-  const int64_t n0 = (int64_t)blockIdx.x * 16;
-  const int g = lane >> 4, r16 = lane & 15;
-  const int64_t n = n0 + r16;
-  const int m = r16;
-  const bool mok = m < p.M;
+  const int64_t n0 = (int64_t)blockIdx.x * kGemvRows;
+  const int g = lane >> 5, l32 = lane & 31;
   const int64_t nblk = p.K >> 6;
-  const int64_t b0 = wave * nblk / 4, b1 = (wave + 1) * nblk / 4;
+  const int64_t b0 = wave * nblk / kGemvWaves, b1 = (wave + 1) * nblk / kGemvWaves;
   const float mu = *p.mean;
-  const uint8_t *crow = p.codes + n * (p.K >> 1) + 8 * g;
-  const int8_t *qrow = p.qabsmax + n * nblk;
-  const uint16_t *xrow = p.X + (int64_t)(mok ? m : 0) * p.ldx + 16 * g;
-  f32x4 acc = {0, 0, 0, 0};
-#pragma unroll 4
-  for (int64_t b = b0; b < b1; ++b) {
-    const u32x2 cw = *reinterpret_cast<const u32x2 *>(crow + b * 32);
-    const float ah = scale_hat(qrow[b], p.scale2[(n * nblk + b) >> 8], mu);
-    const u32x4 x0 = mok ? *reinterpret_cast<const u32x4 *>(xrow + b * 64) : u32x4{0, 0, 0, 0};
-    const u32x4 x1 = mok ? *reinterpret_cast<const u32x4 *>(xrow + b * 64 + 8) : u32x4{0, 0, 0, 0};
-    const u32x4 w0 = {lut2[cw[0] & 0xFF], lut2[(cw[0] >> 8) & 0xFF], lut2[(cw[0] >> 16) & 0xFF], lut2[cw[0] >> 24]};
-    const u32x4 w1 = {lut2[cw[1] & 0xFF], lut2[(cw[1] >> 8) & 0xFF], lut2[(cw[1] >> 16) & 0xFF], lut2[cw[1] >> 24]};
-    f32x4 t = mfma16(x0, w0, f32x4{0, 0, 0, 0});
-    t = mfma16(x1, w1, t);
+  const bool mok = l32 < p.M;  // this lane supplies token row l32 of the A operand
+  const uint16_t *xrow = p.X + (int64_t)(mok ? l32 : 0) * p.ldx + 32 * g;
+  const uint8_t *crow[2];
+  const int8_t *qrow[2];
+  int64_t blkrow[2];
 #pragma unroll
-    for (int v = 0; v < 4; ++v) acc[v] = __builtin_fmaf(ah, t[v], acc[v]);
+  for (int gr = 0; gr < 2; ++gr) {
+    const int64_t n = n0 + 32 * gr + l32;
+    crow[gr] = p.codes + n * (p.K >> 1) + 16 * g;
+    qrow[gr] = p.qabsmax + n * nblk;
+    blkrow[gr] = n * nblk;
   }
-  // acc[v] = partial Y[token 4g + v][n]
+  float acc[2][8];
 #pragma unroll
-  for (int v = 0; v < 4; ++v) red[wave][4 * g + v][r16] = acc[v];
-  __syncthreads();
-  if (wave == 0) {
+  for (int gr = 0; gr < 2; ++gr)
 #pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const int tok = 4 * g + v;
-      float y = red[0][tok][r16] + red[1][tok][r16] + red[2][tok][r16] + red[3][tok][r16];
-      if (tok < p.M) {
-        for (int q = 0; q < p.r; ++q)
-          y = __builtin_fmaf(bf16_lo(p.sT[(int64_t)tok * p.ldt + q]), bf16_lo(p.L2[(int64_t)q * p.N + n]), y);
-        p.Y[(int64_t)tok * p.ldy + n] = to_bf16(y);
+    for (int v = 0; v < 8; ++v) acc[gr][v] = 0.0f;
+
+  for (int64_t bb = b0; bb < b1; bb += kGemvUnroll) {
+    u32x4 cw[kGemvUnroll][2];
+    u32x4 xa[kGemvUnroll][4];
+    int8_t qa[kGemvUnroll][2];
+    float s2[kGemvUnroll][2];
+#pragma unroll
+    for (int u = 0; u < kGemvUnroll; ++u) {
+      const int64_t b = bb + u;
+      const bool ok = b < b1;
+#pragma unroll
+      for (int gr = 0; gr < 2; ++gr) {
+        cw[u][gr] = ok ? *reinterpret_cast<const u32x4 *>(crow[gr] + b * 32) : u32x4{0x77777777u, 0x77777777u,
+                                                                                      0x77777777u, 0x77777777u};
+        qa[u][gr] = ok ? qrow[gr][b] : (int8_t)0;
+        s2[u][gr] = ok ? p.scale2[(blkrow[gr] + b) >> 8] : 0.0f;
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        xa[u][j] = (ok && mok) ? *reinterpret_cast<const u32x4 *>(xrow + b * 64 + 8 * j) : u32x4{0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int u = 0; u < kGemvUnroll; ++u) {
+#pragma unroll
+      for (int gr = 0; gr < 2; ++gr) {
+        f32x16 t;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) t[v] = 0.0f;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const uint32_t w = cw[u][gr][j];
+          const u32x4 bw = {lut2[w & 0xFF], lut2[(w >> 8) & 0xFF], lut2[(w >> 16) & 0xFF], lut2[w >> 24]};
+          t = mfma32(xa[u][j], bw, t);
+        }
+        const float ah = scale_hat(qa[u][gr], s2[u][gr], mu);
+#pragma unroll
+        for (int v = 0; v < 8; ++v) acc[gr][v] = __builtin_fmaf(ah, t[v], acc[gr][v]);
       }
     }
+  }
+  // acc[gr][v] = partial Y[token i][row n0 + 32gr + l32], i = 8(v/4) + 4g + v%4
+#pragma unroll
+  for (int gr = 0; gr < 2; ++gr)
+#pragma unroll
+    for (int v = 0; v < 8; ++v) red[wave][gr][8 * (v >> 2) + 4 * g + (v & 3)][l32] = acc[gr][v];
+  __syncthreads();
+  // 64 rows x 16 tokens = 1024 outputs, two per thread
+  for (int o = tid; o < 2 * 16 * 32; o += 512) {
+    const int gr = o / 512, tok = (o / 32) % 16, col = o % 32;
+    if (tok >= p.M) continue;
+    float y = 0.0f;
+#pragma unroll
+    for (int w = 0; w < kGemvWaves; ++w) y += red[w][gr][tok][col];
+    const int64_t n = n0 + 32 * gr + col;
+    for (int q = 0; q < p.r; ++q)
+      y = __builtin_fmaf(bf16_lo(p.sT[(int64_t)tok * p.ldt + q]), bf16_lo(p.L2[(int64_t)q * p.N + n]), y);
+    p.Y[(int64_t)tok * p.ldy + n] = to_bf16(y);
   }
 }
 
@@ -426,7 +475,7 @@ hipError_t launch_linear_fwd(const LinearArgs &a, const uint16_t *X, const uint1
     fill_levels(gp.level, tab);
     {
       TimedLaunch tl(2, st);
-      nf4_gemv_kernel<<<(unsigned)(a.o / 16), 256, 0, st>>>(gp);
+      nf4_gemv_kernel<<<(unsigned)(a.o / kGemvRows), 512, 0, st>>>(gp);
     }
     return hipGetLastError();
   }

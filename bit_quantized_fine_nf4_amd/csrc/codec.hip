@@ -150,14 +150,19 @@ __global__ __launch_bounds__(256) void quantize_kernel(const void *__restrict__ 
 // The mean of the block scales is computed exactly: every float32 is an
 // integer multiple of 2^-149, so the sum is an integer that the kernels
 // accumulate without rounding, binned by exponent, and the one rounding
-// happens at the very end (mean_from_bins, run by the last workgroup).  Each lane keeps a private 64-bit
-// accumulator for an 8-exponent window anchored at its first value; a value
-// outside the window goes straight to its exponent bin.  Bins live in LDS per
-// workgroup and are flushed to a global array of uint64 bins with atomics.
-// Integer addition is associative, so the result does not depend on the order.
+// happens at the very end (mean_from_bins, run by the last workgroup).  Each
+// lane keeps a private 64-bit accumulator for an 8-exponent window anchored at
+// its first value; a value outside the window goes straight to its exponent
+// bin.  Bins live in LDS per workgroup and are flushed with atomics into one of
+// kSlots copies of the global uint64 bins (workgroup index modulo kSlots), so
+// no single address sees more than grid/kSlots atomics; the last workgroup
+// sums the copies.  Integer addition is associative, so the result does not
+// depend on the order.
 // ---------------------------------------------------------------------------
 
 constexpr int kNumBins = 264;  // bin s holds integers in units of 2^(s-149)
+constexpr int kSlots = 16;     // copies of the global bins
+constexpr int kDqGrid = 512;   // workgroups of the binning pass (at most)
 constexpr int kLimbs = 12;     // the exact sum is below 2^(64+263): 11 32-bit limbs suffice
 
 __global__ void zero_u64_kernel(unsigned long long *p, int n) {
@@ -249,7 +254,8 @@ QL_DEV void mean_from_bins(const unsigned long long *b /* LDS, kNumBins */, int6
 }
 
 // Exact sum of the block scales into exponent bins; the last workgroup to finish turns
-// the bins into the rounded mean.  gbins[kNumBins] doubles as the completion counter.
+// the bins into the rounded mean.  gbins holds kSlots copies of the bins followed by the
+// completion counter.
 __global__ __launch_bounds__(256) void dq_bins_kernel(const float *__restrict__ absmax, int64_t nb,
                                                       unsigned long long *__restrict__ gbins,
                                                       float *__restrict__ mean_out) {
@@ -262,18 +268,17 @@ __global__ __launch_bounds__(256) void dq_bins_kernel(const float *__restrict__ 
   const int64_t nthr = (int64_t)gridDim.x * blockDim.x;
   int anchor = -1;
   unsigned long long acc = 0ull;
+  // Branch-free except for the (rare) out-of-window atomic.  A zero has m == 0:
+  // it adds nothing wherever it lands and never anchors the window.
   auto add = [&](float a) {
-    if (a == 0.0f) return;  // contributes nothing; keeps padding from anchoring the window
     uint32_t m;
     int sh;
     split_f32(a, m, sh);
-    if (anchor < 0) anchor = sh > 3 ? sh - 3 : 0;
-    const int d = sh - anchor;
-    if (d >= 0 && d < 8) {
-      acc += (unsigned long long)(m << d);
-    } else {
-      atomicAdd(&bins[sh], (unsigned long long)m);
-    }
+    anchor = (anchor < 0 && m != 0u) ? (sh > 3 ? sh - 3 : 0) : anchor;
+    const uint32_t d = (uint32_t)(sh - anchor);
+    const bool in = d < 8u;
+    acc += in ? (unsigned long long)(m << (d & 7u)) : 0ull;
+    if (!in && m != 0u) atomicAdd(&bins[sh], (unsigned long long)m);
   };
   // 16-byte loads, four in flight per thread
   const int64_t nvec = nb >> 2;
@@ -291,15 +296,20 @@ __global__ __launch_bounds__(256) void dq_bins_kernel(const float *__restrict__ 
   if (anchor >= 0 && acc) atomicAdd(&bins[anchor], acc);
   __syncthreads();
   for (int i = threadIdx.x; i < kNumBins; i += blockDim.x)
-    if (bins[i]) atomicAdd(&gbins[i], bins[i]);
+    if (bins[i]) atomicAdd(&gbins[(blockIdx.x % kSlots) * kNumBins + i], bins[i]);
   __threadfence();
   __syncthreads();
-  if (threadIdx.x == 0) last = atomicAdd(&gbins[kNumBins], 1ull) == (unsigned long long)(gridDim.x - 1);
+  if (threadIdx.x == 0)
+    last = atomicAdd(&gbins[kSlots * kNumBins], 1ull) == (unsigned long long)(gridDim.x - 1);
   __syncthreads();
   if (!last) return;
   __threadfence();
-  for (int i = threadIdx.x; i < kNumBins; i += blockDim.x)
-    bins[i] = __hip_atomic_load(&gbins[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  for (int i = threadIdx.x; i < kNumBins; i += blockDim.x) {
+    unsigned long long t = 0;
+    for (int k = 0; k < kSlots; ++k)
+      t += __hip_atomic_load(&gbins[k * kNumBins + i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    bins[i] = t;
+  }
   __syncthreads();
   mean_from_bins(bins, nb, mean_out);
 }
@@ -460,13 +470,13 @@ hipError_t launch_quantize(const void *w, bool bf16, int64_t n, uint8_t *codes, 
   return hipGetLastError();
 }
 
-size_t dq_workspace_bytes() { return ((size_t)(kNumBins + 1) * 8 + 255) / 256 * 256; }
+size_t dq_workspace_bytes() { return ((size_t)(kSlots * kNumBins + 1) * 8 + 255) / 256 * 256; }
 
 hipError_t launch_double_quant(const float *absmax, int64_t nb, int8_t *qabsmax, float *scale2,
                                float *mean, void *ws, hipStream_t st) {
   auto *bins = reinterpret_cast<unsigned long long *>(ws);
-  zero_u64_kernel<<<(kNumBins + 1 + 255) / 256, 256, 0, st>>>(bins, kNumBins + 1);
-  const int grid = grid_for(nb, 256 * 16, 4096);
+  zero_u64_kernel<<<(kSlots * kNumBins + 1 + 255) / 256, 256, 0, st>>>(bins, kSlots * kNumBins + 1);
+  const int grid = grid_for(nb, 256 * 16, kDqGrid);
   dq_bins_kernel<<<grid, 256, 0, st>>>(absmax, nb, bins, mean);
   const int64_t nch = (nb + kChunk - 1) / kChunk;
   dq_chunks_kernel<<<(int)((nch + 3) / 4), 256, 0, st>>>(absmax, nb, mean, qabsmax, scale2);

@@ -117,17 +117,18 @@ __global__ void skinny_finish_kernel(const float *__restrict__ part, int S, int6
 }
 
 // ---------------------------------------------------------------------------
-// Few-token forward (M <= 16): Y = X·W_hat (+ s·T·L2), bandwidth-bound on the
-// packed codes.  Matrix-core formulation with the weights as the B operand of
-// v_mfma_f32_32x32x16_bf16: lane l owns output row n = n0 + l%32 and lane group
-// g = l/32 owns k in [32g, 32g+32) of a 64-block, so one 16-byte code load per
-// lane per block feeds four MFMAs (MFMA j takes k = 32g + 8j + 0..7) that span
-// exactly one block.  The MFMAs see bf16(level[code]) (a 256-entry LDS table
-// maps a code byte to the bf16 pair of its two levels) and the block scale
-// a_hat is applied once to the float32 block partial.  Tokens are the MFMA
-// rows (rows >= M are zero; only the 16 lowest rows are kept).
-// Workgroup: 512 threads = 8 waves over 64 output rows (two 32-row groups that
-// share the token fragments); the waves split K and reduce through LDS.
+// Few-token forward (M <= 16): Y[m][n] = sum_k X[m][k] W_hat[n][k] (+ LoRA).
+// Pure streaming of the codes ([TT] §3 storage; [MC] "The algebra" Eq. 3 for
+// the output).  A workgroup owns 64 output features and walks the whole K in
+// stages of 256 weights (4 blocks): every stage (64 rows x 128 code bytes,
+// 16 tokens x 512 activation bytes, 64 x 4 block scales) is fetched by all
+// 256 threads with coalesced loads two stages ahead of use, parked in
+// registers, then written to a double-buffered, XOR-swizzled LDS tile.
+// Wave w takes block w of every stage for all 64 rows (four 16-row MFMA
+// groups share one activation fragment) with 16x16x32 MFMAs, tokens being the
+// MFMA rows.  The B operand is bf16(level[c]) from a byte -> bf16-pair table;
+// the block scale a_hat multiplies each block's float32 partial.  The four
+// waves' partial sums meet in LDS at the end.
 // ---------------------------------------------------------------------------
 struct GemvParams {
   const uint16_t *X;
@@ -147,94 +148,178 @@ struct GemvParams {
   float level[16];
 };
 
-constexpr int kGemvRows = 64, kGemvWaves = 8, kGemvUnroll = 4;
+constexpr int kGvRows = 64;          // output features per workgroup
+constexpr int kGvKS = 256;           // weights along K per stage (4 blocks)
+constexpr int kGvCodeB = kGvKS / 2;  // code bytes per row per stage
+constexpr int kGvXB = kGvKS * 2;     // activation bytes per token per stage
+constexpr int kGvThreads = 512;      // 8 waves: wave w takes block w%4, row groups 2(w/4), 2(w/4)+1
+// Lookup table: 32 copies of the 256-entry table interleaved so that lane l
+// only touches banks l%32 and l%32 + 32 (conflict-free 32-lane phases).
+constexpr int kGvLutWords = 256 * 32;
 
-__global__ __launch_bounds__(512) void nf4_gemv_kernel(GemvParams p) {
-  __shared__ uint32_t lut2[256];
-  __shared__ float red[kGemvWaves][2][16][33];
+struct GvStage {
+  u32x4 c;     // codes: 16 bytes of the stage tile
+  u32x4 x;     // activations: 16 bytes of the stage tile
+  uint32_t q;  // one int8 block scale (threads < 256: row tid/4, block tid%4)
+  float s2;    // its second-level scale
+};
+
+QL_DEV __amdgpu_buffer_rsrc_t gv_rsrc(const void *base, int64_t bytes) {
+  const int64_t cap = 0x7FFFFFF0;
+  const int32_t n = (int32_t)(bytes < 0 ? 0 : (bytes > cap ? cap : bytes));
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, n, 0x00020000);
+}
+constexpr int kGvOOB = (int)0x80000000u;  // offset past every buffer: the load returns zero
+
+// MT: token-count class (1, 4 or 16); output token 4g + v exists only for
+// v < MT when MT < 4, so the block-scale FMAs for absent tokens are skipped.
+template <int MT>
+__global__ __launch_bounds__(kGvThreads) void nf4_gemv_kernel(GemvParams p) {
+  __shared__ uint32_t lut[kGvLutWords];
+  // stage tiles: codes [2][64 rows][128 B], activations [2][16 tokens][512 B];
+  // reused for the cross-wave sum after the K loop
+  __shared__ __attribute__((aligned(16))) uint8_t tiles[2 * kGvRows * kGvCodeB + 2 * 16 * kGvXB];
+  __shared__ __attribute__((aligned(16))) float abuf[2][4 * kGvRows];
+  uint8_t(*cbuf)[kGvRows * kGvCodeB] = reinterpret_cast<uint8_t(*)[kGvRows * kGvCodeB]>(tiles);
+  uint8_t(*xbuf)[16 * kGvXB] = reinterpret_cast<uint8_t(*)[16 * kGvXB]>(tiles + 2 * kGvRows * kGvCodeB);
+  __shared__ float lv[16];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  if (tid < 256) lut2[tid] = pack_bf16x2(p.level[tid >> 4], p.level[tid & 15]);
+  if (tid < 16) lv[tid] = p.level[tid];
   __syncthreads();
+  for (int i = tid; i < kGvLutWords; i += kGvThreads) {
+    const int e = i >> 5;  // word i = 32 e + copy
+    lut[i] = pack_bf16x2(lv[e >> 4], lv[e & 15]);
+  }
 
-  const int64_t n0 = (int64_t)blockIdx.x * kGemvRows;
-  const int g = lane >> 5, l32 = lane & 31;
-  const int64_t nblk = p.K >> 6;
-  const int64_t b0 = wave * nblk / kGemvWaves, b1 = (wave + 1) * nblk / kGemvWaves;
+  const int64_t n0 = (int64_t)blockIdx.x * kGvRows;
+  const int64_t rowB = p.K >> 1, nblk = p.K >> 6;
+  const int nst = (int)((p.K + kGvKS - 1) / kGvKS);
   const float mu = *p.mean;
-  const bool mok = l32 < p.M;  // this lane supplies token row l32 of the A operand
-  const uint16_t *xrow = p.X + (int64_t)(mok ? l32 : 0) * p.ldx + 32 * g;
-  const uint8_t *crow[2];
-  const int8_t *qrow[2];
-  int64_t blkrow[2];
-#pragma unroll
-  for (int gr = 0; gr < 2; ++gr) {
-    const int64_t n = n0 + 32 * gr + l32;
-    crow[gr] = p.codes + n * (p.K >> 1) + 16 * g;
-    qrow[gr] = p.qabsmax + n * nblk;
-    blkrow[gr] = n * nblk;
-  }
-  float acc[2][8];
-#pragma unroll
-  for (int gr = 0; gr < 2; ++gr)
-#pragma unroll
-    for (int v = 0; v < 8; ++v) acc[gr][v] = 0.0f;
+  // Buffer views: the workgroup's 64 code rows, its 64 rows of int8 scales,
+  // all second-level scales, the M activation rows.  Per-thread offsets are
+  // fixed; the stage advances through the scalar offset.  Codes and scales
+  // past a row's end belong to the next row (or read as zero at the end of
+  // the view): they are finite and always meet zero activations, because
+  // activations past K (and tokens >= M) are forced to zero.
+  const __amdgpu_buffer_rsrc_t rc = gv_rsrc(p.codes + n0 * rowB, kGvRows * rowB);
+  const __amdgpu_buffer_rsrc_t rq = gv_rsrc(p.qabsmax + n0 * nblk, kGvRows * nblk);
+  const __amdgpu_buffer_rsrc_t rs = gv_rsrc(p.scale2, ((p.N * nblk + kChunk - 1) / kChunk) * 4);
+  const __amdgpu_buffer_rsrc_t rx = gv_rsrc(p.X, ((int64_t)(p.M - 1) * p.ldx + p.K) * 2);
+  const int cr = tid >> 3, cp = tid & 7;  // code piece: row, 16-byte piece
+  const int voc = (int)(cr * rowB) + 16 * cp;
+  const int lc = (cr * 8 + (cp ^ ((cr >> 1) & 7))) * 16;
+  const int xm = tid >> 5, xp = tid & 31;  // activation piece: token, 16-byte piece
+  const int vox = xm < p.M ? (int)((xm * p.ldx + 8 * xp) * 2) : kGvOOB;
+  const int xlim = p.K > 8 * xp ? (int)((p.K - 8 * xp + kGvKS - 1) / kGvKS) : 0;  // stages with this piece inside K
+  const int lx = (xm * 32 + (xp ^ xm)) * 16;
+  const bool sthr = tid < 4 * kGvRows;         // scale role (waves 0-3)
+  const int srow = (tid >> 2) & 63, sblk = tid & 3;
+  const int voq = (int)(srow * nblk) + sblk;
+  const int64_t sbase = (n0 + srow) * nblk + sblk;
+  const int la = (sblk * 16 + (srow & 15)) * 4 + (srow >> 4);  // abuf [block][n][group]
 
-  for (int64_t bb = b0; bb < b1; bb += kGemvUnroll) {
-    u32x4 cw[kGemvUnroll][2];
-    u32x4 xa[kGemvUnroll][4];
-    int8_t qa[kGemvUnroll][2];
-    float s2[kGemvUnroll][2];
+  auto load = [&](GvStage &R, int st) {
+    R.c = __builtin_amdgcn_raw_buffer_load_b128(rc, voc, st * kGvCodeB, 0);
+    R.x = __builtin_amdgcn_raw_buffer_load_b128(rx, st < xlim ? vox : kGvOOB, st * kGvXB, 0);
+    R.q = __builtin_amdgcn_raw_buffer_load_b8(rq, sthr ? voq : kGvOOB, 4 * st, 0);
+    R.s2 = __builtin_bit_cast(
+        float, __builtin_amdgcn_raw_buffer_load_b32(rs, sthr ? (int)(((sbase + 4 * st) >> 8) * 4) : kGvOOB, 0, 0));
+  };
+  auto store = [&](const GvStage &R, int buf) {
+    *reinterpret_cast<u32x4 *>(&cbuf[buf][lc]) = R.c;
+    *reinterpret_cast<u32x4 *>(&xbuf[buf][lx]) = R.x;
+    if (sthr) abuf[buf][la] = scale_hat((int8_t)(R.q & 0xFF), R.s2, mu);
+  };
+  // compute role: token / feature index within a 16x16 MFMA tile, k-group
+  const int n = lane & 15, g = lane >> 4;
+  const int lsel = lane & 31;
+  const int blk = wave & 3, rp = wave >> 2;
+  const int pcw = 2 * blk + (g >> 1);  // code piece of this block for this k-group
+  const int pxa = 8 * blk + 2 * g;     // activation pieces pxa, pxa + 1
+  const int la0 = (n * 32 + (pxa ^ n)) * 16, la1 = (n * 32 + ((pxa + 1) ^ n)) * 16;
+  int lcode[2];
 #pragma unroll
-    for (int u = 0; u < kGemvUnroll; ++u) {
-      const int64_t b = bb + u;
-      const bool ok = b < b1;
-#pragma unroll
-      for (int gr = 0; gr < 2; ++gr) {
-        cw[u][gr] = ok ? *reinterpret_cast<const u32x4 *>(crow[gr] + b * 32) : u32x4{0x77777777u, 0x77777777u,
-                                                                                      0x77777777u, 0x77777777u};
-        qa[u][gr] = ok ? qrow[gr][b] : (int8_t)0;
-        s2[u][gr] = ok ? p.scale2[(blkrow[gr] + b) >> 8] : 0.0f;
-      }
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        xa[u][j] = (ok && mok) ? *reinterpret_cast<const u32x4 *>(xrow + b * 64 + 8 * j) : u32x4{0, 0, 0, 0};
-    }
-#pragma unroll
-    for (int u = 0; u < kGemvUnroll; ++u) {
-#pragma unroll
-      for (int gr = 0; gr < 2; ++gr) {
-        f32x16 t;
-#pragma unroll
-        for (int v = 0; v < 16; ++v) t[v] = 0.0f;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const uint32_t w = cw[u][gr][j];
-          const u32x4 bw = {lut2[w & 0xFF], lut2[(w >> 8) & 0xFF], lut2[(w >> 16) & 0xFF], lut2[w >> 24]};
-          t = mfma32(xa[u][j], bw, t);
-        }
-        const float ah = scale_hat(qa[u][gr], s2[u][gr], mu);
-#pragma unroll
-        for (int v = 0; v < 8; ++v) acc[gr][v] = __builtin_fmaf(ah, t[v], acc[gr][v]);
-      }
-    }
+  for (int h = 0; h < 2; ++h) {
+    const int row = 16 * (2 * rp + h) + n;
+    lcode[h] = (row * 8 + (pcw ^ ((row >> 1) & 7))) * 16 + 8 * (g & 1);
   }
-  // acc[gr][v] = partial Y[token i][row n0 + 32gr + l32], i = 8(v/4) + 4g + v%4
+  constexpr int NV = MT < 4 ? MT : 4;
+  float acc[2][NV];
 #pragma unroll
-  for (int gr = 0; gr < 2; ++gr)
+  for (int h = 0; h < 2; ++h)
 #pragma unroll
-    for (int v = 0; v < 8; ++v) red[wave][gr][8 * (v >> 2) + 4 * g + (v & 3)][l32] = acc[gr][v];
+    for (int v = 0; v < NV; ++v) acc[h][v] = 0.0f;
+  auto compute = [&](int buf) {
+    const uint8_t *cb = cbuf[buf];
+    const uint8_t *xb = xbuf[buf];
+    const u32x4 a0 = *reinterpret_cast<const u32x4 *>(xb + la0);
+    const u32x4 a1 = *reinterpret_cast<const u32x4 *>(xb + la1);
+    const f32x2 ah = *reinterpret_cast<const f32x2 *>(&abuf[buf][(blk * 16 + n) * 4 + 2 * rp]);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const u32x2 cw = *reinterpret_cast<const u32x2 *>(cb + lcode[h]);
+      u32x4 bw[2];
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const uint32_t w = e ? cw.y : cw.x;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) bw[e][t] = lut[((w >> (8 * t)) & 0xFF) * 32 + lsel];
+      }
+      f32x4 part = mfma16(a0, bw[0], f32x4{0.0f, 0.0f, 0.0f, 0.0f});
+      part = mfma16(a1, bw[1], part);
+#pragma unroll
+      for (int v = 0; v < NV; ++v) acc[h][v] = __builtin_fmaf(ah[h], part[v], acc[h][v]);
+    }
+  };
+
+  // Two register stages in flight.  Every stage issues the same four loads
+  // and the loop body is uniform: stages past the end read zero activations
+  // (an extra stage adds exactly nothing), which keeps the number of loads in
+  // flight identical on every path, so the wait before each LDS store covers
+  // only the older register stage.  The scheduling fences keep the compiler
+  // from interleaving the two register stages (which would make every wait
+  // cover both).
+  GvStage ra, rb;
+  load(ra, 0);
+  store(ra, 0);
+  __builtin_amdgcn_sched_barrier(0);
+  load(ra, 1);
+  __builtin_amdgcn_sched_barrier(0);
+  load(rb, 2);
+  __builtin_amdgcn_sched_barrier(0);
   __syncthreads();
-  // 64 rows x 16 tokens = 1024 outputs, two per thread
-  for (int o = tid; o < 2 * 16 * 32; o += 512) {
-    const int gr = o / 512, tok = (o / 32) % 16, col = o % 32;
-    if (tok >= p.M) continue;
-    float y = 0.0f;
+  for (int st = 0; st < nst; st += 2) {
+    compute(0);
+    store(ra, 1);
+    load(ra, st + 3);
+    __builtin_amdgcn_sched_barrier(0);
+    __syncthreads();
+    compute(1);
+    store(rb, 0);
+    load(rb, st + 4);
+    __builtin_amdgcn_sched_barrier(0);
+    __syncthreads();
+  }
+
+  // Cross-wave sum: acc[h][v] of wave (blk, rp) = partial Y[token 4g + v][row 16(2rp + h) + n]
+  // red[block][token][row], rows padded to 68 floats: the 64 lanes of a store
+  // (16 rows x 4 token groups) land in 64 distinct banks.
+  constexpr int kRedLd = 68;
+  static_assert(4 * 16 * kRedLd * 4 <= sizeof(tiles), "reduction fits in the stage tiles");
+  float *red = reinterpret_cast<float *>(tiles);
 #pragma unroll
-    for (int w = 0; w < kGemvWaves; ++w) y += red[w][gr][tok][col];
-    const int64_t n = n0 + 32 * gr + col;
+  for (int h = 0; h < 2; ++h)
+#pragma unroll
+    for (int v = 0; v < NV; ++v) red[(blk * 16 + 4 * g + v) * kRedLd + 16 * (2 * rp + h) + n] = acc[h][v];
+  __syncthreads();
+  const int row = tid & 63;
+  const int64_t col = n0 + row;
+  for (int m = tid >> 6; m < p.M; m += kGvThreads / 64) {
+    float y = red[m * kRedLd + row] + red[(16 + m) * kRedLd + row] + red[(32 + m) * kRedLd + row] +
+              red[(48 + m) * kRedLd + row];
     for (int q = 0; q < p.r; ++q)
-      y = __builtin_fmaf(bf16_lo(p.sT[(int64_t)tok * p.ldt + q]), bf16_lo(p.L2[(int64_t)q * p.N + n]), y);
-    p.Y[(int64_t)tok * p.ldy + n] = to_bf16(y);
+      y = __builtin_fmaf(bf16_lo(p.sT[(int64_t)m * p.ldt + q]), bf16_lo(p.L2[(int64_t)q * p.N + col]), y);
+    p.Y[(int64_t)m * p.ldy + col] = to_bf16(y);
   }
 }
 
@@ -475,7 +560,13 @@ hipError_t launch_linear_fwd(const LinearArgs &a, const uint16_t *X, const uint1
     fill_levels(gp.level, tab);
     {
       TimedLaunch tl(2, st);
-      nf4_gemv_kernel<<<(unsigned)(a.o / kGemvRows), 512, 0, st>>>(gp);
+      const unsigned grid = (unsigned)(a.o / kGvRows);
+      if (a.M == 1)
+        nf4_gemv_kernel<1><<<grid, kGvThreads, 0, st>>>(gp);
+      else if (a.M <= 4)
+        nf4_gemv_kernel<4><<<grid, kGvThreads, 0, st>>>(gp);
+      else
+        nf4_gemv_kernel<16><<<grid, kGvThreads, 0, st>>>(gp);
     }
     return hipGetLastError();
   }

@@ -52,6 +52,8 @@ def check_full(w, l1, l2, x, dy, s, label):
 SMALL = [  # (M, h, o, r, s)
     (1, 64, 64, 0, 1.0),
     (3, 128, 192, 8, 2.0),
+    (7, 320, 128, 4, 1.0),
+    (12, 576, 192, 0, 1.0),
     (16, 1024, 1024, 8, 2.0),
     (17, 256, 320, 16, 2.0),
     (130, 512, 384, 5, 0.5),

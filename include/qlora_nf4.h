@@ -81,7 +81,7 @@ typedef struct {
  * division) and mapped to the nearest of the 16 NF4 levels, ties to the lower
  * level.  A short last block is zero-padded; an odd n pads the last low nibble
  * with code 7 (the zero level); an all-zero block gets code 7 everywhere.
- * Alignment: w, codes and absmax need only their natural alignment.
+ * Alignment: w 16 bytes; codes and absmax 4 bytes.
  */
 qlora_status_t qlora_quantize(const void *w, qlora_dtype_t w_dtype, int64_t n, uint8_t *codes,
                               float *absmax, void *stream);
@@ -100,6 +100,7 @@ qlora_status_t qlora_quantize(const void *w, qlora_dtype_t w_dtype, int64_t n, u
  * c = fp32(a - mean) gets step s2_j = fp32(max|c| / 127) and codes
  * q = rint(fp32(c / s2_j)) in [-127, 127] ([TT] §2's symmetric int8 scheme;
  * step 0 gives codes 0).  Requires 1 <= nblocks < 2^32.
+ * Alignment: absmax 16 bytes, workspace 256 bytes, qabsmax, scale2 and mean 4.
  */
 qlora_status_t qlora_double_quant(const float *absmax, int64_t nblocks, int8_t *qabsmax, float *scale2,
                                   float *mean, void *workspace, size_t ws_bytes, void *stream);
@@ -110,7 +111,8 @@ qlora_status_t qlora_double_quant(const float *absmax, int64_t nblocks, int8_t *
  *  a_hat = fp32(fp32(qabsmax * scale2) + mean)      (no fused multiply-add)
  *  w_hat = fp32(level[code] * a_hat)                 (out_dtype QLORA_F32)
  *        = bf16 round-to-nearest-even of that value  (out_dtype QLORA_BF16)
- *  out   n float32 or bf16 values.  Alignment: natural alignment only.
+ *  out   n float32 or bf16 values.
+ * Alignment: codes and out 16 bytes; scale2 and mean 4 bytes; qabsmax any.
  */
 qlora_status_t qlora_dequantize(const uint8_t *codes, const int8_t *qabsmax, const float *scale2,
                                 const float *mean, int64_t n, void *out, qlora_dtype_t out_dtype,

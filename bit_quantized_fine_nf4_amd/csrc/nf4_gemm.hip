@@ -152,50 +152,73 @@ __global__ __launch_bounds__(512) void nf4_gemm_kernel(GemmParams p) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
 
-  auto load_a = [&](int kt, u32x4 (&ra)[A_CH]) {
+  // One register set holds everything a K step needs from global memory.
+  struct Stage {
+    u32x4 a[A_CH];  // A tile chunks
+    u32x4 c;        // this thread's code bytes (UB of them)
+    uint32_t q;     // its int8 block scale, zero-extended (see put_part)
+    float s2;       // its second-level scale
+  };
+  auto load_stage = [&](int kt_, Stage &S) {
+    // The step index is wave-uniform; saying so keeps the scalar offsets in SGPRs
+    // (otherwise every buffer load becomes a per-lane waterfall loop).
+    const int kt = __builtin_amdgcn_readfirstlane(kt_);
 #pragma unroll
-    for (int c = 0; c < A_CH; ++c) ra[c] = bload128(rA, voffA[c], kt * BK * 2);
-  };
-  auto store_a = [&](int buf, const u32x4 (&ra)[A_CH]) {
-#pragma unroll
-    for (int c = 0; c < A_CH; ++c) {
-      const int chunk = tid + NT * c;
-      *reinterpret_cast<u32x4 *>(sm + buf * STAGE + (chunk >> 3) * LDA + (chunk & 7) * 8) = ra[c];
-    }
-  };
-  auto load_codes = [&](__amdgpu_buffer_rsrc_t r, int voff, int soff) -> u32x4 {
-    if (UB == 16) return bload128(r, voff, soff);
-    const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0);
-    return u32x4{v[0], v[1], 0u, 0u};
-  };
-  auto load_b = [&](int kt, u32x4 &rc, int8_t &rq, float &rs) {
+    for (int c = 0; c < A_CH; ++c) S.a[c] = bload128(rA, voffA[c], kt * BK * 2);
     if (!TRANS) {
-      rc = load_codes(rCf, voffC, kt * 32);
-      rq = bload_i8(rQf, voffQ, kt);
-      rs = bload_f32(rS2, (int)(((blk0 + kt) >> 8) * 4), 0);
+      if (UB == 16) {
+        S.c = bload128(rCf, voffC, kt * 32);
+      } else {
+        const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(rCf, voffC, kt * 32, 0);
+        S.c = u32x4{v[0], v[1], 0u, 0u};
+      }
+      S.q = __builtin_amdgcn_raw_buffer_load_b8(rQf, voffQ, kt, 0);
+      S.s2 = bload_f32(rS2, (int)(((blk0 + kt) >> 8) * 4), 0);
     } else {
       const int64_t krow0 = (int64_t)kt * BK;
       const auto rC = make_rsrc(p.codes + krow0 * (p.ldw >> 1) + (n0 >> 1),
                                 (p.wrows - krow0) * (p.ldw >> 1) - (n0 >> 1));
       const auto rQ = make_rsrc(p.qabsmax + krow0 * bpr + (n0 >> 6), (p.wrows - krow0) * bpr - (n0 >> 6));
-      rc = load_codes(rC, voffC, 0);
-      rq = bload_i8(rQ, voffQ, 0);
-      rs = bload_f32(rS2, (int)(((blk0 + krow0 * bpr) >> 8) * 4), 0);
+      if (UB == 16) {
+        S.c = bload128(rC, voffC, 0);
+      } else {
+        const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(rC, voffC, 0, 0);
+        S.c = u32x4{v[0], v[1], 0u, 0u};
+      }
+      S.q = __builtin_amdgcn_raw_buffer_load_b8(rQ, voffQ, 0, 0);
+      S.s2 = bload_f32(rS2, (int)(((blk0 + krow0 * bpr) >> 8) * 4), 0);
     }
   };
-  auto decode_b = [&](int buf, const u32x4 &rc, int8_t rq, float rs) {
-    const float ah = scale_hat(rq, rs, mu);
-    uint32_t o[UB];
+  // Part `part` (0..3) of writing a stage into LDS buffer `buf`: a quarter of the
+  // A chunks and a quarter of the code bytes, decoded (LUT pair -> * a_hat ->
+  // bf16) and stored.  `ah` is the stage's block scale (computed by part 0).
+  constexpr int BPP = UB / 4;  // code bytes decoded per part (2 or 4)
+  auto put_part = [&](int buf, int part, const Stage &S, float &ah) {
+    // int8 value from the zero-extended byte by float arithmetic: a plain
+    // sign extension would let instruction selection fuse it with the load
+    // and move that load to this point, next to the younger prefetch.
+    if (part == 0) {
+      const float qf = (float)S.q - (float)(S.q & 0x80u) * 2.0f;
+      ah = qf * S.s2 + mu;
+    }
 #pragma unroll
-    for (int d = 0; d < UB / 4; ++d)
-#pragma unroll
-      for (int b = 0; b < 4; ++b) {
-        const f32x2 l = lut[(rc[d] >> (8 * b)) & 0xFF];
-        o[4 * d + b] = pack_bf16x2(l[0] * ah, l[1] * ah);
+    for (int c = 0; c < A_CH; ++c)
+      if ((c & 3) == part) {
+        const int chunk = tid + NT * c;
+        *reinterpret_cast<u32x4 *>(sm + buf * STAGE + (chunk >> 3) * LDA + (chunk & 7) * 8) = S.a[c];
       }
-    u32x4 *dst = reinterpret_cast<u32x4 *>(bdst0 + buf * STAGE);
+    uint32_t o[BPP];
 #pragma unroll
-    for (int q = 0; q < UB / 4; ++q) dst[q] = u32x4{o[4 * q], o[4 * q + 1], o[4 * q + 2], o[4 * q + 3]};
+    for (int b = 0; b < BPP; ++b) {
+      const int byte = part * BPP + b;
+      const f32x2 l = lut[(S.c[byte >> 2] >> (8 * (byte & 3))) & 0xFF];
+      o[b] = pack_bf16x2(l[0] * ah, l[1] * ah);
+    }
+    uint16_t *dst = bdst0 + buf * STAGE + part * 2 * BPP;
+    if (BPP == 4)
+      *reinterpret_cast<u32x4 *>(dst) = u32x4{o[0], o[1], o[2], o[3]};
+    else
+      *reinterpret_cast<u32x2 *>(dst) = u32x2{o[0], o[BPP - 1]};
   };
   // B fragments of MFMA step kk from an LDS tile; kn: tile is [k][n] (transposing reads)
   auto load_bfrag = [&](const uint16_t *bs, bool kn, int kk, u32x4 (&bf)[TN]) {
@@ -210,57 +233,61 @@ __global__ __launch_bounds__(512) void nf4_gemm_kernel(GemmParams p) {
       for (int j = 0; j < TN; ++j) bf[j] = tr_pair(b0 + j * 32, b0 + 4 * LDKN + j * 32);
     }
   };
-  auto mma_step = [&](int buf, bool kn) {
+  auto mma_kk = [&](int buf, bool kn, int kk) {
     const uint16_t *as = sm + buf * STAGE + (wm * WTM + l32) * LDA + 32 * g;
     const uint16_t *bs = bsm + buf * STAGE;
+    u32x4 af[TM], bf[TN];
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      u32x4 af[TM], bf[TN];
+    for (int i = 0; i < TM; ++i) af[i] = *reinterpret_cast<const u32x4 *>(as + i * 32 * LDA + 8 * kk);
+    load_bfrag(bs, kn, kk, bf);
 #pragma unroll
-      for (int i = 0; i < TM; ++i) af[i] = *reinterpret_cast<const u32x4 *>(as + i * 32 * LDA + 8 * kk);
-      load_bfrag(bs, kn, kk, bf);
+    for (int i = 0; i < TM; ++i)
 #pragma unroll
-      for (int i = 0; i < TM; ++i)
+      for (int j = 0; j < TN; ++j) acc[i][j] = mfma32(af[i], bf[j], acc[i][j]);
+  };
+  auto mma_step = [&](int buf, bool kn) {
 #pragma unroll
-        for (int j = 0; j < TN; ++j) acc[i][j] = mfma32(af[i], bf[j], acc[i][j]);
-    }
+    for (int kk = 0; kk < 4; ++kk) mma_kk(buf, kn, kk);
   };
 
-  u32x4 ra[A_CH];
-  u32x4 rc = {0, 0, 0, 0};
-  int8_t rq = 0;
-  float rs = 0.0f;
-
+  // Software pipeline.  Step kt computes on LDS buffer kt&1 while, between its
+  // four MFMA groups, the next step's A chunks and decoded B are written into
+  // the other buffer from registers loaded one step earlier, and the loads for
+  // step kt+2 are in flight.  One barrier per step.  Loads past the last step
+  // read harmless data (zeros or the next row) that is never used.
+  Stage S0, S1;
+  float ah = 0.0f;
   __syncthreads();  // decode table ready
-  load_a(0, ra);
-  load_b(0, rc, rq, rs);
-  store_a(0, ra);
-  decode_b(0, rc, rq, rs);
-  __syncthreads();
   const int nk = p.ksteps;
-  for (int kt = 0; kt < nk; kt += 2) {
-    // even step: compute on buffer 0 while step kt+1 loads into registers, then into buffer 1
-    if (kt + 1 < nk) {
-      load_a(kt + 1, ra);
-      load_b(kt + 1, rc, rq, rs);
-    }
-    mma_step(0, TRANS);
-    if (kt + 1 < nk) {
-      store_a(1, ra);
-      decode_b(1, rc, rq, rs);
+  load_stage(0, S0);
+  __builtin_amdgcn_sched_barrier(0);
+  load_stage(1, S1);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int part = 0; part < 4; ++part) put_part(0, part, S0, ah);
+  __syncthreads();
+  auto step = [&](int kt, Stage &Snext, Stage &Sfree) {
+    // Snext holds step kt+1; Sfree is refilled with step kt+2 (past the last step
+    // these loads and writes are harmless and unused).
+    const int buf = kt & 1;
+    load_stage(kt + 2, Sfree);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      mma_kk(buf, TRANS, kk);
+      put_part(buf ^ 1, kk, Snext, ah);
     }
     __syncthreads();
-    if (kt + 1 >= nk) break;
-    // odd step
-    if (kt + 2 < nk) {
-      load_a(kt + 2, ra);
-      load_b(kt + 2, rc, rq, rs);
-    }
-    mma_step(1, TRANS);
-    if (kt + 2 < nk) {
-      store_a(0, ra);
-      decode_b(0, rc, rq, rs);
-    }
+  };
+  // Uniform two-step body (the same loads in flight on every path); an odd
+  // last step is peeled.
+  int kt = 0;
+  for (; kt + 1 < nk; kt += 2) {
+    step(kt, S1, S0);
+    step(kt + 1, S0, S1);
+  }
+  if (kt < nk) {
+    mma_step(kt & 1, TRANS);
     __syncthreads();
   }
 

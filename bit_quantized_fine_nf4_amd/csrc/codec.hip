@@ -297,13 +297,16 @@ __global__ __launch_bounds__(256) void dq_bins_kernel(const float *__restrict__ 
   __syncthreads();
   for (int i = threadIdx.x; i < kNumBins; i += blockDim.x)
     if (bins[i]) atomicAdd(&gbins[(blockIdx.x % kSlots) * kNumBins + i], bins[i]);
-  __threadfence();
+  // The bins only ever change through device atomics, which are coherent
+  // across the XCDs: waiting until this workgroup's atomics are acknowledged
+  // is enough before counting in (no device-wide cache writeback).
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   if (threadIdx.x == 0)
     last = atomicAdd(&gbins[kSlots * kNumBins], 1ull) == (unsigned long long)(gridDim.x - 1);
   __syncthreads();
   if (!last) return;
-  __threadfence();
   for (int i = threadIdx.x; i < kNumBins; i += blockDim.x) {
     unsigned long long t = 0;
     for (int k = 0; k < kSlots; ++k)

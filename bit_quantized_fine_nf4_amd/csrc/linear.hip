@@ -17,13 +17,16 @@
 //   nf4_gemv_kernel      M <= 16 forward: streams the codes once, decodes a
 //                        byte (two codes) per LDS lookup, applies the block
 //                        scale after each 64-wide MFMA pair
-//   lora_grad_kernel     dL1 = s·X^T·U and dL2 = s·T^T·dY: reduction over
-//                        tokens, LDS-transposed operands, split over tokens
-//   lora_grad_finish     sums the token splits, scales by s, stores dL1
-//                        [h][r] or dL2 [r][o]
+//   lora_grad_kernel     dL1 = s·X^T·U and dL2 = s·T^T·dY in one launch:
+//                        reduction over tokens, LDS-transposed operands,
+//                        split over tokens; the last split of a tile sums,
+//                        scales by s and stores dL1 [h][r] or dL2 [r][o];
+//                        runs on a side stream concurrently with the dX GEMM
 
 #include "linear.h"
 #include "gemm.h"
+
+#include <mutex>
 
 namespace ql {
 
@@ -47,10 +50,13 @@ QL_DEV uint16_t to_bf16(float v) { return (uint16_t)(pack_bf16x2(v, 0.0f) & 0xFF
 
 // ---------------------------------------------------------------------------
 // dst[a][b] = (a < av && b < bv) ? (trans ? src[b*lds + a] : src[a*lds + b]) : 0
+// Also clears nzero completion counters used later in the same call.
 // ---------------------------------------------------------------------------
 __global__ void relayout_kernel(const uint16_t *__restrict__ src, int64_t lds, bool trans, int64_t A,
-                                int64_t B, int64_t av, int64_t bv, uint16_t *__restrict__ dst) {
+                                int64_t B, int64_t av, int64_t bv, uint16_t *__restrict__ dst,
+                                unsigned *__restrict__ zero, int nzero) {
   const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx < nzero) zero[idx] = 0u;
   if (idx >= A * B) return;
   const int64_t a = idx / B, b = idx % B;
   uint16_t v = 0;
@@ -58,10 +64,30 @@ __global__ void relayout_kernel(const uint16_t *__restrict__ src, int64_t lds, b
   dst[idx] = v;
 }
 
+// Cross-workgroup split reduction.  Partials travel through device-coherent
+// accesses (agent-scope stores and loads bypass the per-XCD L2s), so no
+// device-wide cache writeback is needed: a workgroup stores its partials,
+// waits until they are acknowledged, and counts itself in; the one that brings
+// the count to `splits` then reads every split's partials (in split order, so
+// the sum does not depend on which workgroup finishes last).
+QL_DEV void store_partial(float *p, float v) { __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
+QL_DEV float load_partial(const float *p) { return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
+QL_DEV bool last_of_splits(unsigned *cnt, unsigned splits) {
+  __shared__ bool last;
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");  // keeps the partial stores above this point
+  __builtin_amdgcn_s_waitcnt(0);                           // ... and waits until they are acknowledged
+  __syncthreads();
+  if (threadIdx.x == 0) last = atomicAdd(cnt, 1u) == splits - 1;
+  __syncthreads();
+  return last;
+}
+
 // ---------------------------------------------------------------------------
-// Rank-r products.  part[s][m][q] = sum over split s of A[m][k] * Bt[q][k].
-// A wave owns 16 rows and all NT*16 columns; operands come straight from
-// global memory in MFMA fragment order (16 B per lane per K step).
+// Rank-r products (T = X·L1, U = dY·L2^T).  part[s][m][q] = sum over split s
+// of A[m][k] * Bt[q][k].  A wave owns 16 rows and all NT*16 columns; operands
+// come straight from global memory in MFMA fragment order (16 B per lane per
+// K step).  A separate finish pass sums the splits: a split reduction inside
+// this kernel would leave one workgroup per token tile with a serial tail.
 // ---------------------------------------------------------------------------
 template <int NT>
 __global__ __launch_bounds__(256) void skinny_kernel(const uint16_t *__restrict__ A, int64_t lda, int64_t M,
@@ -324,20 +350,39 @@ __global__ __launch_bounds__(kGvThreads) void nf4_gemv_kernel(GemvParams p) {
 }
 
 // ---------------------------------------------------------------------------
-// Adapter gradients: part[s][i][q] = sum over tokens m of split s of
-// P[m][i] * Q[m][q].  Both operands are token-major in HBM; a workgroup
-// transposes a 64-token slab of each into LDS ([i][m] and [q][m]) so the
-// MFMA fragments are 16-byte LDS reads.  Workgroup = 64 values of i, all q.
+// Adapter gradients, both in one launch: tiles [0, a.tiles) compute
+// dL1 = s·X^T·U ([h][r]) and the rest dL2 = s·T^T·dY (stored [r][o]).  Each
+// is part[split][i][q] = sum over the split's tokens m of P[m][i] * Q[m][q];
+// both operands are token-major in HBM, so a workgroup transposes a 64-token
+// slab of each into LDS ([i][m] and [q][m]) and the MFMA fragments become
+// 16-byte LDS reads.  Workgroup = 64 values of i, all q.  The last token split
+// of a tile sums the splits, scales by s and stores the tile.
 // ---------------------------------------------------------------------------
+struct GradProblem {
+  const uint16_t *P;  // [M][ldp], the i index runs along a row
+  int64_t ldp, I;
+  const uint16_t *Q;  // [M][ldq], q < r valid
+  int64_t ldq;
+  float *out;         // [I][r] (trans = false) or [r][I] (trans = true)
+  bool trans;
+  int64_t tiles;      // I / 64
+  int64_t prow;       // first row of this problem in the partial buffer
+};
+
 template <int NT>
-__global__ __launch_bounds__(256) void lora_grad_kernel(const uint16_t *__restrict__ P, int64_t ldp, int64_t I,
-                                                        const uint16_t *__restrict__ Q, int64_t ldq, int rq,
-                                                        int64_t M, int64_t mchunk, float *__restrict__ part) {
+__global__ __launch_bounds__(256) void lora_grad_kernel(GradProblem pa, GradProblem pb, int rq, float s, int64_t M,
+                                                        int64_t mchunk, int64_t prows, float *__restrict__ part,
+                                                        unsigned *__restrict__ cnt) {
   constexpr int RP = NT * 16, LDT = 64 + 8;
   __shared__ __attribute__((aligned(16))) uint16_t Pt[64 * LDT];
   __shared__ __attribute__((aligned(16))) uint16_t Qt[RP * LDT];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int64_t i0 = (int64_t)blockIdx.x * 64;
+  const bool second = blockIdx.x >= pa.tiles;
+  const GradProblem &pr = second ? pb : pa;
+  const int64_t tile = second ? blockIdx.x - pa.tiles : blockIdx.x;
+  const uint16_t *P = pr.P, *Q = pr.Q;
+  const int64_t ldp = pr.ldp, ldq = pr.ldq;
+  const int64_t i0 = tile * 64;
   const int64_t ms = (int64_t)blockIdx.y * mchunk;
   const int64_t me = ms + mchunk < M ? ms + mchunk : M;
   const bool qvec = (ldq % 8) == 0;
@@ -380,26 +425,26 @@ __global__ __launch_bounds__(256) void lora_grad_kernel(const uint16_t *__restri
     }
     __syncthreads();
   }
-  float *out = part + (int64_t)blockIdx.y * I * RP;
+  float *out = part + ((int64_t)blockIdx.y * prows + pr.prow) * RP;
 #pragma unroll
   for (int t = 0; t < NT; ++t)
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
       const int64_t i = i0 + wave * 16 + 4 * (lane >> 4) + v;
-      out[i * RP + t * 16 + (lane & 15)] = acc[t][v];
+      store_partial(out + i * RP + t * 16 + (lane & 15), acc[t][v]);
     }
-}
-
-// dL[i][q] (trans = false, stride r) or dL[q][i] (trans = true, stride I) = s * sum_s part
-__global__ void lora_grad_finish_kernel(const float *__restrict__ part, int S, int64_t I, int RP, int r, float s,
-                                        bool trans, float *__restrict__ out) {
-  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (idx >= I * r) return;
-  int64_t i, q;
-  if (trans) { q = idx / I; i = idx % I; } else { i = idx / r; q = idx % r; }
-  float acc = 0.0f;
-  for (int k = 0; k < S; ++k) acc += part[((int64_t)k * I + i) * RP + q];
-  out[idx] = s * acc;
+  if (!last_of_splits(cnt + blockIdx.x, gridDim.y)) return;
+  const int S = (int)gridDim.y;
+  for (int idx = tid; idx < 64 * rq; idx += 256) {
+    // consecutive threads write consecutive addresses of the stored layout
+    const int il = pr.trans ? idx % 64 : idx / rq;
+    const int q = pr.trans ? idx / 64 : idx % rq;
+    const int64_t i = i0 + il;
+    float sum = 0.0f;
+#pragma unroll 8
+    for (int k = 0; k < S; ++k) sum += load_partial(part + ((int64_t)k * prows + pr.prow + i) * RP + q);
+    pr.out[pr.trans ? (int64_t)q * pr.I + i : i * rq + q] = s * sum;
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -456,8 +501,8 @@ FwdLayout fwd_layout(int64_t M, int64_t h, int64_t o, int r) {
 
 struct BwdLayout {
   int RP16, RP64;
-  Split sk, g1, g2;
-  size_t off_part, off_u, off_su, off_l1p, off_g1, off_g2, total;
+  Split sk, gs;
+  size_t off_part, off_u, off_su, off_l1p, off_g, off_cnt, total;
 };
 
 BwdLayout bwd_layout(int64_t M, int64_t h, int64_t o, int r) {
@@ -466,16 +511,15 @@ BwdLayout bwd_layout(int64_t M, int64_t h, int64_t o, int r) {
   L.RP16 = (int)rup(r, 16);
   L.RP64 = (int)rup(r, 64);
   L.sk = skinny_split(M, o);
-  L.g1 = grad_split(M, h);
-  L.g2 = grad_split(M, o);
+  L.gs = grad_split(M, h + o);
   size_t off = 0;
   auto take = [&](size_t bytes) { size_t at = off; off += rup((int64_t)bytes, 256); return at; };
   L.off_part = take((size_t)L.sk.S * M * L.RP16 * 4);
   L.off_u = take((size_t)M * L.RP16 * 2);
   L.off_su = take((size_t)M * L.RP64 * 2);
   L.off_l1p = take((size_t)h * L.RP64 * 2);
-  L.off_g1 = take((size_t)L.g1.S * h * L.RP16 * 4);
-  L.off_g2 = take((size_t)L.g2.S * o * L.RP16 * 4);
+  L.off_g = take((size_t)L.gs.S * (h + o) * L.RP16 * 4);
+  L.off_cnt = take((size_t)((h + o) / 64) * 4);
   L.total = off;
   return L;
 }
@@ -484,29 +528,68 @@ template <typename T>
 T *at(void *ws, size_t off) { return reinterpret_cast<T *>(reinterpret_cast<char *>(ws) + off); }
 
 void relayout(const uint16_t *src, int64_t lds, bool trans, int64_t A, int64_t B, int64_t av, int64_t bv,
-              uint16_t *dst, hipStream_t st) {
-  const int64_t n = A * B;
-  relayout_kernel<<<(unsigned)cdiv(n, 256), 256, 0, st>>>(src, lds, trans, A, B, av, bv, dst);
+              uint16_t *dst, unsigned *zero, int nzero, hipStream_t st) {
+  const int64_t n = A * B > nzero ? A * B : nzero;
+  relayout_kernel<<<(unsigned)cdiv(n, 256), 256, 0, st>>>(src, lds, trans, A, B, av, bv, dst, zero, nzero);
 }
 
 void skinny(const uint16_t *A, int64_t lda, int64_t M, int64_t K, const uint16_t *Bt, int64_t ldb, int r, int RP16,
-            const Split &sp, float *part, hipStream_t st) {
+            const Split &sp, float *part, float s, uint16_t *out1, int ld1, uint16_t *out2, int ld2,
+            hipStream_t st) {
   dim3 grid((unsigned)cdiv(M, 64), (unsigned)sp.S);
   switch (RP16 / 16) {
 #define QL_SK(NT) case NT: skinny_kernel<NT><<<grid, 256, 0, st>>>(A, lda, M, K, Bt, ldb, r, sp.chunk, part); break;
     QL_SK(1) QL_SK(2) QL_SK(3) QL_SK(4) QL_SK(5) QL_SK(6) QL_SK(7) QL_SK(8)
 #undef QL_SK
   }
+  const int W = ld2 > ld1 ? ld2 : ld1;
+  skinny_finish_kernel<<<(unsigned)cdiv(M * W, 256), 256, 0, st>>>(part, sp.S, M, RP16, r, s, out1, ld1, out2, ld2);
 }
 
-void lora_grad(const uint16_t *P, int64_t ldp, int64_t I, const uint16_t *Q, int64_t ldq, int r, int RP16,
-               int64_t M, const Split &sp, float *part, hipStream_t st) {
-  dim3 grid((unsigned)(I / 64), (unsigned)sp.S);
+void lora_grad(const GradProblem &pa, const GradProblem &pb, int r, float s, int64_t M, int RP16, const Split &sp,
+               float *part, unsigned *cnt, hipStream_t st) {
+  dim3 grid((unsigned)(pa.tiles + pb.tiles), (unsigned)sp.S);
+  const int64_t prows = pa.I + pb.I;
   switch (RP16 / 16) {
-#define QL_LG(NT) case NT: lora_grad_kernel<NT><<<grid, 256, 0, st>>>(P, ldp, I, Q, ldq, r, M, sp.chunk, part); break;
+#define QL_LG(NT)                                                                                                 \
+  case NT:                                                                                                        \
+    lora_grad_kernel<NT><<<grid, 256, 0, st>>>(pa, pb, r, s, M, sp.chunk, prows, part, cnt); \
+    break;
     QL_LG(1) QL_LG(2) QL_LG(3) QL_LG(4) QL_LG(5) QL_LG(6) QL_LG(7) QL_LG(8)
 #undef QL_LG
   }
+}
+
+// Side stream for work that can overlap the fused GEMM on the caller's stream
+// (the adapter gradients in the backward pass).  One per device, created on
+// first use, default priority.  The caller's stream forks to it with an event
+// and joins back with another, so every call stays ordered on the caller's
+// stream.  The lock covers the fork / launch / join enqueue sequence, which
+// also makes reusing the two events across calls safe (a wait captures the
+// event's state when it is enqueued).
+struct SideStream {
+  hipStream_t s = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
+  bool ready = false;
+};
+constexpr int kMaxDevices = 64;
+std::mutex g_side_mu;
+SideStream g_side[kMaxDevices];
+
+SideStream *side_stream_locked() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  SideStream &ss = g_side[dev];
+  if (!ss.ready) {
+    if (hipStreamCreateWithFlags(&ss.s, hipStreamNonBlocking) != hipSuccess) return nullptr;
+    if (hipEventCreateWithFlags(&ss.fork, hipEventDisableTiming) != hipSuccess ||
+        hipEventCreateWithFlags(&ss.join, hipEventDisableTiming) != hipSuccess) {
+      (void)hipGetLastError();
+      return nullptr;
+    }
+    ss.ready = true;
+  }
+  return &ss;
 }
 
 thread_local hipEvent_t t_ev[3][2] = {};
@@ -543,12 +626,10 @@ hipError_t launch_linear_fwd(const LinearArgs &a, const uint16_t *X, const uint1
   if (a.r > 0) {
     // T = X·L1 (rank r): L1 [h][r] -> L1t [RP16][h]
     uint16_t *L1t = at<uint16_t>(ws, L.off_l1t);
-    relayout(L1, a.r, true, L.RP16, a.h, a.r, a.h, L1t, st);
+    relayout(L1, a.r, true, L.RP16, a.h, a.r, a.h, L1t, nullptr, 0, st);
     float *part = at<float>(ws, L.off_part);
-    skinny(X, a.h, a.M, a.h, L1t, a.h, a.r, L.RP16, L.sk, part, st);
     sT = at<uint16_t>(ws, L.off_st);
-    skinny_finish_kernel<<<(unsigned)cdiv(a.M * (L.RP64 > a.r ? L.RP64 : a.r), 256), 256, 0, st>>>(
-        part, L.sk.S, a.M, L.RP16, a.r, a.s, T, a.r, sT, L.RP64);
+    skinny(X, a.h, a.M, a.h, L1t, a.h, a.r, L.RP16, L.sk, part, a.s, T, a.r, sT, L.RP64, st);
   }
   if (a.M <= 16) {
     GemvParams gp{};
@@ -592,26 +673,24 @@ hipError_t launch_linear_bwd(const LinearArgs &a, const uint16_t *X, const uint1
                              void *ws, const Nf4Tables &tab, hipStream_t st) {
   const BwdLayout L = bwd_layout(a.M, a.h, a.o, a.r);
   uint16_t *sU = nullptr, *L1p = nullptr;
+  GradProblem g1{}, g2{};
+  float *gpart = nullptr;
+  unsigned *gcnt = nullptr;
   if (a.r > 0) {
+    unsigned *cnt = at<unsigned>(ws, L.off_cnt);
+    L1p = at<uint16_t>(ws, L.off_l1p);
+    // L1 [h][r] -> [h][RP64] for the dX GEMM's LoRA step; also clears the gradient split counters
+    relayout(L1, a.r, false, a.h, L.RP64, a.h, a.r, L1p, cnt, (int)((a.h + a.o) / 64), st);
     // U = dY·L2^T: Bt = L2 [r][o] is already k-contiguous
     float *part = at<float>(ws, L.off_part);
-    skinny(dY, a.o, a.M, a.o, L2, a.o, a.r, L.RP16, L.sk, part, st);
     uint16_t *U = at<uint16_t>(ws, L.off_u);
     sU = at<uint16_t>(ws, L.off_su);
-    skinny_finish_kernel<<<(unsigned)cdiv(a.M * L.RP64, 256), 256, 0, st>>>(part, L.sk.S, a.M, L.RP16, a.r, a.s, U,
-                                                                           L.RP16, sU, L.RP64);
-    L1p = at<uint16_t>(ws, L.off_l1p);
-    relayout(L1, a.r, false, a.h, L.RP64, a.h, a.r, L1p, st);  // L1 [h][r] -> [h][RP64]
-    // dL1 = s·X^T·U   (P = X [M][h], Q = U [M][RP16])
-    float *g1 = at<float>(ws, L.off_g1);
-    lora_grad(X, a.h, a.h, U, L.RP16, a.r, L.RP16, a.M, L.g1, g1, st);
-    lora_grad_finish_kernel<<<(unsigned)cdiv(a.h * a.r, 256), 256, 0, st>>>(g1, L.g1.S, a.h, L.RP16, a.r, a.s, false,
-                                                                            dL1);
-    // dL2 = s·T^T·dY  (P = dY [M][o], Q = T [M][r]); stored [r][o]
-    float *g2 = at<float>(ws, L.off_g2);
-    lora_grad(dY, a.o, a.o, T, a.r, a.r, L.RP16, a.M, L.g2, g2, st);
-    lora_grad_finish_kernel<<<(unsigned)cdiv(a.o * a.r, 256), 256, 0, st>>>(g2, L.g2.S, a.o, L.RP16, a.r, a.s, true,
-                                                                            dL2);
+    skinny(dY, a.o, a.M, a.o, L2, a.o, a.r, L.RP16, L.sk, part, a.s, U, L.RP16, sU, L.RP64, st);
+    // dL1 = s·X^T·U (P = X [M][h], Q = U [M][RP16]) and dL2 = s·T^T·dY (P = dY [M][o], Q = T [M][r]), stored [r][o]
+    g1 = GradProblem{X, a.h, a.h, U, L.RP16, dL1, false, a.h / 64, 0};
+    g2 = GradProblem{dY, a.o, a.o, T, a.r, dL2, true, a.o / 64, a.h};
+    gpart = at<float>(ws, L.off_g);
+    gcnt = cnt;
   }
   GemmParams gp{};
   gp.A = dY; gp.lda = a.o;
@@ -623,11 +702,33 @@ hipError_t launch_linear_bwd(const LinearArgs &a, const uint16_t *X, const uint1
   gp.M = a.M; gp.N = a.h;
   gp.C = dX; gp.ldc = a.h;
   fill_levels(gp.level, tab);
+  if (a.r == 0) {
+    TimedLaunch tl(1, st);
+    launch_nf4_gemm(gp, true, st);
+    return hipGetLastError();
+  }
+  // The adapter gradients need only U, X, T and dY: they run on the side stream
+  // while the dX GEMM runs on the caller's stream.
+  std::lock_guard<std::mutex> lock(g_side_mu);
+  SideStream *ss = side_stream_locked();
+  hipError_t e = hipSuccess;
+  if (ss) {
+    e = hipEventRecord(ss->fork, st);
+    if (e == hipSuccess) e = hipStreamWaitEvent(ss->s, ss->fork, 0);
+  }
+  if (e != hipSuccess) return e;
+  lora_grad(g1, g2, a.r, a.s, a.M, L.RP16, L.gs, gpart, gcnt, ss ? ss->s : st);
   {
     TimedLaunch tl(1, st);
     launch_nf4_gemm(gp, true, st);
   }
-  return hipGetLastError();
+  e = hipGetLastError();
+  if (ss) {
+    const hipError_t e1 = hipEventRecord(ss->join, ss->s);
+    const hipError_t e2 = e1 == hipSuccess ? hipStreamWaitEvent(st, ss->join, 0) : e1;
+    if (e == hipSuccess) e = e2;
+  }
+  return e;
 }
 
 }  // namespace ql

@@ -11,8 +11,11 @@
  *    allocates, frees or retains them.  Where an entry point needs temporary
  *    device memory the caller passes a workspace sized by qlora_workspace_size().
  *  - `stream` is a hipStream_t (NULL = the default stream).  Every call only
- *    enqueues work on that stream and returns without synchronizing.  Calls on
- *    different streams are safe when their buffers are disjoint.
+ *    enqueues work and returns without synchronizing; all of a call's work is
+ *    ordered on `stream` (qlora_linear_bwd forks part of its work to a
+ *    library-owned stream of the same device and joins it back to `stream`
+ *    with events before returning).  Calls on different streams are safe when
+ *    their buffers are disjoint.
  *  - bf16 tensors are passed as uint16_t bit patterns (bfloat16: 1 sign, 8
  *    exponent, 7 fraction bits).  All matrices are row-major.
  *  - Pointers must be 16-byte aligned unless stated otherwise.

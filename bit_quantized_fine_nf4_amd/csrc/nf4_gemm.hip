@@ -81,7 +81,10 @@ __global__ __launch_bounds__(512) void nf4_gemm_kernel(GemmParams p) {
   constexpr int WTM = BM / 4, WTN = BN / 2, TM = WTM / 32, TN = WTN / 32;
   constexpr int LDA = BK + 8;     // A [m][k]
   constexpr int LDNK = BK + 8;   // B [n][k]
-  constexpr int LDKN = BN + 16;  // B [k][n]
+  // B [k][n]: a row stride of 12 banks (mod 64) keeps both the decode stores
+  // (2 rows x 8 units per 16 lanes) and the transposing fragment reads
+  // (4 rows x 4 column chunks per 16 lanes) free of bank conflicts
+  constexpr int LDKN = BN + 24;
   constexpr int B_ELEMS = cmax(BN * LDNK, BK * LDKN);
   constexpr int STAGE = BM * LDA + B_ELEMS;  // elements per LDS stage (A then B)
   constexpr int UW = 64 * BN / NT;  // weights per decode unit: every thread decodes one unit
@@ -233,17 +236,26 @@ __global__ __launch_bounds__(512) void nf4_gemm_kernel(GemmParams p) {
       for (int j = 0; j < TN; ++j) bf[j] = tr_pair(b0 + j * 32, b0 + 4 * LDKN + j * 32);
     }
   };
-  auto mma_kk = [&](int buf, bool kn, int kk) {
+  // Fragments of MFMA group kk (A: TM, B: TN 16-byte pieces per lane).
+  struct Frags {
+    u32x4 a[TM], b[TN];
+  };
+  auto load_frags = [&](int buf, bool kn, int kk, Frags &F) {
     const uint16_t *as = sm + buf * STAGE + (wm * WTM + l32) * LDA + 32 * g;
-    const uint16_t *bs = bsm + buf * STAGE;
-    u32x4 af[TM], bf[TN];
 #pragma unroll
-    for (int i = 0; i < TM; ++i) af[i] = *reinterpret_cast<const u32x4 *>(as + i * 32 * LDA + 8 * kk);
-    load_bfrag(bs, kn, kk, bf);
+    for (int i = 0; i < TM; ++i) F.a[i] = *reinterpret_cast<const u32x4 *>(as + i * 32 * LDA + 8 * kk);
+    load_bfrag(bsm + buf * STAGE, kn, kk, F.b);
+  };
+  auto mma_frags = [&](const Frags &F) {
 #pragma unroll
     for (int i = 0; i < TM; ++i)
 #pragma unroll
-      for (int j = 0; j < TN; ++j) acc[i][j] = mfma32(af[i], bf[j], acc[i][j]);
+      for (int j = 0; j < TN; ++j) acc[i][j] = mfma32(F.a[i], F.b[j], acc[i][j]);
+  };
+  auto mma_kk = [&](int buf, bool kn, int kk) {
+    Frags F;
+    load_frags(buf, kn, kk, F);
+    mma_frags(F);
   };
   auto mma_step = [&](int buf, bool kn) {
 #pragma unroll
@@ -268,15 +280,33 @@ __global__ __launch_bounds__(512) void nf4_gemm_kernel(GemmParams p) {
   __syncthreads();
   auto step = [&](int kt, Stage &Snext, Stage &Sfree) {
     // Snext holds step kt+1; Sfree is refilled with step kt+2 (past the last step
-    // these loads and writes are harmless and unused).
+    // these loads and writes are harmless and unused).  The fragments of MFMA
+    // group kk+1 are read while group kk's MFMAs run.
     const int buf = kt & 1;
     load_stage(kt + 2, Sfree);
     __builtin_amdgcn_sched_barrier(0);
+    if constexpr (TM * TN > 4) {  // 256x256 tiles: no registers to spare for a second fragment set
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      mma_kk(buf, TRANS, kk);
-      put_part(buf ^ 1, kk, Snext, ah);
+      for (int kk = 0; kk < 4; ++kk) {
+        mma_kk(buf, TRANS, kk);
+        put_part(buf ^ 1, kk, Snext, ah);
+      }
+      __syncthreads();
+      return;
     }
+    Frags F0, F1;
+    load_frags(buf, TRANS, 0, F0);
+    load_frags(buf, TRANS, 1, F1);
+    mma_frags(F0);
+    put_part(buf ^ 1, 0, Snext, ah);
+    load_frags(buf, TRANS, 2, F0);
+    mma_frags(F1);
+    put_part(buf ^ 1, 1, Snext, ah);
+    load_frags(buf, TRANS, 3, F1);
+    mma_frags(F0);
+    put_part(buf ^ 1, 2, Snext, ah);
+    mma_frags(F1);
+    put_part(buf ^ 1, 3, Snext, ah);
     __syncthreads();
   };
   // Uniform two-step body (the same loads in flight on every path); an odd

@@ -17,7 +17,9 @@ timed with events recorded by the library right around that kernel's launch.
 
 Other workloads (not the default line): --workload codec (quantize + double
 quant + dequantize of 4e9 bf16 weights), gemv (few-token forward on an
-8192 x 28672 weight at 1, 4 and 16 tokens), small (1024 x 1024, 16 tokens).
+8192 x 28672 weight at 1, 4 and 16 tokens), small (1024 x 1024, 16 tokens),
+merge (the r = 64 adapters of a LLaMA-65B-shaped block's seven linears merged
+into bf16 weights, then merged and re-quantized to NF4).
 """
 from __future__ import annotations
 
@@ -42,7 +44,7 @@ def parse_args():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="attn_proj", choices=["attn_proj", "codec", "gemv", "small"])
+    ap.add_argument("--workload", default="attn_proj", choices=["attn_proj", "codec", "gemv", "small", "merge"])
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the CPU oracle timing")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="target CPU work for the oracle baseline")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -383,6 +385,65 @@ def bench_small(args, torch, nf4, wl):
             "roofline": None}
 
 
+def merge_bytes(h, o, r, out_bytes_per_weight):
+    """Algorithmic HBM bytes of one merge: codes, int8 scales, second-level scales,
+    the mean, both factors once, and the output."""
+    n = h * o
+    nb = n // 64
+    return n // 2 + nb + 4 * ((nb + 255) // 256) + 4 + 2 * r * (h + o) + int(n * out_bytes_per_weight)
+
+
+def bench_merge(args, torch, nf4, wl):
+    dev = "cuda:0"
+    c = wl.C5
+    Ws, Ls, outs, reqs = [], [], [], []
+    for li, ls in enumerate(c.linears):
+        Ws.append(nf4.quantize_weight(wl.base_weight(c, li).to(dev)))
+        Ls.append(tuple(t.to(dev) for t in wl.lora_factors(c, li)))
+        outs.append(torch.empty(ls.o, ls.h, dtype=torch.bfloat16, device=dev))
+        n = ls.h * ls.o
+        reqs.append((torch.empty(n // 2, dtype=torch.uint8, device=dev),
+                     torch.empty(n // 64, dtype=torch.float32, device=dev)))
+    E = torch.cuda.Event
+    nl = len(c.linears)
+
+    def step(ev=None):
+        rec = (lambda i: ev[i].record()) if ev is not None else (lambda i: None)
+        rec(0)
+        for li, ls in enumerate(c.linears):
+            nf4.qlora_merge_adapter(Ws[li], Ls[li][0], Ls[li][1], ls.s, torch.bfloat16, out=outs[li])
+        rec(1)
+        for li, ls in enumerate(c.linears):
+            nf4.qlora_merge_requantize(Ws[li], Ls[li][0], Ls[li][1], ls.s, reqs[li][0], reqs[li][1])
+        rec(2)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[E(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = [statistics.mean(e[i].elapsed_time(e[i + 1]) for e in evs) for i in range(2)]
+    b_bf16 = sum(merge_bytes(ls.h, ls.o, ls.r, 2.0) for ls in c.linears)
+    b_req = sum(merge_bytes(ls.h, ls.o, ls.r, 0.5 + 4 / 64) for ls in c.linears)
+    gbs = [b_bf16 / ms[0] / 1e6, b_req / ms[1] / 1e6]
+    ms_step = wall * 1e3 / args.steps
+    return {"metric": METRIC, "value": round((b_bf16 + b_req) / (ms_step * 1e-3) / 1e9, 2), "unit": "GB/s",
+            "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+            "config": {"workload": "merge_" + c.name, "linears": nl, "weights": sum(ls.h * ls.o for ls in c.linears),
+                       "step": "merge to bf16 + merge and re-quantize, all seven linears"},
+            "roofline": {"bound": "hbm", "achieved": round(gbs[0], 2), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                         "frac": round(gbs[0] / PEAK_HBM_GBS, 4), "traffic": None, "kernel": "merge_kernel<bf16>"},
+            "stages": {"merge_bf16": {"ms": round(ms[0], 4), "GB/s": round(gbs[0], 2),
+                                      "frac_hbm": round(gbs[0] / PEAK_HBM_GBS, 4), "bytes": b_bf16},
+                       "merge_requantize": {"ms": round(ms[1], 4), "GB/s": round(gbs[1], 2),
+                                            "frac_hbm": round(gbs[1] / PEAK_HBM_GBS, 4), "bytes": b_req}}}
+
+
 def main():
     args = parse_args()
     if args.gpus != 1:
@@ -401,7 +462,8 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
-    fn = {"attn_proj": bench_attn_proj, "codec": bench_codec, "gemv": bench_gemv, "small": bench_small}[args.workload]
+    fn = {"attn_proj": bench_attn_proj, "codec": bench_codec, "gemv": bench_gemv, "small": bench_small,
+          "merge": bench_merge}[args.workload]
     line = fn(args, torch, nf4, wl)
     if args.workload == "attn_proj" and not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_oracle_attn_proj(wl, args.cpu_seconds)

@@ -23,8 +23,8 @@ QLORA_OP_DOUBLE_QUANT, QLORA_OP_LINEAR_FWD, QLORA_OP_LINEAR_BWD = 0, 1, 2
 BLOCK, CHUNK, MAX_RANK = 64, 256, 128
 
 EXPORTED = ("qlora_quantize", "qlora_double_quant", "qlora_dequantize", "qlora_linear_fwd",
-            "qlora_linear_bwd", "qlora_workspace_size", "qlora_status_string", "qlora_nf4_levels",
-            "qlora_set_timing_events")
+            "qlora_linear_bwd", "qlora_merge_adapter", "qlora_merge_requantize", "qlora_workspace_size",
+            "qlora_status_string", "qlora_nf4_levels", "qlora_set_timing_events")
 
 
 class QloraError(RuntimeError):
@@ -50,6 +50,8 @@ def _load():
     L.qlora_linear_fwd.argtypes = [ctypes.POINTER(NF4WeightT), vp, i64, vp, vp, i32, f32, vp, vp, vp, sz, vp]
     L.qlora_linear_bwd.argtypes = [ctypes.POINTER(NF4WeightT), vp, vp, vp, i64, vp, vp, i32, f32, vp, vp, vp,
                                    vp, sz, vp]
+    L.qlora_merge_adapter.argtypes = [ctypes.POINTER(NF4WeightT), vp, vp, i32, f32, vp, st, vp]
+    L.qlora_merge_requantize.argtypes = [ctypes.POINTER(NF4WeightT), vp, vp, i32, f32, vp, vp, vp]
     L.qlora_workspace_size.argtypes = [st, i64, i64, i64, i32, ctypes.POINTER(sz)]
     L.qlora_status_string.argtypes = [st]
     L.qlora_status_string.restype = ctypes.c_char_p
@@ -130,7 +132,7 @@ class NF4Weight:
 
 
 # ---------------------------------------------------------------------------
-# The five entry points
+# The entry points
 # ---------------------------------------------------------------------------
 
 def qlora_quantize(w: torch.Tensor, codes: Optional[torch.Tensor] = None,
@@ -209,6 +211,37 @@ def qlora_linear_fwd(W: NF4Weight, X: torch.Tensor, L1: Optional[torch.Tensor], 
                                 _ptr(workspace), 0 if workspace is None else workspace.numel(), _stream(dev)),
            "qlora_linear_fwd")
     return Y, T
+
+
+def qlora_merge_adapter(W: NF4Weight, L1: Optional[torch.Tensor], L2: Optional[torch.Tensor], s: float,
+                        out_dtype: torch.dtype = torch.float32, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Dense merged weight W' = W_hat + s·L1·L2 in [o][h] storage (float32 or bf16)."""
+    _dev_check(L1, L2)
+    r = 0 if L1 is None else L1.shape[1]
+    dt = {torch.float32: QLORA_F32, torch.bfloat16: QLORA_BF16}[out_dtype]
+    if out is None:
+        out = torch.empty(W.o, W.h, dtype=out_dtype, device=W.codes.device)
+    wt = W.as_ctypes()
+    _check(lib.qlora_merge_adapter(ctypes.byref(wt), _ptr(L1), _ptr(L2), r, float(s), _ptr(out), dt,
+                                   _stream(W.codes.device)), "qlora_merge_adapter")
+    return out
+
+
+def qlora_merge_requantize(W: NF4Weight, L1: Optional[torch.Tensor], L2: Optional[torch.Tensor], s: float,
+                           codes: Optional[torch.Tensor] = None, absmax: Optional[torch.Tensor] = None):
+    """NF4 codes and float32 block absmax of the merged weight -> (codes, absmax)."""
+    _dev_check(L1, L2)
+    r = 0 if L1 is None else L1.shape[1]
+    dev = W.codes.device
+    n = W.h * W.o
+    if codes is None:
+        codes = torch.empty(n // 2, dtype=torch.uint8, device=dev)
+    if absmax is None:
+        absmax = torch.empty(n // BLOCK, dtype=torch.float32, device=dev)
+    wt = W.as_ctypes()
+    _check(lib.qlora_merge_requantize(ctypes.byref(wt), _ptr(L1), _ptr(L2), r, float(s), _ptr(codes), _ptr(absmax),
+                                      _stream(dev)), "qlora_merge_requantize")
+    return codes, absmax
 
 
 def qlora_linear_bwd(W: NF4Weight, X: Optional[torch.Tensor], T: Optional[torch.Tensor], dY: torch.Tensor,

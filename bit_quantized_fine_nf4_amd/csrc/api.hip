@@ -47,6 +47,32 @@ qlora_status_t qlora_nf4_levels(float out[16]) {
   return QLORA_OK;
 }
 
+qlora_status_t qlora_merge_adapter(const qlora_nf4_weight_t *W, const uint16_t *L1, const uint16_t *L2, int32_t r,
+                                   float s, void *out, qlora_dtype_t out_dtype, void *stream) {
+  if (!valid_weight(W) || !out || r < 0 || r > QLORA_MAX_RANK) return QLORA_ERR_INVALID_VALUE;
+  if (out_dtype != QLORA_F32 && out_dtype != QLORA_BF16) return QLORA_ERR_INVALID_VALUE;
+  if (r > 0 && (!L1 || !L2 || !aligned(L1, 16) || !aligned(L2, 16))) return QLORA_ERR_INVALID_VALUE;
+  if (!aligned(out, 16)) return QLORA_ERR_INVALID_VALUE;
+  const Nf4Tables *t = host_tables();
+  if (!t) return QLORA_ERR_INTERNAL;
+  (void)hipGetLastError();
+  const MergeArgs m{W->codes, W->qabsmax, W->scale2, W->mean, W->h, W->o, L1, L2, r, s, out, nullptr, nullptr};
+  return launch_status(launch_merge(m, out_dtype == QLORA_BF16 ? 1 : 0, *t, reinterpret_cast<hipStream_t>(stream)));
+}
+
+qlora_status_t qlora_merge_requantize(const qlora_nf4_weight_t *W, const uint16_t *L1, const uint16_t *L2,
+                                      int32_t r, float s, uint8_t *codes_out, float *absmax_out, void *stream) {
+  if (!valid_weight(W) || !codes_out || !absmax_out || r < 0 || r > QLORA_MAX_RANK) return QLORA_ERR_INVALID_VALUE;
+  if (r > 0 && (!L1 || !L2 || !aligned(L1, 16) || !aligned(L2, 16))) return QLORA_ERR_INVALID_VALUE;
+  if (!aligned(codes_out, 8) || !aligned(absmax_out, 4)) return QLORA_ERR_INVALID_VALUE;
+  const Nf4Tables *t = host_tables();
+  if (!t) return QLORA_ERR_INTERNAL;
+  (void)hipGetLastError();
+  const MergeArgs m{W->codes, W->qabsmax, W->scale2, W->mean, W->h, W->o, L1, L2, r, s, nullptr, codes_out,
+                    absmax_out};
+  return launch_status(launch_merge(m, 2, *t, reinterpret_cast<hipStream_t>(stream)));
+}
+
 qlora_status_t qlora_set_timing_events(int32_t kernel, void *start, void *stop) {
   if (kernel < 0 || kernel > 2) return QLORA_ERR_INVALID_VALUE;
   set_timing_events(kernel, reinterpret_cast<hipEvent_t>(start), reinterpret_cast<hipEvent_t>(stop));

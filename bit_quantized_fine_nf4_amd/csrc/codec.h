@@ -14,4 +14,21 @@ hipError_t launch_dequantize(const uint8_t *codes, const int8_t *qabsmax, const 
                              const float *mean, int64_t n, void *out, bool bf16, const Nf4Tables &tab,
                              hipStream_t st);
 
+// Adapter merge W' = W_hat + s·L1·L2 ([o][h] storage); mode 0: float32 out,
+// 1: bf16 out, 2: NF4 codes_out / absmax_out of W'.
+struct MergeArgs {
+  const uint8_t *codes;
+  const int8_t *qabsmax;
+  const float *scale2;
+  const float *mean;
+  int64_t h, o;
+  const uint16_t *L1, *L2;
+  int r;
+  float s;
+  void *out;
+  uint8_t *codes_out;
+  float *absmax_out;
+};
+hipError_t launch_merge(const MergeArgs &m, int mode, const Nf4Tables &tab, hipStream_t st);
+
 }  // namespace ql

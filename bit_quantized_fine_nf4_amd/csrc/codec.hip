@@ -76,6 +76,43 @@ QL_DEV uint32_t exact_code(float x, const Nf4Tables &t) {
   return c;
 }
 
+// NF4 codes of 8 consecutive weights of one block whose largest magnitude is a
+// (already reduced over the block): element i in byte i/2, even i in the high
+// nibble.  Fast path: y = 16 * x + 16 indexes a bucket of the threshold table;
+// anything inside a bucket's guard band (or a scale outside [2^-100, 2^100])
+// takes the exact IEEE divide-and-compare path, so the result always equals
+// the nearest-level rule on fp32(w / a).
+QL_DEV uint32_t encode8(const float (&v)[8], float a, const EncBucket *lut, const Nf4Tables &tab) {
+  bool slow = !(a >= 0x1p-100f && a <= 0x1p100f);
+  const float r16 = 16.0f * __builtin_amdgcn_rcpf(a);
+  uint32_t word = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    float y = __builtin_fmaf(v[i], r16, 16.0f);
+    uint32_t idx = (uint32_t)(int32_t)y;
+    idx = idx > 32u ? 32u : idx;
+    const EncBucket e = lut[idx];
+    const bool up = y > e.hi;
+    slow |= (y > e.lo) && !up;
+    uint32_t c = e.base + (up ? 1u : 0u);
+    word |= c << (8 * (i >> 1) + ((i & 1) ? 0 : 4));
+  }
+  if (slow) {
+    word = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      float x = a > 0.0f ? v[i] / a : 0.0f;
+      word |= exact_code(x, tab) << (8 * (i >> 1) + ((i & 1) ? 0 : 4));
+    }
+  }
+  return word;
+}
+
+QL_DEV float absmax8(const float (&v)[8]) {
+  return fmaxf(fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3]))),
+               fmaxf(fmaxf(fabsf(v[4]), fabsf(v[5])), fmaxf(fabsf(v[6]), fabsf(v[7]))));
+}
+
 template <bool kBf16>
 __global__ __launch_bounds__(256) void quantize_kernel(const void *__restrict__ w, int64_t n,
                                                        uint8_t *__restrict__ codes,
@@ -90,33 +127,8 @@ __global__ __launch_bounds__(256) void quantize_kernel(const void *__restrict__ 
   const int64_t ncodes = (n + 1) >> 1;
 
   auto encode = [&](const float (&v)[8], int64_t e0) {
-    float m = fmaxf(fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3]))),
-                    fmaxf(fmaxf(fabsf(v[4]), fabsf(v[5])), fmaxf(fabsf(v[6]), fabsf(v[7]))));
-    const float a = dpp_max8(m);
-
-    bool slow = !(a >= 0x1p-100f && a <= 0x1p100f);
-    const float r16 = 16.0f * __builtin_amdgcn_rcpf(a);
-    uint32_t word = 0;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      float y = __builtin_fmaf(v[i], r16, 16.0f);
-      uint32_t idx = (uint32_t)(int32_t)y;
-      idx = idx > 32u ? 32u : idx;
-      const EncBucket e = lut[idx];
-      const bool up = y > e.hi;
-      slow |= (y > e.lo) && !up;
-      uint32_t c = e.base + (up ? 1u : 0u);
-      // element i goes to byte i/2; even i in the high nibble
-      word |= c << (8 * (i >> 1) + ((i & 1) ? 0 : 4));
-    }
-    if (slow) {
-      word = 0;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        float x = a > 0.0f ? v[i] / a : 0.0f;
-        word |= exact_code(x, tab) << (8 * (i >> 1) + ((i & 1) ? 0 : 4));
-      }
-    }
+    const float a = dpp_max8(absmax8(v));
+    uint32_t word = encode8(v, a, lut, tab);
     const int64_t c0 = e0 >> 1;  // first byte index of this lane
     if (e0 + 8 <= n) {
       *reinterpret_cast<uint32_t *>(codes + c0) = word;
@@ -140,6 +152,213 @@ __global__ __launch_bounds__(256) void quantize_kernel(const void *__restrict__ 
     load8<kBf16>(w, e1, n, v1);
     encode(v0, e0);
     if (base + stride < n) encode(v1, e1);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Adapter merge ([TT] §11 "Saving, Loading, and Merging QLoRA Adapters"): the
+// base is dequantized to a wider precision, the LoRA update added, and the
+// result optionally quantized again.  Stored [o][h] entry (n, k) of
+//   W' = W_hat + s * L1·L2            (W_hat h x o, L1 h x r, L2 r x o)
+// is fp32(w_hat + fp32(s * P)) with w_hat = fp32(level * a_hat) exactly as
+// qlora_dequantize computes it and P = sum_q L1[k][q] * L2[q][n] from bf16
+// MFMAs with float32 accumulation.
+//
+// A workgroup owns a strip of 64 rows n and walks a range of 64-column tiles
+// along k (each tile column range is one quantization block of every row).
+// Wave w owns rows 16w..16w+15 of the strip: its MFMA B operand (L2 transposed,
+// 16 rows x r) is built once in LDS and then held in registers for the whole
+// walk.  Per tile, the 64 x r slice of L1 (contiguous in memory) goes through
+// a double-buffered LDS tile as the A operand, four 16x16x32 MFMA tiles per
+// wave produce P for 64 k x 16 n, and the A rows are permuted so that lane
+// (i, g) ends up holding P for row n = 16w + i at the 16 consecutive columns
+// 16g..16g+15: the accumulators feed the epilogue directly.  Each lane then
+// decodes its 16 codes (8 bytes), adds s * P, and stores 16 weights (fp32 /
+// bf16), or re-encodes them with the encoder of qlora_quantize (block absmax
+// over the 4 lanes of the row, nearest level, packed codes).  The next tile's
+// L1 slice and the next codes / scales are loaded one tile ahead; one
+// barrier per tile.
+// ---------------------------------------------------------------------------
+struct MergeParams {
+  const uint8_t *codes;
+  const int8_t *qabsmax;
+  const float *scale2;
+  const float *mean;
+  int64_t h, o;
+  const uint16_t *L1;  // [h][r]
+  const uint16_t *L2;  // [r][o]
+  int r;
+  float s;
+  int kper;             // k tiles per workgroup
+  void *out;            // modes 0 / 1: [o][h] float32 / bf16
+  uint8_t *codes_out;   // mode 2
+  float *absmax_out;    // mode 2
+};
+
+QL_DEV f32x4 mfma16x32(u32x4 a, u32x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c,
+                                                 0, 0, 0);
+}
+
+// Codes and scales of one lane's 16 weights of one tile.
+struct MergeIn {
+  u32x2 cw;
+  int qa;
+  float s2;
+};
+
+// MODE 0: float32 W'; 1: bf16 W'; 2: NF4 codes + absmax of W'.  RQ = ceil(r / 32) (0: no adapter).
+template <int MODE, int RQ>
+__global__ __launch_bounds__(256) void merge_kernel(MergeParams p, Nf4Tables tab) {
+  constexpr int RP = 32 * (RQ > 0 ? RQ : 1);
+  constexpr int LDR = RP + 8;                   // bf16 row stride of an LDS tile
+  constexpr int TILE = RQ > 0 ? 64 * LDR : 8;   // one buffer
+  __shared__ __attribute__((aligned(16))) uint16_t tile[2 * TILE];
+  __shared__ f32x2 lv2[256];
+  __shared__ EncBucket lut[kBuckets];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int i = lane & 15, g = lane >> 4;
+  lv2[tid] = f32x2{tab.level[tid >> 4], tab.level[tid & 15]};
+  if (MODE == 2 && tid < kBuckets) lut[tid] = tab.bucket[tid];
+
+  const int64_t h = p.h, nblk = h >> 6;
+  const int64_t row = (int64_t)blockIdx.x * 64 + 16 * wave + i;
+  const int ta = (int)blockIdx.y * p.kper;
+  const int tb = (int)(ta + p.kper < nblk ? ta + p.kper : nblk);
+  const int r = p.r;
+  const float mu = *p.mean;
+
+  auto load_in = [&](int kt) {
+    MergeIn m;
+    const int64_t blk = row * nblk + kt;
+    m.cw = *reinterpret_cast<const u32x2 *>(p.codes + ((row * h + (int64_t)kt * 64 + 16 * g) >> 1));
+    m.qa = p.qabsmax[blk];
+    m.s2 = p.scale2[blk / kChunk];
+    return m;
+  };
+
+  // L1 slice of tile kt: 64 rows x r bf16 contiguous, 8r chunks of 16 bytes;
+  // thread tid takes chunks tid + 256 m (clamped: surplus lanes reload the last chunk).
+  u32x4 lr[RQ > 0 ? RQ : 1];
+  const int nch = 8 * r;
+  auto load_l1 = [&](int kt) {
+    const uint16_t *base = p.L1 + (int64_t)kt * 64 * r;
+#pragma unroll
+    for (int m = 0; m < RQ; ++m) {
+      int c = tid + 256 * m;
+      c = c < nch ? c : nch - 1;
+      lr[m] = *reinterpret_cast<const u32x4 *>(base + 8 * c);
+    }
+  };
+  int soff[RQ > 0 ? RQ : 1];  // LDS offset of each chunk when r is a multiple of 8
+#pragma unroll
+  for (int m = 0; m < RQ; ++m) {
+    const int c = tid + 256 * m, k = (8 * c) / r;
+    soff[m] = k * LDR + 8 * c - k * r;
+  }
+  auto store_l1 = [&](uint16_t *buf) {
+#pragma unroll
+    for (int m = 0; m < RQ; ++m) {
+      const int c = tid + 256 * m;
+      if (c < nch) {
+        if ((r & 7) == 0) {
+          *reinterpret_cast<u32x4 *>(&buf[soff[m]]) = lr[m];
+        } else {
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            const int e = 8 * c + j, k = e / r, q = e - k * r;
+            buf[k * LDR + q] = (uint16_t)(lr[m][j >> 1] >> (16 * (j & 1)));
+          }
+        }
+      }
+    }
+  };
+
+  u32x4 bfr[RQ > 0 ? RQ : 1];
+  if (RQ > 0) {
+    // zero the padding columns q in [r, RP) of both buffers; stage L2^T of the strip in buffer 1
+    for (int idx = tid; idx < 2 * 64 * (RP - r); idx += 256) {
+      const int row2 = idx / (RP - r), q = r + idx % (RP - r);
+      tile[(row2 >> 6) * TILE + (row2 & 63) * LDR + q] = 0;
+    }
+    const int64_t n0 = (int64_t)blockIdx.x * 64;
+    for (int c = tid; c < nch; c += 256) {
+      const int q = c >> 3, cn = c & 7;
+      const u32x4 d = *reinterpret_cast<const u32x4 *>(p.L2 + (int64_t)q * p.o + n0 + 8 * cn);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) tile[TILE + (8 * cn + j) * LDR + q] = (uint16_t)(d[j >> 1] >> (16 * (j & 1)));
+    }
+    load_l1(ta);
+  }
+  MergeIn cur = load_in(ta);
+  __syncthreads();
+  if (RQ > 0) {
+#pragma unroll
+    for (int qq = 0; qq < RQ; ++qq)
+      bfr[qq] = *reinterpret_cast<const u32x4 *>(&tile[TILE + (16 * wave + i) * LDR + 32 * qq + 8 * g]);
+    store_l1(tile);
+  }
+  __syncthreads();
+
+  for (int kt = ta; kt < tb; ++kt) {
+    const int j = kt - ta;
+    const int kn = kt + 1 < tb ? kt + 1 : kt;
+    if (RQ > 0) load_l1(kn);
+    const MergeIn nxt = load_in(kn);
+
+    float v[16];
+    {
+      const float ah = scale_hat((int8_t)cur.qa, cur.s2, mu);
+#pragma unroll
+      for (int b = 0; b < 8; ++b) {
+        const f32x2 l = lv2[(cur.cw[b >> 2] >> (8 * (b & 3))) & 0xFF];
+        v[2 * b] = l[0] * ah;
+        v[2 * b + 1] = l[1] * ah;
+      }
+    }
+    if (RQ > 0) {
+      const uint16_t *buf = tile + (j & 1) * TILE;
+      // tile t, A row m = i -> column 16 (i >> 2) + 4 t + (i & 3); lane (i, g) receives
+      // P at columns 16 g + 4 t + v, v = 0..3, of row 16 wave + i
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        f32x4 acc = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+        const int ka = 16 * (i >> 2) + 4 * t + (i & 3);
+#pragma unroll
+        for (int qq = 0; qq < RQ; ++qq) {
+          const u32x4 a = *reinterpret_cast<const u32x4 *>(&buf[ka * LDR + 32 * qq + 8 * g]);
+          acc = mfma16x32(a, bfr[qq], acc);
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float tt = p.s * acc[e];
+          v[4 * t + e] = v[4 * t + e] + tt;
+        }
+      }
+    }
+    const int64_t e0 = row * h + (int64_t)kt * 64 + 16 * g;
+    if (MODE == 0) {
+      f32x4 *o = reinterpret_cast<f32x4 *>(reinterpret_cast<float *>(p.out) + e0);
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) o[q4] = f32x4{v[4 * q4], v[4 * q4 + 1], v[4 * q4 + 2], v[4 * q4 + 3]};
+    } else if (MODE == 1) {
+      u32x4 *o = reinterpret_cast<u32x4 *>(reinterpret_cast<uint16_t *>(p.out) + e0);
+      o[0] = u32x4{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]),
+                   pack_bf16x2(v[6], v[7])};
+      o[1] = u32x4{pack_bf16x2(v[8], v[9]), pack_bf16x2(v[10], v[11]), pack_bf16x2(v[12], v[13]),
+                   pack_bf16x2(v[14], v[15])};
+    } else {
+      const float (&v0)[8] = *reinterpret_cast<const float (*)[8]>(&v[0]);
+      const float (&v1)[8] = *reinterpret_cast<const float (*)[8]>(&v[8]);
+      float a = fmaxf(absmax8(v0), absmax8(v1));
+      a = fmaxf(a, __shfl_xor(a, 16));
+      a = fmaxf(a, __shfl_xor(a, 32));
+      *reinterpret_cast<u32x2 *>(p.codes_out + (e0 >> 1)) = u32x2{encode8(v0, a, lut, tab), encode8(v1, a, lut, tab)};
+      if (g == 0) p.absmax_out[row * nblk + kt] = a;
+    }
+    if (RQ > 0) store_l1(tile + ((j + 1) & 1) * TILE);
+    __syncthreads();
+    cur = nxt;
   }
 }
 
@@ -483,6 +702,36 @@ hipError_t launch_double_quant(const float *absmax, int64_t nb, int8_t *qabsmax,
   dq_bins_kernel<<<grid, 256, 0, st>>>(absmax, nb, bins, mean);
   const int64_t nch = (nb + kChunk - 1) / kChunk;
   dq_chunks_kernel<<<(int)((nch + 3) / 4), 256, 0, st>>>(absmax, nb, mean, qabsmax, scale2);
+  return hipGetLastError();
+}
+
+template <int MODE>
+static void launch_merge_rq(int rq, dim3 grid, const MergeParams &p, const Nf4Tables &tab, hipStream_t st) {
+  switch (rq) {
+    case 0: merge_kernel<MODE, 0><<<grid, 256, 0, st>>>(p, tab); break;
+    case 1: merge_kernel<MODE, 1><<<grid, 256, 0, st>>>(p, tab); break;
+    case 2: merge_kernel<MODE, 2><<<grid, 256, 0, st>>>(p, tab); break;
+    case 3: merge_kernel<MODE, 3><<<grid, 256, 0, st>>>(p, tab); break;
+    default: merge_kernel<MODE, 4><<<grid, 256, 0, st>>>(p, tab); break;
+  }
+}
+
+hipError_t launch_merge(const MergeArgs &m, int mode, const Nf4Tables &tab, hipStream_t st) {
+  MergeParams p{};
+  p.codes = m.codes; p.qabsmax = m.qabsmax; p.scale2 = m.scale2; p.mean = m.mean;
+  p.h = m.h; p.o = m.o; p.L1 = m.L1; p.L2 = m.L2; p.r = m.r; p.s = m.s;
+  p.out = m.out; p.codes_out = m.codes_out; p.absmax_out = m.absmax_out;
+  // about 2048 workgroups (8 per CU): strips of 64 rows x a range of k tiles
+  const int64_t strips = m.o / 64, ktiles = m.h / 64;
+  int64_t ksplit = (2048 + strips - 1) / strips;
+  ksplit = ksplit < 1 ? 1 : (ksplit > ktiles ? ktiles : ksplit);
+  p.kper = (int)((ktiles + ksplit - 1) / ksplit);
+  ksplit = (ktiles + p.kper - 1) / p.kper;
+  const dim3 grid((unsigned)strips, (unsigned)ksplit);
+  const int rq = (m.r + 31) / 32;
+  if (mode == 0) launch_merge_rq<0>(rq, grid, p, tab, st);
+  else if (mode == 1) launch_merge_rq<1>(rq, grid, p, tab, st);
+  else launch_merge_rq<2>(rq, grid, p, tab, st);
   return hipGetLastError();
 }
 

@@ -154,6 +154,34 @@ qlora_status_t qlora_linear_bwd(const qlora_nf4_weight_t *W, const uint16_t *X, 
                                 int32_t r, float s, uint16_t *dX, float *dL1, float *dL2,
                                 void *workspace, size_t ws_bytes, void *stream);
 
+/*
+ * qlora_merge_adapter — merge a trained adapter into the frozen base
+ * ([TT] §11 "Saving, Loading, and Merging QLoRA Adapters": dequantize the base
+ * to a wider precision and add the LoRA update; [GO] "What it added up to").
+ *  W' = W_hat + s·L1·L2 in W's [o][h] storage: entry (n, k) =
+ *       fp32(w_hat + fp32(s * P)),  P = sum_q L1[k][q] * L2[q][n]
+ *  where w_hat is qlora_dequantize's float32 value and P comes from bf16
+ *  products with float32 accumulation (summation order unspecified).
+ *  L1 [h][r] bf16, L2 [r][o] bf16, 16-byte aligned (may be NULL when r = 0),
+ *       0 <= r <= 128.
+ *  out  [o][h] float32 or bf16 (round to nearest even of the float32 value);
+ *       16-byte aligned.
+ */
+qlora_status_t qlora_merge_adapter(const qlora_nf4_weight_t *W, const uint16_t *L1, const uint16_t *L2,
+                                   int32_t r, float s, void *out, qlora_dtype_t out_dtype, void *stream);
+
+/*
+ * qlora_merge_requantize — the merge followed by NF4 re-quantization in one
+ * pass ([TT] §11: merging and quantizing again adds a second quantization
+ * error).  codes_out (h*o/2 bytes) and absmax_out (h*o/64 float32) are what
+ * qlora_quantize returns for the float32 merged weight qlora_merge_adapter
+ * computes; follow with qlora_double_quant(absmax_out, ...) to obtain the new
+ * weight's int8 scales.  codes_out 8-byte and absmax_out 4-byte aligned; they must not
+ * alias W's buffers.
+ */
+qlora_status_t qlora_merge_requantize(const qlora_nf4_weight_t *W, const uint16_t *L1, const uint16_t *L2,
+                                      int32_t r, float s, uint8_t *codes_out, float *absmax_out, void *stream);
+
 /* Workspace bytes an entry point needs (always a multiple of 256; may be 0). */
 qlora_status_t qlora_workspace_size(qlora_op_t op, int64_t a, int64_t b, int64_t c, int32_t r,
                                     size_t *bytes);

@@ -24,5 +24,5 @@ from .nf4 import (  # noqa: F401
     int8_absmax_quantize, exact_mean_f32, double_quant, scale_reconstruct, dequantize,
     dequantize_no_dq, f32_to_bf16_bits, bf16_bits_to_f32, unpack_codes,
 )
-from .linear import linear_fwd, linear_bwd, dequantized_weight  # noqa: F401
+from .linear import linear_fwd, linear_bwd, dequantized_weight, merged_weight  # noqa: F401
 from .ledger import storage_bits_per_weight, storage_bytes, lora_param_count  # noqa: F401

@@ -65,3 +65,26 @@ def linear_bwd(w_oh: np.ndarray, x: np.ndarray, dy: np.ndarray, l1, l2, s: float
     dL1 = s * (X.T @ U)
     dL2 = s * (T.T @ dY)
     return dX, dL1, dL2
+
+
+def merged_weight(packed, qabsmax, scale2, mean, h: int, o: int, l1, l2, s: float) -> np.ndarray:
+    """float32 [o][h] merge of the adapter into the base: W' = W_hat + s * L1 L2.
+
+    [TT] §11 "Saving, Loading, and Merging QLoRA Adapters": the base is
+    dequantized to a wider precision, the LoRA update added, and the result may
+    be quantized again (adding another quantization error); [GO] "What it
+    added up to" notes that trained adapters fit the quantized base.  In the
+    pages' orientation W is h x o, so the stored [o][h] entry (n, k) gets
+    s * sum_q L1[k][q] L2[q][n].  float32 steps: each product of two bf16
+    values is exact in float32; the r products are summed in float32 in
+    ascending q; then fp32(s * P) and fp32(W_hat + that).
+    """
+    wh = dequantized_weight(packed, qabsmax, scale2, mean, h, o)
+    if l1 is None or np.asarray(l1).shape[1] == 0:
+        return wh.copy()
+    L1 = np.asarray(l1, dtype=np.float32)      # [h][r]
+    L2 = np.asarray(l2, dtype=np.float32)      # [r][o]
+    P = np.zeros((o, h), dtype=np.float32)
+    for q in range(L1.shape[1]):
+        P = P + np.outer(L2[q, :], L1[:, q]).astype(np.float32)
+    return wh + np.float32(s) * P

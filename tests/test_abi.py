@@ -122,3 +122,25 @@ def test_linear_rejects_bad_arguments():
     assert b(dL1=None) == INV
     assert b(M=-1) == INV
     assert b(W=weight(h=64, o=65)) == INV
+
+
+def test_merge_rejects_bad_arguments():
+    mg, rq = lib.qlora_merge_adapter, lib.qlora_merge_requantize
+    ok = weight()
+    m = lambda W=ok, L1=FAKE, L2=FAKE, r=8, out=FAKE, dt=0: mg(ctypes.byref(W), L1, L2, r, 2.0, out, dt, None)
+    assert m(weight(h=100)) == INV
+    assert m(weight(codes=ODD)) == INV
+    assert m(out=None) == INV
+    assert m(out=ODD) == INV
+    assert m(dt=2) == INV
+    assert m(r=-1) == INV
+    assert m(r=129) == INV
+    assert m(L1=None) == INV
+    assert m(L2=ODD) == INV
+    q = lambda W=ok, L1=FAKE, L2=FAKE, r=8, c=FAKE, a=FAKE: rq(ctypes.byref(W), L1, L2, r, 2.0, c, a, None)
+    assert q(c=None) == INV
+    assert q(a=None) == INV
+    assert q(c=ODD) == INV
+    assert q(L2=None) == INV
+    assert q(r=200) == INV
+    assert q(weight(o=32)) == INV

@@ -6,6 +6,8 @@
 
 #include "codec.h"
 
+#include <type_traits>
+
 namespace ql {
 
 // ---------------------------------------------------------------------------
@@ -164,20 +166,20 @@ __global__ __launch_bounds__(256) void quantize_kernel(const void *__restrict__ 
 // qlora_dequantize computes it and P = sum_q L1[k][q] * L2[q][n] from bf16
 // MFMAs with float32 accumulation.
 //
-// A workgroup owns a strip of 64 rows n and walks a range of 64-column tiles
-// along k (each tile column range is one quantization block of every row).
-// Wave w owns rows 16w..16w+15 of the strip: its MFMA B operand (L2 transposed,
-// 16 rows x r) is built once in LDS and then held in registers for the whole
-// walk.  Per tile, the 64 x r slice of L1 (contiguous in memory) goes through
-// a double-buffered LDS tile as the A operand, four 16x16x32 MFMA tiles per
-// wave produce P for 64 k x 16 n, and the A rows are permuted so that lane
-// (i, g) ends up holding P for row n = 16w + i at the 16 consecutive columns
-// 16g..16g+15: the accumulators feed the epilogue directly.  Each lane then
-// decodes its 16 codes (8 bytes), adds s * P, and stores 16 weights (fp32 /
-// bf16), or re-encodes them with the encoder of qlora_quantize (block absmax
-// over the 4 lanes of the row, nearest level, packed codes).  The next tile's
-// L1 slice and the next codes / scales are loaded one tile ahead; one
-// barrier per tile.
+// A workgroup owns a strip of 64 rows n and walks a range of 64-column k
+// tiles (one quantization block of every row per tile).  Wave w owns rows
+// 16w..16w+15: its MFMA B operand (L2 transposed, 16 rows x r) is built once
+// in LDS and then held in registers.  Per tile, the 64 x r slice of L1
+// (contiguous in memory) goes through a double-buffered LDS tile as the A
+// operand shared by the four waves, and the A rows are permuted so that lane
+// (i, g) ends up holding P for row 16w + i at the 16 consecutive columns
+// 16g..16g+15: the 16x16x32 MFMA accumulators feed the epilogue directly.
+// The strip's codes and rebuilt block scales come through LDS in chunks of
+// kMergeChunk tiles (one contiguous run per row: short per-row reads spread
+// over many rows cost HBM efficiency).  Each lane decodes its 16 codes, adds
+// s * P, and stores 16 weights (fp32 / bf16), or re-encodes them with the
+// encoder of qlora_quantize (block absmax over the row's 4 lanes, nearest
+// level, packed codes).  One barrier per tile.
 // ---------------------------------------------------------------------------
 struct MergeParams {
   const uint8_t *codes;
@@ -195,25 +197,33 @@ struct MergeParams {
   float *absmax_out;    // mode 2
 };
 
+constexpr int kMergeChunk = 4;                    // tiles per staged chunk of codes
+constexpr int kMergeRowBytes = kMergeChunk * 32;  // code bytes per row per chunk
+
 QL_DEV f32x4 mfma16x32(u32x4 a, u32x4 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c,
                                                  0, 0, 0);
 }
 
-// Codes and scales of one lane's 16 weights of one tile.
-struct MergeIn {
-  u32x2 cw;
-  int qa;
-  float s2;
-};
-
 // MODE 0: float32 W'; 1: bf16 W'; 2: NF4 codes + absmax of W'.  RQ = ceil(r / 32) (0: no adapter).
 template <int MODE, int RQ>
 __global__ __launch_bounds__(256) void merge_kernel(MergeParams p, Nf4Tables tab) {
   constexpr int RP = 32 * (RQ > 0 ? RQ : 1);
-  constexpr int LDR = RP + 8;                   // bf16 row stride of an LDS tile
-  constexpr int TILE = RQ > 0 ? 64 * LDR : 8;   // one buffer
+  // LDS tile: row k holds q = 0..RP-1 with its 16-byte pieces permuted, piece c stored at
+  // c ^ swz(k).  The MFMA A reads of one 16-lane pass take rows {a + 16 b + 4 t : a, b < 4}
+  // and one piece each; the permutation puts those 16 reads on 16 distinct 4-bank groups
+  // (for RP = 96 the 48-bank row stride alone does).
+  constexpr int LDR = RP;
+  constexpr int TILE = RQ > 0 ? 64 * LDR : 8;  // one buffer
+  auto swz = [](int k) {
+    return RP == 32 ? (k >> 4) & 3
+         : RP == 64 ? ((k >> 1) & 1) | (((k >> 4) & 3) << 1)
+         : RP == 128 ? (k & 3) | (((k >> 4) & 3) << 2) : 0;
+  };
+  auto radr = [&](int k, int q) { return k * LDR + 8 * ((q >> 3) ^ swz(k)) + (q & 7); };
   __shared__ __attribute__((aligned(16))) uint16_t tile[2 * TILE];
+  __shared__ __attribute__((aligned(16))) uint8_t cbuf[2][64][kMergeRowBytes + 16];  // codes
+  __shared__ float abuf[2][64][kMergeChunk + 1];                                      // a_hat
   __shared__ f32x2 lv2[256];
   __shared__ EncBucket lut[kBuckets];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -222,52 +232,75 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeParams p, Nf4Tables tab
   if (MODE == 2 && tid < kBuckets) lut[tid] = tab.bucket[tid];
 
   const int64_t h = p.h, nblk = h >> 6;
-  const int64_t row = (int64_t)blockIdx.x * 64 + 16 * wave + i;
+  const int64_t n0 = (int64_t)blockIdx.x * 64;
+  const int64_t row = n0 + 16 * wave + i;
   const int ta = (int)blockIdx.y * p.kper;
   const int tb = (int)(ta + p.kper < nblk ? ta + p.kper : nblk);
   const int r = p.r;
   const float mu = *p.mean;
 
-  auto load_in = [&](int kt) {
-    MergeIn m;
-    const int64_t blk = row * nblk + kt;
-    m.cw = *reinterpret_cast<const u32x2 *>(p.codes + ((row * h + (int64_t)kt * 64 + 16 * g) >> 1));
-    m.qa = p.qabsmax[blk];
-    m.s2 = p.scale2[blk / kChunk];
-    return m;
+  // Chunk staging: thread t copies bytes [32 (t & 3), +32) of row t >> 2's chunk of codes
+  // (clamped into the valid part of a short last chunk), and rebuilds a_hat for the
+  // (row, tile) pair t of the chunk.
+  static_assert(kMergeRowBytes == 4 * 32 && 64 * kMergeChunk == 256, "staging split");
+  struct Stage {
+    u32x4 c[2];
+    int qa;
+    float s2;
+  };
+  auto stage_load = [&](int c0, Stage &st) {
+    const int nt = tb - c0 < kMergeChunk ? tb - c0 : kMergeChunk;
+    const uint8_t *base = p.codes + (((n0 + (tid >> 2)) * h + (int64_t)c0 * 64) >> 1);
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      int off = 32 * (tid & 3) + 16 * u;
+      off = off < 32 * nt - 16 ? off : 32 * nt - 16;
+      st.c[u] = *reinterpret_cast<const u32x4 *>(base + off);
+    }
+    int tt = tid % kMergeChunk;
+    tt = tt < nt ? tt : nt - 1;
+    const int64_t blk = (n0 + tid / kMergeChunk) * nblk + c0 + tt;
+    st.qa = p.qabsmax[blk];
+    st.s2 = p.scale2[blk / kChunk];
+  };
+  auto stage_store = [&](int buf, const Stage &st) {
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+      *reinterpret_cast<u32x4 *>(&cbuf[buf][tid >> 2][32 * (tid & 3) + 16 * u]) = st.c[u];
+    abuf[buf][tid / kMergeChunk][tid % kMergeChunk] = scale_hat((int8_t)st.qa, st.s2, mu);
   };
 
-  // L1 slice of tile kt: 64 rows x r bf16 contiguous, 8r chunks of 16 bytes;
-  // thread tid takes chunks tid + 256 m (clamped: surplus lanes reload the last chunk).
+  // L1 slice of tile kt: 64 rows x r bf16 contiguous, 8r pieces of 16 bytes;
+  // thread tid takes pieces tid + 256 m (clamped: surplus lanes reload the last piece).
   u32x4 lr[RQ > 0 ? RQ : 1];
-  const int nch = 8 * r;
+  const int npc = 8 * r;
   auto load_l1 = [&](int kt) {
     const uint16_t *base = p.L1 + (int64_t)kt * 64 * r;
 #pragma unroll
     for (int m = 0; m < RQ; ++m) {
       int c = tid + 256 * m;
-      c = c < nch ? c : nch - 1;
+      c = c < npc ? c : npc - 1;
       lr[m] = *reinterpret_cast<const u32x4 *>(base + 8 * c);
     }
   };
-  int soff[RQ > 0 ? RQ : 1];  // LDS offset of each chunk when r is a multiple of 8
+  int soff[RQ > 0 ? RQ : 1];  // LDS offset of each piece when r is a multiple of 8
 #pragma unroll
   for (int m = 0; m < RQ; ++m) {
     const int c = tid + 256 * m, k = (8 * c) / r;
-    soff[m] = k * LDR + 8 * c - k * r;
+    soff[m] = radr(k, 8 * c - k * r);
   }
   auto store_l1 = [&](uint16_t *buf) {
 #pragma unroll
     for (int m = 0; m < RQ; ++m) {
       const int c = tid + 256 * m;
-      if (c < nch) {
+      if (c < npc) {
         if ((r & 7) == 0) {
           *reinterpret_cast<u32x4 *>(&buf[soff[m]]) = lr[m];
         } else {
 #pragma unroll
           for (int j = 0; j < 8; ++j) {
             const int e = 8 * c + j, k = e / r, q = e - k * r;
-            buf[k * LDR + q] = (uint16_t)(lr[m][j >> 1] >> (16 * (j & 1)));
+            buf[radr(k, q)] = (uint16_t)(lr[m][j >> 1] >> (16 * (j & 1)));
           }
         }
       }
@@ -279,45 +312,43 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeParams p, Nf4Tables tab
     // zero the padding columns q in [r, RP) of both buffers; stage L2^T of the strip in buffer 1
     for (int idx = tid; idx < 2 * 64 * (RP - r); idx += 256) {
       const int row2 = idx / (RP - r), q = r + idx % (RP - r);
-      tile[(row2 >> 6) * TILE + (row2 & 63) * LDR + q] = 0;
+      tile[(row2 >> 6) * TILE + radr(row2 & 63, q)] = 0;
     }
-    const int64_t n0 = (int64_t)blockIdx.x * 64;
-    for (int c = tid; c < nch; c += 256) {
+    for (int c = tid; c < npc; c += 256) {
       const int q = c >> 3, cn = c & 7;
       const u32x4 d = *reinterpret_cast<const u32x4 *>(p.L2 + (int64_t)q * p.o + n0 + 8 * cn);
 #pragma unroll
-      for (int j = 0; j < 8; ++j) tile[TILE + (8 * cn + j) * LDR + q] = (uint16_t)(d[j >> 1] >> (16 * (j & 1)));
+      for (int j = 0; j < 8; ++j) tile[TILE + radr(8 * cn + j, q)] = (uint16_t)(d[j >> 1] >> (16 * (j & 1)));
     }
-    load_l1(ta);
   }
-  MergeIn cur = load_in(ta);
+  Stage st;
+  stage_load(ta, st);
+  if (RQ > 0) load_l1(ta);
+  stage_store(0, st);
   __syncthreads();
   if (RQ > 0) {
 #pragma unroll
     for (int qq = 0; qq < RQ; ++qq)
-      bfr[qq] = *reinterpret_cast<const u32x4 *>(&tile[TILE + (16 * wave + i) * LDR + 32 * qq + 8 * g]);
+      bfr[qq] = *reinterpret_cast<const u32x4 *>(&tile[TILE + radr(16 * wave + i, 32 * qq + 8 * g)]);
     store_l1(tile);
   }
   __syncthreads();
 
-  for (int kt = ta; kt < tb; ++kt) {
-    const int j = kt - ta;
-    const int kn = kt + 1 < tb ? kt + 1 : kt;
-    if (RQ > 0) load_l1(kn);
-    const MergeIn nxt = load_in(kn);
-
+  // One tile: its L1 slice is in LDS tile buffer `tbuf`, its codes in chunk buffer `cb`
+  // at tile offset `ct`.
+  auto step = [&](const int kt, const int tbuf, const int cb, const int ct) {
+    if (RQ > 0) load_l1(kt + 1 < tb ? kt + 1 : kt);
+    const u32x2 cw = *reinterpret_cast<const u32x2 *>(&cbuf[cb][16 * wave + i][32 * ct + 8 * g]);
+    const float ah = abuf[cb][16 * wave + i][ct];
     float v[16];
-    {
-      const float ah = scale_hat((int8_t)cur.qa, cur.s2, mu);
 #pragma unroll
-      for (int b = 0; b < 8; ++b) {
-        const f32x2 l = lv2[(cur.cw[b >> 2] >> (8 * (b & 3))) & 0xFF];
-        v[2 * b] = l[0] * ah;
-        v[2 * b + 1] = l[1] * ah;
-      }
+    for (int b = 0; b < 8; ++b) {
+      const f32x2 l = lv2[(cw[b >> 2] >> (8 * (b & 3))) & 0xFF];
+      v[2 * b] = l[0] * ah;
+      v[2 * b + 1] = l[1] * ah;
     }
     if (RQ > 0) {
-      const uint16_t *buf = tile + (j & 1) * TILE;
+      const uint16_t *buf = tile + tbuf * TILE;
       // tile t, A row m = i -> column 16 (i >> 2) + 4 t + (i & 3); lane (i, g) receives
       // P at columns 16 g + 4 t + v, v = 0..3, of row 16 wave + i
 #pragma unroll
@@ -326,7 +357,7 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeParams p, Nf4Tables tab
         const int ka = 16 * (i >> 2) + 4 * t + (i & 3);
 #pragma unroll
         for (int qq = 0; qq < RQ; ++qq) {
-          const u32x4 a = *reinterpret_cast<const u32x4 *>(&buf[ka * LDR + 32 * qq + 8 * g]);
+          const u32x4 a = *reinterpret_cast<const u32x4 *>(&buf[radr(ka, 32 * qq + 8 * g)]);
           acc = mfma16x32(a, bfr[qq], acc);
         }
 #pragma unroll
@@ -354,11 +385,22 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeParams p, Nf4Tables tab
       a = fmaxf(a, __shfl_xor(a, 16));
       a = fmaxf(a, __shfl_xor(a, 32));
       *reinterpret_cast<u32x2 *>(p.codes_out + (e0 >> 1)) = u32x2{encode8(v0, a, lut, tab), encode8(v1, a, lut, tab)};
-      if (g == 0) p.absmax_out[row * nblk + kt] = a;
+      p.absmax_out[row * nblk + kt] = a;  // the row's 4 lanes store the same value (no branch)
     }
-    if (RQ > 0) store_l1(tile + ((j + 1) & 1) * TILE);
-    __syncthreads();
-    cur = nxt;
+    if (RQ > 0) store_l1(tile + (1 - tbuf) * TILE);
+  };
+
+  int j = 0;
+  for (int c0 = ta; c0 < tb; c0 += kMergeChunk) {
+    const int cb = ((c0 - ta) / kMergeChunk) & 1;
+    const int ce = c0 + kMergeChunk < tb ? c0 + kMergeChunk : tb;
+    const bool more = ce < tb;
+    if (more) stage_load(ce, st);
+    for (int kt = c0; kt < ce; ++kt, ++j) {
+      step(kt, j & 1, cb, kt - c0);
+      if (more && kt + 1 == ce) stage_store(cb ^ 1, st);
+      __syncthreads();
+    }
   }
 }
 
@@ -721,7 +763,7 @@ hipError_t launch_merge(const MergeArgs &m, int mode, const Nf4Tables &tab, hipS
   p.codes = m.codes; p.qabsmax = m.qabsmax; p.scale2 = m.scale2; p.mean = m.mean;
   p.h = m.h; p.o = m.o; p.L1 = m.L1; p.L2 = m.L2; p.r = m.r; p.s = m.s;
   p.out = m.out; p.codes_out = m.codes_out; p.absmax_out = m.absmax_out;
-  // about 2048 workgroups (8 per CU): strips of 64 rows x a range of k tiles
+  // about 2048 workgroups: strips of 64 rows x a range of k tiles
   const int64_t strips = m.o / 64, ktiles = m.h / 64;
   int64_t ksplit = (2048 + strips - 1) / strips;
   ksplit = ksplit < 1 ? 1 : (ksplit > ktiles ? ktiles : ksplit);

@@ -19,7 +19,9 @@ Other workloads (not the default line): --workload codec (quantize + double
 quant + dequantize of 4e9 bf16 weights), gemv (few-token forward on an
 8192 x 28672 weight at 1, 4 and 16 tokens), small (1024 x 1024, 16 tokens),
 merge (the r = 64 adapters of a LLaMA-65B-shaped block's seven linears merged
-into bf16 weights, then merged and re-quantized to NF4).
+into bf16 weights, then merged and re-quantized to NF4), adamw (one AdamW step
+on those seven adapters' 10.0 M parameters, moments in HBM, then with the
+moments in pinned host memory).
 """
 from __future__ import annotations
 
@@ -44,7 +46,7 @@ def parse_args():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="attn_proj", choices=["attn_proj", "codec", "gemv", "small", "merge"])
+    ap.add_argument("--workload", default="attn_proj", choices=["attn_proj", "codec", "gemv", "small", "merge", "adamw"])
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the CPU oracle timing")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="target CPU work for the oracle baseline")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -444,6 +446,51 @@ def bench_merge(args, torch, nf4, wl):
                                             "frac_hbm": round(gbs[1] / PEAK_HBM_GBS, 4), "bytes": b_req}}}
 
 
+def bench_adamw(args, torch, nf4, wl):
+    dev = "cuda:0"
+    c = wl.C5
+    n = sum(ls.r * (ls.h + ls.o) for ls in c.linears)  # L1 and L2 of every linear, flat
+    g = torch.Generator(device=dev).manual_seed(0)
+    # three independent copies of (p, g, m, v, bf16 p), 540 MB, used in turn: more than the
+    # 256 MB Infinity Cache, so every step streams from HBM
+    copies = [(torch.randn(n, device=dev, generator=g) * 0.01, torch.randn(n, device=dev, generator=g) * 1e-3,
+               torch.zeros(n, device=dev), torch.zeros(n, device=dev),
+               torch.empty(n, dtype=torch.bfloat16, device=dev)) for _ in range(3)]
+    mh = torch.zeros(n, pin_memory=True)
+    vh = torch.zeros(n, pin_memory=True)
+    hp = dict(lr=2e-4, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.01)
+    E = torch.cuda.Event
+    bytes_step = n * (4 * 4 + 3 * 4 + 2)  # read p, g, m, v; write p, m, v and the bf16 copy
+    res = {}
+    for name in ("hbm", "host_state"):
+        def args_for(i):
+            p, grad, m, v, pbf = copies[i % 3]
+            return (p, grad, m, v, pbf) if name == "hbm" else (p, grad, mh, vh, pbf)
+        for t in range(1, args.warmup + 1):
+            p, grad, M, V, pbf = args_for(t)
+            nf4.qlora_adamw_step(p, grad, M, V, t, param_bf16=pbf, **hp)
+        torch.cuda.synchronize()
+        ev = [(E(enable_timing=True), E(enable_timing=True)) for _ in range(args.steps)]
+        for i in range(args.steps):
+            p, grad, M, V, pbf = args_for(i)
+            ev[i][0].record()
+            nf4.qlora_adamw_step(p, grad, M, V, args.warmup + 1 + i, param_bf16=pbf, **hp)
+            ev[i][1].record()
+        torch.cuda.synchronize()
+        ms = statistics.median(a.elapsed_time(b) for a, b in ev)
+        res[name] = {"ms": round(ms, 5), "GB/s": round(bytes_step / ms / 1e6, 2),
+                     "frac_hbm": round(bytes_step / ms / 1e6 / PEAK_HBM_GBS, 4)}
+    h = res["hbm"]
+    return {"metric": METRIC, "value": h["GB/s"], "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+            "warmup": args.warmup, "ms_per_step": h["ms"], "higher_is_better": True, "scaling": "weak",
+            "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+            "config": {"workload": "adamw_" + c.name, "params": n, "state": "float32 m, v", "copies": 3,
+                       "step": "one AdamW step on all seven adapters (flat), bf16 copy written"},
+            "roofline": {"bound": "hbm", "achieved": h["GB/s"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                         "frac": h["frac_hbm"], "traffic": None, "kernel": "adamw_kernel"},
+            "stages": res}
+
+
 def main():
     args = parse_args()
     if args.gpus != 1:
@@ -463,7 +510,7 @@ def main():
         torch.cuda.synchronize()
         del src, dst
     fn = {"attn_proj": bench_attn_proj, "codec": bench_codec, "gemv": bench_gemv, "small": bench_small,
-          "merge": bench_merge}[args.workload]
+          "merge": bench_merge, "adamw": bench_adamw}[args.workload]
     line = fn(args, torch, nf4, wl)
     if args.workload == "attn_proj" and not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_oracle_attn_proj(wl, args.cpu_seconds)

@@ -23,7 +23,8 @@ QLORA_OP_DOUBLE_QUANT, QLORA_OP_LINEAR_FWD, QLORA_OP_LINEAR_BWD = 0, 1, 2
 BLOCK, CHUNK, MAX_RANK = 64, 256, 128
 
 EXPORTED = ("qlora_quantize", "qlora_double_quant", "qlora_dequantize", "qlora_linear_fwd",
-            "qlora_linear_bwd", "qlora_merge_adapter", "qlora_merge_requantize", "qlora_workspace_size",
+            "qlora_linear_bwd", "qlora_merge_adapter", "qlora_merge_requantize", "qlora_adamw_step",
+            "qlora_workspace_size",
             "qlora_status_string", "qlora_nf4_levels", "qlora_set_timing_events")
 
 
@@ -52,6 +53,7 @@ def _load():
                                    vp, sz, vp]
     L.qlora_merge_adapter.argtypes = [ctypes.POINTER(NF4WeightT), vp, vp, i32, f32, vp, st, vp]
     L.qlora_merge_requantize.argtypes = [ctypes.POINTER(NF4WeightT), vp, vp, i32, f32, vp, vp, vp]
+    L.qlora_adamw_step.argtypes = [vp, vp, vp, vp, i64, i64, f32, f32, f32, f32, f32, vp, vp]
     L.qlora_workspace_size.argtypes = [st, i64, i64, i64, i32, ctypes.POINTER(sz)]
     L.qlora_status_string.argtypes = [st]
     L.qlora_status_string.restype = ctypes.c_char_p
@@ -242,6 +244,31 @@ def qlora_merge_requantize(W: NF4Weight, L1: Optional[torch.Tensor], L2: Optiona
     _check(lib.qlora_merge_requantize(ctypes.byref(wt), _ptr(L1), _ptr(L2), r, float(s), _ptr(codes), _ptr(absmax),
                                       _stream(dev)), "qlora_merge_requantize")
     return codes, absmax
+
+
+def qlora_adamw_step(param: torch.Tensor, grad: torch.Tensor, exp_avg: torch.Tensor, exp_avg_sq: torch.Tensor,
+                     step: int, lr: float, beta1: float = 0.9, beta2: float = 0.999, eps: float = 1e-8,
+                     weight_decay: float = 0.0, param_bf16: Optional[torch.Tensor] = None,
+                     device=None) -> None:
+    """AdamW step on float32 `param` (in place, with its moments).  Each tensor is a
+    contiguous float32 GPU tensor or a pinned host tensor (optimizer state kept in CPU RAM);
+    `device` names the GPU whose current stream runs the step (default: param's, else cuda:0)."""
+    ts = (param, grad, exp_avg, exp_avg_sq)
+    for t in ts + (param_bf16,):
+        if t is None:
+            continue
+        if not t.is_contiguous() or not (t.is_cuda or t.is_pinned()):
+            raise ValueError("tensors must be contiguous, on the GPU or in pinned host memory")
+    if any(t.dtype != torch.float32 for t in ts) or (param_bf16 is not None and param_bf16.dtype != torch.bfloat16):
+        raise ValueError("param, grad and moments are float32; param_bf16 is bf16")
+    n = param.numel()
+    if any(t.numel() != n for t in ts[1:]) or (param_bf16 is not None and param_bf16.numel() != n):
+        raise ValueError("all arrays must have param's size")
+    if device is None:
+        device = param.device if param.is_cuda else torch.device("cuda:0")
+    _check(lib.qlora_adamw_step(_ptr(param), _ptr(grad), _ptr(exp_avg), _ptr(exp_avg_sq), n, int(step), float(lr),
+                                float(beta1), float(beta2), float(eps), float(weight_decay), _ptr(param_bf16),
+                                _stream(device)), "qlora_adamw_step")
 
 
 def qlora_linear_bwd(W: NF4Weight, X: Optional[torch.Tensor], T: Optional[torch.Tensor], dY: torch.Tensor,

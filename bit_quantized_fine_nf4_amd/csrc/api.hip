@@ -5,6 +5,9 @@
 #include "../../include/qlora_nf4.h"
 #include "codec.h"
 #include "linear.h"
+#include "optim.h"
+
+#include <cmath>
 
 using namespace ql;
 
@@ -71,6 +74,21 @@ qlora_status_t qlora_merge_requantize(const qlora_nf4_weight_t *W, const uint16_
   const MergeArgs m{W->codes, W->qabsmax, W->scale2, W->mean, W->h, W->o, L1, L2, r, s, nullptr, codes_out,
                     absmax_out};
   return launch_status(launch_merge(m, 2, *t, reinterpret_cast<hipStream_t>(stream)));
+}
+
+qlora_status_t qlora_adamw_step(float *param, const float *grad, float *exp_avg, float *exp_avg_sq, int64_t n,
+                                int64_t step, float lr, float beta1, float beta2, float eps, float weight_decay,
+                                uint16_t *param_bf16, void *stream) {
+  if (n < 1 || step < 1 || !param || !grad || !exp_avg || !exp_avg_sq) return QLORA_ERR_INVALID_VALUE;
+  if (!aligned(param, 16) || !aligned(grad, 16) || !aligned(exp_avg, 16) || !aligned(exp_avg_sq, 16))
+    return QLORA_ERR_INVALID_VALUE;
+  if (param_bf16 && !aligned(param_bf16, 8)) return QLORA_ERR_INVALID_VALUE;
+  if (!(beta1 >= 0.0f && beta1 < 1.0f) || !(beta2 >= 0.0f && beta2 < 1.0f)) return QLORA_ERR_INVALID_VALUE;
+  if (!(eps > 0.0f) || !std::isfinite(eps) || !(lr >= 0.0f) || !std::isfinite(lr)) return QLORA_ERR_INVALID_VALUE;
+  if (!(weight_decay >= 0.0f) || !std::isfinite(weight_decay)) return QLORA_ERR_INVALID_VALUE;
+  (void)hipGetLastError();
+  const AdamwArgs a{param, grad, exp_avg, exp_avg_sq, param_bf16, n, step, lr, beta1, beta2, eps, weight_decay};
+  return launch_status(launch_adamw(a, reinterpret_cast<hipStream_t>(stream)));
 }
 
 qlora_status_t qlora_set_timing_events(int32_t kernel, void *start, void *stop) {

@@ -182,6 +182,31 @@ qlora_status_t qlora_merge_adapter(const qlora_nf4_weight_t *W, const uint16_t *
 qlora_status_t qlora_merge_requantize(const qlora_nf4_weight_t *W, const uint16_t *L1, const uint16_t *L2,
                                       int32_t r, float s, uint8_t *codes_out, float *absmax_out, void *stream);
 
+/*
+ * qlora_adamw_step — one optimizer step on adapter parameters ([TT] §4 "One
+ * QLoRA Training Step, End to End": only the adapters are updated; the update
+ * itself is not written out on the pages, so this is AdamW with decoupled
+ * weight decay, Loshchilov and Hutter).  Elementwise over n float32 values:
+ *   p <- p * (1 - lr*wd)
+ *   m <- beta1*m + (1 - beta1)*g          v <- beta2*v + (1 - beta2)*g*g
+ *   p <- p - lr/(1 - beta1^t) * m / (sqrt(v)/sqrt(1 - beta2^t) + eps)
+ *  param      float32 master values, updated in place (e.g. L1 then L2, flat)
+ *  grad       float32 gradients (qlora_linear_bwd's dL1 / dL2)
+ *  exp_avg, exp_avg_sq   float32 first / second moments, updated in place;
+ *             start at 0 before step 1.  Like param and grad they may live in
+ *             device memory or in pinned host memory allocated with
+ *             hipHostMalloc (optimizer state kept in CPU RAM, [TT] §7 "Paged
+ *             Optimizers"; the kernel then reads and writes it over the link).
+ *  step       t, 1-based.   0 <= beta1, beta2 < 1;  eps > 0;  lr, wd >= 0.
+ *  param_bf16 optional (may be NULL): receives bf16(p) (round to nearest even),
+ *             the copy the linear layer consumes.
+ *  param, grad, exp_avg, exp_avg_sq 16-byte aligned, param_bf16 8-byte aligned;
+ *  no two of the arrays may overlap.
+ */
+qlora_status_t qlora_adamw_step(float *param, const float *grad, float *exp_avg, float *exp_avg_sq, int64_t n,
+                                int64_t step, float lr, float beta1, float beta2, float eps, float weight_decay,
+                                uint16_t *param_bf16, void *stream);
+
 /* Workspace bytes an entry point needs (always a multiple of 256; may be 0). */
 qlora_status_t qlora_workspace_size(qlora_op_t op, int64_t a, int64_t b, int64_t c, int32_t r,
                                     size_t *bytes);

@@ -144,3 +144,20 @@ def test_merge_rejects_bad_arguments():
     assert q(L2=None) == INV
     assert q(r=200) == INV
     assert q(weight(o=32)) == INV
+
+
+def test_adamw_rejects_bad_arguments():
+    ad = lib.qlora_adamw_step
+    a = lambda p=FAKE, g=FAKE, m=FAKE, v=FAKE, n=10, t=1, lr=1e-3, b1=0.9, b2=0.999, eps=1e-8, wd=0.0, bf=None: \
+        ad(p, g, m, v, n, t, lr, b1, b2, eps, wd, bf, None)
+    assert a(n=0) == INV
+    assert a(t=0) == INV
+    assert a(p=None) == INV
+    assert a(v=None) == INV
+    assert a(g=ODD) == INV
+    assert a(bf=ODD) == INV
+    assert a(b1=1.0) == INV
+    assert a(b2=-0.1) == INV
+    assert a(eps=0.0) == INV
+    assert a(lr=-1.0) == INV
+    assert a(wd=float("nan")) == INV

@@ -21,7 +21,9 @@ quant + dequantize of 4e9 bf16 weights), gemv (few-token forward on an
 merge (the r = 64 adapters of a LLaMA-65B-shaped block's seven linears merged
 into bf16 weights, then merged and re-quantized to NF4), adamw (one AdamW step
 on those seven adapters' 10.0 M parameters, moments in HBM, then with the
-moments in pinned host memory).
+moments in pinned host memory), codebooks (NF4 / INT4 / FP4 with and without
+double quantization: reconstruction MSE on 2^26 N(0, 1) and Student-t(4)
+weights, and quantize + dequantize throughput per codebook).
 """
 from __future__ import annotations
 
@@ -46,7 +48,7 @@ def parse_args():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="attn_proj", choices=["attn_proj", "codec", "gemv", "small", "merge", "adamw"])
+    ap.add_argument("--workload", default="attn_proj", choices=["attn_proj", "codec", "gemv", "small", "merge", "adamw", "codebooks"])
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the CPU oracle timing")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="target CPU work for the oracle baseline")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -491,6 +493,64 @@ def bench_adamw(args, torch, nf4, wl):
             "stages": res}
 
 
+def bench_codebooks(args, torch, nf4, wl):
+    """Reconstruction-MSE study (stands in for the pages' quality-vs-bits comparison with
+    synthetic weights) and per-codebook codec throughput, all on the GPU."""
+    dev = "cuda:0"
+    n = 1 << 26
+    g = torch.Generator(device=dev).manual_seed(0)
+    data = {"normal": torch.randn(n, device=dev, generator=g)}
+    # Student-t(4) = N / sqrt(chi2_4 / 4)
+    chi = sum(torch.randn(n, device=dev, generator=g) ** 2 for _ in range(4)) / 4
+    data["student_t4"] = torch.randn(n, device=dev, generator=g) / chi.sqrt()
+    del chi
+    mse = {}
+    for dname, w in data.items():
+        w64 = w.double()
+        for cname, c in nf4.CODEBOOKS.items():
+            codes, absmax = nf4.qlora_quantize(w, codebook=c)
+            qa, s2, mean = nf4.qlora_double_quant(absmax)
+            for dq in (True, False):
+                rec = (nf4.qlora_dequantize(codes, qa, s2, mean, n, torch.float32, codebook=c) if dq else
+                       nf4.qlora_dequantize_nodq(codes, absmax, n, torch.float32, codebook=c))
+                mse[f"{dname}/{cname}/{'dq' if dq else 'no_dq'}"] = float(((rec.double() - w64) ** 2).mean())
+        del w64
+    w = data["normal"].to(torch.bfloat16)
+    out = torch.empty(n, dtype=torch.bfloat16, device=dev)
+    E = torch.cuda.Event
+    rates = {}
+    qb, dqb, deqb = codec_bytes(n, 2, 2)
+    for cname, c in nf4.CODEBOOKS.items():
+        codes = torch.empty(n // 2, dtype=torch.uint8, device=dev)
+        absmax = torch.empty(n // 64, dtype=torch.float32, device=dev)
+        for _ in range(args.warmup):
+            nf4.qlora_quantize(w, codes, absmax, codebook=c)
+        qa, s2, mean = nf4.qlora_double_quant(absmax)
+        torch.cuda.synchronize()
+        ev = [[E(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+        for e in ev:
+            e[0].record()
+            nf4.qlora_quantize(w, codes, absmax, codebook=c)
+            e[1].record()
+            nf4.qlora_dequantize(codes, qa, s2, mean, n, torch.bfloat16, out=out, codebook=c)
+            e[2].record()
+        torch.cuda.synchronize()
+        tq = statistics.median(e[0].elapsed_time(e[1]) for e in ev)
+        td = statistics.median(e[1].elapsed_time(e[2]) for e in ev)
+        rates[cname] = {"quantize_ms": round(tq, 4), "quantize_GB/s": round(qb / tq / 1e6, 1),
+                        "dequantize_ms": round(td, 4), "dequantize_GB/s": round(deqb / td / 1e6, 1)}
+    q = rates["nf4"]
+    return {"metric": METRIC, "value": q["quantize_GB/s"], "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+            "warmup": args.warmup, "ms_per_step": round(q["quantize_ms"] + q["dequantize_ms"], 4),
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+            "config": {"workload": "codebooks_2e26", "n": n, "codebooks": list(nf4.CODEBOOKS),
+                       "inputs": ["N(0,1)", "Student-t(4)"]},
+            "roofline": {"bound": "hbm", "achieved": q["quantize_GB/s"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                         "frac": round(q["quantize_GB/s"] / PEAK_HBM_GBS, 4), "traffic": None,
+                         "kernel": "quantize_kernel<bf16> (NF4)"},
+            "stages": rates, "mse": mse}
+
+
 def main():
     args = parse_args()
     if args.gpus != 1:
@@ -510,7 +570,7 @@ def main():
         torch.cuda.synchronize()
         del src, dst
     fn = {"attn_proj": bench_attn_proj, "codec": bench_codec, "gemv": bench_gemv, "small": bench_small,
-          "merge": bench_merge, "adamw": bench_adamw}[args.workload]
+          "merge": bench_merge, "adamw": bench_adamw, "codebooks": bench_codebooks}[args.workload]
     line = fn(args, torch, nf4, wl)
     if args.workload == "attn_proj" and not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_oracle_attn_proj(wl, args.cpu_seconds)

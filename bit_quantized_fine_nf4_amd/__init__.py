@@ -19,11 +19,14 @@ LIB_PATH = os.path.join(_HERE, "libqlora_nf4.so")
 
 QLORA_OK, QLORA_ERR_INVALID_VALUE, QLORA_ERR_UNSUPPORTED, QLORA_ERR_LAUNCH, QLORA_ERR_INTERNAL = range(5)
 QLORA_F32, QLORA_BF16 = 0, 1
+QLORA_CB_NF4, QLORA_CB_INT4, QLORA_CB_FP4 = 0, 1, 2
+CODEBOOKS = {"nf4": QLORA_CB_NF4, "int4": QLORA_CB_INT4, "fp4": QLORA_CB_FP4}
 QLORA_OP_DOUBLE_QUANT, QLORA_OP_LINEAR_FWD, QLORA_OP_LINEAR_BWD = 0, 1, 2
 BLOCK, CHUNK, MAX_RANK = 64, 256, 128
 
 EXPORTED = ("qlora_quantize", "qlora_double_quant", "qlora_dequantize", "qlora_linear_fwd",
             "qlora_linear_bwd", "qlora_merge_adapter", "qlora_merge_requantize", "qlora_adamw_step",
+            "qlora_quantize_cb", "qlora_dequantize_cb", "qlora_dequantize_nodq", "qlora_codebook_levels",
             "qlora_workspace_size",
             "qlora_status_string", "qlora_nf4_levels", "qlora_set_timing_events")
 
@@ -36,7 +39,8 @@ class QloraError(RuntimeError):
 
 class NF4WeightT(ctypes.Structure):
     _fields_ = [("codes", ctypes.c_void_p), ("qabsmax", ctypes.c_void_p), ("scale2", ctypes.c_void_p),
-                ("mean", ctypes.c_void_p), ("h", ctypes.c_int64), ("o", ctypes.c_int64)]
+                ("mean", ctypes.c_void_p), ("h", ctypes.c_int64), ("o", ctypes.c_int64),
+                ("codebook", ctypes.c_int32)]
 
 
 def _load():
@@ -48,6 +52,10 @@ def _load():
     L.qlora_quantize.argtypes = [vp, st, i64, vp, vp, vp]
     L.qlora_double_quant.argtypes = [vp, i64, vp, vp, vp, vp, sz, vp]
     L.qlora_dequantize.argtypes = [vp, vp, vp, vp, i64, vp, st, vp]
+    L.qlora_quantize_cb.argtypes = [vp, st, i64, st, vp, vp, vp]
+    L.qlora_dequantize_cb.argtypes = [vp, vp, vp, vp, i64, st, vp, st, vp]
+    L.qlora_dequantize_nodq.argtypes = [vp, vp, i64, st, vp, st, vp]
+    L.qlora_codebook_levels.argtypes = [st, ctypes.POINTER(ctypes.c_float)]
     L.qlora_linear_fwd.argtypes = [ctypes.POINTER(NF4WeightT), vp, i64, vp, vp, i32, f32, vp, vp, vp, sz, vp]
     L.qlora_linear_bwd.argtypes = [ctypes.POINTER(NF4WeightT), vp, vp, vp, i64, vp, vp, i32, f32, vp, vp, vp,
                                    vp, sz, vp]
@@ -127,19 +135,27 @@ class NF4Weight:
     mean: torch.Tensor     # float32 [1]
     h: int
     o: int
+    codebook: int = QLORA_CB_NF4
 
     def as_ctypes(self) -> NF4WeightT:
         return NF4WeightT(self.codes.data_ptr(), self.qabsmax.data_ptr(), self.scale2.data_ptr(),
-                          self.mean.data_ptr(), self.h, self.o)
+                          self.mean.data_ptr(), self.h, self.o, self.codebook)
 
 
 # ---------------------------------------------------------------------------
 # The entry points
 # ---------------------------------------------------------------------------
 
+def codebook_levels(codebook: int = QLORA_CB_NF4) -> list:
+    buf = (ctypes.c_float * 16)()
+    _check(lib.qlora_codebook_levels(codebook, buf), "qlora_codebook_levels")
+    return list(buf)
+
+
 def qlora_quantize(w: torch.Tensor, codes: Optional[torch.Tensor] = None,
-                   absmax: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
-    """Blockwise NF4 quantization of any float32/bf16 GPU tensor (flattened)."""
+                   absmax: Optional[torch.Tensor] = None, codebook: int = QLORA_CB_NF4) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Blockwise 4-bit quantization (NF4 unless `codebook` says otherwise) of any float32/bf16
+    GPU tensor (flattened)."""
     _dev_check(w)
     n = w.numel()
     dtype = {torch.float32: QLORA_F32, torch.bfloat16: QLORA_BF16}[w.dtype]
@@ -147,7 +163,11 @@ def qlora_quantize(w: torch.Tensor, codes: Optional[torch.Tensor] = None,
         codes = torch.empty((n + 1) // 2, dtype=torch.uint8, device=w.device)
     if absmax is None:
         absmax = torch.empty((n + BLOCK - 1) // BLOCK, dtype=torch.float32, device=w.device)
-    _check(lib.qlora_quantize(_ptr(w), dtype, n, _ptr(codes), _ptr(absmax), _stream(w.device)), "qlora_quantize")
+    if codebook == QLORA_CB_NF4:
+        _check(lib.qlora_quantize(_ptr(w), dtype, n, _ptr(codes), _ptr(absmax), _stream(w.device)), "qlora_quantize")
+    else:
+        _check(lib.qlora_quantize_cb(_ptr(w), dtype, n, codebook, _ptr(codes), _ptr(absmax), _stream(w.device)),
+               "qlora_quantize_cb")
     return codes, absmax
 
 
@@ -174,23 +194,39 @@ def qlora_double_quant(absmax: torch.Tensor, qabsmax: Optional[torch.Tensor] = N
 
 def qlora_dequantize(codes: torch.Tensor, qabsmax: torch.Tensor, scale2: torch.Tensor, mean: torch.Tensor,
                      n: int, out_dtype: torch.dtype = torch.bfloat16,
-                     out: Optional[torch.Tensor] = None) -> torch.Tensor:
+                     out: Optional[torch.Tensor] = None, codebook: int = QLORA_CB_NF4) -> torch.Tensor:
     """Rebuild n weights as float32 or bf16."""
     _dev_check(codes, qabsmax, scale2, mean)
     dt = {torch.float32: QLORA_F32, torch.bfloat16: QLORA_BF16}[out_dtype]
     if out is None:
         out = torch.empty(n, dtype=out_dtype, device=codes.device)
-    _check(lib.qlora_dequantize(_ptr(codes), _ptr(qabsmax), _ptr(scale2), _ptr(mean), n, _ptr(out), dt,
-                                _stream(codes.device)), "qlora_dequantize")
+    if codebook == QLORA_CB_NF4:
+        _check(lib.qlora_dequantize(_ptr(codes), _ptr(qabsmax), _ptr(scale2), _ptr(mean), n, _ptr(out), dt,
+                                    _stream(codes.device)), "qlora_dequantize")
+    else:
+        _check(lib.qlora_dequantize_cb(_ptr(codes), _ptr(qabsmax), _ptr(scale2), _ptr(mean), n, codebook,
+                                       _ptr(out), dt, _stream(codes.device)), "qlora_dequantize_cb")
     return out
 
 
-def quantize_weight(w_oh: torch.Tensor) -> NF4Weight:
+def qlora_dequantize_nodq(codes: torch.Tensor, absmax: torch.Tensor, n: int, out_dtype: torch.dtype = torch.bfloat16,
+                          out: Optional[torch.Tensor] = None, codebook: int = QLORA_CB_NF4) -> torch.Tensor:
+    """Rebuild n weights from the float32 block scales (no double quantization)."""
+    _dev_check(codes, absmax)
+    dt = {torch.float32: QLORA_F32, torch.bfloat16: QLORA_BF16}[out_dtype]
+    if out is None:
+        out = torch.empty(n, dtype=out_dtype, device=codes.device)
+    _check(lib.qlora_dequantize_nodq(_ptr(codes), _ptr(absmax), n, codebook, _ptr(out), dt, _stream(codes.device)),
+           "qlora_dequantize_nodq")
+    return out
+
+
+def quantize_weight(w_oh: torch.Tensor, codebook: int = QLORA_CB_NF4) -> NF4Weight:
     """quantize + double_quant of a [o][h] float32/bf16 weight."""
     o, h = w_oh.shape
-    codes, absmax = qlora_quantize(w_oh)
+    codes, absmax = qlora_quantize(w_oh, codebook=codebook)
     qa, s2, mean = qlora_double_quant(absmax)
-    return NF4Weight(codes, qa, s2, mean, h, o)
+    return NF4Weight(codes, qa, s2, mean, h, o, codebook)
 
 
 def qlora_linear_fwd(W: NF4Weight, X: torch.Tensor, L1: Optional[torch.Tensor], L2: Optional[torch.Tensor],

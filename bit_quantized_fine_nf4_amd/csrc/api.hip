@@ -24,6 +24,7 @@ bool valid_weight(const qlora_nf4_weight_t *W) {
   if (W->h <= 0 || W->o <= 0 || W->h % 64 || W->o % 64) return false;
   if (W->h > (int64_t(1) << 20) || W->o > (int64_t(1) << 20)) return false;
   if (W->h * W->o / 64 >= (int64_t(1) << 32)) return false;
+  if (W->codebook < 0 || W->codebook >= kCodebooks) return false;
   return aligned(W->codes, 16) && aligned(W->qabsmax, 4) && aligned(W->scale2, 4) && aligned(W->mean, 4);
 }
 
@@ -56,7 +57,7 @@ qlora_status_t qlora_merge_adapter(const qlora_nf4_weight_t *W, const uint16_t *
   if (out_dtype != QLORA_F32 && out_dtype != QLORA_BF16) return QLORA_ERR_INVALID_VALUE;
   if (r > 0 && (!L1 || !L2 || !aligned(L1, 16) || !aligned(L2, 16))) return QLORA_ERR_INVALID_VALUE;
   if (!aligned(out, 16)) return QLORA_ERR_INVALID_VALUE;
-  const Nf4Tables *t = host_tables();
+  const Nf4Tables *t = host_tables(W->codebook);
   if (!t) return QLORA_ERR_INTERNAL;
   (void)hipGetLastError();
   const MergeArgs m{W->codes, W->qabsmax, W->scale2, W->mean, W->h, W->o, L1, L2, r, s, out, nullptr, nullptr};
@@ -68,7 +69,7 @@ qlora_status_t qlora_merge_requantize(const qlora_nf4_weight_t *W, const uint16_
   if (!valid_weight(W) || !codes_out || !absmax_out || r < 0 || r > QLORA_MAX_RANK) return QLORA_ERR_INVALID_VALUE;
   if (r > 0 && (!L1 || !L2 || !aligned(L1, 16) || !aligned(L2, 16))) return QLORA_ERR_INVALID_VALUE;
   if (!aligned(codes_out, 8) || !aligned(absmax_out, 4)) return QLORA_ERR_INVALID_VALUE;
-  const Nf4Tables *t = host_tables();
+  const Nf4Tables *t = host_tables(W->codebook);
   if (!t) return QLORA_ERR_INTERNAL;
   (void)hipGetLastError();
   const MergeArgs m{W->codes, W->qabsmax, W->scale2, W->mean, W->h, W->o, L1, L2, r, s, nullptr, codes_out,
@@ -115,16 +116,22 @@ qlora_status_t qlora_workspace_size(qlora_op_t op, int64_t a, int64_t b, int64_t
   return QLORA_ERR_INVALID_VALUE;
 }
 
-qlora_status_t qlora_quantize(const void *w, qlora_dtype_t w_dtype, int64_t n, uint8_t *codes,
-                              float *absmax, void *stream) {
+qlora_status_t qlora_quantize_cb(const void *w, qlora_dtype_t w_dtype, int64_t n, qlora_codebook_t codebook,
+                                 uint8_t *codes, float *absmax, void *stream) {
   if (!w || !codes || !absmax || n < 1) return QLORA_ERR_INVALID_VALUE;
   if (w_dtype != QLORA_F32 && w_dtype != QLORA_BF16) return QLORA_ERR_INVALID_VALUE;
+  if (codebook < 0 || codebook >= kCodebooks) return QLORA_ERR_INVALID_VALUE;
   if (!aligned(w, 16) || !aligned(codes, 4) || !aligned(absmax, 4)) return QLORA_ERR_INVALID_VALUE;
-  const Nf4Tables *t = host_tables();
+  const Nf4Tables *t = host_tables(codebook);
   if (!t) return QLORA_ERR_INTERNAL;
   (void)hipGetLastError();
   return launch_status(launch_quantize(w, w_dtype == QLORA_BF16, n, codes, absmax, *t,
                                        reinterpret_cast<hipStream_t>(stream)));
+}
+
+qlora_status_t qlora_quantize(const void *w, qlora_dtype_t w_dtype, int64_t n, uint8_t *codes,
+                              float *absmax, void *stream) {
+  return qlora_quantize_cb(w, w_dtype, n, QLORA_CB_NF4, codes, absmax, stream);
 }
 
 qlora_status_t qlora_double_quant(const float *absmax, int64_t nblocks, int8_t *qabsmax, float *scale2,
@@ -140,18 +147,47 @@ qlora_status_t qlora_double_quant(const float *absmax, int64_t nblocks, int8_t *
                                            reinterpret_cast<hipStream_t>(stream)));
 }
 
-qlora_status_t qlora_dequantize(const uint8_t *codes, const int8_t *qabsmax, const float *scale2,
-                                const float *mean, int64_t n, void *out, qlora_dtype_t out_dtype,
-                                void *stream) {
+qlora_status_t qlora_dequantize_cb(const uint8_t *codes, const int8_t *qabsmax, const float *scale2,
+                                   const float *mean, int64_t n, qlora_codebook_t codebook, void *out,
+                                   qlora_dtype_t out_dtype, void *stream) {
   if (!codes || !qabsmax || !scale2 || !mean || !out || n < 1) return QLORA_ERR_INVALID_VALUE;
   if (out_dtype != QLORA_F32 && out_dtype != QLORA_BF16) return QLORA_ERR_INVALID_VALUE;
+  if (codebook < 0 || codebook >= kCodebooks) return QLORA_ERR_INVALID_VALUE;
   if (!aligned(codes, 16) || !aligned(out, 16) || !aligned(scale2, 4) || !aligned(mean, 4))
     return QLORA_ERR_INVALID_VALUE;
-  const Nf4Tables *t = host_tables();
+  const Nf4Tables *t = host_tables(codebook);
   if (!t) return QLORA_ERR_INTERNAL;
   (void)hipGetLastError();
   return launch_status(launch_dequantize(codes, qabsmax, scale2, mean, n, out, out_dtype == QLORA_BF16,
                                          *t, reinterpret_cast<hipStream_t>(stream)));
+}
+
+qlora_status_t qlora_dequantize(const uint8_t *codes, const int8_t *qabsmax, const float *scale2,
+                                const float *mean, int64_t n, void *out, qlora_dtype_t out_dtype,
+                                void *stream) {
+  return qlora_dequantize_cb(codes, qabsmax, scale2, mean, n, QLORA_CB_NF4, out, out_dtype, stream);
+}
+
+qlora_status_t qlora_dequantize_nodq(const uint8_t *codes, const float *absmax, int64_t n,
+                                     qlora_codebook_t codebook, void *out, qlora_dtype_t out_dtype,
+                                     void *stream) {
+  if (!codes || !absmax || !out || n < 1) return QLORA_ERR_INVALID_VALUE;
+  if (out_dtype != QLORA_F32 && out_dtype != QLORA_BF16) return QLORA_ERR_INVALID_VALUE;
+  if (codebook < 0 || codebook >= kCodebooks) return QLORA_ERR_INVALID_VALUE;
+  if (!aligned(codes, 16) || !aligned(out, 16) || !aligned(absmax, 4)) return QLORA_ERR_INVALID_VALUE;
+  const Nf4Tables *t = host_tables(codebook);
+  if (!t) return QLORA_ERR_INTERNAL;
+  (void)hipGetLastError();
+  return launch_status(launch_dequantize(codes, nullptr, nullptr, nullptr, n, out, out_dtype == QLORA_BF16,
+                                         *t, reinterpret_cast<hipStream_t>(stream), absmax));
+}
+
+qlora_status_t qlora_codebook_levels(qlora_codebook_t codebook, float *levels) {
+  if (!levels || codebook < 0 || codebook >= kCodebooks) return QLORA_ERR_INVALID_VALUE;
+  const Nf4Tables *t = host_tables(codebook);
+  if (!t) return QLORA_ERR_INTERNAL;
+  for (int i = 0; i < 16; ++i) levels[i] = t->level[i];
+  return QLORA_OK;
 }
 
 qlora_status_t qlora_linear_fwd(const qlora_nf4_weight_t *W, const uint16_t *X, int64_t M,
@@ -165,7 +201,7 @@ qlora_status_t qlora_linear_fwd(const qlora_nf4_weight_t *W, const uint16_t *X, 
   if (r > 0 && (!aligned(L1, 16) || !aligned(L2, 16) || !aligned(T, 16))) return QLORA_ERR_INVALID_VALUE;
   const size_t need = round256(linear_fwd_workspace(M, W->h, W->o, r));
   if (need && (!workspace || ws_bytes < need || !aligned(workspace, 256))) return QLORA_ERR_INVALID_VALUE;
-  const Nf4Tables *t = host_tables();
+  const Nf4Tables *t = host_tables(W->codebook);
   if (!t) return QLORA_ERR_INTERNAL;
   (void)hipGetLastError();
   LinearArgs a{W->codes, W->qabsmax, W->scale2, W->mean, W->h, W->o, M, r, s};
@@ -186,7 +222,7 @@ qlora_status_t qlora_linear_bwd(const qlora_nf4_weight_t *W, const uint16_t *X, 
     return QLORA_ERR_INVALID_VALUE;
   const size_t need = round256(linear_bwd_workspace(M, W->h, W->o, r));
   if (need && (!workspace || ws_bytes < need || !aligned(workspace, 256))) return QLORA_ERR_INVALID_VALUE;
-  const Nf4Tables *t = host_tables();
+  const Nf4Tables *t = host_tables(W->codebook);
   if (!t) return QLORA_ERR_INTERNAL;
   (void)hipGetLastError();
   LinearArgs a{W->codes, W->qabsmax, W->scale2, W->mean, W->h, W->o, M, r, s};

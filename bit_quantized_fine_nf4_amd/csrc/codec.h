@@ -10,9 +10,10 @@ hipError_t launch_quantize(const void *w, bool bf16, int64_t n, uint8_t *codes, 
 size_t dq_workspace_bytes();
 hipError_t launch_double_quant(const float *absmax, int64_t nb, int8_t *qabsmax, float *scale2,
                                float *mean, void *ws, hipStream_t st);
+// absmax != nullptr: no double quantization (qabsmax, scale2, mean unused, may be null).
 hipError_t launch_dequantize(const uint8_t *codes, const int8_t *qabsmax, const float *scale2,
                              const float *mean, int64_t n, void *out, bool bf16, const Nf4Tables &tab,
-                             hipStream_t st);
+                             hipStream_t st, const float *absmax = nullptr);
 
 // Adapter merge W' = W_hat + s·L1·L2 ([o][h] storage); mode 0: float32 out,
 // 1: bf16 out, 2: NF4 codes_out / absmax_out of W'.

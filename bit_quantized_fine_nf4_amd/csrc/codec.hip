@@ -17,10 +17,11 @@ namespace ql {
 // Lane layout: each lane owns 8 consecutive weights, so the 8 lanes of a
 // half-row own one 64-weight block.  The block's largest magnitude is reduced
 // with three DPP max steps inside the 8-lane group.  Each weight's code comes
-// from the bucket table (see nf4_tables.cpp): y = fma(w, 16/absmax, 16),
-// bucket floor(y), one comparison against the bucket's guard band.  A lane
-// with any weight inside a guard band, or a block whose scale is 0 or outside
-// [2^-100, 2^100], recomputes its 8 codes with the IEEE division.  The 8 codes
+// from the bucket table (see nf4_tables.hip): y = fma(w, 16/absmax, yoff),
+// bucket floor(y), one comparison against the bucket's guard band.  A weight
+// inside a guard band is decided by the IEEE division against the one
+// threshold there; a block whose scale is 0 or outside [2^-100, 2^100] takes
+// the IEEE division for all its codes.  The 8 codes
 // are packed into one 32-bit word (first weight in the high nibble of the
 // first byte) and stored with one coalesced dword store per lane.
 // ---------------------------------------------------------------------------
@@ -78,29 +79,30 @@ QL_DEV uint32_t exact_code(float x, const Nf4Tables &t) {
   return c;
 }
 
-// NF4 codes of 8 consecutive weights of one block whose largest magnitude is a
+// Codes of 8 consecutive weights of one block whose largest magnitude is a
 // (already reduced over the block): element i in byte i/2, even i in the high
-// nibble.  Fast path: y = 16 * x + 16 indexes a bucket of the threshold table;
-// anything inside a bucket's guard band (or a scale outside [2^-100, 2^100])
-// takes the exact IEEE divide-and-compare path, so the result always equals
-// the nearest-level rule on fp32(w / a).
+// nibble.  Fast path: y = 16 * x + yoff indexes a bucket of the threshold
+// table.  A weight whose y falls inside its bucket's guard band is decided by
+// the exact rule for the one threshold that can matter there: x = fp32(w / a)
+// (IEEE division) against the bucket's float32 threshold tx.  A scale outside
+// [2^-100, 2^100] takes the exact divide-and-compare path for all 8 weights.
+// Either way the result equals the nearest-level rule on fp32(w / a).
 QL_DEV uint32_t encode8(const float (&v)[8], float a, const EncBucket *lut, const Nf4Tables &tab) {
-  bool slow = !(a >= 0x1p-100f && a <= 0x1p100f);
-  const float r16 = 16.0f * __builtin_amdgcn_rcpf(a);
   uint32_t word = 0;
+  if (a >= 0x1p-100f && a <= 0x1p100f) {
+    const float r16 = 16.0f * __builtin_amdgcn_rcpf(a);
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    float y = __builtin_fmaf(v[i], r16, 16.0f);
-    uint32_t idx = (uint32_t)(int32_t)y;
-    idx = idx > 32u ? 32u : idx;
-    const EncBucket e = lut[idx];
-    const bool up = y > e.hi;
-    slow |= (y > e.lo) && !up;
-    uint32_t c = e.base + (up ? 1u : 0u);
-    word |= c << (8 * (i >> 1) + ((i & 1) ? 0 : 4));
-  }
-  if (slow) {
-    word = 0;
+    for (int i = 0; i < 8; ++i) {
+      float y = __builtin_fmaf(v[i], r16, tab.yoff);
+      uint32_t idx = (uint32_t)(int32_t)y;
+      idx = idx > (uint32_t)(kBuckets - 1) ? (uint32_t)(kBuckets - 1) : idx;
+      const EncBucket e = lut[idx];
+      const bool up = y > e.hi;
+      uint32_t c = e.base + (up ? 1u : 0u);
+      if ((y > e.lo) && !up) c = e.base + ((v[i] / a > e.tx) ? 1u : 0u);
+      word |= c << (8 * (i >> 1) + ((i & 1) ? 0 : 4));
+    }
+  } else {
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       float x = a > 0.0f ? v[i] / a : 0.0f;
@@ -135,10 +137,10 @@ __global__ __launch_bounds__(256) void quantize_kernel(const void *__restrict__ 
     if (e0 + 8 <= n) {
       *reinterpret_cast<uint32_t *>(codes + c0) = word;
     } else if (e0 < n) {
-      // tail: pad codes beyond n are code 7 (zero level), bytes beyond ceil(n/2) untouched
+      // tail: pad codes beyond n are the zero level's code, bytes beyond ceil(n/2) untouched
       for (int i = 0; i < 8; ++i)
         if (e0 + i >= n) word = (word & ~(0xFu << (8 * (i >> 1) + ((i & 1) ? 0 : 4)))) |
-                                (7u << (8 * (i >> 1) + ((i & 1) ? 0 : 4)));
+                                (tab.zero_code << (8 * (i >> 1) + ((i & 1) ? 0 : 4)));
       for (int b = 0; b < 4; ++b)
         if (c0 + b < ncodes) codes[c0 + b] = (uint8_t)(word >> (8 * b));
     }
@@ -665,16 +667,19 @@ QL_DEV void dequant_unit(const f32x2 *lut, uint32_t cw, float ah, int64_t e0, in
   }
 }
 
-template <bool kOutBf16>
+template <bool kOutBf16, bool kNoDq>
 __global__ __launch_bounds__(256) void dequantize_kernel(const uint8_t *__restrict__ codes,
                                                          const int8_t *__restrict__ qabsmax,
                                                          const float *__restrict__ scale2,
                                                          const float *__restrict__ mean_in, int64_t n,
-                                                         void *__restrict__ out, Nf4Tables tab) {
+                                                         void *__restrict__ out, Nf4Tables tab,
+                                                         const float *__restrict__ absmax) {
+  // kNoDq: no double quantization, the float32 block scales (absmax) are used as stored
   __shared__ f32x2 lut[256];
   lut[threadIdx.x] = f32x2{tab.level[threadIdx.x >> 4], tab.level[threadIdx.x & 15]};
   __syncthreads();
-  const float mu = *mean_in;
+  constexpr bool nodq = kNoDq;
+  const float mu = nodq ? 0.0f : *mean_in;
   const int64_t nunits = (n + 7) / 8;
   const int64_t nbytes = (n + 1) / 2;
   const int64_t per_block = (int64_t)kDeqUnroll * blockDim.x;
@@ -691,8 +696,12 @@ __global__ __launch_bounds__(256) void dequantize_kernel(const uint8_t *__restri
       s2[u] = 0.0f;
       if (unit < nunits) {
         const int64_t blk = e0 >> 6;
-        q[u] = qabsmax[blk];
-        s2[u] = scale2[blk / kChunk];
+        if constexpr (nodq) {
+          s2[u] = absmax[blk];  // used as a_hat directly below
+        } else {
+          q[u] = qabsmax[blk];
+          s2[u] = scale2[blk / kChunk];
+        }
         if (e0 + 8 <= n) {
           cw[u] = *reinterpret_cast<const uint32_t *>(codes + (e0 >> 1));
         } else {
@@ -707,7 +716,8 @@ __global__ __launch_bounds__(256) void dequantize_kernel(const uint8_t *__restri
 #pragma unroll
     for (int u = 0; u < kDeqUnroll; ++u) {
       const int64_t unit = base + u * blockDim.x + threadIdx.x;
-      if (unit < nunits) dequant_unit<kOutBf16>(lut, cw[u], scale_hat(q[u], s2[u], mu), unit * 8, n, out);
+      if (unit < nunits)
+        dequant_unit<kOutBf16>(lut, cw[u], nodq ? s2[u] : scale_hat(q[u], s2[u], mu), unit * 8, n, out);
     }
   }
 }
@@ -779,12 +789,19 @@ hipError_t launch_merge(const MergeArgs &m, int mode, const Nf4Tables &tab, hipS
 
 hipError_t launch_dequantize(const uint8_t *codes, const int8_t *qabsmax, const float *scale2,
                              const float *mean, int64_t n, void *out, bool bf16, const Nf4Tables &tab,
-                             hipStream_t st) {
+                             hipStream_t st, const float *absmax) {
   const int grid = grid_for((n + 7) / 8, 256 * kDeqUnroll, 256 * 16);
-  if (bf16)
-    dequantize_kernel<true><<<grid, 256, 0, st>>>(codes, qabsmax, scale2, mean, n, out, tab);
-  else
-    dequantize_kernel<false><<<grid, 256, 0, st>>>(codes, qabsmax, scale2, mean, n, out, tab);
+  if (absmax) {
+    if (bf16)
+      dequantize_kernel<true, true><<<grid, 256, 0, st>>>(codes, qabsmax, scale2, mean, n, out, tab, absmax);
+    else
+      dequantize_kernel<false, true><<<grid, 256, 0, st>>>(codes, qabsmax, scale2, mean, n, out, tab, absmax);
+  } else {
+    if (bf16)
+      dequantize_kernel<true, false><<<grid, 256, 0, st>>>(codes, qabsmax, scale2, mean, n, out, tab, absmax);
+    else
+      dequantize_kernel<false, false><<<grid, 256, 0, st>>>(codes, qabsmax, scale2, mean, n, out, tab, absmax);
+  }
   return hipGetLastError();
 }
 

@@ -20,9 +20,9 @@ constexpr int kBlock = 64;   // weights per first-level scale
 constexpr int kChunk = 256;  // first-level scales per second-level step
 constexpr int kWave = 64;
 
-// Encoder bucket table: y = 16*x + 16 for a normalised weight x in [-1, 1]
-// falls in bucket floor(y) (0..32).  Each bucket holds at most one decision
-// threshold; `lo`/`hi` bound its guard band (see nf4_tables.cpp).
+// Encoder bucket table: y = 16*x + yoff (yoff = 16 plus a shift in [0, 1)) for
+// a normalised weight x in [-1, 1] falls in bucket floor(y) (0..33).  Each bucket holds at most one
+// decision threshold; `lo`/`hi` bound its guard band (see nf4_tables.hip).
 struct EncBucket {
   float hi;     // y > hi: code is base + 1 for certain
   float lo;     // y <= lo: code is base for certain
@@ -30,16 +30,21 @@ struct EncBucket {
   uint32_t base;
 };
 
-constexpr int kBuckets = 33;
+constexpr int kBuckets = 34;
+
+// 4-bit codebooks: the index of a value in an ascending 16-entry table is its code.
+constexpr int kCodebooks = 3;  // 0 NF4, 1 INT4 (symmetric absmax grid), 2 FP4 (E2M1 values)
 
 struct Nf4Tables {
   float level[16];              // the codebook, ascending
   float thr[15];                // thr[j] = largest float32 <= midpoint(level[j], level[j+1])
   EncBucket bucket[kBuckets];
+  float yoff;                   // y = 16 x + yoff
+  uint32_t zero_code;           // the code of level 0 (padding)
 };
 
-// Built once on the host (nf4_tables.cpp); passed to kernels by value.
-const Nf4Tables *host_tables();  // nullptr if construction failed
+// Built once per codebook on the host (nf4_tables.hip); passed to kernels by value.
+const Nf4Tables *host_tables(int codebook = 0);  // nullptr if construction failed
 
 // ---- small device helpers ------------------------------------------------
 

@@ -46,6 +46,20 @@ typedef enum {
 
 typedef enum { QLORA_F32 = 0, QLORA_BF16 = 1 } qlora_dtype_t;
 
+/*
+ * 4-bit codebooks.  A code is the index of its value in an ascending 16-entry
+ * table (qlora_codebook_levels), chosen as the nearest value to
+ * fp32(w / absmax), ties to the lower one.
+ *  NF4   the NormalFloat values ([MC] "1. NormalFloat", [TT] §5), code 7 = 0.
+ *  INT4  the symmetric absmax integer grid of [TT] §2 at 4 bits: q/7 for
+ *        q = -8..7 at code q + 8 (q = -8 is never produced).
+ *  FP4   the E2M1 values {0, 0.5, 1, 1.5, 2, 3, 4, 6} and negatives, divided
+ *        by 6, at codes 1..15 (code 0, -1.5, is never produced); the pages
+ *        compare NF4 with FP4 ([MC] "What the experiments establish") but fix
+ *        no FP4 layout, so this one is a reading.
+ */
+typedef enum { QLORA_CB_NF4 = 0, QLORA_CB_INT4 = 1, QLORA_CB_FP4 = 2 } qlora_codebook_t;
+
 /* Workspace queries (qlora_workspace_size `op`). */
 typedef enum {
   QLORA_OP_DOUBLE_QUANT = 0, /* a = number of block scales */
@@ -61,8 +75,9 @@ typedef enum {
  * One frozen NF4 weight with double-quantized scales.  Logical shape h x o
  * (the pages' W: h inputs, o outputs, [MC] "The algebra").  Stored in
  * PyTorch's Linear.weight order [o][h]: row n holds output n's h weights, so
- * each 64-weight block runs along h.  Produced by qlora_quantize on the
- * [o][h] buffer followed by qlora_double_quant.  This struct is a host
+ * each 64-weight block runs along h.  Produced by qlora_quantize (or
+ * qlora_quantize_cb with the codebook recorded in `codebook`) on the [o][h]
+ * buffer followed by qlora_double_quant.  This struct is a host
  * object; the pointers in it are device pointers.
  */
 typedef struct {
@@ -72,6 +87,7 @@ typedef struct {
   const float *mean;      /* 1 float32: the mean of the float32 block scales */
   int64_t h;              /* input width, a positive multiple of 64, at most 2^20 */
   int64_t o;              /* output width, a positive multiple of 64, at most 2^20 */
+  int32_t codebook;       /* qlora_codebook_t of the codes; QLORA_CB_NF4 (0) for NF4 */
 } qlora_nf4_weight_t;
 
 /*
@@ -120,6 +136,30 @@ qlora_status_t qlora_double_quant(const float *absmax, int64_t nblocks, int8_t *
 qlora_status_t qlora_dequantize(const uint8_t *codes, const int8_t *qabsmax, const float *scale2,
                                 const float *mean, int64_t n, void *out, qlora_dtype_t out_dtype,
                                 void *stream);
+
+/*
+ * Codebook variants of the codec: the same storage, encoder and scales with
+ * the levels of `codebook` (qlora_quantize / qlora_dequantize are the
+ * QLORA_CB_NF4 cases).  Arguments, layouts and alignment as above.
+ */
+qlora_status_t qlora_quantize_cb(const void *w, qlora_dtype_t w_dtype, int64_t n, qlora_codebook_t codebook,
+                                 uint8_t *codes, float *absmax, void *stream);
+qlora_status_t qlora_dequantize_cb(const uint8_t *codes, const int8_t *qabsmax, const float *scale2,
+                                   const float *mean, int64_t n, qlora_codebook_t codebook, void *out,
+                                   qlora_dtype_t out_dtype, void *stream);
+
+/*
+ * qlora_dequantize_nodq — reconstruction without double quantization: the
+ * float32 block scales from quantization are used as stored,
+ * w_hat = fp32(level[code] * absmax[block]) ([MC] "2. Double quantization"
+ * is an addition on top of blockwise quantization).  absmax 4-byte aligned.
+ */
+qlora_status_t qlora_dequantize_nodq(const uint8_t *codes, const float *absmax, int64_t n,
+                                     qlora_codebook_t codebook, void *out, qlora_dtype_t out_dtype,
+                                     void *stream);
+
+/* The 16 float32 values of a codebook, ascending (index = code). */
+qlora_status_t qlora_codebook_levels(qlora_codebook_t codebook, float *levels);
 
 /*
  * qlora_linear_fwd — Y = X·W_hat + s·(X·L1)·L2 ([MC] "The algebra", Eq. 3;

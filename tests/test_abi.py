@@ -161,3 +161,24 @@ def test_adamw_rejects_bad_arguments():
     assert a(eps=0.0) == INV
     assert a(lr=-1.0) == INV
     assert a(wd=float("nan")) == INV
+
+
+@pytest.mark.parametrize("name", ["nf4", "int4", "fp4"])
+def test_codebook_levels_match_oracle_bitwise(name):
+    got = np.array(nf4.codebook_levels(nf4.CODEBOOKS[name]), np.float32)
+    assert np.array_equal(got.view(np.uint32), oracle.codebooks.levels(name).view(np.uint32))
+
+
+def test_codebook_entry_points_reject_bad_arguments():
+    buf = (ctypes.c_float * 16)()
+    assert lib.qlora_codebook_levels(3, buf) == INV
+    assert lib.qlora_codebook_levels(-1, buf) == INV
+    assert lib.qlora_quantize_cb(FAKE, 0, 10, 3, FAKE, FAKE, None) == INV
+    assert lib.qlora_quantize_cb(FAKE, 0, 0, 1, FAKE, FAKE, None) == INV
+    assert lib.qlora_dequantize_cb(FAKE, FAKE, FAKE, FAKE, 10, 7, FAKE, 0, None) == INV
+    assert lib.qlora_dequantize_nodq(FAKE, None, 10, 1, FAKE, 0, None) == INV
+    assert lib.qlora_dequantize_nodq(FAKE, FAKE, 10, 1, ODD, 0, None) == INV
+    assert lib.qlora_dequantize_nodq(FAKE, FAKE, 0, 1, FAKE, 0, None) == INV
+    W = weight()
+    W.codebook = 3
+    assert lib.qlora_merge_adapter(ctypes.byref(W), FAKE, FAKE, 8, 1.0, FAKE, 0, None) == INV

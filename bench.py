@@ -351,6 +351,33 @@ def bench_gemv(args, torch, nf4, wl):
         bytes_ = h * o // 2 + nb + 4 * ((nb + 255) // 256) + 2 * m * h + 2 * m * o
         res[m] = {"ms": round(ms, 5), "GB/s": round(bytes_ / ms / 1e6, 2),
                   "frac_hbm": round(bytes_ / ms / 1e6 / PEAK_HBM_GBS, 4), "bytes": bytes_}
+    # few-token backward dX = dY·W_hat^T (no adapter): the dX GEMV kernel timed by the library's
+    # hook, and the whole call (GEMV + the partial-sum finish) by events on the stream
+    bwd = {}
+    E = torch.cuda.Event
+    for m in wl.C4_GEMV_TOKENS:
+        dY = wl.activations(c, 0, tokens=m, tensor=wl.TENSOR_DY).to(dev)
+        dX = torch.empty(m, h, dtype=torch.bfloat16, device=dev)
+        ws = torch.empty(nf4.workspace_size(nf4.QLORA_OP_LINEAR_BWD, m, h, o, 0), dtype=torch.uint8, device=dev)
+        for i in range(args.warmup):
+            nf4.qlora_linear_bwd(Ws[i % copies], None, None, dY, None, None, 1.0, dX=dX, workspace=ws)
+        torch.cuda.synchronize()
+        reps = max(args.steps, 8)
+        kev = [[hev.create(), hev.create()] for _ in range(reps)]
+        tev = [(E(enable_timing=True), E(enable_timing=True)) for _ in range(reps)]
+        for i in range(reps):
+            nf4.qlora_set_timing_events(nf4.TIMED_GEMM_DX, kev[i][0], kev[i][1])
+            tev[i][0].record()
+            nf4.qlora_linear_bwd(Ws[i % copies], None, None, dY, None, None, 1.0, dX=dX, workspace=ws)
+            tev[i][1].record()
+        torch.cuda.synchronize()
+        nf4.qlora_set_timing_events(nf4.TIMED_GEMM_DX, None, None)
+        ms = statistics.median(hev.elapsed_ms(k[0], k[1]) for k in kev)
+        call_ms = statistics.median(a.elapsed_time(b) for a, b in tev)
+        nb = h * o // 64
+        bytes_ = h * o // 2 + nb + 4 * ((nb + 255) // 256) + 2 * m * o + 2 * m * h
+        bwd[m] = {"kernel_ms": round(ms, 5), "call_ms": round(call_ms, 5), "GB/s": round(bytes_ / ms / 1e6, 2),
+                  "frac_hbm": round(bytes_ / ms / 1e6 / PEAK_HBM_GBS, 4), "bytes": bytes_}
     worst = min(res, key=lambda k: res[k]["GB/s"])
     return {"metric": METRIC, "value": res[16]["GB/s"], "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
             "warmup": args.warmup, "ms_per_step": res[16]["ms"], "higher_is_better": True, "scaling": "weak",
@@ -358,7 +385,8 @@ def bench_gemv(args, torch, nf4, wl):
             "config": {"workload": c.name, "h": h, "o": o, "tokens": list(wl.C4_GEMV_TOKENS), "weight_copies": copies},
             "roofline": {"bound": "hbm", "achieved": res[worst]["GB/s"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
                          "frac": res[worst]["frac_hbm"], "traffic": None, "kernel": f"nf4_gemv_kernel (M={worst})"},
-            "stages": {f"M={k}": v for k, v in res.items()}}
+            "stages": {f"M={k}": v for k, v in res.items()},
+            "backward_dx": {f"M={k}": v for k, v in bwd.items()}}
 
 
 def bench_small(args, torch, nf4, wl):

@@ -126,18 +126,37 @@ __global__ __launch_bounds__(256) void skinny_kernel(const uint16_t *__restrict_
     }
 }
 
-// out1[m][q] = bf16(sum) for q < n1 (row stride ld1; zero for r <= q < n1)
+// out1[m][q] = bf16(sum) for q < ld1 (zero for r <= q < ld1)
 // out2[m][q] = bf16(s * sum) for q < ld2 (zero for q >= r)
-__global__ void skinny_finish_kernel(const float *__restrict__ part, int S, int64_t M, int RP, int r, float s,
-                                     uint16_t *__restrict__ out1, int ld1, uint16_t *__restrict__ out2, int ld2) {
-  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  const int64_t W = ld2 > ld1 ? ld2 : ld1;
-  if (idx >= M * W) return;
-  const int64_t m = idx / W;
-  const int q = (int)(idx % W);
-  float acc = 0.0f;
-  if (q < r)
-    for (int i = 0; i < S; ++i) acc += part[((int64_t)i * M + m) * RP + q];
+// Block b takes token b / qb and 64 columns q; its four waves sum the splits
+// i = w, w + 4, ... (four independent accumulators each, so a long split list is
+// not one serial chain of loads), then meet in LDS in a fixed order.
+__global__ __launch_bounds__(256) void skinny_finish_kernel(const float *__restrict__ part, int S, int64_t M, int RP,
+                                                            int r, float s, uint16_t *__restrict__ out1, int ld1,
+                                                            uint16_t *__restrict__ out2, int ld2) {
+  __shared__ float red[4][64];
+  const int W = ld2 > ld1 ? ld2 : ld1;
+  const int qb = (W + 63) / 64;
+  const int64_t m = blockIdx.x / qb;
+  const int q = 64 * (int)(blockIdx.x % qb) + (threadIdx.x & 63);
+  const int g = threadIdx.x >> 6;
+  float a0 = 0.0f, a1 = 0.0f, a2 = 0.0f, a3 = 0.0f;
+  if (q < r) {
+    const float *src = part + m * RP + q;
+    const int64_t step = (int64_t)M * RP;
+    int i = g;
+    for (; i + 12 < S; i += 16) {
+      a0 += src[(int64_t)i * step];
+      a1 += src[(int64_t)(i + 4) * step];
+      a2 += src[(int64_t)(i + 8) * step];
+      a3 += src[(int64_t)(i + 12) * step];
+    }
+    for (; i < S; i += 4) a0 += src[(int64_t)i * step];
+  }
+  red[g][threadIdx.x & 63] = (a0 + a1) + (a2 + a3);
+  __syncthreads();
+  if (g != 0 || m >= M) return;
+  const float acc = (red[0][threadIdx.x] + red[1][threadIdx.x]) + (red[2][threadIdx.x] + red[3][threadIdx.x]);
   if (out1 && q < ld1) out1[m * ld1 + q] = q < r ? to_bf16(acc) : (uint16_t)0;
   if (out2 && q < ld2) out2[m * ld2 + q] = q < r ? to_bf16(s * acc) : (uint16_t)0;
 }
@@ -502,18 +521,26 @@ FwdLayout fwd_layout(int64_t M, int64_t h, int64_t o, int r) {
 struct BwdLayout {
   int RP16, RP64;
   Split sk, gs;
-  size_t off_part, off_u, off_su, off_l1p, off_g, off_cnt, total;
+  int dxc;  // few-token path (M <= 16): row chunks of the dX partial sums
+  size_t off_part, off_u, off_su, off_l1p, off_g, off_cnt, off_dxp, total;
 };
+
+int gemv_dx_chunks(int64_t M, int64_t h, int64_t o);
 
 BwdLayout bwd_layout(int64_t M, int64_t h, int64_t o, int r) {
   BwdLayout L{};
+  size_t off = 0;
+  auto take = [&](size_t bytes) { size_t at = off; off += rup((int64_t)bytes, 256); return at; };
+  if (M <= 16) {
+    L.dxc = gemv_dx_chunks(M, h, o);
+    L.off_dxp = take((size_t)L.dxc * M * h * 4);
+  }
+  L.total = off;
   if (r == 0) return L;
   L.RP16 = (int)rup(r, 16);
   L.RP64 = (int)rup(r, 64);
   L.sk = skinny_split(M, o);
   L.gs = grad_split(M, h + o);
-  size_t off = 0;
-  auto take = [&](size_t bytes) { size_t at = off; off += rup((int64_t)bytes, 256); return at; };
   L.off_part = take((size_t)L.sk.S * M * L.RP16 * 4);
   L.off_u = take((size_t)M * L.RP16 * 2);
   L.off_su = take((size_t)M * L.RP64 * 2);
@@ -543,7 +570,7 @@ void skinny(const uint16_t *A, int64_t lda, int64_t M, int64_t K, const uint16_t
 #undef QL_SK
   }
   const int W = ld2 > ld1 ? ld2 : ld1;
-  skinny_finish_kernel<<<(unsigned)cdiv(M * W, 256), 256, 0, st>>>(part, sp.S, M, RP16, r, s, out1, ld1, out2, ld2);
+  skinny_finish_kernel<<<(unsigned)(M * cdiv(W, 64)), 256, 0, st>>>(part, sp.S, M, RP16, r, s, out1, ld1, out2, ld2);
 }
 
 void lora_grad(const GradProblem &pa, const GradProblem &pb, int r, float s, int64_t M, int RP16, const Split &sp,
@@ -604,6 +631,209 @@ struct TimedLaunch {
     if (t_ev[k][1]) (void)hipEventRecord(t_ev[k][1], st);
   }
 };
+
+// ---------------------------------------------------------------------------
+// Few-token backward: dX = dY·Ŵᵀ + s·U·L1ᵀ for M <= 16 ([MC] "One training
+// step": gradients flow through the frozen dequantized weight; [TT] §4).
+// HBM-bound like the forward GEMV, but the sum runs down the columns of the
+// stored [o][h] weight.  A workgroup takes 512 columns (64 lanes x 8) and a
+// chunk of rows; wave w takes the row pairs w, w + 4, ... of the chunk, so the
+// four waves read 256 contiguous code bytes from each of 8 rows per step and
+// the column-neighbour workgroups read the rest of those rows at the same
+// time.  Per pair (n, n+1) a lane decodes its 8 columns of both rows to
+// bf16(level * a_hat), packs the two rows' values of each column into a bf16
+// pair and accumulates dY[m][n..n+1] . pair with one v_dot2 per (token,
+// column).  Codes and scales are loaded four (two for 16 tokens) pairs ahead
+// into a ring of register sets; dY pairs are wave-uniform (scalar loads).  The four waves'
+// sums meet in LDS and each workgroup writes one float32 partial; the finish
+// kernel sums the row chunks in order (deterministic), adds s·U·L1ᵀ and rounds
+// to bf16.
+// ---------------------------------------------------------------------------
+struct GvdParams {
+  const uint16_t *dY;  // [M][ldy] bf16
+  int64_t ldy;
+  int M;
+  const uint8_t *codes;
+  const int8_t *qabsmax;
+  const float *scale2;
+  const float *mean;
+  int64_t h, o;  // W is [o][h]
+  int rows;      // rows per chunk (even)
+  float *part;   // [chunks][M][h]
+  float level[16];
+};
+
+constexpr int kGvdCols = 512;  // columns per workgroup
+
+int gemv_dx_chunks(int64_t M, int64_t h, int64_t o) {
+  // about 1024 workgroups (512 for more than 4 tokens, whose partial sums cost more),
+  // at least 64 rows per chunk
+  const int64_t ct = (h + kGvdCols - 1) / kGvdCols;
+  const int64_t target = M <= 4 ? 1024 : 512;
+  int64_t rc = (target + ct - 1) / ct;
+  const int64_t maxc = o / 64 > 0 ? o / 64 : 1;
+  rc = rc < 1 ? 1 : (rc > maxc ? maxc : rc);
+  const int64_t rows = rup((o + rc - 1) / rc, 2);
+  return (int)((o + rows - 1) / rows);
+}
+
+template <int MT>
+struct GvdIn {
+  uint32_t c0, c1;  // 8 codes of rows n and n+1
+  int q0, q1;       // their int8 block scales
+  float s0, s1;     // second-level scales
+  uint32_t dy[MT];  // dY[m][n..n+1] (wave-uniform)
+};
+
+template <int MT>
+__global__ __launch_bounds__(256) void nf4_gemv_dx_kernel(GvdParams p) {
+  constexpr int RW = 8 * (MT < 4 ? MT : 4) + 1;  // floats per lane in the LDS reduction
+  __shared__ f32x2 lv2[256];
+  __shared__ float red[4][64][RW];
+  // wave index in a scalar register: row addresses (and so the dY loads) are wave-uniform
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  lv2[tid] = f32x2{p.level[tid >> 4], p.level[tid & 15]};
+  __syncthreads();
+  const int64_t h = p.h, nblk = h >> 6;
+  int64_t k0 = (int64_t)blockIdx.x * kGvdCols + 8 * lane;
+  const bool live = k0 < h;  // h is a multiple of 64, so a lane's 8 columns are all in or all out
+  k0 = live ? k0 : h - 8;    // out-of-range lanes read valid data and store nothing
+  const int64_t n0 = (int64_t)blockIdx.y * p.rows;
+  const int64_t n1 = n0 + p.rows < p.o ? n0 + p.rows : p.o;
+  const int npairs = (int)((n1 - n0) >> 1);
+  const int cnt = npairs > wave ? (npairs - wave + 3) >> 2 : 0;  // pairs of this wave
+  const float mu = *p.mean;
+  const int64_t kb = k0 >> 6;
+
+  auto load = [&](int j, GvdIn<MT> &in) {
+    const int jj = j < cnt ? j : (cnt > 0 ? cnt - 1 : 0);
+    int64_t n = n0 + 2 * (wave + 4 * (int64_t)jj);
+    n = n < n1 - 2 ? n : n1 - 2;  // a wave without pairs reads the chunk's last pair and uses nothing
+    in.c0 = *reinterpret_cast<const uint32_t *>(p.codes + ((n * h + k0) >> 1));
+    in.c1 = *reinterpret_cast<const uint32_t *>(p.codes + (((n + 1) * h + k0) >> 1));
+    const int64_t b0 = n * nblk + kb, b1 = b0 + nblk;
+    in.q0 = p.qabsmax[b0];
+    in.q1 = p.qabsmax[b1];
+    in.s0 = p.scale2[b0 / kChunk];
+    in.s1 = p.scale2[b1 / kChunk];
+#pragma unroll
+    for (int m = 0; m < MT; ++m) {
+      const int mm = m < p.M ? m : p.M - 1;  // rows past M are computed from a valid row and dropped
+      in.dy[m] = *reinterpret_cast<const uint32_t *>(p.dY + mm * p.ldy + n);
+    }
+  };
+
+  float acc[MT][8];
+#pragma unroll
+  for (int m = 0; m < MT; ++m)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[m][j] = 0.0f;
+
+  auto step = [&](int j, GvdIn<MT> &in) {
+    __builtin_amdgcn_sched_barrier(0);
+    const float a0 = scale_hat((int8_t)in.q0, in.s0, mu), a1 = scale_hat((int8_t)in.q1, in.s1, mu);
+    uint32_t wp[8];
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      const f32x2 l0 = lv2[(in.c0 >> (8 * b)) & 0xFF];
+      const f32x2 l1 = lv2[(in.c1 >> (8 * b)) & 0xFF];
+      wp[2 * b] = pack_bf16x2(l0[0] * a0, l1[0] * a1);
+      wp[2 * b + 1] = pack_bf16x2(l0[1] * a0, l1[1] * a1);
+    }
+#pragma unroll
+    for (int m = 0; m < MT; ++m) {
+#pragma unroll
+      for (int c = 0; c < 8; ++c)
+        acc[m][c] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, in.dy[m]),
+                                                   __builtin_bit_cast(bf16x2, wp[c]), acc[m][c], false);
+    }
+    load(j + (MT <= 4 ? 4 : 2), in);
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
+  // D register sets in a ring, each reloaded D pairs ahead right after its use
+  constexpr int D = MT <= 4 ? 4 : 2;
+  GvdIn<MT> in[D];
+#pragma unroll
+  for (int d = 0; d < D; ++d) load(d, in[d]);
+  int j = 0;
+  for (; j + D - 1 < cnt; j += D) {
+#pragma unroll
+    for (int d = 0; d < D; ++d) step(j + d, in[d]);
+  }
+#pragma unroll
+  for (int d = 0; d < D - 1; ++d)
+    if (j + d < cnt) step(j + d, in[d]);
+
+  // the four waves' sums, four tokens at a time, through LDS
+  float *outp = p.part + ((int64_t)blockIdx.y * p.M) * h;
+#pragma unroll
+  for (int mg = 0; mg < MT; mg += 4) {
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi)
+      if (mg + mi < MT)
+#pragma unroll
+        for (int c = 0; c < 8; ++c) red[wave][lane][8 * mi + c] = acc[mg + mi][c];
+    __syncthreads();
+    const int m = mg + wave;  // thread (wave, lane) sums token mg + wave of lane's 8 columns
+    if (m < MT && m < p.M && live) {
+      float v[8];
+#pragma unroll
+      for (int c = 0; c < 8; ++c)
+        v[c] = red[0][lane][8 * wave + c] + red[1][lane][8 * wave + c] + red[2][lane][8 * wave + c] +
+               red[3][lane][8 * wave + c];
+      float *o = outp + (int64_t)m * h + k0;
+      *reinterpret_cast<f32x4 *>(o) = f32x4{v[0], v[1], v[2], v[3]};
+      *reinterpret_cast<f32x4 *>(o + 4) = f32x4{v[4], v[5], v[6], v[7]};
+    }
+    __syncthreads();
+  }
+}
+
+// dX[m][k..k+7] = bf16(sum of the row-chunk partials + s·U[m]·L1[k..k+7]ᵀ); sU is the
+// s-scaled bf16 U ([M][ldsu]), L1 [h][r] bf16.  Block b takes token b / cg and 64
+// groups of 8 columns; wave w sums the chunks c = w, w + 4, ... and the four waves
+// meet in LDS in a fixed order.
+__global__ __launch_bounds__(256) void gemv_dx_finish_kernel(const float *part, int chunks, int M, int64_t h,
+                                                             const uint16_t *sU, int ldsu, const uint16_t *L1,
+                                                             int r, uint16_t *dX, int64_t ldx) {
+  __shared__ float red[4][64][9];
+  const int64_t groups = h / 8;
+  const int64_t cg = (groups + 63) / 64;
+  const int m = (int)(blockIdx.x / cg);
+  const int64_t grp = 64 * (int64_t)(blockIdx.x % cg) + (threadIdx.x & 63);
+  const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
+  const bool live = grp < groups;
+  const int64_t k = (live ? grp : groups - 1) * 8;
+  float v[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  for (int c = w; c < chunks; c += 4) {
+    const float *src = part + ((int64_t)c * M + m) * h + k;
+    const f32x4 a = *reinterpret_cast<const f32x4 *>(src), b = *reinterpret_cast<const f32x4 *>(src + 4);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[i] += a[i];
+      v[4 + i] += b[i];
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) red[w][l][i] = v[i];
+  __syncthreads();
+  if (w != 0 || !live) return;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) v[i] = (red[0][l][i] + red[1][l][i]) + (red[2][l][i] + red[3][l][i]);
+  if (r > 0) {
+    float t[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    for (int q = 0; q < r; ++q) {
+      const float su = bf16_lo(sU[(int64_t)m * ldsu + q]);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) t[i] += su * bf16_lo(L1[(k + i) * r + q]);
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] += t[i];
+  }
+  *reinterpret_cast<u32x4 *>(dX + (int64_t)m * ldx + k) =
+      u32x4{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7])};
+}
 
 void fill_levels(float *dst, const Nf4Tables &tab) {
   for (int i = 0; i < 16; ++i) dst[i] = tab.level[i];
@@ -691,6 +921,48 @@ hipError_t launch_linear_bwd(const LinearArgs &a, const uint16_t *X, const uint1
     g2 = GradProblem{dY, a.o, a.o, T, a.r, dL2, true, a.o / 64, a.h};
     gpart = at<float>(ws, L.off_g);
     gcnt = cnt;
+  }
+  if (a.M <= 16) {
+    GvdParams vp{};
+    vp.dY = dY; vp.ldy = a.o; vp.M = (int)a.M;
+    vp.codes = a.codes; vp.qabsmax = a.qabsmax; vp.scale2 = a.scale2; vp.mean = a.mean;
+    vp.h = a.h; vp.o = a.o;
+    vp.rows = (int)rup((a.o + L.dxc - 1) / L.dxc, 2);
+    vp.part = at<float>(ws, L.off_dxp);
+    fill_levels(vp.level, tab);
+    const dim3 grid((unsigned)((a.h + kGvdCols - 1) / kGvdCols), (unsigned)L.dxc);
+    auto launch_dx = [&]() {
+      {
+        TimedLaunch tl(1, st);
+        if (a.M == 1) nf4_gemv_dx_kernel<1><<<grid, 256, 0, st>>>(vp);
+        else if (a.M <= 4) nf4_gemv_dx_kernel<4><<<grid, 256, 0, st>>>(vp);
+        else nf4_gemv_dx_kernel<16><<<grid, 256, 0, st>>>(vp);
+      }
+      const int64_t cg = (a.h / 8 + 63) / 64;
+      gemv_dx_finish_kernel<<<(unsigned)(a.M * cg), 256, 0, st>>>(vp.part, L.dxc, (int)a.M, a.h, sU, L.RP64, L1,
+                                                                 a.r, dX, a.h);
+    };
+    if (a.r == 0) {
+      launch_dx();
+      return hipGetLastError();
+    }
+    std::lock_guard<std::mutex> lock(g_side_mu);
+    SideStream *ss = side_stream_locked();
+    hipError_t e = hipSuccess;
+    if (ss) {
+      e = hipEventRecord(ss->fork, st);
+      if (e == hipSuccess) e = hipStreamWaitEvent(ss->s, ss->fork, 0);
+    }
+    if (e != hipSuccess) return e;
+    lora_grad(g1, g2, a.r, a.s, a.M, L.RP16, L.gs, gpart, gcnt, ss ? ss->s : st);
+    launch_dx();
+    e = hipGetLastError();
+    if (ss) {
+      const hipError_t e1 = hipEventRecord(ss->join, ss->s);
+      const hipError_t e2 = e1 == hipSuccess ? hipStreamWaitEvent(st, ss->join, 0) : e1;
+      if (e == hipSuccess) e = e2;
+    }
+    return e;
   }
   GemmParams gp{};
   gp.A = dY; gp.lda = a.o;

@@ -52,6 +52,9 @@ def test_status_strings():
 def test_workspace_sizes():
     assert nf4.workspace_size(nf4.QLORA_OP_DOUBLE_QUANT, 1000) % 256 == 0
     assert nf4.workspace_size(nf4.QLORA_OP_LINEAR_FWD, 16, 1024, 1024, 0) == 0
+    # the few-token backward keeps float32 partial sums of dX even without an adapter
+    assert nf4.workspace_size(nf4.QLORA_OP_LINEAR_BWD, 16, 1024, 1024, 0) >= 16 * 1024 * 4
+    assert nf4.workspace_size(nf4.QLORA_OP_LINEAR_BWD, 17, 1024, 1024, 0) == 0
     for op in (nf4.QLORA_OP_LINEAR_FWD, nf4.QLORA_OP_LINEAR_BWD):
         b = nf4.workspace_size(op, 2048, 4096, 4096, 16)
         assert b > 0 and b % 256 == 0

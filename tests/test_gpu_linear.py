@@ -161,3 +161,18 @@ def test_adjoint_identities_on_gpu_outputs():
     lora = np.sum(f(dy) * (f(Y) - f(Yb)))
     scale = np.sqrt(np.sum(f(dL2) ** 2) * np.sum(f(l2) ** 2))
     assert abs(a1 - a2) <= 2e-2 * scale and abs(a1 - lora) <= 5e-2 * scale
+
+
+FEW_TOKEN_BWD = [  # (M, h, o, r, s): the few-token backward (dX GEMV), several column tiles and row chunks
+    (1, 8192, 4096, 0, 1.0),
+    (2, 4096, 11008, 64, 0.25),
+    (4, 1536, 2048, 8, 2.0),
+    (9, 11008, 4096, 16, 2.0),
+    (16, 2560, 1088, 128, 0.5),
+]
+
+
+@pytest.mark.parametrize("M,h,o,r,s", FEW_TOKEN_BWD)
+def test_few_token_backward(M, h, o, r, s):
+    w, l1, l2, x, dy = wl.small_linear(h, o, r, M, seed=3 * M + h + r)
+    check_full(w, l1, l2, x, dy, s, f"few-token M={M} h={h} o={o} r={r}")

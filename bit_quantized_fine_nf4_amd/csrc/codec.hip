@@ -411,27 +411,28 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeParams p, Nf4Tables tab
 // symmetric int8 scheme).
 //
 // The mean of the block scales is computed exactly: every float32 is an
-// integer multiple of 2^-149, so the sum is an integer that the kernels
-// accumulate without rounding, binned by exponent, and the one rounding
-// happens at the very end (mean_from_bins, run by the last workgroup).  Each
-// lane keeps a private 64-bit accumulator for an 8-exponent window anchored at
-// its first value; a value outside the window goes straight to its exponent
-// bin.  Bins live in LDS per workgroup and are flushed with atomics into one of
-// kSlots copies of the global uint64 bins (workgroup index modulo kSlots), so
-// no single address sees more than grid/kSlots atomics; the last workgroup
-// sums the copies.  Integer addition is associative, so the result does not
-// depend on the order.
+// integer multiple of 2^-149, so their sum is an integer, accumulated without
+// rounding and rounded once at the very end.  Two launches, with no
+// cross-workgroup counter and nothing to clear beforehand:
+//  dq_partial_kernel  each workgroup sums its share of the scales exactly and
+//                     writes that integer as kLimbs 64-bit limbs (limb j holds
+//                     bits [32j, 32j + 32), unnormalised, so it may exceed
+//                     2^32) into its own slot of the workspace.  Inside the
+//                     workgroup each lane keeps a 64-bit accumulator for an
+//                     8-exponent window anchored at its first nonzero value;
+//                     a value outside the window goes to its LDS exponent bin.
+//  dq_chunks_kernel   every workgroup issues the loads of its first chunks'
+//                     scales, adds the limbs of all slots, carries, divides by
+//                     the count with correct rounding (mean_from_limbs) and
+//                     quantizes its chunks; workgroup 0 also stores the mean.
+//                     Integer addition is exact, so every workgroup derives
+//                     the same mean whatever the order of the additions.
 // ---------------------------------------------------------------------------
 
 constexpr int kNumBins = 264;  // bin s holds integers in units of 2^(s-149)
-constexpr int kSlots = 16;     // copies of the global bins
-constexpr int kDqGrid = 512;   // workgroups of the binning pass (at most)
+constexpr int kDqGrid = 512;   // workgroups of the partial-sum pass (at most)
+constexpr int kDqChGrid = 1024;  // workgroups of the chunk pass (at most; they loop)
 constexpr int kLimbs = 12;     // the exact sum is below 2^(64+263): 11 32-bit limbs suffice
-
-__global__ void zero_u64_kernel(unsigned long long *p, int n) {
-  int i = blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < n) p[i] = 0ull;
-}
 
 QL_DEV void split_f32(float a, uint32_t &mant, int &shift) {
   uint32_t b = __builtin_bit_cast(uint32_t, a);
@@ -440,25 +441,8 @@ QL_DEV void split_f32(float a, uint32_t &mant, int &shift) {
   shift = e ? (int)e - 1 : 0;  // value = mant * 2^(shift - 149)
 }
 
-// mean = RNE_f32(S / nb) with S = sum_s bins[s] * 2^(s-149), computed by one workgroup.
-QL_DEV void mean_from_bins(const unsigned long long *b /* LDS, kNumBins */, int64_t nb, float *mean_out) {
-  __shared__ unsigned long long csum[kLimbs];
-  const int tid = threadIdx.x;
-  if (tid < kLimbs) {
-    // limb tid collects the bits of every bins[s] << s that fall in [32*tid, 32*tid + 32)
-    const int j = tid;
-    unsigned long long c = 0;
-    const int s_lo = 32 * j - 63 > 0 ? 32 * j - 63 : 0;
-    const int s_hi = 32 * j + 31 < kNumBins - 1 ? 32 * j + 31 : kNumBins - 1;
-    for (int sidx = s_lo; sidx <= s_hi; ++sidx) {
-      const unsigned long long v = b[sidx];
-      const int sh = sidx - 32 * j;
-      c += (uint32_t)(sh >= 0 ? (v << sh) : (v >> -sh));
-    }
-    csum[j] = c;
-  }
-  __syncthreads();
-  if (tid != 0) return;
+// RNE_f32(S / nb) for S = sum_j csum[j] * 2^(32j) in units of 2^-149 (csum[j] < 2^63).
+QL_DEV float mean_from_limbs(const unsigned long long *csum, int64_t nb) {
   uint32_t S[kLimbs];
   unsigned long long carry = 0;
   for (int j = 0; j < kLimbs; ++j) {
@@ -468,7 +452,7 @@ QL_DEV void mean_from_bins(const unsigned long long *b /* LDS, kNumBins */, int6
   }
   int top = kLimbs - 1;
   while (top >= 0 && S[top] == 0) --top;
-  if (top < 0) { *mean_out = 0.0f; return; }
+  if (top < 0) return 0.0f;
   const int bitsS = 32 * top + 32 - __builtin_clz(S[top]);
   // W = S >> e keeps the top 96 bits; sticky0 records whether anything below was dropped
   const int e = bitsS > 96 ? bitsS - 96 : 0;
@@ -496,8 +480,7 @@ QL_DEV void mean_from_bins(const unsigned long long *b /* LDS, kNumBins */, int6
     if (Q[k]) { bitsQ = 32 * k + 32 - __builtin_clz(Q[k]); break; }
   if (bitsQ == 0) {  // S/nb < 2^-149 * 1: rounds to 0 or the smallest denormal
     const bool up = 2 * rem > den || (2 * rem == den && sticky0);
-    *mean_out = up ? ldexpf(1.0f, -149) : 0.0f;
-    return;
+    return up ? ldexpf(1.0f, -149) : 0.0f;
   }
   // value = (Q + frac) * 2^(e - 149); leading bit exponent E, float32 quantum 2^qe
   const int E = bitsQ - 1 + e - 149;
@@ -513,18 +496,16 @@ QL_DEV void mean_from_bins(const unsigned long long *b /* LDS, kNumBins */, int6
     up = half && (lower || (mant & 1ull));
   }
   if (up) ++mant;
-  *mean_out = ldexpf((float)mant, qe);
+  return ldexpf((float)mant, qe);
 }
 
-// Exact sum of the block scales into exponent bins; the last workgroup to finish turns
-// the bins into the rounded mean.  gbins holds kSlots copies of the bins followed by the
-// completion counter.
-__global__ __launch_bounds__(256) void dq_bins_kernel(const float *__restrict__ absmax, int64_t nb,
-                                                      unsigned long long *__restrict__ gbins,
-                                                      float *__restrict__ mean_out) {
+// Exact sum of this workgroup's share of the scales -> partial[blockIdx.x][kLimbs].
+__global__ __launch_bounds__(256) void dq_partial_kernel(const float *__restrict__ absmax, int64_t nb,
+                                                         unsigned long long *__restrict__ partial) {
   __shared__ unsigned long long bins[kNumBins];
-  __shared__ bool last;
+  __shared__ unsigned long long limbs[kLimbs];
   for (int i = threadIdx.x; i < kNumBins; i += blockDim.x) bins[i] = 0ull;
+  if (threadIdx.x < kLimbs) limbs[threadIdx.x] = 0ull;
   __syncthreads();
 
   const int64_t tid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -558,71 +539,92 @@ __global__ __launch_bounds__(256) void dq_bins_kernel(const float *__restrict__ 
   for (int64_t i = (nvec << 2) + tid; i < nb; i += nthr) add(absmax[i]);
   if (anchor >= 0 && acc) atomicAdd(&bins[anchor], acc);
   __syncthreads();
-  for (int i = threadIdx.x; i < kNumBins; i += blockDim.x)
-    if (bins[i]) atomicAdd(&gbins[(blockIdx.x % kSlots) * kNumBins + i], bins[i]);
-  // The bins only ever change through device atomics, which are coherent
-  // across the XCDs: waiting until this workgroup's atomics are acknowledged
-  // is enough before counting in (no device-wide cache writeback).
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  if (threadIdx.x == 0)
-    last = atomicAdd(&gbins[kSlots * kNumBins], 1ull) == (unsigned long long)(gridDim.x - 1);
-  __syncthreads();
-  if (!last) return;
-  for (int i = threadIdx.x; i < kNumBins; i += blockDim.x) {
-    unsigned long long t = 0;
-    for (int k = 0; k < kSlots; ++k)
-      t += __hip_atomic_load(&gbins[k * kNumBins + i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    bins[i] = t;
+  // bin s holds v * 2^s (units of 2^-149), i.e. bits [s, s + 64): pieces of limbs s/32 .. s/32 + 2
+  for (int s = threadIdx.x; s < kNumBins; s += blockDim.x) {
+    const unsigned long long v = bins[s];
+    if (!v) continue;
+    const int a = s >> 5, b = s & 31;
+    const unsigned long long lo = v << b;                       // low 64 bits of v * 2^b
+    const unsigned long long hi = b ? (v >> (64 - b)) : 0ull;  // the bits above them
+    atomicAdd(&limbs[a], lo & 0xFFFFFFFFull);
+    atomicAdd(&limbs[a + 1], lo >> 32);
+    if (hi) atomicAdd(&limbs[a + 2], hi);
   }
   __syncthreads();
-  mean_from_bins(bins, nb, mean_out);
+  if (threadIdx.x < kLimbs) partial[(int64_t)blockIdx.x * kLimbs + threadIdx.x] = limbs[threadIdx.x];
 }
 
 // One wave per chunk of 256 scales: c = fp32(a - mean); s2 = fp32(max|c| / 127);
 // q = rint(fp32(c / s2)) clamped to [-127, 127]; s2 == 0 gives q = 0.
 __global__ __launch_bounds__(256) void dq_chunks_kernel(const float *__restrict__ absmax, int64_t nb,
-                                                        const float *__restrict__ mean_in,
-                                                        int8_t *__restrict__ qabsmax,
-                                                        float *__restrict__ scale2) {
-  const int lane = threadIdx.x & 63;
-  const int64_t chunk = (int64_t)blockIdx.x * (blockDim.x / 64) + (threadIdx.x >> 6);
+                                                        const unsigned long long *__restrict__ partial,
+                                                        int nparts, int8_t *__restrict__ qabsmax,
+                                                        float *__restrict__ scale2, float *__restrict__ mean_out) {
+  __shared__ unsigned long long csum[kLimbs];
+  __shared__ float mean_s;
+  const int tid = threadIdx.x, lane = tid & 63;
   const int64_t nch = (nb + kChunk - 1) / kChunk;
-  if (chunk >= nch) return;
-  const float mu = *mean_in;
-  const int64_t i0 = chunk * kChunk + lane * 4;
-  float c[4];
-  if (i0 + 4 <= nb) {
-    f32x4 a = *reinterpret_cast<const f32x4 *>(absmax + i0);
+  const int64_t cstep = (int64_t)gridDim.x * 4;
+  int64_t chunk = (int64_t)blockIdx.x * 4 + (tid >> 6);
+  // this lane's four scales of its first chunk, in flight while the mean is formed
+  auto load4 = [&](int64_t ch, float (&a)[4]) {
+    const int64_t i0 = ch * kChunk + lane * 4;
+    if (ch < nch && i0 + 4 <= nb) {
+      const f32x4 v = *reinterpret_cast<const f32x4 *>(absmax + i0);
 #pragma unroll
-    for (int k = 0; k < 4; ++k) c[k] = a[k] - mu;
-  } else {
+      for (int k = 0; k < 4; ++k) a[k] = v[k];
+    } else {
 #pragma unroll
-    for (int k = 0; k < 4; ++k) c[k] = (i0 + k < nb) ? absmax[i0 + k] - mu : 0.0f;
-  }
-  float m = fmaxf(fmaxf(fabsf(c[0]), fabsf(c[1])), fmaxf(fabsf(c[2]), fabsf(c[3])));
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
-  const float s2 = m / 127.0f;
-  uint32_t word = 0;
-#pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    int q = 0;
-    if (s2 != 0.0f) {
-      float r = rintf(c[k] / s2);
-      r = fminf(fmaxf(r, -127.0f), 127.0f);
-      q = (int)r;
+      for (int k = 0; k < 4; ++k) a[k] = (ch < nch && i0 + k < nb) ? absmax[i0 + k] : 0.0f;
     }
-    word |= ((uint32_t)(q & 0xFF)) << (8 * k);
+  };
+  float a[4];
+  load4(chunk, a);
+  if (tid < kLimbs) csum[tid] = 0ull;
+  __syncthreads();
+  constexpr int kLanesPerLimb = 256 / kLimbs;  // 21
+  if (tid < kLanesPerLimb * kLimbs) {
+    const int j = tid % kLimbs;
+    unsigned long long t = 0;
+    for (int p = tid / kLimbs; p < nparts; p += kLanesPerLimb) t += partial[(int64_t)p * kLimbs + j];
+    if (t) atomicAdd(&csum[j], t);
   }
-  if (i0 + 4 <= nb) {
-    *reinterpret_cast<uint32_t *>(qabsmax + i0) = word;
-  } else {
-    for (int k = 0; k < 4; ++k)
-      if (i0 + k < nb) qabsmax[i0 + k] = (int8_t)(word >> (8 * k));
+  __syncthreads();
+  if (tid == 0) {
+    mean_s = mean_from_limbs(csum, nb);
+    if (blockIdx.x == 0) *mean_out = mean_s;
   }
-  if (lane == 0) scale2[chunk] = s2;
+  __syncthreads();
+  const float mu = mean_s;
+  for (; chunk < nch; chunk += cstep) {
+    const int64_t i0 = chunk * kChunk + lane * 4;
+    float c[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) c[k] = (i0 + k < nb) ? a[k] - mu : 0.0f;
+    float m = fmaxf(fmaxf(fabsf(c[0]), fabsf(c[1])), fmaxf(fabsf(c[2]), fabsf(c[3])));
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
+    const float s2 = m / 127.0f;
+    uint32_t word = 0;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      int q = 0;
+      if (s2 != 0.0f) {
+        float r = rintf(c[k] / s2);
+        r = fminf(fmaxf(r, -127.0f), 127.0f);
+        q = (int)r;
+      }
+      word |= ((uint32_t)(q & 0xFF)) << (8 * k);
+    }
+    if (i0 + 4 <= nb) {
+      *reinterpret_cast<uint32_t *>(qabsmax + i0) = word;
+    } else {
+      for (int k = 0; k < 4; ++k)
+        if (i0 + k < nb) qabsmax[i0 + k] = (int8_t)(word >> (8 * k));
+    }
+    if (lane == 0) scale2[chunk] = s2;
+    if (chunk + cstep < nch) load4(chunk + cstep, a);
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -744,16 +746,16 @@ hipError_t launch_quantize(const void *w, bool bf16, int64_t n, uint8_t *codes, 
   return hipGetLastError();
 }
 
-size_t dq_workspace_bytes() { return ((size_t)(kSlots * kNumBins + 1) * 8 + 255) / 256 * 256; }
+size_t dq_workspace_bytes() { return ((size_t)kDqGrid * kLimbs * 8 + 255) / 256 * 256; }
 
 hipError_t launch_double_quant(const float *absmax, int64_t nb, int8_t *qabsmax, float *scale2,
                                float *mean, void *ws, hipStream_t st) {
-  auto *bins = reinterpret_cast<unsigned long long *>(ws);
-  zero_u64_kernel<<<(kSlots * kNumBins + 1 + 255) / 256, 256, 0, st>>>(bins, kSlots * kNumBins + 1);
+  auto *partial = reinterpret_cast<unsigned long long *>(ws);
   const int grid = grid_for(nb, 256 * 16, kDqGrid);
-  dq_bins_kernel<<<grid, 256, 0, st>>>(absmax, nb, bins, mean);
+  dq_partial_kernel<<<grid, 256, 0, st>>>(absmax, nb, partial);
   const int64_t nch = (nb + kChunk - 1) / kChunk;
-  dq_chunks_kernel<<<(int)((nch + 3) / 4), 256, 0, st>>>(absmax, nb, mean, qabsmax, scale2);
+  const int cgrid = grid_for(nch, 4, kDqChGrid);
+  dq_chunks_kernel<<<cgrid, 256, 0, st>>>(absmax, nb, partial, grid, qabsmax, scale2, mean);
   return hipGetLastError();
 }
 

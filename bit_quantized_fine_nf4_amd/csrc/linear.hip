@@ -5,11 +5,11 @@
 // block scale and hands bf16 values to the matrix cores.
 //
 // Kernels
-//   relayout_kernel      tiny bf16 transposes / zero padding of L1, L2
-//   skinny_kernel        P = A·Bt^T for a narrow Bt (the rank-r products
-//                        X·L1 and dY·L2^T), MFMA 16x16x32, split-K partials
-//   skinny_finish        sums the partials, rounds to bf16 (T or U) and
-//                        writes the s-scaled copy the GEMM epilogue uses
+//   rank_r_kernel        the rank-r products T = X·L1 and U = dY·L2^T in one
+//                        launch each (MFMA 16x16x32, K split over the 16
+//                        waves of a workgroup, fixed-order LDS sum), rounded
+//                        to bf16 with the s-scaled copy the GEMM's rank-r
+//                        step uses
 //   nf4_gemm_kernel      fused dequant-GEMM, MFMA 32x32x16: forward
 //                        (B = W_hat, K along h) and dX (B = W_hat^T, K
 //                        along o); the rank-r LoRA product is added as extra
@@ -46,23 +46,26 @@ QL_DEV f32x4 mfma16(u32x4 a, u32x4 b, f32x4 c) {
 
 QL_DEV uint16_t to_bf16(float v) { return (uint16_t)(pack_bf16x2(v, 0.0f) & 0xFFFFu); }
 
-}  // namespace
-
-// ---------------------------------------------------------------------------
-// dst[a][b] = (a < av && b < bv) ? (trans ? src[b*lds + a] : src[a*lds + b]) : 0
-// Also clears nzero completion counters used later in the same call.
-// ---------------------------------------------------------------------------
-__global__ void relayout_kernel(const uint16_t *__restrict__ src, int64_t lds, bool trans, int64_t A,
-                                int64_t B, int64_t av, int64_t bv, uint16_t *__restrict__ dst,
-                                unsigned *__restrict__ zero, int nzero) {
-  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (idx < nzero) zero[idx] = 0u;
-  if (idx >= A * B) return;
-  const int64_t a = idx / B, b = idx % B;
-  uint16_t v = 0;
-  if (a < av && b < bv) v = trans ? src[b * lds + a] : src[a * lds + b];
-  dst[idx] = v;
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+// Two transposing LDS reads (ds_read_b64_tr_b16), 4 rows each: in every 16-lane
+// group, lane 4j + q names the 8 bytes at row j, columns 4q..4q+3 of a 4 x 16
+// bf16 block and lane i receives the block's column i (4 values per read).
+QL_DEV u32x4 tr_pair(const uint16_t *lo, const uint16_t *hi) {
+  typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+  const s16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(lo));
+  const s16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(hi));
+  const u32x2 ua = __builtin_bit_cast(u32x2, a), ub = __builtin_bit_cast(u32x2, b);
+  return u32x4{ua[0], ua[1], ub[0], ub[1]};
 }
+
+// Buffer resource over [base, base + bytes): loads past the end return zero.
+QL_DEV __amdgpu_buffer_rsrc_t gv_rsrc(const void *base, int64_t bytes) {
+  const int64_t cap = 0x7FFFFFF0;
+  const int32_t n = (int32_t)(bytes < 0 ? 0 : (bytes > cap ? cap : bytes));
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, n, 0x00020000);
+}
+
+}  // namespace
 
 // Cross-workgroup split reduction.  Partials travel through device-coherent
 // accesses (agent-scope stores and loads bypass the per-XCD L2s), so no
@@ -83,82 +86,153 @@ QL_DEV bool last_of_splits(unsigned *cnt, unsigned splits) {
 }
 
 // ---------------------------------------------------------------------------
-// Rank-r products (T = X·L1, U = dY·L2^T).  part[s][m][q] = sum over split s
-// of A[m][k] * Bt[q][k].  A wave owns 16 rows and all NT*16 columns; operands
-// come straight from global memory in MFMA fragment order (16 B per lane per
-// K step).  A separate finish pass sums the splits: a split reduction inside
-// this kernel would leave one workgroup per token tile with a serial tail.
+// Rank-r products T = X·L1 (forward) and U = dY·L2^T (backward) in one launch
+// ([MC] "The algebra", Eq. 3: the adapter's down projection; [TT] §4).  A
+// workgroup owns `rows` (16, 8 or 4: enough workgroups to cover every compute
+// unit; the MFMA rows past them read as zero) rows and the whole K; its 16
+// waves split K into equal runs
+// of 32-wide steps, accumulate with 16x16x32 MFMAs and meet in LDS, where the
+// sum over the waves runs in a fixed order (deterministic, with no partial
+// sums in HBM and no second launch).  A operand: lane (i, g) loads 16 bytes of
+// row i at k + 8g, D steps ahead; rows past M read as zero.  B operand: the
+// backward's L2 [r][o] is k-contiguous, so its fragments are 16-byte loads of
+// L2 rows; the forward's L1 [h][r] is r-contiguous, so each step's 32 x r
+// slab (contiguous in memory) is copied into the wave's own LDS area and
+// gathered column by column.
+// Outputs: out1[m][q] = bf16(sum) (zero for r <= q < ld1) and
+// out2[m][q] = bf16(s * sum) (zero for q >= r).  The backward launch also
+// writes the zero-padded copy L1p [h][ldp] of L1 that the dX GEMM's rank-r
+// step reads, and clears the adapter-gradient split counters.
 // ---------------------------------------------------------------------------
-template <int NT>
-__global__ __launch_bounds__(256) void skinny_kernel(const uint16_t *__restrict__ A, int64_t lda, int64_t M,
-                                                     int64_t K, const uint16_t *__restrict__ Bt, int64_t ldb,
-                                                     int rvalid, int64_t kchunk, float *__restrict__ part) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int64_t m0 = (int64_t)blockIdx.x * 64 + wave * 16;
-  const int64_t kb = (int64_t)blockIdx.y * kchunk;
-  const int64_t ke = kb + kchunk < K ? kb + kchunk : K;
-  const int g = lane >> 4, r16 = lane & 15;
-  const int64_t m = m0 + r16;
-  const bool mok = m < M;
+struct RankParams {
+  const uint16_t *A;  // [M][lda] bf16
+  int64_t lda, M, K;  // K: a multiple of 32
+  const uint16_t *B;  // forward: L1 [K][r]; backward: L2 [r][ldb]
+  int64_t ldb;
+  int r;
+  int rows;  // rows per workgroup: 16, 8 or 4
+  float s;
+  uint16_t *out1;
+  int ld1;
+  uint16_t *out2;
+  int ld2;
+  // backward only (L1p == nullptr otherwise)
+  const uint16_t *L1;
+  int64_t h;
+  int ldp;
+  uint16_t *L1p;
+  unsigned *cnt;
+  int ncnt;
+};
+
+constexpr int kRankWaves = 16;
+
+template <int NT, bool KN>
+__global__ __launch_bounds__(1024) void rank_r_kernel(RankParams p) {
+  constexpr int D = NT <= 4 ? 4 : 2;  // steps whose loads are in flight together
+  constexpr int RP = NT * 16;
+  constexpr int SLAB = 32 * RP * 2;                    // bytes of one wave's L1 slab (32 rows of r <= RP)
+  constexpr int RED = 16 * RP * 4;                     // bytes of one wave's partial sums
+  constexpr int LDS = kRankWaves * (SLAB > RED ? SLAB : RED);
+  __shared__ __attribute__((aligned(16))) char lds[LDS];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = lane >> 4, i16 = lane & 15;
+  const int r = p.r;
+
+  const int64_t m0 = (int64_t)blockIdx.x * p.rows;
+  const int64_t mrows = p.M - m0 < p.rows ? p.M - m0 : p.rows;
+  const auto rA = gv_rsrc(p.A + m0 * p.lda, mrows * p.lda * 2);
+  const int voffA = (int)((i16 * p.lda + 8 * g) * 2);
+  const auto rB = KN ? gv_rsrc(p.B, p.K * r * 2) : gv_rsrc(p.B, (int64_t)r * p.ldb * 2);
+  const int64_t ksteps = p.K >> 5;
+  const int64_t per = (ksteps + kRankWaves - 1) / kRankWaves;
+  const int64_t s0 = wave * per, s1 = s0 + per < ksteps ? s0 + per : ksteps;
+  char *slab = lds + wave * SLAB;
+
   f32x4 acc[NT];
 #pragma unroll
   for (int t = 0; t < NT; ++t) acc[t] = f32x4{0, 0, 0, 0};
-  const uint16_t *arow = A + (mok ? m : 0) * lda + 8 * g;
-#pragma unroll 2
-  for (int64_t k = kb; k < ke; k += 32) {
-    u32x4 a = mok ? *reinterpret_cast<const u32x4 *>(arow + k) : u32x4{0, 0, 0, 0};
+
+  for (int64_t sb = s0; sb < s1; sb += D) {
+    u32x4 a[D], b[D][NT];
 #pragma unroll
-    for (int t = 0; t < NT; ++t) {
-      const int q = t * 16 + r16;
-      u32x4 b = q < rvalid ? *reinterpret_cast<const u32x4 *>(Bt + (int64_t)q * ldb + k + 8 * g)
-                           : u32x4{0, 0, 0, 0};
-      acc[t] = mfma16(a, b, acc[t]);
+    for (int u = 0; u < D; ++u) {
+      const int64_t st = sb + u;
+      if (st < s1) {  // wave-uniform
+        const int ko = __builtin_amdgcn_readfirstlane((int)(st * 64));      // byte offset of k = 32 st
+        const int so = __builtin_amdgcn_readfirstlane((int)(st * 64 * r));  // byte offset of its L1 slab
+        a[u] = __builtin_amdgcn_raw_buffer_load_b128(rA, voffA, ko, 0);
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+          if (KN)  // 16-byte chunk lane + 64 t of the slab (64 r bytes)
+            b[u][t] = __builtin_amdgcn_raw_buffer_load_b128(rB, (lane + 64 * t) * 16, so, 0);
+          else     // L2 row 16 t + i16, k = 32 st + 8 g
+            b[u][t] = __builtin_amdgcn_raw_buffer_load_b128(rB, (int)(((16 * t + i16) * p.ldb + 8 * g) * 2), ko, 0);
+        }
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < D; ++u) {
+      if (sb + u < s1) {
+        if (KN) {
+          // The slab is stored as 16-byte words and read back as bf16 values by other lanes of
+          // this wave: the empty asm statements keep the compiler from moving the reads across
+          // the stores (type-based alias analysis would allow it); a wave's LDS accesses execute
+          // in order, so no hardware barrier is needed.
+          asm volatile("" ::: "memory");
+#pragma unroll
+          for (int t = 0; t < NT; ++t)
+            if ((lane + 64 * t) * 16 < 64 * r) *reinterpret_cast<u32x4 *>(slab + (lane + 64 * t) * 16) = b[u][t];
+          asm volatile("" ::: "memory");
+          const uint16_t *sl = reinterpret_cast<const uint16_t *>(slab);
+#pragma unroll
+          for (int t = 0; t < NT; ++t) {
+            const int q = 16 * t + i16;
+            uint32_t w[4];
+#pragma unroll
+            for (int x = 0; x < 4; ++x) {  // unconditional reads inside the slab area, masked after
+              const uint32_t lo = sl[(8 * g + 2 * x) * r + q], hi = sl[(8 * g + 2 * x + 1) * r + q];
+              w[x] = q < r ? lo | (hi << 16) : 0u;
+            }
+            acc[t] = mfma16(a[u], u32x4{w[0], w[1], w[2], w[3]}, acc[t]);
+          }
+        } else {
+#pragma unroll
+          for (int t = 0; t < NT; ++t) acc[t] = mfma16(a[u], b[u][t], acc[t]);
+        }
+      }
     }
   }
-  constexpr int RP = NT * 16;
-  float *out = part + (int64_t)blockIdx.y * M * RP;
+
+  // the waves' sums meet in LDS: red[w][row][q], row = 4g + v, q = 16t + i16
+  __syncthreads();
+  float *red = reinterpret_cast<float *>(lds);
 #pragma unroll
   for (int t = 0; t < NT; ++t)
 #pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const int64_t row = m0 + 4 * g + v;
-      if (row < M) out[row * RP + t * 16 + r16] = acc[t][v];
-    }
-}
-
-// out1[m][q] = bf16(sum) for q < ld1 (zero for r <= q < ld1)
-// out2[m][q] = bf16(s * sum) for q < ld2 (zero for q >= r)
-// Block b takes token b / qb and 64 columns q; its four waves sum the splits
-// i = w, w + 4, ... (four independent accumulators each, so a long split list is
-// not one serial chain of loads), then meet in LDS in a fixed order.
-__global__ __launch_bounds__(256) void skinny_finish_kernel(const float *__restrict__ part, int S, int64_t M, int RP,
-                                                            int r, float s, uint16_t *__restrict__ out1, int ld1,
-                                                            uint16_t *__restrict__ out2, int ld2) {
-  __shared__ float red[4][64];
-  const int W = ld2 > ld1 ? ld2 : ld1;
-  const int qb = (W + 63) / 64;
-  const int64_t m = blockIdx.x / qb;
-  const int q = 64 * (int)(blockIdx.x % qb) + (threadIdx.x & 63);
-  const int g = threadIdx.x >> 6;
-  float a0 = 0.0f, a1 = 0.0f, a2 = 0.0f, a3 = 0.0f;
-  if (q < r) {
-    const float *src = part + m * RP + q;
-    const int64_t step = (int64_t)M * RP;
-    int i = g;
-    for (; i + 12 < S; i += 16) {
-      a0 += src[(int64_t)i * step];
-      a1 += src[(int64_t)(i + 4) * step];
-      a2 += src[(int64_t)(i + 8) * step];
-      a3 += src[(int64_t)(i + 12) * step];
-    }
-    for (; i < S; i += 4) a0 += src[(int64_t)i * step];
-  }
-  red[g][threadIdx.x & 63] = (a0 + a1) + (a2 + a3);
+    for (int v = 0; v < 4; ++v) red[(wave * 16 + 4 * g + v) * RP + 16 * t + i16] = acc[t][v];
   __syncthreads();
-  if (g != 0 || m >= M) return;
-  const float acc = (red[0][threadIdx.x] + red[1][threadIdx.x]) + (red[2][threadIdx.x] + red[3][threadIdx.x]);
-  if (out1 && q < ld1) out1[m * ld1 + q] = q < r ? to_bf16(acc) : (uint16_t)0;
-  if (out2 && q < ld2) out2[m * ld2 + q] = q < r ? to_bf16(s * acc) : (uint16_t)0;
+  const int W = p.ld1 > p.ld2 ? p.ld1 : p.ld2;
+  for (int o = tid; o < p.rows * W; o += 1024) {
+    const int row = o / W, q = o % W;
+    const int64_t m = m0 + row;
+    if (m >= p.M) continue;
+    float sum = 0.0f;
+    if (q < r)
+#pragma unroll
+      for (int w = 0; w < kRankWaves; ++w) sum += red[(w * 16 + row) * RP + q];
+    if (p.out1 && q < p.ld1) p.out1[m * p.ld1 + q] = q < r ? to_bf16(sum) : (uint16_t)0;
+    if (p.out2 && q < p.ld2) p.out2[m * p.ld2 + q] = q < r ? to_bf16(p.s * sum) : (uint16_t)0;
+  }
+  if (p.L1p) {  // backward extras, spread over the whole grid (after the main loads: no stall in front of them)
+    const int64_t gt = (int64_t)blockIdx.x * 1024 + tid, gn = (int64_t)gridDim.x * 1024;
+    for (int64_t idx = gt; idx < p.h * p.ldp; idx += gn) {
+      const int64_t a = idx / p.ldp, b = idx % p.ldp;
+      p.L1p[idx] = b < r ? p.L1[a * r + b] : (uint16_t)0;
+    }
+    if (gt < p.ncnt) p.cnt[gt] = 0u;
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -209,11 +283,6 @@ struct GvStage {
   float s2;    // its second-level scale
 };
 
-QL_DEV __amdgpu_buffer_rsrc_t gv_rsrc(const void *base, int64_t bytes) {
-  const int64_t cap = 0x7FFFFFF0;
-  const int32_t n = (int32_t)(bytes < 0 ? 0 : (bytes > cap ? cap : bytes));
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, n, 0x00020000);
-}
 constexpr int kGvOOB = (int)0x80000000u;  // offset past every buffer: the load returns zero
 
 // MT: token-count class (1, 4 or 16); output token 4g + v exists only for
@@ -369,96 +438,161 @@ __global__ __launch_bounds__(kGvThreads) void nf4_gemv_kernel(GemvParams p) {
 }
 
 // ---------------------------------------------------------------------------
-// Adapter gradients, both in one launch: tiles [0, a.tiles) compute
-// dL1 = s·X^T·U ([h][r]) and the rest dL2 = s·T^T·dY (stored [r][o]).  Each
-// is part[split][i][q] = sum over the split's tokens m of P[m][i] * Q[m][q];
-// both operands are token-major in HBM, so a workgroup transposes a 64-token
-// slab of each into LDS ([i][m] and [q][m]) and the MFMA fragments become
-// 16-byte LDS reads.  Workgroup = 64 values of i, all q.  The last token split
-// of a tile sums the splits, scales by s and stores the tile.
+// Adapter gradients, both in one launch ([MC] "One training step": only the
+// adapters receive gradients; [TT] §4): tiles [0, pa.tiles) compute
+// dL1 = s·X^T·U ([h][r]) and the rest dL2 = s·T^T·dY (stored [r][o]).  Each is
+// part[split][i][q] = sum over the split's tokens m of P[m][i] * Q[m][q].
+// Both operands are token-major in HBM.  A workgroup owns 128 values of i (all
+// q) and a token range, walked in 64-token slabs: a slab of P (256-byte row
+// runs) and the matching rows of Q (one contiguous run) are copied into LDS as
+// they are, with 16-byte stores; the MFMA fragments need 8 consecutive tokens
+// per lane, so P's come from transposing LDS reads (ds_read_b64_tr_b16) and
+// Q's from 2-byte gathers.  The next two slabs' loads are in flight while one
+// is multiplied (two register stages, double-buffered LDS, one barrier per
+// slab); loads past the token range read as zero.  The last token split of a
+// tile sums the splits in split order, scales by s and stores the tile.
 // ---------------------------------------------------------------------------
 struct GradProblem {
   const uint16_t *P;  // [M][ldp], the i index runs along a row
   int64_t ldp, I;
-  const uint16_t *Q;  // [M][ldq], q < r valid
+  const uint16_t *Q;  // [M][ldq], q < r valid (rows contiguous: ldq elements each)
   int64_t ldq;
   float *out;         // [I][r] (trans = false) or [r][I] (trans = true)
   bool trans;
-  int64_t tiles;      // I / 64
+  int64_t tiles;      // ceil(I / kGradTile)
   int64_t prow;       // first row of this problem in the partial buffer
 };
+
+constexpr int kGradTile = 128;  // values of i per workgroup
 
 template <int NT>
 __global__ __launch_bounds__(256) void lora_grad_kernel(GradProblem pa, GradProblem pb, int rq, float s, int64_t M,
                                                         int64_t mchunk, int64_t prows, float *__restrict__ part,
                                                         unsigned *__restrict__ cnt) {
-  constexpr int RP = NT * 16, LDT = 64 + 8;
-  __shared__ __attribute__((aligned(16))) uint16_t Pt[64 * LDT];
-  __shared__ __attribute__((aligned(16))) uint16_t Qt[RP * LDT];
+  constexpr int RP = NT * 16;
+  constexpr int LP = kGradTile + 8;                   // P slab row stride (elements)
+  constexpr int PCH = 64 * kGradTile / 8 / 256;       // 16-byte P chunks per thread per slab
+  constexpr int QCH = (64 * RP / 8 + 255) / 256;      // 16-byte Q chunks per thread per slab (at most)
+  __shared__ __attribute__((aligned(16))) uint16_t Ps[2][64 * LP];
+  __shared__ __attribute__((aligned(16))) uint16_t Qs[2][64 * RP];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int g = lane >> 4, c16 = lane & 15;
   const bool second = blockIdx.x >= pa.tiles;
   const GradProblem &pr = second ? pb : pa;
   const int64_t tile = second ? blockIdx.x - pa.tiles : blockIdx.x;
-  const uint16_t *P = pr.P, *Q = pr.Q;
-  const int64_t ldp = pr.ldp, ldq = pr.ldq;
-  const int64_t i0 = tile * 64;
+  const int64_t i0 = tile * kGradTile;
   const int64_t ms = (int64_t)blockIdx.y * mchunk;
   const int64_t me = ms + mchunk < M ? ms + mchunk : M;
-  const bool qvec = (ldq % 8) == 0;
-  f32x4 acc[NT];
+  const int nsteps = (int)((me - ms + 63) / 64);
+  const int64_t ldp = pr.ldp, ldq = pr.ldq;
+  // rows [ms, me) of P from column i0, and of Q; everything past them reads as zero
+  const auto rP = gv_rsrc(pr.P + ms * ldp + i0, (me - ms) * ldp * 2 - i0 * 2);
+  const auto rQ = gv_rsrc(pr.Q + ms * ldq, (me - ms) * ldq * 2);
+  int voffP[PCH], soffP[PCH], voffQ[QCH];
 #pragma unroll
-  for (int t = 0; t < NT; ++t) acc[t] = f32x4{0, 0, 0, 0};
-  for (int64_t mb = ms; mb < me; mb += 64) {
+  for (int u = 0; u < PCH; ++u) {
+    const int ch = tid + 256 * u, row = ch >> 4, col8 = ch & 15;  // 16 chunks per 256-byte row
+    voffP[u] = (int)((row * ldp + col8 * 8) * 2);
+    soffP[u] = row * LP + col8 * 8;
+  }
 #pragma unroll
-    for (int c = 0; c < 2; ++c) {
-      const int chunk = tid + 256 * c, mm = chunk >> 3, i8 = chunk & 7;
-      const int64_t m = mb + mm;
-      const u32x4 v = m < me ? *reinterpret_cast<const u32x4 *>(P + m * ldp + i0 + i8 * 8) : u32x4{0, 0, 0, 0};
+  for (int u = 0; u < QCH; ++u) {
+    const int ch = tid + 256 * u;                      // the slab of Q is 128 * ldq contiguous bytes
+    voffQ[u] = ch < 8 * ldq ? ch * 16 : (int)0x80000000u;  // past every buffer: reads zero
+  }
+
+  f32x4 acc[2][NT];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) Pt[(i8 * 8 + e) * LDT + mm] = (uint16_t)(v[e >> 1] >> (16 * (e & 1)));
-    }
-    for (int chunk = tid; chunk < 64 * (RP / 8); chunk += 256) {
-      const int mm = chunk / (RP / 8), q8 = chunk % (RP / 8);
-      const int64_t m = mb + mm;
-      uint16_t vals[8];
-      if (m < me && qvec && q8 * 8 + 8 <= rq) {
-        const u32x4 v = *reinterpret_cast<const u32x4 *>(Q + m * ldq + q8 * 8);
+  for (int a = 0; a < 2; ++a)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) vals[e] = (uint16_t)(v[e >> 1] >> (16 * (e & 1)));
-      } else {
+    for (int t = 0; t < NT; ++t) acc[a][t] = f32x4{0, 0, 0, 0};
+
+  struct Stage {
+    u32x4 p[PCH], q[QCH];
+  };
+  auto load = [&](int st, Stage &S) {
+    const int sp = __builtin_amdgcn_readfirstlane((int)(st * 64 * ldp * 2));
+    const int sq = __builtin_amdgcn_readfirstlane((int)(st * 128 * ldq));
 #pragma unroll
-        for (int e = 0; e < 8; ++e) vals[e] = (m < me && q8 * 8 + e < rq) ? Q[m * ldq + q8 * 8 + e] : (uint16_t)0;
+    for (int u = 0; u < PCH; ++u) S.p[u] = __builtin_amdgcn_raw_buffer_load_b128(rP, voffP[u], sp, 0);
+#pragma unroll
+    for (int u = 0; u < QCH; ++u) S.q[u] = __builtin_amdgcn_raw_buffer_load_b128(rQ, voffQ[u], sq, 0);
+  };
+  auto put = [&](int buf, const Stage &S) {
+#pragma unroll
+    for (int u = 0; u < PCH; ++u) *reinterpret_cast<u32x4 *>(&Ps[buf][soffP[u]]) = S.p[u];
+#pragma unroll
+    for (int u = 0; u < QCH; ++u)
+      if (tid + 256 * u < 8 * ldq) *reinterpret_cast<u32x4 *>(&Qs[buf][(tid + 256 * u) * 8]) = S.q[u];
+  };
+  // lane 4j + qq of a 16-lane group names row k0 + j, columns 4qq..4qq+3 of the transposing read
+  const int trow = c16 >> 2, tcol = (c16 & 3) * 4;
+  auto compute = [&](int buf) {
+#pragma unroll
+    for (int mk = 0; mk < 64; mk += 32) {
+      u32x4 af[2];
+#pragma unroll
+      for (int a = 0; a < 2; ++a) {
+        const uint16_t *lo = &Ps[buf][(mk + 8 * g + trow) * LP + wave * 32 + 16 * a + tcol];
+        af[a] = tr_pair(lo, lo + 4 * LP);
       }
-#pragma unroll
-      for (int e = 0; e < 8; ++e) Qt[(q8 * 8 + e) * LDT + mm] = vals[e];
-    }
-    __syncthreads();
-#pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-      const u32x4 af = *reinterpret_cast<const u32x4 *>(Pt + (wave * 16 + (lane & 15)) * LDT + kk * 32 + (lane >> 4) * 8);
 #pragma unroll
       for (int t = 0; t < NT; ++t) {
-        const u32x4 bq = *reinterpret_cast<const u32x4 *>(Qt + (t * 16 + (lane & 15)) * LDT + kk * 32 + (lane >> 4) * 8);
-        acc[t] = mfma16(af, bq, acc[t]);
+        const int q = 16 * t + c16;
+        uint32_t w[4];
+#pragma unroll
+        for (int x = 0; x < 4; ++x) {
+          const uint32_t lo = q < rq ? Qs[buf][(mk + 8 * g + 2 * x) * ldq + q] : 0u;
+          const uint32_t hi = q < rq ? Qs[buf][(mk + 8 * g + 2 * x + 1) * ldq + q] : 0u;
+          w[x] = lo | (hi << 16);
+        }
+        const u32x4 bq{w[0], w[1], w[2], w[3]};
+#pragma unroll
+        for (int a = 0; a < 2; ++a) acc[a][t] = mfma16(af[a], bq, acc[a][t]);
       }
     }
+  };
+
+  Stage S0, S1;
+  load(0, S0);
+  __builtin_amdgcn_sched_barrier(0);
+  load(1, S1);
+  __builtin_amdgcn_sched_barrier(0);
+  put(0, S0);
+  __syncthreads();
+  for (int st = 0; st < nsteps; st += 2) {
+    load(st + 2, S0);
+    __builtin_amdgcn_sched_barrier(0);
+    compute(0);
+    put(1, S1);
+    __syncthreads();
+    if (st + 1 >= nsteps) break;
+    load(st + 3, S1);
+    __builtin_amdgcn_sched_barrier(0);
+    compute(1);
+    put(0, S0);
     __syncthreads();
   }
+
+  // D layout: lane (q = 16t + c16, g) holds rows i = 4g + v of each 16-row tile
   float *out = part + ((int64_t)blockIdx.y * prows + pr.prow) * RP;
 #pragma unroll
-  for (int t = 0; t < NT; ++t)
+  for (int a = 0; a < 2; ++a)
 #pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const int64_t i = i0 + wave * 16 + 4 * (lane >> 4) + v;
-      store_partial(out + i * RP + t * 16 + (lane & 15), acc[t][v]);
-    }
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int64_t i = i0 + wave * 32 + 16 * a + 4 * g + v;
+        if (i < pr.I) store_partial(out + i * RP + t * 16 + c16, acc[a][t][v]);
+      }
   if (!last_of_splits(cnt + blockIdx.x, gridDim.y)) return;
   const int S = (int)gridDim.y;
-  for (int idx = tid; idx < 64 * rq; idx += 256) {
+  for (int idx = tid; idx < kGradTile * rq; idx += 256) {
     // consecutive threads write consecutive addresses of the stored layout
-    const int il = pr.trans ? idx % 64 : idx / rq;
-    const int q = pr.trans ? idx / 64 : idx % rq;
+    const int il = pr.trans ? idx % kGradTile : idx / rq;
+    const int q = pr.trans ? idx / kGradTile : idx % rq;
     const int64_t i = i0 + il;
+    if (i >= pr.I) continue;
     float sum = 0.0f;
 #pragma unroll 8
     for (int k = 0; k < S; ++k) sum += load_partial(part + ((int64_t)k * prows + pr.prow + i) * RP + q);
@@ -478,17 +612,9 @@ struct Split {
   int64_t chunk;
 };
 
-Split skinny_split(int64_t M, int64_t K) {
-  const int64_t mt = cdiv(M, 64);
-  int64_t S = cdiv(kTargetGroups, mt);
-  S = S < 1 ? 1 : S;
-  S = S > K / 64 ? K / 64 : S;
-  int64_t chunk = rup(cdiv(K, S), 64);
-  return {(int)cdiv(K, chunk), chunk};
-}
-
 Split grad_split(int64_t M, int64_t I) {
-  const int64_t it = I / 64;
+  // about 512 workgroups: more token splits cost more in partial sums than they save
+  const int64_t it = cdiv(I, kGradTile);
   int64_t S = cdiv(kTargetGroups, it);
   const int64_t msteps = cdiv(M, 64);
   S = S < 1 ? 1 : S;
@@ -499,8 +625,7 @@ Split grad_split(int64_t M, int64_t I) {
 
 struct FwdLayout {
   int RP16, RP64;
-  Split sk;
-  size_t off_l1t, off_part, off_st, total;
+  size_t off_st, total;
 };
 
 FwdLayout fwd_layout(int64_t M, int64_t h, int64_t o, int r) {
@@ -508,11 +633,8 @@ FwdLayout fwd_layout(int64_t M, int64_t h, int64_t o, int r) {
   if (r == 0) return L;
   L.RP16 = (int)rup(r, 16);
   L.RP64 = (int)rup(r, 64);
-  L.sk = skinny_split(M, h);
   size_t off = 0;
   auto take = [&](size_t bytes) { size_t at = off; off += rup((int64_t)bytes, 256); return at; };
-  L.off_l1t = take((size_t)L.RP16 * h * 2);
-  L.off_part = take((size_t)L.sk.S * M * L.RP16 * 4);
   L.off_st = take((size_t)M * L.RP64 * 2);
   L.total = off;
   return L;
@@ -520,9 +642,9 @@ FwdLayout fwd_layout(int64_t M, int64_t h, int64_t o, int r) {
 
 struct BwdLayout {
   int RP16, RP64;
-  Split sk, gs;
+  Split gs;
   int dxc;  // few-token path (M <= 16): row chunks of the dX partial sums
-  size_t off_part, off_u, off_su, off_l1p, off_g, off_cnt, off_dxp, total;
+  size_t off_u, off_su, off_l1p, off_g, off_cnt, off_dxp, total;
 };
 
 int gemv_dx_chunks(int64_t M, int64_t h, int64_t o);
@@ -539,9 +661,7 @@ BwdLayout bwd_layout(int64_t M, int64_t h, int64_t o, int r) {
   if (r == 0) return L;
   L.RP16 = (int)rup(r, 16);
   L.RP64 = (int)rup(r, 64);
-  L.sk = skinny_split(M, o);
   L.gs = grad_split(M, h + o);
-  L.off_part = take((size_t)L.sk.S * M * L.RP16 * 4);
   L.off_u = take((size_t)M * L.RP16 * 2);
   L.off_su = take((size_t)M * L.RP64 * 2);
   L.off_l1p = take((size_t)h * L.RP64 * 2);
@@ -554,23 +674,19 @@ BwdLayout bwd_layout(int64_t M, int64_t h, int64_t o, int r) {
 template <typename T>
 T *at(void *ws, size_t off) { return reinterpret_cast<T *>(reinterpret_cast<char *>(ws) + off); }
 
-void relayout(const uint16_t *src, int64_t lds, bool trans, int64_t A, int64_t B, int64_t av, int64_t bv,
-              uint16_t *dst, unsigned *zero, int nzero, hipStream_t st) {
-  const int64_t n = A * B > nzero ? A * B : nzero;
-  relayout_kernel<<<(unsigned)cdiv(n, 256), 256, 0, st>>>(src, lds, trans, A, B, av, bv, dst, zero, nzero);
-}
-
-void skinny(const uint16_t *A, int64_t lda, int64_t M, int64_t K, const uint16_t *Bt, int64_t ldb, int r, int RP16,
-            const Split &sp, float *part, float s, uint16_t *out1, int ld1, uint16_t *out2, int ld2,
-            hipStream_t st) {
-  dim3 grid((unsigned)cdiv(M, 64), (unsigned)sp.S);
+void rank_r(RankParams &rp, bool kn, int RP16, hipStream_t st) {
+  // the fewest rows per workgroup that still give 256 workgroups (one per compute unit)
+  rp.rows = rp.M >= 16 * 256 ? 16 : (rp.M >= 8 * 256 ? 8 : 4);
+  const unsigned grid = (unsigned)cdiv(rp.M, rp.rows);
   switch (RP16 / 16) {
-#define QL_SK(NT) case NT: skinny_kernel<NT><<<grid, 256, 0, st>>>(A, lda, M, K, Bt, ldb, r, sp.chunk, part); break;
-    QL_SK(1) QL_SK(2) QL_SK(3) QL_SK(4) QL_SK(5) QL_SK(6) QL_SK(7) QL_SK(8)
-#undef QL_SK
+#define QL_RK(NT)                                                                       \
+  case NT:                                                                              \
+    if (kn) rank_r_kernel<NT, true><<<grid, 1024, 0, st>>>(rp);                          \
+    else rank_r_kernel<NT, false><<<grid, 1024, 0, st>>>(rp);                            \
+    break;
+    QL_RK(1) QL_RK(2) QL_RK(3) QL_RK(4) QL_RK(5) QL_RK(6) QL_RK(7) QL_RK(8)
+#undef QL_RK
   }
-  const int W = ld2 > ld1 ? ld2 : ld1;
-  skinny_finish_kernel<<<(unsigned)(M * cdiv(W, 64)), 256, 0, st>>>(part, sp.S, M, RP16, r, s, out1, ld1, out2, ld2);
 }
 
 void lora_grad(const GradProblem &pa, const GradProblem &pb, int r, float s, int64_t M, int RP16, const Split &sp,
@@ -854,12 +970,13 @@ hipError_t launch_linear_fwd(const LinearArgs &a, const uint16_t *X, const uint1
   const FwdLayout L = fwd_layout(a.M, a.h, a.o, a.r);
   uint16_t *sT = nullptr;
   if (a.r > 0) {
-    // T = X·L1 (rank r): L1 [h][r] -> L1t [RP16][h]
-    uint16_t *L1t = at<uint16_t>(ws, L.off_l1t);
-    relayout(L1, a.r, true, L.RP16, a.h, a.r, a.h, L1t, nullptr, 0, st);
-    float *part = at<float>(ws, L.off_part);
+    // T = X·L1 (rank r) and its s-scaled, zero-padded copy sT for the GEMM's rank-r step
     sT = at<uint16_t>(ws, L.off_st);
-    skinny(X, a.h, a.M, a.h, L1t, a.h, a.r, L.RP16, L.sk, part, a.s, T, a.r, sT, L.RP64, st);
+    RankParams rp{};
+    rp.A = X; rp.lda = a.h; rp.M = a.M; rp.K = a.h;
+    rp.B = L1; rp.ldb = a.r; rp.r = a.r; rp.s = a.s;
+    rp.out1 = T; rp.ld1 = a.r; rp.out2 = sT; rp.ld2 = L.RP64;
+    rank_r(rp, true, L.RP16, st);
   }
   if (a.M <= 16) {
     GemvParams gp{};
@@ -909,16 +1026,19 @@ hipError_t launch_linear_bwd(const LinearArgs &a, const uint16_t *X, const uint1
   if (a.r > 0) {
     unsigned *cnt = at<unsigned>(ws, L.off_cnt);
     L1p = at<uint16_t>(ws, L.off_l1p);
-    // L1 [h][r] -> [h][RP64] for the dX GEMM's LoRA step; also clears the gradient split counters
-    relayout(L1, a.r, false, a.h, L.RP64, a.h, a.r, L1p, cnt, (int)((a.h + a.o) / 64), st);
-    // U = dY·L2^T: Bt = L2 [r][o] is already k-contiguous
-    float *part = at<float>(ws, L.off_part);
+    // U = dY·L2^T (L2 [r][o] is k-contiguous) and sU; the same launch writes L1 [h][r] ->
+    // L1p [h][RP64] for the dX GEMM's rank-r step and clears the gradient split counters
     uint16_t *U = at<uint16_t>(ws, L.off_u);
     sU = at<uint16_t>(ws, L.off_su);
-    skinny(dY, a.o, a.M, a.o, L2, a.o, a.r, L.RP16, L.sk, part, a.s, U, L.RP16, sU, L.RP64, st);
+    RankParams rp{};
+    rp.A = dY; rp.lda = a.o; rp.M = a.M; rp.K = a.o;
+    rp.B = L2; rp.ldb = a.o; rp.r = a.r; rp.s = a.s;
+    rp.out1 = U; rp.ld1 = L.RP16; rp.out2 = sU; rp.ld2 = L.RP64;
+    rp.L1 = L1; rp.h = a.h; rp.ldp = L.RP64; rp.L1p = L1p; rp.cnt = cnt; rp.ncnt = (int)((a.h + a.o) / 64);
+    rank_r(rp, false, L.RP16, st);
     // dL1 = s·X^T·U (P = X [M][h], Q = U [M][RP16]) and dL2 = s·T^T·dY (P = dY [M][o], Q = T [M][r]), stored [r][o]
-    g1 = GradProblem{X, a.h, a.h, U, L.RP16, dL1, false, a.h / 64, 0};
-    g2 = GradProblem{dY, a.o, a.o, T, a.r, dL2, true, a.o / 64, a.h};
+    g1 = GradProblem{X, a.h, a.h, U, L.RP16, dL1, false, cdiv(a.h, kGradTile), 0};
+    g2 = GradProblem{dY, a.o, a.o, T, a.r, dL2, true, cdiv(a.o, kGradTile), a.h};
     gpart = at<float>(ws, L.off_g);
     gcnt = cnt;
   }

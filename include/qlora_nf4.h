@@ -113,7 +113,8 @@ qlora_status_t qlora_quantize(const void *w, qlora_dtype_t w_dtype, int64_t n, u
  *  scale2   out, ceil(nblocks/256) float32 steps.
  *  mean     out, 1 float32 (device).
  *  workspace/ws_bytes  device scratch of at least
- *           qlora_workspace_size(QLORA_OP_DOUBLE_QUANT, nblocks, ...) bytes.
+ *           qlora_workspace_size(QLORA_OP_DOUBLE_QUANT, nblocks, ...) bytes;
+ *           its contents on entry do not matter.
  * mean = the exact mean of all scales rounded once to float32 (independent of
  * summation order).  Each chunk j of 256 consecutive centred scales
  * c = fp32(a - mean) gets step s2_j = fp32(max|c| / 127) and codes

@@ -103,7 +103,7 @@ def test_quantize_random_scales_large():
     check_quantize(w, "random scales")
 
 
-@pytest.mark.parametrize("nb", [1, 2, 255, 256, 257, 1000, 100003])
+@pytest.mark.parametrize("nb", [1, 2, 255, 256, 257, 1000, 100003, 5000011])
 def test_double_quant(nb):
     print(f"double quant nb={nb}", flush=True)
     rng = np.random.default_rng(nb)

@@ -21,12 +21,11 @@
 //                        reduction over tokens, LDS-transposed operands,
 //                        split over tokens; the last split of a tile sums,
 //                        scales by s and stores dL1 [h][r] or dL2 [r][o];
-//                        runs on a side stream concurrently with the dX GEMM
+//                        runs before the dX GEMM on the caller's stream
 
 #include "linear.h"
 #include "gemm.h"
 
-#include <mutex>
 
 namespace ql {
 
@@ -703,38 +702,6 @@ void lora_grad(const GradProblem &pa, const GradProblem &pb, int r, float s, int
   }
 }
 
-// Side stream for work that can overlap the fused GEMM on the caller's stream
-// (the adapter gradients in the backward pass).  One per device, created on
-// first use, default priority.  The caller's stream forks to it with an event
-// and joins back with another, so every call stays ordered on the caller's
-// stream.  The lock covers the fork / launch / join enqueue sequence, which
-// also makes reusing the two events across calls safe (a wait captures the
-// event's state when it is enqueued).
-struct SideStream {
-  hipStream_t s = nullptr;
-  hipEvent_t fork = nullptr, join = nullptr;
-  bool ready = false;
-};
-constexpr int kMaxDevices = 64;
-std::mutex g_side_mu;
-SideStream g_side[kMaxDevices];
-
-SideStream *side_stream_locked() {
-  int dev = -1;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
-  SideStream &ss = g_side[dev];
-  if (!ss.ready) {
-    if (hipStreamCreateWithFlags(&ss.s, hipStreamNonBlocking) != hipSuccess) return nullptr;
-    if (hipEventCreateWithFlags(&ss.fork, hipEventDisableTiming) != hipSuccess ||
-        hipEventCreateWithFlags(&ss.join, hipEventDisableTiming) != hipSuccess) {
-      (void)hipGetLastError();
-      return nullptr;
-    }
-    ss.ready = true;
-  }
-  return &ss;
-}
-
 thread_local hipEvent_t t_ev[3][2] = {};
 
 struct TimedLaunch {
@@ -1062,27 +1029,9 @@ hipError_t launch_linear_bwd(const LinearArgs &a, const uint16_t *X, const uint1
       gemv_dx_finish_kernel<<<(unsigned)(a.M * cg), 256, 0, st>>>(vp.part, L.dxc, (int)a.M, a.h, sU, L.RP64, L1,
                                                                  a.r, dX, a.h);
     };
-    if (a.r == 0) {
-      launch_dx();
-      return hipGetLastError();
-    }
-    std::lock_guard<std::mutex> lock(g_side_mu);
-    SideStream *ss = side_stream_locked();
-    hipError_t e = hipSuccess;
-    if (ss) {
-      e = hipEventRecord(ss->fork, st);
-      if (e == hipSuccess) e = hipStreamWaitEvent(ss->s, ss->fork, 0);
-    }
-    if (e != hipSuccess) return e;
-    lora_grad(g1, g2, a.r, a.s, a.M, L.RP16, L.gs, gpart, gcnt, ss ? ss->s : st);
+    if (a.r > 0) lora_grad(g1, g2, a.r, a.s, a.M, L.RP16, L.gs, gpart, gcnt, st);
     launch_dx();
-    e = hipGetLastError();
-    if (ss) {
-      const hipError_t e1 = hipEventRecord(ss->join, ss->s);
-      const hipError_t e2 = e1 == hipSuccess ? hipStreamWaitEvent(st, ss->join, 0) : e1;
-      if (e == hipSuccess) e = e2;
-    }
-    return e;
+    return hipGetLastError();
   }
   GemmParams gp{};
   gp.A = dY; gp.lda = a.o;
@@ -1094,33 +1043,16 @@ hipError_t launch_linear_bwd(const LinearArgs &a, const uint16_t *X, const uint1
   gp.M = a.M; gp.N = a.h;
   gp.C = dX; gp.ldc = a.h;
   fill_levels(gp.level, tab);
-  if (a.r == 0) {
-    TimedLaunch tl(1, st);
-    launch_nf4_gemm(gp, true, st);
-    return hipGetLastError();
-  }
-  // The adapter gradients need only U, X, T and dY: they run on the side stream
-  // while the dX GEMM runs on the caller's stream.
-  std::lock_guard<std::mutex> lock(g_side_mu);
-  SideStream *ss = side_stream_locked();
-  hipError_t e = hipSuccess;
-  if (ss) {
-    e = hipEventRecord(ss->fork, st);
-    if (e == hipSuccess) e = hipStreamWaitEvent(ss->s, ss->fork, 0);
-  }
-  if (e != hipSuccess) return e;
-  lora_grad(g1, g2, a.r, a.s, a.M, L.RP16, L.gs, gpart, gcnt, ss ? ss->s : st);
+  // Everything runs in order on the caller's stream: the adapter gradients on a
+  // side stream beside the dX GEMM cost the GEMM more than they saved (they share
+  // the compute units and the cache hierarchy, and the stream fork and join add
+  // their own gaps).
+  if (a.r > 0) lora_grad(g1, g2, a.r, a.s, a.M, L.RP16, L.gs, gpart, gcnt, st);
   {
     TimedLaunch tl(1, st);
     launch_nf4_gemm(gp, true, st);
   }
-  e = hipGetLastError();
-  if (ss) {
-    const hipError_t e1 = hipEventRecord(ss->join, ss->s);
-    const hipError_t e2 = e1 == hipSuccess ? hipStreamWaitEvent(st, ss->join, 0) : e1;
-    if (e == hipSuccess) e = e2;
-  }
-  return e;
+  return hipGetLastError();
 }
 
 }  // namespace ql

@@ -60,6 +60,8 @@ SMALL = [  # (M, h, o, r, s)
     (300, 1024, 512, 64, 0.25),
     (513, 320, 640, 128, 1.5),
     (257, 576, 1088, 16, 2.0),
+    (2050, 256, 320, 3, 1.0),     # rank-r products: 8 rows per workgroup, ragged last workgroup
+    (4100, 192, 256, 100, 0.5),   # 16 rows per workgroup, ragged, r not a multiple of 8
 ]
 
 

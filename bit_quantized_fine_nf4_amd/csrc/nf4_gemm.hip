@@ -196,6 +196,18 @@ __global__ __launch_bounds__(512) void nf4_gemm_kernel(GemmParams p) {
   // A chunks and a quarter of the code bytes, decoded (LUT pair -> * a_hat ->
   // bf16) and stored.  `ah` is the stage's block scale (computed by part 0).
   constexpr int BPP = UB / 4;  // code bytes decoded per part (2 or 4)
+  // With 8 code bytes per unit, all eight table reads of a step are issued at its
+  // start (right after the next stage's loads), so their LDS latency is paid once
+  // rather than once per part; with 16 (256-wide tiles) the extra 16 registers
+  // would spill, and each part reads its own.
+  constexpr bool kEarly = UB == 8;
+  f32x2 LV[kEarly ? UB : 1];
+  auto read_levels = [&](const Stage &S) {
+    if constexpr (kEarly) {
+#pragma unroll
+      for (int byte = 0; byte < UB; ++byte) LV[byte] = lut[(S.c[byte >> 2] >> (8 * (byte & 3))) & 0xFF];
+    }
+  };
   auto put_part = [&](int buf, int part, const Stage &S, float &ah) {
     // int8 value from the zero-extended byte by float arithmetic: a plain
     // sign extension would let instruction selection fuse it with the load
@@ -214,7 +226,9 @@ __global__ __launch_bounds__(512) void nf4_gemm_kernel(GemmParams p) {
 #pragma unroll
     for (int b = 0; b < BPP; ++b) {
       const int byte = part * BPP + b;
-      const f32x2 l = lut[(S.c[byte >> 2] >> (8 * (byte & 3))) & 0xFF];
+      f32x2 l;
+      if constexpr (kEarly) l = LV[byte];
+      else l = lut[(S.c[byte >> 2] >> (8 * (byte & 3))) & 0xFF];
       o[b] = pack_bf16x2(l[0] * ah, l[1] * ah);
     }
     uint16_t *dst = bdst0 + buf * STAGE + part * 2 * BPP;
@@ -275,6 +289,7 @@ __global__ __launch_bounds__(512) void nf4_gemm_kernel(GemmParams p) {
   __builtin_amdgcn_sched_barrier(0);
   load_stage(1, S1);
   __builtin_amdgcn_sched_barrier(0);
+  read_levels(S0);
 #pragma unroll
   for (int part = 0; part < 4; ++part) put_part(0, part, S0, ah);
   __syncthreads();
@@ -285,6 +300,10 @@ __global__ __launch_bounds__(512) void nf4_gemm_kernel(GemmParams p) {
     const int buf = kt & 1;
     load_stage(kt + 2, Sfree);
     __builtin_amdgcn_sched_barrier(0);
+    if constexpr (kEarly) {
+      read_levels(Snext);
+      __builtin_amdgcn_sched_barrier(0);
+    }
     if constexpr (TM * TN > 4) {  // 256x256 tiles: no registers to spare for a second fragment set
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) {

@@ -9,12 +9,16 @@
 // Workgroup: 512 threads = 4 x 2 waves (two waves per SIMD, so one wave's
 // matrix-core work overlaps the other's LDS and decode work), tile BM x BN,
 // K step 64, wave tile (BM/4) x (BN/2).  Both operands are staged through
-// double-buffered LDS; the next K step's global loads are in flight while the
+// double-buffered LDS; later K steps' global loads are in flight while the
 // matrix cores work on the current buffers.  Within a K step, lane group
 // g = lane/32 owns k in [32g, 32g+32) and MFMA kk takes k = 32g + 8kk + 0..7
 // (the contraction may visit k in any order as long as A and B agree).
-//  A operand (X or dY, k-contiguous): tile [m][k] (row stride 72), loaded with
-//   16-byte loads, 8 lanes per 128-byte row.
+//  A operand (X or dY, k-contiguous): tile [m][k].  It goes from memory straight
+//   into LDS (buffer_load ... lds, 16 bytes per lane, 1 KB = 8 rows per
+//   instruction) one step ahead, in unpadded 128-byte rows whose 16-byte chunks
+//   are XOR-swizzled by row so fragment reads stay free of bank conflicts; for the
+//   256-wide dX tiles it is staged through registers two steps ahead instead
+//   (row stride 72, 16-byte stores), which measured faster there.
 //  B operand is decoded into LDS:
 //   Every thread decodes one unit of BN/8 consecutive weights of one codes row
 //   per K step (16 or 32: inside one 64-weight block, so one scale per unit).
@@ -38,6 +42,8 @@
 //  by extra K steps over (A2, B2) on the same accumulators.
 
 #include "gemm.h"
+
+#include <type_traits>
 
 namespace ql {
 namespace {
@@ -70,6 +76,11 @@ QL_DEV u32x4 tr_pair(const uint16_t *lo, const uint16_t *hi) {
   return u32x4{ua[0], ua[1], ub[0], ub[1]};
 }
 QL_DEV uint16_t to_bf16(float v) { return (uint16_t)(pack_bf16x2(v, 0.0f) & 0xFFFFu); }
+// 16 bytes per lane from a buffer straight into LDS (buffer_load ... lds): lane L's
+// bytes land at dst + 16 L; dst must be the same in every lane of the wave.
+QL_DEV void load16_to_lds(__amdgpu_buffer_rsrc_t r, uint16_t *dst, int voff, int soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void *)dst, 16, voff, soff, 0, 0);
+}
 
 constexpr int cmax(int a, int b) { return a > b ? a : b; }
 
@@ -79,7 +90,10 @@ template <int BM, int BN, bool TRANS>
 __global__ __launch_bounds__(512) void nf4_gemm_kernel(GemmParams p) {
   constexpr int NT = 512, BK = 64;
   constexpr int WTM = BM / 4, WTN = BN / 2, TM = WTM / 32, TN = WTN / 32;
-  constexpr int LDA = BK + 8;     // A [m][k]
+  // A reaches LDS straight from memory (kDma) except for the 256-wide dX tiles, where
+  // staging it through registers (two steps ahead rather than one) measured faster.
+  constexpr bool kDma = !(TRANS && BN == 256);
+  constexpr int LDA = kDma ? BK : BK + 8;  // A [m][k]: swizzled chunks (kDma) or a padded row
   constexpr int LDNK = BK + 8;   // B [n][k]
   // B [k][n]: a row stride of 12 banks (mod 64) keeps both the decode stores
   // (2 rows x 8 units per 16 lanes) and the transposing fragment reads
@@ -102,6 +116,12 @@ __global__ __launch_bounds__(512) void nf4_gemm_kernel(GemmParams p) {
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
+  const int wv = __builtin_amdgcn_readfirstlane(wave);
+  // kDma: row r keeps its 8 chunks of 16 bytes in the order c ^ aswz(r), so the 16 lanes of a
+  // fragment read (16 rows, one chunk) hit 16 different 16-byte bank groups without padding.
+  auto a_off = [](int r, int chunk) {
+    return kDma ? r * LDA + ((chunk ^ ((r >> 1) & 7)) << 3) : r * LDA + chunk * 8;
+  };
   if (tid < 256) reinterpret_cast<f32x2 *>(lds)[tid] = f32x2{p.level[tid >> 4], p.level[tid & 15]};
 
   int bid = blockIdx.x;
@@ -115,14 +135,27 @@ __global__ __launch_bounds__(512) void nf4_gemm_kernel(GemmParams p) {
   const int64_t bpr = p.ldw >> 6;  // 64-blocks per codes row
   const int g = lane >> 5, l32 = lane & 31;
 
-  // ---- A tile: 16-byte chunks, 8 lanes per 128-byte row ----
+  // ---- A tile ----
+  // kDma: each wave loads A_CH blocks of 8 rows into LDS, one 1 KB block per instruction, so
+  // lane L fetches the global chunk that belongs at row 8 rb + L / 8, physical chunk L % 8.
+  // Otherwise: 16-byte chunks through registers, 8 lanes per 128-byte row.
   const auto rA = make_rsrc(p.A + m0 * p.lda, mrows * p.lda * 2);
   int voffA[A_CH];
 #pragma unroll
   for (int c = 0; c < A_CH; ++c) {
-    const int chunk = tid + NT * c;
-    voffA[c] = (int)(((chunk >> 3) * p.lda + (chunk & 7) * 8) * 2);
+    if (kDma) {
+      const int r = 8 * (wv * A_CH + c) + (lane >> 3), lc = (lane & 7) ^ ((r >> 1) & 7);
+      voffA[c] = (int)((r * p.lda + lc * 8) * 2);
+    } else {
+      const int chunk = tid + NT * c;
+      voffA[c] = (int)(((chunk >> 3) * p.lda + (chunk & 7) * 8) * 2);
+    }
   }
+  auto load_a_lds = [&](int kt_, int buf) {
+    const int kt = __builtin_amdgcn_readfirstlane(kt_);
+#pragma unroll
+    for (int c = 0; c < A_CH; ++c) load16_to_lds(rA, sm + buf * STAGE + (wv * A_CH + c) * 8 * LDA, voffA[c], kt * BK * 2);
+  };
 
   // ---- B decode unit of this thread: UW consecutive weights of one codes row ----
   int voffC = 0, voffQ = 0;
@@ -157,7 +190,7 @@ __global__ __launch_bounds__(512) void nf4_gemm_kernel(GemmParams p) {
 
   // One register set holds everything a K step needs from global memory.
   struct Stage {
-    u32x4 a[A_CH];  // A tile chunks
+    u32x4 a[kDma ? 1 : A_CH];  // A tile chunks (register staging only)
     u32x4 c;        // this thread's code bytes (UB of them)
     uint32_t q;     // its int8 block scale, zero-extended (see put_part)
     float s2;       // its second-level scale
@@ -166,8 +199,10 @@ __global__ __launch_bounds__(512) void nf4_gemm_kernel(GemmParams p) {
     // The step index is wave-uniform; saying so keeps the scalar offsets in SGPRs
     // (otherwise every buffer load becomes a per-lane waterfall loop).
     const int kt = __builtin_amdgcn_readfirstlane(kt_);
+    if constexpr (!kDma) {
 #pragma unroll
-    for (int c = 0; c < A_CH; ++c) S.a[c] = bload128(rA, voffA[c], kt * BK * 2);
+      for (int c = 0; c < A_CH; ++c) S.a[c] = bload128(rA, voffA[c], kt * BK * 2);
+    }
     if (!TRANS) {
       if (UB == 16) {
         S.c = bload128(rCf, voffC, kt * 32);
@@ -216,12 +251,14 @@ __global__ __launch_bounds__(512) void nf4_gemm_kernel(GemmParams p) {
       const float qf = (float)S.q - (float)(S.q & 0x80u) * 2.0f;
       ah = qf * S.s2 + mu;
     }
+    if constexpr (!kDma) {
 #pragma unroll
-    for (int c = 0; c < A_CH; ++c)
-      if ((c & 3) == part) {
-        const int chunk = tid + NT * c;
-        *reinterpret_cast<u32x4 *>(sm + buf * STAGE + (chunk >> 3) * LDA + (chunk & 7) * 8) = S.a[c];
-      }
+      for (int c = 0; c < A_CH; ++c)
+        if ((c & 3) == part) {
+          const int chunk = tid + NT * c;
+          *reinterpret_cast<u32x4 *>(sm + buf * STAGE + a_off(chunk >> 3, chunk & 7)) = S.a[c];
+        }
+    }
     uint32_t o[BPP];
 #pragma unroll
     for (int b = 0; b < BPP; ++b) {
@@ -255,9 +292,9 @@ __global__ __launch_bounds__(512) void nf4_gemm_kernel(GemmParams p) {
     u32x4 a[TM], b[TN];
   };
   auto load_frags = [&](int buf, bool kn, int kk, Frags &F) {
-    const uint16_t *as = sm + buf * STAGE + (wm * WTM + l32) * LDA + 32 * g;
 #pragma unroll
-    for (int i = 0; i < TM; ++i) F.a[i] = *reinterpret_cast<const u32x4 *>(as + i * 32 * LDA + 8 * kk);
+    for (int i = 0; i < TM; ++i)
+      F.a[i] = *reinterpret_cast<const u32x4 *>(sm + buf * STAGE + a_off(wm * WTM + i * 32 + l32, 4 * g + kk));
     load_bfrag(bsm + buf * STAGE, kn, kk, F.b);
   };
   auto mma_frags = [&](const Frags &F) {
@@ -285,6 +322,14 @@ __global__ __launch_bounds__(512) void nf4_gemm_kernel(GemmParams p) {
   float ah = 0.0f;
   __syncthreads();  // decode table ready
   const int nk = p.ksteps;
+  // kDma: wait until at most n vector-memory operations of this wave are outstanding
+  // (the LDS-bound A loads count; the compiler cannot know that other waves read them)
+  auto wait_vm = [](auto nconst) {
+    constexpr int n = decltype(nconst)::value;
+    if constexpr (kDma) __builtin_amdgcn_s_waitcnt((n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14));
+  };
+  if constexpr (kDma) load_a_lds(0, 0);
+  __builtin_amdgcn_sched_barrier(0);
   load_stage(0, S0);
   __builtin_amdgcn_sched_barrier(0);
   load_stage(1, S1);
@@ -292,12 +337,15 @@ __global__ __launch_bounds__(512) void nf4_gemm_kernel(GemmParams p) {
   read_levels(S0);
 #pragma unroll
   for (int part = 0; part < 4; ++part) put_part(0, part, S0, ah);
+  wait_vm(std::integral_constant<int, 3>{});  // stage 0's A, and everything older than stage 1's codes
   __syncthreads();
   auto step = [&](int kt, Stage &Snext, Stage &Sfree) {
     // Snext holds step kt+1; Sfree is refilled with step kt+2 (past the last step
     // these loads and writes are harmless and unused).  The fragments of MFMA
     // group kk+1 are read while group kk's MFMAs run.
     const int buf = kt & 1;
+    if constexpr (kDma) load_a_lds(kt + 1, buf ^ 1);  // that buffer is read by nobody since the last barrier
+    __builtin_amdgcn_sched_barrier(0);
     load_stage(kt + 2, Sfree);
     __builtin_amdgcn_sched_barrier(0);
     if constexpr (kEarly) {
@@ -310,6 +358,7 @@ __global__ __launch_bounds__(512) void nf4_gemm_kernel(GemmParams p) {
         mma_kk(buf, TRANS, kk);
         put_part(buf ^ 1, kk, Snext, ah);
       }
+      wait_vm(std::integral_constant<int, 3>{});  // stage kt+1's A in LDS; stage kt+2's codes may fly
       __syncthreads();
       return;
     }
@@ -326,6 +375,7 @@ __global__ __launch_bounds__(512) void nf4_gemm_kernel(GemmParams p) {
     put_part(buf ^ 1, 2, Snext, ah);
     mma_frags(F1);
     put_part(buf ^ 1, 3, Snext, ah);
+    wait_vm(std::integral_constant<int, 3>{});  // stage kt+1's A in LDS; stage kt+2's codes may fly
     __syncthreads();
   };
   // Uniform two-step body (the same loads in flight on every path); an odd
@@ -335,10 +385,9 @@ __global__ __launch_bounds__(512) void nf4_gemm_kernel(GemmParams p) {
     step(kt, S1, S0);
     step(kt + 1, S0, S1);
   }
-  if (kt < nk) {
-    mma_step(kt & 1, TRANS);
-    __syncthreads();
-  }
+  if (kt < nk) mma_step(kt & 1, TRANS);
+  __builtin_amdgcn_s_waitcnt(0);  // no LDS-bound load of a stage past the end may still land
+  __syncthreads();
 
   // LoRA K steps.  Forward: B2 = L2 [r][N] read as a [k][n] tile; dX: B2 = L1 padded
   // to [N][ldb2] read as an [n][k] tile.  Rows past the ends read as zero.
@@ -350,7 +399,7 @@ __global__ __launch_bounds__(512) void nf4_gemm_kernel(GemmParams p) {
 #pragma unroll
       for (int c = 0; c < A_CH; ++c) {
         const int chunk = tid + NT * c, row = chunk >> 3, col8 = chunk & 7;
-        *reinterpret_cast<u32x4 *>(sm + row * LDA + col8 * 8) =
+        *reinterpret_cast<u32x4 *>(sm + a_off(row, col8)) =
             bload128(rA2, (int)((row * p.lda2 + col8 * 8) * 2), k2 * BK * 2);
       }
       for (int chunk = tid; chunk < BN * 8; chunk += NT) {

@@ -322,6 +322,57 @@ __global__ __launch_bounds__(512) void nf4_gemm_kernel(GemmParams p) {
   float ah = 0.0f;
   __syncthreads();  // decode table ready
   const int nk = p.ksteps;
+  // LoRA K steps.  Forward: B2 = L2 [r][N] read as a [k][n] tile; dX: B2 = L1 padded
+  // to [N][ldb2] read as an [n][k] tile.  Rows past the ends read as zero (and every
+  // load reads zero when there is no LoRA term: the resources are then empty).
+  constexpr int B2CH = BN * 8 / NT;  // 16-byte B2 chunks per thread per LoRA step
+  constexpr bool kLoraEarly = kDma;  // registers to spare for the first step's operands
+  const bool lora = p.ksteps2 > 0;
+  const auto rA2 = make_rsrc(p.A2 + m0 * p.lda2, lora ? mrows * p.lda2 * 2 : 0);
+  const auto rB2 = TRANS ? make_rsrc(p.B2 + n0 * p.ldb2, lora ? nrows * p.ldb2 * 2 : 0)
+                         : make_rsrc(p.B2 + n0, lora ? ((int64_t)p.b2rows * p.ldb2 - n0) * 2 : 0);
+  struct LoraStage {
+    u32x4 a[A_CH], b[B2CH];
+  };
+  auto lora_load = [&](int k2, LoraStage &L) {
+#pragma unroll
+    for (int c = 0; c < A_CH; ++c) {
+      const int chunk = tid + NT * c, row = chunk >> 3, col8 = chunk & 7;
+      L.a[c] = bload128(rA2, (int)((row * p.lda2 + col8 * 8) * 2), k2 * BK * 2);
+    }
+#pragma unroll
+    for (int c = 0; c < B2CH; ++c) {
+      const int chunk = tid + NT * c;
+      if (TRANS) {  // [n][k] tile: BN rows of 8 chunks
+        const int row = chunk >> 3, col8 = chunk & 7;
+        L.b[c] = bload128(rB2, (int)((row * p.ldb2 + col8 * 8) * 2), k2 * BK * 2);
+      } else {  // [k][n] tile: 64 rows of BN/8 chunks
+        const int krow = chunk / (BN / 8), col8 = chunk % (BN / 8);
+        L.b[c] = bload128(rB2, (int)(((int64_t)(k2 * BK + krow) * p.ldb2 + col8 * 8) * 2), 0);
+      }
+    }
+  };
+  auto lora_put = [&](const LoraStage &L) {
+#pragma unroll
+    for (int c = 0; c < A_CH; ++c) {
+      const int chunk = tid + NT * c, row = chunk >> 3, col8 = chunk & 7;
+      *reinterpret_cast<u32x4 *>(sm + a_off(row, col8)) = L.a[c];
+    }
+#pragma unroll
+    for (int c = 0; c < B2CH; ++c) {
+      const int chunk = tid + NT * c;
+      if (TRANS) {
+        const int row = chunk >> 3, col8 = chunk & 7;
+        *reinterpret_cast<u32x4 *>(bsm + row * LDNK + col8 * 8) = L.b[c];
+      } else {
+        const int krow = chunk / (BN / 8), col8 = chunk % (BN / 8);
+        *reinterpret_cast<u32x4 *>(bsm + krow * LDKN + col8 * 8) = L.b[c];
+      }
+    }
+  };
+  LoraStage L0;
+  if constexpr (kLoraEarly) lora_load(0, L0);  // oldest loads: done long before they are used
+
   // kDma: wait until at most n vector-memory operations of this wave are outstanding
   // (the LDS-bound A loads count; the compiler cannot know that other waves read them)
   auto wait_vm = [](auto nconst) {
@@ -389,34 +440,16 @@ __global__ __launch_bounds__(512) void nf4_gemm_kernel(GemmParams p) {
   __builtin_amdgcn_s_waitcnt(0);  // no LDS-bound load of a stage past the end may still land
   __syncthreads();
 
-  // LoRA K steps.  Forward: B2 = L2 [r][N] read as a [k][n] tile; dX: B2 = L1 padded
-  // to [N][ldb2] read as an [n][k] tile.  Rows past the ends read as zero.
-  if (p.ksteps2 > 0) {
-    const auto rA2 = make_rsrc(p.A2 + m0 * p.lda2, mrows * p.lda2 * 2);
-    const auto rB2 = TRANS ? make_rsrc(p.B2 + n0 * p.ldb2, nrows * p.ldb2 * 2)
-                           : make_rsrc(p.B2 + n0, ((int64_t)p.b2rows * p.ldb2 - n0) * 2);
-    for (int k2 = 0; k2 < p.ksteps2; ++k2) {
-#pragma unroll
-      for (int c = 0; c < A_CH; ++c) {
-        const int chunk = tid + NT * c, row = chunk >> 3, col8 = chunk & 7;
-        *reinterpret_cast<u32x4 *>(sm + a_off(row, col8)) =
-            bload128(rA2, (int)((row * p.lda2 + col8 * 8) * 2), k2 * BK * 2);
-      }
-      for (int chunk = tid; chunk < BN * 8; chunk += NT) {
-        if (TRANS) {  // [n][k] tile: BN rows of 8 chunks
-          const int row = chunk >> 3, col8 = chunk & 7;
-          *reinterpret_cast<u32x4 *>(bsm + row * LDNK + col8 * 8) =
-              bload128(rB2, (int)((row * p.ldb2 + col8 * 8) * 2), k2 * BK * 2);
-        } else {  // [k][n] tile: 64 rows of BN/8 chunks
-          const int krow = chunk / (BN / 8), col8 = chunk % (BN / 8);
-          *reinterpret_cast<u32x4 *>(bsm + krow * LDKN + col8 * 8) =
-              bload128(rB2, (int)(((int64_t)(k2 * BK + krow) * p.ldb2 + col8 * 8) * 2), 0);
-        }
-      }
-      __syncthreads();
-      mma_step(0, !TRANS);
-      __syncthreads();
-    }
+  // LoRA K steps (after the main loop, on the same accumulators).  The first one's
+  // operands were loaded in the prologue (lora_load above) where registers allow.
+  for (int k2 = 0; k2 < p.ksteps2; ++k2) {
+    LoraStage L;
+    if (kLoraEarly && k2 == 0) L = L0;
+    else lora_load(k2, L);
+    lora_put(L);
+    __syncthreads();
+    mma_step(0, !TRANS);
+    __syncthreads();
   }
 
   // Epilogue: fp32 -> bf16 through LDS, then coalesced 16-byte stores.

@@ -326,7 +326,10 @@ __global__ __launch_bounds__(512) void nf4_gemm_kernel(GemmParams p) {
   // to [N][ldb2] read as an [n][k] tile.  Rows past the ends read as zero (and every
   // load reads zero when there is no LoRA term: the resources are then empty).
   constexpr int B2CH = BN * 8 / NT;  // 16-byte B2 chunks per thread per LoRA step
-  constexpr bool kLoraEarly = kDma;  // registers to spare for the first step's operands
+  // two fragment register sets (fragments of MFMA group kk+1 read while group kk runs)
+  // wherever registers allow: all but the 256-wide dX tiles
+  constexpr bool kTwoFrag = TM * TN <= 4 || kDma;
+  constexpr bool kLoraEarly = kDma && TM * TN <= 4;  // registers to spare for the first step's operands
   const bool lora = p.ksteps2 > 0;
   const auto rA2 = make_rsrc(p.A2 + m0 * p.lda2, lora ? mrows * p.lda2 * 2 : 0);
   const auto rB2 = TRANS ? make_rsrc(p.B2 + n0 * p.ldb2, lora ? nrows * p.ldb2 * 2 : 0)
@@ -403,7 +406,7 @@ __global__ __launch_bounds__(512) void nf4_gemm_kernel(GemmParams p) {
       read_levels(Snext);
       __builtin_amdgcn_sched_barrier(0);
     }
-    if constexpr (TM * TN > 4) {  // 256x256 tiles: no registers to spare for a second fragment set
+    if constexpr (!kTwoFrag) {  // 256-wide dX tiles: no registers to spare for a second fragment set
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) {
         mma_kk(buf, TRANS, kk);

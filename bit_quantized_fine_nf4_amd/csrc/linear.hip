@@ -540,10 +540,10 @@ __global__ __launch_bounds__(256) void lora_grad_kernel(GradProblem pa, GradProb
         const int q = 16 * t + c16;
         uint32_t w[4];
 #pragma unroll
-        for (int x = 0; x < 4; ++x) {
-          const uint32_t lo = q < rq ? Qs[buf][(mk + 8 * g + 2 * x) * ldq + q] : 0u;
-          const uint32_t hi = q < rq ? Qs[buf][(mk + 8 * g + 2 * x + 1) * ldq + q] : 0u;
-          w[x] = lo | (hi << 16);
+        for (int x = 0; x < 4; ++x) {  // unconditional reads inside the slab (ldq <= RP), masked after
+          const uint32_t lo = Qs[buf][(mk + 8 * g + 2 * x) * ldq + q];
+          const uint32_t hi = Qs[buf][(mk + 8 * g + 2 * x + 1) * ldq + q];
+          w[x] = q < rq ? lo | (hi << 16) : 0u;
         }
         const u32x4 bq{w[0], w[1], w[2], w[3]};
 #pragma unroll

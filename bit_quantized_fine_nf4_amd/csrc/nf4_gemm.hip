@@ -243,6 +243,7 @@ __global__ __launch_bounds__(512) void nf4_gemm_kernel(GemmParams p) {
       for (int byte = 0; byte < UB; ++byte) LV[byte] = lut[(S.c[byte >> 2] >> (8 * (byte & 3))) & 0xFF];
     }
   };
+  uint32_t oprev[2] = {0u, 0u};  // an even part's decoded words, stored with the next part's
   auto put_part = [&](int buf, int part, const Stage &S, float &ah) {
     // int8 value from the zero-extended byte by float arithmetic: a plain
     // sign extension would let instruction selection fuse it with the load
@@ -269,10 +270,15 @@ __global__ __launch_bounds__(512) void nf4_gemm_kernel(GemmParams p) {
       o[b] = pack_bf16x2(l[0] * ah, l[1] * ah);
     }
     uint16_t *dst = bdst0 + buf * STAGE + part * 2 * BPP;
-    if (BPP == 4)
+    if constexpr (BPP == 4) {
       *reinterpret_cast<u32x4 *>(dst) = u32x4{o[0], o[1], o[2], o[3]};
-    else
-      *reinterpret_cast<u32x2 *>(dst) = u32x2{o[0], o[BPP - 1]};
+    } else {
+      // two parts per 16-byte store: even parts keep their words, odd parts store both
+      if (part & 1)
+        *reinterpret_cast<u32x4 *>(dst - 2 * BPP) = u32x4{oprev[0], oprev[1], o[0], o[BPP - 1]};
+      else
+        oprev[0] = o[0], oprev[1] = o[BPP - 1];
+    }
   };
   // B fragments of MFMA step kk from an LDS tile; kn: tile is [k][n] (transposing reads)
   auto load_bfrag = [&](const uint16_t *bs, bool kn, int kk, u32x4 (&bf)[TN]) {

@@ -726,7 +726,8 @@ struct TimedLaunch {
 // time.  Per pair (n, n+1) a lane decodes its 8 columns of both rows to
 // bf16(level * a_hat), packs the two rows' values of each column into a bf16
 // pair and accumulates dY[m][n..n+1] . pair with one v_dot2 per (token,
-// column).  Codes and scales are loaded four (two for 16 tokens) pairs ahead
+// column).  This variant serves up to kDxMfmaMin tokens (more take the
+// matrix-core variant below).  Codes and scales are loaded four pairs ahead
 // into a ring of register sets; dY pairs are wave-uniform (scalar loads).  The four waves'
 // sums meet in LDS and each workgroup writes one float32 partial; the finish
 // kernel sums the row chunks in order (deterministic), adds s·U·L1ᵀ and rounds
@@ -747,16 +748,19 @@ struct GvdParams {
 };
 
 constexpr int kGvdCols = 512;  // columns per workgroup
+// up to this many tokens the dot-product variant (4 tokens: 53 us on an 8192 x 28672
+// weight, against 65 us for the matrix-core variant, whose cost hardly depends on M)
+constexpr int kDxMfmaMin = 4;
 
 int gemv_dx_chunks(int64_t M, int64_t h, int64_t o) {
   // about 1024 workgroups (512 for more than 4 tokens, whose partial sums cost more),
-  // at least 64 rows per chunk
+  // at least 64 rows per chunk; the matrix-core path takes whole 32-row stages
   const int64_t ct = (h + kGvdCols - 1) / kGvdCols;
   const int64_t target = M <= 4 ? 1024 : 512;
   int64_t rc = (target + ct - 1) / ct;
   const int64_t maxc = o / 64 > 0 ? o / 64 : 1;
   rc = rc < 1 ? 1 : (rc > maxc ? maxc : rc);
-  const int64_t rows = rup((o + rc - 1) / rc, 2);
+  const int64_t rows = rup((o + rc - 1) / rc, M > kDxMfmaMin ? 32 : 2);
   return (int)((o + rows - 1) / rows);
 }
 
@@ -870,6 +874,126 @@ __global__ __launch_bounds__(256) void nf4_gemv_dx_kernel(GvdParams p) {
       *reinterpret_cast<f32x4 *>(o + 4) = f32x4{v[4], v[5], v[6], v[7]};
     }
     __syncthreads();
+  }
+}
+
+// Few-token backward on the matrix cores (more than kDxMfmaMin tokens): the same
+// row chunks and partial sums as nf4_gemv_dx_kernel, but each 32-row stage of the
+// workgroup's 512 columns is decoded once into an LDS [k][n] tile of
+// bf16(level * a_hat), and 16x16x32 MFMAs take the tokens as their rows: A =
+// dY[token][32 rows of o] straight from memory (tokens past M read as zero), B =
+// the tile through transposing LDS reads (ds_read_b64_tr_b16).  512 threads:
+// wave w owns columns [64 w, 64 w + 64) (4 MFMA tiles); decode role: thread t
+// takes row t / 16 of a stage and 32 columns of it (16 code bytes, inside one
+// 64-column block).  Codes, scales and dY fragments are loaded two stages ahead;
+// the tile is double-buffered with one barrier per stage, and two workgroups fit
+// on a compute unit.  Chunks hold whole stages.
+constexpr int kGvmRows = 32;                 // rows (of o) per stage
+constexpr int kGvmLd = kGvdCols + 24;        // tile row stride: 12 banks mod 64, as in the dX GEMM
+
+constexpr int kGvmThreads = 512;
+
+struct GvmStage {
+  u32x4 c0;      // this thread's 16 code bytes (32 columns of one row)
+  uint32_t q;    // its int8 block scale, zero-extended
+  float s2;      // its second-level scale
+  u32x4 a;       // this lane's dY fragment: 8 rows of o for one token
+};
+
+__global__ __launch_bounds__(kGvmThreads) void nf4_gemv_dx_mfma_kernel(GvdParams p) {
+  __shared__ f32x2 lv2[256];
+  __shared__ __attribute__((aligned(16))) uint16_t tile[2][kGvmRows * kGvmLd];
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  if (tid < 256) lv2[tid] = f32x2{p.level[tid >> 4], p.level[tid & 15]};
+  const int64_t h = p.h, nblk = h >> 6;
+  const int64_t c0 = (int64_t)blockIdx.x * kGvdCols;
+  const int64_t n0 = (int64_t)blockIdx.y * p.rows;
+  const int64_t n1 = n0 + p.rows < p.o ? n0 + p.rows : p.o;
+  const int nst = (int)((n1 - n0) / kGvmRows);
+  const float mu = *p.mean;
+  // decode role; rows past n1 read as zero codes and scales (and meet no stage)
+  const int drow = tid >> 4, dpart = tid & 15;
+  const int64_t dcol = c0 + 32 * dpart;
+  const bool dlive = dcol < h;  // h is a multiple of 64
+  const auto rc = gv_rsrc(p.codes + n0 * (h >> 1), (n1 - n0) * (h >> 1));
+  const auto rq = gv_rsrc(p.qabsmax + n0 * nblk, (n1 - n0) * nblk);
+  const auto rs = gv_rsrc(p.scale2, ((p.o * nblk + kChunk - 1) / kChunk) * 4);
+  const auto ry = gv_rsrc(p.dY, (int64_t)p.M * p.ldy * 2);
+  const int voc = dlive ? (int)(drow * (h >> 1) + (dcol >> 1)) : kGvOOB;
+  const int voq = dlive ? (int)(drow * nblk + (dcol >> 6)) : kGvOOB;
+  const int64_t blk0 = (n0 + drow) * nblk + (dcol >> 6);
+  // MFMA role: lane (i = lane % 16, g = lane / 16)
+  const int i16 = lane & 15, g = lane >> 4;
+  const int voy = (int)((i16 * p.ldy + n0 + 8 * g) * 2);  // tokens >= M: past the buffer, zero
+  auto load = [&](int st_, GvmStage &S) {
+    const int st = __builtin_amdgcn_readfirstlane(st_);
+    S.c0 = __builtin_amdgcn_raw_buffer_load_b128(rc, voc, st * kGvmRows * (int)(h >> 1), 0);
+    S.q = __builtin_amdgcn_raw_buffer_load_b8(rq, voq, st * kGvmRows * (int)nblk, 0);
+    S.s2 = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                         rs, (int)(((blk0 + (int64_t)st * kGvmRows * nblk) >> 8) * 4), 0, 0));
+    S.a = __builtin_amdgcn_raw_buffer_load_b128(ry, voy, st * kGvmRows * 2, 0);
+  };
+  auto put = [&](const GvmStage &S, int buf) {
+    const float ah = scale_hat((int8_t)(S.q & 0xFF), S.s2, mu);
+    uint16_t *dst = &tile[buf][drow * kGvmLd + 32 * dpart];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {  // 16-byte piece e: code bytes 4e .. 4e + 3, columns 8e .. 8e + 7
+      const uint32_t w = S.c0[e];
+      uint32_t o[4];
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        const f32x2 l = lv2[(w >> (8 * b)) & 0xFF];
+        o[b] = pack_bf16x2(l[0] * ah, l[1] * ah);
+      }
+      *reinterpret_cast<u32x4 *>(dst + 8 * e) = u32x4{o[0], o[1], o[2], o[3]};
+    }
+  };
+  f32x4 acc[4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) acc[t] = f32x4{0, 0, 0, 0};
+  // lane 4j + q of a 16-lane group names row 8g + j (+4), columns 4q .. 4q + 3 of the MFMA tile
+  const int trow = i16 >> 2, tcol = (i16 & 3) * 4;
+  auto compute = [&](int buf, const u32x4 &a) {
+    const uint16_t *b0 = &tile[buf][(8 * g + trow) * kGvmLd + 64 * wave + tcol];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) acc[t] = mfma16(a, tr_pair(b0 + 16 * t, b0 + 4 * kGvmLd + 16 * t), acc[t]);
+  };
+  auto step = [&](int st, GvmStage &Rcur, GvmStage &Rnext) {
+    // Rcur: stage st (tile in buffer st & 1, dY fragment needed now); Rnext: stage st + 1 (codes to decode)
+    const u32x4 a = Rcur.a;
+    __builtin_amdgcn_sched_barrier(0);
+    load(st + 2, Rcur);
+    __builtin_amdgcn_sched_barrier(0);
+    compute(st & 1, a);
+    put(Rnext, (st + 1) & 1);
+    __syncthreads();
+  };
+  GvmStage R0, R1;
+  load(0, R0);
+  __builtin_amdgcn_sched_barrier(0);
+  load(1, R1);
+  __builtin_amdgcn_sched_barrier(0);
+  __syncthreads();  // decode table ready
+  put(R0, 0);
+  __syncthreads();
+  int st = 0;
+  for (; st + 1 < nst; st += 2) {
+    step(st, R0, R1);
+    step(st + 1, R1, R0);
+  }
+  if (st < nst) compute(st & 1, R0.a);
+
+  // D layout: lane (n = lane % 16, g) holds tokens 4g + v of column 64 wave + 16 t + n
+  float *outp = p.part + (int64_t)blockIdx.y * p.M * h;
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    const int64_t col = c0 + 64 * wave + 16 * t + i16;
+    if (col >= h) continue;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int m = 4 * g + v;
+      if (m < p.M) outp[(int64_t)m * h + col] = acc[t][v];
+    }
   }
 }
 
@@ -1014,7 +1138,8 @@ hipError_t launch_linear_bwd(const LinearArgs &a, const uint16_t *X, const uint1
     vp.dY = dY; vp.ldy = a.o; vp.M = (int)a.M;
     vp.codes = a.codes; vp.qabsmax = a.qabsmax; vp.scale2 = a.scale2; vp.mean = a.mean;
     vp.h = a.h; vp.o = a.o;
-    vp.rows = (int)rup((a.o + L.dxc - 1) / L.dxc, 2);
+    // rows per chunk (at most L.dxc chunks; trailing ones may be empty and then store zeros)
+    vp.rows = (int)rup((a.o + L.dxc - 1) / L.dxc, a.M > kDxMfmaMin ? kGvmRows : 2);
     vp.part = at<float>(ws, L.off_dxp);
     fill_levels(vp.level, tab);
     const dim3 grid((unsigned)((a.h + kGvdCols - 1) / kGvdCols), (unsigned)L.dxc);
@@ -1022,8 +1147,8 @@ hipError_t launch_linear_bwd(const LinearArgs &a, const uint16_t *X, const uint1
       {
         TimedLaunch tl(1, st);
         if (a.M == 1) nf4_gemv_dx_kernel<1><<<grid, 256, 0, st>>>(vp);
-        else if (a.M <= 4) nf4_gemv_dx_kernel<4><<<grid, 256, 0, st>>>(vp);
-        else nf4_gemv_dx_kernel<16><<<grid, 256, 0, st>>>(vp);
+        else if (a.M <= kDxMfmaMin) nf4_gemv_dx_kernel<kDxMfmaMin><<<grid, 256, 0, st>>>(vp);
+        else nf4_gemv_dx_mfma_kernel<<<grid, kGvmThreads, 0, st>>>(vp);
       }
       const int64_t cg = (a.h / 8 + 63) / 64;
       gemv_dx_finish_kernel<<<(unsigned)(a.M * cg), 256, 0, st>>>(vp.part, L.dxc, (int)a.M, a.h, sU, L.RP64, L1,

@@ -758,6 +758,9 @@ int gemv_dx_chunks(int64_t M, int64_t h, int64_t o) {
   const int64_t ct = (h + kGvdCols - 1) / kGvdCols;
   const int64_t target = M <= 4 ? 1024 : 512;
   int64_t rc = (target + ct - 1) / ct;
+  // a chunk's codes stay under 2^30 bytes (32-bit buffer offsets in the matrix-core variant)
+  const int64_t minc = (o * (h >> 1) + (int64_t(1) << 30) - 1) >> 30;
+  rc = rc > minc ? rc : minc;
   const int64_t maxc = o / 64 > 0 ? o / 64 : 1;
   rc = rc < 1 ? 1 : (rc > maxc ? maxc : rc);
   const int64_t rows = rup((o + rc - 1) / rc, M > kDxMfmaMin ? 32 : 2);
@@ -879,32 +882,45 @@ __global__ __launch_bounds__(256) void nf4_gemv_dx_kernel(GvdParams p) {
 
 // Few-token backward on the matrix cores (more than kDxMfmaMin tokens): the same
 // row chunks and partial sums as nf4_gemv_dx_kernel, but each 32-row stage of the
-// workgroup's 512 columns is decoded once into an LDS [k][n] tile of
-// bf16(level * a_hat), and 16x16x32 MFMAs take the tokens as their rows: A =
-// dY[token][32 rows of o] straight from memory (tokens past M read as zero), B =
-// the tile through transposing LDS reads (ds_read_b64_tr_b16).  512 threads:
-// wave w owns columns [64 w, 64 w + 64) (4 MFMA tiles); decode role: thread t
-// takes row t / 16 of a stage and 32 columns of it (16 code bytes, inside one
-// 64-column block).  Codes, scales and dY fragments are loaded two stages ahead;
-// the tile is double-buffered with one barrier per stage, and two workgroups fit
-// on a compute unit.  Chunks hold whole stages.
+// workgroup's 512 columns is decoded once into an LDS [k][n] tile of bf16(level)
+// (a code byte is one read of a table of bf16 pairs), and 16x16x32 MFMAs take the
+// tokens as their rows.  The block scale rides on the other operand: wave w owns
+// columns [64 w, 64 w + 64), one 64-column block, so its A operand is
+// bf16(dY[token][n] * a_hat[n][block]) for the 32 rows n of the stage (tokens past
+// M read as zero), and B is the tile through transposing LDS reads
+// (ds_read_b64_tr_b16), 4 MFMA tiles per wave.  Decode role: thread t takes row
+// t / 16 of a stage and the 8-column pieces t % 16 + 16 e (e < 4) of it, so the
+// 16 threads of a row store 256 contiguous bytes per 16-byte store (no bank
+// conflicts); threads t % 16 < 8 also publish the row's a_hat of block t % 16.
+// Columns past h decode whatever the buffer holds (a finite level) and are
+// never stored.  Codes, scales and dY fragments are
+// loaded two stages ahead; the tile and the scales are double-buffered with one
+// barrier per stage, and two workgroups fit on a compute unit.  Chunks hold whole
+// stages.
 constexpr int kGvmRows = 32;                 // rows (of o) per stage
 constexpr int kGvmLd = kGvdCols + 24;        // tile row stride: 12 banks mod 64, as in the dX GEMM
 
 constexpr int kGvmThreads = 512;
+constexpr int kGvmLutCopies = 8;             // interleaved copies of the byte table (fewer bank conflicts)
+static_assert(kGvmThreads == kGvdCols, "one wave per 64-column block");
 
 struct GvmStage {
-  u32x4 c0;      // this thread's 16 code bytes (32 columns of one row)
+  u32x4 c;       // this thread's 4 code dwords (pieces e = 0 .. 3, 8 columns each)
   uint32_t q;    // its int8 block scale, zero-extended
   float s2;      // its second-level scale
   u32x4 a;       // this lane's dY fragment: 8 rows of o for one token
 };
 
 __global__ __launch_bounds__(kGvmThreads) void nf4_gemv_dx_mfma_kernel(GvdParams p) {
-  __shared__ f32x2 lv2[256];
+  // lut[kGvmLutCopies * byte + copy] = bf16 pair (level[high nibble], level[low nibble])
+  __shared__ uint32_t lut[256 * kGvmLutCopies];
+  __shared__ __attribute__((aligned(16))) float ahs[2][kGvdCols / 64][kGvmRows];  // a_hat per [block][row]
   __shared__ __attribute__((aligned(16))) uint16_t tile[2][kGvmRows * kGvmLd];
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  if (tid < 256) lv2[tid] = f32x2{p.level[tid >> 4], p.level[tid & 15]};
+  for (int i = tid; i < 256 * kGvmLutCopies; i += kGvmThreads) {
+    const int e = i / kGvmLutCopies;
+    lut[i] = pack_bf16x2(p.level[e >> 4], p.level[e & 15]);
+  }
   const int64_t h = p.h, nblk = h >> 6;
   const int64_t c0 = (int64_t)blockIdx.x * kGvdCols;
   const int64_t n0 = (int64_t)blockIdx.y * p.rows;
@@ -913,39 +929,38 @@ __global__ __launch_bounds__(kGvmThreads) void nf4_gemv_dx_mfma_kernel(GvdParams
   const float mu = *p.mean;
   // decode role; rows past n1 read as zero codes and scales (and meet no stage)
   const int drow = tid >> 4, dpart = tid & 15;
-  const int64_t dcol = c0 + 32 * dpart;
-  const bool dlive = dcol < h;  // h is a multiple of 64
   const auto rc = gv_rsrc(p.codes + n0 * (h >> 1), (n1 - n0) * (h >> 1));
   const auto rq = gv_rsrc(p.qabsmax + n0 * nblk, (n1 - n0) * nblk);
   const auto rs = gv_rsrc(p.scale2, ((p.o * nblk + kChunk - 1) / kChunk) * 4);
   const auto ry = gv_rsrc(p.dY, (int64_t)p.M * p.ldy * 2);
-  const int voc = dlive ? (int)(drow * (h >> 1) + (dcol >> 1)) : kGvOOB;
-  const int voq = dlive ? (int)(drow * nblk + (dcol >> 6)) : kGvOOB;
-  const int64_t blk0 = (n0 + drow) * nblk + (dcol >> 6);
+  const int voc = (int)(drow * (h >> 1) + (c0 >> 1) + 4 * dpart);  // piece e at + 64 e
+  const int sblk = (int)(c0 >> 6) + (dpart & 7);                   // the block whose a_hat it publishes
+  const int voq = (int)(drow * nblk + sblk);
+  const int64_t blk0 = (n0 + drow) * nblk + sblk;
   // MFMA role: lane (i = lane % 16, g = lane / 16)
   const int i16 = lane & 15, g = lane >> 4;
   const int voy = (int)((i16 * p.ldy + n0 + 8 * g) * 2);  // tokens >= M: past the buffer, zero
   auto load = [&](int st_, GvmStage &S) {
     const int st = __builtin_amdgcn_readfirstlane(st_);
-    S.c0 = __builtin_amdgcn_raw_buffer_load_b128(rc, voc, st * kGvmRows * (int)(h >> 1), 0);
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      S.c[e] = __builtin_amdgcn_raw_buffer_load_b32(rc, voc + 64 * e, st * kGvmRows * (int)(h >> 1), 0);
     S.q = __builtin_amdgcn_raw_buffer_load_b8(rq, voq, st * kGvmRows * (int)nblk, 0);
     S.s2 = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
                                          rs, (int)(((blk0 + (int64_t)st * kGvmRows * nblk) >> 8) * 4), 0, 0));
     S.a = __builtin_amdgcn_raw_buffer_load_b128(ry, voy, st * kGvmRows * 2, 0);
   };
+  const int lcopy = lane % kGvmLutCopies;
   auto put = [&](const GvmStage &S, int buf) {
-    const float ah = scale_hat((int8_t)(S.q & 0xFF), S.s2, mu);
-    uint16_t *dst = &tile[buf][drow * kGvmLd + 32 * dpart];
+    if (dpart < 8) ahs[buf][dpart][drow] = scale_hat((int8_t)(S.q & 0xFF), S.s2, mu);
+    uint16_t *dst = &tile[buf][drow * kGvmLd + 8 * dpart];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {  // 16-byte piece e: code bytes 4e .. 4e + 3, columns 8e .. 8e + 7
-      const uint32_t w = S.c0[e];
+    for (int e = 0; e < 4; ++e) {  // piece e: columns 8 (16 e + dpart) .. + 7
+      const uint32_t w = S.c[e];
       uint32_t o[4];
 #pragma unroll
-      for (int b = 0; b < 4; ++b) {
-        const f32x2 l = lv2[(w >> (8 * b)) & 0xFF];
-        o[b] = pack_bf16x2(l[0] * ah, l[1] * ah);
-      }
-      *reinterpret_cast<u32x4 *>(dst + 8 * e) = u32x4{o[0], o[1], o[2], o[3]};
+      for (int b = 0; b < 4; ++b) o[b] = lut[((w >> (8 * b)) & 0xFF) * kGvmLutCopies + lcopy];
+      *reinterpret_cast<u32x4 *>(dst + 128 * e) = u32x4{o[0], o[1], o[2], o[3]};
     }
   };
   f32x4 acc[4];
@@ -954,9 +969,16 @@ __global__ __launch_bounds__(kGvmThreads) void nf4_gemv_dx_mfma_kernel(GvdParams
   // lane 4j + q of a 16-lane group names row 8g + j (+4), columns 4q .. 4q + 3 of the MFMA tile
   const int trow = i16 >> 2, tcol = (i16 & 3) * 4;
   auto compute = [&](int buf, const u32x4 &a) {
+    // A = bf16(dY * a_hat): lane's rows 8g .. 8g + 7, all in this wave's block
+    const f32x4 sa = *reinterpret_cast<const f32x4 *>(&ahs[buf][wave][8 * g]);
+    const f32x4 sb = *reinterpret_cast<const f32x4 *>(&ahs[buf][wave][8 * g + 4]);
+    const u32x4 as{pack_bf16x2(bf16_lo(a[0]) * sa[0], bf16_hi(a[0]) * sa[1]),
+                   pack_bf16x2(bf16_lo(a[1]) * sa[2], bf16_hi(a[1]) * sa[3]),
+                   pack_bf16x2(bf16_lo(a[2]) * sb[0], bf16_hi(a[2]) * sb[1]),
+                   pack_bf16x2(bf16_lo(a[3]) * sb[2], bf16_hi(a[3]) * sb[3])};
     const uint16_t *b0 = &tile[buf][(8 * g + trow) * kGvmLd + 64 * wave + tcol];
 #pragma unroll
-    for (int t = 0; t < 4; ++t) acc[t] = mfma16(a, tr_pair(b0 + 16 * t, b0 + 4 * kGvmLd + 16 * t), acc[t]);
+    for (int t = 0; t < 4; ++t) acc[t] = mfma16(as, tr_pair(b0 + 16 * t, b0 + 4 * kGvmLd + 16 * t), acc[t]);
   };
   auto step = [&](int st, GvmStage &Rcur, GvmStage &Rnext) {
     // Rcur: stage st (tile in buffer st & 1, dY fragment needed now); Rnext: stage st + 1 (codes to decode)

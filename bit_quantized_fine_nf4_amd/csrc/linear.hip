@@ -26,6 +26,8 @@
 #include "linear.h"
 #include "gemm.h"
 
+#include <type_traits>
+
 
 namespace ql {
 
@@ -751,10 +753,11 @@ constexpr int kGvdCols = 512;  // columns per workgroup
 // up to this many tokens the dot-product variant (4 tokens: 53 us on an 8192 x 28672
 // weight, against 65 us for the matrix-core variant, whose cost hardly depends on M)
 constexpr int kDxMfmaMin = 4;
+constexpr int kGvmRows = 64;  // rows (of o) per stage of the matrix-core variant
 
 int gemv_dx_chunks(int64_t M, int64_t h, int64_t o) {
   // about 1024 workgroups (512 for more than 4 tokens, whose partial sums cost more),
-  // at least 64 rows per chunk; the matrix-core path takes whole 32-row stages
+  // at least 64 rows per chunk; the matrix-core path takes whole stages
   const int64_t ct = (h + kGvdCols - 1) / kGvdCols;
   const int64_t target = M <= 4 ? 1024 : 512;
   int64_t rc = (target + ct - 1) / ct;
@@ -763,7 +766,7 @@ int gemv_dx_chunks(int64_t M, int64_t h, int64_t o) {
   rc = rc > minc ? rc : minc;
   const int64_t maxc = o / 64 > 0 ? o / 64 : 1;
   rc = rc < 1 ? 1 : (rc > maxc ? maxc : rc);
-  const int64_t rows = rup((o + rc - 1) / rc, M > kDxMfmaMin ? 32 : 2);
+  const int64_t rows = rup((o + rc - 1) / rc, M > kDxMfmaMin ? kGvmRows : 2);
   return (int)((o + rows - 1) / rows);
 }
 
@@ -881,45 +884,55 @@ __global__ __launch_bounds__(256) void nf4_gemv_dx_kernel(GvdParams p) {
 }
 
 // Few-token backward on the matrix cores (more than kDxMfmaMin tokens): the same
-// row chunks and partial sums as nf4_gemv_dx_kernel, but each 32-row stage of the
-// workgroup's 512 columns is decoded once into an LDS [k][n] tile of bf16(level)
-// (a code byte is one read of a table of bf16 pairs), and 16x16x32 MFMAs take the
-// tokens as their rows.  The block scale rides on the other operand: wave w owns
-// columns [64 w, 64 w + 64), one 64-column block, so its A operand is
-// bf16(dY[token][n] * a_hat[n][block]) for the 32 rows n of the stage (tokens past
-// M read as zero), and B is the tile through transposing LDS reads
-// (ds_read_b64_tr_b16), 4 MFMA tiles per wave.  Decode role: thread t takes row
-// t / 16 of a stage and the 8-column pieces t % 16 + 16 e (e < 4) of it, so the
-// 16 threads of a row store 256 contiguous bytes per 16-byte store (no bank
-// conflicts); threads t % 16 < 8 also publish the row's a_hat of block t % 16.
-// Columns past h decode whatever the buffer holds (a finite level) and are
-// never stored.  Codes, scales and dY fragments are
-// loaded two stages ahead; the tile and the scales are double-buffered with one
-// barrier per stage, and two workgroups fit on a compute unit.  Chunks hold whole
-// stages.
-constexpr int kGvmRows = 32;                 // rows (of o) per stage
-constexpr int kGvmLd = kGvdCols + 24;        // tile row stride: 12 banks mod 64, as in the dX GEMM
+// row chunks and partial sums as nf4_gemv_dx_kernel, computed with 16x16x32 bf16
+// MFMAs that take the tokens as their rows.  A workgroup of 8 waves takes 512
+// columns, wave w the 64-column block w; a stage is 64 rows of o.
+//   - The stage's raw codes (64 rows x 256 bytes) go to LDS by direct-to-LDS
+//     loads, kGvmBufs - 1 stages ahead, in 16-byte chunks placed at
+//     chunk ^ (row % 16) within their row.
+//   - B: one 4-bit transposing LDS read (ds_read_b64_tr_b4) gives lane i of a
+//     16-lane group g the codes of rows 16 g .. 16 g + 15 of one column; each code
+//     byte (two consecutive rows) indexes a table of bf16 level pairs, which is
+//     exactly an MFMA B dword.  The low 8 rows feed one MFMA, the high 8 another.
+//   - A: the block scale rides here: bf16(dY[token][n] * a_hat[n][block]) for the
+//     same rows n (tokens past M read as zero).  Each stage's 512 a_hat values are
+//     published in LDS by the 512 threads, one each.
+// The 4-bit read returns a byte's low nibble first, so lane i of a group holds
+// column i ^ 1 (the stored byte keeps the even column in its high nibble).
+// Columns past h decode whatever the buffer holds (finite levels) and are never
+// stored.  Chunks hold whole stages.
+constexpr int kGvmThreads = 512;             // 8 waves: one 64-column block each
+constexpr int kGvmRowB = kGvdCols / 2;       // code bytes of a stage row
+constexpr int kGvmBufs = 2;                  // code stages held in LDS (3, with 16 table copies: 5-10 % slower)
+constexpr int kGvmLutCopies = 32;            // interleaved copies of the byte table (fewer bank conflicts)
+static_assert(kGvmThreads == kGvdCols && kGvmThreads == 8 * kGvmRows, "one wave per block, one a_hat per thread");
+static_assert(kGvmRows * kGvmRowB == 2 * 16 * kGvmThreads, "two 16-byte loads per thread and stage");
 
-constexpr int kGvmThreads = 512;
-constexpr int kGvmLutCopies = 8;             // interleaved copies of the byte table (fewer bank conflicts)
-static_assert(kGvmThreads == kGvdCols, "one wave per 64-column block");
+QL_DEV void lds_load16(__amdgpu_buffer_rsrc_t r, void *dst, int voff, int soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void *)dst, 16, voff, soff, 0, 0);
+}
 
-struct GvmStage {
-  u32x4 c;       // this thread's 4 code dwords (pieces e = 0 .. 3, 8 columns each)
-  uint32_t q;    // its int8 block scale, zero-extended
+typedef int i32x2 __attribute__((ext_vector_type(2)));
+QL_DEV u32x2 tr4(const uint8_t *p) {
+  typedef __attribute__((address_space(3))) i32x2 lds_i32x2;
+  return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr4_b64_v2i32((lds_i32x2 *)(p)));
+}
+
+struct GvmRegs {
+  u32x4 a0, a1;  // dY[token][rows 16 g .. 16 g + 7] and [16 g + 8 .. 16 g + 15] of the stage (bf16)
+  uint32_t q;    // int8 block scale of this thread's (row, block), zero-extended
   float s2;      // its second-level scale
-  u32x4 a;       // this lane's dY fragment: 8 rows of o for one token
 };
 
 __global__ __launch_bounds__(kGvmThreads) void nf4_gemv_dx_mfma_kernel(GvdParams p) {
-  // lut[kGvmLutCopies * byte + copy] = bf16 pair (level[high nibble], level[low nibble])
+  __shared__ __attribute__((aligned(16))) uint8_t cb[kGvmBufs][kGvmRows * kGvmRowB];
+  // lut[kGvmLutCopies * byte + copy] = bf16 pair (level[low nibble], level[high nibble])
   __shared__ uint32_t lut[256 * kGvmLutCopies];
   __shared__ __attribute__((aligned(16))) float ahs[2][kGvdCols / 64][kGvmRows];  // a_hat per [block][row]
-  __shared__ __attribute__((aligned(16))) uint16_t tile[2][kGvmRows * kGvmLd];
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   for (int i = tid; i < 256 * kGvmLutCopies; i += kGvmThreads) {
     const int e = i / kGvmLutCopies;
-    lut[i] = pack_bf16x2(p.level[e >> 4], p.level[e & 15]);
+    lut[i] = pack_bf16x2(p.level[e & 15], p.level[e >> 4]);
   }
   const int64_t h = p.h, nblk = h >> 6;
   const int64_t c0 = (int64_t)blockIdx.x * kGvdCols;
@@ -927,89 +940,128 @@ __global__ __launch_bounds__(kGvmThreads) void nf4_gemv_dx_mfma_kernel(GvdParams
   const int64_t n1 = n0 + p.rows < p.o ? n0 + p.rows : p.o;
   const int nst = (int)((n1 - n0) / kGvmRows);
   const float mu = *p.mean;
-  // decode role; rows past n1 read as zero codes and scales (and meet no stage)
-  const int drow = tid >> 4, dpart = tid & 15;
+  // rows past n1 read as zero codes and scales (and meet no stage)
   const auto rc = gv_rsrc(p.codes + n0 * (h >> 1), (n1 - n0) * (h >> 1));
   const auto rq = gv_rsrc(p.qabsmax + n0 * nblk, (n1 - n0) * nblk);
   const auto rs = gv_rsrc(p.scale2, ((p.o * nblk + kChunk - 1) / kChunk) * 4);
   const auto ry = gv_rsrc(p.dY, (int64_t)p.M * p.ldy * 2);
-  const int voc = (int)(drow * (h >> 1) + (c0 >> 1) + 4 * dpart);  // piece e at + 64 e
-  const int sblk = (int)(c0 >> 6) + (dpart & 7);                   // the block whose a_hat it publishes
-  const int voq = (int)(drow * nblk + sblk);
-  const int64_t blk0 = (n0 + drow) * nblk + sblk;
+  const int rowB = (int)(h >> 1);
+  // code loads: wave w's load j fills the stage's LDS bytes [1024 (2w + j), +1024),
+  // rows 4 (2w + j) .. + 3; lane L takes row r = 4 (2w + j) + L / 16 and puts its
+  // logical chunk (L % 16) ^ (r % 16) at physical chunk L % 16
+  int vcode[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int r = 4 * (2 * wave + j) + (lane >> 4);
+    vcode[j] = r * rowB + (int)(c0 >> 1) + 16 * ((lane & 15) ^ (r & 15));
+  }
+  // scale role: thread t publishes a_hat of stage row t / 8, block t % 8
+  const int srow = tid >> 3, sblk = tid & 7;
+  const int voq = (int)(srow * nblk + (c0 >> 6) + sblk);
+  const int64_t blk0 = (n0 + srow) * nblk + (c0 >> 6) + sblk;
   // MFMA role: lane (i = lane % 16, g = lane / 16)
   const int i16 = lane & 15, g = lane >> 4;
-  const int voy = (int)((i16 * p.ldy + n0 + 8 * g) * 2);  // tokens >= M: past the buffer, zero
-  auto load = [&](int st_, GvmStage &S) {
-    const int st = __builtin_amdgcn_readfirstlane(st_);
-#pragma unroll
-    for (int e = 0; e < 4; ++e)
-      S.c[e] = __builtin_amdgcn_raw_buffer_load_b32(rc, voc + 64 * e, st * kGvmRows * (int)(h >> 1), 0);
-    S.q = __builtin_amdgcn_raw_buffer_load_b8(rq, voq, st * kGvmRows * (int)nblk, 0);
-    S.s2 = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
-                                         rs, (int)(((blk0 + (int64_t)st * kGvmRows * nblk) >> 8) * 4), 0, 0));
-    S.a = __builtin_amdgcn_raw_buffer_load_b128(ry, voy, st * kGvmRows * 2, 0);
-  };
+  const int voy = (int)((i16 * p.ldy + n0 + 16 * g) * 2);  // tokens >= M: past the buffer, zero
   const int lcopy = lane % kGvmLutCopies;
-  auto put = [&](const GvmStage &S, int buf) {
-    if (dpart < 8) ahs[buf][dpart][drow] = scale_hat((int8_t)(S.q & 0xFF), S.s2, mu);
-    uint16_t *dst = &tile[buf][drow * kGvmLd + 8 * dpart];
+
+  auto load_codes = [&](int st_) {
+    const int st = __builtin_amdgcn_readfirstlane(st_);
+    uint8_t *base = &cb[st % kGvmBufs][0];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {  // piece e: columns 8 (16 e + dpart) .. + 7
-      const uint32_t w = S.c[e];
-      uint32_t o[4];
-#pragma unroll
-      for (int b = 0; b < 4; ++b) o[b] = lut[((w >> (8 * b)) & 0xFF) * kGvmLutCopies + lcopy];
-      *reinterpret_cast<u32x4 *>(dst + 128 * e) = u32x4{o[0], o[1], o[2], o[3]};
-    }
+    for (int j = 0; j < 2; ++j) lds_load16(rc, base + 1024 * (2 * wave + j), vcode[j], st * kGvmRows * rowB);
   };
+  auto load_regs = [&](int st_, GvmRegs &R) {
+    const int st = __builtin_amdgcn_readfirstlane(st_);
+    R.a0 = __builtin_amdgcn_raw_buffer_load_b128(ry, voy, st * kGvmRows * 2, 0);
+    R.a1 = __builtin_amdgcn_raw_buffer_load_b128(ry, voy + 16, st * kGvmRows * 2, 0);
+    R.q = __builtin_amdgcn_raw_buffer_load_b8(rq, voq, st * kGvmRows * (int)nblk, 0);
+    R.s2 = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                         rs, (int)(((blk0 + (int64_t)st * kGvmRows * nblk) >> 8) * 4), 0, 0));
+  };
+  auto put = [&](const GvmRegs &R, int buf) {
+    ahs[buf][sblk][srow] = scale_hat((int8_t)(R.q & 0xFF), R.s2, mu);
+  };
+  // vmcnt wait (the direct-to-LDS loads are invisible to the compiler's own waits)
+  auto wait_vm = [](auto nconst) {
+    constexpr int n = decltype(nconst)::value;
+    __builtin_amdgcn_s_waitcnt((n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14));
+  };
+  // loads issued after a stage's code loads and before its wait: that stage's
+  // register loads (4) and, with three buffers, the next stage's code loads (2)
+  // and register loads (4)
+  constexpr int kAfter = kGvmBufs == 3 ? 10 : 4;
+  static_assert(kGvmBufs == 2 || kGvmBufs == 3, "two or three code buffers");
+
   f32x4 acc[4];
 #pragma unroll
   for (int t = 0; t < 4; ++t) acc[t] = f32x4{0, 0, 0, 0};
-  // lane 4j + q of a 16-lane group names row 8g + j (+4), columns 4q .. 4q + 3 of the MFMA tile
-  const int trow = i16 >> 2, tcol = (i16 & 3) * 4;
-  auto compute = [&](int buf, const u32x4 &a) {
-    // A = bf16(dY * a_hat): lane's rows 8g .. 8g + 7, all in this wave's block
-    const f32x4 sa = *reinterpret_cast<const f32x4 *>(&ahs[buf][wave][8 * g]);
-    const f32x4 sb = *reinterpret_cast<const f32x4 *>(&ahs[buf][wave][8 * g + 4]);
-    const u32x4 as{pack_bf16x2(bf16_lo(a[0]) * sa[0], bf16_hi(a[0]) * sa[1]),
-                   pack_bf16x2(bf16_lo(a[1]) * sa[2], bf16_hi(a[1]) * sa[3]),
-                   pack_bf16x2(bf16_lo(a[2]) * sb[0], bf16_hi(a[2]) * sb[1]),
-                   pack_bf16x2(bf16_lo(a[3]) * sb[2], bf16_hi(a[3]) * sb[3])};
-    const uint16_t *b0 = &tile[buf][(8 * g + trow) * kGvmLd + 64 * wave + tcol];
+  auto compute = [&](int st, const u32x4 &a0, const u32x4 &a1) {
+    const float *sp = &ahs[st & 1][wave][16 * g];
+    const f32x4 s0 = *reinterpret_cast<const f32x4 *>(sp), s1 = *reinterpret_cast<const f32x4 *>(sp + 4);
+    const f32x4 s2 = *reinterpret_cast<const f32x4 *>(sp + 8), s3 = *reinterpret_cast<const f32x4 *>(sp + 12);
+    const u32x4 A0{pack_bf16x2(bf16_lo(a0[0]) * s0[0], bf16_hi(a0[0]) * s0[1]),
+                   pack_bf16x2(bf16_lo(a0[1]) * s0[2], bf16_hi(a0[1]) * s0[3]),
+                   pack_bf16x2(bf16_lo(a0[2]) * s1[0], bf16_hi(a0[2]) * s1[1]),
+                   pack_bf16x2(bf16_lo(a0[3]) * s1[2], bf16_hi(a0[3]) * s1[3])};
+    const u32x4 A1{pack_bf16x2(bf16_lo(a1[0]) * s2[0], bf16_hi(a1[0]) * s2[1]),
+                   pack_bf16x2(bf16_lo(a1[1]) * s2[2], bf16_hi(a1[1]) * s2[3]),
+                   pack_bf16x2(bf16_lo(a1[2]) * s3[0], bf16_hi(a1[2]) * s3[1]),
+                   pack_bf16x2(bf16_lo(a1[3]) * s3[2], bf16_hi(a1[3]) * s3[3])};
+    // lane i of group g names row 16 g + i; the block's bytes 32 w + 8 t .. + 7 are
+    // logical chunk 2 w + t / 2, half t % 2
+    const uint8_t *rowp = &cb[st % kGvmBufs][(16 * g + i16) * kGvmRowB];
 #pragma unroll
-    for (int t = 0; t < 4; ++t) acc[t] = mfma16(as, tr_pair(b0 + 16 * t, b0 + 4 * kGvmLd + 16 * t), acc[t]);
+    for (int t = 0; t < 4; ++t) {
+      const u32x2 v = tr4(rowp + 16 * ((2 * wave + (t >> 1)) ^ i16) + 8 * (t & 1));
+      u32x4 b0, b1;
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+        b0[d] = lut[((v[0] >> (8 * d)) & 0xFF) * kGvmLutCopies + lcopy];
+        b1[d] = lut[((v[1] >> (8 * d)) & 0xFF) * kGvmLutCopies + lcopy];
+      }
+      acc[t] = mfma16(A0, b0, acc[t]);
+      acc[t] = mfma16(A1, b1, acc[t]);
+    }
   };
-  auto step = [&](int st, GvmStage &Rcur, GvmStage &Rnext) {
-    // Rcur: stage st (tile in buffer st & 1, dY fragment needed now); Rnext: stage st + 1 (codes to decode)
-    const u32x4 a = Rcur.a;
+  auto step = [&](int st, GvmRegs &Rcur, GvmRegs &Rnext) {
+    // Rcur: stage st (dY fragments needed now), refilled with stage st + 2;
+    // Rnext: stage st + 1 (its a_hat is published here)
+    const u32x4 a0 = Rcur.a0, a1 = Rcur.a1;
     __builtin_amdgcn_sched_barrier(0);
-    load(st + 2, Rcur);
+    load_codes(st + kGvmBufs - 1);
+    __builtin_amdgcn_sched_barrier(0);  // the waits count loads in this order
+    load_regs(st + 2, Rcur);
     __builtin_amdgcn_sched_barrier(0);
-    compute(st & 1, a);
+    compute(st, a0, a1);
     put(Rnext, (st + 1) & 1);
+    wait_vm(std::integral_constant<int, kAfter>{});  // stage st + 1's codes in LDS
     __syncthreads();
   };
-  GvmStage R0, R1;
-  load(0, R0);
+  GvmRegs R0, R1;
+  load_codes(0);
   __builtin_amdgcn_sched_barrier(0);
-  load(1, R1);
+  load_regs(0, R0);
   __builtin_amdgcn_sched_barrier(0);
-  __syncthreads();  // decode table ready
+  if constexpr (kGvmBufs == 3) load_codes(1);
+  __builtin_amdgcn_sched_barrier(0);
+  load_regs(1, R1);
+  __builtin_amdgcn_sched_barrier(0);
   put(R0, 0);
-  __syncthreads();
+  wait_vm(std::integral_constant<int, kAfter>{});  // stage 0's codes in LDS
+  __syncthreads();                                 // and the table, and stage 0's a_hat
   int st = 0;
   for (; st + 1 < nst; st += 2) {
     step(st, R0, R1);
     step(st + 1, R1, R0);
   }
-  if (st < nst) compute(st & 1, R0.a);
+  if (st < nst) compute(st, R0.a0, R0.a1);
+  wait_vm(std::integral_constant<int, 0>{});  // no load outlives the workgroup
 
-  // D layout: lane (n = lane % 16, g) holds tokens 4g + v of column 64 wave + 16 t + n
+  // D layout: lane (n = lane % 16, g) holds tokens 4g + v of column 64 wave + 16 t + (n ^ 1)
   float *outp = p.part + (int64_t)blockIdx.y * p.M * h;
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
-    const int64_t col = c0 + 64 * wave + 16 * t + i16;
+    const int64_t col = c0 + 64 * wave + 16 * t + (i16 ^ 1);
     if (col >= h) continue;
 #pragma unroll
     for (int v = 0; v < 4; ++v) {

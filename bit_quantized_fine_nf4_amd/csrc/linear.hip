@@ -648,14 +648,14 @@ struct BwdLayout {
   size_t off_u, off_su, off_l1p, off_g, off_cnt, off_dxp, total;
 };
 
-int gemv_dx_chunks(int64_t M, int64_t h, int64_t o);
+int gemv_dx_chunks(int64_t h, int64_t o);
 
 BwdLayout bwd_layout(int64_t M, int64_t h, int64_t o, int r) {
   BwdLayout L{};
   size_t off = 0;
   auto take = [&](size_t bytes) { size_t at = off; off += rup((int64_t)bytes, 256); return at; };
   if (M <= 16) {
-    L.dxc = gemv_dx_chunks(M, h, o);
+    L.dxc = gemv_dx_chunks(h, o);
     L.off_dxp = take((size_t)L.dxc * M * h * 4);
   }
   L.total = off;
@@ -721,19 +721,9 @@ struct TimedLaunch {
 // Few-token backward: dX = dY·Ŵᵀ + s·U·L1ᵀ for M <= 16 ([MC] "One training
 // step": gradients flow through the frozen dequantized weight; [TT] §4).
 // HBM-bound like the forward GEMV, but the sum runs down the columns of the
-// stored [o][h] weight.  A workgroup takes 512 columns (64 lanes x 8) and a
-// chunk of rows; wave w takes the row pairs w, w + 4, ... of the chunk, so the
-// four waves read 256 contiguous code bytes from each of 8 rows per step and
-// the column-neighbour workgroups read the rest of those rows at the same
-// time.  Per pair (n, n+1) a lane decodes its 8 columns of both rows to
-// bf16(level * a_hat), packs the two rows' values of each column into a bf16
-// pair and accumulates dY[m][n..n+1] . pair with one v_dot2 per (token,
-// column).  This variant serves up to kDxMfmaMin tokens (more take the
-// matrix-core variant below).  Codes and scales are loaded four pairs ahead
-// into a ring of register sets; dY pairs are wave-uniform (scalar loads).  The four waves'
-// sums meet in LDS and each workgroup writes one float32 partial; the finish
-// kernel sums the row chunks in order (deterministic), adds s·U·L1ᵀ and rounds
-// to bf16.
+// stored [o][h] weight.  A workgroup takes 512 columns and a chunk of rows and
+// writes one float32 partial per (token, column); the finish kernel sums the row
+// chunks in order (deterministic), adds s·U·L1ᵀ and rounds to bf16.
 // ---------------------------------------------------------------------------
 struct GvdParams {
   const uint16_t *dY;  // [M][ldy] bf16
@@ -744,148 +734,31 @@ struct GvdParams {
   const float *scale2;
   const float *mean;
   int64_t h, o;  // W is [o][h]
-  int rows;      // rows per chunk (even)
+  int rows;      // rows per chunk (a multiple of kGvmRows)
   float *part;   // [chunks][M][h]
   float level[16];
 };
 
 constexpr int kGvdCols = 512;  // columns per workgroup
-// up to this many tokens the dot-product variant (4 tokens: 53 us on an 8192 x 28672
-// weight, against 65 us for the matrix-core variant, whose cost hardly depends on M)
-constexpr int kDxMfmaMin = 4;
-constexpr int kGvmRows = 64;  // rows (of o) per stage of the matrix-core variant
+constexpr int kGvmRows = 64;   // rows (of o) per stage
 
-int gemv_dx_chunks(int64_t M, int64_t h, int64_t o) {
-  // about 1024 workgroups (512 for more than 4 tokens, whose partial sums cost more),
-  // at least 64 rows per chunk; the matrix-core path takes whole stages
+int gemv_dx_chunks(int64_t h, int64_t o) {
+  // about 512 workgroups (two per compute unit), whole stages per chunk
   const int64_t ct = (h + kGvdCols - 1) / kGvdCols;
-  const int64_t target = M <= 4 ? 1024 : 512;
+  const int64_t target = 512;
   int64_t rc = (target + ct - 1) / ct;
-  // a chunk's codes stay under 2^30 bytes (32-bit buffer offsets in the matrix-core variant)
+  // a chunk's codes stay under 2^30 bytes (32-bit buffer offsets)
   const int64_t minc = (o * (h >> 1) + (int64_t(1) << 30) - 1) >> 30;
   rc = rc > minc ? rc : minc;
   const int64_t maxc = o / 64 > 0 ? o / 64 : 1;
   rc = rc < 1 ? 1 : (rc > maxc ? maxc : rc);
-  const int64_t rows = rup((o + rc - 1) / rc, M > kDxMfmaMin ? kGvmRows : 2);
+  const int64_t rows = rup((o + rc - 1) / rc, kGvmRows);
   return (int)((o + rows - 1) / rows);
 }
 
-template <int MT>
-struct GvdIn {
-  uint32_t c0, c1;  // 8 codes of rows n and n+1
-  int q0, q1;       // their int8 block scales
-  float s0, s1;     // second-level scales
-  uint32_t dy[MT];  // dY[m][n..n+1] (wave-uniform)
-};
-
-template <int MT>
-__global__ __launch_bounds__(256) void nf4_gemv_dx_kernel(GvdParams p) {
-  constexpr int RW = 8 * (MT < 4 ? MT : 4) + 1;  // floats per lane in the LDS reduction
-  __shared__ f32x2 lv2[256];
-  __shared__ float red[4][64][RW];
-  // wave index in a scalar register: row addresses (and so the dY loads) are wave-uniform
-  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  lv2[tid] = f32x2{p.level[tid >> 4], p.level[tid & 15]};
-  __syncthreads();
-  const int64_t h = p.h, nblk = h >> 6;
-  int64_t k0 = (int64_t)blockIdx.x * kGvdCols + 8 * lane;
-  const bool live = k0 < h;  // h is a multiple of 64, so a lane's 8 columns are all in or all out
-  k0 = live ? k0 : h - 8;    // out-of-range lanes read valid data and store nothing
-  const int64_t n0 = (int64_t)blockIdx.y * p.rows;
-  const int64_t n1 = n0 + p.rows < p.o ? n0 + p.rows : p.o;
-  const int npairs = (int)((n1 - n0) >> 1);
-  const int cnt = npairs > wave ? (npairs - wave + 3) >> 2 : 0;  // pairs of this wave
-  const float mu = *p.mean;
-  const int64_t kb = k0 >> 6;
-
-  auto load = [&](int j, GvdIn<MT> &in) {
-    const int jj = j < cnt ? j : (cnt > 0 ? cnt - 1 : 0);
-    int64_t n = n0 + 2 * (wave + 4 * (int64_t)jj);
-    n = n < n1 - 2 ? n : n1 - 2;  // a wave without pairs reads the chunk's last pair and uses nothing
-    in.c0 = *reinterpret_cast<const uint32_t *>(p.codes + ((n * h + k0) >> 1));
-    in.c1 = *reinterpret_cast<const uint32_t *>(p.codes + (((n + 1) * h + k0) >> 1));
-    const int64_t b0 = n * nblk + kb, b1 = b0 + nblk;
-    in.q0 = p.qabsmax[b0];
-    in.q1 = p.qabsmax[b1];
-    in.s0 = p.scale2[b0 / kChunk];
-    in.s1 = p.scale2[b1 / kChunk];
-#pragma unroll
-    for (int m = 0; m < MT; ++m) {
-      const int mm = m < p.M ? m : p.M - 1;  // rows past M are computed from a valid row and dropped
-      in.dy[m] = *reinterpret_cast<const uint32_t *>(p.dY + mm * p.ldy + n);
-    }
-  };
-
-  float acc[MT][8];
-#pragma unroll
-  for (int m = 0; m < MT; ++m)
-#pragma unroll
-    for (int j = 0; j < 8; ++j) acc[m][j] = 0.0f;
-
-  auto step = [&](int j, GvdIn<MT> &in) {
-    __builtin_amdgcn_sched_barrier(0);
-    const float a0 = scale_hat((int8_t)in.q0, in.s0, mu), a1 = scale_hat((int8_t)in.q1, in.s1, mu);
-    uint32_t wp[8];
-#pragma unroll
-    for (int b = 0; b < 4; ++b) {
-      const f32x2 l0 = lv2[(in.c0 >> (8 * b)) & 0xFF];
-      const f32x2 l1 = lv2[(in.c1 >> (8 * b)) & 0xFF];
-      wp[2 * b] = pack_bf16x2(l0[0] * a0, l1[0] * a1);
-      wp[2 * b + 1] = pack_bf16x2(l0[1] * a0, l1[1] * a1);
-    }
-#pragma unroll
-    for (int m = 0; m < MT; ++m) {
-#pragma unroll
-      for (int c = 0; c < 8; ++c)
-        acc[m][c] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, in.dy[m]),
-                                                   __builtin_bit_cast(bf16x2, wp[c]), acc[m][c], false);
-    }
-    load(j + (MT <= 4 ? 4 : 2), in);
-    __builtin_amdgcn_sched_barrier(0);
-  };
-
-  // D register sets in a ring, each reloaded D pairs ahead right after its use
-  constexpr int D = MT <= 4 ? 4 : 2;
-  GvdIn<MT> in[D];
-#pragma unroll
-  for (int d = 0; d < D; ++d) load(d, in[d]);
-  int j = 0;
-  for (; j + D - 1 < cnt; j += D) {
-#pragma unroll
-    for (int d = 0; d < D; ++d) step(j + d, in[d]);
-  }
-#pragma unroll
-  for (int d = 0; d < D - 1; ++d)
-    if (j + d < cnt) step(j + d, in[d]);
-
-  // the four waves' sums, four tokens at a time, through LDS
-  float *outp = p.part + ((int64_t)blockIdx.y * p.M) * h;
-#pragma unroll
-  for (int mg = 0; mg < MT; mg += 4) {
-#pragma unroll
-    for (int mi = 0; mi < 4; ++mi)
-      if (mg + mi < MT)
-#pragma unroll
-        for (int c = 0; c < 8; ++c) red[wave][lane][8 * mi + c] = acc[mg + mi][c];
-    __syncthreads();
-    const int m = mg + wave;  // thread (wave, lane) sums token mg + wave of lane's 8 columns
-    if (m < MT && m < p.M && live) {
-      float v[8];
-#pragma unroll
-      for (int c = 0; c < 8; ++c)
-        v[c] = red[0][lane][8 * wave + c] + red[1][lane][8 * wave + c] + red[2][lane][8 * wave + c] +
-               red[3][lane][8 * wave + c];
-      float *o = outp + (int64_t)m * h + k0;
-      *reinterpret_cast<f32x4 *>(o) = f32x4{v[0], v[1], v[2], v[3]};
-      *reinterpret_cast<f32x4 *>(o + 4) = f32x4{v[4], v[5], v[6], v[7]};
-    }
-    __syncthreads();
-  }
-}
-
-// Few-token backward on the matrix cores (more than kDxMfmaMin tokens): the same
-// row chunks and partial sums as nf4_gemv_dx_kernel, computed with 16x16x32 bf16
-// MFMAs that take the tokens as their rows.  A workgroup of 8 waves takes 512
+// The few-token dX kernel runs on the matrix cores: 16x16x32 bf16 MFMAs take the
+// tokens as their rows (padded to 16; on an 8192 x 28672 weight 1, 4 and 16
+// tokens take 35, 38 and 44 us, where a v_dot2 kernel took 42, 55 and 114).  A workgroup of 8 waves takes 512
 // columns, wave w the 64-column block w; a stage is 64 rows of o.
 //   - The stage's raw codes (64 rows x 256 bytes) go to LDS by direct-to-LDS
 //     loads, kGvmBufs - 1 stages ahead, in 16-byte chunks placed at
@@ -924,7 +797,7 @@ struct GvmRegs {
   float s2;      // its second-level scale
 };
 
-__global__ __launch_bounds__(kGvmThreads) void nf4_gemv_dx_mfma_kernel(GvdParams p) {
+__global__ __launch_bounds__(kGvmThreads) void nf4_gemv_dx_kernel(GvdParams p) {
   __shared__ __attribute__((aligned(16))) uint8_t cb[kGvmBufs][kGvmRows * kGvmRowB];
   // lut[kGvmLutCopies * byte + copy] = bf16 pair (level[low nibble], level[high nibble])
   __shared__ uint32_t lut[256 * kGvmLutCopies];
@@ -1213,16 +1086,14 @@ hipError_t launch_linear_bwd(const LinearArgs &a, const uint16_t *X, const uint1
     vp.codes = a.codes; vp.qabsmax = a.qabsmax; vp.scale2 = a.scale2; vp.mean = a.mean;
     vp.h = a.h; vp.o = a.o;
     // rows per chunk (at most L.dxc chunks; trailing ones may be empty and then store zeros)
-    vp.rows = (int)rup((a.o + L.dxc - 1) / L.dxc, a.M > kDxMfmaMin ? kGvmRows : 2);
+    vp.rows = (int)rup((a.o + L.dxc - 1) / L.dxc, kGvmRows);
     vp.part = at<float>(ws, L.off_dxp);
     fill_levels(vp.level, tab);
     const dim3 grid((unsigned)((a.h + kGvdCols - 1) / kGvdCols), (unsigned)L.dxc);
     auto launch_dx = [&]() {
       {
         TimedLaunch tl(1, st);
-        if (a.M == 1) nf4_gemv_dx_kernel<1><<<grid, 256, 0, st>>>(vp);
-        else if (a.M <= kDxMfmaMin) nf4_gemv_dx_kernel<kDxMfmaMin><<<grid, 256, 0, st>>>(vp);
-        else nf4_gemv_dx_mfma_kernel<<<grid, kGvmThreads, 0, st>>>(vp);
+        nf4_gemv_dx_kernel<<<grid, kGvmThreads, 0, st>>>(vp);
       }
       const int64_t cg = (a.h / 8 + 63) / 64;
       gemv_dx_finish_kernel<<<(unsigned)(a.M * cg), 256, 0, st>>>(vp.part, L.dxc, (int)a.M, a.h, sU, L.RP64, L1,

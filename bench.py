@@ -13,8 +13,9 @@ by the whole step's time (the codec stages are inside the step).  The `roofline`
 object reports the dominant kernel (the slower of the two fused dequant-GEMMs)
 timed in the timed steps with events the library records right around that
 kernel's launch.  Per-stage times come from a second pass of the same steps with
-HIP events between the stages, kept out of the timed steps because each event
-recorded between two kernels holds the stream for a few microseconds.
+HIP events between the stages, kept out of the timed steps: even without the
+system-scope fence (all events here are created with hipEventDisableSystemFence)
+an event between two kernels keeps them from overlapping.
 `cpu_baseline` times the CPU oracle on the same workload.
 
 Other workloads (not the default line): --workload codec (quantize + double
@@ -88,14 +89,20 @@ class HipEvents:
                 path = line.split()[-1]
                 break
         self.hip = ctypes.CDLL(path or os.path.join(os.path.dirname(torch.__file__), "lib", "libamdhip64.so"))
-        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
         self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
         self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
         self.live = []
+
+    # hipEventDisableSystemFence: the events only time kernels (read after a full
+    # synchronize), so recording them skips the system-scope cache writeback and
+    # invalidation that otherwise holds the stream for about 5-6 us per event
+    DISABLE_SYSTEM_FENCE = 0x20000000
 
     def create(self):
         ev = self.ct.c_void_p()
-        rc = self.hip.hipEventCreate(self.ct.byref(ev))
+        rc = self.hip.hipEventCreateWithFlags(self.ct.byref(ev), self.DISABLE_SYSTEM_FENCE)
         if rc != 0:
             raise RuntimeError(f"hipEventCreate failed ({rc})")
         self.live.append(ev)
@@ -108,10 +115,32 @@ class HipEvents:
             raise RuntimeError(f"hipEventElapsedTime failed ({rc})")
         return ms.value
 
+    def record(self, ev, torch):
+        """Record ev on torch's current stream."""
+        rc = self.hip.hipEventRecord(ev, self.ct.c_void_p(torch.cuda.current_stream().cuda_stream))
+        if rc != 0:
+            raise RuntimeError(f"hipEventRecord failed ({rc})")
+
+    def event(self, enable_timing=True):
+        """A stand-in for torch.cuda.Event(enable_timing=True) built on these events."""
+        return _Event(self)
+
     def close(self):
         for ev in self.live:
             self.hip.hipEventDestroy(ev)
         self.live = []
+
+
+class _Event:
+    def __init__(self, hev):
+        import torch
+        self.hev, self.torch, self.ev = hev, torch, hev.create()
+
+    def record(self):
+        self.hev.record(self.ev, self.torch)
+
+    def elapsed_time(self, other) -> float:
+        return self.hev.elapsed_ms(self.ev, other.ev)
 
 
 def read_traffic(kernel: str):
@@ -198,7 +227,7 @@ def bench_attn_proj(args, torch, nf4, wl):
     bws = torch.empty(nf4.workspace_size(nf4.QLORA_OP_LINEAR_BWD, M, h, o, r), dtype=torch.uint8, device=dev)
     W = nf4.NF4Weight(codes, qa, s2, mean, h, o)
     stages = ["quantize", "double_quant", "dequantize", "fwd", "bwd"]
-    E = torch.cuda.Event
+    E = HipEvents(torch).event  # fence-free timing events
 
     def step(ev=None, kev=None):
         if kev is not None:
@@ -233,7 +262,7 @@ def bench_attn_proj(args, torch, nf4, wl):
     nf4.qlora_set_timing_events(nf4.TIMED_GEMM_FWD, None, None)
     nf4.qlora_set_timing_events(nf4.TIMED_GEMM_DX, None, None)
     # Stage breakdown from a second pass: an event recorded between two kernels
-    # holds the stream for a few microseconds, so it stays out of the timed steps.
+    # keeps them from overlapping, so it stays out of the timed steps.
     evs = [[E(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     for i in range(args.steps):
@@ -291,7 +320,7 @@ def bench_codec(args, torch, nf4, wl):
     mean = torch.empty(1, dtype=torch.float32, device=dev)
     ws = torch.empty(nf4.workspace_size(nf4.QLORA_OP_DOUBLE_QUANT, nb), dtype=torch.uint8, device=dev)
     out = torch.empty(n, dtype=torch.bfloat16, device=dev)
-    E = torch.cuda.Event
+    E = HipEvents(torch).event  # fence-free timing events
 
     def step(ev=None):
         rec = (lambda i: ev[i].record()) if ev is not None else (lambda i: None)
@@ -364,7 +393,7 @@ def bench_gemv(args, torch, nf4, wl):
     # few-token backward dX = dY·W_hat^T (no adapter): the dX GEMV kernel timed by the library's
     # hook, and the whole call (GEMV + the partial-sum finish) by events on the stream
     bwd = {}
-    E = torch.cuda.Event
+    E = HipEvents(torch).event  # fence-free timing events
     for m in wl.C4_GEMV_TOKENS:
         dY = wl.activations(c, 0, tokens=m, tensor=wl.TENSOR_DY).to(dev)
         dX = torch.empty(m, h, dtype=torch.bfloat16, device=dev)
@@ -446,7 +475,7 @@ def bench_merge(args, torch, nf4, wl):
         n = ls.h * ls.o
         reqs.append((torch.empty(n // 2, dtype=torch.uint8, device=dev),
                      torch.empty(n // 64, dtype=torch.float32, device=dev)))
-    E = torch.cuda.Event
+    E = HipEvents(torch).event  # fence-free timing events
     nl = len(c.linears)
 
     def step(ev=None):
@@ -499,7 +528,7 @@ def bench_adamw(args, torch, nf4, wl):
     mh = torch.zeros(n, pin_memory=True)
     vh = torch.zeros(n, pin_memory=True)
     hp = dict(lr=2e-4, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.01)
-    E = torch.cuda.Event
+    E = HipEvents(torch).event  # fence-free timing events
     bytes_step = n * (4 * 4 + 3 * 4 + 2)  # read p, g, m, v; write p, m, v and the bf16 copy
     res = {}
     for name in ("hbm", "host_state"):
@@ -555,7 +584,7 @@ def bench_codebooks(args, torch, nf4, wl):
         del w64
     w = data["normal"].to(torch.bfloat16)
     out = torch.empty(n, dtype=torch.bfloat16, device=dev)
-    E = torch.cuda.Event
+    E = HipEvents(torch).event  # fence-free timing events
     rates = {}
     qb, dqb, deqb = codec_bytes(n, 2, 2)
     for cname, c in nf4.CODEBOOKS.items():

@@ -254,11 +254,14 @@ qlora_status_t qlora_workspace_size(qlora_op_t op, int64_t a, int64_t b, int64_t
 
 /*
  * Timing hook for benchmarks and profilers.  `kernel` 0 = the forward fused
- * dequant-GEMM, 1 = the dX fused dequant-GEMM, 2 = the few-token forward
+ * dequant-GEMM, 1 = the dX kernel of qlora_linear_bwd (the fused dequant-GEMM,
+ * or for M <= 16 the few-token dX kernel), 2 = the few-token forward
  * (M <= 16).  When `start`/`stop` (hipEvent_t handles) are non-NULL, every
  * later launch of that kernel by the calling thread records `start` just
  * before and `stop` just after itself on the call's stream.  NULL/NULL turns
  * the hook off.  Per thread; the library only records, never synchronizes.
+ * Events created with hipEventDisableSystemFence disturb the timed stream
+ * least (a default event's system-scope fence stalls it for microseconds).
  */
 qlora_status_t qlora_set_timing_events(int32_t kernel, void *start, void *stop);
 

@@ -12,10 +12,11 @@ dequantize it to bf16, run the forward Y = X·W_hat + s·X·L1·L2 and the backw
 by the whole step's time (the codec stages are inside the step).  The `roofline`
 object reports the dominant kernel (the slower of the two fused dequant-GEMMs)
 timed in the timed steps with events the library records right around that
-kernel's launch.  Per-stage times come from a second pass of the same steps with
-HIP events between the stages, kept out of the timed steps: even without the
-system-scope fence (all events here are created with hipEventDisableSystemFence)
-an event between two kernels keeps them from overlapping.
+kernel's launch (the forward GEMM in even steps, the dX GEMM in odd ones).  Every
+event recorded between two kernels holds the stream about 4.5 us, also without
+the system-scope fence (all events here are created with
+hipEventDisableSystemFence), so per-stage times come from a second pass of the
+same steps with HIP events between the stages.
 `cpu_baseline` times the CPU oracle on the same workload.
 
 Other workloads (not the default line): --workload codec (quantize + double
@@ -97,7 +98,8 @@ class HipEvents:
 
     # hipEventDisableSystemFence: the events only time kernels (read after a full
     # synchronize), so recording them skips the system-scope cache writeback and
-    # invalidation that otherwise holds the stream for about 5-6 us per event
+    # invalidation (a kernel trace shows the stream held 4.5 us per event with it
+    # against 5.7 us without)
     DISABLE_SYSTEM_FENCE = 0x20000000
 
     def create(self):
@@ -229,10 +231,10 @@ def bench_attn_proj(args, torch, nf4, wl):
     stages = ["quantize", "double_quant", "dequantize", "fwd", "bwd"]
     E = HipEvents(torch).event  # fence-free timing events
 
-    def step(ev=None, kev=None):
+    def step(ev=None, kev=None, which=(True, True)):
         if kev is not None:
-            nf4.qlora_set_timing_events(nf4.TIMED_GEMM_FWD, kev[0], kev[1])
-            nf4.qlora_set_timing_events(nf4.TIMED_GEMM_DX, kev[2], kev[3])
+            nf4.qlora_set_timing_events(nf4.TIMED_GEMM_FWD, *(kev[0:2] if which[0] else (None, None)))
+            nf4.qlora_set_timing_events(nf4.TIMED_GEMM_DX, *(kev[2:4] if which[1] else (None, None)))
         rec = (lambda i: ev[i].record()) if ev is not None else (lambda i: None)
         rec(0)
         nf4.qlora_quantize(w, codes, absmax)
@@ -252,17 +254,20 @@ def bench_attn_proj(args, torch, nf4, wl):
     hev = HipEvents(torch)
     kevs = [[hev.create() for _ in range(4)] for _ in range(args.steps)]
     torch.cuda.synchronize()
-    # Timed region: K steps; the only events in it are the pair the library records
-    # around each fused GEMM launch (the dominant kernel's duration).
+    # Timed region: K steps; the only events in it are the pairs the library records
+    # around a fused GEMM launch: the forward GEMM in even steps, the dX GEMM in odd
+    # ones (every event pair holds the stream a few microseconds; with one step,
+    # both).
+    timed = [(i % 2 == 0, i % 2 == 1) if args.steps > 1 else (True, True) for i in range(args.steps)]
     t0 = time.perf_counter()
     for i in range(args.steps):
-        step(None, kevs[i])
+        step(None, kevs[i], timed[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     nf4.qlora_set_timing_events(nf4.TIMED_GEMM_FWD, None, None)
     nf4.qlora_set_timing_events(nf4.TIMED_GEMM_DX, None, None)
     # Stage breakdown from a second pass: an event recorded between two kernels
-    # keeps them from overlapping, so it stays out of the timed steps.
+    # holds the stream a few microseconds, so it stays out of the timed steps.
     evs = [[E(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     for i in range(args.steps):
@@ -271,8 +276,8 @@ def bench_attn_proj(args, torch, nf4, wl):
 
     ms_per_step = wall * 1e3 / args.steps
     st_ms = {k: statistics.mean(e[i].elapsed_time(e[i + 1]) for e in evs) for i, k in enumerate(stages)}
-    gemm_fwd_ms = statistics.mean(hev.elapsed_ms(k[0], k[1]) for k in kevs)
-    gemm_dx_ms = statistics.mean(hev.elapsed_ms(k[2], k[3]) for k in kevs)
+    gemm_fwd_ms = statistics.mean(hev.elapsed_ms(k[0], k[1]) for k, w in zip(kevs, timed) if w[0])
+    gemm_dx_ms = statistics.mean(hev.elapsed_ms(k[2], k[3]) for k, w in zip(kevs, timed) if w[1])
     hev.close()
     fwd_f, bwd_f = linear_flops(M, h, o, r)
     qb, dqb, deqb = codec_bytes(n, 4, 2)

@@ -17,6 +17,12 @@
 //   nf4_gemv_kernel      M <= 16 forward: streams the codes once, decodes a
 //                        byte (two codes) per LDS lookup, applies the block
 //                        scale after each 64-wide MFMA pair
+//   nf4_gemv_dx_kernel   M <= 16 dX: streams the codes once in 64-row stages
+//                        through LDS; 4-bit transposing reads give each lane
+//                        a column's codes, a byte table yields the bf16 MFMA
+//                        operand, the block scale rides on dY; one float32
+//                        partial per row chunk
+//   gemv_dx_finish_kernel  sums the row-chunk partials in order, adds s·U·L1^T
 //   lora_grad_kernel     dL1 = s·X^T·U and dL2 = s·T^T·dY in one launch:
 //                        reduction over tokens, LDS-transposed operands,
 //                        split over tokens; the last split of a tile sums,
@@ -758,8 +764,9 @@ int gemv_dx_chunks(int64_t h, int64_t o) {
 
 // The few-token dX kernel runs on the matrix cores: 16x16x32 bf16 MFMAs take the
 // tokens as their rows (padded to 16; on an 8192 x 28672 weight 1, 4 and 16
-// tokens take 35, 38 and 44 us, where a v_dot2 kernel took 42, 55 and 114).  A workgroup of 8 waves takes 512
-// columns, wave w the 64-column block w; a stage is 64 rows of o.
+// tokens take 35, 38 and 44 us, where a v_dot2 kernel took 42, 55 and 114).  A
+// workgroup of 8 waves takes 512 columns, wave w the 64-column block w; a stage
+// is 64 rows of o.
 //   - The stage's raw codes (64 rows x 256 bytes) go to LDS by direct-to-LDS
 //     loads, kGvmBufs - 1 stages ahead, in 16-byte chunks placed at
 //     chunk ^ (row % 16) within their row.

@@ -34,7 +34,9 @@
 // Decoding: a 256-entry table at LDS offset 0 maps a code byte to the pair
 //  (level[high nibble], level[low nibble]); one shifted byte gives the table
 //  address, one 8-byte LDS read gives both levels, two multiplies by a_hat and
-//  one packed convert give the two bf16 weights.
+//  one packed convert give the two bf16 weights.  The 256x128 tiles keep 16
+//  interleaved copies of the table (lane l reads copy l % 16) against bank
+//  conflicts.
 // Loads: raw buffer loads with per-tile descriptors — rows past the end of a
 //  matrix read as zero, so the K loop has no branches and no 64-bit address
 //  arithmetic.
@@ -104,7 +106,12 @@ __global__ __launch_bounds__(512) void nf4_gemm_kernel(GemmParams p) {
   constexpr int UW = 64 * BN / NT;  // weights per decode unit: every thread decodes one unit
   constexpr int UB = UW / 2;        // code bytes per unit (8 or 16)
   constexpr int A_CH = BM * 8 / NT;  // 16-byte A chunks per thread per K step
-  constexpr int LUT_BYTES = 256 * 8;
+  // Interleaved copies of the decode table: lane l reads copy l % LUT_COPIES,
+  // which cuts the bank conflicts of the random code-byte reads.  The 256x128
+  // tiles have the LDS for 16 copies (C2 dX GEMM 97.7 -> 93.8 us; a conflict-free
+  // timing knob reaches 92.8); 4 copies on the 256x256 tiles did not pay.
+  constexpr int LUT_COPIES = BM == 256 && BN == 128 ? 16 : 1;
+  constexpr int LUT_BYTES = 256 * 8 * LUT_COPIES;
   constexpr int LDC = BN + 8;
   constexpr int LDS_BYTES = cmax(LUT_BYTES + 2 * STAGE * 2, BM * LDC * 2);
   static_assert(UW == 16 || UW == 32, "decode unit of 16 or 32 weights");
@@ -122,7 +129,10 @@ __global__ __launch_bounds__(512) void nf4_gemm_kernel(GemmParams p) {
   auto a_off = [](int r, int chunk) {
     return kDma ? r * LDA + ((chunk ^ ((r >> 1) & 7)) << 3) : r * LDA + chunk * 8;
   };
-  if (tid < 256) reinterpret_cast<f32x2 *>(lds)[tid] = f32x2{p.level[tid >> 4], p.level[tid & 15]};
+  for (int i = tid; i < 256 * LUT_COPIES; i += NT) {
+    const int e = i / LUT_COPIES;
+    reinterpret_cast<f32x2 *>(lds)[i] = f32x2{p.level[e >> 4], p.level[e & 15]};
+  }
 
   int bid = blockIdx.x;
   const int ntiles = p.tiles_m * p.tiles_n;
@@ -236,11 +246,13 @@ __global__ __launch_bounds__(512) void nf4_gemm_kernel(GemmParams p) {
   // rather than once per part; with 16 (256-wide tiles) the extra 16 registers
   // would spill, and each part reads its own.
   constexpr bool kEarly = UB == 8;
+  const int lcopy = lane % LUT_COPIES;
+  auto lut_index = [&](uint32_t w) { return (int)(w & 0xFF) * LUT_COPIES + lcopy; };
   f32x2 LV[kEarly ? UB : 1];
   auto read_levels = [&](const Stage &S) {
     if constexpr (kEarly) {
 #pragma unroll
-      for (int byte = 0; byte < UB; ++byte) LV[byte] = lut[(S.c[byte >> 2] >> (8 * (byte & 3))) & 0xFF];
+      for (int byte = 0; byte < UB; ++byte) LV[byte] = lut[lut_index(S.c[byte >> 2] >> (8 * (byte & 3)))];
     }
   };
   uint32_t oprev[2] = {0u, 0u};  // an even part's decoded words, stored with the next part's
@@ -266,7 +278,7 @@ __global__ __launch_bounds__(512) void nf4_gemm_kernel(GemmParams p) {
       const int byte = part * BPP + b;
       f32x2 l;
       if constexpr (kEarly) l = LV[byte];
-      else l = lut[(S.c[byte >> 2] >> (8 * (byte & 3))) & 0xFF];
+      else l = lut[lut_index(S.c[byte >> 2] >> (8 * (byte & 3)))];
       o[b] = pack_bf16x2(l[0] * ah, l[1] * ah);
     }
     uint16_t *dst = bdst0 + buf * STAGE + part * 2 * BPP;

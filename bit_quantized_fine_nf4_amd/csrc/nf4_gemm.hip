@@ -97,12 +97,12 @@ __global__ __launch_bounds__(512) void nf4_gemm_kernel(GemmParams p) {
   constexpr bool kDma = !(TRANS && BN == 256);
   constexpr int LDA = kDma ? BK : BK + 8;  // A [m][k]: swizzled chunks (kDma) or a padded row
   constexpr int LDNK = BK + 8;   // B [n][k]
-  // B [k][n] row stride.  128 wide: 16 banks (mod 64), so the 32 lanes of a
-  // transposing fragment read (4 rows x 2 groups of 4 eight-byte chunks) cover
-  // the 64 banks once; the decode stores (2 rows x 8 units per 16 lanes) then
-  // pair up 2-way, but they are 8x rarer (C2 dX GEMM 93.8 -> 90.6 us against a
-  // 12-bank stride).  256 wide: 12 banks.
-  constexpr int LDKN = BN == 128 ? BN + 32 : BN + 24;
+  // B [k][n] row stride: 16 banks (mod 64), so the 32 lanes of a transposing
+  // fragment read (4 rows x 2 groups of 4 eight-byte chunks) cover the 64 banks
+  // once.  The decode stores (2 rows of 16-byte units per 16 lanes) then pair
+  // up, but they are 8x rarer.  Against a 12-bank stride: C2 dX GEMM 93.8 ->
+  // 90.6 us, C3's 256-wide dX GEMM 438 -> 422 us.
+  constexpr int LDKN = BN + 32;
   constexpr int B_ELEMS = cmax(BN * LDNK, BK * LDKN);
   constexpr int STAGE = BM * LDA + B_ELEMS;  // elements per LDS stage (A then B)
   constexpr int UW = 64 * BN / NT;  // weights per decode unit: every thread decodes one unit

@@ -178,3 +178,86 @@ FEW_TOKEN_BWD = [  # (M, h, o, r, s): the few-token backward (dX GEMV), several 
 def test_few_token_backward(M, h, o, r, s):
     w, l1, l2, x, dy = wl.small_linear(h, o, r, M, seed=3 * M + h + r)
     check_full(w, l1, l2, x, dy, s, f"few-token M={M} h={h} o={o} r={r}")
+
+
+class _HipEvents:
+    """Raw hipEvent_t handles (the library records them; torch would refuse to time
+    events it did not record itself)."""
+
+    def __init__(self):
+        import ctypes
+        import os
+        path = None
+        for line in open("/proc/self/maps"):
+            if "libamdhip64" in line:
+                path = line.split()[-1]
+                break
+        self.ct = ctypes
+        self.hip = ctypes.CDLL(path or os.path.join(os.path.dirname(torch.__file__), "lib", "libamdhip64.so"))
+        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.live = []
+
+    def create(self):
+        ev = self.ct.c_void_p()
+        assert self.hip.hipEventCreate(self.ct.byref(ev)) == 0
+        self.live.append(ev)
+        return ev
+
+    def elapsed(self, a, b):
+        """(status, ms): status is non-zero when either event was never recorded (the
+        runtime's last-error state is cleared then, so no later launch check sees it)."""
+        ms = self.ct.c_float()
+        rc = self.hip.hipEventElapsedTime(self.ct.byref(ms), a, b)
+        if rc != 0:
+            self.hip.hipGetLastError()
+        return rc, ms.value
+
+    def close(self):
+        for ev in self.live:
+            self.hip.hipEventDestroy(ev)
+
+
+@pytest.mark.parametrize("M,expect", [(512, (0, 1)), (4, (1, 2))])
+def test_timing_hook_slots(M, expect):
+    """qlora_set_timing_events: slot 0 brackets the forward fused GEMM, slot 1 the
+    dX kernel (the fused GEMM, or for M <= 16 the few-token dX kernel), slot 2 the
+    few-token forward.  A slot whose kernel does not run leaves its events
+    unrecorded, and NULL/NULL switches the hook off."""
+    h, o, r, s = 512, 768, 8, 2.0
+    print(f"timing hook M={M}", flush=True)
+    g = torch.Generator().manual_seed(11)
+    w = torch.randn(o, h, generator=g) * 0.02
+    l1, l2 = torch.randn(h, r, generator=g) * 0.01, torch.randn(r, o, generator=g) * 0.01
+    x = torch.randn(M, h, generator=g).to(torch.bfloat16)
+    dy = torch.randn(M, o, generator=g).to(torch.bfloat16)
+    W = nf4.quantize_weight(w.to(DEV))
+    X, dY, L1, L2 = x.to(DEV), dy.to(DEV), l1.to(DEV).to(torch.bfloat16), l2.to(DEV).to(torch.bfloat16)
+    hev = _HipEvents()
+    slots = [nf4.TIMED_GEMM_FWD, nf4.TIMED_GEMM_DX, nf4.TIMED_GEMV]
+    evs = {k: (hev.create(), hev.create()) for k in slots}
+    try:
+        for k in slots:
+            nf4.qlora_set_timing_events(k, *evs[k])
+        Y, T = nf4.qlora_linear_fwd(W, X, L1, L2, s)
+        nf4.qlora_linear_bwd(W, X, T, dY, L1, L2, s)
+        torch.cuda.synchronize()
+    finally:
+        for k in slots:
+            nf4.qlora_set_timing_events(k, None, None)
+    first = {}
+    for k in slots:
+        rc, ms = hev.elapsed(*evs[k])
+        if k in expect:
+            assert rc == 0 and 0.0 < ms < 1000.0, (k, rc, ms)
+            first[k] = ms
+        else:
+            assert rc != 0, f"slot {k} recorded although its kernel did not run"
+    # switched off: another pass records nothing, so the timed pairs keep their values
+    Y, T = nf4.qlora_linear_fwd(W, X, L1, L2, s)
+    nf4.qlora_linear_bwd(W, X, T, dY, L1, L2, s)
+    torch.cuda.synchronize()
+    for k in expect:
+        assert hev.elapsed(*evs[k]) == (0, first[k])
+    hev.close()

@@ -93,29 +93,51 @@ def test_linear_workload_c2():
     check_full(w, l1, l2, wl.activations(c, 0), wl.activations(c, 0, tensor=wl.TENSOR_DY), ls.s, c.name)
 
 
-def check_sampled(c, li, nrows=48):
-    """Full-size linear of a workload: Y and dX on sampled token rows, T/dL1/dL2 in full."""
-    ls = c.linears[li]
-    print(f"linear {c.name}/{ls.name} sampled", flush=True)
-    w = wl.base_weight(c, li)
-    l1, l2 = wl.lora_factors(c, li)
-    x = wl.activations(c, li)
-    dy = wl.activations(c, li, tensor=wl.TENSOR_DY)
-    Y, T, dX, dL1, dL2 = gpu_run(w, l1, l2, x, dy, ls.s)
+def check_sampled_tensors(w, l1, l2, x, dy, s, label, seed, nrows=48):
+    """Y and dX on sampled token rows (the first and last included), T/dL1/dL2 in full."""
+    print(f"linear {label} sampled", flush=True)
+    tokens = x.shape[0]
+    Y, T, dX, dL1, dL2 = gpu_run(w, l1, l2, x, dy, s)
     wh = oracle_weight(w)
-    del w
-    rows = np.unique(np.concatenate([np.random.default_rng(li).integers(0, c.tokens, nrows), [0, c.tokens - 1]]))
+    rows = np.unique(np.concatenate([np.random.default_rng(seed).integers(0, tokens, nrows), [0, tokens - 1]]))
     X, DY = to_np(x).astype(np.float64), to_np(dy).astype(np.float64)
     L1, L2 = to_np(l1), to_np(l2)
-    rY, rT = oracle.linear_fwd(wh, X[rows], L1, L2, ls.s)
-    rdX, _, _ = oracle.linear_bwd(wh, X[rows], DY[rows], L1, L2, ls.s)
+    rY, rT = oracle.linear_fwd(wh, X[rows], L1, L2, s)
+    rdX, _, _ = oracle.linear_bwd(wh, X[rows], DY[rows], L1, L2, s)
     assert_close("Y[rows]", to_np(Y)[rows], rY)
     assert_close("dX[rows]", to_np(dX)[rows], rdX)
     T64 = X @ L1.astype(np.float64)
     U64 = DY @ L2.astype(np.float64).T
     assert_close("T", to_np(T), T64)
-    assert_close("dL1", to_np(dL1), ls.s * (X.T @ U64))
-    assert_close("dL2", to_np(dL2), ls.s * (T64.T @ DY))
+    assert_close("dL1", to_np(dL1), s * (X.T @ U64))
+    assert_close("dL2", to_np(dL2), s * (T64.T @ DY))
+
+
+def check_sampled(c, li, nrows=48):
+    """Full-size linear of a workload: Y and dX on sampled token rows, T/dL1/dL2 in full."""
+    ls = c.linears[li]
+    w = wl.base_weight(c, li)
+    l1, l2 = wl.lora_factors(c, li)
+    x = wl.activations(c, li)
+    dy = wl.activations(c, li, tensor=wl.TENSOR_DY)
+    check_sampled_tensors(w, l1, l2, x, dy, ls.s, f"{c.name}/{ls.name}", li, nrows)
+
+
+def test_linear_256x128_tiles_ragged():
+    """M = 2000, h = o = 2624 selects the 256x128 fused-GEMM tiles in both
+    directions, with partial last tiles along M (208 rows) and N (64 columns);
+    compared in full."""
+    M, h, o, r, s = 2000, 2624, 2624, 16, 2.0
+    w, l1, l2, x, dy = wl.small_linear(h, o, r, M, seed=2000)
+    check_full(w, l1, l2, x, dy, s, f"M={M} h={h} o={o} r={r} (256x128 tiles)")
+
+
+def test_linear_256x256_tiles_ragged():
+    """M = 3000, h = o = 5184 selects the 256x256 fused-GEMM tiles in both
+    directions, with partial last tiles along M (184 rows) and N (64 columns)."""
+    M, h, o, r, s = 3000, 5184, 5184, 16, 0.5
+    w, l1, l2, x, dy = wl.small_linear(h, o, r, M, seed=3000)
+    check_sampled_tensors(w, l1, l2, x, dy, s, f"M={M} h={h} o={o} r={r} (256x256 tiles)", 3)
 
 
 @pytest.mark.parametrize("li", [0, 2])

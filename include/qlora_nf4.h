@@ -12,10 +12,8 @@
  *    device memory the caller passes a workspace sized by qlora_workspace_size().
  *  - `stream` is a hipStream_t (NULL = the default stream).  Every call only
  *    enqueues work and returns without synchronizing; all of a call's work is
- *    ordered on `stream` (qlora_linear_bwd forks part of its work to a
- *    library-owned stream of the same device and joins it back to `stream`
- *    with events before returning).  Calls on different streams are safe when
- *    their buffers are disjoint.
+ *    ordered on `stream`.  Calls on different streams are safe when their
+ *    buffers (workspaces included) are disjoint.
  *  - bf16 tensors are passed as uint16_t bit patterns (bfloat16: 1 sign, 8
  *    exponent, 7 fraction bits).  All matrices are row-major.
  *  - Pointers must be 16-byte aligned unless stated otherwise.
@@ -23,8 +21,9 @@
  *    QLORA_ERR_INVALID_VALUE nothing is launched and no output is touched.
  *    A failed kernel launch returns QLORA_ERR_LAUNCH.  No exception crosses
  *    the ABI.  Non-finite inputs give unspecified (but memory-safe) results.
- *  - Thread safety: the library holds no mutable state after its one-time
- *    initialisation of the NF4 tables (done under a lock on first use).
+ *  - Thread safety: the library holds no shared mutable state after its
+ *    one-time initialisation of the NF4 tables (done under a lock on first
+ *    use); the timing hook's events are per thread.
  */
 #ifndef QLORA_NF4_H_
 #define QLORA_NF4_H_

@@ -1,10 +1,12 @@
 """Pins for the oracle's blockwise NF4 quantization, double quantization and
 dequantization: brute force with exact rationals, round trips, the worked INT8
 example printed on the pages, tie and padding cases, and error bounds."""
+import math
 from fractions import Fraction
 
 import numpy as np
 import pytest
+import torch
 
 import oracle
 
@@ -255,3 +257,63 @@ def test_bf16_rounding_vs_torch_and_ties():
     # ties: 1 + 2^-8 is halfway between 1 and 1 + 2^-7 -> even (1.0)
     assert oracle.f32_to_bf16_bits(np.array([1.0 + 2 ** -8], F32))[0] == 0x3F80
     assert oracle.f32_to_bf16_bits(np.array([1.0 + 3 * 2 ** -8], F32))[0] == 0x3F82
+
+
+def _bf16_value(u: int) -> float:
+    """The value of a bf16 bit pattern from its fields ([TT] §1 "FP32, FP16, BF16,
+    and FP8": 1 sign bit, 8 exponent bits with float32's bias, 7 fraction bits)."""
+    sign = -1.0 if u >> 15 else 1.0
+    e, f = (u >> 7) & 0xFF, u & 0x7F
+    if e == 0xFF:
+        return sign * math.inf if f == 0 else math.nan
+    if e == 0:
+        return sign * math.ldexp(f, -126 - 7)
+    return sign * math.ldexp(128 + f, e - 127 - 7)
+
+
+def test_bf16_widening_every_pattern():
+    """oracle.bf16_bits_to_f32 against the field definition for all 65,536 patterns
+    (NaNs: still NaN, sign kept) and against torch's bfloat16 -> float32 widening."""
+    u = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    got = oracle.bf16_bits_to_f32(u)
+    assert got.dtype == np.float32 and got.shape == u.shape
+    ref = np.array([_bf16_value(int(v)) for v in u], dtype=np.float64)
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan].astype(np.float64), ref[~nan])
+    assert np.array_equal(np.signbit(got), u >= 0x8000)
+    t = torch.from_numpy(u.view(np.int16).copy()).view(torch.bfloat16).float().numpy()
+    assert np.array_equal(t.view(np.uint32), got.view(np.uint32))
+
+
+def test_bf16_widening_hand_built():
+    cases = {0x0000: 0.0, 0x8000: -0.0, 0x0001: math.ldexp(1.0, -133), 0x807F: -math.ldexp(127.0, -133),
+             0x0080: math.ldexp(1.0, -126), 0x3F80: 1.0, 0xBF80: -1.0, 0x4049: 3.140625,
+             0x7F7F: math.ldexp(255.0, 120), 0xFF7F: -math.ldexp(255.0, 120), 0x7F80: math.inf, 0xFF80: -math.inf}
+    u = np.array(list(cases), dtype=np.uint16)
+    got = oracle.bf16_bits_to_f32(u)
+    for v, g in zip(cases.values(), got):
+        assert g == v and math.copysign(1.0, g) == math.copysign(1.0, v)
+
+
+def test_quantize_bf16_matches_widened_input():
+    """quantize_bf16 is quantize() of the widened values: checked on bf16 patterns whose
+    values are fixed by hand (the codebook ends, zero, a level times a power of two) and
+    on random patterns widened by torch (not by the oracle)."""
+    # one block: 1.0, -1.0, +0, -0, 0.5, then zeros; absmax 1, codes 15, 0, 7, 7 and
+    # the nearest level to 0.5 (found by brute force over the levels)
+    u = np.zeros(64, np.uint16)
+    u[:5] = [0x3F80, 0xBF80, 0x0000, 0x8000, 0x3F00]
+    packed, absmax = oracle.quantize_bf16(u)
+    lv = oracle.nf4_levels().astype(np.float64)
+    c_half = int(np.argmin(np.abs(lv - 0.5)))
+    codes = oracle.unpack_codes(packed, 64)
+    assert absmax[0] == 1.0
+    assert list(codes[:5]) == [15, 0, 7, 7, c_half] and set(codes[5:]) == {7}
+    rng = np.random.default_rng(7)
+    r = rng.integers(0, 1 << 16, size=4096).astype(np.uint16)
+    r = r[((r >> 7) & 0xFF) != 0xFF]  # finite values only ([TT] weights are finite)
+    widened = torch.from_numpy(r.view(np.int16).copy()).view(torch.bfloat16).float().numpy()
+    p1, a1 = oracle.quantize_bf16(r)
+    p2, a2 = oracle.quantize(widened)
+    assert np.array_equal(p1, p2) and np.array_equal(a1.view(np.uint32), a2.view(np.uint32))

@@ -27,6 +27,7 @@ BLOCK, CHUNK, MAX_RANK = 64, 256, 128
 EXPORTED = ("qlora_quantize", "qlora_double_quant", "qlora_dequantize", "qlora_linear_fwd",
             "qlora_linear_bwd", "qlora_merge_adapter", "qlora_merge_requantize", "qlora_adamw_step",
             "qlora_quantize_cb", "qlora_dequantize_cb", "qlora_dequantize_nodq", "qlora_codebook_levels",
+            "qlora_linear_fwd_cb", "qlora_linear_bwd_cb", "qlora_merge_adapter_cb", "qlora_merge_requantize_cb",
             "qlora_workspace_size",
             "qlora_status_string", "qlora_nf4_levels", "qlora_set_timing_events")
 
@@ -38,9 +39,9 @@ class QloraError(RuntimeError):
 
 
 class NF4WeightT(ctypes.Structure):
+    """qlora_nf4_weight_t: four device pointers, then h and o."""
     _fields_ = [("codes", ctypes.c_void_p), ("qabsmax", ctypes.c_void_p), ("scale2", ctypes.c_void_p),
-                ("mean", ctypes.c_void_p), ("h", ctypes.c_int64), ("o", ctypes.c_int64),
-                ("codebook", ctypes.c_int32)]
+                ("mean", ctypes.c_void_p), ("h", ctypes.c_int64), ("o", ctypes.c_int64)]
 
 
 def _load():
@@ -61,6 +62,11 @@ def _load():
                                    vp, sz, vp]
     L.qlora_merge_adapter.argtypes = [ctypes.POINTER(NF4WeightT), vp, vp, i32, f32, vp, st, vp]
     L.qlora_merge_requantize.argtypes = [ctypes.POINTER(NF4WeightT), vp, vp, i32, f32, vp, vp, vp]
+    W = ctypes.POINTER(NF4WeightT)
+    L.qlora_linear_fwd_cb.argtypes = [W, st] + L.qlora_linear_fwd.argtypes[1:]
+    L.qlora_linear_bwd_cb.argtypes = [W, st] + L.qlora_linear_bwd.argtypes[1:]
+    L.qlora_merge_adapter_cb.argtypes = [W, st] + L.qlora_merge_adapter.argtypes[1:]
+    L.qlora_merge_requantize_cb.argtypes = [W, st] + L.qlora_merge_requantize.argtypes[1:]
     L.qlora_adamw_step.argtypes = [vp, vp, vp, vp, i64, i64, f32, f32, f32, f32, f32, vp, vp]
     L.qlora_workspace_size.argtypes = [st, i64, i64, i64, i32, ctypes.POINTER(sz)]
     L.qlora_status_string.argtypes = [st]
@@ -139,7 +145,15 @@ class NF4Weight:
 
     def as_ctypes(self) -> NF4WeightT:
         return NF4WeightT(self.codes.data_ptr(), self.qabsmax.data_ptr(), self.scale2.data_ptr(),
-                          self.mean.data_ptr(), self.h, self.o, self.codebook)
+                          self.mean.data_ptr(), self.h, self.o)
+
+    def call(self, name: str, *args):
+        """Call entry point `name` on this weight: the NF4 entry point, or its `_cb` variant
+        with the codebook for other codebooks."""
+        wt = self.as_ctypes()
+        if self.codebook == QLORA_CB_NF4:
+            return getattr(lib, name)(ctypes.byref(wt), *args)
+        return getattr(lib, name + "_cb")(ctypes.byref(wt), self.codebook, *args)
 
 
 # ---------------------------------------------------------------------------
@@ -244,9 +258,8 @@ def qlora_linear_fwd(W: NF4Weight, X: torch.Tensor, L1: Optional[torch.Tensor], 
     ws_bytes = workspace_size(QLORA_OP_LINEAR_FWD, M, W.h, W.o, r)
     if workspace is None and ws_bytes:
         workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
-    wt = W.as_ctypes()
-    _check(lib.qlora_linear_fwd(ctypes.byref(wt), _ptr(X), M, _ptr(L1), _ptr(L2), r, float(s), _ptr(Y), _ptr(T),
-                                _ptr(workspace), 0 if workspace is None else workspace.numel(), _stream(dev)),
+    _check(W.call("qlora_linear_fwd", _ptr(X), M, _ptr(L1), _ptr(L2), r, float(s), _ptr(Y), _ptr(T),
+                  _ptr(workspace), 0 if workspace is None else workspace.numel(), _stream(dev)),
            "qlora_linear_fwd")
     return Y, T
 
@@ -259,9 +272,8 @@ def qlora_merge_adapter(W: NF4Weight, L1: Optional[torch.Tensor], L2: Optional[t
     dt = {torch.float32: QLORA_F32, torch.bfloat16: QLORA_BF16}[out_dtype]
     if out is None:
         out = torch.empty(W.o, W.h, dtype=out_dtype, device=W.codes.device)
-    wt = W.as_ctypes()
-    _check(lib.qlora_merge_adapter(ctypes.byref(wt), _ptr(L1), _ptr(L2), r, float(s), _ptr(out), dt,
-                                   _stream(W.codes.device)), "qlora_merge_adapter")
+    _check(W.call("qlora_merge_adapter", _ptr(L1), _ptr(L2), r, float(s), _ptr(out), dt, _stream(W.codes.device)),
+           "qlora_merge_adapter")
     return out
 
 
@@ -276,9 +288,8 @@ def qlora_merge_requantize(W: NF4Weight, L1: Optional[torch.Tensor], L2: Optiona
         codes = torch.empty(n // 2, dtype=torch.uint8, device=dev)
     if absmax is None:
         absmax = torch.empty(n // BLOCK, dtype=torch.float32, device=dev)
-    wt = W.as_ctypes()
-    _check(lib.qlora_merge_requantize(ctypes.byref(wt), _ptr(L1), _ptr(L2), r, float(s), _ptr(codes), _ptr(absmax),
-                                      _stream(dev)), "qlora_merge_requantize")
+    _check(W.call("qlora_merge_requantize", _ptr(L1), _ptr(L2), r, float(s), _ptr(codes), _ptr(absmax),
+                  _stream(dev)), "qlora_merge_requantize")
     return codes, absmax
 
 
@@ -325,9 +336,8 @@ def qlora_linear_bwd(W: NF4Weight, X: Optional[torch.Tensor], T: Optional[torch.
     ws_bytes = workspace_size(QLORA_OP_LINEAR_BWD, M, W.h, W.o, r)
     if workspace is None and ws_bytes:
         workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
-    wt = W.as_ctypes()
-    _check(lib.qlora_linear_bwd(ctypes.byref(wt), _ptr(X), _ptr(T), _ptr(dY), M, _ptr(L1), _ptr(L2), r, float(s),
-                                _ptr(dX), _ptr(dL1), _ptr(dL2), _ptr(workspace),
-                                0 if workspace is None else workspace.numel(), _stream(dev)),
+    _check(W.call("qlora_linear_bwd", _ptr(X), _ptr(T), _ptr(dY), M, _ptr(L1), _ptr(L2), r, float(s),
+                  _ptr(dX), _ptr(dL1), _ptr(dL2), _ptr(workspace),
+                  0 if workspace is None else workspace.numel(), _stream(dev)),
            "qlora_linear_bwd")
     return dX, dL1, dL2

@@ -8,6 +8,7 @@
 #include "optim.h"
 
 #include <cmath>
+#include <cstddef>
 
 using namespace ql;
 
@@ -19,12 +20,17 @@ inline qlora_status_t launch_status(hipError_t e) { return e == hipSuccess ? QLO
 
 inline size_t round256(size_t b) { return (b + 255) / 256 * 256; }
 
-bool valid_weight(const qlora_nf4_weight_t *W) {
+// The weight descriptor keeps the layout callers compile against.
+static_assert(sizeof(qlora_nf4_weight_t) == 48, "qlora_nf4_weight_t layout");
+static_assert(offsetof(qlora_nf4_weight_t, h) == 32 && offsetof(qlora_nf4_weight_t, o) == 40,
+              "qlora_nf4_weight_t layout");
+
+bool valid_weight(const qlora_nf4_weight_t *W, int codebook) {
   if (!W || !W->codes || !W->qabsmax || !W->scale2 || !W->mean) return false;
   if (W->h <= 0 || W->o <= 0 || W->h % 64 || W->o % 64) return false;
   if (W->h > (int64_t(1) << 20) || W->o > (int64_t(1) << 20)) return false;
   if (W->h * W->o / 64 >= (int64_t(1) << 32)) return false;
-  if (W->codebook < 0 || W->codebook >= kCodebooks) return false;
+  if (codebook < 0 || codebook >= kCodebooks) return false;
   return aligned(W->codes, 16) && aligned(W->qabsmax, 4) && aligned(W->scale2, 4) && aligned(W->mean, 4);
 }
 
@@ -51,30 +57,41 @@ qlora_status_t qlora_nf4_levels(float out[16]) {
   return QLORA_OK;
 }
 
-qlora_status_t qlora_merge_adapter(const qlora_nf4_weight_t *W, const uint16_t *L1, const uint16_t *L2, int32_t r,
-                                   float s, void *out, qlora_dtype_t out_dtype, void *stream) {
-  if (!valid_weight(W) || !out || r < 0 || r > QLORA_MAX_RANK) return QLORA_ERR_INVALID_VALUE;
+qlora_status_t qlora_merge_adapter_cb(const qlora_nf4_weight_t *W, qlora_codebook_t codebook, const uint16_t *L1,
+                                      const uint16_t *L2, int32_t r, float s, void *out, qlora_dtype_t out_dtype,
+                                      void *stream) {
+  if (!valid_weight(W, codebook) || !out || r < 0 || r > QLORA_MAX_RANK) return QLORA_ERR_INVALID_VALUE;
   if (out_dtype != QLORA_F32 && out_dtype != QLORA_BF16) return QLORA_ERR_INVALID_VALUE;
   if (r > 0 && (!L1 || !L2 || !aligned(L1, 16) || !aligned(L2, 16))) return QLORA_ERR_INVALID_VALUE;
   if (!aligned(out, 16)) return QLORA_ERR_INVALID_VALUE;
-  const Nf4Tables *t = host_tables(W->codebook);
+  const Nf4Tables *t = host_tables(codebook);
   if (!t) return QLORA_ERR_INTERNAL;
-  (void)hipGetLastError();
   const MergeArgs m{W->codes, W->qabsmax, W->scale2, W->mean, W->h, W->o, L1, L2, r, s, out, nullptr, nullptr};
   return launch_status(launch_merge(m, out_dtype == QLORA_BF16 ? 1 : 0, *t, reinterpret_cast<hipStream_t>(stream)));
 }
 
-qlora_status_t qlora_merge_requantize(const qlora_nf4_weight_t *W, const uint16_t *L1, const uint16_t *L2,
-                                      int32_t r, float s, uint8_t *codes_out, float *absmax_out, void *stream) {
-  if (!valid_weight(W) || !codes_out || !absmax_out || r < 0 || r > QLORA_MAX_RANK) return QLORA_ERR_INVALID_VALUE;
+qlora_status_t qlora_merge_adapter(const qlora_nf4_weight_t *W, const uint16_t *L1, const uint16_t *L2, int32_t r,
+                                   float s, void *out, qlora_dtype_t out_dtype, void *stream) {
+  return qlora_merge_adapter_cb(W, QLORA_CB_NF4, L1, L2, r, s, out, out_dtype, stream);
+}
+
+qlora_status_t qlora_merge_requantize_cb(const qlora_nf4_weight_t *W, qlora_codebook_t codebook, const uint16_t *L1,
+                                         const uint16_t *L2, int32_t r, float s, uint8_t *codes_out,
+                                         float *absmax_out, void *stream) {
+  if (!valid_weight(W, codebook) || !codes_out || !absmax_out || r < 0 || r > QLORA_MAX_RANK)
+    return QLORA_ERR_INVALID_VALUE;
   if (r > 0 && (!L1 || !L2 || !aligned(L1, 16) || !aligned(L2, 16))) return QLORA_ERR_INVALID_VALUE;
   if (!aligned(codes_out, 8) || !aligned(absmax_out, 4)) return QLORA_ERR_INVALID_VALUE;
-  const Nf4Tables *t = host_tables(W->codebook);
+  const Nf4Tables *t = host_tables(codebook);
   if (!t) return QLORA_ERR_INTERNAL;
-  (void)hipGetLastError();
   const MergeArgs m{W->codes, W->qabsmax, W->scale2, W->mean, W->h, W->o, L1, L2, r, s, nullptr, codes_out,
                     absmax_out};
   return launch_status(launch_merge(m, 2, *t, reinterpret_cast<hipStream_t>(stream)));
+}
+
+qlora_status_t qlora_merge_requantize(const qlora_nf4_weight_t *W, const uint16_t *L1, const uint16_t *L2,
+                                      int32_t r, float s, uint8_t *codes_out, float *absmax_out, void *stream) {
+  return qlora_merge_requantize_cb(W, QLORA_CB_NF4, L1, L2, r, s, codes_out, absmax_out, stream);
 }
 
 qlora_status_t qlora_adamw_step(float *param, const float *grad, float *exp_avg, float *exp_avg_sq, int64_t n,
@@ -87,7 +104,6 @@ qlora_status_t qlora_adamw_step(float *param, const float *grad, float *exp_avg,
   if (!(beta1 >= 0.0f && beta1 < 1.0f) || !(beta2 >= 0.0f && beta2 < 1.0f)) return QLORA_ERR_INVALID_VALUE;
   if (!(eps > 0.0f) || !std::isfinite(eps) || !(lr >= 0.0f) || !std::isfinite(lr)) return QLORA_ERR_INVALID_VALUE;
   if (!(weight_decay >= 0.0f) || !std::isfinite(weight_decay)) return QLORA_ERR_INVALID_VALUE;
-  (void)hipGetLastError();
   const AdamwArgs a{param, grad, exp_avg, exp_avg_sq, param_bf16, n, step, lr, beta1, beta2, eps, weight_decay};
   return launch_status(launch_adamw(a, reinterpret_cast<hipStream_t>(stream)));
 }
@@ -124,7 +140,6 @@ qlora_status_t qlora_quantize_cb(const void *w, qlora_dtype_t w_dtype, int64_t n
   if (!aligned(w, 16) || !aligned(codes, 4) || !aligned(absmax, 4)) return QLORA_ERR_INVALID_VALUE;
   const Nf4Tables *t = host_tables(codebook);
   if (!t) return QLORA_ERR_INTERNAL;
-  (void)hipGetLastError();
   return launch_status(launch_quantize(w, w_dtype == QLORA_BF16, n, codes, absmax, *t,
                                        reinterpret_cast<hipStream_t>(stream)));
 }
@@ -142,7 +157,6 @@ qlora_status_t qlora_double_quant(const float *absmax, int64_t nblocks, int8_t *
       !aligned(workspace, 256))
     return QLORA_ERR_INVALID_VALUE;
   if (ws_bytes < dq_workspace_bytes()) return QLORA_ERR_INVALID_VALUE;
-  (void)hipGetLastError();
   return launch_status(launch_double_quant(absmax, nblocks, qabsmax, scale2, mean, workspace,
                                            reinterpret_cast<hipStream_t>(stream)));
 }
@@ -157,7 +171,6 @@ qlora_status_t qlora_dequantize_cb(const uint8_t *codes, const int8_t *qabsmax, 
     return QLORA_ERR_INVALID_VALUE;
   const Nf4Tables *t = host_tables(codebook);
   if (!t) return QLORA_ERR_INTERNAL;
-  (void)hipGetLastError();
   return launch_status(launch_dequantize(codes, qabsmax, scale2, mean, n, out, out_dtype == QLORA_BF16,
                                          *t, reinterpret_cast<hipStream_t>(stream)));
 }
@@ -177,7 +190,6 @@ qlora_status_t qlora_dequantize_nodq(const uint8_t *codes, const float *absmax, 
   if (!aligned(codes, 16) || !aligned(out, 16) || !aligned(absmax, 4)) return QLORA_ERR_INVALID_VALUE;
   const Nf4Tables *t = host_tables(codebook);
   if (!t) return QLORA_ERR_INTERNAL;
-  (void)hipGetLastError();
   return launch_status(launch_dequantize(codes, nullptr, nullptr, nullptr, n, out, out_dtype == QLORA_BF16,
                                          *t, reinterpret_cast<hipStream_t>(stream), absmax));
 }
@@ -190,22 +202,48 @@ qlora_status_t qlora_codebook_levels(qlora_codebook_t codebook, float *levels) {
   return QLORA_OK;
 }
 
-qlora_status_t qlora_linear_fwd(const qlora_nf4_weight_t *W, const uint16_t *X, int64_t M,
-                                const uint16_t *L1, const uint16_t *L2, int32_t r, float s,
-                                uint16_t *Y, uint16_t *T, void *workspace, size_t ws_bytes,
-                                void *stream) {
-  if (!valid_weight(W) || !X || !Y || M < 1 || M > (int64_t(1) << 31)) return QLORA_ERR_INVALID_VALUE;
+qlora_status_t qlora_linear_fwd_cb(const qlora_nf4_weight_t *W, qlora_codebook_t codebook, const uint16_t *X,
+                                   int64_t M, const uint16_t *L1, const uint16_t *L2, int32_t r, float s,
+                                   uint16_t *Y, uint16_t *T, void *workspace, size_t ws_bytes, void *stream) {
+  if (!valid_weight(W, codebook) || !X || !Y || M < 1 || M > (int64_t(1) << 31)) return QLORA_ERR_INVALID_VALUE;
   if (r < 0 || r > QLORA_MAX_RANK) return QLORA_ERR_INVALID_VALUE;
   if (r > 0 && (!L1 || !L2 || !T)) return QLORA_ERR_INVALID_VALUE;
   if (!aligned(X, 16) || !aligned(Y, 16)) return QLORA_ERR_INVALID_VALUE;
   if (r > 0 && (!aligned(L1, 16) || !aligned(L2, 16) || !aligned(T, 16))) return QLORA_ERR_INVALID_VALUE;
   const size_t need = round256(linear_fwd_workspace(M, W->h, W->o, r));
   if (need && (!workspace || ws_bytes < need || !aligned(workspace, 256))) return QLORA_ERR_INVALID_VALUE;
-  const Nf4Tables *t = host_tables(W->codebook);
+  const Nf4Tables *t = host_tables(codebook);
   if (!t) return QLORA_ERR_INTERNAL;
-  (void)hipGetLastError();
   LinearArgs a{W->codes, W->qabsmax, W->scale2, W->mean, W->h, W->o, M, r, s};
   return launch_status(launch_linear_fwd(a, X, L1, L2, Y, T, workspace, *t,
+                                         reinterpret_cast<hipStream_t>(stream)));
+}
+
+qlora_status_t qlora_linear_fwd(const qlora_nf4_weight_t *W, const uint16_t *X, int64_t M,
+                                const uint16_t *L1, const uint16_t *L2, int32_t r, float s,
+                                uint16_t *Y, uint16_t *T, void *workspace, size_t ws_bytes,
+                                void *stream) {
+  return qlora_linear_fwd_cb(W, QLORA_CB_NF4, X, M, L1, L2, r, s, Y, T, workspace, ws_bytes, stream);
+}
+
+qlora_status_t qlora_linear_bwd_cb(const qlora_nf4_weight_t *W, qlora_codebook_t codebook, const uint16_t *X,
+                                   const uint16_t *T, const uint16_t *dY, int64_t M, const uint16_t *L1,
+                                   const uint16_t *L2, int32_t r, float s, uint16_t *dX, float *dL1, float *dL2,
+                                   void *workspace, size_t ws_bytes, void *stream) {
+  if (!valid_weight(W, codebook) || !dY || !dX || M < 1 || M > (int64_t(1) << 31)) return QLORA_ERR_INVALID_VALUE;
+  if (r < 0 || r > QLORA_MAX_RANK) return QLORA_ERR_INVALID_VALUE;
+  if (r > 0 && (!X || !T || !L1 || !L2 || !dL1 || !dL2)) return QLORA_ERR_INVALID_VALUE;
+  if (!aligned(dY, 16) || !aligned(dX, 16)) return QLORA_ERR_INVALID_VALUE;
+  if (r > 0 && (!aligned(X, 16) || !aligned(T, 16) || !aligned(L1, 16) || !aligned(L2, 16) ||
+                !aligned(dL1, 16) || !aligned(dL2, 16)))
+    return QLORA_ERR_INVALID_VALUE;
+  if (!linear_bwd_supported(M, W->h, W->o, r)) return QLORA_ERR_UNSUPPORTED;
+  const size_t need = round256(linear_bwd_workspace(M, W->h, W->o, r));
+  if (need && (!workspace || ws_bytes < need || !aligned(workspace, 256))) return QLORA_ERR_INVALID_VALUE;
+  const Nf4Tables *t = host_tables(codebook);
+  if (!t) return QLORA_ERR_INTERNAL;
+  LinearArgs a{W->codes, W->qabsmax, W->scale2, W->mean, W->h, W->o, M, r, s};
+  return launch_status(launch_linear_bwd(a, X, T, dY, L1, L2, dX, dL1, dL2, workspace, *t,
                                          reinterpret_cast<hipStream_t>(stream)));
 }
 
@@ -213,21 +251,7 @@ qlora_status_t qlora_linear_bwd(const qlora_nf4_weight_t *W, const uint16_t *X, 
                                 const uint16_t *dY, int64_t M, const uint16_t *L1, const uint16_t *L2,
                                 int32_t r, float s, uint16_t *dX, float *dL1, float *dL2,
                                 void *workspace, size_t ws_bytes, void *stream) {
-  if (!valid_weight(W) || !dY || !dX || M < 1 || M > (int64_t(1) << 31)) return QLORA_ERR_INVALID_VALUE;
-  if (r < 0 || r > QLORA_MAX_RANK) return QLORA_ERR_INVALID_VALUE;
-  if (r > 0 && (!X || !T || !L1 || !L2 || !dL1 || !dL2)) return QLORA_ERR_INVALID_VALUE;
-  if (!aligned(dY, 16) || !aligned(dX, 16)) return QLORA_ERR_INVALID_VALUE;
-  if (r > 0 && (!aligned(X, 16) || !aligned(T, 16) || !aligned(L1, 16) || !aligned(L2, 16) ||
-                !aligned(dL1, 16) || !aligned(dL2, 16)))
-    return QLORA_ERR_INVALID_VALUE;
-  const size_t need = round256(linear_bwd_workspace(M, W->h, W->o, r));
-  if (need && (!workspace || ws_bytes < need || !aligned(workspace, 256))) return QLORA_ERR_INVALID_VALUE;
-  const Nf4Tables *t = host_tables(W->codebook);
-  if (!t) return QLORA_ERR_INTERNAL;
-  (void)hipGetLastError();
-  LinearArgs a{W->codes, W->qabsmax, W->scale2, W->mean, W->h, W->o, M, r, s};
-  return launch_status(launch_linear_bwd(a, X, T, dY, L1, L2, dX, dL1, dL2, workspace, *t,
-                                         reinterpret_cast<hipStream_t>(stream)));
+  return qlora_linear_bwd_cb(W, QLORA_CB_NF4, X, T, dY, M, L1, L2, r, s, dX, dL1, dL2, workspace, ws_bytes, stream);
 }
 
 }  // extern "C"

@@ -739,11 +739,8 @@ hipError_t launch_quantize(const void *w, bool bf16, int64_t n, uint8_t *codes, 
                            const Nf4Tables &tab, hipStream_t st) {
   // 512 weights per wave-iteration, 4 waves per block
   const int grid = grid_for((n + 511) / 512, 4, 256 * 32);
-  if (bf16)
-    quantize_kernel<true><<<grid, 256, 0, st>>>(w, n, codes, absmax, tab);
-  else
-    quantize_kernel<false><<<grid, 256, 0, st>>>(w, n, codes, absmax, tab);
-  return hipGetLastError();
+  return bf16 ? launch(quantize_kernel<true>, grid, 256, st, w, n, codes, absmax, tab)
+              : launch(quantize_kernel<false>, grid, 256, st, w, n, codes, absmax, tab);
 }
 
 size_t dq_workspace_bytes() { return ((size_t)kDqGrid * kLimbs * 8 + 255) / 256 * 256; }
@@ -752,21 +749,22 @@ hipError_t launch_double_quant(const float *absmax, int64_t nb, int8_t *qabsmax,
                                float *mean, void *ws, hipStream_t st) {
   auto *partial = reinterpret_cast<unsigned long long *>(ws);
   const int grid = grid_for(nb, 256 * 16, kDqGrid);
-  dq_partial_kernel<<<grid, 256, 0, st>>>(absmax, nb, partial);
+  const hipError_t e = launch(dq_partial_kernel, grid, 256, st, absmax, nb, partial);
+  if (e != hipSuccess) return e;
   const int64_t nch = (nb + kChunk - 1) / kChunk;
   const int cgrid = grid_for(nch, 4, kDqChGrid);
-  dq_chunks_kernel<<<cgrid, 256, 0, st>>>(absmax, nb, partial, grid, qabsmax, scale2, mean);
-  return hipGetLastError();
+  return launch(dq_chunks_kernel, cgrid, 256, st, absmax, nb, (const unsigned long long *)partial, grid, qabsmax,
+                scale2, mean);
 }
 
 template <int MODE>
-static void launch_merge_rq(int rq, dim3 grid, const MergeParams &p, const Nf4Tables &tab, hipStream_t st) {
+static hipError_t launch_merge_rq(int rq, dim3 grid, const MergeParams &p, const Nf4Tables &tab, hipStream_t st) {
   switch (rq) {
-    case 0: merge_kernel<MODE, 0><<<grid, 256, 0, st>>>(p, tab); break;
-    case 1: merge_kernel<MODE, 1><<<grid, 256, 0, st>>>(p, tab); break;
-    case 2: merge_kernel<MODE, 2><<<grid, 256, 0, st>>>(p, tab); break;
-    case 3: merge_kernel<MODE, 3><<<grid, 256, 0, st>>>(p, tab); break;
-    default: merge_kernel<MODE, 4><<<grid, 256, 0, st>>>(p, tab); break;
+    case 0: return launch(merge_kernel<MODE, 0>, grid, 256, st, p, tab);
+    case 1: return launch(merge_kernel<MODE, 1>, grid, 256, st, p, tab);
+    case 2: return launch(merge_kernel<MODE, 2>, grid, 256, st, p, tab);
+    case 3: return launch(merge_kernel<MODE, 3>, grid, 256, st, p, tab);
+    default: return launch(merge_kernel<MODE, 4>, grid, 256, st, p, tab);
   }
 }
 
@@ -783,28 +781,18 @@ hipError_t launch_merge(const MergeArgs &m, int mode, const Nf4Tables &tab, hipS
   ksplit = (ktiles + p.kper - 1) / p.kper;
   const dim3 grid((unsigned)strips, (unsigned)ksplit);
   const int rq = (m.r + 31) / 32;
-  if (mode == 0) launch_merge_rq<0>(rq, grid, p, tab, st);
-  else if (mode == 1) launch_merge_rq<1>(rq, grid, p, tab, st);
-  else launch_merge_rq<2>(rq, grid, p, tab, st);
-  return hipGetLastError();
+  if (mode == 0) return launch_merge_rq<0>(rq, grid, p, tab, st);
+  if (mode == 1) return launch_merge_rq<1>(rq, grid, p, tab, st);
+  return launch_merge_rq<2>(rq, grid, p, tab, st);
 }
 
 hipError_t launch_dequantize(const uint8_t *codes, const int8_t *qabsmax, const float *scale2,
                              const float *mean, int64_t n, void *out, bool bf16, const Nf4Tables &tab,
                              hipStream_t st, const float *absmax) {
   const int grid = grid_for((n + 7) / 8, 256 * kDeqUnroll, 256 * 16);
-  if (absmax) {
-    if (bf16)
-      dequantize_kernel<true, true><<<grid, 256, 0, st>>>(codes, qabsmax, scale2, mean, n, out, tab, absmax);
-    else
-      dequantize_kernel<false, true><<<grid, 256, 0, st>>>(codes, qabsmax, scale2, mean, n, out, tab, absmax);
-  } else {
-    if (bf16)
-      dequantize_kernel<true, false><<<grid, 256, 0, st>>>(codes, qabsmax, scale2, mean, n, out, tab, absmax);
-    else
-      dequantize_kernel<false, false><<<grid, 256, 0, st>>>(codes, qabsmax, scale2, mean, n, out, tab, absmax);
-  }
-  return hipGetLastError();
+  auto k = absmax ? (bf16 ? dequantize_kernel<true, true> : dequantize_kernel<false, true>)
+                  : (bf16 ? dequantize_kernel<true, false> : dequantize_kernel<false, false>);
+  return launch(k, grid, 256, st, codes, qabsmax, scale2, mean, n, out, tab, absmax);
 }
 
 }  // namespace ql

@@ -4,6 +4,9 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <tuple>
+#include <utility>
+
 #define QL_DEV __device__ __forceinline__
 
 namespace ql {
@@ -63,6 +66,24 @@ QL_DEV float bf16_hi(uint32_t d) { return __builtin_bit_cast(float, d & 0xFFFF00
 QL_DEV float scale_hat(int8_t q, float s2, float mean) {
   float p = (float)q * s2;
   return p + mean;
+}
+
+// ---- launches ------------------------------------------------------------
+
+// Launch through hipLaunchKernel and return that launch's own status: a failed
+// launch is reported without reading (or clearing) the calling thread's
+// last-error state, which belongs to the caller.
+template <typename... P, size_t... I>
+hipError_t launch_tuple(void (*k)(P...), dim3 grid, dim3 block, hipStream_t st, std::tuple<P...> &t,
+                        std::index_sequence<I...>) {
+  void *args[] = {static_cast<void *>(&std::get<I>(t))...};
+  return hipLaunchKernel(reinterpret_cast<const void *>(k), grid, block, args, 0, st);
+}
+template <typename... P, typename... A>
+hipError_t launch(void (*k)(P...), dim3 grid, dim3 block, hipStream_t st, A... a) {
+  static_assert(sizeof...(P) == sizeof...(A), "kernel argument count");
+  std::tuple<P...> t(a...);
+  return launch_tuple(k, grid, block, st, t, std::index_sequence_for<P...>{});
 }
 
 }  // namespace ql

@@ -34,6 +34,6 @@ struct GemmParams {
   float level[16];
 };
 
-void launch_nf4_gemm(GemmParams &gp, bool trans, hipStream_t st);
+hipError_t launch_nf4_gemm(GemmParams &gp, bool trans, hipStream_t st);
 
 }  // namespace ql

@@ -21,6 +21,12 @@ void set_timing_events(int kernel, hipEvent_t start, hipEvent_t stop);
 
 size_t linear_fwd_workspace(int64_t M, int64_t h, int64_t o, int r);
 size_t linear_bwd_workspace(int64_t M, int64_t h, int64_t o, int r);
+// false when the adapter gradients of this shape would need more token splits than
+// one launch holds (very large M with very wide layers)
+bool linear_bwd_supported(int64_t M, int64_t h, int64_t o, int r);
+// token splits of the adapter-gradient reduction (each split's operand slab stays
+// below 2^31 bytes)
+int64_t linear_bwd_token_splits(int64_t M, int64_t h, int64_t o);
 
 hipError_t launch_linear_fwd(const LinearArgs &a, const uint16_t *X, const uint16_t *L1, const uint16_t *L2,
                              uint16_t *Y, uint16_t *T, void *ws, const Nf4Tables &tab, hipStream_t st);

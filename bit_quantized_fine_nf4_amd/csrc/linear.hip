@@ -84,11 +84,16 @@ QL_DEV void store_partial(float *p, float v) { __hip_atomic_store(p, v, __ATOMIC
 QL_DEV float load_partial(const float *p) { return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
 QL_DEV bool last_of_splits(unsigned *cnt, unsigned splits) {
   __shared__ bool last;
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");  // keeps the partial stores above this point
-  __builtin_amdgcn_s_waitcnt(0);                           // ... and waits until they are acknowledged
+  // Release at agent scope: each thread's partial stores are complete and visible to
+  // every workgroup before the barrier; thread 0's release RMW then publishes the whole
+  // workgroup's stores (they happen before it through the barrier).
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
   __syncthreads();
-  if (threadIdx.x == 0) last = atomicAdd(cnt, 1u) == splits - 1;
+  if (threadIdx.x == 0)
+    last = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT) == splits - 1;
   __syncthreads();
+  // Acquire: the last workgroup reads the other splits' partials only after their releases.
+  if (last) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
   return last;
 }
 
@@ -238,7 +243,7 @@ __global__ __launch_bounds__(1024) void rank_r_kernel(RankParams p) {
       const int64_t a = idx / p.ldp, b = idx % p.ldp;
       p.L1p[idx] = b < r ? p.L1[a * r + b] : (uint16_t)0;
     }
-    if (gt < p.ncnt) p.cnt[gt] = 0u;
+    for (int64_t idx = gt; idx < p.ncnt; idx += gn) p.cnt[idx] = 0u;
   }
 }
 
@@ -619,7 +624,12 @@ struct Split {
   int64_t chunk;
 };
 
-Split grad_split(int64_t M, int64_t I) {
+// Largest token chunk whose slab of a token-major operand with rows of `ld` bf16
+// values fits one buffer view: the kernel addresses a split's rows with 32-bit
+// offsets and its view is capped below 2^31 bytes.
+int64_t grad_chunk_cap(int64_t ld) { return ((int64_t)0x7FFFFFF0 / (2 * ld)) / 64 * 64; }
+
+Split grad_split(int64_t M, int64_t I, int64_t maxld) {
   // about 512 workgroups: more token splits cost more in partial sums than they save
   const int64_t it = cdiv(I, kGradTile);
   int64_t S = cdiv(kTargetGroups, it);
@@ -627,6 +637,8 @@ Split grad_split(int64_t M, int64_t I) {
   S = S < 1 ? 1 : S;
   S = S > msteps ? msteps : S;
   int64_t chunk = rup(cdiv(M, S), 64);
+  const int64_t cap = grad_chunk_cap(maxld);
+  if (chunk > cap) chunk = cap;
   return {(int)cdiv(M, chunk), chunk};
 }
 
@@ -668,7 +680,7 @@ BwdLayout bwd_layout(int64_t M, int64_t h, int64_t o, int r) {
   if (r == 0) return L;
   L.RP16 = (int)rup(r, 16);
   L.RP64 = (int)rup(r, 64);
-  L.gs = grad_split(M, h + o);
+  L.gs = grad_split(M, h + o, h > o ? h : o);
   L.off_u = take((size_t)M * L.RP16 * 2);
   L.off_su = take((size_t)M * L.RP64 * 2);
   L.off_l1p = take((size_t)h * L.RP64 * 2);
@@ -681,33 +693,30 @@ BwdLayout bwd_layout(int64_t M, int64_t h, int64_t o, int r) {
 template <typename T>
 T *at(void *ws, size_t off) { return reinterpret_cast<T *>(reinterpret_cast<char *>(ws) + off); }
 
-void rank_r(RankParams &rp, bool kn, int RP16, hipStream_t st) {
+hipError_t rank_r(RankParams &rp, bool kn, int RP16, hipStream_t st) {
   // the fewest rows per workgroup that still give 256 workgroups (one per compute unit)
   rp.rows = rp.M >= 16 * 256 ? 16 : (rp.M >= 8 * 256 ? 8 : 4);
   const unsigned grid = (unsigned)cdiv(rp.M, rp.rows);
   switch (RP16 / 16) {
-#define QL_RK(NT)                                                                       \
-  case NT:                                                                              \
-    if (kn) rank_r_kernel<NT, true><<<grid, 1024, 0, st>>>(rp);                          \
-    else rank_r_kernel<NT, false><<<grid, 1024, 0, st>>>(rp);                            \
-    break;
+#define QL_RK(NT) \
+  case NT: return kn ? launch(rank_r_kernel<NT, true>, grid, 1024, st, rp) : launch(rank_r_kernel<NT, false>, grid, 1024, st, rp);
     QL_RK(1) QL_RK(2) QL_RK(3) QL_RK(4) QL_RK(5) QL_RK(6) QL_RK(7) QL_RK(8)
 #undef QL_RK
   }
+  return hipErrorInvalidValue;
 }
 
-void lora_grad(const GradProblem &pa, const GradProblem &pb, int r, float s, int64_t M, int RP16, const Split &sp,
-               float *part, unsigned *cnt, hipStream_t st) {
+hipError_t lora_grad(const GradProblem &pa, const GradProblem &pb, int r, float s, int64_t M, int RP16,
+                     const Split &sp, float *part, unsigned *cnt, hipStream_t st) {
   dim3 grid((unsigned)(pa.tiles + pb.tiles), (unsigned)sp.S);
   const int64_t prows = pa.I + pb.I;
   switch (RP16 / 16) {
-#define QL_LG(NT)                                                                                                 \
-  case NT:                                                                                                        \
-    lora_grad_kernel<NT><<<grid, 256, 0, st>>>(pa, pb, r, s, M, sp.chunk, prows, part, cnt); \
-    break;
+#define QL_LG(NT) \
+  case NT: return launch(lora_grad_kernel<NT>, grid, 256, st, pa, pb, r, s, M, sp.chunk, prows, part, cnt);
     QL_LG(1) QL_LG(2) QL_LG(3) QL_LG(4) QL_LG(5) QL_LG(6) QL_LG(7) QL_LG(8)
 #undef QL_LG
   }
+  return hipErrorInvalidValue;
 }
 
 thread_local hipEvent_t t_ev[3][2] = {};
@@ -1010,6 +1019,15 @@ void set_timing_events(int kernel, hipEvent_t start, hipEvent_t stop) {
 size_t linear_fwd_workspace(int64_t M, int64_t h, int64_t o, int r) { return fwd_layout(M, h, o, r).total; }
 size_t linear_bwd_workspace(int64_t M, int64_t h, int64_t o, int r) { return bwd_layout(M, h, o, r).total; }
 
+bool linear_bwd_supported(int64_t M, int64_t h, int64_t o, int r) {
+  // the adapter-gradient launch has one grid row per token split
+  return r == 0 || grad_split(M, h + o, h > o ? h : o).S <= 65535;
+}
+
+int64_t linear_bwd_token_splits(int64_t M, int64_t h, int64_t o) {
+  return grad_split(M, h + o, h > o ? h : o).S;
+}
+
 hipError_t launch_linear_fwd(const LinearArgs &a, const uint16_t *X, const uint16_t *L1, const uint16_t *L2,
                              uint16_t *Y, uint16_t *T, void *ws, const Nf4Tables &tab, hipStream_t st) {
   const FwdLayout L = fwd_layout(a.M, a.h, a.o, a.r);
@@ -1021,7 +1039,8 @@ hipError_t launch_linear_fwd(const LinearArgs &a, const uint16_t *X, const uint1
     rp.A = X; rp.lda = a.h; rp.M = a.M; rp.K = a.h;
     rp.B = L1; rp.ldb = a.r; rp.r = a.r; rp.s = a.s;
     rp.out1 = T; rp.ld1 = a.r; rp.out2 = sT; rp.ld2 = L.RP64;
-    rank_r(rp, true, L.RP16, st);
+    const hipError_t e = rank_r(rp, true, L.RP16, st);
+    if (e != hipSuccess) return e;
   }
   if (a.M <= 16) {
     GemvParams gp{};
@@ -1031,17 +1050,10 @@ hipError_t launch_linear_fwd(const LinearArgs &a, const uint16_t *X, const uint1
     gp.sT = sT; gp.ldt = L.RP64; gp.r = a.r; gp.L2 = L2;
     gp.Y = Y; gp.ldy = a.o;
     fill_levels(gp.level, tab);
-    {
-      TimedLaunch tl(2, st);
-      const unsigned grid = (unsigned)(a.o / kGvRows);
-      if (a.M == 1)
-        nf4_gemv_kernel<1><<<grid, kGvThreads, 0, st>>>(gp);
-      else if (a.M <= 4)
-        nf4_gemv_kernel<4><<<grid, kGvThreads, 0, st>>>(gp);
-      else
-        nf4_gemv_kernel<16><<<grid, kGvThreads, 0, st>>>(gp);
-    }
-    return hipGetLastError();
+    TimedLaunch tl(2, st);
+    const unsigned grid = (unsigned)(a.o / kGvRows);
+    auto k = a.M == 1 ? nf4_gemv_kernel<1> : (a.M <= 4 ? nf4_gemv_kernel<4> : nf4_gemv_kernel<16>);
+    return launch(k, grid, kGvThreads, st, gp);
   }
   GemmParams gp{};
   gp.A = X; gp.lda = a.h;
@@ -1053,11 +1065,8 @@ hipError_t launch_linear_fwd(const LinearArgs &a, const uint16_t *X, const uint1
   gp.M = a.M; gp.N = a.o;
   gp.C = Y; gp.ldc = a.o;
   fill_levels(gp.level, tab);
-  {
-    TimedLaunch tl(0, st);
-    launch_nf4_gemm(gp, false, st);
-  }
-  return hipGetLastError();
+  TimedLaunch tl(0, st);
+  return launch_nf4_gemm(gp, false, st);
 }
 
 hipError_t launch_linear_bwd(const LinearArgs &a, const uint16_t *X, const uint16_t *T, const uint16_t *dY,
@@ -1080,7 +1089,8 @@ hipError_t launch_linear_bwd(const LinearArgs &a, const uint16_t *X, const uint1
     rp.B = L2; rp.ldb = a.o; rp.r = a.r; rp.s = a.s;
     rp.out1 = U; rp.ld1 = L.RP16; rp.out2 = sU; rp.ld2 = L.RP64;
     rp.L1 = L1; rp.h = a.h; rp.ldp = L.RP64; rp.L1p = L1p; rp.cnt = cnt; rp.ncnt = (int)((a.h + a.o) / 64);
-    rank_r(rp, false, L.RP16, st);
+    const hipError_t e = rank_r(rp, false, L.RP16, st);
+    if (e != hipSuccess) return e;
     // dL1 = s·X^T·U (P = X [M][h], Q = U [M][RP16]) and dL2 = s·T^T·dY (P = dY [M][o], Q = T [M][r]), stored [r][o]
     g1 = GradProblem{X, a.h, a.h, U, L.RP16, dL1, false, cdiv(a.h, kGradTile), 0};
     g2 = GradProblem{dY, a.o, a.o, T, a.r, dL2, true, cdiv(a.o, kGradTile), a.h};
@@ -1097,18 +1107,18 @@ hipError_t launch_linear_bwd(const LinearArgs &a, const uint16_t *X, const uint1
     vp.part = at<float>(ws, L.off_dxp);
     fill_levels(vp.level, tab);
     const dim3 grid((unsigned)((a.h + kGvdCols - 1) / kGvdCols), (unsigned)L.dxc);
-    auto launch_dx = [&]() {
-      {
-        TimedLaunch tl(1, st);
-        nf4_gemv_dx_kernel<<<grid, kGvmThreads, 0, st>>>(vp);
-      }
-      const int64_t cg = (a.h / 8 + 63) / 64;
-      gemv_dx_finish_kernel<<<(unsigned)(a.M * cg), 256, 0, st>>>(vp.part, L.dxc, (int)a.M, a.h, sU, L.RP64, L1,
-                                                                 a.r, dX, a.h);
-    };
-    if (a.r > 0) lora_grad(g1, g2, a.r, a.s, a.M, L.RP16, L.gs, gpart, gcnt, st);
-    launch_dx();
-    return hipGetLastError();
+    if (a.r > 0) {
+      const hipError_t e = lora_grad(g1, g2, a.r, a.s, a.M, L.RP16, L.gs, gpart, gcnt, st);
+      if (e != hipSuccess) return e;
+    }
+    {
+      TimedLaunch tl(1, st);
+      const hipError_t e = launch(nf4_gemv_dx_kernel, grid, kGvmThreads, st, vp);
+      if (e != hipSuccess) return e;
+    }
+    const int64_t cg = (a.h / 8 + 63) / 64;
+    return launch(gemv_dx_finish_kernel, (unsigned)(a.M * cg), 256, st, (const float *)vp.part, L.dxc, (int)a.M,
+                  a.h, (const uint16_t *)sU, L.RP64, L1, a.r, dX, a.h);
   }
   GemmParams gp{};
   gp.A = dY; gp.lda = a.o;
@@ -1124,12 +1134,12 @@ hipError_t launch_linear_bwd(const LinearArgs &a, const uint16_t *X, const uint1
   // side stream beside the dX GEMM cost the GEMM more than they saved (they share
   // the compute units and the cache hierarchy, and the stream fork and join add
   // their own gaps).
-  if (a.r > 0) lora_grad(g1, g2, a.r, a.s, a.M, L.RP16, L.gs, gpart, gcnt, st);
-  {
-    TimedLaunch tl(1, st);
-    launch_nf4_gemm(gp, true, st);
+  if (a.r > 0) {
+    const hipError_t e = lora_grad(g1, g2, a.r, a.s, a.M, L.RP16, L.gs, gpart, gcnt, st);
+    if (e != hipSuccess) return e;
   }
-  return hipGetLastError();
+  TimedLaunch tl(1, st);
+  return launch_nf4_gemm(gp, true, st);
 }
 
 }  // namespace ql

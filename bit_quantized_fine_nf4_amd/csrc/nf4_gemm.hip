@@ -501,26 +501,25 @@ namespace {
 inline int64_t cdiv(int64_t x, int64_t m) { return (x + m - 1) / m; }
 
 template <int BM, int BN, bool TRANS>
-void gemm_launch(GemmParams &gp, hipStream_t st) {
+hipError_t gemm_launch(GemmParams &gp, hipStream_t st) {
   gp.tiles_m = (int)cdiv(gp.M, BM);
   gp.tiles_n = (int)cdiv(gp.N, BN);
-  nf4_gemm_kernel<BM, BN, TRANS><<<gp.tiles_m * gp.tiles_n, 512, 0, st>>>(gp);
+  return launch(nf4_gemm_kernel<BM, BN, TRANS>, gp.tiles_m * gp.tiles_n, 512, st, gp);
 }
 
 template <bool TRANS>
-void gemm_select(GemmParams &gp, hipStream_t st) {
+hipError_t gemm_select(GemmParams &gp, hipStream_t st) {
   const int64_t t256 = cdiv(gp.M, 256) * cdiv(gp.N, 256);
   const int64_t t256x128 = cdiv(gp.M, 256) * cdiv(gp.N, 128);
-  if (gp.M >= 256 && t256 >= 240) gemm_launch<256, 256, TRANS>(gp, st);
-  else if (gp.M >= 192 && t256x128 >= 160) gemm_launch<256, 128, TRANS>(gp, st);
-  else gemm_launch<128, 128, TRANS>(gp, st);
+  if (gp.M >= 256 && t256 >= 240) return gemm_launch<256, 256, TRANS>(gp, st);
+  if (gp.M >= 192 && t256x128 >= 160) return gemm_launch<256, 128, TRANS>(gp, st);
+  return gemm_launch<128, 128, TRANS>(gp, st);
 }
 
 }  // namespace
 
-void launch_nf4_gemm(GemmParams &gp, bool trans, hipStream_t st) {
-  if (trans) gemm_select<true>(gp, st);
-  else gemm_select<false>(gp, st);
+hipError_t launch_nf4_gemm(GemmParams &gp, bool trans, hipStream_t st) {
+  return trans ? gemm_select<true>(gp, st) : gemm_select<false>(gp, st);
 }
 
 }  // namespace ql

@@ -93,8 +93,7 @@ hipError_t launch_adamw(const AdamwArgs &x, hipStream_t st) {
   const int64_t n4 = x.n >> 2;
   int64_t grid = (n4 + 255) / 256;
   grid = grid < 1 ? 1 : (grid > 4096 ? 4096 : grid);
-  adamw_kernel<<<(int)grid, 256, 0, st>>>(a);
-  return hipGetLastError();
+  return launch(adamw_kernel, (int)grid, 256, st, a);
 }
 
 }  // namespace ql

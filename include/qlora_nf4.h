@@ -18,9 +18,14 @@
  *    exponent, 7 fraction bits).  All matrices are row-major.
  *  - Pointers must be 16-byte aligned unless stated otherwise.
  *  - Errors: arguments are validated before anything is enqueued; on
- *    QLORA_ERR_INVALID_VALUE nothing is launched and no output is touched.
- *    A failed kernel launch returns QLORA_ERR_LAUNCH.  No exception crosses
- *    the ABI.  Non-finite inputs give unspecified (but memory-safe) results.
+ *    QLORA_ERR_INVALID_VALUE or QLORA_ERR_UNSUPPORTED nothing is launched and
+ *    no output is touched.  A failed kernel launch returns QLORA_ERR_LAUNCH
+ *    (kernels of the same call already enqueued before it still run).  The
+ *    library takes each launch's status from the launch call itself: it never
+ *    reads or clears the calling thread's HIP last-error state, so an error
+ *    left there by the caller's own earlier work stays for the caller to see.
+ *    No exception crosses the ABI.  Non-finite inputs give unspecified (but
+ *    memory-safe) results.
  *  - Thread safety: the library holds no shared mutable state after its
  *    one-time initialisation of the NF4 tables (done under a lock on first
  *    use); the timing hook's events are per thread.
@@ -74,10 +79,12 @@ typedef enum {
  * One frozen NF4 weight with double-quantized scales.  Logical shape h x o
  * (the pages' W: h inputs, o outputs, [MC] "The algebra").  Stored in
  * PyTorch's Linear.weight order [o][h]: row n holds output n's h weights, so
- * each 64-weight block runs along h.  Produced by qlora_quantize (or
- * qlora_quantize_cb with the codebook recorded in `codebook`) on the [o][h]
- * buffer followed by qlora_double_quant.  This struct is a host
- * object; the pointers in it are device pointers.
+ * each 64-weight block runs along h.  Produced by qlora_quantize on the [o][h]
+ * buffer followed by qlora_double_quant.  This struct is a host object (48
+ * bytes on LP64: four pointers, then h at offset 32 and o at offset 40); the
+ * pointers in it are device pointers.  Weights encoded with another codebook
+ * (qlora_quantize_cb) use the same struct with the `_cb` entry points, which
+ * take the codebook as an argument.
  */
 typedef struct {
   const uint8_t *codes;   /* h*o/2 bytes: two 4-bit codes per byte, first in the high nibble */
@@ -86,7 +93,6 @@ typedef struct {
   const float *mean;      /* 1 float32: the mean of the float32 block scales */
   int64_t h;              /* input width, a positive multiple of 64, at most 2^20 */
   int64_t o;              /* output width, a positive multiple of 64, at most 2^20 */
-  int32_t codebook;       /* qlora_codebook_t of the codes; QLORA_CB_NF4 (0) for NF4 */
 } qlora_nf4_weight_t;
 
 /*
@@ -188,11 +194,29 @@ qlora_status_t qlora_linear_fwd(const qlora_nf4_weight_t *W, const uint16_t *X, 
  *  T is the forward's saved [M][r] bf16 product X·L1.  r = 0: only dX is
  *  computed and X, T, L1, L2, dL1, dL2 may be NULL.
  *  workspace: qlora_workspace_size(QLORA_OP_LINEAR_BWD, M, h, o, r) bytes.
+ *  The token sum behind dL1 and dL2 is split into chunks whose operand rows
+ *  stay below 2^31 bytes each; a shape that would need more than 65535 such
+ *  chunks (only for M in the hundreds of millions on the widest layers)
+ *  returns QLORA_ERR_UNSUPPORTED.
  */
 qlora_status_t qlora_linear_bwd(const qlora_nf4_weight_t *W, const uint16_t *X, const uint16_t *T,
                                 const uint16_t *dY, int64_t M, const uint16_t *L1, const uint16_t *L2,
                                 int32_t r, float s, uint16_t *dX, float *dL1, float *dL2,
                                 void *workspace, size_t ws_bytes, void *stream);
+
+/*
+ * The linear layer on a weight encoded with another codebook
+ * (qlora_quantize_cb): arguments, layouts and errors as qlora_linear_fwd and
+ * qlora_linear_bwd, the codes decoded with the levels of `codebook`
+ * (qlora_linear_fwd / qlora_linear_bwd are the QLORA_CB_NF4 cases).
+ */
+qlora_status_t qlora_linear_fwd_cb(const qlora_nf4_weight_t *W, qlora_codebook_t codebook, const uint16_t *X,
+                                   int64_t M, const uint16_t *L1, const uint16_t *L2, int32_t r, float s,
+                                   uint16_t *Y, uint16_t *T, void *workspace, size_t ws_bytes, void *stream);
+qlora_status_t qlora_linear_bwd_cb(const qlora_nf4_weight_t *W, qlora_codebook_t codebook, const uint16_t *X,
+                                   const uint16_t *T, const uint16_t *dY, int64_t M, const uint16_t *L1,
+                                   const uint16_t *L2, int32_t r, float s, uint16_t *dX, float *dL1, float *dL2,
+                                   void *workspace, size_t ws_bytes, void *stream);
 
 /*
  * qlora_merge_adapter — merge a trained adapter into the frozen base
@@ -221,6 +245,19 @@ qlora_status_t qlora_merge_adapter(const qlora_nf4_weight_t *W, const uint16_t *
  */
 qlora_status_t qlora_merge_requantize(const qlora_nf4_weight_t *W, const uint16_t *L1, const uint16_t *L2,
                                       int32_t r, float s, uint8_t *codes_out, float *absmax_out, void *stream);
+
+/*
+ * The merge and the merge with re-quantization for a weight encoded with
+ * another codebook: W_hat uses the levels of `codebook` and the re-encoding
+ * uses the same codebook.  Otherwise as qlora_merge_adapter and
+ * qlora_merge_requantize (the QLORA_CB_NF4 cases).
+ */
+qlora_status_t qlora_merge_adapter_cb(const qlora_nf4_weight_t *W, qlora_codebook_t codebook, const uint16_t *L1,
+                                      const uint16_t *L2, int32_t r, float s, void *out, qlora_dtype_t out_dtype,
+                                      void *stream);
+qlora_status_t qlora_merge_requantize_cb(const qlora_nf4_weight_t *W, qlora_codebook_t codebook, const uint16_t *L1,
+                                         const uint16_t *L2, int32_t r, float s, uint8_t *codes_out,
+                                         float *absmax_out, void *stream);
 
 /*
  * qlora_adamw_step — one optimizer step on adapter parameters ([TT] §4 "One

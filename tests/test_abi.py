@@ -183,5 +183,61 @@ def test_codebook_entry_points_reject_bad_arguments():
     assert lib.qlora_dequantize_nodq(FAKE, FAKE, 10, 1, ODD, 0, None) == INV
     assert lib.qlora_dequantize_nodq(FAKE, FAKE, 0, 1, FAKE, 0, None) == INV
     W = weight()
-    W.codebook = 3
-    assert lib.qlora_merge_adapter(ctypes.byref(W), FAKE, FAKE, 8, 1.0, FAKE, 0, None) == INV
+    for cb in (3, -1):
+        assert lib.qlora_merge_adapter_cb(ctypes.byref(W), cb, FAKE, FAKE, 8, 1.0, FAKE, 0, None) == INV
+        assert lib.qlora_merge_requantize_cb(ctypes.byref(W), cb, FAKE, FAKE, 8, 1.0, FAKE, FAKE, None) == INV
+        assert lib.qlora_linear_fwd_cb(ctypes.byref(W), cb, FAKE, 4, FAKE, FAKE, 8, 2.0, FAKE, FAKE, FAKE,
+                                       1 << 30, None) == INV
+        assert lib.qlora_linear_bwd_cb(ctypes.byref(W), cb, FAKE, FAKE, FAKE, 4, FAKE, FAKE, 8, 2.0, FAKE, FAKE,
+                                       FAKE, FAKE, 1 << 30, None) == INV
+
+
+LAYOUT_PROBE = r"""
+#include <stddef.h>
+#include <stdio.h>
+#include "qlora_nf4.h"
+int main(void) {
+  printf("%zu %zu %zu %zu %zu %zu %zu\n", sizeof(qlora_nf4_weight_t), offsetof(qlora_nf4_weight_t, codes),
+         offsetof(qlora_nf4_weight_t, qabsmax), offsetof(qlora_nf4_weight_t, scale2),
+         offsetof(qlora_nf4_weight_t, mean), offsetof(qlora_nf4_weight_t, h), offsetof(qlora_nf4_weight_t, o));
+  return 0;
+}
+"""
+
+
+def test_weight_struct_layout(tmp_path):
+    """The weight descriptor is the boundary's plain struct: four pointers (codes,
+    qabsmax, scale2, mean) then the int64 sizes h and o, 48 bytes.  Checked as a C
+    compiler sees the header, and against the binding's ctypes mirror."""
+    src = tmp_path / "layout.c"
+    src.write_text(LAYOUT_PROBE)
+    exe = tmp_path / "layout"
+    subprocess.run(["gcc", "-std=c99", "-I", os.path.dirname(HEADER), str(src), "-o", str(exe)], check=True)
+    got = [int(v) for v in subprocess.run([str(exe)], capture_output=True, text=True, check=True).stdout.split()]
+    assert got == [48, 0, 8, 16, 24, 32, 40]
+    assert ctypes.sizeof(nf4.NF4WeightT) == 48
+    assert [getattr(nf4.NF4WeightT, f).offset for f in ("codes", "qabsmax", "scale2", "mean", "h", "o")] == \
+        [0, 8, 16, 24, 32, 40]
+
+
+def test_linear_bwd_token_split_bound():
+    """The adapter-gradient reduction splits the tokens into chunks whose operand slab
+    (chunk rows of max(h, o) bf16 values) stays below 2^31 bytes.  Observable on the host:
+    the workspace holds one float32 partial tile per split, so its size grows with the
+    number of splits once M passes the cap; a shape needing more than 65535 splits is
+    rejected before anything is launched."""
+    h, o, r = 22016, 8192, 64
+    cap = (0x7FFFFFF0 // (2 * h)) // 64 * 64          # 48768 tokens per split
+    ws = lambda M: nf4.workspace_size(nf4.QLORA_OP_LINEAR_BWD, M, h, o, r)
+    part = (h + o) * 64 * 4        # one split's float32 partial tiles (r = 64)
+    per_token = (64 + 64) * 2      # U and s*U, bf16, r padded to 16 and to 64
+    for M in (cap, 5 * cap + 1, 40 * cap, 100 * cap):
+        # without the cap about 3 splits would do (512 workgroups over 236 tiles)
+        splits = -(-M // cap)
+        assert ws(M) >= M * per_token + splits * part, M
+    assert ws(cap) < cap * per_token + 4 * part
+    big = weight(h=1 << 20, o=64)
+    M = 1 << 31                                         # 1024-token chunks -> 2^21 splits: unsupported
+    st = lib.qlora_linear_bwd(ctypes.byref(big), FAKE, FAKE, FAKE, M, FAKE, FAKE, 8, 1.0, FAKE, FAKE, FAKE, FAKE,
+                              ctypes.c_size_t(1 << 62), None)
+    assert st == nf4.QLORA_ERR_UNSUPPORTED

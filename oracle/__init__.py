@@ -27,4 +27,5 @@ from .nf4 import (  # noqa: F401
 from .linear import linear_fwd, linear_bwd, dequantized_weight, merged_weight  # noqa: F401
 from .ledger import storage_bits_per_weight, storage_bytes, lora_param_count  # noqa: F401
 from .optim import adamw_step  # noqa: F401
+from .glue import sigmoid, silu_gate_fwd, silu_gate_bwd, grad_sum  # noqa: F401
 from . import codebooks  # noqa: F401

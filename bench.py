@@ -1,23 +1,32 @@
 #!/usr/bin/env python3
 """Benchmark of the NF4 + LoRA linear layer hot path on one MI355X.
 
-Default workload: the LLaMA-7B-shaped attention projection (h = o = 4096,
-2048 tokens, LoRA rank 16, s = 2.0; base weight N(0, 0.02) with 0.1% x10
-outliers).  One step is one pass of the whole hot path on one batch:
-quantize the float32 weight to NF4, double-quantize its block scales,
-dequantize it to bf16, run the forward Y = X·W_hat + s·X·L1·L2 and the backward
-(dX, dL1, dL2).  All inputs are resident in HBM before timing starts.
+Default workload (block65b): one LLaMA-65B-shaped transformer block's seven NF4
+linears (q, k, v, o 8192 -> 8192; gate, up 8192 -> 22016; down 22016 -> 8192),
+LoRA rank 64 on each, s = 0.25, 2048 tokens.  One step is one pass of the whole
+hot path on one batch:
+  - codec: each float32 base weight quantized to NF4, its block scales
+    double-quantized, and the weight dequantized to bf16;
+  - forward: q, k, v, gate and up read the block input X; o reads a seeded
+    stand-in for the attention output (attention itself is not a QLoRA linear);
+    H = SiLU(gate) * up; down reads H;
+  - backward: down from a seeded output gradient; the SiLU gate's backward; gate
+    and up; o from a seeded output gradient; q, k, v from seeded stand-ins for
+    attention's backward; the block input's gradient is the sum of the five dX.
+All inputs are resident in HBM before timing starts.  mlp7b is the same step on
+a LLaMA-7B feed-forward (gate, up 4096 -> 11008, down 11008 -> 4096, 4096 tokens,
+r = 64, s = 0.25); attn_proj is one 4096 x 4096 linear (2048 tokens, r = 16, s = 2).
 
-`value` is the algorithmic forward+backward FLOP of the linear layer divided
-by the whole step's time (the codec stages are inside the step).  The `roofline`
-object reports the dominant kernel (the slower of the two fused dequant-GEMMs)
-timed in the timed steps with events the library records right around that
-kernel's launch (the forward GEMM in even steps, the dX GEMM in odd ones).  Every
-event recorded between two kernels holds the stream about 4.5 us, also without
-the system-scope fence (all events here are created with
-hipEventDisableSystemFence), so per-stage times come from a second pass of the
-same steps with HIP events between the stages.
-`cpu_baseline` times the CPU oracle on the same workload.
+`value` is the algorithmic forward+backward FLOP of the linears divided by the
+whole step's time (codec and glue are inside the step).  The `roofline` object
+reports the dominant kernel: the fused dequant-GEMM direction (forward or dX)
+with the larger total time, timed inside the timed steps with events the library
+records right around one launch (each step times one linear's forward GEMM and
+one linear's dX GEMM, in rotation).  Every event recorded between two kernels
+holds the stream about 4.5 us, also without the system-scope fence (all events
+here are created with hipEventDisableSystemFence), so per-stage times come from
+a second pass of the same steps with HIP events between the stages.
+`cpu_baseline` times the CPU oracle on a bounded sample of the same step.
 
 Other workloads (not the default line): --workload codec (quantize + double
 quant + dequantize of 4e9 bf16 weights), gemv (few-token forward on an
@@ -50,9 +59,12 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.txt")
 def parse_args():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="attn_proj", choices=["attn_proj", "codec", "gemv", "small", "merge", "adamw", "codebooks"])
+    ap.add_argument("--steps", type=int, default=None,
+                    help="timed steps (default 14 for the block workloads, 20 otherwise)")
+    ap.add_argument("--warmup", type=int, default=None, help="untimed steps (default 3 / 5)")
+    ap.add_argument("--workload", default="block65b",
+                    choices=["block65b", "mlp7b", "attn_proj", "codec", "gemv", "small", "merge", "adamw",
+                             "codebooks"])
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the CPU oracle timing")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="target CPU work for the oracle baseline")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -165,7 +177,7 @@ def read_traffic(kernel: str):
     if rec.get("source_sha256_16") != sha:
         return None
     key = f"{kernel}.bytes_per_launch"
-    return float(rec[key]) if key in rec else None
+    return round(float(rec[key])) if key in rec else None
 
 
 def cpu_oracle_attn_proj(wl_mod, target_s):
@@ -311,6 +323,296 @@ def bench_attn_proj(args, torch, nf4, wl):
                        "step": "quantize(fp32 W) + double_quant + dequantize(bf16) + linear_fwd + linear_bwd"},
             "tokens_per_s": round(M / (ms_per_step * 1e-3), 1), "roofline": roofline, "stages": stages_out}
     return line
+
+
+class BlockPlan:
+    """The linears of a transformer block, what each one reads and where its output
+    gradient comes from (the workload's seeded tensors, or the glue)."""
+
+    def __init__(self, wl, c):
+        self.c = c
+        names = [ls.name for ls in c.linears]
+        self.names = names
+        self.ffn = ("gate" in names and "up" in names and "down" in names)
+        self.x_readers = [i for i, n in enumerate(names) if n in ("q", "k", "v", "gate", "up")]
+        self.li = {n: i for i, n in enumerate(names)}
+        h0 = c.linears[self.x_readers[0]].h
+        self.h_in = h0
+        # seeded inputs: X for the readers of the block input, a stand-in for the
+        # attention output (o), gradients from outside the block for o, down and the
+        # attention backward into q, k, v
+        self.stand_in_inputs = {i: wl.TENSOR_AUX for i, n in enumerate(names) if n == "o"}
+        self.seeded_grads = [i for i, n in enumerate(names) if n in ("q", "k", "v", "o", "down")]
+
+    def order_fwd(self):
+        return [i for i, n in enumerate(self.names) if n != "down"] + [self.li["down"]]
+
+    def order_bwd(self):
+        first = [self.li["down"]]
+        rest = [self.li["gate"], self.li["up"]] + [i for i, n in enumerate(self.names) if n in ("o", "q", "k", "v")]
+        return first + rest
+
+
+def block_flops(c):
+    f = b = 0
+    for ls in c.linears:
+        fw, bw = linear_flops(c.tokens, ls.h, ls.o, ls.r)
+        f += fw
+        b += bw
+    return f, b
+
+
+def bench_block(args, torch, nf4, wl, c):
+    dev = "cuda:0"
+    M = c.tokens
+    plan = BlockPlan(wl, c)
+    L = len(c.linears)
+    host_w, w32, Ws, Ls = [], [], [], []
+    codec_bufs = []
+    for li, ls in enumerate(c.linears):
+        w = wl.base_weight(c, li)
+        host_w.append(w)
+        w32.append(w.to(dev))
+        n = ls.h * ls.o
+        nb = n // 64
+        codes = torch.empty(n // 2, dtype=torch.uint8, device=dev)
+        absmax = torch.empty(nb, dtype=torch.float32, device=dev)
+        qa = torch.empty(nb, dtype=torch.int8, device=dev)
+        s2 = torch.empty((nb + 255) // 256, dtype=torch.float32, device=dev)
+        mean = torch.empty(1, dtype=torch.float32, device=dev)
+        codec_bufs.append((codes, absmax, qa, s2, mean))
+        Ws.append(nf4.NF4Weight(codes, qa, s2, mean, ls.h, ls.o))
+        Ls.append(tuple(t.to(dev) for t in wl.lora_factors(c, li)))
+    nmax = max(ls.h * ls.o for ls in c.linears)
+    wdeq = torch.empty(nmax, dtype=torch.bfloat16, device=dev)
+    dq_ws = torch.empty(nf4.workspace_size(nf4.QLORA_OP_DOUBLE_QUANT, nmax // 64), dtype=torch.uint8, device=dev)
+    fws = torch.empty(max(nf4.workspace_size(nf4.QLORA_OP_LINEAR_FWD, M, ls.h, ls.o, ls.r) for ls in c.linears),
+                      dtype=torch.uint8, device=dev)
+    bws = torch.empty(max(nf4.workspace_size(nf4.QLORA_OP_LINEAR_BWD, M, ls.h, ls.o, ls.r) for ls in c.linears),
+                      dtype=torch.uint8, device=dev)
+    X = wl.activations(c, plan.x_readers[0]).to(dev)
+    inputs, grads = {}, {}
+    for li, ls in enumerate(c.linears):
+        if li in plan.x_readers:
+            inputs[li] = X
+        elif li in plan.stand_in_inputs:
+            inputs[li] = wl.activations(c, li, width=ls.h, tensor=wl.TENSOR_AUX).to(dev)
+    for li in plan.seeded_grads:
+        grads[li] = wl.activations(c, li, tensor=wl.TENSOR_DY).to(dev)
+    gi, ui, di = plan.li["gate"], plan.li["up"], plan.li["down"]
+    f_mid = c.linears[gi].o
+    Hbuf = torch.empty(M, f_mid, dtype=torch.bfloat16, device=dev)
+    inputs[di] = Hbuf
+    Y = {li: torch.empty(M, ls.o, dtype=torch.bfloat16, device=dev) for li, ls in enumerate(c.linears)}
+    T = {li: torch.empty(M, ls.r, dtype=torch.bfloat16, device=dev) for li, ls in enumerate(c.linears)}
+    dXs = {li: torch.empty(M, ls.h, dtype=torch.bfloat16, device=dev) for li, ls in enumerate(c.linears)}
+    dL1 = {li: torch.empty(ls.h, ls.r, dtype=torch.float32, device=dev) for li, ls in enumerate(c.linears)}
+    dL2 = {li: torch.empty(ls.r, ls.o, dtype=torch.float32, device=dev) for li, ls in enumerate(c.linears)}
+    dG = torch.empty(M, f_mid, dtype=torch.bfloat16, device=dev)
+    dU = torch.empty(M, f_mid, dtype=torch.bfloat16, device=dev)
+    grads[gi], grads[ui] = dG, dU
+    dX_block = torch.empty(M, plan.h_in, dtype=torch.bfloat16, device=dev)
+    E = HipEvents(torch).event  # fence-free timing events
+
+    def step(ev=None, kev=None, timed=None):
+        """One pass of the whole hot path.  ev: stage events (second pass); kev/timed:
+        the GEMM launches bracketed by the library's timing hook in this step."""
+        marks = []
+        rec = (lambda name: (ev[len(marks)].record(), marks.append(name))) if ev is not None else (lambda name: None)
+
+        def hook(kind, li, on):
+            if kev is None or timed is None or timed[kind] != li:
+                return
+            slot = nf4.TIMED_GEMM_FWD if kind == 0 else nf4.TIMED_GEMM_DX
+            nf4.qlora_set_timing_events(slot, *((kev[2 * kind], kev[2 * kind + 1]) if on else (None, None)))
+
+        rec("start")
+        for li, ls in enumerate(c.linears):
+            codes, absmax, qa, s2, mean = codec_bufs[li]
+            n = ls.h * ls.o
+            nf4.qlora_quantize(w32[li], codes, absmax)
+            nf4.qlora_double_quant(absmax, qa, s2, mean, dq_ws)
+            nf4.qlora_dequantize(codes, qa, s2, mean, n, torch.bfloat16, out=wdeq[:n])
+        rec("codec")
+        for li in plan.order_fwd():
+            if li == di:
+                nf4.qlora_silu_gate_fwd(Y[gi], Y[ui], Hbuf)
+                rec("glue_fwd")
+            ls = c.linears[li]
+            hook(0, li, True)
+            nf4.qlora_linear_fwd(Ws[li], inputs[li], Ls[li][0], Ls[li][1], ls.s, Y[li], T[li], fws)
+            hook(0, li, False)
+            rec("fwd_" + ls.name)
+        for li in plan.order_bwd():
+            ls = c.linears[li]
+            hook(1, li, True)
+            nf4.qlora_linear_bwd(Ws[li], inputs[li], T[li], grads[li], Ls[li][0], Ls[li][1], ls.s, dXs[li],
+                                 dL1[li], dL2[li], bws)
+            hook(1, li, False)
+            rec("bwd_" + ls.name)
+            if li == di:
+                nf4.qlora_silu_gate_bwd(Y[gi], Y[ui], dXs[di], dG, dU)
+                rec("glue_bwd")
+        nf4.qlora_grad_sum([dXs[li] for li in plan.x_readers], out=dX_block)
+        rec("grad_sum")
+        return marks
+
+    steps, warmup = args.steps, args.warmup
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    hev = HipEvents(torch)
+    kevs = [[hev.create() for _ in range(4)] for _ in range(steps)]
+    # step i times linear i % L's forward GEMM and linear (i + i // L) % L's dX GEMM
+    timed = [(i % L, (i + i // L) % L) for i in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step(None, kevs[i], timed[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    nf4.qlora_set_timing_events(nf4.TIMED_GEMM_FWD, None, None)
+    nf4.qlora_set_timing_events(nf4.TIMED_GEMM_DX, None, None)
+    gemm_ms = {0: {}, 1: {}}
+    for k, (lf, ld) in zip(kevs, timed):
+        gemm_ms[0].setdefault(lf, []).append(hev.elapsed_ms(k[0], k[1]))
+        gemm_ms[1].setdefault(ld, []).append(hev.elapsed_ms(k[2], k[3]))
+    hev.close()
+    # stage breakdown from a second pass (events between stages stall the stream)
+    nstage = 2 + 2 * L + 3
+    evs = [[E(enable_timing=True) for _ in range(nstage)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    names = None
+    for i in range(steps):
+        names = step(evs[i])
+    torch.cuda.synchronize()
+    st_ms = {}
+    for j in range(1, len(names)):
+        st_ms[names[j]] = statistics.mean(e[j - 1].elapsed_time(e[j]) for e in evs)
+
+    ms_per_step = wall * 1e3 / steps
+    fwd_f, bwd_f = block_flops(c)
+    stages = {"codec": {"ms": st_ms["codec"]}}
+    for li, ls in enumerate(c.linears):
+        fw, bw = linear_flops(M, ls.h, ls.o, ls.r)
+        stages["fwd_" + ls.name] = {"ms": st_ms["fwd_" + ls.name], "TFLOP/s": fw / st_ms["fwd_" + ls.name] / 1e9}
+        stages["bwd_" + ls.name] = {"ms": st_ms["bwd_" + ls.name], "TFLOP/s": bw / st_ms["bwd_" + ls.name] / 1e9}
+    nmid = M * f_mid
+    stages["glue_fwd"] = {"ms": st_ms["glue_fwd"], "GB/s": 6 * nmid / st_ms["glue_fwd"] / 1e6}
+    stages["glue_bwd"] = {"ms": st_ms["glue_bwd"], "GB/s": 10 * nmid / st_ms["glue_bwd"] / 1e6}
+    nsum = M * plan.h_in
+    stages["grad_sum"] = {"ms": st_ms["grad_sum"],
+                          "GB/s": 2 * nsum * (len(plan.x_readers) + 1) / st_ms["grad_sum"] / 1e6}
+    gem = {}
+    for kind, label in ((0, "fwd"), (1, "dx")):
+        # rate over the timed launches; a linear no step timed (fewer steps than
+        # linears) is counted at that rate in the per-step estimate
+        flop = lambda ls: 2 * M * ls.h * ls.o + 2 * M * ls.r * (ls.o if kind == 0 else ls.h)
+        t_f = sum(flop(c.linears[li]) * len(v) for li, v in gemm_ms[kind].items())
+        t_ms = sum(sum(v) for v in gemm_ms[kind].values())
+        rate = t_f / t_ms  # FLOP per ms
+        tot_ms = tot_f = 0.0
+        per = {}
+        for li, ls in enumerate(c.linears):
+            f = flop(ls)
+            v = gemm_ms[kind].get(li, [])
+            ms = statistics.mean(v) if v else f / rate
+            per[ls.name] = {"ms": round(ms, 5), "TFLOP/s": round(f / ms / 1e9, 2), "launches_timed": len(v)}
+            tot_ms += ms
+            tot_f += f
+        gem[label] = {"ms_per_step": tot_ms, "flop_per_step": tot_f, "per_linear": per,
+                      "timed_flop": t_f, "timed_ms": t_ms}
+    for v in stages.values():
+        for k in list(v):
+            v[k] = round(v[k], 4)
+    dom = "dx" if gem["dx"]["ms_per_step"] >= gem["fwd"]["ms_per_step"] else "fwd"
+    achieved = gem[dom]["timed_flop"] / gem[dom]["timed_ms"] / 1e9
+    kname = "nf4_gemm_kernel<256,256,%s>" % ("true" if dom == "dx" else "false")
+    roofline = {"bound": "mfma", "achieved": round(achieved, 3), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": read_traffic(f"{c.name}.gemm_{dom}"),
+                "kernel": kname, "kernel_ms_mean": round(gem[dom]["ms_per_step"] / L, 5),
+                "flop_per_launch_mean": gem[dom]["flop_per_step"] / L,
+                "launches_per_step": L}
+    value = (fwd_f + bwd_f) / (ms_per_step * 1e-3) / 1e12
+    line = {"metric": METRIC, "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1, "steps": steps,
+            "warmup": warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True,
+            "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+            "config": {"workload": c.name, "linears": {ls.name: [ls.h, ls.o] for ls in c.linears},
+                       "tokens": M, "r": c.linears[0].r, "s": c.linears[0].s,
+                       "step": "codec (quantize fp32 W + double_quant + dequantize bf16) of every linear + block "
+                               "forward (with SiLU gate) + block backward (with SiLU gate, input-gradient sum)"},
+            "tokens_per_s": round(M / (ms_per_step * 1e-3), 1), "roofline": roofline,
+            "gemm": {k: {"TFLOP/s": round(v["timed_flop"] / v["timed_ms"] / 1e9, 2),
+                         "ms_per_step": round(v["ms_per_step"], 4), "per_linear": v["per_linear"]}
+                     for k, v in gem.items()},
+            "stages": stages}
+    line["_cpu_sample_host"] = host_w  # consumed by the CPU baseline (removed before printing)
+    return line
+
+
+def cpu_oracle_block(wl, c, host_w, target_s, ns=128):
+    """The oracle on a bounded sample of the block step: every linear restricted to
+    its first `ns` outputs (rows [0, ns) of the [o][h] weight, columns [0, ns) of L2)
+    with all tokens, so the codec and the matmuls shrink by the same factor.  The SiLU
+    gate runs on the sampled gate/up columns; down reads a seeded stand-in for its
+    full-width input, q/k/v/o and down take seeded output gradients and gate/up the
+    glue's.  Repeated to at least target_s seconds; value = the sample's linear FLOP
+    per second."""
+    import numpy as np
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = os.cpu_count() or 1
+    plan = BlockPlan(wl, c)
+    M = c.tokens
+    f64 = lambda t: t.float().numpy().astype(np.float64)
+    X = f64(wl.activations(c, plan.x_readers[0]))
+    gi, ui, di = plan.li["gate"], plan.li["up"], plan.li["down"]
+    per = []
+    for li, ls in enumerate(c.linears):
+        w = host_w[li][:ns].numpy().ravel()
+        l1, l2 = wl.lora_factors(c, li)
+        L1, L2 = l1.float().numpy(), l2.float().numpy()[:, :ns]
+        if li in plan.x_readers:
+            xin = X
+        elif li == di:
+            xin = f64(wl.activations(c, li, width=ls.h, tensor=wl.TENSOR_AUX))
+        else:
+            xin = f64(wl.activations(c, li, width=ls.h, tensor=wl.TENSOR_AUX))
+        dy = f64(wl.activations(c, li, tensor=wl.TENSOR_DY))[:, :ns] if li in plan.seeded_grads else None
+        per.append((ls, w, L1, L2, xin, dy))
+    dH = f64(wl.activations(c, di, width=c.linears[gi].o, tensor=wl.TENSOR_DY))[:, :ns]
+    reps, t_total = 0, 0.0
+    while t_total < target_s and reps < 50:
+        t0 = time.perf_counter()
+        outs = {}
+        for li, (ls, w, L1, L2, xin, dy) in enumerate(per):
+            p, a = oracle.quantize(w)
+            q, s2, mean = oracle.double_quant(a)
+            oracle.dequantize(p, q, s2, mean, w.size, out="bf16")
+            wh = oracle.dequantized_weight(p, q, s2, mean, ls.h, ns)
+            outs[li] = (wh, oracle.linear_fwd(wh, xin, L1, L2, ls.s)[0])
+        oracle.silu_gate_fwd(outs[gi][1], outs[ui][1])
+        dG, dU = oracle.silu_gate_bwd(outs[gi][1], outs[ui][1], dH)
+        dxs = []
+        for li, (ls, w, L1, L2, xin, dy) in enumerate(per):
+            g = dG if li == gi else (dU if li == ui else dy)
+            dx, _, _ = oracle.linear_bwd(outs[li][0], xin, g, L1, L2, ls.s)
+            if li in plan.x_readers:
+                dxs.append(dx)
+        oracle.grad_sum(dxs)
+        t_total += time.perf_counter() - t0
+        reps += 1
+    flops = sum(sum(linear_flops(M, ls.h, ns, ls.r)) for ls in c.linears)
+    return {"value": round(flops * reps / t_total / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"the whole step restricted to each linear's first {ns} outputs (all {M} tokens; codec of "
+                      f"{ns} weight rows per linear, fp64 forward and backward, SiLU gate on the sampled columns, "
+                      f"input-gradient sum) x {reps} reps, {t_total:.1f} s; codec single-threaded NumPy, fp64 "
+                      f"matmuls on {threads} BLAS threads; value = sampled linear FLOP / time",
+            "s_per_sample": round(t_total / reps, 4)}
 
 
 def bench_codec(args, torch, nf4, wl):
@@ -635,6 +937,11 @@ def main():
         return 1
     import bit_quantized_fine_nf4_amd as nf4
     import workloads as wl
+    block = args.workload in ("block65b", "mlp7b")
+    if args.steps is None:
+        args.steps = 14 if block else 20
+    if args.warmup is None:
+        args.warmup = 3 if block else 5
     if args.copy_calibration:
         src = torch.ones(1 << 28, dtype=torch.float32, device="cuda:0")
         dst = torch.empty_like(src)
@@ -642,10 +949,17 @@ def main():
         torch.cuda.synchronize()
         del src, dst
     fn = {"attn_proj": bench_attn_proj, "codec": bench_codec, "gemv": bench_gemv, "small": bench_small,
-          "merge": bench_merge, "adamw": bench_adamw, "codebooks": bench_codebooks}[args.workload]
+          "merge": bench_merge, "adamw": bench_adamw, "codebooks": bench_codebooks,
+          "block65b": lambda *a: bench_block(*a, wl.C5), "mlp7b": lambda *a: bench_block(*a, wl.C3)}[args.workload]
     line = fn(args, torch, nf4, wl)
-    if args.workload == "attn_proj" and not args.no_cpu_baseline:
+    host_w = line.pop("_cpu_sample_host", None)
+    if args.no_cpu_baseline:
+        line["cpu_baseline"] = None
+    elif args.workload == "attn_proj":
         line["cpu_baseline"] = cpu_oracle_attn_proj(wl, args.cpu_seconds)
+    elif block:
+        line["cpu_baseline"] = cpu_oracle_block(wl, wl.C5 if args.workload == "block65b" else wl.C3, host_w,
+                                                args.cpu_seconds)
     else:
         line["cpu_baseline"] = None
     print(json.dumps(line), flush=True)

@@ -28,6 +28,7 @@ EXPORTED = ("qlora_quantize", "qlora_double_quant", "qlora_dequantize", "qlora_l
             "qlora_linear_bwd", "qlora_merge_adapter", "qlora_merge_requantize", "qlora_adamw_step",
             "qlora_quantize_cb", "qlora_dequantize_cb", "qlora_dequantize_nodq", "qlora_codebook_levels",
             "qlora_linear_fwd_cb", "qlora_linear_bwd_cb", "qlora_merge_adapter_cb", "qlora_merge_requantize_cb",
+            "qlora_silu_gate_fwd", "qlora_silu_gate_bwd", "qlora_grad_sum",
             "qlora_workspace_size",
             "qlora_status_string", "qlora_nf4_levels", "qlora_set_timing_events")
 
@@ -67,6 +68,9 @@ def _load():
     L.qlora_linear_bwd_cb.argtypes = [W, st] + L.qlora_linear_bwd.argtypes[1:]
     L.qlora_merge_adapter_cb.argtypes = [W, st] + L.qlora_merge_adapter.argtypes[1:]
     L.qlora_merge_requantize_cb.argtypes = [W, st] + L.qlora_merge_requantize.argtypes[1:]
+    L.qlora_silu_gate_fwd.argtypes = [vp, vp, i64, vp, vp]
+    L.qlora_silu_gate_bwd.argtypes = [vp, vp, vp, i64, vp, vp, vp]
+    L.qlora_grad_sum.argtypes = [ctypes.POINTER(vp), i32, i64, vp, vp]
     L.qlora_adamw_step.argtypes = [vp, vp, vp, vp, i64, i64, f32, f32, f32, f32, f32, vp, vp]
     L.qlora_workspace_size.argtypes = [st, i64, i64, i64, i32, ctypes.POINTER(sz)]
     L.qlora_status_string.argtypes = [st]
@@ -341,3 +345,49 @@ def qlora_linear_bwd(W: NF4Weight, X: Optional[torch.Tensor], T: Optional[torch.
                   0 if workspace is None else workspace.numel(), _stream(dev)),
            "qlora_linear_bwd")
     return dX, dL1, dL2
+
+
+# ---------------------------------------------------------------------------
+# Block glue between the linears
+# ---------------------------------------------------------------------------
+
+def _same(*ts):
+    n = ts[0].numel()
+    for t in ts:
+        if t.dtype != torch.bfloat16 or t.numel() != n:
+            raise ValueError("glue tensors are bf16 of one size")
+    return n
+
+
+def qlora_silu_gate_fwd(G: torch.Tensor, U: torch.Tensor, H: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """H = SiLU(G) * U (bf16, elementwise)."""
+    _dev_check(G, U, H)
+    if H is None:
+        H = torch.empty_like(G)
+    n = _same(G, U, H)
+    _check(lib.qlora_silu_gate_fwd(_ptr(G), _ptr(U), n, _ptr(H), _stream(G.device)), "qlora_silu_gate_fwd")
+    return H
+
+
+def qlora_silu_gate_bwd(G: torch.Tensor, U: torch.Tensor, dH: torch.Tensor, dG: Optional[torch.Tensor] = None,
+                        dU: Optional[torch.Tensor] = None):
+    """(dG, dU) of H = SiLU(G) * U for the upstream gradient dH."""
+    _dev_check(G, U, dH, dG, dU)
+    dG = torch.empty_like(G) if dG is None else dG
+    dU = torch.empty_like(U) if dU is None else dU
+    n = _same(G, U, dH, dG, dU)
+    _check(lib.qlora_silu_gate_bwd(_ptr(G), _ptr(U), _ptr(dH), n, _ptr(dG), _ptr(dU), _stream(G.device)),
+           "qlora_silu_gate_bwd")
+    return dG, dU
+
+
+def qlora_grad_sum(parts, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """out = parts[0] + ... + parts[k-1] (bf16, float32 sum in order, one rounding)."""
+    parts = list(parts)
+    _dev_check(*parts, out)
+    if out is None:
+        out = torch.empty_like(parts[0])
+    n = _same(*parts, out)
+    arr = (ctypes.c_void_p * len(parts))(*[p.data_ptr() for p in parts])
+    _check(lib.qlora_grad_sum(arr, len(parts), n, _ptr(out), _stream(out.device)), "qlora_grad_sum")
+    return out

@@ -4,6 +4,7 @@
 
 #include "../../include/qlora_nf4.h"
 #include "codec.h"
+#include "glue.h"
 #include "linear.h"
 #include "optim.h"
 
@@ -106,6 +107,33 @@ qlora_status_t qlora_adamw_step(float *param, const float *grad, float *exp_avg,
   if (!(weight_decay >= 0.0f) || !std::isfinite(weight_decay)) return QLORA_ERR_INVALID_VALUE;
   const AdamwArgs a{param, grad, exp_avg, exp_avg_sq, param_bf16, n, step, lr, beta1, beta2, eps, weight_decay};
   return launch_status(launch_adamw(a, reinterpret_cast<hipStream_t>(stream)));
+}
+
+qlora_status_t qlora_silu_gate_fwd(const uint16_t *G, const uint16_t *U, int64_t n, uint16_t *H, void *stream) {
+  if (!G || !U || !H || n < 1) return QLORA_ERR_INVALID_VALUE;
+  if (!aligned(G, 16) || !aligned(U, 16) || !aligned(H, 16)) return QLORA_ERR_INVALID_VALUE;
+  return launch_status(launch_silu_gate_fwd(G, U, n, H, reinterpret_cast<hipStream_t>(stream)));
+}
+
+qlora_status_t qlora_silu_gate_bwd(const uint16_t *G, const uint16_t *U, const uint16_t *dH, int64_t n, uint16_t *dG,
+                                   uint16_t *dU, void *stream) {
+  if (!G || !U || !dH || !dG || !dU || n < 1) return QLORA_ERR_INVALID_VALUE;
+  if (!aligned(G, 16) || !aligned(U, 16) || !aligned(dH, 16) || !aligned(dG, 16) || !aligned(dU, 16))
+    return QLORA_ERR_INVALID_VALUE;
+  if (dG == dU) return QLORA_ERR_INVALID_VALUE;
+  return launch_status(launch_silu_gate_bwd(G, U, dH, n, dG, dU, reinterpret_cast<hipStream_t>(stream)));
+}
+
+qlora_status_t qlora_grad_sum(const uint16_t *const *parts, int32_t k, int64_t n, uint16_t *out, void *stream) {
+  if (!parts || !out || k < 1 || k > kMaxSumParts || n < 1) return QLORA_ERR_INVALID_VALUE;
+  if (!aligned(out, 16)) return QLORA_ERR_INVALID_VALUE;
+  SumParts sp{};
+  sp.k = k;
+  for (int i = 0; i < k; ++i) {
+    if (!parts[i] || !aligned(parts[i], 16)) return QLORA_ERR_INVALID_VALUE;
+    sp.p[i] = parts[i];
+  }
+  return launch_status(launch_grad_sum(sp, n, out, reinterpret_cast<hipStream_t>(stream)));
 }
 
 qlora_status_t qlora_set_timing_events(int32_t kernel, void *start, void *stop) {

@@ -284,6 +284,32 @@ qlora_status_t qlora_adamw_step(float *param, const float *grad, float *exp_avg,
                                 int64_t step, float lr, float beta1, float beta2, float eps, float weight_decay,
                                 uint16_t *param_bf16, void *stream);
 
+/*
+ * Block glue: the elementwise steps between the NF4 linears of a transformer
+ * block.  [MC] "A closer look: Design choices and memory costs" puts adapters
+ * on every linear of the block, attention and feed-forward; the feed-forward of
+ * the LLaMA models the pages name is gated, its gate and up projections G and
+ * U meeting in H = SiLU(G) * U with SiLU(g) = g / (1 + exp(-g)) before the down
+ * projection.  All tensors are n bf16 values in any matching shape, 16-byte
+ * aligned; arithmetic is float32, each output rounded once to nearest even.
+ * Outputs must not overlap the inputs (qlora_grad_sum excepted, see there).
+ *
+ * qlora_silu_gate_fwd  H = SiLU(G) * U.
+ * qlora_silu_gate_bwd  for the upstream gradient dH:
+ *                        dU = dH * SiLU(G)
+ *                        dG = dH * U * sigmoid(G) * (1 + G * (1 - sigmoid(G)))
+ *                      dG and dU must be different buffers.
+ * qlora_grad_sum       out = parts[0] + ... + parts[k-1], summed in that order:
+ *                      the gradient of an input that several linears read (the
+ *                      block input feeds q, k, v, gate and up).  `parts` is a
+ *                      HOST array of k device pointers, 1 <= k <= 8; `out` may
+ *                      be one of them (exactly, not a partial overlap).
+ */
+qlora_status_t qlora_silu_gate_fwd(const uint16_t *G, const uint16_t *U, int64_t n, uint16_t *H, void *stream);
+qlora_status_t qlora_silu_gate_bwd(const uint16_t *G, const uint16_t *U, const uint16_t *dH, int64_t n, uint16_t *dG,
+                                   uint16_t *dU, void *stream);
+qlora_status_t qlora_grad_sum(const uint16_t *const *parts, int32_t k, int64_t n, uint16_t *out, void *stream);
+
 /* Workspace bytes an entry point needs (always a multiple of 256; may be 0). */
 qlora_status_t qlora_workspace_size(qlora_op_t op, int64_t a, int64_t b, int64_t c, int32_t r,
                                     size_t *bytes);

@@ -241,3 +241,20 @@ def test_linear_bwd_token_split_bound():
     st = lib.qlora_linear_bwd(ctypes.byref(big), FAKE, FAKE, FAKE, M, FAKE, FAKE, 8, 1.0, FAKE, FAKE, FAKE, FAKE,
                               ctypes.c_size_t(1 << 62), None)
     assert st == nf4.QLORA_ERR_UNSUPPORTED
+
+
+def test_glue_entry_points_reject_bad_arguments():
+    f, b, sm = lib.qlora_silu_gate_fwd, lib.qlora_silu_gate_bwd, lib.qlora_grad_sum
+    assert f(None, FAKE, 10, FAKE, None) == INV
+    assert f(FAKE, FAKE, 0, FAKE, None) == INV
+    assert f(FAKE, ODD, 10, FAKE, None) == INV
+    assert b(FAKE, FAKE, FAKE, 10, FAKE, None, None) == INV
+    assert b(FAKE, FAKE, FAKE, 10, FAKE, FAKE, None) == INV        # dG and dU the same buffer
+    assert b(FAKE, FAKE, ODD, 10, FAKE, ctypes.c_void_p(0x200000), None) == INV
+    arr = (ctypes.c_void_p * 9)(*([FAKE.value] * 9))
+    assert sm(arr, 0, 10, FAKE, None) == INV
+    assert sm(arr, 9, 10, FAKE, None) == INV
+    assert sm(arr, 2, 0, FAKE, None) == INV
+    assert sm(None, 2, 10, FAKE, None) == INV
+    bad = (ctypes.c_void_p * 2)(FAKE.value, ODD.value)
+    assert sm(bad, 2, 10, FAKE, None) == INV

@@ -1,8 +1,11 @@
 """GPU parity of qlora_linear_fwd / qlora_linear_bwd against the float64 oracle:
 relative Frobenius error <= 1e-2 and max-abs error <= 2e-2 * max|ref| for Y, T,
-dX, dL1, dL2.  Small shapes span several tiles with ragged token counts; the
-workload shapes run at full size, compared in full where the oracle is quick
-and on sampled token rows otherwise (dL1 and dL2 are always compared in full)."""
+dX, dL1, dL2, every output compared in full against oracle.linear_fwd /
+oracle.linear_bwd.  Small shapes span several tiles with ragged token counts; the
+workload shapes run at full size.  The rank-r term is isolated on each fused-GEMM
+tile size (W = 0, and adapters large enough to be 25-70 % of the output, with one
+and two rank-r K steps), since with the workloads' own small adapters it is about
+1 % of Y and dX and a 1e-2 check could not see it."""
 import numpy as np
 import pytest
 import torch
@@ -93,34 +96,14 @@ def test_linear_workload_c2():
     check_full(w, l1, l2, wl.activations(c, 0), wl.activations(c, 0, tensor=wl.TENSOR_DY), ls.s, c.name)
 
 
-def check_sampled_tensors(w, l1, l2, x, dy, s, label, seed, nrows=48):
-    """Y and dX on sampled token rows (the first and last included), T/dL1/dL2 in full."""
-    print(f"linear {label} sampled", flush=True)
-    tokens = x.shape[0]
-    Y, T, dX, dL1, dL2 = gpu_run(w, l1, l2, x, dy, s)
-    wh = oracle_weight(w)
-    rows = np.unique(np.concatenate([np.random.default_rng(seed).integers(0, tokens, nrows), [0, tokens - 1]]))
-    X, DY = to_np(x).astype(np.float64), to_np(dy).astype(np.float64)
-    L1, L2 = to_np(l1), to_np(l2)
-    rY, rT = oracle.linear_fwd(wh, X[rows], L1, L2, s)
-    rdX, _, _ = oracle.linear_bwd(wh, X[rows], DY[rows], L1, L2, s)
-    assert_close("Y[rows]", to_np(Y)[rows], rY)
-    assert_close("dX[rows]", to_np(dX)[rows], rdX)
-    T64 = X @ L1.astype(np.float64)
-    U64 = DY @ L2.astype(np.float64).T
-    assert_close("T", to_np(T), T64)
-    assert_close("dL1", to_np(dL1), s * (X.T @ U64))
-    assert_close("dL2", to_np(dL2), s * (T64.T @ DY))
-
-
-def check_sampled(c, li, nrows=48):
-    """Full-size linear of a workload: Y and dX on sampled token rows, T/dL1/dL2 in full."""
+def check_workload(c, li):
+    """Full-size linear of a workload, every output compared in full."""
     ls = c.linears[li]
     w = wl.base_weight(c, li)
     l1, l2 = wl.lora_factors(c, li)
     x = wl.activations(c, li)
     dy = wl.activations(c, li, tensor=wl.TENSOR_DY)
-    check_sampled_tensors(w, l1, l2, x, dy, ls.s, f"{c.name}/{ls.name}", li, nrows)
+    check_full(w, l1, l2, x, dy, ls.s, f"{c.name}/{ls.name}")
 
 
 def test_linear_256x128_tiles_ragged():
@@ -137,17 +120,45 @@ def test_linear_256x256_tiles_ragged():
     directions, with partial last tiles along M (184 rows) and N (64 columns)."""
     M, h, o, r, s = 3000, 5184, 5184, 16, 0.5
     w, l1, l2, x, dy = wl.small_linear(h, o, r, M, seed=3000)
-    check_sampled_tensors(w, l1, l2, x, dy, s, f"M={M} h={h} o={o} r={r} (256x256 tiles)", 3)
+    check_full(w, l1, l2, x, dy, s, f"M={M} h={h} o={o} r={r} (256x256 tiles)")
+
+
+# The rank-r K steps of each fused-GEMM tile size, isolated.  (M, h, o) picks the
+# tile: 4096 x 4096 x 4096 and 3000 x 5184 x 5184 the 256x256 tiles, 2000 x 2624 x 2624
+# the 256x128 tiles (both directions).  r = 100 and 128 take two rank-r K steps.
+@pytest.mark.parametrize("r,s", [(16, 2.0), (64, 0.25), (128, 0.5)])
+def test_rank_r_only_256x256_tiles(r, s):
+    """W = 0: Y = s X L1 L2 and dX = s dY L2^T L1^T come from the rank-r steps alone."""
+    M, h, o = 4096, 4096, 4096
+    w, l1, l2, x, dy = wl.small_linear(h, o, r, M, seed=40 + r, lora_std=0.05)
+    check_full(torch.zeros_like(w), l1, l2, x, dy, s, f"W=0 M={M} h={h} o={o} r={r} (256x256 tiles)")
+
+
+@pytest.mark.parametrize("M,h,o,r,s", [(2000, 2624, 2624, 100, 0.5), (2000, 2624, 2624, 128, 0.5),
+                                       (3000, 5184, 5184, 100, 0.5), (3000, 5184, 5184, 128, 0.25)])
+def test_large_adapter_wide_tiles(M, h, o, r, s):
+    """Adapters with std 0.05: the rank-r term is 25-70 % of Y and dX, so a dropped or
+    mis-scaled K step fails the 1e-2 check."""
+    w, l1, l2, x, dy = wl.small_linear(h, o, r, M, seed=M + r, lora_std=0.05)
+    check_full(w, l1, l2, x, dy, s, f"M={M} h={h} o={o} r={r} lora_std=0.05")
+
+
+def test_large_adapter_c5_shape():
+    """The 65B block's attention projection shape (2048 x 8192 x 8192, r = 64, s = 0.25,
+    256x256 tiles) with adapters of std 0.05: the rank-r term is about 25 % of Y."""
+    M, h, o, r, s = 2048, 8192, 8192, 64, 0.25
+    w, l1, l2, x, dy = wl.small_linear(h, o, r, M, seed=65, lora_std=0.05)
+    check_full(w, l1, l2, x, dy, s, f"C5 shape M={M} h={h} o={o} r={r} lora_std=0.05")
 
 
 @pytest.mark.parametrize("li", [0, 2])
-def test_linear_workload_c3_sampled(li):
-    check_sampled(wl.C3, li)
+def test_linear_workload_c3(li):
+    check_workload(wl.C3, li)
 
 
 @pytest.mark.parametrize("li", [0, 4, 6])
-def test_linear_workload_c5_sampled(li):
-    check_sampled(wl.C5, li)
+def test_linear_workload_c5(li):
+    check_workload(wl.C5, li)
 
 
 @pytest.mark.parametrize("m", wl.C4_GEMV_TOKENS)
@@ -283,3 +294,28 @@ def test_timing_hook_slots(M, expect):
     for k in expect:
         assert hev.elapsed(*evs[k]) == (0, first[k])
     hev.close()
+
+
+def test_few_token_backward_many_gradient_tiles():
+    """M = 1 with h + o > 131072 (h = 128, o = 131072, r = 8): the adapter gradients have
+    1025 tiles, more than the one 1024-thread workgroup of the rank-r launch that clears
+    their split counters.  The workspace starts as garbage and is reused by a second call
+    (which then finds the first call's counts), and both calls must match the oracle."""
+    M, h, o, r, s = 1, 128, 131072, 8, 2.0
+    print(f"few-token bwd M={M} h={h} o={o} r={r} (1025 gradient tiles)", flush=True)
+    w, l1, l2, x, dy = wl.small_linear(h, o, r, M, seed=131, lora_std=0.05)
+    W = nf4.quantize_weight(w.to(DEV))
+    X, dY, L1, L2 = x.to(DEV), dy.to(DEV), l1.to(DEV), l2.to(DEV)
+    Y, T = nf4.qlora_linear_fwd(W, X, L1, L2, s)
+    ws = torch.full((nf4.workspace_size(nf4.QLORA_OP_LINEAR_BWD, M, h, o, r),), 0x7F, dtype=torch.uint8,
+                    device=DEV)
+    wh = oracle_weight(w)
+    rdX, rdL1, rdL2 = oracle.linear_bwd(wh, to_np(x).astype(np.float64), to_np(dy).astype(np.float64),
+                                        to_np(l1), to_np(l2), s)
+    for call in range(2):
+        dX, dL1, dL2 = nf4.qlora_linear_bwd(W, X, T, dY, L1, L2, s, workspace=ws)
+        torch.cuda.synchronize()
+        print(f" call {call}", flush=True)
+        assert_close("dX", to_np(dX), rdX)
+        assert_close("dL1", to_np(dL1), rdL1)
+        assert_close("dL2", to_np(dL2), rdL2)

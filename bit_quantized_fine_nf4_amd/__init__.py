@@ -28,7 +28,7 @@ EXPORTED = ("qlora_quantize", "qlora_double_quant", "qlora_dequantize", "qlora_l
             "qlora_linear_bwd", "qlora_merge_adapter", "qlora_merge_requantize", "qlora_adamw_step",
             "qlora_quantize_cb", "qlora_dequantize_cb", "qlora_dequantize_nodq", "qlora_codebook_levels",
             "qlora_linear_fwd_cb", "qlora_linear_bwd_cb", "qlora_merge_adapter_cb", "qlora_merge_requantize_cb",
-            "qlora_silu_gate_fwd", "qlora_silu_gate_bwd", "qlora_grad_sum",
+            "qlora_silu_gate_fwd", "qlora_silu_gate_bwd", "qlora_grad_sum", "qlora_double_quant_noalloc",
             "qlora_workspace_size",
             "qlora_status_string", "qlora_nf4_levels", "qlora_set_timing_events")
 
@@ -53,6 +53,7 @@ def _load():
     sz = ctypes.c_size_t
     L.qlora_quantize.argtypes = [vp, st, i64, vp, vp, vp]
     L.qlora_double_quant.argtypes = [vp, i64, vp, vp, vp, vp, sz, vp]
+    L.qlora_double_quant_noalloc.argtypes = [vp, i64, vp, vp, vp, vp]
     L.qlora_dequantize.argtypes = [vp, vp, vp, vp, i64, vp, st, vp]
     L.qlora_quantize_cb.argtypes = [vp, st, i64, st, vp, vp, vp]
     L.qlora_dequantize_cb.argtypes = [vp, vp, vp, vp, i64, st, vp, st, vp]

@@ -189,6 +189,18 @@ qlora_status_t qlora_double_quant(const float *absmax, int64_t nblocks, int8_t *
                                            reinterpret_cast<hipStream_t>(stream)));
 }
 
+qlora_status_t qlora_double_quant_noalloc(const float *absmax, int64_t nblocks, int8_t *qabsmax, float *scale2,
+                                          float *mean, void *stream) {
+  if (!absmax || !qabsmax || !scale2 || !mean) return QLORA_ERR_INVALID_VALUE;
+  if (nblocks < 1 || nblocks >= (int64_t(1) << 32)) return QLORA_ERR_INVALID_VALUE;
+  if (!aligned(absmax, 16) || !aligned(qabsmax, 4) || !aligned(scale2, 4) || !aligned(mean, 4))
+    return QLORA_ERR_INVALID_VALUE;
+  const hipError_t e = launch_double_quant_noalloc(absmax, nblocks, qabsmax, scale2, mean,
+                                                   reinterpret_cast<hipStream_t>(stream));
+  if (e == hipErrorInvalidDevice) return QLORA_ERR_INVALID_VALUE;
+  return launch_status(e);
+}
+
 qlora_status_t qlora_dequantize_cb(const uint8_t *codes, const int8_t *qabsmax, const float *scale2,
                                    const float *mean, int64_t n, qlora_codebook_t codebook, void *out,
                                    qlora_dtype_t out_dtype, void *stream) {

@@ -6,7 +6,9 @@
 
 #include "codec.h"
 
+#include <mutex>
 #include <type_traits>
+#include <vector>
 
 namespace ql {
 
@@ -744,6 +746,48 @@ hipError_t launch_quantize(const void *w, bool bf16, int64_t n, uint8_t *codes, 
 }
 
 size_t dq_workspace_bytes() { return ((size_t)kDqGrid * kLimbs * 8 + 255) / 256 * 256; }
+
+// The partial-sum slots of the allocation-free double quantization: one slot of
+// kLimbs limbs per partial-sum workgroup, whatever the number of scales (the
+// partial pass never has more than kDqGrid workgroups).  48 KB on every GPU the
+// library runs on, held until the process ends.  Every slot a call's chunk pass
+// reads is written by the same call's partial pass first, so nothing is cleared;
+// calls that overlap on one GPU race on it.
+static __device__ __align__(256) unsigned long long scratch[kDqGrid * kLimbs];
+
+namespace {
+std::mutex g_scratch_mu;
+std::vector<unsigned long long *> g_scratch_ptr;  // per device: the device address of `scratch`
+}  // namespace
+
+hipError_t dq_scratch(hipStream_t st, unsigned long long **out) {
+  int cur = -1, sdev = -1;
+  hipError_t e = hipGetDevice(&cur);
+  if (e != hipSuccess) return e;
+  e = hipStreamGetDevice(st, &sdev);
+  if (e != hipSuccess) return e;
+  if (sdev != cur) return hipErrorInvalidDevice;  // the kernels must see this device's copy
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if ((int)g_scratch_ptr.size() <= cur) g_scratch_ptr.resize(cur + 1, nullptr);
+  if (!g_scratch_ptr[cur]) {
+    // in host code `scratch` names a host-side stand-in: the device copy's address
+    // comes from the runtime, once per device, with that device current
+    void *p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    g_scratch_ptr[cur] = reinterpret_cast<unsigned long long *>(p);
+  }
+  *out = g_scratch_ptr[cur];
+  return hipSuccess;
+}
+
+hipError_t launch_double_quant_noalloc(const float *absmax, int64_t nb, int8_t *qabsmax, float *scale2,
+                                       float *mean, hipStream_t st) {
+  unsigned long long *ws = nullptr;
+  const hipError_t e = dq_scratch(st, &ws);
+  if (e != hipSuccess) return e;
+  return launch_double_quant(absmax, nb, qabsmax, scale2, mean, ws, st);
+}
 
 hipError_t launch_double_quant(const float *absmax, int64_t nb, int8_t *qabsmax, float *scale2,
                                float *mean, void *ws, hipStream_t st) {

@@ -131,6 +131,24 @@ qlora_status_t qlora_double_quant(const float *absmax, int64_t nblocks, int8_t *
                                   float *mean, void *workspace, size_t ws_bytes, void *stream);
 
 /*
+ * qlora_double_quant_noalloc — qlora_double_quant without a workspace, for
+ * callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc).  Same arguments,
+ * results and errors as qlora_double_quant minus workspace/ws_bytes; it
+ * allocates nothing and calls no allocating routine.  Its partial sums live in
+ * a 48 KB static array the library keeps on each GPU it runs on until the
+ * process ends; every accepted size (1 <= nblocks < 2^32) fits in it, since the
+ * partial-sum pass never uses more than 512 slots.  The first call on a device
+ * looks the array's address up once (hipGetSymbolAddress).  `stream` must
+ * belong to the current device (QLORA_ERR_INVALID_VALUE otherwise).  All
+ * calls on one GPU share the array: calls that overlap in time on one GPU (on
+ * different streams) race and give wrong results; calls ordered on one stream
+ * are safe.
+ */
+qlora_status_t qlora_double_quant_noalloc(const float *absmax, int64_t nblocks, int8_t *qabsmax, float *scale2,
+                                          float *mean, void *stream);
+
+/*
  * qlora_dequantize — rebuild n weights ([MC] "1. NormalFloat": codes are
  * dequantized to BF16 for computation; [GO] "The core move").
  *  a_hat = fp32(fp32(qabsmax * scale2) + mean)      (no fused multiply-add)

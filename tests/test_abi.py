@@ -258,3 +258,12 @@ def test_glue_entry_points_reject_bad_arguments():
     assert sm(None, 2, 10, FAKE, None) == INV
     bad = (ctypes.c_void_p * 2)(FAKE.value, ODD.value)
     assert sm(bad, 2, 10, FAKE, None) == INV
+
+
+def test_double_quant_noalloc_rejects_bad_arguments():
+    dq = lib.qlora_double_quant_noalloc
+    assert dq(None, 10, FAKE, FAKE, FAKE, None) == INV
+    assert dq(FAKE, 0, FAKE, FAKE, FAKE, None) == INV
+    assert dq(FAKE, 1 << 32, FAKE, FAKE, FAKE, None) == INV
+    assert dq(ODD, 10, FAKE, FAKE, FAKE, None) == INV
+    assert dq(FAKE, 10, FAKE, None, FAKE, None) == INV

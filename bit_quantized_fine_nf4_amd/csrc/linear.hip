@@ -74,14 +74,12 @@ QL_DEV __amdgpu_buffer_rsrc_t gv_rsrc(const void *base, int64_t bytes) {
 
 }  // namespace
 
-// Cross-workgroup split reduction.  Partials travel through device-coherent
-// accesses (agent-scope stores and loads bypass the per-XCD L2s), so no
-// device-wide cache writeback is needed: a workgroup stores its partials,
-// waits until they are acknowledged, and counts itself in; the one that brings
-// the count to `splits` then reads every split's partials (in split order, so
-// the sum does not depend on which workgroup finishes last).
+// Cross-workgroup split reduction.  A workgroup stores its partials (agent-scope
+// stores: written through to the device-coherent level, so the release below has
+// little to write back), releases them and counts itself in; the one that brings
+// the count to `splits` acquires and then reads every split's partials (in split
+// order, so the sum does not depend on which workgroup finishes last).
 QL_DEV void store_partial(float *p, float v) { __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
-QL_DEV float load_partial(const float *p) { return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
 QL_DEV bool last_of_splits(unsigned *cnt, unsigned splits) {
   __shared__ bool last;
   // Release at agent scope: each thread's partial stores are complete and visible to
@@ -98,31 +96,36 @@ QL_DEV bool last_of_splits(unsigned *cnt, unsigned splits) {
 }
 
 // ---------------------------------------------------------------------------
-// Rank-r products T = X·L1 (forward) and U = dY·L2^T (backward) in one launch
-// ([MC] "The algebra", Eq. 3: the adapter's down projection; [TT] §4).  A
-// workgroup owns `rows` (16, 8 or 4: enough workgroups to cover every compute
-// unit; the MFMA rows past them read as zero) rows and the whole K; its 16
-// waves split K into equal runs
-// of 32-wide steps, accumulate with 16x16x32 MFMAs and meet in LDS, where the
-// sum over the waves runs in a fixed order (deterministic, with no partial
-// sums in HBM and no second launch).  A operand: lane (i, g) loads 16 bytes of
-// row i at k + 8g, D steps ahead; rows past M read as zero.  B operand: the
-// backward's L2 [r][o] is k-contiguous, so its fragments are 16-byte loads of
-// L2 rows; the forward's L1 [h][r] is r-contiguous, so each step's 32 x r
-// slab (contiguous in memory) is copied into the wave's own LDS area and
-// gathered column by column.
+// Rank-r products T = X·L1 (forward) and U = dY·L2^T (backward), split over K
+// ([MC] "The algebra", Eq. 3: the adapter's down projection; [TT] §4).
+// lora_rank_kernel: a workgroup owns 64 rows and one K range (a multiple of 64
+// wide); its four waves take 16 rows each and every rank column, with 16x16x32
+// MFMAs.  A operand (X or dY, k-contiguous): lane (i, g) loads 16 bytes of row i
+// at k + 8g straight into registers, one 64-wide chunk ahead; rows past M read
+// as zero.  B operand: L2 [r][o] (backward) is k-contiguous, so its fragments
+// are 16-byte loads of L2 rows; L1 [h][r] (forward) is r-contiguous, so each
+// 64 x r chunk of it goes into a double-buffered LDS tile with rows padded by
+// 16 bytes, and two transposing reads (ds_read_b64_tr_b16) give each lane one
+// column's 8 consecutive k.  Each workgroup reads only its own K range of the
+// factor, so the factor is read once per 64 rows (the whole factor per
+// workgroup made the previous single-pass kernel's factor traffic 8x that of X).
+// With one K range the kernel writes the outputs itself; otherwise it stores
+// float32 partial sums and lora_rank_reduce_kernel adds them in split order
+// (deterministic) and writes them.
 // Outputs: out1[m][q] = bf16(sum) (zero for r <= q < ld1) and
-// out2[m][q] = bf16(s * sum) (zero for q >= r).  The backward launch also
-// writes the zero-padded copy L1p [h][ldp] of L1 that the dX GEMM's rank-r
-// step reads, and clears the adapter-gradient split counters.
+// out2[m][q] = bf16(s * sum) (zero for q >= r).  In the backward, the kernel
+// that writes the outputs also writes the zero-padded copy L1p [h][ldp] of L1
+// that the dX GEMM's rank-r step reads, and clears the adapter-gradient split
+// counters.
 // ---------------------------------------------------------------------------
 struct RankParams {
   const uint16_t *A;  // [M][lda] bf16
-  int64_t lda, M, K;  // K: a multiple of 32
+  int64_t lda, M, K;  // K: a multiple of 64
   const uint16_t *B;  // forward: L1 [K][r]; backward: L2 [r][ldb]
   int64_t ldb;
   int r;
-  int rows;  // rows per workgroup: 16, 8 or 4
+  int kper, ks;       // K per split (a multiple of 64) and number of splits
+  float *part;        // [ks][M][16 NT] float32 partial sums (ks > 1)
   float s;
   uint16_t *out1;
   int ld1;
@@ -137,114 +140,183 @@ struct RankParams {
   int ncnt;
 };
 
-constexpr int kRankWaves = 16;
+constexpr int kRankRows = 64;  // rows per workgroup: 16 per wave
 
-template <int NT, bool KN>
-__global__ __launch_bounds__(1024) void rank_r_kernel(RankParams p) {
-  constexpr int D = NT <= 4 ? 4 : 2;  // steps whose loads are in flight together
+// The backward's extra duties, spread over a whole grid (gt: this thread's index,
+// gn: the grid's thread count).
+QL_DEV void rank_extras(const RankParams &p, int64_t gt, int64_t gn) {
+  if (!p.L1p) return;
+  for (int64_t idx = gt; idx < p.h * p.ldp; idx += gn) {
+    const int64_t a = idx / p.ldp, b = idx % p.ldp;
+    p.L1p[idx] = b < p.r ? p.L1[a * p.r + b] : (uint16_t)0;
+  }
+  for (int64_t idx = gt; idx < p.ncnt; idx += gn) p.cnt[idx] = 0u;
+}
+
+// KN: the factor is L1 [K][r] (r-contiguous); VEC: r is a multiple of 8, so each
+// L1 row starts on a 16-byte boundary and the chunk copies in 16-byte pieces
+// (otherwise element by element).  !KN: the factor is L2 [r][ldb] (k-contiguous).
+// Either way a chunk of the factor is staged once in LDS for all four waves.
+template <int NT, bool KN, bool VEC>
+__global__ __launch_bounds__(256) void lora_rank_kernel(RankParams p) {
   constexpr int RP = NT * 16;
-  constexpr int SLAB = 32 * RP * 2;                    // bytes of one wave's L1 slab (32 rows of r <= RP)
-  constexpr int RED = 16 * RP * 4;                     // bytes of one wave's partial sums
-  constexpr int LDS = kRankWaves * (SLAB > RED ? SLAB : RED);
-  __shared__ __attribute__((aligned(16))) char lds[LDS];
+  constexpr int LDB = RP + 8;  // KN tile [64 k][LDB]: row stride of the transposing reads
+  constexpr int LDK = 64 + 8;  // NK tile [RP q][LDK]: row stride of the 16-byte fragment reads
+  constexpr int TILE = KN ? 64 * LDB : RP * LDK;
+  constexpr int BV = (8 * RP + 255) / 256;  // 16-byte factor pieces per thread per chunk (at most)
+  __shared__ __attribute__((aligned(16))) uint16_t Bs[2][TILE];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 4, i16 = lane & 15;
   const int r = p.r;
-
-  const int64_t m0 = (int64_t)blockIdx.x * p.rows;
-  const int64_t mrows = p.M - m0 < p.rows ? p.M - m0 : p.rows;
-  const auto rA = gv_rsrc(p.A + m0 * p.lda, mrows * p.lda * 2);
-  const int voffA = (int)((i16 * p.lda + 8 * g) * 2);
-  const auto rB = KN ? gv_rsrc(p.B, p.K * r * 2) : gv_rsrc(p.B, (int64_t)r * p.ldb * 2);
-  const int64_t ksteps = p.K >> 5;
-  const int64_t per = (ksteps + kRankWaves - 1) / kRankWaves;
-  const int64_t s0 = wave * per, s1 = s0 + per < ksteps ? s0 + per : ksteps;
-  char *slab = lds + wave * SLAB;
+  const int64_t m0 = (int64_t)blockIdx.x * kRankRows;
+  const int64_t mrows = p.M - m0 < kRankRows ? p.M - m0 : kRankRows;
+  const int64_t k0 = (int64_t)blockIdx.y * p.kper;
+  const int64_t k1 = k0 + p.kper < p.K ? k0 + p.kper : p.K;
+  const int nch = (int)((k1 - k0) >> 6);
+  const auto rA = gv_rsrc(p.A + m0 * p.lda + k0, mrows * p.lda * 2 - k0 * 2);
+  const int voffA = (int)(((16 * wave + i16) * p.lda + 8 * g) * 2);
+  // KN: rows [k0, k1) of L1, (k1 - k0) * r contiguous elements;
+  // NK: rows [0, r) of L2 from column k0 (rows past r read as zero)
+  const auto rB = KN ? gv_rsrc(p.B + k0 * r, (k1 - k0) * r * 2) : gv_rsrc(p.B + k0, (int64_t)r * p.ldb * 2 - k0 * 2);
+  int voffB[BV], soffB[BV];
+#pragma unroll
+  for (int j = 0; j < BV; ++j) {
+    const int idx = tid + 256 * j;
+    if (KN) {  // piece idx of the chunk's 64 x r contiguous elements
+      const int pr = r >> 3;
+      voffB[j] = idx < 8 * r ? idx * 16 : (int)0x80000000u;
+      soffB[j] = VEC && idx < 8 * r ? (idx / pr) * LDB + (idx % pr) * 8 : 0;
+    } else {   // row idx / 8, piece idx % 8 of 64 k
+      voffB[j] = idx < 8 * RP ? (int)(((idx >> 3) * p.ldb + (idx & 7) * 8) * 2) : (int)0x80000000u;
+      soffB[j] = (idx >> 3) * LDK + (idx & 7) * 8;
+    }
+  }
 
   f32x4 acc[NT];
 #pragma unroll
   for (int t = 0; t < NT; ++t) acc[t] = f32x4{0, 0, 0, 0};
 
-  for (int64_t sb = s0; sb < s1; sb += D) {
-    u32x4 a[D], b[D][NT];
+  struct Chunk {
+    u32x4 a[2];
+    u32x4 b[BV];
+  };
+  auto load = [&](int c, Chunk &C) {
+    const int so = __builtin_amdgcn_readfirstlane(c * 128);  // bytes of 64 k
+    C.a[0] = __builtin_amdgcn_raw_buffer_load_b128(rA, voffA, so, 0);
+    C.a[1] = __builtin_amdgcn_raw_buffer_load_b128(rA, voffA + 64, so, 0);
+    if (!KN || VEC) {
+      const int sb = KN ? __builtin_amdgcn_readfirstlane(c * 128 * r) : so;  // KN: 64 rows of r
 #pragma unroll
-    for (int u = 0; u < D; ++u) {
-      const int64_t st = sb + u;
-      if (st < s1) {  // wave-uniform
-        const int ko = __builtin_amdgcn_readfirstlane((int)(st * 64));      // byte offset of k = 32 st
-        const int so = __builtin_amdgcn_readfirstlane((int)(st * 64 * r));  // byte offset of its L1 slab
-        a[u] = __builtin_amdgcn_raw_buffer_load_b128(rA, voffA, ko, 0);
+      for (int j = 0; j < BV; ++j) C.b[j] = __builtin_amdgcn_raw_buffer_load_b128(rB, voffB[j], sb, 0);
+    }
+  };
+  // the chunk's factor into LDS buffer `buf`
+  auto put = [&](int c, int buf, const Chunk &C) {
+    if (!KN || VEC) {
 #pragma unroll
-        for (int t = 0; t < NT; ++t) {
-          if (KN)  // 16-byte chunk lane + 64 t of the slab (64 r bytes)
-            b[u][t] = __builtin_amdgcn_raw_buffer_load_b128(rB, (lane + 64 * t) * 16, so, 0);
-          else     // L2 row 16 t + i16, k = 32 st + 8 g
-            b[u][t] = __builtin_amdgcn_raw_buffer_load_b128(rB, (int)(((16 * t + i16) * p.ldb + 8 * g) * 2), ko, 0);
-        }
+      for (int j = 0; j < BV; ++j)
+        if (tid + 256 * j < 8 * (KN ? r : RP)) *reinterpret_cast<u32x4 *>(&Bs[buf][soffB[j]]) = C.b[j];
+    } else {
+      const int sb = __builtin_amdgcn_readfirstlane(c * 128 * r);
+      for (int idx = tid; idx < 64 * r; idx += 256) {
+        const uint16_t v = __builtin_amdgcn_raw_buffer_load_b16(rB, idx * 2, sb, 0);
+        Bs[buf][(idx / r) * LDB + idx % r] = v;
       }
     }
+  };
+  const int trow = i16 >> 2, tcol = (i16 & 3) * 4;
+  auto compute = [&](int buf, const Chunk &C) {
 #pragma unroll
-    for (int u = 0; u < D; ++u) {
-      if (sb + u < s1) {
-        if (KN) {
-          // The slab is stored as 16-byte words and read back as bf16 values by other lanes of
-          // this wave: the empty asm statements keep the compiler from moving the reads across
-          // the stores (type-based alias analysis would allow it); a wave's LDS accesses execute
-          // in order, so no hardware barrier is needed.
-          asm volatile("" ::: "memory");
+    for (int sub = 0; sub < 2; ++sub)
 #pragma unroll
-          for (int t = 0; t < NT; ++t)
-            if ((lane + 64 * t) * 16 < 64 * r) *reinterpret_cast<u32x4 *>(slab + (lane + 64 * t) * 16) = b[u][t];
-          asm volatile("" ::: "memory");
-          const uint16_t *sl = reinterpret_cast<const uint16_t *>(slab);
-#pragma unroll
-          for (int t = 0; t < NT; ++t) {
-            const int q = 16 * t + i16;
-            uint32_t w[4];
-#pragma unroll
-            for (int x = 0; x < 4; ++x) {  // unconditional reads inside the slab area, masked after
-              const uint32_t lo = sl[(8 * g + 2 * x) * r + q], hi = sl[(8 * g + 2 * x + 1) * r + q];
-              w[x] = q < r ? lo | (hi << 16) : 0u;
-            }
-            acc[t] = mfma16(a[u], u32x4{w[0], w[1], w[2], w[3]}, acc[t]);
-          }
+      for (int t = 0; t < NT; ++t) {
+        u32x4 b;
+        if constexpr (KN) {
+          const uint16_t *lo = &Bs[buf][(32 * sub + 8 * g + trow) * LDB + 16 * t + tcol];
+          b = tr_pair(lo, lo + 4 * LDB);
         } else {
-#pragma unroll
-          for (int t = 0; t < NT; ++t) acc[t] = mfma16(a[u], b[u][t], acc[t]);
+          b = *reinterpret_cast<const u32x4 *>(&Bs[buf][(16 * t + i16) * LDK + 32 * sub + 8 * g]);
         }
+        acc[t] = mfma16(C.a[sub], b, acc[t]);
       }
+  };
+
+  // Chunk c computes from LDS buffer c & 1 while chunk c + 1's loads are in flight;
+  // it is written to the other buffer after the computation (whose reads of that
+  // buffer ended at the previous barrier), then one barrier.
+  Chunk C0, C1;
+  load(0, C0);
+  put(0, 0, C0);
+  __syncthreads();
+  for (int c = 0; c < nch; c += 2) {
+    if (c + 1 < nch) load(c + 1, C1);
+    __builtin_amdgcn_sched_barrier(0);
+    compute(0, C0);
+    if (c + 1 >= nch) break;
+    put(c + 1, 1, C1);
+    __syncthreads();
+    if (c + 2 < nch) load(c + 2, C0);
+    __builtin_amdgcn_sched_barrier(0);
+    compute(1, C1);
+    if (c + 2 < nch) {
+      put(c + 2, 0, C0);
+      __syncthreads();
     }
   }
 
-  // the waves' sums meet in LDS: red[w][row][q], row = 4g + v, q = 16t + i16
-  __syncthreads();
-  float *red = reinterpret_cast<float *>(lds);
+  // C layout: lane (q = 16t + i16, g) holds rows 16 wave + 4g + v
+  if (p.ks > 1) {
+    float *out = p.part + ((int64_t)blockIdx.y * p.M + m0) * RP;
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int row = 16 * wave + 4 * g + v;
+        if (row < mrows) out[(int64_t)row * RP + 16 * t + i16] = acc[t][v];
+      }
+    return;
+  }
+  const int W = p.ld1 > p.ld2 ? p.ld1 : p.ld2;
 #pragma unroll
   for (int t = 0; t < NT; ++t)
 #pragma unroll
-    for (int v = 0; v < 4; ++v) red[(wave * 16 + 4 * g + v) * RP + 16 * t + i16] = acc[t][v];
-  __syncthreads();
-  const int W = p.ld1 > p.ld2 ? p.ld1 : p.ld2;
-  for (int o = tid; o < p.rows * W; o += 1024) {
-    const int row = o / W, q = o % W;
-    const int64_t m = m0 + row;
-    if (m >= p.M) continue;
-    float sum = 0.0f;
-    if (q < r)
-#pragma unroll
-      for (int w = 0; w < kRankWaves; ++w) sum += red[(w * 16 + row) * RP + q];
-    if (p.out1 && q < p.ld1) p.out1[m * p.ld1 + q] = q < r ? to_bf16(sum) : (uint16_t)0;
-    if (p.out2 && q < p.ld2) p.out2[m * p.ld2 + q] = q < r ? to_bf16(p.s * sum) : (uint16_t)0;
-  }
-  if (p.L1p) {  // backward extras, spread over the whole grid (after the main loads: no stall in front of them)
-    const int64_t gt = (int64_t)blockIdx.x * 1024 + tid, gn = (int64_t)gridDim.x * 1024;
-    for (int64_t idx = gt; idx < p.h * p.ldp; idx += gn) {
-      const int64_t a = idx / p.ldp, b = idx % p.ldp;
-      p.L1p[idx] = b < r ? p.L1[a * r + b] : (uint16_t)0;
+    for (int v = 0; v < 4; ++v) {
+      const int row = 16 * wave + 4 * g + v, q = 16 * t + i16;
+      if (row >= mrows) continue;
+      const int64_t m = m0 + row;
+      if (p.out1 && q < p.ld1) p.out1[m * p.ld1 + q] = q < r ? to_bf16(acc[t][v]) : (uint16_t)0;
+      if (p.out2 && q < p.ld2) p.out2[m * p.ld2 + q] = q < r ? to_bf16(p.s * acc[t][v]) : (uint16_t)0;
     }
-    for (int64_t idx = gt; idx < p.ncnt; idx += gn) p.cnt[idx] = 0u;
+  for (int q = RP + i16; q < W; q += 16)  // columns past the rank tiles: zero
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int row = 16 * wave + 4 * g + v;
+      if (row >= mrows) continue;
+      const int64_t m = m0 + row;
+      if (p.out1 && q < p.ld1) p.out1[m * p.ld1 + q] = 0;
+      if (p.out2 && q < p.ld2) p.out2[m * p.ld2 + q] = 0;
+    }
+  rank_extras(p, (int64_t)(blockIdx.y * gridDim.x + blockIdx.x) * 256 + tid, (int64_t)gridDim.x * gridDim.y * 256);
+}
+
+// Sum of the K splits' partials in split order, then the outputs (and the
+// backward's extras).  One thread per (row, column).
+template <int RP>
+__global__ __launch_bounds__(256) void lora_rank_reduce_kernel(RankParams p) {
+  const int W = p.ld1 > p.ld2 ? p.ld1 : p.ld2;
+  const int64_t gt = (int64_t)blockIdx.x * 256 + threadIdx.x, gn = (int64_t)gridDim.x * 256;
+  const int64_t stride = p.M * RP;
+  for (int64_t idx = gt; idx < p.M * W; idx += gn) {
+    const int64_t m = idx / W;
+    const int q = (int)(idx % W);
+    float sum = 0.0f;
+    if (q < p.r)
+      for (int k = 0; k < p.ks; ++k) sum += p.part[k * stride + m * RP + q];
+    if (p.out1 && q < p.ld1) p.out1[m * p.ld1 + q] = q < p.r ? to_bf16(sum) : (uint16_t)0;
+    if (p.out2 && q < p.ld2) p.out2[m * p.ld2 + q] = q < p.r ? to_bf16(p.s * sum) : (uint16_t)0;
   }
+  rank_extras(p, gt, gn);
 }
 
 // ---------------------------------------------------------------------------
@@ -486,7 +558,10 @@ __global__ __launch_bounds__(256) void lora_grad_kernel(GradProblem pa, GradProb
   constexpr int PCH = 64 * kGradTile / 8 / 256;       // 16-byte P chunks per thread per slab
   constexpr int QCH = (64 * RP / 8 + 255) / 256;      // 16-byte Q chunks per thread per slab (at most)
   __shared__ __attribute__((aligned(16))) uint16_t Ps[2][64 * LP];
-  __shared__ __attribute__((aligned(16))) uint16_t Qs[2][64 * RP];
+  // Q slab: rows padded to LQ when ldq is a multiple of 8 (transposing reads), else
+  // kept as it is in memory (ldq-element rows, 2-byte gathers)
+  constexpr int LQ = RP + 8;
+  __shared__ __attribute__((aligned(16))) uint16_t Qs[2][64 * LQ];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, c16 = lane & 15;
   const bool second = blockIdx.x >= pa.tiles;
@@ -497,6 +572,8 @@ __global__ __launch_bounds__(256) void lora_grad_kernel(GradProblem pa, GradProb
   const int64_t me = ms + mchunk < M ? ms + mchunk : M;
   const int nsteps = (int)((me - ms + 63) / 64);
   const int64_t ldp = pr.ldp, ldq = pr.ldq;
+  const bool qtr = (ldq & 7) == 0;  // wave-uniform: one problem per workgroup
+  const int qpr = (int)(ldq >> 3);  // 16-byte pieces per Q row (qtr)
   // rows [ms, me) of P from column i0, and of Q; everything past them reads as zero
   const auto rP = gv_rsrc(pr.P + ms * ldp + i0, (me - ms) * ldp * 2 - i0 * 2);
   const auto rQ = gv_rsrc(pr.Q + ms * ldq, (me - ms) * ldq * 2);
@@ -534,8 +611,13 @@ __global__ __launch_bounds__(256) void lora_grad_kernel(GradProblem pa, GradProb
 #pragma unroll
     for (int u = 0; u < PCH; ++u) *reinterpret_cast<u32x4 *>(&Ps[buf][soffP[u]]) = S.p[u];
 #pragma unroll
-    for (int u = 0; u < QCH; ++u)
-      if (tid + 256 * u < 8 * ldq) *reinterpret_cast<u32x4 *>(&Qs[buf][(tid + 256 * u) * 8]) = S.q[u];
+    for (int u = 0; u < QCH; ++u) {
+      const int ch = tid + 256 * u;
+      if (ch < 8 * ldq) {
+        const int off = qtr ? (ch / qpr) * LQ + (ch % qpr) * 8 : ch * 8;
+        *reinterpret_cast<u32x4 *>(&Qs[buf][off]) = S.q[u];
+      }
+    }
   };
   // lane 4j + qq of a 16-lane group names row k0 + j, columns 4qq..4qq+3 of the transposing read
   const int trow = c16 >> 2, tcol = (c16 & 3) * 4;
@@ -551,14 +633,22 @@ __global__ __launch_bounds__(256) void lora_grad_kernel(GradProblem pa, GradProb
 #pragma unroll
       for (int t = 0; t < NT; ++t) {
         const int q = 16 * t + c16;
-        uint32_t w[4];
+        u32x4 bq;
+        if (qtr) {
+          // columns past ldq hold stale values; they only reach output columns q >= rq,
+          // which are never stored
+          const uint16_t *lo = &Qs[buf][(mk + 8 * g + trow) * LQ + 16 * t + tcol];
+          bq = tr_pair(lo, lo + 4 * LQ);
+        } else {
+          uint32_t w[4];
 #pragma unroll
-        for (int x = 0; x < 4; ++x) {  // unconditional reads inside the slab (ldq <= RP), masked after
-          const uint32_t lo = Qs[buf][(mk + 8 * g + 2 * x) * ldq + q];
-          const uint32_t hi = Qs[buf][(mk + 8 * g + 2 * x + 1) * ldq + q];
-          w[x] = q < rq ? lo | (hi << 16) : 0u;
+          for (int x = 0; x < 4; ++x) {  // unconditional reads inside the slab (ldq <= RP), masked after
+            const uint32_t lo = Qs[buf][(mk + 8 * g + 2 * x) * ldq + q];
+            const uint32_t hi = Qs[buf][(mk + 8 * g + 2 * x + 1) * ldq + q];
+            w[x] = q < rq ? lo | (hi << 16) : 0u;
+          }
+          bq = u32x4{w[0], w[1], w[2], w[3]};
         }
-        const u32x4 bq{w[0], w[1], w[2], w[3]};
 #pragma unroll
         for (int a = 0; a < 2; ++a) acc[a][t] = mfma16(af[a], bq, acc[a][t]);
       }
@@ -598,17 +688,44 @@ __global__ __launch_bounds__(256) void lora_grad_kernel(GradProblem pa, GradProb
         if (i < pr.I) store_partial(out + i * RP + t * 16 + c16, acc[a][t][v]);
       }
   if (!last_of_splits(cnt + blockIdx.x, gridDim.y)) return;
+  // The last split sums the splits' partials (in split order) and stores the tile.
+  // Eight outputs per thread per pass with every load of a split issued before any
+  // is added: the loads are independent, so their latencies overlap (one output at a
+  // time made this tail a chain of memory round trips).  Plain loads: the acquire in
+  // last_of_splits ordered them after every split's release.
   const int S = (int)gridDim.y;
-  for (int idx = tid; idx < kGradTile * rq; idx += 256) {
-    // consecutive threads write consecutive addresses of the stored layout
-    const int il = pr.trans ? idx % kGradTile : idx / rq;
-    const int q = pr.trans ? idx / kGradTile : idx % rq;
-    const int64_t i = i0 + il;
-    if (i >= pr.I) continue;
-    float sum = 0.0f;
-#pragma unroll 8
-    for (int k = 0; k < S; ++k) sum += load_partial(part + ((int64_t)k * prows + pr.prow + i) * RP + q);
-    pr.out[pr.trans ? (int64_t)q * pr.I + i : i * rq + q] = s * sum;
+  const int nout = kGradTile * rq;
+  const int64_t kstride = prows * RP;
+  for (int base = 0; base < nout; base += 256 * 8) {
+    float sum[8];
+    int64_t src[8];
+    bool ok[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      // consecutive threads write consecutive addresses of the stored layout
+      const int idx = base + tid + 256 * u;
+      const int il = pr.trans ? idx % kGradTile : idx / rq;
+      const int q = pr.trans ? idx / kGradTile : idx % rq;
+      ok[u] = idx < nout && i0 + il < pr.I;
+      src[u] = ok[u] ? (pr.prow + i0 + il) * RP + q : 0;
+      sum[u] = 0.0f;
+    }
+    for (int k = 0; k < S; ++k) {
+      float v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = part[k * kstride + src[u]];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) sum[u] += v[u];
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      if (!ok[u]) continue;
+      const int idx = base + tid + 256 * u;
+      const int il = pr.trans ? idx % kGradTile : idx / rq;
+      const int q = pr.trans ? idx / kGradTile : idx % rq;
+      const int64_t i = i0 + il;
+      pr.out[pr.trans ? (int64_t)q * pr.I + i : i * rq + q] = s * sum[u];
+    }
   }
 }
 
@@ -642,9 +759,28 @@ Split grad_split(int64_t M, int64_t I, int64_t maxld) {
   return {(int)cdiv(M, chunk), chunk};
 }
 
+// K split of a rank-r product over M rows and K (a multiple of 64): about 512
+// workgroups of 64 rows, each K range a multiple of 64 wide.
+struct RankSplit {
+  int ks, kper;
+};
+
+RankSplit rank_split(int64_t M, int64_t K) {
+  const int64_t rb = cdiv(M, kRankRows), kc = K / 64;
+  int64_t ks = cdiv(kTargetGroups, rb);
+  ks = ks < 1 ? 1 : (ks > kc ? kc : ks);
+  const int64_t per = cdiv(kc, ks);
+  return {(int)cdiv(kc, per), (int)(per * 64)};
+}
+
+size_t rank_partial_bytes(int64_t M, int64_t K, int RP16) {
+  const RankSplit rs = rank_split(M, K);
+  return rs.ks > 1 ? (size_t)rs.ks * M * RP16 * 4 : 0;
+}
+
 struct FwdLayout {
   int RP16, RP64;
-  size_t off_st, total;
+  size_t off_st, off_tp, total;
 };
 
 FwdLayout fwd_layout(int64_t M, int64_t h, int64_t o, int r) {
@@ -655,6 +791,7 @@ FwdLayout fwd_layout(int64_t M, int64_t h, int64_t o, int r) {
   size_t off = 0;
   auto take = [&](size_t bytes) { size_t at = off; off += rup((int64_t)bytes, 256); return at; };
   L.off_st = take((size_t)M * L.RP64 * 2);
+  L.off_tp = take(rank_partial_bytes(M, h, L.RP16));
   L.total = off;
   return L;
 }
@@ -663,7 +800,7 @@ struct BwdLayout {
   int RP16, RP64;
   Split gs;
   int dxc;  // few-token path (M <= 16): row chunks of the dX partial sums
-  size_t off_u, off_su, off_l1p, off_g, off_cnt, off_dxp, total;
+  size_t off_u, off_su, off_l1p, off_g, off_cnt, off_up, off_dxp, total;
 };
 
 int gemv_dx_chunks(int64_t h, int64_t o);
@@ -686,6 +823,7 @@ BwdLayout bwd_layout(int64_t M, int64_t h, int64_t o, int r) {
   L.off_l1p = take((size_t)h * L.RP64 * 2);
   L.off_g = take((size_t)L.gs.S * (h + o) * L.RP16 * 4);
   L.off_cnt = take((size_t)((h + o) / 64) * 4);
+  L.off_up = take(rank_partial_bytes(M, o, L.RP16));
   L.total = off;
   return L;
 }
@@ -693,17 +831,30 @@ BwdLayout bwd_layout(int64_t M, int64_t h, int64_t o, int r) {
 template <typename T>
 T *at(void *ws, size_t off) { return reinterpret_cast<T *>(reinterpret_cast<char *>(ws) + off); }
 
-hipError_t rank_r(RankParams &rp, bool kn, int RP16, hipStream_t st) {
-  // the fewest rows per workgroup that still give 256 workgroups (one per compute unit)
-  rp.rows = rp.M >= 16 * 256 ? 16 : (rp.M >= 8 * 256 ? 8 : 4);
-  const unsigned grid = (unsigned)cdiv(rp.M, rp.rows);
+hipError_t rank_r(RankParams &rp, bool kn, int RP16, float *part, hipStream_t st) {
+  const RankSplit rs = rank_split(rp.M, rp.K);
+  rp.ks = rs.ks;
+  rp.kper = rs.kper;
+  rp.part = part;
+  const dim3 grid((unsigned)cdiv(rp.M, kRankRows), (unsigned)rs.ks);
+  const bool vec = rp.r % 8 == 0;
+  hipError_t e = hipErrorInvalidValue;
   switch (RP16 / 16) {
-#define QL_RK(NT) \
-  case NT: return kn ? launch(rank_r_kernel<NT, true>, grid, 1024, st, rp) : launch(rank_r_kernel<NT, false>, grid, 1024, st, rp);
+#define QL_RK(NT)                                                                              \
+  case NT:                                                                                     \
+    e = !kn ? launch(lora_rank_kernel<NT, false, true>, grid, 256, st, rp)                     \
+            : (vec ? launch(lora_rank_kernel<NT, true, true>, grid, 256, st, rp)               \
+                   : launch(lora_rank_kernel<NT, true, false>, grid, 256, st, rp));           \
+    if (e == hipSuccess && rs.ks > 1) {                                                        \
+      int64_t rg = cdiv(rp.M * (rp.ld1 > rp.ld2 ? rp.ld1 : rp.ld2), 256);                      \
+      rg = rg > 2048 ? 2048 : rg;                                                              \
+      e = launch(lora_rank_reduce_kernel<NT * 16>, (unsigned)rg, 256, st, rp);                 \
+    }                                                                                          \
+    break;
     QL_RK(1) QL_RK(2) QL_RK(3) QL_RK(4) QL_RK(5) QL_RK(6) QL_RK(7) QL_RK(8)
 #undef QL_RK
   }
-  return hipErrorInvalidValue;
+  return e;
 }
 
 hipError_t lora_grad(const GradProblem &pa, const GradProblem &pb, int r, float s, int64_t M, int RP16,
@@ -1039,7 +1190,7 @@ hipError_t launch_linear_fwd(const LinearArgs &a, const uint16_t *X, const uint1
     rp.A = X; rp.lda = a.h; rp.M = a.M; rp.K = a.h;
     rp.B = L1; rp.ldb = a.r; rp.r = a.r; rp.s = a.s;
     rp.out1 = T; rp.ld1 = a.r; rp.out2 = sT; rp.ld2 = L.RP64;
-    const hipError_t e = rank_r(rp, true, L.RP16, st);
+    const hipError_t e = rank_r(rp, true, L.RP16, at<float>(ws, L.off_tp), st);
     if (e != hipSuccess) return e;
   }
   if (a.M <= 16) {
@@ -1089,7 +1240,7 @@ hipError_t launch_linear_bwd(const LinearArgs &a, const uint16_t *X, const uint1
     rp.B = L2; rp.ldb = a.o; rp.r = a.r; rp.s = a.s;
     rp.out1 = U; rp.ld1 = L.RP16; rp.out2 = sU; rp.ld2 = L.RP64;
     rp.L1 = L1; rp.h = a.h; rp.ldp = L.RP64; rp.L1p = L1p; rp.cnt = cnt; rp.ncnt = (int)((a.h + a.o) / 64);
-    const hipError_t e = rank_r(rp, false, L.RP16, st);
+    const hipError_t e = rank_r(rp, false, L.RP16, at<float>(ws, L.off_up), st);
     if (e != hipSuccess) return e;
     // dL1 = s·X^T·U (P = X [M][h], Q = U [M][RP16]) and dL2 = s·T^T·dY (P = dY [M][o], Q = T [M][r]), stored [r][o]
     g1 = GradProblem{X, a.h, a.h, U, L.RP16, dL1, false, cdiv(a.h, kGradTile), 0};

@@ -65,6 +65,8 @@ SMALL = [  # (M, h, o, r, s)
     (257, 576, 1088, 16, 2.0),
     (2050, 256, 320, 3, 1.0),     # rank-r products: 8 rows per workgroup, ragged last workgroup
     (4100, 192, 256, 100, 0.5),   # 16 rows per workgroup, ragged, r not a multiple of 8
+    (33000, 128, 192, 8, 1.0),    # rank-r products in one K range (no split partials), ragged rows
+    (32769, 64, 128, 100, 0.5),   # the same with r not a multiple of 8 (element-wise L1 copies)
 ]
 
 

@@ -5,15 +5,16 @@
 // block scale and hands bf16 values to the matrix cores.
 //
 // Kernels
-//   rank_r_kernel        the rank-r products T = X·L1 and U = dY·L2^T in one
-//                        launch each (MFMA 16x16x32, K split over the 16
-//                        waves of a workgroup, fixed-order LDS sum), rounded
-//                        to bf16 with the s-scaled copy the GEMM's rank-r
-//                        step uses
+//   lora_rank_kernel     the rank-r products T = X·L1 and U = dY·L2^T, split
+//                        over K (64-row workgroups, MFMA 16x16x32, factor
+//                        chunk staged once in LDS); lora_rank_reduce_kernel
+//                        adds the K splits in order and rounds to bf16 with
+//                        the s-scaled copy the GEMM's rank-r step uses
 //   nf4_gemm_kernel      fused dequant-GEMM, MFMA 32x32x16: forward
 //                        (B = W_hat, K along h) and dX (B = W_hat^T, K
 //                        along o); the rank-r LoRA product is added as extra
-//                        K steps on the same accumulators
+//                        K steps on the same accumulators (the 256x256
+//                        forward tiles run nf4_gemm_wide_fwd_kernel)
 //   nf4_gemv_kernel      M <= 16 forward: streams the codes once, decodes a
 //                        byte (two codes) per LDS lookup, applies the block
 //                        scale after each 64-wide MFMA pair
@@ -25,9 +26,10 @@
 //   gemv_dx_finish_kernel  sums the row-chunk partials in order, adds s·U·L1^T
 //   lora_grad_kernel     dL1 = s·X^T·U and dL2 = s·T^T·dY in one launch:
 //                        reduction over tokens, LDS-transposed operands,
-//                        split over tokens; the last split of a tile sums,
-//                        scales by s and stores dL1 [h][r] or dL2 [r][o];
-//                        runs before the dX GEMM on the caller's stream
+//                        split over tokens; lora_grad_reduce_kernel sums the
+//                        splits in order, scales by s and stores dL1 [h][r]
+//                        and dL2 [r][o]; both run before the dX GEMM on the
+//                        caller's stream
 
 #include "linear.h"
 #include "gemm.h"
@@ -74,27 +76,6 @@ QL_DEV __amdgpu_buffer_rsrc_t gv_rsrc(const void *base, int64_t bytes) {
 
 }  // namespace
 
-// Cross-workgroup split reduction.  A workgroup stores its partials (agent-scope
-// stores: written through to the device-coherent level, so the release below has
-// little to write back), releases them and counts itself in; the one that brings
-// the count to `splits` acquires and then reads every split's partials (in split
-// order, so the sum does not depend on which workgroup finishes last).
-QL_DEV void store_partial(float *p, float v) { __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
-QL_DEV bool last_of_splits(unsigned *cnt, unsigned splits) {
-  __shared__ bool last;
-  // Release at agent scope: each thread's partial stores are complete and visible to
-  // every workgroup before the barrier; thread 0's release RMW then publishes the whole
-  // workgroup's stores (they happen before it through the barrier).
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-  __syncthreads();
-  if (threadIdx.x == 0)
-    last = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT) == splits - 1;
-  __syncthreads();
-  // Acquire: the last workgroup reads the other splits' partials only after their releases.
-  if (last) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-  return last;
-}
-
 // ---------------------------------------------------------------------------
 // Rank-r products T = X·L1 (forward) and U = dY·L2^T (backward), split over K
 // ([MC] "The algebra", Eq. 3: the adapter's down projection; [TT] §4).
@@ -115,8 +96,7 @@ QL_DEV bool last_of_splits(unsigned *cnt, unsigned splits) {
 // Outputs: out1[m][q] = bf16(sum) (zero for r <= q < ld1) and
 // out2[m][q] = bf16(s * sum) (zero for q >= r).  In the backward, the kernel
 // that writes the outputs also writes the zero-padded copy L1p [h][ldp] of L1
-// that the dX GEMM's rank-r step reads, and clears the adapter-gradient split
-// counters.
+// that the dX GEMM's rank-r step reads.
 // ---------------------------------------------------------------------------
 struct RankParams {
   const uint16_t *A;  // [M][lda] bf16
@@ -136,8 +116,6 @@ struct RankParams {
   int64_t h;
   int ldp;
   uint16_t *L1p;
-  unsigned *cnt;
-  int ncnt;
 };
 
 constexpr int kRankRows = 64;  // rows per workgroup: 16 per wave
@@ -150,7 +128,6 @@ QL_DEV void rank_extras(const RankParams &p, int64_t gt, int64_t gn) {
     const int64_t a = idx / p.ldp, b = idx % p.ldp;
     p.L1p[idx] = b < p.r ? p.L1[a * p.r + b] : (uint16_t)0;
   }
-  for (int64_t idx = gt; idx < p.ncnt; idx += gn) p.cnt[idx] = 0u;
 }
 
 // KN: the factor is L1 [K][r] (r-contiguous); VEC: r is a multiple of 8, so each
@@ -531,10 +508,15 @@ __global__ __launch_bounds__(kGvThreads) void nf4_gemv_kernel(GemvParams p) {
 // runs) and the matching rows of Q (one contiguous run) are copied into LDS as
 // they are, with 16-byte stores; the MFMA fragments need 8 consecutive tokens
 // per lane, so P's come from transposing LDS reads (ds_read_b64_tr_b16) and
-// Q's from 2-byte gathers.  The next two slabs' loads are in flight while one
-// is multiplied (two register stages, double-buffered LDS, one barrier per
-// slab); loads past the token range read as zero.  The last token split of a
-// tile sums the splits in split order, scales by s and stores the tile.
+// Q's from transposing reads too when its rows are a multiple of 8 elements
+// (2-byte gathers otherwise).  The next two slabs' loads are in flight while
+// one is multiplied (two register stages, double-buffered LDS, one barrier per
+// slab); loads past the token range read as zero.  With one token split the
+// kernel scales by s and stores the tile; otherwise each split stores float32
+// partial sums and lora_grad_reduce_kernel adds them in split order
+// (deterministic).  The launch boundary orders the two, so no cross-workgroup
+// synchronisation is needed (an in-kernel last-arriving reduction paid an
+// agent-scope release per workgroup: 58 against 16 us on a 65B projection).
 // ---------------------------------------------------------------------------
 struct GradProblem {
   const uint16_t *P;  // [M][ldp], the i index runs along a row
@@ -551,8 +533,7 @@ constexpr int kGradTile = 128;  // values of i per workgroup
 
 template <int NT>
 __global__ __launch_bounds__(256) void lora_grad_kernel(GradProblem pa, GradProblem pb, int rq, float s, int64_t M,
-                                                        int64_t mchunk, int64_t prows, float *__restrict__ part,
-                                                        unsigned *__restrict__ cnt) {
+                                                        int64_t mchunk, int64_t prows, float *__restrict__ part) {
   constexpr int RP = NT * 16;
   constexpr int LP = kGradTile + 8;                   // P slab row stride (elements)
   constexpr int PCH = 64 * kGradTile / 8 / 256;       // 16-byte P chunks per thread per slab
@@ -677,7 +658,19 @@ __global__ __launch_bounds__(256) void lora_grad_kernel(GradProblem pa, GradProb
   }
 
   // D layout: lane (q = 16t + c16, g) holds rows i = 4g + v of each 16-row tile
-  float *out = part + ((int64_t)blockIdx.y * prows + pr.prow) * RP;
+  if (gridDim.y > 1) {
+    float *out = part + ((int64_t)blockIdx.y * prows + pr.prow) * RP;
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+      for (int t = 0; t < NT; ++t)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const int64_t i = i0 + wave * 32 + 16 * a + 4 * g + v;
+          if (i < pr.I) out[i * RP + t * 16 + c16] = acc[a][t][v];
+        }
+    return;
+  }
 #pragma unroll
   for (int a = 0; a < 2; ++a)
 #pragma unroll
@@ -685,47 +678,52 @@ __global__ __launch_bounds__(256) void lora_grad_kernel(GradProblem pa, GradProb
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
         const int64_t i = i0 + wave * 32 + 16 * a + 4 * g + v;
-        if (i < pr.I) store_partial(out + i * RP + t * 16 + c16, acc[a][t][v]);
+        const int q = t * 16 + c16;
+        if (i < pr.I && q < rq) pr.out[pr.trans ? (int64_t)q * pr.I + i : i * rq + q] = s * acc[a][t][v];
       }
-  if (!last_of_splits(cnt + blockIdx.x, gridDim.y)) return;
-  // The last split sums the splits' partials (in split order) and stores the tile.
-  // Eight outputs per thread per pass with every load of a split issued before any
-  // is added: the loads are independent, so their latencies overlap (one output at a
-  // time made this tail a chain of memory round trips).  Plain loads: the acquire in
-  // last_of_splits ordered them after every split's release.
-  const int S = (int)gridDim.y;
-  const int nout = kGradTile * rq;
-  const int64_t kstride = prows * RP;
-  for (int base = 0; base < nout; base += 256 * 8) {
-    float sum[8];
-    int64_t src[8];
-    bool ok[8];
+}
+
+// Sum of the adapter gradients' token splits, in split order, scaled by s.  A
+// workgroup takes 32 rows i of the partial buffer (one problem: h and o are
+// multiples of 64) and every rank column; each thread owns RP / 8 outputs and
+// issues all their loads of one split before adding them (independent loads, so
+// their latencies overlap).  Reads run along q (coalesced); dL2's [r][o] tile is
+// transposed through LDS so its stores run along i too.
+constexpr int kGradRedRows = 32;
+
+template <int RP>
+__global__ __launch_bounds__(256) void lora_grad_reduce_kernel(GradProblem pa, GradProblem pb, int rq, float s,
+                                                               int S, int64_t prows, const float *__restrict__ part) {
+  constexpr int PER = kGradRedRows * RP / 256;
+  __shared__ float tr[RP][kGradRedRows + 1];
+  const int tid = threadIdx.x;
+  const int64_t row0 = (int64_t)blockIdx.x * kGradRedRows;  // in the partial buffer's row space
+  const bool second = row0 >= pa.I;
+  const GradProblem &pr = second ? pb : pa;
+  const int64_t i0 = row0 - pr.prow;
+  const float *base = part + row0 * RP;
+  float sum[PER];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      // consecutive threads write consecutive addresses of the stored layout
-      const int idx = base + tid + 256 * u;
-      const int il = pr.trans ? idx % kGradTile : idx / rq;
-      const int q = pr.trans ? idx / kGradTile : idx % rq;
-      ok[u] = idx < nout && i0 + il < pr.I;
-      src[u] = ok[u] ? (pr.prow + i0 + il) * RP + q : 0;
-      sum[u] = 0.0f;
-    }
-    for (int k = 0; k < S; ++k) {
-      float v[8];
+  for (int u = 0; u < PER; ++u) sum[u] = 0.0f;
+  for (int k = 0; k < S; ++k) {
+    const float *src = base + (int64_t)k * prows * RP;
+    float v[PER];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) v[u] = part[k * kstride + src[u]];
+    for (int u = 0; u < PER; ++u) v[u] = src[tid + 256 * u];  // row (tid + 256u) / RP, column % RP
 #pragma unroll
-      for (int u = 0; u < 8; ++u) sum[u] += v[u];
-    }
+    for (int u = 0; u < PER; ++u) sum[u] += v[u];
+  }
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      if (!ok[u]) continue;
-      const int idx = base + tid + 256 * u;
-      const int il = pr.trans ? idx % kGradTile : idx / rq;
-      const int q = pr.trans ? idx / kGradTile : idx % rq;
-      const int64_t i = i0 + il;
-      pr.out[pr.trans ? (int64_t)q * pr.I + i : i * rq + q] = s * sum[u];
-    }
+  for (int u = 0; u < PER; ++u) {
+    const int idx = tid + 256 * u, il = idx / RP, q = idx % RP;
+    if (pr.trans) tr[q][il] = s * sum[u];
+    else if (q < rq) pr.out[(i0 + il) * rq + q] = s * sum[u];
+  }
+  if (!pr.trans) return;
+  __syncthreads();
+  for (int idx = tid; idx < rq * kGradRedRows; idx += 256) {
+    const int q = idx / kGradRedRows, il = idx % kGradRedRows;
+    pr.out[(int64_t)q * pr.I + i0 + il] = tr[q][il];
   }
 }
 
@@ -800,7 +798,7 @@ struct BwdLayout {
   int RP16, RP64;
   Split gs;
   int dxc;  // few-token path (M <= 16): row chunks of the dX partial sums
-  size_t off_u, off_su, off_l1p, off_g, off_cnt, off_up, off_dxp, total;
+  size_t off_u, off_su, off_l1p, off_g, off_up, off_dxp, total;
 };
 
 int gemv_dx_chunks(int64_t h, int64_t o);
@@ -822,7 +820,6 @@ BwdLayout bwd_layout(int64_t M, int64_t h, int64_t o, int r) {
   L.off_su = take((size_t)M * L.RP64 * 2);
   L.off_l1p = take((size_t)h * L.RP64 * 2);
   L.off_g = take((size_t)L.gs.S * (h + o) * L.RP16 * 4);
-  L.off_cnt = take((size_t)((h + o) / 64) * 4);
   L.off_up = take(rank_partial_bytes(M, o, L.RP16));
   L.total = off;
   return L;
@@ -858,16 +855,23 @@ hipError_t rank_r(RankParams &rp, bool kn, int RP16, float *part, hipStream_t st
 }
 
 hipError_t lora_grad(const GradProblem &pa, const GradProblem &pb, int r, float s, int64_t M, int RP16,
-                     const Split &sp, float *part, unsigned *cnt, hipStream_t st) {
+                     const Split &sp, float *part, hipStream_t st) {
   dim3 grid((unsigned)(pa.tiles + pb.tiles), (unsigned)sp.S);
   const int64_t prows = pa.I + pb.I;
+  const unsigned rgrid = (unsigned)(prows / kGradRedRows);
+  hipError_t e = hipErrorInvalidValue;
   switch (RP16 / 16) {
-#define QL_LG(NT) \
-  case NT: return launch(lora_grad_kernel<NT>, grid, 256, st, pa, pb, r, s, M, sp.chunk, prows, part, cnt);
+#define QL_LG(NT)                                                                                   \
+  case NT:                                                                                          \
+    e = launch(lora_grad_kernel<NT>, grid, 256, st, pa, pb, r, s, M, sp.chunk, prows, part);        \
+    if (e == hipSuccess && sp.S > 1)                                                                \
+      e = launch(lora_grad_reduce_kernel<NT * 16>, rgrid, 256, st, pa, pb, r, s, sp.S, prows,       \
+                 (const float *)part);                                                              \
+    break;
     QL_LG(1) QL_LG(2) QL_LG(3) QL_LG(4) QL_LG(5) QL_LG(6) QL_LG(7) QL_LG(8)
 #undef QL_LG
   }
-  return hipErrorInvalidValue;
+  return e;
 }
 
 thread_local hipEvent_t t_ev[3][2] = {};
@@ -1227,26 +1231,23 @@ hipError_t launch_linear_bwd(const LinearArgs &a, const uint16_t *X, const uint1
   uint16_t *sU = nullptr, *L1p = nullptr;
   GradProblem g1{}, g2{};
   float *gpart = nullptr;
-  unsigned *gcnt = nullptr;
   if (a.r > 0) {
-    unsigned *cnt = at<unsigned>(ws, L.off_cnt);
     L1p = at<uint16_t>(ws, L.off_l1p);
-    // U = dY·L2^T (L2 [r][o] is k-contiguous) and sU; the same launch writes L1 [h][r] ->
-    // L1p [h][RP64] for the dX GEMM's rank-r step and clears the gradient split counters
+    // U = dY·L2^T (L2 [r][o] is k-contiguous) and sU; the launch that writes them also
+    // copies L1 [h][r] -> L1p [h][RP64] for the dX GEMM's rank-r step
     uint16_t *U = at<uint16_t>(ws, L.off_u);
     sU = at<uint16_t>(ws, L.off_su);
     RankParams rp{};
     rp.A = dY; rp.lda = a.o; rp.M = a.M; rp.K = a.o;
     rp.B = L2; rp.ldb = a.o; rp.r = a.r; rp.s = a.s;
     rp.out1 = U; rp.ld1 = L.RP16; rp.out2 = sU; rp.ld2 = L.RP64;
-    rp.L1 = L1; rp.h = a.h; rp.ldp = L.RP64; rp.L1p = L1p; rp.cnt = cnt; rp.ncnt = (int)((a.h + a.o) / 64);
+    rp.L1 = L1; rp.h = a.h; rp.ldp = L.RP64; rp.L1p = L1p;
     const hipError_t e = rank_r(rp, false, L.RP16, at<float>(ws, L.off_up), st);
     if (e != hipSuccess) return e;
     // dL1 = s·X^T·U (P = X [M][h], Q = U [M][RP16]) and dL2 = s·T^T·dY (P = dY [M][o], Q = T [M][r]), stored [r][o]
     g1 = GradProblem{X, a.h, a.h, U, L.RP16, dL1, false, cdiv(a.h, kGradTile), 0};
     g2 = GradProblem{dY, a.o, a.o, T, a.r, dL2, true, cdiv(a.o, kGradTile), a.h};
     gpart = at<float>(ws, L.off_g);
-    gcnt = cnt;
   }
   if (a.M <= 16) {
     GvdParams vp{};
@@ -1259,7 +1260,7 @@ hipError_t launch_linear_bwd(const LinearArgs &a, const uint16_t *X, const uint1
     fill_levels(vp.level, tab);
     const dim3 grid((unsigned)((a.h + kGvdCols - 1) / kGvdCols), (unsigned)L.dxc);
     if (a.r > 0) {
-      const hipError_t e = lora_grad(g1, g2, a.r, a.s, a.M, L.RP16, L.gs, gpart, gcnt, st);
+      const hipError_t e = lora_grad(g1, g2, a.r, a.s, a.M, L.RP16, L.gs, gpart, st);
       if (e != hipSuccess) return e;
     }
     {
@@ -1286,7 +1287,7 @@ hipError_t launch_linear_bwd(const LinearArgs &a, const uint16_t *X, const uint1
   // the compute units and the cache hierarchy, and the stream fork and join add
   // their own gaps).
   if (a.r > 0) {
-    const hipError_t e = lora_grad(g1, g2, a.r, a.s, a.M, L.RP16, L.gs, gpart, gcnt, st);
+    const hipError_t e = lora_grad(g1, g2, a.r, a.s, a.M, L.RP16, L.gs, gpart, st);
     if (e != hipSuccess) return e;
   }
   TimedLaunch tl(1, st);

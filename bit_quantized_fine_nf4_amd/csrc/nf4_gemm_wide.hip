@@ -1,0 +1,370 @@
+// Fused NF4 dequant-GEMM, 256 x 256 tiles, forward direction, for gfx950.
+//
+// [MC] "1. NormalFloat" / [GO] "The core move": the 4-bit weights are
+// dequantized to BF16 on the fly for the matrix multiplication and never stored
+// in wider form.  C[M][N] = A[M][K] · B[K][N] with A = X and B[k][n] = W_hat[n][k]
+// (codes row n, 64-weight blocks along k), plus the rank-r term s·T·L2 as extra
+// K steps on the same accumulators ([MC] "The algebra", Eq. 3).
+//
+// Workgroup: 4 waves, one per SIMD.  Wave w owns output columns [64w, 64w + 64)
+// of the tile and all 256 rows: 8 x 2 tiles of v_mfma_f32_32x32x16_bf16, 256
+// accumulator registers.  Because no other wave needs its columns, each wave
+// decodes its own B fragments straight into registers: lane (n, g) (n = lane % 32,
+// g = lane / 32) loads the 16 code bytes of row n that hold k in [32g, 32g + 32)
+// of the K step (one 64-weight block, so one scale), looks each byte up in a
+// 256-entry LDS table of level pairs (level[high nibble], level[low nibble]),
+// multiplies by the block's rebuilt scale a_hat and converts to bf16 pairs:
+// MFMA group kk takes k = 32g + 8kk + 0..7, exactly the lane's bytes 4kk..4kk+3.
+// B therefore never passes through LDS and needs no synchronisation.
+// A (X, k-contiguous) is shared by all four waves: it goes from memory straight
+// into a 3-stage LDS ring (buffer_load ... lds, 16 bytes per lane, 1 KB = 8 rows
+// per instruction) two K steps ahead, in unpadded 128-byte rows whose 16-byte
+// chunks are XOR-swizzled by row so the fragment reads are free of bank
+// conflicts.  One barrier per K step.
+// Per K step and wave: 8 A-fragment reads per MFMA group, 64 MFMAs, 32 table
+// reads and about 5 VALU operations per code byte for the next step's decode
+// (issued between the current step's MFMA groups), 14 vector-memory operations
+// (8 A copies, 2 code, 2 int8-scale, 2 second-level-scale loads) two steps ahead.
+
+#include "gemm.h"
+
+namespace ql {
+namespace {
+
+QL_DEV __amdgpu_buffer_rsrc_t wrsrc(const void *base, int64_t bytes) {
+  const int64_t cap = 0x7FFFFFF0;
+  const int32_t n = (int32_t)(bytes < 0 ? 0 : (bytes > cap ? cap : bytes));
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, n, 0x00020000);
+}
+QL_DEV u32x4 wload128(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
+}
+QL_DEV f32x16 wmfma(u32x4 a, u32x4 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c, 0,
+                                                0, 0);
+}
+typedef short s16x4w __attribute__((ext_vector_type(4)));
+QL_DEV u32x4 wtr_pair(const uint16_t *lo, const uint16_t *hi) {
+  typedef __attribute__((address_space(3))) s16x4w lds_s16x4;
+  const s16x4w a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(lo));
+  const s16x4w b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(hi));
+  const u32x2 ua = __builtin_bit_cast(u32x2, a), ub = __builtin_bit_cast(u32x2, b);
+  return u32x4{ua[0], ua[1], ub[0], ub[1]};
+}
+QL_DEV void wload16_to_lds(__amdgpu_buffer_rsrc_t r, uint16_t *dst, int voff, int soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void *)dst, 16, voff, soff, 0, 0);
+}
+QL_DEV uint16_t wbf16(float v) { return (uint16_t)(pack_bf16x2(v, 0.0f) & 0xFFFFu); }
+// Workgroup barrier without the memory fences of __syncthreads(): those make the
+// compiler wait for every outstanding load, the prefetches included.  The K loop
+// orders its LDS traffic itself (an explicit wait for this wave's own copies into
+// LDS before the barrier); the empty asm statements keep the compiler from moving
+// memory accesses across it.
+QL_DEV void wbarrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+constexpr int kBM = 256, kBN = 256, kBK = 64, kThreads = 256;
+constexpr int kTM = 8, kTN = 2;       // 32x32 MFMA tiles per wave: 8 along M, 2 along N
+constexpr int kStages = 3;            // A ring depth
+constexpr int kStageElems = kBM * kBK;  // 256 rows x 64 k (bf16)
+constexpr int kLutCopies = 16;        // lane l reads copy l % 16 of the pair table
+constexpr int kLutBytes = 256 * 8 * kLutCopies;
+constexpr int kLdc = kBN + 8;         // epilogue staging row stride (elements)
+constexpr int kLdsBytes = (kLutBytes + kStages * kStageElems * 2) > (kBM * kLdc * 2)
+                              ? (kLutBytes + kStages * kStageElems * 2)
+                              : (kBM * kLdc * 2);
+constexpr int kLdkn = kBN + 32;       // LoRA B2 tile [64 k][kLdkn] (transposing reads)
+
+// row r of an A stage keeps its 8 chunks of 16 bytes in the order c ^ swz(r)
+QL_DEV int a_swz(int r) { return (r >> 1) & 7; }
+
+}  // namespace
+
+__global__ __launch_bounds__(kThreads) void nf4_gemm_wide_fwd_kernel(GemmParams p) {
+  __shared__ __attribute__((aligned(16))) char lds[kLdsBytes];
+  const f32x2 *lut = reinterpret_cast<const f32x2 *>(lds);
+  uint16_t *ring = reinterpret_cast<uint16_t *>(lds + kLutBytes);
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = lane >> 5, l32 = lane & 31;
+
+  for (int i = tid; i < 256 * kLutCopies; i += kThreads) {
+    const int e = i / kLutCopies;
+    reinterpret_cast<f32x2 *>(lds)[i] = f32x2{p.level[e >> 4], p.level[e & 15]};
+  }
+
+  int bid = blockIdx.x;
+  const int ntiles = p.tiles_m * p.tiles_n;
+  if ((ntiles & 7) == 0) bid = (bid & 7) * (ntiles >> 3) + (bid >> 3);  // one XCD -> contiguous tiles
+  const int tn = bid % p.tiles_n, tm = bid / p.tiles_n;
+  const int64_t m0 = (int64_t)tm * kBM, n0 = (int64_t)tn * kBN;
+  const int64_t mrows = p.M - m0 < kBM ? p.M - m0 : kBM;
+  const int64_t nrows = p.N - n0 < kBN ? p.N - n0 : kBN;
+  const float mu = *p.mean;
+  const int64_t bpr = p.ldw >> 6;  // 64-blocks per codes row
+
+  // ---- A: each wave copies 8 blocks of 8 rows per stage, lane L -> row 8 blk + L / 8,
+  // physical chunk L % 8 (global chunk (L % 8) ^ swz(row))
+  const auto rA = wrsrc(p.A + m0 * p.lda, mrows * p.lda * 2);
+  int voffA[8];
+#pragma unroll
+  for (int c = 0; c < 8; ++c) {
+    const int r = 8 * (wv * 8 + c) + (lane >> 3), lc = (lane & 7) ^ a_swz(r);
+    voffA[c] = (int)((r * p.lda + lc * 8) * 2);
+  }
+  auto dma_a = [&](int kt_, int buf) {
+    const int kt = __builtin_amdgcn_readfirstlane(kt_);
+#pragma unroll
+    for (int c = 0; c < 8; ++c)
+      wload16_to_lds(rA, ring + buf * kStageElems + (wv * 8 + c) * 8 * kBK, voffA[c], kt * kBK * 2);
+  };
+
+  // ---- B: lane (l32, g) of wave w decodes codes rows 64w + 32j + l32 (j = 0, 1)
+  const auto rC = wrsrc(p.codes + n0 * (p.ldw >> 1), nrows * (p.ldw >> 1));
+  const auto rQ = wrsrc(p.qabsmax + n0 * bpr, nrows * bpr);
+  const auto rS2 = wrsrc(p.scale2, ((p.wrows * bpr + 255) >> 8) * 4);
+  int voffC[kTN], voffQ[kTN];
+  int64_t blk0[kTN];
+#pragma unroll
+  for (int j = 0; j < kTN; ++j) {
+    const int row = 64 * wv + 32 * j + l32;
+    voffC[j] = (int)(row * (p.ldw >> 1) + 16 * g);
+    voffQ[j] = (int)(row * bpr);
+    blk0[j] = (n0 + row) * bpr;
+  }
+  struct BRegs {
+    u32x4 c[kTN];     // 16 code bytes per row
+    uint32_t q[kTN];  // int8 block scale, zero-extended
+    float s2[kTN];    // its second-level step
+  };
+  auto load_b = [&](int kt_, BRegs &R) {
+    const int kt = __builtin_amdgcn_readfirstlane(kt_);
+#pragma unroll
+    for (int j = 0; j < kTN; ++j) {
+      R.c[j] = wload128(rC, voffC[j], kt * 32);
+      R.q[j] = __builtin_amdgcn_raw_buffer_load_b8(rQ, voffQ[j], kt, 0);
+      R.s2[j] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                              rS2, (int)(((blk0[j] + kt) >> 8) * 4), 0, 0));
+    }
+  };
+  const int lcopy8 = (lane % kLutCopies) * 8;
+  // Decode of one part (4 code bytes of each of the lane's two rows = MFMA group
+  // `part`) in two halves so the table reads can run ahead of their use:
+  //   lut_read: the 8 table reads (level pairs) of part `part`;
+  //   lut_use:  the rebuilt scales times those levels, converted to bf16 pairs.
+  typedef f32x2 Lv[kTN][4];
+  auto lut_read = [&](const BRegs &R, int part, Lv &lv) {
+#pragma unroll
+    for (int j = 0; j < kTN; ++j) {
+      const uint32_t w = R.c[j][part];
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        const uint32_t byte = (w >> (8 * b)) & 0xFFu;
+        lv[j][b] = *reinterpret_cast<const f32x2 *>(lds + (byte << 7) + lcopy8);
+      }
+    }
+  };
+  auto scale_of = [&](const BRegs &R, float (&ah)[kTN]) {
+#pragma unroll
+    for (int j = 0; j < kTN; ++j) {
+      // int8 from the zero-extended byte by float arithmetic (a sign-extending load
+      // would be fused with the load and moved next to the younger prefetch)
+      const float qf = (float)R.q[j] - (float)(R.q[j] & 0x80u) * 2.0f;
+      ah[j] = qf * R.s2[j] + mu;  // two roundings: the library builds without contraction
+    }
+  };
+  auto lut_use = [&](const Lv &lv, const float (&ah)[kTN], int part, u32x4 (&bf)[kTN][4]) {
+#pragma unroll
+    for (int j = 0; j < kTN; ++j) {
+      uint32_t o[4];
+#pragma unroll
+      for (int b = 0; b < 4; ++b) o[b] = pack_bf16x2(lv[j][b][0] * ah[j], lv[j][b][1] * ah[j]);
+      bf[j][part] = u32x4{o[0], o[1], o[2], o[3]};
+    }
+  };
+
+  f32x16 acc[kTM][kTN];
+#pragma unroll
+  for (int i = 0; i < kTM; ++i)
+#pragma unroll
+    for (int j = 0; j < kTN; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
+
+  // A fragments of MFMA group kk from stage buffer `buf`: rows 32i + l32, chunk 4g + kk
+  auto read_a = [&](int buf, int kk, u32x4 (&af)[kTM]) {
+#pragma unroll
+    for (int i = 0; i < kTM; ++i) {
+      const int r = 32 * i + l32;
+      af[i] = *reinterpret_cast<const u32x4 *>(ring + buf * kStageElems + r * kBK + (((4 * g + kk) ^ a_swz(r)) << 3));
+    }
+  };
+
+  // wait until at most n vector-memory operations of this wave are outstanding
+  // (the LDS-bound A copies count; the compiler cannot know other waves read them)
+  auto wait_vm = [](auto nconst) {
+    constexpr int n = decltype(nconst)::value;
+    __builtin_amdgcn_s_waitcnt((n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14));
+  };
+
+  const int nk = p.ksteps;
+  BRegs R0, R1, R2;
+  u32x4 bcur[kTN][4], bnext[kTN][4];
+  __syncthreads();  // pair table ready
+  dma_a(0, 0);
+  load_b(0, R0);
+  __builtin_amdgcn_sched_barrier(0);
+  dma_a(1, 1);
+  load_b(1, R1);
+  __builtin_amdgcn_sched_barrier(0);
+  {
+    float ah[kTN];
+    scale_of(R0, ah);
+#pragma unroll
+    for (int part = 0; part < 4; ++part) {
+      Lv lv;
+      lut_read(R0, part, lv);
+      lut_use(lv, ah, part, bcur);
+    }
+  }
+
+  // Step kt (ring buffer BUF = kt % 3, a compile-time constant: the loop is unrolled
+  // three times, with three B register sets): A from buffer BUF (copied two steps
+  // earlier), B from bcur.  Issued at its start: the A copy and the B loads of step
+  // kt + 2 (into the register set step kt's own B came from, decoded during step
+  // kt - 1).  The decode of step kt + 1 (loaded during step kt - 1) runs between
+  // the MFMAs: while group kk's 16 MFMAs issue, the A fragments of group kk + 1 and
+  // the table reads of decode part kk + 1 are in flight and part kk's levels are
+  // scaled and converted.  Loads past the last step read harmless data that is
+  // never used.
+  auto step = [&](auto bufc, int kt, BRegs &Rnext, BRegs &Rfree) {
+    constexpr int BUF = decltype(bufc)::value;
+    // this wave's copy of stage kt is done once at most 20 younger operations are
+    // outstanding (step kt's B loads, step kt + 1's copy and B loads); the barrier
+    // makes every wave's copy visible and frees buffer (kt + 2) % 3, last read in
+    // step kt - 1
+    wait_vm(std::integral_constant<int, 20>{});
+    wbarrier();
+    dma_a(kt + 2, (BUF + 2) % kStages);
+    load_b(kt + 2, Rfree);
+    u32x4 af[2][kTM];
+    Lv lv[2];
+    float ah[kTN];
+    read_a(BUF, 0, af[0]);
+    lut_read(Rnext, 0, lv[0]);
+    scale_of(Rnext, ah);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      if (kk < 3) {
+        read_a(BUF, kk + 1, af[(kk + 1) & 1]);
+        lut_read(Rnext, kk + 1, lv[(kk + 1) & 1]);
+      }
+#pragma unroll
+      for (int i = 0; i < kTM; ++i)
+#pragma unroll
+        for (int j = 0; j < kTN; ++j) acc[i][j] = wmfma(af[kk & 1][i], bcur[j][kk], acc[i][j]);
+      lut_use(lv[kk & 1], ah, kk, bnext);
+      // interleave: each MFMA followed by one LDS read and a few decode instructions
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
+        __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);  // VALU
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int j = 0; j < kTN; ++j)
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) bcur[j][kk] = bnext[j][kk];
+  };
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using I2 = std::integral_constant<int, 2>;
+  int kt = 0;
+  for (; kt + 2 < nk; kt += 3) {
+    step(I0{}, kt, R1, R2);
+    step(I1{}, kt + 1, R2, R0);
+    step(I2{}, kt + 2, R0, R1);
+  }
+  if (kt < nk) step(I0{}, kt, R1, R2);
+  if (kt + 1 < nk) step(I1{}, kt + 1, R2, R0);
+  __builtin_amdgcn_s_waitcnt(0);  // no copy of a stage past the end may still land in LDS
+  __syncthreads();
+
+  // ---- rank-r K steps: A2 = s-scaled T [M][lda2] through ring buffer 0, B2 = L2
+  // [r][N] as a [k][n] tile (rows past r read as zero) in the space of buffers 1-2,
+  // read with transposing loads (lane n receives column n's 8 consecutive k)
+  if (p.ksteps2 > 0) {
+    const auto rA2 = wrsrc(p.A2 + m0 * p.lda2, mrows * p.lda2 * 2);
+    const auto rB2 = wrsrc(p.B2 + n0, ((int64_t)p.b2rows * p.ldb2 - n0) * 2);
+    uint16_t *a2 = ring;
+    uint16_t *b2 = ring + kStageElems;
+    const int c = lane & 15;
+    for (int k2 = 0; k2 < p.ksteps2; ++k2) {
+      // A2: 256 rows x 64 k, 8 chunks per row (same swizzle as A), 8 per thread
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int ch = tid + kThreads * u, r = ch >> 3, lc = ch & 7;
+        const u32x4 v = wload128(rA2, (int)((r * p.lda2 + lc * 8) * 2), k2 * kBK * 2);
+        *reinterpret_cast<u32x4 *>(a2 + r * kBK + ((lc ^ a_swz(r)) << 3)) = v;
+      }
+      // B2: 64 rows (k) x 256 columns, 32 chunks per row, 8 per thread
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int ch = tid + kThreads * u, kr = ch >> 5, c8 = ch & 31;
+        const u32x4 v = wload128(rB2, (int)(((int64_t)(k2 * kBK + kr) * p.ldb2 + c8 * 8) * 2), 0);
+        *reinterpret_cast<u32x4 *>(b2 + kr * kLdkn + c8 * 8) = v;
+      }
+      __syncthreads();
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        u32x4 af[kTM];
+        read_a(0, kk, af);
+        u32x4 bf[kTN];
+        const uint16_t *b0 = b2 + (32 * g + 8 * kk + (c >> 2)) * kLdkn + 64 * wv + ((lane >> 4) & 1) * 16 + (c & 3) * 4;
+#pragma unroll
+        for (int j = 0; j < kTN; ++j) bf[j] = wtr_pair(b0 + 32 * j, b0 + 4 * kLdkn + 32 * j);
+#pragma unroll
+        for (int i = 0; i < kTM; ++i)
+#pragma unroll
+          for (int j = 0; j < kTN; ++j) acc[i][j] = wmfma(af[i], bf[j], acc[i][j]);
+      }
+      __syncthreads();
+    }
+  }
+
+  // ---- epilogue: fp32 -> bf16 through LDS, then coalesced 16-byte stores
+  uint16_t *cs = reinterpret_cast<uint16_t *>(lds);
+#pragma unroll
+  for (int i = 0; i < kTM; ++i)
+#pragma unroll
+    for (int j = 0; j < kTN; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int row = 32 * i + 8 * (v >> 2) + 4 * g + (v & 3);
+        const int col = 64 * wv + 32 * j + l32;
+        cs[row * kLdc + col] = wbf16(acc[i][j][v]);
+      }
+  __syncthreads();
+  for (int ch = tid; ch < kBM * kBN / 8; ch += kThreads) {
+    const int row = ch / (kBN / 8), c8 = ch % (kBN / 8);
+    const int64_t m = m0 + row, n = n0 + c8 * 8;
+    if (m < p.M && n < p.N)
+      *reinterpret_cast<u32x4 *>(p.C + m * p.ldc + n) = *reinterpret_cast<const u32x4 *>(cs + row * kLdc + c8 * 8);
+  }
+}
+
+hipError_t launch_nf4_gemm_wide(GemmParams &gp, bool trans, hipStream_t st) {
+  gp.tiles_m = (int)((gp.M + kBM - 1) / kBM);
+  gp.tiles_n = (int)((gp.N + kBN - 1) / kBN);
+  if (trans) return hipErrorInvalidValue;
+  return launch(nf4_gemm_wide_fwd_kernel, gp.tiles_m * gp.tiles_n, kThreads, st, gp);
+}
+
+}  // namespace ql

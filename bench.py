@@ -157,9 +157,10 @@ class _Event:
         return self.hev.elapsed_ms(self.ev, other.ev)
 
 
-def read_traffic(kernel: str):
-    """HBM bytes per launch from the committed rocprofv3 counter summary, or None
-    when absent or when the kernel source changed since the counters were taken."""
+def read_traffic(key: str):
+    """HBM bytes per launch ("<workload>.<kernel>") from the committed rocprofv3 counter
+    summary, or None when absent or when that kernel's source file changed since the
+    counters were taken."""
     import hashlib
     if not os.path.exists(TRAFFIC_FILE):
         return None
@@ -170,14 +171,16 @@ def read_traffic(kernel: str):
             continue
         k, v = line.split(":", 1)
         rec[k.strip()] = v.strip()
-    src = os.path.join(ROOT, "bit_quantized_fine_nf4_amd", "csrc", rec.get("source", "linear.hip"))
-    if not os.path.exists(src):
+    src = rec.get(f"{key}.source")
+    if src is None or f"{key}.bytes_per_launch" not in rec:
         return None
-    sha = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
-    if rec.get("source_sha256_16") != sha:
+    path = os.path.join(ROOT, "bit_quantized_fine_nf4_amd", "csrc", src)
+    if not os.path.exists(path):
         return None
-    key = f"{kernel}.bytes_per_launch"
-    return round(float(rec[key])) if key in rec else None
+    sha = hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+    if rec.get(f"source.{src}") != sha:
+        return None
+    return round(float(rec[f"{key}.bytes_per_launch"]))
 
 
 def cpu_oracle_attn_proj(wl_mod, target_s):
@@ -313,7 +316,7 @@ def bench_attn_proj(args, torch, nf4, wl):
         tkey = "gemm_fwd"
     achieved = dom_flops / dom_ms / 1e9
     roofline = {"bound": "mfma", "achieved": round(achieved, 3), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": read_traffic(tkey),
+                "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": read_traffic(f"{c.name}.{tkey}"),
                 "kernel": dom, "kernel_ms": round(dom_ms, 5), "flop_per_launch": dom_flops}
     value = (fwd_f + bwd_f) / (ms_per_step * 1e-3) / 1e12
     line = {"metric": METRIC, "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,

@@ -15,9 +15,7 @@
 //                        along o); the rank-r LoRA product is added as extra
 //                        K steps on the same accumulators (the 256x256
 //                        forward tiles run nf4_gemm_wide_fwd_kernel)
-//   nf4_gemv_kernel      M <= 16 forward: streams the codes once, decodes a
-//                        byte (two codes) per LDS lookup, applies the block
-//                        scale after each 64-wide MFMA pair
+//   (the M <= 16 forward, nf4_gemv_stream_kernel, is in gemv.hip)
 //   nf4_gemv_dx_kernel   M <= 16 dX: streams the codes once in 64-row stages
 //                        through LDS; 4-bit transposing reads give each lane
 //                        a column's codes, a byte table yields the bf16 MFMA
@@ -33,6 +31,7 @@
 
 #include "linear.h"
 #include "gemm.h"
+#include "gemv.h"
 
 #include <type_traits>
 
@@ -294,208 +293,6 @@ __global__ __launch_bounds__(256) void lora_rank_reduce_kernel(RankParams p) {
     if (p.out2 && q < p.ld2) p.out2[m * p.ld2 + q] = q < p.r ? to_bf16(p.s * sum) : (uint16_t)0;
   }
   rank_extras(p, gt, gn);
-}
-
-// ---------------------------------------------------------------------------
-// Few-token forward (M <= 16): Y[m][n] = sum_k X[m][k] W_hat[n][k] (+ LoRA).
-// Pure streaming of the codes ([TT] §3 storage; [MC] "The algebra" Eq. 3 for
-// the output).  A workgroup owns 64 output features and walks the whole K in
-// stages of 256 weights (4 blocks): every stage (64 rows x 128 code bytes,
-// 16 tokens x 512 activation bytes, 64 x 4 block scales) is fetched by all
-// 256 threads with coalesced loads two stages ahead of use, parked in
-// registers, then written to a double-buffered, XOR-swizzled LDS tile.
-// Wave w takes block w of every stage for all 64 rows (four 16-row MFMA
-// groups share one activation fragment) with 16x16x32 MFMAs, tokens being the
-// MFMA rows.  The B operand is bf16(level[c]) from a byte -> bf16-pair table;
-// the block scale a_hat multiplies each block's float32 partial.  The four
-// waves' partial sums meet in LDS at the end.
-// ---------------------------------------------------------------------------
-struct GemvParams {
-  const uint16_t *X;
-  int64_t ldx;
-  int M;
-  const uint8_t *codes;
-  const int8_t *qabsmax;
-  const float *scale2;
-  const float *mean;
-  int64_t K, N;
-  const uint16_t *sT;  // [M][ldt] bf16, s already applied (r > 0)
-  int ldt;
-  int r;
-  const uint16_t *L2;  // [r][N] bf16
-  uint16_t *Y;
-  int64_t ldy;
-  float level[16];
-};
-
-constexpr int kGvRows = 64;          // output features per workgroup
-constexpr int kGvKS = 256;           // weights along K per stage (4 blocks)
-constexpr int kGvCodeB = kGvKS / 2;  // code bytes per row per stage
-constexpr int kGvXB = kGvKS * 2;     // activation bytes per token per stage
-constexpr int kGvThreads = 512;      // 8 waves: wave w takes block w%4, row groups 2(w/4), 2(w/4)+1
-// Lookup table: 32 copies of the 256-entry table interleaved so that lane l
-// only touches banks l%32 and l%32 + 32 (conflict-free 32-lane phases).
-constexpr int kGvLutWords = 256 * 32;
-
-struct GvStage {
-  u32x4 c;     // codes: 16 bytes of the stage tile
-  u32x4 x;     // activations: 16 bytes of the stage tile
-  uint32_t q;  // one int8 block scale (threads < 256: row tid/4, block tid%4)
-  float s2;    // its second-level scale
-};
-
-constexpr int kGvOOB = (int)0x80000000u;  // offset past every buffer: the load returns zero
-
-// MT: token-count class (1, 4 or 16); output token 4g + v exists only for
-// v < MT when MT < 4, so the block-scale FMAs for absent tokens are skipped.
-template <int MT>
-__global__ __launch_bounds__(kGvThreads) void nf4_gemv_kernel(GemvParams p) {
-  __shared__ uint32_t lut[kGvLutWords];
-  // stage tiles: codes [2][64 rows][128 B], activations [2][16 tokens][512 B];
-  // reused for the cross-wave sum after the K loop
-  __shared__ __attribute__((aligned(16))) uint8_t tiles[2 * kGvRows * kGvCodeB + 2 * 16 * kGvXB];
-  __shared__ __attribute__((aligned(16))) float abuf[2][4 * kGvRows];
-  uint8_t(*cbuf)[kGvRows * kGvCodeB] = reinterpret_cast<uint8_t(*)[kGvRows * kGvCodeB]>(tiles);
-  uint8_t(*xbuf)[16 * kGvXB] = reinterpret_cast<uint8_t(*)[16 * kGvXB]>(tiles + 2 * kGvRows * kGvCodeB);
-  __shared__ float lv[16];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  if (tid < 16) lv[tid] = p.level[tid];
-  __syncthreads();
-  for (int i = tid; i < kGvLutWords; i += kGvThreads) {
-    const int e = i >> 5;  // word i = 32 e + copy
-    lut[i] = pack_bf16x2(lv[e >> 4], lv[e & 15]);
-  }
-
-  const int64_t n0 = (int64_t)blockIdx.x * kGvRows;
-  const int64_t rowB = p.K >> 1, nblk = p.K >> 6;
-  const int nst = (int)((p.K + kGvKS - 1) / kGvKS);
-  const float mu = *p.mean;
-  // Buffer views: the workgroup's 64 code rows, its 64 rows of int8 scales,
-  // all second-level scales, the M activation rows.  Per-thread offsets are
-  // fixed; the stage advances through the scalar offset.  Codes and scales
-  // past a row's end belong to the next row (or read as zero at the end of
-  // the view): they are finite and always meet zero activations, because
-  // activations past K (and tokens >= M) are forced to zero.
-  const __amdgpu_buffer_rsrc_t rc = gv_rsrc(p.codes + n0 * rowB, kGvRows * rowB);
-  const __amdgpu_buffer_rsrc_t rq = gv_rsrc(p.qabsmax + n0 * nblk, kGvRows * nblk);
-  const __amdgpu_buffer_rsrc_t rs = gv_rsrc(p.scale2, ((p.N * nblk + kChunk - 1) / kChunk) * 4);
-  const __amdgpu_buffer_rsrc_t rx = gv_rsrc(p.X, ((int64_t)(p.M - 1) * p.ldx + p.K) * 2);
-  const int cr = tid >> 3, cp = tid & 7;  // code piece: row, 16-byte piece
-  const int voc = (int)(cr * rowB) + 16 * cp;
-  const int lc = (cr * 8 + (cp ^ ((cr >> 1) & 7))) * 16;
-  const int xm = tid >> 5, xp = tid & 31;  // activation piece: token, 16-byte piece
-  const int vox = xm < p.M ? (int)((xm * p.ldx + 8 * xp) * 2) : kGvOOB;
-  const int xlim = p.K > 8 * xp ? (int)((p.K - 8 * xp + kGvKS - 1) / kGvKS) : 0;  // stages with this piece inside K
-  const int lx = (xm * 32 + (xp ^ xm)) * 16;
-  const bool sthr = tid < 4 * kGvRows;         // scale role (waves 0-3)
-  const int srow = (tid >> 2) & 63, sblk = tid & 3;
-  const int voq = (int)(srow * nblk) + sblk;
-  const int64_t sbase = (n0 + srow) * nblk + sblk;
-  const int la = (sblk * 16 + (srow & 15)) * 4 + (srow >> 4);  // abuf [block][n][group]
-
-  auto load = [&](GvStage &R, int st) {
-    R.c = __builtin_amdgcn_raw_buffer_load_b128(rc, voc, st * kGvCodeB, 0);
-    R.x = __builtin_amdgcn_raw_buffer_load_b128(rx, st < xlim ? vox : kGvOOB, st * kGvXB, 0);
-    R.q = __builtin_amdgcn_raw_buffer_load_b8(rq, sthr ? voq : kGvOOB, 4 * st, 0);
-    R.s2 = __builtin_bit_cast(
-        float, __builtin_amdgcn_raw_buffer_load_b32(rs, sthr ? (int)(((sbase + 4 * st) >> 8) * 4) : kGvOOB, 0, 0));
-  };
-  auto store = [&](const GvStage &R, int buf) {
-    *reinterpret_cast<u32x4 *>(&cbuf[buf][lc]) = R.c;
-    *reinterpret_cast<u32x4 *>(&xbuf[buf][lx]) = R.x;
-    if (sthr) abuf[buf][la] = scale_hat((int8_t)(R.q & 0xFF), R.s2, mu);
-  };
-  // compute role: token / feature index within a 16x16 MFMA tile, k-group
-  const int n = lane & 15, g = lane >> 4;
-  const int lsel = lane & 31;
-  const int blk = wave & 3, rp = wave >> 2;
-  const int pcw = 2 * blk + (g >> 1);  // code piece of this block for this k-group
-  const int pxa = 8 * blk + 2 * g;     // activation pieces pxa, pxa + 1
-  const int la0 = (n * 32 + (pxa ^ n)) * 16, la1 = (n * 32 + ((pxa + 1) ^ n)) * 16;
-  int lcode[2];
-#pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const int row = 16 * (2 * rp + h) + n;
-    lcode[h] = (row * 8 + (pcw ^ ((row >> 1) & 7))) * 16 + 8 * (g & 1);
-  }
-  constexpr int NV = MT < 4 ? MT : 4;
-  float acc[2][NV];
-#pragma unroll
-  for (int h = 0; h < 2; ++h)
-#pragma unroll
-    for (int v = 0; v < NV; ++v) acc[h][v] = 0.0f;
-  auto compute = [&](int buf) {
-    const uint8_t *cb = cbuf[buf];
-    const uint8_t *xb = xbuf[buf];
-    const u32x4 a0 = *reinterpret_cast<const u32x4 *>(xb + la0);
-    const u32x4 a1 = *reinterpret_cast<const u32x4 *>(xb + la1);
-    const f32x2 ah = *reinterpret_cast<const f32x2 *>(&abuf[buf][(blk * 16 + n) * 4 + 2 * rp]);
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const u32x2 cw = *reinterpret_cast<const u32x2 *>(cb + lcode[h]);
-      u32x4 bw[2];
-#pragma unroll
-      for (int e = 0; e < 2; ++e) {
-        const uint32_t w = e ? cw.y : cw.x;
-#pragma unroll
-        for (int t = 0; t < 4; ++t) bw[e][t] = lut[((w >> (8 * t)) & 0xFF) * 32 + lsel];
-      }
-      f32x4 part = mfma16(a0, bw[0], f32x4{0.0f, 0.0f, 0.0f, 0.0f});
-      part = mfma16(a1, bw[1], part);
-#pragma unroll
-      for (int v = 0; v < NV; ++v) acc[h][v] = __builtin_fmaf(ah[h], part[v], acc[h][v]);
-    }
-  };
-
-  // Two register stages in flight.  Every stage issues the same four loads
-  // and the loop body is uniform: stages past the end read zero activations
-  // (an extra stage adds exactly nothing), which keeps the number of loads in
-  // flight identical on every path, so the wait before each LDS store covers
-  // only the older register stage.  The scheduling fences keep the compiler
-  // from interleaving the two register stages (which would make every wait
-  // cover both).
-  GvStage ra, rb;
-  load(ra, 0);
-  store(ra, 0);
-  __builtin_amdgcn_sched_barrier(0);
-  load(ra, 1);
-  __builtin_amdgcn_sched_barrier(0);
-  load(rb, 2);
-  __builtin_amdgcn_sched_barrier(0);
-  __syncthreads();
-  for (int st = 0; st < nst; st += 2) {
-    compute(0);
-    store(ra, 1);
-    load(ra, st + 3);
-    __builtin_amdgcn_sched_barrier(0);
-    __syncthreads();
-    compute(1);
-    store(rb, 0);
-    load(rb, st + 4);
-    __builtin_amdgcn_sched_barrier(0);
-    __syncthreads();
-  }
-
-  // Cross-wave sum: acc[h][v] of wave (blk, rp) = partial Y[token 4g + v][row 16(2rp + h) + n]
-  // red[block][token][row], rows padded to 68 floats: the 64 lanes of a store
-  // (16 rows x 4 token groups) land in 64 distinct banks.
-  constexpr int kRedLd = 68;
-  static_assert(4 * 16 * kRedLd * 4 <= sizeof(tiles), "reduction fits in the stage tiles");
-  float *red = reinterpret_cast<float *>(tiles);
-#pragma unroll
-  for (int h = 0; h < 2; ++h)
-#pragma unroll
-    for (int v = 0; v < NV; ++v) red[(blk * 16 + 4 * g + v) * kRedLd + 16 * (2 * rp + h) + n] = acc[h][v];
-  __syncthreads();
-  const int row = tid & 63;
-  const int64_t col = n0 + row;
-  for (int m = tid >> 6; m < p.M; m += kGvThreads / 64) {
-    float y = red[m * kRedLd + row] + red[(16 + m) * kRedLd + row] + red[(32 + m) * kRedLd + row] +
-              red[(48 + m) * kRedLd + row];
-    for (int q = 0; q < p.r; ++q)
-      y = __builtin_fmaf(bf16_lo(p.sT[(int64_t)m * p.ldt + q]), bf16_lo(p.L2[(int64_t)q * p.N + col]), y);
-    p.Y[(int64_t)m * p.ldy + col] = to_bf16(y);
-  }
 }
 
 // ---------------------------------------------------------------------------
@@ -1164,6 +961,13 @@ void fill_levels(float *dst, const Nf4Tables &tab) {
   for (int i = 0; i < 16; ++i) dst[i] = tab.level[i];
 }
 
+// The few-token kernel addresses a workgroup's 64 code rows, a row's block scales
+// and a token's activations with 32-bit offsets; larger shapes take the GEMM.
+bool gemv_fits(const LinearArgs &a) {
+  const int64_t lim = (int64_t)1 << 30;
+  return 64 * (a.h / 2) < lim && a.o * (a.h / 64) < lim && 16 * a.h * 2 < lim;
+}
+
 }  // namespace
 
 void set_timing_events(int kernel, hipEvent_t start, hipEvent_t stop) {
@@ -1197,7 +1001,7 @@ hipError_t launch_linear_fwd(const LinearArgs &a, const uint16_t *X, const uint1
     const hipError_t e = rank_r(rp, true, L.RP16, at<float>(ws, L.off_tp), st);
     if (e != hipSuccess) return e;
   }
-  if (a.M <= 16) {
+  if (a.M <= 16 && gemv_fits(a)) {
     GemvParams gp{};
     gp.X = X; gp.ldx = a.h; gp.M = (int)a.M;
     gp.codes = a.codes; gp.qabsmax = a.qabsmax; gp.scale2 = a.scale2; gp.mean = a.mean;
@@ -1206,9 +1010,7 @@ hipError_t launch_linear_fwd(const LinearArgs &a, const uint16_t *X, const uint1
     gp.Y = Y; gp.ldy = a.o;
     fill_levels(gp.level, tab);
     TimedLaunch tl(2, st);
-    const unsigned grid = (unsigned)(a.o / kGvRows);
-    auto k = a.M == 1 ? nf4_gemv_kernel<1> : (a.M <= 4 ? nf4_gemv_kernel<4> : nf4_gemv_kernel<16>);
-    return launch(k, grid, kGvThreads, st, gp);
+    return launch_nf4_gemv(gp, st);
   }
   GemmParams gp{};
   gp.A = X; gp.lda = a.h;

@@ -209,6 +209,23 @@ FEW_TOKEN_BWD = [  # (M, h, o, r, s): the few-token backward (dX GEMV), several 
 ]
 
 
+FEW_TOKEN_FWD = [  # (M, h, o, r, s): the few-token forward with K not a whole number of 16-block
+    # prefetch rounds or of 256-weight activation phases, one or many workgroups, every token class
+    (1, 2368, 640, 8, 1.0),
+    (2, 64, 4096, 16, 2.0),
+    (4, 4160, 64, 0, 1.0),
+    (5, 192, 1152, 4, 0.5),
+    (13, 1088, 320, 32, 2.0),
+    (16, 5184, 192, 0, 1.0),
+]
+
+
+@pytest.mark.parametrize("M,h,o,r,s", FEW_TOKEN_FWD)
+def test_few_token_forward(M, h, o, r, s):
+    w, l1, l2, x, dy = wl.small_linear(h, o, r, M, seed=5 * M + h + o + r)
+    check_full(w, l1, l2, x, dy, s, f"few-token fwd M={M} h={h} o={o} r={r}")
+
+
 @pytest.mark.parametrize("M,h,o,r,s", FEW_TOKEN_BWD)
 def test_few_token_backward(M, h, o, r, s):
     w, l1, l2, x, dy = wl.small_linear(h, o, r, M, seed=3 * M + h + r)

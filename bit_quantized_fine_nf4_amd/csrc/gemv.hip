@@ -50,7 +50,6 @@ QL_DEV uint16_t bf16_bits(float v) { return (uint16_t)(pack_bf16x2(v, 0.0f) & 0x
 // One token
 // ---------------------------------------------------------------------------
 constexpr int kG1Threads = 256;   // 4 waves sharing the table
-constexpr int kG1Ring = 8;        // 1 KB loads in flight per wave
 constexpr int kG1TargetWaves = 2048;  // two workgroups on each of the 256 compute units
 
 template <int N>
@@ -84,7 +83,10 @@ struct G1Load {
 template <int P>
 __global__ __launch_bounds__(kG1Threads) __attribute__((amdgpu_waves_per_eu(2, 4))) void nf4_gemv1_kernel(
     GemvParams p, int rows_per_wave) {
-  static_assert(kG1Ring % P == 0 || P % kG1Ring == 0, "loads of a row line up with the ring");
+  // one row of loads in flight: deeper rings measured slower (K = 8192: one, two and
+  // four rows ahead took 26.0, 27.6 and 31.1 us), as more rows open at once cost
+  // DRAM page locality; a ring of P also starts every pass on a row boundary
+  constexpr int kG1Ring = P;
   __shared__ __attribute__((aligned(1024))) uint8_t lut[256 * 256];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);

@@ -217,6 +217,10 @@ FEW_TOKEN_FWD = [  # (M, h, o, r, s): the few-token forward with K not a whole n
     (5, 192, 1152, 4, 0.5),
     (13, 1088, 320, 32, 2.0),
     (16, 5184, 192, 0, 1.0),
+    (1, 11008, 256, 16, 2.0),     # one token, K above 8192: eight 1 KB loads per row
+    (1, 16384, 128, 0, 1.0),
+    (1, 16448, 64, 8, 0.5),       # one token, K above 16384: the MFMA kernel
+    (1, 64, 131136, 4, 1.0),      # one token, 65 rows per wave: results flushed every 64 rows
 ]
 
 

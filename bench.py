@@ -734,9 +734,14 @@ def bench_gemv(args, torch, nf4, wl):
             "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
             "config": {"workload": c.name, "h": h, "o": o, "tokens": list(wl.C4_GEMV_TOKENS), "weight_copies": copies},
             "roofline": {"bound": "hbm", "achieved": res[worst]["GB/s"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                         "frac": res[worst]["frac_hbm"], "traffic": None, "kernel": f"nf4_gemv_kernel (M={worst})"},
+                         "frac": res[worst]["frac_hbm"], "traffic": read_traffic(f"{c.name}.gemv_m{worst}"),
+                         "kernel": GEMV_KERNEL[worst]},
             "stages": {f"M={k}": v for k, v in res.items()},
             "backward_dx": {f"M={k}": v for k, v in bwd.items()}}
+
+
+# the few-token forward kernel each token count of the GEMV workload runs (K = 8192)
+GEMV_KERNEL = {1: "nf4_gemv1_kernel<4>", 4: "nf4_gemv_kernel<4>", 16: "nf4_gemv_kernel<16>"}
 
 
 def bench_small(args, torch, nf4, wl):

@@ -36,7 +36,10 @@ into bf16 weights, then merged and re-quantized to NF4), adamw (one AdamW step
 on those seven adapters' 10.0 M parameters, moments in HBM, then with the
 moments in pinned host memory), codebooks (NF4 / INT4 / FP4 with and without
 double quantization: reconstruction MSE on 2^26 N(0, 1) and Student-t(4)
-weights, and quantize + dequantize throughput per codebook).
+weights, and quantize + dequantize throughput per codebook), stream (the plain
+HBM streaming ceilings the bandwidth-bound kernels are compared with: a pure
+read, 4 bytes read per byte written and 1 read per 4 written, on 8 GiB and on
+four rotating GEMV-sized 117 MiB buffers).
 """
 from __future__ import annotations
 
@@ -64,7 +67,7 @@ def parse_args():
     ap.add_argument("--warmup", type=int, default=None, help="untimed steps (default 3 / 5)")
     ap.add_argument("--workload", default="block65b",
                     choices=["block65b", "mlp7b", "attn_proj", "codec", "gemv", "small", "merge", "adamw",
-                             "codebooks"])
+                             "codebooks", "stream"])
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the CPU oracle timing")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="target CPU work for the oracle baseline")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -619,6 +622,68 @@ def cpu_oracle_block(wl, c, host_w, target_s, ns=128):
             "s_per_sample": round(t_total / reps, 4)}
 
 
+STREAM_SHAPES = [(d, b) for d in (1, 2, 4, 8) for b in (1024, 2048, 4096, 8192, 16384)]
+
+
+def stream_rate(torch, nf4, rd, wr, srcs, dst, tiles, reps, shapes=STREAM_SHAPES, warmup=2):
+    """Best GB/s (bytes read + written) of the stream probe over `tiles` tiles across the launch
+    shapes (tiles per wave and pass, workgroups), rotating over the source buffers `srcs`; each
+    shape's rate is the median of `reps` launches timed with fence-free events.
+    Returns (GB/s, ms, {"depth": d, "blocks": b})."""
+    E = HipEvents(torch).event
+    best = None
+    for depth, blocks in shapes:
+        for i in range(warmup):
+            nf4.qlora_stream_probe(rd, wr, srcs[i % len(srcs)], dst, tiles, depth=depth, blocks=blocks)
+        torch.cuda.synchronize()
+        ev = [(E(enable_timing=True), E(enable_timing=True)) for _ in range(reps)]
+        for i in range(reps):
+            ev[i][0].record()
+            nf4.qlora_stream_probe(rd, wr, srcs[i % len(srcs)], dst, tiles, depth=depth, blocks=blocks)
+            ev[i][1].record()
+        torch.cuda.synchronize()
+        ms = statistics.median(a.elapsed_time(b) for a, b in ev)
+        if best is None or ms < best[1]:
+            best = (tiles * 1024 * (rd + wr) / ms / 1e6, ms, {"depth": depth, "blocks": blocks})
+    return best
+
+
+def bench_stream(args, torch, nf4, wl):
+    """Plain streaming ceilings: the stream probe at the codec's byte mixes on an 8 GiB source,
+    and a pure read over four rotating buffers of the GEMV weight's code size (4 x 117 MiB, more
+    than the last-level cache).  Not a step of the method: the reference rate for the HBM-bound
+    kernels."""
+    dev = "cuda:0"
+    reps = max(args.steps, 8)
+    big = torch.full((1 << 31,), 0x5A5A5A5A, dtype=torch.int32, device=dev)  # 8 GiB source
+    out = torch.empty(1 << 31, dtype=torch.int32, device=dev)  # 8 GiB destination
+    res = {}
+    for rd, wr in ((1, 0), (4, 1), (1, 4)):
+        tiles = (8 << 30) // (1024 * max(rd, wr))  # the larger side spans the 8 GiB buffer
+        gbs, ms, shape = stream_rate(torch, nf4, rd, wr, [big], out, tiles, reps)
+        res[f"read{rd}_write{wr}_8GiB"] = {"ms": round(ms, 4), "GB/s": round(gbs, 2),
+                                            "frac_hbm": round(gbs / PEAK_HBM_GBS, 4), "shape": shape}
+    del big, out
+    c = wl.C4_GEMV
+    nbytes = c.linears[0].h * c.linears[0].o // 2
+    srcs = [torch.full((nbytes // 4,), 0x3C3C3C3C, dtype=torch.int32, device=dev) for _ in range(4)]
+    sink = torch.empty(4, dtype=torch.int32, device=dev)
+    gbs, ms, shape = stream_rate(torch, nf4, 1, 0, srcs, sink, nbytes // 1024, reps)
+    res["read1_write0_gemv_codes_x4"] = {"ms": round(ms, 5), "GB/s": round(gbs, 2),
+                                         "frac_hbm": round(gbs / PEAK_HBM_GBS, 4), "bytes": nbytes,
+                                         "shape": shape}
+    top = res["read1_write0_8GiB"]
+    return {"metric": METRIC, "value": top["GB/s"], "unit": "GB/s", "n_gpus": 1, "steps": reps,
+            "warmup": 2, "ms_per_step": top["ms"], "higher_is_better": True, "scaling": "weak",
+            "vs_baseline": None, "dtype": "u32", "data": "synthetic",
+            "config": {"workload": "stream_probe", "tile_kb_read_write": [[1, 0], [4, 1], [1, 4]],
+                       "source": "8 GiB, and 4 rotating buffers of the 8192 x 28672 NF4 codes"},
+            "roofline": {"bound": "hbm", "achieved": top["GB/s"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                         "frac": top["frac_hbm"], "traffic": None,
+                         "kernel": f"stream_probe_kernel<1, 0, {top['shape']['depth']}>"},
+            "stages": res}
+
+
 def bench_codec(args, torch, nf4, wl):
     dev = "cuda:0"
     n = wl.C4_CODEC_N
@@ -655,6 +720,10 @@ def bench_codec(args, torch, nf4, wl):
     ms = [statistics.mean(e[i].elapsed_time(e[i + 1]) for e in evs) for i in range(3)]
     qb, dqb, deqb = codec_bytes(n, 2, 2)
     gbs = [qb / ms[0] / 1e6, dqb / ms[1] / 1e6, deqb / ms[2] / 1e6]
+    # the plain stream ceilings of the same byte mixes (after the timed steps; the probe
+    # overwrites `out`): read 2n, write n/2 like quantize; read n/2, write 2n like dequantize
+    ceil_q = stream_rate(torch, nf4, 4, 1, [w], out, (2 * n) // 4096, 5)[0]
+    ceil_d = stream_rate(torch, nf4, 1, 4, [codes], out, (n // 2) // 1024, 5)[0]
     dom = max(range(3), key=lambda i: ms[i])
     names = ["quantize_kernel<bf16>", "double_quant", "dequantize_kernel<bf16>"]
     total_bytes = qb + dqb + deqb
@@ -666,10 +735,14 @@ def bench_codec(args, torch, nf4, wl):
             "roofline": {"bound": "hbm", "achieved": round(gbs[dom], 2), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                          "frac": round(gbs[dom] / PEAK_HBM_GBS, 4), "traffic": None, "kernel": names[dom]},
             "stages": {"quantize": {"ms": round(ms[0], 4), "GB/s": round(gbs[0], 2),
-                                    "frac_hbm": round(gbs[0] / PEAK_HBM_GBS, 4)},
+                                    "frac_hbm": round(gbs[0] / PEAK_HBM_GBS, 4),
+                                    "stream_ceiling_GB/s": round(ceil_q, 2),
+                                    "frac_of_ceiling": round(gbs[0] / ceil_q, 4)},
                        "double_quant": {"ms": round(ms[1], 4), "GB/s": round(gbs[1], 2)},
                        "dequantize_bf16": {"ms": round(ms[2], 4), "GB/s": round(gbs[2], 2),
-                                           "frac_hbm": round(gbs[2] / PEAK_HBM_GBS, 4)}}}
+                                           "frac_hbm": round(gbs[2] / PEAK_HBM_GBS, 4),
+                                           "stream_ceiling_GB/s": round(ceil_d, 2),
+                                           "frac_of_ceiling": round(gbs[2] / ceil_d, 4)}}}
 
 
 def bench_gemv(args, torch, nf4, wl):
@@ -729,6 +802,12 @@ def bench_gemv(args, torch, nf4, wl):
         bwd[m] = {"kernel_ms": round(ms, 5), "call_ms": round(call_ms, 5), "GB/s": round(bytes_ / ms / 1e6, 2),
                   "frac_hbm": round(bytes_ / ms / 1e6 / PEAK_HBM_GBS, 4), "bytes": bytes_}
     worst = min(res, key=lambda k: res[k]["GB/s"])
+    # read-only stream ceiling over the same four rotating code buffers
+    sink = torch.empty(4, dtype=torch.int32, device=dev)
+    ceil_r = stream_rate(torch, nf4, 1, 0, [W.codes for W in Ws], sink, Ws[0].codes.numel() // 1024,
+                         max(args.steps, 8))[0]
+    for v in res.values():
+        v["frac_of_read_ceiling"] = round(v["GB/s"] / ceil_r, 4)
     return {"metric": METRIC, "value": res[16]["GB/s"], "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
             "warmup": args.warmup, "ms_per_step": res[16]["ms"], "higher_is_better": True, "scaling": "weak",
             "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
@@ -737,6 +816,7 @@ def bench_gemv(args, torch, nf4, wl):
                          "frac": res[worst]["frac_hbm"], "traffic": read_traffic(f"{c.name}.gemv_m{worst}"),
                          "kernel": GEMV_KERNEL[worst]},
             "stages": {f"M={k}": v for k, v in res.items()},
+            "read_stream_ceiling_GB/s": round(ceil_r, 2),
             "backward_dx": {f"M={k}": v for k, v in bwd.items()}}
 
 
@@ -958,7 +1038,7 @@ def main():
         torch.cuda.synchronize()
         del src, dst
     fn = {"attn_proj": bench_attn_proj, "codec": bench_codec, "gemv": bench_gemv, "small": bench_small,
-          "merge": bench_merge, "adamw": bench_adamw, "codebooks": bench_codebooks,
+          "merge": bench_merge, "adamw": bench_adamw, "codebooks": bench_codebooks, "stream": bench_stream,
           "block65b": lambda *a: bench_block(*a, wl.C5), "mlp7b": lambda *a: bench_block(*a, wl.C3)}[args.workload]
     line = fn(args, torch, nf4, wl)
     host_w = line.pop("_cpu_sample_host", None)

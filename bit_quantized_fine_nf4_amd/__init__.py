@@ -29,7 +29,7 @@ EXPORTED = ("qlora_quantize", "qlora_double_quant", "qlora_dequantize", "qlora_l
             "qlora_quantize_cb", "qlora_dequantize_cb", "qlora_dequantize_nodq", "qlora_codebook_levels",
             "qlora_linear_fwd_cb", "qlora_linear_bwd_cb", "qlora_merge_adapter_cb", "qlora_merge_requantize_cb",
             "qlora_silu_gate_fwd", "qlora_silu_gate_bwd", "qlora_grad_sum", "qlora_double_quant_noalloc",
-            "qlora_workspace_size",
+            "qlora_workspace_size", "qlora_stream_probe",
             "qlora_status_string", "qlora_nf4_levels", "qlora_set_timing_events")
 
 
@@ -72,6 +72,7 @@ def _load():
     L.qlora_silu_gate_fwd.argtypes = [vp, vp, i64, vp, vp]
     L.qlora_silu_gate_bwd.argtypes = [vp, vp, vp, i64, vp, vp, vp]
     L.qlora_grad_sum.argtypes = [ctypes.POINTER(vp), i32, i64, vp, vp]
+    L.qlora_stream_probe.argtypes = [i32, i32, i32, i32, vp, vp, i64, vp]
     L.qlora_adamw_step.argtypes = [vp, vp, vp, vp, i64, i64, f32, f32, f32, f32, f32, vp, vp]
     L.qlora_workspace_size.argtypes = [st, i64, i64, i64, i32, ctypes.POINTER(sz)]
     L.qlora_status_string.argtypes = [st]
@@ -380,6 +381,17 @@ def qlora_silu_gate_bwd(G: torch.Tensor, U: torch.Tensor, dH: torch.Tensor, dG: 
     _check(lib.qlora_silu_gate_bwd(_ptr(G), _ptr(U), _ptr(dH), n, _ptr(dG), _ptr(dU), _stream(G.device)),
            "qlora_silu_gate_bwd")
     return dG, dU
+
+
+def qlora_stream_probe(rd: int, wr: int, src: torch.Tensor, dst: torch.Tensor, n_tiles: int,
+                       depth: int = 2, blocks: int = 0) -> None:
+    """Measurement helper: stream n_tiles tiles of rd KB read and wr KB written, depth tiles per
+    wave and pass, `blocks` workgroups (0: the library's default) (see the C header)."""
+    _dev_check(src, dst)
+    if src.numel() * src.element_size() < n_tiles * 1024 * rd or dst.numel() * dst.element_size() < max(16, n_tiles * 1024 * wr):
+        raise ValueError("qlora_stream_probe: buffers too small for n_tiles")
+    _check(lib.qlora_stream_probe(rd, wr, depth, blocks, _ptr(src), _ptr(dst), n_tiles, _stream(src.device)),
+           "qlora_stream_probe")
 
 
 def qlora_grad_sum(parts, out: Optional[torch.Tensor] = None) -> torch.Tensor:

@@ -19,7 +19,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libqlora_nf4.so")
-SOURCES = ["nf4_tables.hip", "codec.hip", "linear.hip", "gemv.hip", "nf4_gemm.hip", "nf4_gemm_wide.hip", "optim.hip", "glue.hip", "api.hip"]
+SOURCES = ["nf4_tables.hip", "codec.hip", "linear.hip", "gemv.hip", "nf4_gemm.hip", "nf4_gemm_wide.hip", "optim.hip", "glue.hip", "stream.hip", "api.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

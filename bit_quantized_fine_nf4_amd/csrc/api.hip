@@ -7,6 +7,7 @@
 #include "glue.h"
 #include "linear.h"
 #include "optim.h"
+#include "stream.h"
 
 #include <cmath>
 #include <cstddef>
@@ -134,6 +135,17 @@ qlora_status_t qlora_grad_sum(const uint16_t *const *parts, int32_t k, int64_t n
     sp.p[i] = parts[i];
   }
   return launch_status(launch_grad_sum(sp, n, out, reinterpret_cast<hipStream_t>(stream)));
+}
+
+qlora_status_t qlora_stream_probe(int32_t rd, int32_t wr, int32_t depth, int32_t blocks, const void *src, void *dst,
+                                  int64_t n_tiles, void *stream) {
+  const bool kind = (rd == 1 && wr == 0) || (rd == 4 && wr == 1) || (rd == 1 && wr == 4);
+  const bool shape = (depth == 1 || depth == 2 || depth == 4 || depth == 8) && blocks >= 0 && blocks <= (1 << 20);
+  if (!kind || !shape || !src || !dst || n_tiles < 1) return QLORA_ERR_INVALID_VALUE;
+  if (!aligned(src, 16) || !aligned(dst, 16)) return QLORA_ERR_INVALID_VALUE;
+  if (n_tiles > ((int64_t)1 << 40) / 4096) return QLORA_ERR_INVALID_VALUE;  // beyond any device's memory
+  return launch_status(
+      launch_stream_probe(rd, wr, depth, blocks, src, dst, n_tiles, reinterpret_cast<hipStream_t>(stream)));
 }
 
 qlora_status_t qlora_set_timing_events(int32_t kernel, void *start, void *stop) {

@@ -345,6 +345,29 @@ qlora_status_t qlora_workspace_size(qlora_op_t op, int64_t a, int64_t b, int64_t
  */
 qlora_status_t qlora_set_timing_events(int32_t kernel, void *start, void *stop);
 
+/*
+ * Stream probe, a measurement helper rather than a step of the method: the
+ * plain HBM streaming rate for the byte mix of a bandwidth-bound kernel, the
+ * ceiling its own rate is compared with.  Moves `n_tiles` tiles; tile t reads
+ * the 1024 * rd contiguous bytes of `src` at byte 1024 * rd * t and writes the
+ * 1024 * wr contiguous bytes of `dst` at byte 1024 * wr * t, with fully
+ * coalesced 16-byte accesses.  Launch shape: `blocks` workgroups of 256
+ * threads (0: min(ceil(n_tiles / 8), 8192); at most 2^20), each wave taking
+ * `depth` tiles (1, 2, 4 or 8) per pass with all their loads issued first; a
+ * caller takes the best rate over a sweep of shapes as the ceiling.
+ *   (rd, wr) = (1, 0)  read only (the few-token forward's weight stream);
+ *              (4, 1)  four bytes read per byte written (quantization of bf16
+ *                      weights reads 2 and writes 0.52 bytes per weight);
+ *              (1, 4)  the reverse (dequantization to bf16).
+ *  src: n_tiles * 1024 * rd bytes; dst: n_tiles * 1024 * wr bytes, or 16 bytes
+ *  when wr = 0 (it may receive one store).  Both 16-byte aligned.  The values
+ *  written are a function of those read and otherwise unspecified.
+ *  QLORA_ERR_INVALID_VALUE for any other (rd, wr) or depth, blocks out of
+ *  range, NULL or misaligned pointers, or n_tiles < 1.
+ */
+qlora_status_t qlora_stream_probe(int32_t rd, int32_t wr, int32_t depth, int32_t blocks, const void *src, void *dst,
+                                  int64_t n_tiles, void *stream);
+
 /* Static description of a status code (never NULL). */
 const char *qlora_status_string(qlora_status_t status);
 

@@ -267,3 +267,19 @@ def test_double_quant_noalloc_rejects_bad_arguments():
     assert dq(FAKE, 1 << 32, FAKE, FAKE, FAKE, None) == INV
     assert dq(ODD, 10, FAKE, FAKE, FAKE, None) == INV
     assert dq(FAKE, 10, FAKE, None, FAKE, None) == INV
+
+
+def test_stream_probe_rejects_bad_arguments():
+    sp = lib.qlora_stream_probe
+    assert sp(2, 1, 2, 0, FAKE, FAKE, 4, None) == INV       # only (1, 0), (4, 1), (1, 4)
+    assert sp(1, 1, 2, 0, FAKE, FAKE, 4, None) == INV
+    assert sp(1, 0, 3, 0, FAKE, FAKE, 4, None) == INV       # depth 1, 2, 4 or 8
+    assert sp(1, 0, 16, 0, FAKE, FAKE, 4, None) == INV
+    assert sp(1, 0, 2, -1, FAKE, FAKE, 4, None) == INV      # blocks in [0, 2^20]
+    assert sp(1, 0, 2, (1 << 20) + 1, FAKE, FAKE, 4, None) == INV
+    assert sp(1, 0, 2, 0, None, FAKE, 4, None) == INV
+    assert sp(4, 1, 2, 0, FAKE, None, 4, None) == INV
+    assert sp(1, 4, 2, 0, ODD, FAKE, 4, None) == INV
+    assert sp(1, 4, 2, 0, FAKE, ODD, 4, None) == INV
+    assert sp(1, 0, 2, 0, FAKE, FAKE, 0, None) == INV
+    assert sp(1, 0, 2, 0, FAKE, FAKE, 1 << 40, None) == INV

@@ -287,8 +287,20 @@ __global__ __launch_bounds__(256) void lora_rank_reduce_kernel(RankParams p) {
     const int64_t m = idx / W;
     const int q = (int)(idx % W);
     float sum = 0.0f;
-    if (q < p.r)
-      for (int k = 0; k < p.ks; ++k) sum += p.part[k * stride + m * RP + q];
+    if (q < p.r) {
+      // the partials were written by other workgroups (other L2s): issue eight
+      // loads before adding, still in split order
+      const float *src = p.part + m * RP + q;
+      int k = 0;
+      for (; k + 8 <= p.ks; k += 8) {
+        float v[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) v[j] = src[(k + j) * stride];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) sum += v[j];
+      }
+      for (; k < p.ks; ++k) sum += src[k * stride];
+    }
     if (p.out1 && q < p.ld1) p.out1[m * p.ld1 + q] = q < p.r ? to_bf16(sum) : (uint16_t)0;
     if (p.out2 && q < p.ld2) p.out2[m * p.ld2 + q] = q < p.r ? to_bf16(p.s * sum) : (uint16_t)0;
   }
@@ -502,11 +514,26 @@ __global__ __launch_bounds__(256) void lora_grad_reduce_kernel(GradProblem pa, G
   float sum[PER];
 #pragma unroll
   for (int u = 0; u < PER; ++u) sum[u] = 0.0f;
-  for (int k = 0; k < S; ++k) {
+  // row (tid + 256u) / RP, column % RP; loads of up to 16 / PER splits in flight
+  // before they are added in split order
+  constexpr int KB = PER >= 16 ? 1 : 16 / PER;
+  int k = 0;
+  for (; k + KB <= S; k += KB) {
+    float v[KB][PER];
+#pragma unroll
+    for (int j = 0; j < KB; ++j)
+#pragma unroll
+      for (int u = 0; u < PER; ++u) v[j][u] = base[(int64_t)(k + j) * prows * RP + tid + 256 * u];
+#pragma unroll
+    for (int j = 0; j < KB; ++j)
+#pragma unroll
+      for (int u = 0; u < PER; ++u) sum[u] += v[j][u];
+  }
+  for (; k < S; ++k) {
     const float *src = base + (int64_t)k * prows * RP;
     float v[PER];
 #pragma unroll
-    for (int u = 0; u < PER; ++u) v[u] = src[tid + 256 * u];  // row (tid + 256u) / RP, column % RP
+    for (int u = 0; u < PER; ++u) v[u] = src[tid + 256 * u];
 #pragma unroll
     for (int u = 0; u < PER; ++u) sum[u] += v[u];
   }
@@ -928,14 +955,29 @@ __global__ __launch_bounds__(256) void gemv_dx_finish_kernel(const float *part, 
   const bool live = grp < groups;
   const int64_t k = (live ? grp : groups - 1) * 8;
   float v[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-  for (int c = w; c < chunks; c += 4) {
-    const float *src = part + ((int64_t)c * M + m) * h + k;
-    const f32x4 a = *reinterpret_cast<const f32x4 *>(src), b = *reinterpret_cast<const f32x4 *>(src + 4);
+  // wave w adds chunks w, w + 4, ... in order, four chunks' loads in flight at a time
+  auto add = [&](const f32x4 &a, const f32x4 &b) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       v[i] += a[i];
       v[4 + i] += b[i];
     }
+  };
+  int c = w;
+  for (; c + 12 < chunks; c += 16) {
+    f32x4 a[4], b[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float *src = part + ((int64_t)(c + 4 * j) * M + m) * h + k;
+      a[j] = *reinterpret_cast<const f32x4 *>(src);
+      b[j] = *reinterpret_cast<const f32x4 *>(src + 4);
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) add(a[j], b[j]);
+  }
+  for (; c < chunks; c += 4) {
+    const float *src = part + ((int64_t)c * M + m) * h + k;
+    add(*reinterpret_cast<const f32x4 *>(src), *reinterpret_cast<const f32x4 *>(src + 4));
   }
 #pragma unroll
   for (int i = 0; i < 8; ++i) red[w][l][i] = v[i];

@@ -17,14 +17,19 @@
 // MFMA group kk takes k = 32g + 8kk + 0..7, exactly the lane's bytes 4kk..4kk+3.
 // B therefore never passes through LDS and needs no synchronisation.
 // A (X, k-contiguous) is shared by all four waves: it goes from memory straight
-// into a 3-stage LDS ring (buffer_load ... lds, 16 bytes per lane, 1 KB = 8 rows
-// per instruction) two K steps ahead, in unpadded 128-byte rows whose 16-byte
-// chunks are XOR-swizzled by row so the fragment reads are free of bank
-// conflicts.  One barrier per K step.
+// into a 4-stage LDS ring (buffer_load ... lds, 16 bytes per lane, 1 KB = 8 rows
+// per instruction) between two and three K steps ahead, in unpadded 128-byte rows
+// whose 16-byte chunks are XOR-swizzled by row so the fragment reads are free of
+// bank conflicts.  One barrier per K step, placed after the step's third MFMA
+// group rather than at its start: the last group's MFMAs then cover the reads of
+// the next step's first A fragments and table entries, so a step no longer opens
+// with an LDS round trip (2048 tokens, one MI355X: 314 -> 258 us on 8192 -> 8192,
+// 826 -> 774 us on 8192 -> 22016, bit-identical results).
 // Per K step and wave: 8 A-fragment reads per MFMA group, 64 MFMAs, 32 table
 // reads and about 5 VALU operations per code byte for the next step's decode
 // (issued between the current step's MFMA groups), 14 vector-memory operations
-// (8 A copies, 2 code, 2 int8-scale, 2 second-level-scale loads) two steps ahead.
+// (8 A copies, 2 code, 2 int8-scale, 2 second-level-scale loads), the B loads two
+// steps ahead.
 
 #include "gemm.h"
 
@@ -68,7 +73,7 @@ QL_DEV void wbarrier() {
 
 constexpr int kBM = 256, kBN = 256, kBK = 64, kThreads = 256;
 constexpr int kTM = 8, kTN = 2;       // 32x32 MFMA tiles per wave: 8 along M, 2 along N
-constexpr int kStages = 3;            // A ring depth
+constexpr int kStages = 4;            // A ring depth
 constexpr int kStageElems = kBM * kBK;  // 256 rows x 64 k (bf16)
 constexpr int kLutCopies = 16;        // lane l reads copy l % 16 of the pair table
 constexpr int kLutBytes = 256 * 8 * kLutCopies;
@@ -85,8 +90,10 @@ QL_DEV int a_swz(int r) { return (r >> 1) & 7; }
 
 __global__ __launch_bounds__(kThreads) void nf4_gemm_wide_fwd_kernel(GemmParams p) {
   __shared__ __attribute__((aligned(16))) char lds[kLdsBytes];
-  const f32x2 *lut = reinterpret_cast<const f32x2 *>(lds);
-  uint16_t *ring = reinterpret_cast<uint16_t *>(lds + kLutBytes);
+  // the A ring first, so the fragment reads of all four buffers reach their
+  // addresses from two base registers (16-bit offsets); the table after it
+  char *const tab = lds + kStages * kStageElems * 2;
+  uint16_t *ring = reinterpret_cast<uint16_t *>(lds);
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -94,7 +101,7 @@ __global__ __launch_bounds__(kThreads) void nf4_gemm_wide_fwd_kernel(GemmParams 
 
   for (int i = tid; i < 256 * kLutCopies; i += kThreads) {
     const int e = i / kLutCopies;
-    reinterpret_cast<f32x2 *>(lds)[i] = f32x2{p.level[e >> 4], p.level[e & 15]};
+    reinterpret_cast<f32x2 *>(tab)[i] = f32x2{p.level[e >> 4], p.level[e & 15]};
   }
 
   int bid = blockIdx.x;
@@ -110,17 +117,21 @@ __global__ __launch_bounds__(kThreads) void nf4_gemm_wide_fwd_kernel(GemmParams 
   // ---- A: each wave copies 8 blocks of 8 rows per stage, lane L -> row 8 blk + L / 8,
   // physical chunk L % 8 (global chunk (L % 8) ^ swz(row))
   const auto rA = wrsrc(p.A + m0 * p.lda, mrows * p.lda * 2);
-  int voffA[8];
+  // the swizzle of row 8 (8 wv + c) + lane / 8 depends on c only through c's parity,
+  // so two lane offsets serve all eight copies; the rest of the row offset is uniform
+  int voffA[2];
 #pragma unroll
-  for (int c = 0; c < 8; ++c) {
+  for (int c = 0; c < 2; ++c) {
     const int r = 8 * (wv * 8 + c) + (lane >> 3), lc = (lane & 7) ^ a_swz(r);
     voffA[c] = (int)((r * p.lda + lc * 8) * 2);
   }
+  const int rowstepA = __builtin_amdgcn_readfirstlane((int)(8 * p.lda * 2));
   auto dma_a = [&](int kt_, int buf) {
     const int kt = __builtin_amdgcn_readfirstlane(kt_);
 #pragma unroll
     for (int c = 0; c < 8; ++c)
-      wload16_to_lds(rA, ring + buf * kStageElems + (wv * 8 + c) * 8 * kBK, voffA[c], kt * kBK * 2);
+      wload16_to_lds(rA, ring + buf * kStageElems + (wv * 8 + c) * 8 * kBK, voffA[c & 1],
+                     kt * kBK * 2 + (c & ~1) * rowstepA);
   };
 
   // ---- B: lane (l32, g) of wave w decodes codes rows 64w + 32j + l32 (j = 0, 1)
@@ -164,7 +175,7 @@ __global__ __launch_bounds__(kThreads) void nf4_gemm_wide_fwd_kernel(GemmParams 
 #pragma unroll
       for (int b = 0; b < 4; ++b) {
         const uint32_t byte = (w >> (8 * b)) & 0xFFu;
-        lv[j][b] = *reinterpret_cast<const f32x2 *>(lds + (byte << 7) + lcopy8);
+        lv[j][b] = *reinterpret_cast<const f32x2 *>(tab + (byte << 7) + lcopy8);
       }
     }
   };
@@ -212,14 +223,17 @@ __global__ __launch_bounds__(kThreads) void nf4_gemm_wide_fwd_kernel(GemmParams 
   };
 
   const int nk = p.ksteps;
-  BRegs R0, R1, R2;
+  BRegs R0, R1;
   u32x4 bcur[kTN][4], bnext[kTN][4];
+  u32x4 af[2][kTM];
   __syncthreads();  // pair table ready
   dma_a(0, 0);
   load_b(0, R0);
   __builtin_amdgcn_sched_barrier(0);
   dma_a(1, 1);
   load_b(1, R1);
+  __builtin_amdgcn_sched_barrier(0);
+  dma_a(2, 2);
   __builtin_amdgcn_sched_barrier(0);
   {
     float ah[kTN];
@@ -231,38 +245,43 @@ __global__ __launch_bounds__(kThreads) void nf4_gemm_wide_fwd_kernel(GemmParams 
       lut_use(lv, ah, part, bcur);
     }
   }
+  // step 0's B loads and so stage 0 are done once the 22 younger operations (stage 1,
+  // step 1's B loads, stage 2) are all that may be outstanding
+  wait_vm(std::integral_constant<int, 22>{});
+  wbarrier();
+  read_a(0, 0, af[0]);
+  Lv lv[2];
+  float ahn[kTN];
+  lut_read(R1, 0, lv[0]);
+  scale_of(R1, ahn);
 
-  // Step kt (ring buffer BUF = kt % 3, a compile-time constant: the loop is unrolled
-  // three times, with three B register sets): A from buffer BUF (copied two steps
-  // earlier), B from bcur.  Issued at its start: the A copy and the B loads of step
-  // kt + 2 (into the register set step kt's own B came from, decoded during step
-  // kt - 1).  The decode of step kt + 1 (loaded during step kt - 1) runs between
-  // the MFMAs: while group kk's 16 MFMAs issue, the A fragments of group kk + 1 and
-  // the table reads of decode part kk + 1 are in flight and part kk's levels are
-  // scaled and converted.  Loads past the last step read harmless data that is
-  // never used.
+  // Step kt (ring buffer BUF = kt % 4, compile-time: the loop is unrolled four
+  // times; the two B register sets alternate).  On entry af[0] holds group 0's A
+  // fragments of step kt, bcur its decoded B, lv[0] and ahn the first table reads
+  // and scales of step kt + 1's decode.  Issued at its start: the B loads of step
+  // kt + 2 (into the set step kt's own B came from).  The decode of step kt + 1
+  // runs between the MFMAs: while group kk's 16 MFMAs issue, the A fragments of
+  // group kk + 1 and the table reads of part kk + 1 are in flight and part kk's
+  // levels are scaled and converted.  After group 2's MFMAs this wave's copy of
+  // stage kt + 1 is awaited, one barrier makes every wave's copy visible and frees
+  // buffer (kt + 3) % 4 (last read in step kt - 1), and the copy of stage kt + 3
+  // goes there; group 3's MFMAs then cover the reads of step kt + 1's group-0
+  // fragments and of the first part of step kt + 2's decode.  Loads past the last
+  // step read harmless data that is never used.
   auto step = [&](auto bufc, int kt, BRegs &Rnext, BRegs &Rfree) {
     constexpr int BUF = decltype(bufc)::value;
-    // this wave's copy of stage kt is done once at most 20 younger operations are
-    // outstanding (step kt's B loads, step kt + 1's copy and B loads); the barrier
-    // makes every wave's copy visible and frees buffer (kt + 2) % 3, last read in
-    // step kt - 1
-    wait_vm(std::integral_constant<int, 20>{});
-    wbarrier();
-    dma_a(kt + 2, (BUF + 2) % kStages);
     load_b(kt + 2, Rfree);
-    u32x4 af[2][kTM];
-    Lv lv[2];
-    float ah[kTN];
-    read_a(BUF, 0, af[0]);
-    lut_read(Rnext, 0, lv[0]);
-    scale_of(Rnext, ah);
+    float ah[kTN] = {ahn[0], ahn[1]};
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
       if (kk < 3) {
         read_a(BUF, kk + 1, af[(kk + 1) & 1]);
         lut_read(Rnext, kk + 1, lv[(kk + 1) & 1]);
+      } else {
+        read_a((BUF + 1) % kStages, 0, af[0]);
+        lut_read(Rfree, 0, lv[0]);
+        scale_of(Rfree, ahn);
       }
 #pragma unroll
       for (int i = 0; i < kTM; ++i)
@@ -277,6 +296,14 @@ __global__ __launch_bounds__(kThreads) void nf4_gemm_wide_fwd_kernel(GemmParams 
         __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);  // VALU
       }
       __builtin_amdgcn_sched_barrier(0);
+      if (kk == 2) {
+        // younger than this wave's copy of stage kt + 1: the B loads of step kt + 1,
+        // the copy of stage kt + 2, the B loads of step kt + 2
+        wait_vm(std::integral_constant<int, 20>{});
+        wbarrier();
+        dma_a(kt + 3, (BUF + 3) % kStages);
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
 #pragma unroll
     for (int j = 0; j < kTN; ++j)
@@ -286,14 +313,17 @@ __global__ __launch_bounds__(kThreads) void nf4_gemm_wide_fwd_kernel(GemmParams 
   using I0 = std::integral_constant<int, 0>;
   using I1 = std::integral_constant<int, 1>;
   using I2 = std::integral_constant<int, 2>;
+  using I3 = std::integral_constant<int, 3>;
   int kt = 0;
-  for (; kt + 2 < nk; kt += 3) {
-    step(I0{}, kt, R1, R2);
-    step(I1{}, kt + 1, R2, R0);
-    step(I2{}, kt + 2, R0, R1);
+  for (; kt + 3 < nk; kt += 4) {
+    step(I0{}, kt, R1, R0);
+    step(I1{}, kt + 1, R0, R1);
+    step(I2{}, kt + 2, R1, R0);
+    step(I3{}, kt + 3, R0, R1);
   }
-  if (kt < nk) step(I0{}, kt, R1, R2);
-  if (kt + 1 < nk) step(I1{}, kt + 1, R2, R0);
+  if (kt < nk) step(I0{}, kt, R1, R0);
+  if (kt + 1 < nk) step(I1{}, kt + 1, R0, R1);
+  if (kt + 2 < nk) step(I2{}, kt + 2, R1, R0);
   __builtin_amdgcn_s_waitcnt(0);  // no copy of a stage past the end may still land in LDS
   __syncthreads();
 

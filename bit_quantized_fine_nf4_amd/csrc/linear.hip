@@ -13,9 +13,10 @@
 //   nf4_gemm_kernel      fused dequant-GEMM, MFMA 32x32x16: forward
 //                        (B = W_hat, K along h) and dX (B = W_hat^T, K
 //                        along o); the rank-r LoRA product is added as extra
-//                        K steps on the same accumulators (the 256x256
-//                        forward tiles run nf4_gemm_wide_fwd_kernel)
-//   (the M <= 16 forward, nf4_gemv_stream_kernel, is in gemv.hip)
+//                        K steps on the same accumulators (256x256 tiles
+//                        run nf4_gemm_wide_fwd_kernel and
+//                        nf4_gemm_wide_dx_kernel instead)
+//   (the M <= 16 forward, nf4_gemv1_kernel and nf4_gemv_kernel, is in gemv.hip)
 //   nf4_gemv_dx_kernel   M <= 16 dX: streams the codes once in 64-row stages
 //                        through LDS; 4-bit transposing reads give each lane
 //                        a column's codes, a byte table yields the bf16 MFMA

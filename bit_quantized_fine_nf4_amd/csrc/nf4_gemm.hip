@@ -511,7 +511,7 @@ template <bool TRANS>
 hipError_t gemm_select(GemmParams &gp, hipStream_t st) {
   const int64_t t256 = cdiv(gp.M, 256) * cdiv(gp.N, 256);
   const int64_t t256x128 = cdiv(gp.M, 256) * cdiv(gp.N, 128);
-  if (gp.M >= 256 && t256 >= 240) return TRANS ? gemm_launch<256, 256, TRANS>(gp, st) : launch_nf4_gemm_wide(gp, TRANS, st);
+  if (gp.M >= 256 && t256 >= 240) return launch_nf4_gemm_wide(gp, TRANS, st);
   if (gp.M >= 192 && t256x128 >= 160) return gemm_launch<256, 128, TRANS>(gp, st);
   return gemm_launch<128, 128, TRANS>(gp, st);
 }

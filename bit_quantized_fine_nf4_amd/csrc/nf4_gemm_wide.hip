@@ -1,4 +1,5 @@
-// Fused NF4 dequant-GEMM, 256 x 256 tiles, forward direction, for gfx950.
+// Fused NF4 dequant-GEMM, 256 x 256 tiles, for gfx950: the forward kernel
+// below, and the dX kernel (nf4_gemm_wide_dx_kernel) further down.
 //
 // [MC] "1. NormalFloat" / [GO] "The core move": the 4-bit weights are
 // dequantized to BF16 on the fly for the matrix multiplication and never stored
@@ -390,10 +391,379 @@ __global__ __launch_bounds__(kThreads) void nf4_gemm_wide_fwd_kernel(GemmParams 
   }
 }
 
+
+// ---------------------------------------------------------------------------
+// dX direction: C[M][N] = dY[M][K] · W_hat[K][N] + s·U·L1^T, K = o, N = h
+// ([MC] "One training step": the gradient flows through the frozen dequantized
+// weight).  Same four-wave split as the forward: wave w owns output columns
+// [64w, 64w + 64) and all 256 rows, with 8 x 2 tiles of 32x32x16 MFMAs.  The
+// stored codes run along N, so a wave's B fragment (8 consecutive k of one
+// column) is a transpose of the stored rows:
+//  - each K step's 64 code rows x 256 columns (8 KB) go to LDS by direct-to-LDS
+//    loads, 16-byte chunks at chunk ^ ((row >> 1) & 7), in a 5-stage ring;
+//  - one 4-bit transposing read (ds_read_b64_tr_b4) gives lane i of a 16-lane
+//    group the nibbles of 16 consecutive rows of one column.  It returns a
+//    byte's low nibble first, and a stored byte keeps the even column in its
+//    high nibble, so lane i holds column i ^ 1: the epilogue (and the rank-r
+//    operand) use the same swapped column, so every accumulator column is one
+//    output column;
+//  - each byte of the result is two consecutive rows of the column: one table
+//    read gives both levels, each multiplied by its own row's a_hat (the block
+//    scale belongs to a row and a 64-column block; a wave's 64 columns are one
+//    block), then one packed conversion gives the MFMA dword;
+//  - the 256 a_hat values of a stage (64 rows x the tile's 4 blocks) are
+//    rebuilt by the 256 threads, one each, two steps ahead, and published in a
+//    4-stage LDS ring; a lane reads its 8 values per MFMA group as two
+//    broadcast 16-byte reads.
+// A (dY) takes the forward's path through a 3-stage ring.  One barrier per K
+// step after the third MFMA group, as in the forward; the last group's MFMAs
+// cover the next step's first A fragments and the first part of the decode
+// after next.
+// ---------------------------------------------------------------------------
+namespace {
+constexpr int kXStagesA = 3;                  // A (dY) ring
+constexpr int kXStagesC = 5;                  // code ring
+constexpr int kXStagesS = 4;                  // a_hat ring
+constexpr int kXCodeBytes = 64 * (kBN / 2);   // 64 code rows x 256 columns
+constexpr int kXAhFloats = 4 * 64;            // [4 blocks][64 rows]
+constexpr int kXLutCopies = 8;                // lane l reads copy l % 8 of the pair table
+constexpr int kXOffC = kXStagesA * kStageElems * 2;
+constexpr int kXOffS = kXOffC + kXStagesC * kXCodeBytes;
+constexpr int kXOffLut = kXOffS + kXStagesS * kXAhFloats * 4;
+constexpr int kXLdsBytes = (kXOffLut + 256 * 8 * kXLutCopies) > (kBM * kLdc * 2) ? (kXOffLut + 256 * 8 * kXLutCopies)
+                                                                                 : (kBM * kLdc * 2);
+typedef int wi32x2 __attribute__((ext_vector_type(2)));
+QL_DEV u32x2 wtr4(const uint8_t *ptr) {
+  typedef __attribute__((address_space(3))) wi32x2 lds_i32x2;
+  return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr4_b64_v2i32((lds_i32x2 *)(ptr)));
+}
+}  // namespace
+
+__global__ __launch_bounds__(kThreads) void nf4_gemm_wide_dx_kernel(GemmParams p) {
+  __shared__ __attribute__((aligned(16))) char lds[kXLdsBytes];
+  uint16_t *ring = reinterpret_cast<uint16_t *>(lds);
+  uint8_t *cring = reinterpret_cast<uint8_t *>(lds + kXOffC);
+  float *ahs = reinterpret_cast<float *>(lds + kXOffS);
+  char *const tab = lds + kXOffLut;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = lane >> 5, l32 = lane & 31, i16 = lane & 15, half = (lane >> 4) & 1;
+
+  // entry e of copy c (at 64 e + 8 c): (level[low nibble], level[high nibble]), the
+  // levels of a byte's earlier and later row
+  for (int i = tid; i < 256 * kXLutCopies; i += kThreads) {
+    const int e = i / kXLutCopies;
+    reinterpret_cast<f32x2 *>(tab)[i] = f32x2{p.level[e & 15], p.level[e >> 4]};
+  }
+
+  int bid = blockIdx.x;
+  const int ntiles = p.tiles_m * p.tiles_n;
+  if ((ntiles & 7) == 0) bid = (bid & 7) * (ntiles >> 3) + (bid >> 3);  // one XCD -> contiguous tiles
+  const int tn = bid % p.tiles_n, tm = bid / p.tiles_n;
+  const int64_t m0 = (int64_t)tm * kBM, n0 = (int64_t)tn * kBN;
+  const int64_t mrows = p.M - m0 < kBM ? p.M - m0 : kBM;
+  const int64_t nrows = p.N - n0 < kBN ? p.N - n0 : kBN;
+  const float mu = *p.mean;
+  const int64_t bpr = p.ldw >> 6;   // 64-blocks per codes row
+  const int64_t rowB = p.ldw >> 1;  // bytes per codes row
+
+  // ---- A (dY): as in the forward, 8 copies of 8 rows per wave and stage
+  const auto rA = wrsrc(p.A + m0 * p.lda, mrows * p.lda * 2);
+  int voffA[2];
+#pragma unroll
+  for (int c = 0; c < 2; ++c) {
+    const int r = 8 * (wv * 8 + c) + (lane >> 3), lc = (lane & 7) ^ a_swz(r);
+    voffA[c] = (int)((r * p.lda + lc * 8) * 2);
+  }
+  const int rowstepA = __builtin_amdgcn_readfirstlane((int)(8 * p.lda * 2));
+  auto dma_a = [&](int kt_, int buf) {
+    const int kt = __builtin_amdgcn_readfirstlane(kt_);
+#pragma unroll
+    for (int c = 0; c < 8; ++c)
+      wload16_to_lds(rA, ring + buf * kStageElems + (wv * 8 + c) * 8 * kBK, voffA[c & 1],
+                     kt * kBK * 2 + (c & ~1) * rowstepA);
+  };
+  auto read_a = [&](int buf, int kk, u32x4 (&af)[kTM]) {
+#pragma unroll
+    for (int i = 0; i < kTM; ++i) {
+      const int r = 32 * i + l32;
+      af[i] = *reinterpret_cast<const u32x4 *>(ring + buf * kStageElems + r * kBK + (((4 * g + kk) ^ a_swz(r)) << 3));
+    }
+  };
+
+  // ---- codes: wave w copies rows 8 (2w + j) + L / 8 (j = 0, 1) of a stage; lane L
+  // fetches the logical chunk that belongs at physical chunk L % 8 of its row
+  int voffC[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int r = 8 * (2 * wv + j) + (lane >> 3), lc = (lane & 7) ^ a_swz(r);
+    voffC[j] = (int)(r * rowB + 16 * lc);
+  }
+  auto dma_c = [&](int s_, int buf) {
+    const int s = __builtin_amdgcn_readfirstlane(s_);
+    const int64_t r0 = (int64_t)s * 64;
+    const auto rC = wrsrc(p.codes + r0 * rowB + (n0 >> 1), (p.wrows - r0) * rowB - (n0 >> 1));
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rC, (__attribute__((address_space(3))) void *)(cring + buf * kXCodeBytes + 1024 * (2 * wv + j)), 16,
+          voffC[j], 0, 0, 0);
+  };
+  // transposing read t (rows 16t .. 16t + 15 of the lane's 32) of column tile j:
+  // lane i of its 16-lane group names row 32 g + 16 t + i, whose swizzle is (i >> 1) & 7
+  int troff[kTN];
+#pragma unroll
+  for (int j = 0; j < kTN; ++j) troff[j] = (32 * g + i16) * 128 + 16 * ((2 * wv + j) ^ ((i16 >> 1) & 7)) + 8 * half;
+  auto read_tr = [&](int buf, int t, u32x2 (&tw)[kTN]) {
+#pragma unroll
+    for (int j = 0; j < kTN; ++j) tw[j] = wtr4(cring + buf * kXCodeBytes + troff[j] + 16 * t * 128);
+  };
+
+  // ---- a_hat: thread t rebuilds row t / 4, block t % 4 of a stage
+  const int qrow = tid >> 2, qblk = tid & 3;
+  const auto rQ = wrsrc(p.qabsmax, p.wrows * bpr);
+  const auto rS2 = wrsrc(p.scale2, ((p.wrows * bpr + 255) >> 8) * 4);
+  struct QS {
+    uint32_t q;  // int8 block scale, zero-extended
+    float s2;
+  };
+  auto load_qs = [&](int s_, QS &Q) {
+    const int s = __builtin_amdgcn_readfirstlane(s_);
+    const int64_t bi = ((int64_t)s * 64 + qrow) * bpr + (n0 >> 6) + qblk;
+    Q.q = __builtin_amdgcn_raw_buffer_load_b8(rQ, (int)bi, 0, 0);
+    Q.s2 = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rS2, (int)((bi >> 8) * 4), 0, 0));
+  };
+  auto put_ah = [&](const QS &Q, int buf) {
+    // int8 from the zero-extended byte by float arithmetic; two roundings
+    const float qf = (float)Q.q - (float)(Q.q & 0x80u) * 2.0f;
+    ahs[buf * kXAhFloats + qblk * 64 + qrow] = qf * Q.s2 + mu;
+  };
+
+  // ---- decode of one part (MFMA group kk: rows 32 g + 8 kk .. + 7 of the lane's column)
+  const int lcopy8 = (lane % kXLutCopies) * 8;
+  typedef f32x2 XLv[kTN][4];
+  auto lut_read = [&](const u32x2 (&tw)[kTN], int kk, XLv &lv) {
+#pragma unroll
+    for (int j = 0; j < kTN; ++j) {
+      const uint32_t w = tw[j][kk & 1];
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+        const uint32_t byte = (w >> (8 * d)) & 0xFFu;
+        lv[j][d] = *reinterpret_cast<const f32x2 *>(tab + (byte << 6) + lcopy8);
+      }
+    }
+  };
+  auto sc_read = [&](int buf, int kk, f32x4 (&sc)[2]) {
+    const float *sp = ahs + buf * kXAhFloats + wv * 64 + 32 * g + 8 * kk;
+    sc[0] = *reinterpret_cast<const f32x4 *>(sp);
+    sc[1] = *reinterpret_cast<const f32x4 *>(sp + 4);
+  };
+  auto lut_use = [&](const XLv &lv, const f32x4 (&sc)[2], int kk, u32x4 (&bf)[kTN][4]) {
+#pragma unroll
+    for (int j = 0; j < kTN; ++j) {
+      uint32_t o[4];
+#pragma unroll
+      for (int d = 0; d < 4; ++d)
+        o[d] = pack_bf16x2(lv[j][d][0] * sc[d >> 1][2 * (d & 1)], lv[j][d][1] * sc[d >> 1][2 * (d & 1) + 1]);
+      bf[j][kk] = u32x4{o[0], o[1], o[2], o[3]};
+    }
+  };
+
+  // lgkmcnt(0) (this wave's a_hat stores) and vmcnt(n) (its copies into LDS)
+  auto wait_vm_lgkm = [](auto nconst) {
+    constexpr int n = decltype(nconst)::value;
+    __builtin_amdgcn_s_waitcnt((n & 15) | (7 << 4) | ((n >> 4) << 14));
+  };
+
+  f32x16 acc[kTM][kTN];
+#pragma unroll
+  for (int i = 0; i < kTM; ++i)
+#pragma unroll
+    for (int j = 0; j < kTN; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
+
+  const int nk = p.ksteps;
+  QS Q0, Q1;
+  u32x4 bcur[kTN][4], bnext[kTN][4];
+  u32x4 af[2][kTM];
+  XLv lv[2];
+  f32x4 sc[2][2];
+  u32x2 tw0[kTN], tw1[kTN];
+  __syncthreads();  // pair table ready
+  // Prologue: codes of stages 0-3, A of stage 0, scales of stages 0 and 1; then, in
+  // the order a step issues them, the scales of stage 2, the codes of stage 4, A of
+  // stage 1 and the scales of stage 3.
+#pragma unroll
+  for (int s = 0; s < 4; ++s) dma_c(s, s);
+  dma_a(0, 0);
+  load_qs(0, Q0);
+  load_qs(1, Q1);
+  __builtin_amdgcn_s_waitcnt(0);
+  put_ah(Q0, 0);
+  put_ah(Q1, 1);
+  __builtin_amdgcn_sched_barrier(0);
+  load_qs(2, Q0);
+  __builtin_amdgcn_sched_barrier(0);
+  dma_c(4, 4);
+  __builtin_amdgcn_sched_barrier(0);
+  dma_a(1, 1);
+  __builtin_amdgcn_sched_barrier(0);
+  load_qs(3, Q1);
+  __builtin_amdgcn_sched_barrier(0);
+  __syncthreads();  // stage 0's A and codes, stages 0-3's codes, a_hat of stages 0 and 1
+  {
+    read_tr(0, 0, tw0);
+    read_tr(0, 1, tw1);
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      XLv l;
+      f32x4 c2[2];
+      lut_read(kk < 2 ? tw0 : tw1, kk, l);
+      sc_read(0, kk, c2);
+      lut_use(l, c2, kk, bcur);
+    }
+  }
+  read_a(0, 0, af[0]);
+  read_tr(1, 0, tw0);
+  lut_read(tw0, 0, lv[0]);
+  sc_read(1, 0, sc[0]);
+
+  // Step kt: A from ring buffer kt % 3, B from bcur; decodes stage kt + 1 into
+  // bnext (its part 0 read during step kt - 1).  On entry af[0] holds group 0's A
+  // fragments, tw0 the first transposing reads of stage kt + 1, lv[0] / sc[0] its
+  // part-0 table entries and scales.  At its start the a_hat values of stage
+  // kt + 2 are published.  After group 2: this wave's copies of A stage kt + 1 and
+  // code stages up to kt + 4 are awaited (2 younger operations: the scales of
+  // stage kt + 3), one barrier publishes every wave's copies and a_hat values and
+  // frees A buffer (kt + 2) % 3, code buffer kt % 5; then the copies of code stage
+  // kt + 5 and A stage kt + 2 and the scale loads of stage kt + 4 are issued.
+  auto step = [&](int kt, QS &Qcur) {
+    const int bA = kt % kXStagesA, bC1 = (kt + 1) % kXStagesC, bC2 = (kt + 2) % kXStagesC;
+    const int bS1 = (kt + 1) % kXStagesS, bS2 = (kt + 2) % kXStagesS;
+    put_ah(Qcur, bS2);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      if (kk == 0) {
+        read_a(bA, 1, af[1]);
+        read_tr(bC1, 1, tw1);
+        lut_read(tw0, 1, lv[1]);
+        sc_read(bS1, 1, sc[1]);
+      } else if (kk == 1) {
+        read_a(bA, 2, af[0]);
+        lut_read(tw1, 2, lv[0]);
+        sc_read(bS1, 2, sc[0]);
+      } else if (kk == 2) {
+        read_a(bA, 3, af[1]);
+        lut_read(tw1, 3, lv[1]);
+        sc_read(bS1, 3, sc[1]);
+        read_tr(bC2, 0, tw0);
+      } else {
+        read_a((kt + 1) % kXStagesA, 0, af[0]);
+        lut_read(tw0, 0, lv[0]);
+        sc_read(bS2, 0, sc[0]);
+      }
+#pragma unroll
+      for (int i = 0; i < kTM; ++i)
+#pragma unroll
+        for (int j = 0; j < kTN; ++j) acc[i][j] = wmfma(af[kk & 1][i], bcur[j][kk], acc[i][j]);
+      lut_use(lv[kk & 1], sc[kk & 1], kk, bnext);
+      // interleave: each MFMA followed by one LDS read and a few decode instructions
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
+        __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);  // VALU
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      if (kk == 2) {
+        wait_vm_lgkm(std::integral_constant<int, 2>{});
+        wbarrier();
+        dma_c(kt + 5, kt % kXStagesC);
+        __builtin_amdgcn_sched_barrier(0);
+        dma_a(kt + 2, (kt + 2) % kXStagesA);
+        __builtin_amdgcn_sched_barrier(0);
+        load_qs(kt + 4, Qcur);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < kTN; ++j)
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) bcur[j][kk] = bnext[j][kk];
+  };
+  int kt = 0;
+  for (; kt + 1 < nk; kt += 2) {
+    step(kt, Q0);
+    step(kt + 1, Q1);
+  }
+  if (kt < nk) step(kt, Q0);
+  __builtin_amdgcn_s_waitcnt(0);  // no copy of a stage past the end may still land in LDS
+  __syncthreads();
+
+  // ---- rank-r K steps: A2 = s-scaled U [M][lda2] through ring buffer 0; B2 = L1
+  // padded to [N][ldb2]: lane (n, g) takes row n ^ 1 of its column tile (the
+  // swapped column of the code path), 16 contiguous bytes per MFMA group
+  if (p.ksteps2 > 0) {
+    const auto rA2 = wrsrc(p.A2 + m0 * p.lda2, mrows * p.lda2 * 2);
+    const auto rB2 = wrsrc(p.B2 + n0 * p.ldb2, nrows * p.ldb2 * 2);
+    uint16_t *a2 = ring;
+    for (int k2 = 0; k2 < p.ksteps2; ++k2) {
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int ch = tid + kThreads * u, r = ch >> 3, lc = ch & 7;
+        const u32x4 v = wload128(rA2, (int)((r * p.lda2 + lc * 8) * 2), k2 * kBK * 2);
+        *reinterpret_cast<u32x4 *>(a2 + r * kBK + ((lc ^ a_swz(r)) << 3)) = v;
+      }
+      u32x4 b2[kTN][4];
+#pragma unroll
+      for (int j = 0; j < kTN; ++j)
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk)
+          b2[j][kk] = wload128(rB2, (int)(((64 * wv + 32 * j + (l32 ^ 1)) * p.ldb2 + 32 * g + 8 * kk) * 2),
+                               k2 * kBK * 2);
+      __syncthreads();
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        u32x4 a[kTM];
+        read_a(0, kk, a);
+#pragma unroll
+        for (int i = 0; i < kTM; ++i)
+#pragma unroll
+          for (int j = 0; j < kTN; ++j) acc[i][j] = wmfma(a[i], b2[j][kk], acc[i][j]);
+      }
+      __syncthreads();
+    }
+  }
+
+  // ---- epilogue: fp32 -> bf16 through LDS (accumulator column l32 is output column
+  // l32 ^ 1 of its tile), then coalesced 16-byte stores
+  uint16_t *cs = reinterpret_cast<uint16_t *>(lds);
+#pragma unroll
+  for (int i = 0; i < kTM; ++i)
+#pragma unroll
+    for (int j = 0; j < kTN; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int row = 32 * i + 8 * (v >> 2) + 4 * g + (v & 3);
+        const int col = 64 * wv + 32 * j + (l32 ^ 1);
+        cs[row * kLdc + col] = wbf16(acc[i][j][v]);
+      }
+  __syncthreads();
+  for (int ch = tid; ch < kBM * kBN / 8; ch += kThreads) {
+    const int row = ch / (kBN / 8), c8 = ch % (kBN / 8);
+    const int64_t m = m0 + row, n = n0 + c8 * 8;
+    if (m < p.M && n < p.N)
+      *reinterpret_cast<u32x4 *>(p.C + m * p.ldc + n) = *reinterpret_cast<const u32x4 *>(cs + row * kLdc + c8 * 8);
+  }
+}
+
 hipError_t launch_nf4_gemm_wide(GemmParams &gp, bool trans, hipStream_t st) {
   gp.tiles_m = (int)((gp.M + kBM - 1) / kBM);
   gp.tiles_n = (int)((gp.N + kBN - 1) / kBN);
-  if (trans) return hipErrorInvalidValue;
+  if (trans) return launch(nf4_gemm_wide_dx_kernel, gp.tiles_m * gp.tiles_n, kThreads, st, gp);
   return launch(nf4_gemm_wide_fwd_kernel, gp.tiles_m * gp.tiles_n, kThreads, st, gp);
 }
 

@@ -533,8 +533,8 @@ def bench_block(args, torch, nf4, wl, c):
             v[k] = round(v[k], 4)
     dom = "dx" if gem["dx"]["ms_per_step"] >= gem["fwd"]["ms_per_step"] else "fwd"
     achieved = gem[dom]["timed_flop"] / gem[dom]["timed_ms"] / 1e9
-    # 256x256 tiles: the dX direction runs nf4_gemm_kernel<256, 256, true>, the forward its own kernel
-    kname = "nf4_gemm_kernel<256,256,true>" if dom == "dx" else "nf4_gemm_wide_fwd_kernel"
+    # 256x256 tiles: both directions run the four-wave kernels
+    kname = "nf4_gemm_wide_dx_kernel" if dom == "dx" else "nf4_gemm_wide_fwd_kernel"
     roofline = {"bound": "mfma", "achieved": round(achieved, 3), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": read_traffic(f"{c.name}.gemm_{dom}"),
                 "kernel": kname, "kernel_ms_mean": round(gem[dom]["ms_per_step"] / L, 5),

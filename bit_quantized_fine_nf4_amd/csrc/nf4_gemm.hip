@@ -13,15 +13,15 @@
 // matrix cores work on the current buffers.  Within a K step, lane group
 // g = lane/32 owns k in [32g, 32g+32) and MFMA kk takes k = 32g + 8kk + 0..7
 // (the contraction may visit k in any order as long as A and B agree).
+// The tiles are 256 x 128 and 128 x 128 (256 x 256 tiles, in both directions,
+// run the four-wave kernels of nf4_gemm_wide.hip).
 //  A operand (X or dY, k-contiguous): tile [m][k].  It goes from memory straight
 //   into LDS (buffer_load ... lds, 16 bytes per lane, 1 KB = 8 rows per
 //   instruction) one step ahead, in unpadded 128-byte rows whose 16-byte chunks
-//   are XOR-swizzled by row so fragment reads stay free of bank conflicts; for the
-//   256-wide dX tiles it is staged through registers two steps ahead instead
-//   (row stride 72, 16-byte stores), which measured faster there.
+//   are XOR-swizzled by row so fragment reads stay free of bank conflicts.
 //  B operand is decoded into LDS:
-//   Every thread decodes one unit of BN/8 consecutive weights of one codes row
-//   per K step (16 or 32: inside one 64-weight block, so one scale per unit).
+//   Every thread decodes one unit of 16 consecutive weights of one codes row
+//   per K step (inside one 64-weight block, so one scale per unit).
 //   forward: tile [n][k] (row stride 72), units along k of codes row n;
 //    fragments are 16-byte LDS reads.
 //   dX: tile [k][n] (row stride BN + 16); codes are contiguous along n (h),
@@ -92,31 +92,28 @@ template <int BM, int BN, bool TRANS>
 __global__ __launch_bounds__(512) void nf4_gemm_kernel(GemmParams p) {
   constexpr int NT = 512, BK = 64;
   constexpr int WTM = BM / 4, WTN = BN / 2, TM = WTM / 32, TN = WTN / 32;
-  // A reaches LDS straight from memory (kDma) except for the 256-wide dX tiles, where
-  // staging it through registers (two steps ahead rather than one) measured faster.
-  constexpr bool kDma = !(TRANS && BN == 256);
-  constexpr int LDA = kDma ? BK : BK + 8;  // A [m][k]: swizzled chunks (kDma) or a padded row
+  static_assert(BN == 128 && (BM == 256 || BM == 128), "256 x 128 or 128 x 128 tiles");
+  constexpr int LDA = BK;        // A [m][k]: unpadded rows of swizzled chunks
   constexpr int LDNK = BK + 8;   // B [n][k]
   // B [k][n] row stride: 16 banks (mod 64), so the 32 lanes of a transposing
   // fragment read (4 rows x 2 groups of 4 eight-byte chunks) cover the 64 banks
   // once.  The decode stores (2 rows of 16-byte units per 16 lanes) then pair
-  // up, but they are 8x rarer.  Against a 12-bank stride: C2 dX GEMM 93.8 ->
-  // 90.6 us, C3's 256-wide dX GEMM 438 -> 422 us.
+  // up, but they are 8x rarer.  Against a 12-bank stride: dX GEMM on a
+  // 4096 x 4096 weight with 2048 tokens 93.8 -> 90.6 us.
   constexpr int LDKN = BN + 32;
   constexpr int B_ELEMS = cmax(BN * LDNK, BK * LDKN);
   constexpr int STAGE = BM * LDA + B_ELEMS;  // elements per LDS stage (A then B)
-  constexpr int UW = 64 * BN / NT;  // weights per decode unit: every thread decodes one unit
-  constexpr int UB = UW / 2;        // code bytes per unit (8 or 16)
+  constexpr int UW = 64 * BN / NT;  // weights per decode unit (16): every thread decodes one unit
+  constexpr int UB = UW / 2;        // code bytes per unit (8)
   constexpr int A_CH = BM * 8 / NT;  // 16-byte A chunks per thread per K step
   // Interleaved copies of the decode table: lane l reads copy l % LUT_COPIES,
   // which cuts the bank conflicts of the random code-byte reads.  The 256x128
-  // tiles have the LDS for 16 copies (C2 dX GEMM 97.7 -> 93.8 us; a conflict-free
-  // timing knob reaches 92.8); 4 copies on the 256x256 tiles did not pay.
-  constexpr int LUT_COPIES = BM == 256 && BN == 128 ? 16 : 1;
+  // tiles have the LDS for 16 copies (dX GEMM on a 4096 x 4096 weight with 2048
+  // tokens 97.7 -> 93.8 us; a conflict-free timing knob reaches 92.8).
+  constexpr int LUT_COPIES = BM == 256 ? 16 : 1;
   constexpr int LUT_BYTES = 256 * 8 * LUT_COPIES;
   constexpr int LDC = BN + 8;
   constexpr int LDS_BYTES = cmax(LUT_BYTES + 2 * STAGE * 2, BM * LDC * 2);
-  static_assert(UW == 16 || UW == 32, "decode unit of 16 or 32 weights");
   static_assert(A_CH >= 1, "A tile too small");
   __shared__ __attribute__((aligned(16))) char lds[LDS_BYTES];
   const f32x2 *lut = reinterpret_cast<const f32x2 *>(lds);
@@ -126,11 +123,9 @@ __global__ __launch_bounds__(512) void nf4_gemm_kernel(GemmParams p) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
   const int wv = __builtin_amdgcn_readfirstlane(wave);
-  // kDma: row r keeps its 8 chunks of 16 bytes in the order c ^ aswz(r), so the 16 lanes of a
+  // row r keeps its 8 chunks of 16 bytes in the order c ^ aswz(r), so the 16 lanes of a
   // fragment read (16 rows, one chunk) hit 16 different 16-byte bank groups without padding.
-  auto a_off = [](int r, int chunk) {
-    return kDma ? r * LDA + ((chunk ^ ((r >> 1) & 7)) << 3) : r * LDA + chunk * 8;
-  };
+  auto a_off = [](int r, int chunk) { return r * LDA + ((chunk ^ ((r >> 1) & 7)) << 3); };
   for (int i = tid; i < 256 * LUT_COPIES; i += NT) {
     const int e = i / LUT_COPIES;
     reinterpret_cast<f32x2 *>(lds)[i] = f32x2{p.level[e >> 4], p.level[e & 15]};
@@ -148,20 +143,14 @@ __global__ __launch_bounds__(512) void nf4_gemm_kernel(GemmParams p) {
   const int g = lane >> 5, l32 = lane & 31;
 
   // ---- A tile ----
-  // kDma: each wave loads A_CH blocks of 8 rows into LDS, one 1 KB block per instruction, so
+  // Each wave loads A_CH blocks of 8 rows into LDS, one 1 KB block per instruction, so
   // lane L fetches the global chunk that belongs at row 8 rb + L / 8, physical chunk L % 8.
-  // Otherwise: 16-byte chunks through registers, 8 lanes per 128-byte row.
   const auto rA = make_rsrc(p.A + m0 * p.lda, mrows * p.lda * 2);
   int voffA[A_CH];
 #pragma unroll
   for (int c = 0; c < A_CH; ++c) {
-    if (kDma) {
-      const int r = 8 * (wv * A_CH + c) + (lane >> 3), lc = (lane & 7) ^ ((r >> 1) & 7);
-      voffA[c] = (int)((r * p.lda + lc * 8) * 2);
-    } else {
-      const int chunk = tid + NT * c;
-      voffA[c] = (int)(((chunk >> 3) * p.lda + (chunk & 7) * 8) * 2);
-    }
+    const int r = 8 * (wv * A_CH + c) + (lane >> 3), lc = (lane & 7) ^ ((r >> 1) & 7);
+    voffA[c] = (int)((r * p.lda + lc * 8) * 2);
   }
   auto load_a_lds = [&](int kt_, int buf) {
     const int kt = __builtin_amdgcn_readfirstlane(kt_);
@@ -202,7 +191,6 @@ __global__ __launch_bounds__(512) void nf4_gemm_kernel(GemmParams p) {
 
   // One register set holds everything a K step needs from global memory.
   struct Stage {
-    u32x4 a[kDma ? 1 : A_CH];  // A tile chunks (register staging only)
     u32x4 c;        // this thread's code bytes (UB of them)
     uint32_t q;     // its int8 block scale, zero-extended (see put_part)
     float s2;       // its second-level scale
@@ -211,17 +199,9 @@ __global__ __launch_bounds__(512) void nf4_gemm_kernel(GemmParams p) {
     // The step index is wave-uniform; saying so keeps the scalar offsets in SGPRs
     // (otherwise every buffer load becomes a per-lane waterfall loop).
     const int kt = __builtin_amdgcn_readfirstlane(kt_);
-    if constexpr (!kDma) {
-#pragma unroll
-      for (int c = 0; c < A_CH; ++c) S.a[c] = bload128(rA, voffA[c], kt * BK * 2);
-    }
     if (!TRANS) {
-      if (UB == 16) {
-        S.c = bload128(rCf, voffC, kt * 32);
-      } else {
-        const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(rCf, voffC, kt * 32, 0);
-        S.c = u32x4{v[0], v[1], 0u, 0u};
-      }
+      const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(rCf, voffC, kt * 32, 0);
+      S.c = u32x4{v[0], v[1], 0u, 0u};
       S.q = __builtin_amdgcn_raw_buffer_load_b8(rQf, voffQ, kt, 0);
       S.s2 = bload_f32(rS2, (int)(((blk0 + kt) >> 8) * 4), 0);
     } else {
@@ -229,33 +209,24 @@ __global__ __launch_bounds__(512) void nf4_gemm_kernel(GemmParams p) {
       const auto rC = make_rsrc(p.codes + krow0 * (p.ldw >> 1) + (n0 >> 1),
                                 (p.wrows - krow0) * (p.ldw >> 1) - (n0 >> 1));
       const auto rQ = make_rsrc(p.qabsmax + krow0 * bpr + (n0 >> 6), (p.wrows - krow0) * bpr - (n0 >> 6));
-      if (UB == 16) {
-        S.c = bload128(rC, voffC, 0);
-      } else {
-        const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(rC, voffC, 0, 0);
-        S.c = u32x4{v[0], v[1], 0u, 0u};
-      }
+      const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(rC, voffC, 0, 0);
+      S.c = u32x4{v[0], v[1], 0u, 0u};
       S.q = __builtin_amdgcn_raw_buffer_load_b8(rQ, voffQ, 0, 0);
       S.s2 = bload_f32(rS2, (int)(((blk0 + krow0 * bpr) >> 8) * 4), 0);
     }
   };
-  // Part `part` (0..3) of writing a stage into LDS buffer `buf`: a quarter of the
-  // A chunks and a quarter of the code bytes, decoded (LUT pair -> * a_hat ->
-  // bf16) and stored.  `ah` is the stage's block scale (computed by part 0).
-  constexpr int BPP = UB / 4;  // code bytes decoded per part (2 or 4)
-  // With 8 code bytes per unit, all eight table reads of a step are issued at its
-  // start (right after the next stage's loads), so their LDS latency is paid once
-  // rather than once per part; with 16 (256-wide tiles) the extra 16 registers
-  // would spill, and each part reads its own.
-  constexpr bool kEarly = UB == 8;
+  // Part `part` (0..3) of writing a stage's B into LDS buffer `buf`: a quarter of
+  // the code bytes, decoded (LUT pair -> * a_hat -> bf16) and stored.  `ah` is the
+  // stage's block scale (computed by part 0).
+  constexpr int BPP = UB / 4;  // code bytes decoded per part (2)
+  // All eight table reads of a step are issued at its start (right after the next
+  // stage's loads), so their LDS latency is paid once rather than once per part.
   const int lcopy = lane % LUT_COPIES;
   auto lut_index = [&](uint32_t w) { return (int)(w & 0xFF) * LUT_COPIES + lcopy; };
-  f32x2 LV[kEarly ? UB : 1];
+  f32x2 LV[UB];
   auto read_levels = [&](const Stage &S) {
-    if constexpr (kEarly) {
 #pragma unroll
-      for (int byte = 0; byte < UB; ++byte) LV[byte] = lut[lut_index(S.c[byte >> 2] >> (8 * (byte & 3)))];
-    }
+    for (int byte = 0; byte < UB; ++byte) LV[byte] = lut[lut_index(S.c[byte >> 2] >> (8 * (byte & 3)))];
   };
   uint32_t oprev[2] = {0u, 0u};  // an even part's decoded words, stored with the next part's
   auto put_part = [&](int buf, int part, const Stage &S, float &ah) {
@@ -266,33 +237,18 @@ __global__ __launch_bounds__(512) void nf4_gemm_kernel(GemmParams p) {
       const float qf = (float)S.q - (float)(S.q & 0x80u) * 2.0f;
       ah = qf * S.s2 + mu;
     }
-    if constexpr (!kDma) {
-#pragma unroll
-      for (int c = 0; c < A_CH; ++c)
-        if ((c & 3) == part) {
-          const int chunk = tid + NT * c;
-          *reinterpret_cast<u32x4 *>(sm + buf * STAGE + a_off(chunk >> 3, chunk & 7)) = S.a[c];
-        }
-    }
     uint32_t o[BPP];
 #pragma unroll
     for (int b = 0; b < BPP; ++b) {
-      const int byte = part * BPP + b;
-      f32x2 l;
-      if constexpr (kEarly) l = LV[byte];
-      else l = lut[lut_index(S.c[byte >> 2] >> (8 * (byte & 3)))];
+      const f32x2 l = LV[part * BPP + b];
       o[b] = pack_bf16x2(l[0] * ah, l[1] * ah);
     }
+    // two parts per 16-byte store: even parts keep their words, odd parts store both
     uint16_t *dst = bdst0 + buf * STAGE + part * 2 * BPP;
-    if constexpr (BPP == 4) {
-      *reinterpret_cast<u32x4 *>(dst) = u32x4{o[0], o[1], o[2], o[3]};
-    } else {
-      // two parts per 16-byte store: even parts keep their words, odd parts store both
-      if (part & 1)
-        *reinterpret_cast<u32x4 *>(dst - 2 * BPP) = u32x4{oprev[0], oprev[1], o[0], o[BPP - 1]};
-      else
-        oprev[0] = o[0], oprev[1] = o[BPP - 1];
-    }
+    if (part & 1)
+      *reinterpret_cast<u32x4 *>(dst - 2 * BPP) = u32x4{oprev[0], oprev[1], o[0], o[1]};
+    else
+      oprev[0] = o[0], oprev[1] = o[1];
   };
   // B fragments of MFMA step kk from an LDS tile; kn: tile is [k][n] (transposing reads)
   auto load_bfrag = [&](const uint16_t *bs, bool kn, int kk, u32x4 (&bf)[TN]) {
@@ -346,10 +302,6 @@ __global__ __launch_bounds__(512) void nf4_gemm_kernel(GemmParams p) {
   // to [N][ldb2] read as an [n][k] tile.  Rows past the ends read as zero (and every
   // load reads zero when there is no LoRA term: the resources are then empty).
   constexpr int B2CH = BN * 8 / NT;  // 16-byte B2 chunks per thread per LoRA step
-  // two fragment register sets (fragments of MFMA group kk+1 read while group kk runs)
-  // wherever registers allow: all but the 256-wide dX tiles
-  constexpr bool kTwoFrag = TM * TN <= 4 || kDma;
-  constexpr bool kLoraEarly = kDma && TM * TN <= 4;  // registers to spare for the first step's operands
   const bool lora = p.ksteps2 > 0;
   const auto rA2 = make_rsrc(p.A2 + m0 * p.lda2, lora ? mrows * p.lda2 * 2 : 0);
   const auto rB2 = TRANS ? make_rsrc(p.B2 + n0 * p.ldb2, lora ? nrows * p.ldb2 * 2 : 0)
@@ -393,16 +345,17 @@ __global__ __launch_bounds__(512) void nf4_gemm_kernel(GemmParams p) {
       }
     }
   };
+  // the first LoRA step's operands: the oldest loads, done long before they are used
   LoraStage L0;
-  if constexpr (kLoraEarly) lora_load(0, L0);  // oldest loads: done long before they are used
+  lora_load(0, L0);
 
-  // kDma: wait until at most n vector-memory operations of this wave are outstanding
+  // wait until at most n vector-memory operations of this wave are outstanding
   // (the LDS-bound A loads count; the compiler cannot know that other waves read them)
   auto wait_vm = [](auto nconst) {
     constexpr int n = decltype(nconst)::value;
-    if constexpr (kDma) __builtin_amdgcn_s_waitcnt((n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14));
+    __builtin_amdgcn_s_waitcnt((n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14));
   };
-  if constexpr (kDma) load_a_lds(0, 0);
+  load_a_lds(0, 0);
   __builtin_amdgcn_sched_barrier(0);
   load_stage(0, S0);
   __builtin_amdgcn_sched_barrier(0);
@@ -418,24 +371,12 @@ __global__ __launch_bounds__(512) void nf4_gemm_kernel(GemmParams p) {
     // these loads and writes are harmless and unused).  The fragments of MFMA
     // group kk+1 are read while group kk's MFMAs run.
     const int buf = kt & 1;
-    if constexpr (kDma) load_a_lds(kt + 1, buf ^ 1);  // that buffer is read by nobody since the last barrier
+    load_a_lds(kt + 1, buf ^ 1);  // that buffer is read by nobody since the last barrier
     __builtin_amdgcn_sched_barrier(0);
     load_stage(kt + 2, Sfree);
     __builtin_amdgcn_sched_barrier(0);
-    if constexpr (kEarly) {
-      read_levels(Snext);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    if constexpr (!kTwoFrag) {  // 256-wide dX tiles: no registers to spare for a second fragment set
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        mma_kk(buf, TRANS, kk);
-        put_part(buf ^ 1, kk, Snext, ah);
-      }
-      wait_vm(std::integral_constant<int, 3>{});  // stage kt+1's A in LDS; stage kt+2's codes may fly
-      __syncthreads();
-      return;
-    }
+    read_levels(Snext);
+    __builtin_amdgcn_sched_barrier(0);
     Frags F0, F1;
     load_frags(buf, TRANS, 0, F0);
     load_frags(buf, TRANS, 1, F1);
@@ -467,7 +408,7 @@ __global__ __launch_bounds__(512) void nf4_gemm_kernel(GemmParams p) {
   // operands were loaded in the prologue (lora_load above) where registers allow.
   for (int k2 = 0; k2 < p.ksteps2; ++k2) {
     LoraStage L;
-    if (kLoraEarly && k2 == 0) L = L0;
+    if (k2 == 0) L = L0;
     else lora_load(k2, L);
     lora_put(L);
     __syncthreads();

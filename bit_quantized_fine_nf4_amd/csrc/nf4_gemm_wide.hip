@@ -670,12 +670,13 @@ __global__ __launch_bounds__(kThreads) void nf4_gemm_wide_dx_kernel(GemmParams p
 #pragma unroll
         for (int j = 0; j < kTN; ++j) acc[i][j] = wmfma(af[kk & 1][i], bcur[j][kk], acc[i][j]);
       lut_use(lv[kk & 1], sc[kk & 1], kk, bnext);
-      // interleave: each MFMA followed by one LDS read and a few decode instructions
+      // interleave: each MFMA followed by one LDS read and three decode instructions
+      // (two measured 2 % slower here: this decode has more VALU work per group)
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
         __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
-        __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);  // VALU
+        __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);  // VALU
       }
       __builtin_amdgcn_sched_barrier(0);
       if (kk == 2) {

@@ -311,11 +311,13 @@ def bench_attn_proj(args, torch, nf4, wl):
     for v in stages_out.values():
         for k in list(v):
             v[k] = round(v[k], 4)
+    # 4096 x 4096 with 2048 tokens: 256x128 tiles, the forward on the four-wave kernel,
+    # dX on the eight-wave one
     if gemm_dx_ms >= gemm_fwd_ms:
-        dom, dom_ms, dom_flops = "nf4_gemm_kernel<dX>", gemm_dx_ms, 2 * M * h * o + 2 * M * r * h
+        dom, dom_ms, dom_flops = "nf4_gemm_kernel<256,128,true>", gemm_dx_ms, 2 * M * h * o + 2 * M * r * h
         tkey = "gemm_dx"
     else:
-        dom, dom_ms, dom_flops = "nf4_gemm_kernel<fwd>", gemm_fwd_ms, 2 * M * h * o + 2 * M * r * o
+        dom, dom_ms, dom_flops = "nf4_gemm_wide_fwd_kernel<1>", gemm_fwd_ms, 2 * M * h * o + 2 * M * r * o
         tkey = "gemm_fwd"
     achieved = dom_flops / dom_ms / 1e9
     roofline = {"bound": "mfma", "achieved": round(achieved, 3), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",

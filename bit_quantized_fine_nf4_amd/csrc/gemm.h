@@ -35,8 +35,8 @@ struct GemmParams {
 };
 
 hipError_t launch_nf4_gemm(GemmParams &gp, bool trans, hipStream_t st);
-// 256 x 256 tiles with four waves that decode B in registers, both directions
-// (nf4_gemm_wide.hip)
-hipError_t launch_nf4_gemm_wide(GemmParams &gp, bool trans, hipStream_t st);
+// 256 x bn tiles (bn = 256 or 128) with four waves that decode B in registers, both
+// directions (nf4_gemm_wide.hip)
+hipError_t launch_nf4_gemm_wide(GemmParams &gp, bool trans, int bn, hipStream_t st);
 
 }  // namespace ql

@@ -57,6 +57,9 @@ QL_DEV u32x4 wtr_pair(const uint16_t *lo, const uint16_t *hi) {
   const u32x2 ua = __builtin_bit_cast(u32x2, a), ub = __builtin_bit_cast(u32x2, b);
   return u32x4{ua[0], ua[1], ub[0], ub[1]};
 }
+// (a device function, not the builtin inline in a kernel template's lambda: there
+// the host pass of this compiler drops the kernel's launch stub without a
+// diagnostic, and loading the library then fails on the undefined symbol)
 QL_DEV void wload16_to_lds(__amdgpu_buffer_rsrc_t r, uint16_t *dst, int voff, int soff) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void *)dst, 16, voff, soff, 0, 0);
 }
@@ -72,24 +75,27 @@ QL_DEV void wbarrier() {
   asm volatile("" ::: "memory");
 }
 
-constexpr int kBM = 256, kBN = 256, kBK = 64, kThreads = 256;
-constexpr int kTM = 8, kTN = 2;       // 32x32 MFMA tiles per wave: 8 along M, 2 along N
+// Tiles are 256 x (128 TN): TN = 2 for 256-wide tiles, 1 for 128-wide ones.  Wave w
+// owns output columns [32 TN w, 32 TN (w + 1)): TN tiles of 32 columns.
+constexpr int kBM = 256, kBK = 64, kThreads = 256;
+constexpr int kTM = 8;                // 32x32 MFMA tiles per wave along M
 constexpr int kStages = 4;            // A ring depth
 constexpr int kStageElems = kBM * kBK;  // 256 rows x 64 k (bf16)
 constexpr int kLutCopies = 16;        // lane l reads copy l % 16 of the pair table
 constexpr int kLutBytes = 256 * 8 * kLutCopies;
-constexpr int kLdc = kBN + 8;         // epilogue staging row stride (elements)
-constexpr int kLdsBytes = (kLutBytes + kStages * kStageElems * 2) > (kBM * kLdc * 2)
-                              ? (kLutBytes + kStages * kStageElems * 2)
-                              : (kBM * kLdc * 2);
-constexpr int kLdkn = kBN + 32;       // LoRA B2 tile [64 k][kLdkn] (transposing reads)
+constexpr int wmax(int a, int b) { return a > b ? a : b; }
 
 // row r of an A stage keeps its 8 chunks of 16 bytes in the order c ^ swz(r)
 QL_DEV int a_swz(int r) { return (r >> 1) & 7; }
 
 }  // namespace
 
+template <int TN>
 __global__ __launch_bounds__(kThreads) void nf4_gemm_wide_fwd_kernel(GemmParams p) {
+  constexpr int kTN = TN, kBN = 128 * TN, kWC = 32 * TN;
+  constexpr int kLdc = kBN + 8;    // epilogue staging row stride (elements)
+  constexpr int kLdkn = kBN + 32;  // LoRA B2 tile [64 k][kLdkn] (transposing reads)
+  constexpr int kLdsBytes = wmax(kLutBytes + kStages * kStageElems * 2, kBM * kLdc * 2);
   __shared__ __attribute__((aligned(16))) char lds[kLdsBytes];
   // the A ring first, so the fragment reads of all four buffers reach their
   // addresses from two base registers (16-bit offsets); the table after it
@@ -135,7 +141,7 @@ __global__ __launch_bounds__(kThreads) void nf4_gemm_wide_fwd_kernel(GemmParams 
                      kt * kBK * 2 + (c & ~1) * rowstepA);
   };
 
-  // ---- B: lane (l32, g) of wave w decodes codes rows 64w + 32j + l32 (j = 0, 1)
+  // ---- B: lane (l32, g) of wave w decodes codes rows 32 TN w + 32j + l32 (j < TN)
   const auto rC = wrsrc(p.codes + n0 * (p.ldw >> 1), nrows * (p.ldw >> 1));
   const auto rQ = wrsrc(p.qabsmax + n0 * bpr, nrows * bpr);
   const auto rS2 = wrsrc(p.scale2, ((p.wrows * bpr + 255) >> 8) * 4);
@@ -143,7 +149,7 @@ __global__ __launch_bounds__(kThreads) void nf4_gemm_wide_fwd_kernel(GemmParams 
   int64_t blk0[kTN];
 #pragma unroll
   for (int j = 0; j < kTN; ++j) {
-    const int row = 64 * wv + 32 * j + l32;
+    const int row = kWC * wv + 32 * j + l32;
     voffC[j] = (int)(row * (p.ldw >> 1) + 16 * g);
     voffQ[j] = (int)(row * bpr);
     blk0[j] = (n0 + row) * bpr;
@@ -246,9 +252,9 @@ __global__ __launch_bounds__(kThreads) void nf4_gemm_wide_fwd_kernel(GemmParams 
       lut_use(lv, ah, part, bcur);
     }
   }
-  // step 0's B loads and so stage 0 are done once the 22 younger operations (stage 1,
-  // step 1's B loads, stage 2) are all that may be outstanding
-  wait_vm(std::integral_constant<int, 22>{});
+  // step 0's B loads and so stage 0 are done once the 16 + 3 TN younger operations
+  // (stage 1, step 1's B loads, stage 2) are all that may be outstanding
+  wait_vm(std::integral_constant<int, 16 + 3 * TN>{});
   wbarrier();
   read_a(0, 0, af[0]);
   Lv lv[2];
@@ -272,7 +278,9 @@ __global__ __launch_bounds__(kThreads) void nf4_gemm_wide_fwd_kernel(GemmParams 
   auto step = [&](auto bufc, int kt, BRegs &Rnext, BRegs &Rfree) {
     constexpr int BUF = decltype(bufc)::value;
     load_b(kt + 2, Rfree);
-    float ah[kTN] = {ahn[0], ahn[1]};
+    float ah[kTN];
+#pragma unroll
+    for (int j = 0; j < kTN; ++j) ah[j] = ahn[j];
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
@@ -289,18 +297,19 @@ __global__ __launch_bounds__(kThreads) void nf4_gemm_wide_fwd_kernel(GemmParams 
 #pragma unroll
         for (int j = 0; j < kTN; ++j) acc[i][j] = wmfma(af[kk & 1][i], bcur[j][kk], acc[i][j]);
       lut_use(lv[kk & 1], ah, kk, bnext);
-      // interleave: each MFMA followed by one LDS read and a few decode instructions
+      // interleave: each MFMA followed by LDS reads and a few decode instructions
+      // (128-wide tiles: half the MFMAs per group for the same A reads)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
-        __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);  // VALU
+      for (int i = 0; i < 8 * TN; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);           // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x100, TN == 2 ? 1 : 2, 0);  // LDS read
+        __builtin_amdgcn_sched_group_barrier(0x002, TN == 2 ? 2 : 3, 0);  // VALU
       }
       __builtin_amdgcn_sched_barrier(0);
       if (kk == 2) {
         // younger than this wave's copy of stage kt + 1: the B loads of step kt + 1,
-        // the copy of stage kt + 2, the B loads of step kt + 2
-        wait_vm(std::integral_constant<int, 20>{});
+        // the copy of stage kt + 2, the B loads of step kt + 2 (3 TN + 8 + 3 TN)
+        wait_vm(std::integral_constant<int, 8 + 6 * TN>{});
         wbarrier();
         dma_a(kt + 3, (BUF + 3) % kStages);
         __builtin_amdgcn_sched_barrier(0);
@@ -345,10 +354,10 @@ __global__ __launch_bounds__(kThreads) void nf4_gemm_wide_fwd_kernel(GemmParams 
         const u32x4 v = wload128(rA2, (int)((r * p.lda2 + lc * 8) * 2), k2 * kBK * 2);
         *reinterpret_cast<u32x4 *>(a2 + r * kBK + ((lc ^ a_swz(r)) << 3)) = v;
       }
-      // B2: 64 rows (k) x 256 columns, 32 chunks per row, 8 per thread
+      // B2: 64 rows (k) x kBN columns, kBN / 8 chunks per row, kBN / 32 per thread
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int ch = tid + kThreads * u, kr = ch >> 5, c8 = ch & 31;
+      for (int u = 0; u < kBN / 32; ++u) {
+        const int ch = tid + kThreads * u, kr = (int)((unsigned)ch / (kBN / 8)), c8 = (int)((unsigned)ch % (kBN / 8));
         const u32x4 v = wload128(rB2, (int)(((int64_t)(k2 * kBK + kr) * p.ldb2 + c8 * 8) * 2), 0);
         *reinterpret_cast<u32x4 *>(b2 + kr * kLdkn + c8 * 8) = v;
       }
@@ -358,7 +367,7 @@ __global__ __launch_bounds__(kThreads) void nf4_gemm_wide_fwd_kernel(GemmParams 
         u32x4 af[kTM];
         read_a(0, kk, af);
         u32x4 bf[kTN];
-        const uint16_t *b0 = b2 + (32 * g + 8 * kk + (c >> 2)) * kLdkn + 64 * wv + ((lane >> 4) & 1) * 16 + (c & 3) * 4;
+        const uint16_t *b0 = b2 + (32 * g + 8 * kk + (c >> 2)) * kLdkn + kWC * wv + ((lane >> 4) & 1) * 16 + (c & 3) * 4;
 #pragma unroll
         for (int j = 0; j < kTN; ++j) bf[j] = wtr_pair(b0 + 32 * j, b0 + 4 * kLdkn + 32 * j);
 #pragma unroll
@@ -379,7 +388,7 @@ __global__ __launch_bounds__(kThreads) void nf4_gemm_wide_fwd_kernel(GemmParams 
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         const int row = 32 * i + 8 * (v >> 2) + 4 * g + (v & 3);
-        const int col = 64 * wv + 32 * j + l32;
+        const int col = kWC * wv + 32 * j + l32;
         cs[row * kLdc + col] = wbf16(acc[i][j][v]);
       }
   __syncthreads();
@@ -424,14 +433,15 @@ namespace {
 constexpr int kXStagesA = 3;                  // A (dY) ring
 constexpr int kXStagesC = 5;                  // code ring
 constexpr int kXStagesS = 4;                  // a_hat ring
-constexpr int kXCodeBytes = 64 * (kBN / 2);   // 64 code rows x 256 columns
+constexpr int kXBN = 256, kXTN = 2;           // 256-wide tiles: two 32-column MFMA tiles per wave
+constexpr int kXLdc = kXBN + 8;               // epilogue staging row stride (elements)
+constexpr int kXCodeBytes = 64 * (kXBN / 2);  // 64 code rows x 256 columns
 constexpr int kXAhFloats = 4 * 64;            // [4 blocks][64 rows]
 constexpr int kXLutCopies = 8;                // lane l reads copy l % 8 of the pair table
 constexpr int kXOffC = kXStagesA * kStageElems * 2;
 constexpr int kXOffS = kXOffC + kXStagesC * kXCodeBytes;
 constexpr int kXOffLut = kXOffS + kXStagesS * kXAhFloats * 4;
-constexpr int kXLdsBytes = (kXOffLut + 256 * 8 * kXLutCopies) > (kBM * kLdc * 2) ? (kXOffLut + 256 * 8 * kXLutCopies)
-                                                                                 : (kBM * kLdc * 2);
+constexpr int kXLdsBytes = wmax(kXOffLut + 256 * 8 * kXLutCopies, kBM * kXLdc * 2);
 typedef int wi32x2 __attribute__((ext_vector_type(2)));
 QL_DEV u32x2 wtr4(const uint8_t *ptr) {
   typedef __attribute__((address_space(3))) wi32x2 lds_i32x2;
@@ -440,6 +450,7 @@ QL_DEV u32x2 wtr4(const uint8_t *ptr) {
 }  // namespace
 
 __global__ __launch_bounds__(kThreads) void nf4_gemm_wide_dx_kernel(GemmParams p) {
+  constexpr int kTN = kXTN, kBN = kXBN, kLdc = kXLdc;
   __shared__ __attribute__((aligned(16))) char lds[kXLdsBytes];
   uint16_t *ring = reinterpret_cast<uint16_t *>(lds);
   uint8_t *cring = reinterpret_cast<uint8_t *>(lds + kXOffC);
@@ -506,9 +517,7 @@ __global__ __launch_bounds__(kThreads) void nf4_gemm_wide_dx_kernel(GemmParams p
     const auto rC = wrsrc(p.codes + r0 * rowB + (n0 >> 1), (p.wrows - r0) * rowB - (n0 >> 1));
 #pragma unroll
     for (int j = 0; j < 2; ++j)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rC, (__attribute__((address_space(3))) void *)(cring + buf * kXCodeBytes + 1024 * (2 * wv + j)), 16,
-          voffC[j], 0, 0, 0);
+      wload16_to_lds(rC, reinterpret_cast<uint16_t *>(cring + buf * kXCodeBytes + 1024 * (2 * wv + j)), voffC[j], 0);
   };
   // transposing read t (rows 16t .. 16t + 15 of the lane's 32) of column tile j:
   // lane i of its 16-lane group names row 32 g + 16 t + i, whose swizzle is (i >> 1) & 7
@@ -761,11 +770,16 @@ __global__ __launch_bounds__(kThreads) void nf4_gemm_wide_dx_kernel(GemmParams p
   }
 }
 
-hipError_t launch_nf4_gemm_wide(GemmParams &gp, bool trans, hipStream_t st) {
+hipError_t launch_nf4_gemm_wide(GemmParams &gp, bool trans, int bn, hipStream_t st) {
+  if (bn != 256 && bn != 128) return hipErrorInvalidValue;
   gp.tiles_m = (int)((gp.M + kBM - 1) / kBM);
-  gp.tiles_n = (int)((gp.N + kBN - 1) / kBN);
-  if (trans) return launch(nf4_gemm_wide_dx_kernel, gp.tiles_m * gp.tiles_n, kThreads, st, gp);
-  return launch(nf4_gemm_wide_fwd_kernel, gp.tiles_m * gp.tiles_n, kThreads, st, gp);
+  gp.tiles_n = (int)((gp.N + bn - 1) / bn);
+  const unsigned grid = (unsigned)(gp.tiles_m * gp.tiles_n);
+  // the dX kernel has 256-wide tiles only: a 128-wide version measured slower than
+  // the eight-wave kernel on a 4096 x 4096 weight with 2048 tokens (101 vs 90 us)
+  if (trans) return bn == 256 ? launch(nf4_gemm_wide_dx_kernel, grid, kThreads, st, gp) : hipErrorInvalidValue;
+  return bn == 256 ? launch(nf4_gemm_wide_fwd_kernel<2>, grid, kThreads, st, gp)
+                   : launch(nf4_gemm_wide_fwd_kernel<1>, grid, kThreads, st, gp);
 }
 
 }  // namespace ql

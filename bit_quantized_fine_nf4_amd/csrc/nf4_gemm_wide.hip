@@ -265,19 +265,18 @@ __global__ __launch_bounds__(kThreads) void nf4_gemm_wide_fwd_kernel(GemmParams 
   // Step kt (ring buffer BUF = kt % 4, compile-time: the loop is unrolled four
   // times; the two B register sets alternate).  On entry af[0] holds group 0's A
   // fragments of step kt, bcur its decoded B, lv[0] and ahn the first table reads
-  // and scales of step kt + 1's decode.  Issued at its start: the B loads of step
-  // kt + 2 (into the set step kt's own B came from).  The decode of step kt + 1
-  // runs between the MFMAs: while group kk's 16 MFMAs issue, the A fragments of
-  // group kk + 1 and the table reads of part kk + 1 are in flight and part kk's
-  // levels are scaled and converted.  After group 2's MFMAs this wave's copy of
-  // stage kt + 1 is awaited, one barrier makes every wave's copy visible and frees
-  // buffer (kt + 3) % 4 (last read in step kt - 1), and the copy of stage kt + 3
-  // goes there; group 3's MFMAs then cover the reads of step kt + 1's group-0
-  // fragments and of the first part of step kt + 2's decode.  Loads past the last
-  // step read harmless data that is never used.
+  // and scales of step kt + 1's decode.  Issued between group 0's MFMAs: the B
+  // loads of step kt + 2 (into the set step kt's own B came from).  The decode of
+  // step kt + 1 runs between the MFMAs: while group kk's MFMAs issue, the A
+  // fragments of group kk + 1 and the table reads of part kk + 1 are in flight and
+  // part kk's levels are scaled and converted.  After group 2's MFMAs this wave's
+  // copy of stage kt + 1 is awaited, one barrier makes every wave's copy visible
+  // and frees buffer (kt + 3) % 4 (last read in step kt - 1), and group 3 issues
+  // the copy of stage kt + 3 into it between its MFMAs, which also cover the reads
+  // of step kt + 1's group-0 fragments and of the first part of step kt + 2's
+  // decode.  Loads past the last step read harmless data that is never used.
   auto step = [&](auto bufc, int kt, BRegs &Rnext, BRegs &Rfree) {
     constexpr int BUF = decltype(bufc)::value;
-    load_b(kt + 2, Rfree);
     float ah[kTN];
 #pragma unroll
     for (int j = 0; j < kTN; ++j) ah[j] = ahn[j];
@@ -285,9 +284,11 @@ __global__ __launch_bounds__(kThreads) void nf4_gemm_wide_fwd_kernel(GemmParams 
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
       if (kk < 3) {
+        if (kk == 0) load_b(kt + 2, Rfree);
         read_a(BUF, kk + 1, af[(kk + 1) & 1]);
         lut_read(Rnext, kk + 1, lv[(kk + 1) & 1]);
       } else {
+        dma_a(kt + 3, (BUF + 3) % kStages);
         read_a((BUF + 1) % kStages, 0, af[0]);
         lut_read(Rfree, 0, lv[0]);
         scale_of(Rfree, ahn);
@@ -302,6 +303,10 @@ __global__ __launch_bounds__(kThreads) void nf4_gemm_wide_fwd_kernel(GemmParams 
 #pragma unroll
       for (int i = 0; i < 8 * TN; ++i) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);           // MFMA
+        // the step's B loads ride on group 0, the copy of stage kt + 3 on group 3: issued
+        // back to back by all four waves they queue at the compute unit's address unit
+        // and stall the issuing wave, and the matrix core with it
+        if ((kk == 0 && i < 3 * TN) || (kk == 3 && i < 8)) __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);  // VMEM
         __builtin_amdgcn_sched_group_barrier(0x100, TN == 2 ? 1 : 2, 0);  // LDS read
         __builtin_amdgcn_sched_group_barrier(0x002, TN == 2 ? 2 : 3, 0);  // VALU
       }
@@ -311,7 +316,6 @@ __global__ __launch_bounds__(kThreads) void nf4_gemm_wide_fwd_kernel(GemmParams 
         // the copy of stage kt + 2, the B loads of step kt + 2 (3 TN + 8 + 3 TN)
         wait_vm(std::integral_constant<int, 8 + 6 * TN>{});
         wbarrier();
-        dma_a(kt + 3, (BUF + 3) % kStages);
         __builtin_amdgcn_sched_barrier(0);
       }
     }
@@ -643,11 +647,12 @@ __global__ __launch_bounds__(kThreads) void nf4_gemm_wide_dx_kernel(GemmParams p
   // bnext (its part 0 read during step kt - 1).  On entry af[0] holds group 0's A
   // fragments, tw0 the first transposing reads of stage kt + 1, lv[0] / sc[0] its
   // part-0 table entries and scales.  At its start the a_hat values of stage
-  // kt + 2 are published.  After group 2: this wave's copies of A stage kt + 1 and
-  // code stages up to kt + 4 are awaited (2 younger operations: the scales of
-  // stage kt + 3), one barrier publishes every wave's copies and a_hat values and
-  // frees A buffer (kt + 2) % 3, code buffer kt % 5; then the copies of code stage
-  // kt + 5 and A stage kt + 2 and the scale loads of stage kt + 4 are issued.
+  // kt + 2 are published.  After group 2: all of this wave's vector-memory
+  // operations (A stage kt + 1, code stage kt + 4, the scales of stage kt + 3) and
+  // its a_hat stores are awaited, one barrier publishes every wave's copies and
+  // a_hat values and frees A buffer (kt + 2) % 3 and code buffer kt % 5; group 3
+  // then issues the copies of code stage kt + 5 and A stage kt + 2 and the scale
+  // loads of stage kt + 4 between its MFMAs.
   auto step = [&](int kt, QS &Qcur) {
     const int bA = kt % kXStagesA, bC1 = (kt + 1) % kXStagesC, bC2 = (kt + 2) % kXStagesC;
     const int bS1 = (kt + 1) % kXStagesS, bS2 = (kt + 2) % kXStagesS;
@@ -670,6 +675,9 @@ __global__ __launch_bounds__(kThreads) void nf4_gemm_wide_dx_kernel(GemmParams p
         sc_read(bS1, 3, sc[1]);
         read_tr(bC2, 0, tw0);
       } else {
+        dma_c(kt + 5, kt % kXStagesC);
+        dma_a(kt + 2, (kt + 2) % kXStagesA);
+        load_qs(kt + 4, Qcur);
         read_a((kt + 1) % kXStagesA, 0, af[0]);
         lut_read(tw0, 0, lv[0]);
         sc_read(bS2, 0, sc[0]);
@@ -680,22 +688,24 @@ __global__ __launch_bounds__(kThreads) void nf4_gemm_wide_dx_kernel(GemmParams p
         for (int j = 0; j < kTN; ++j) acc[i][j] = wmfma(af[kk & 1][i], bcur[j][kk], acc[i][j]);
       lut_use(lv[kk & 1], sc[kk & 1], kk, bnext);
       // interleave: each MFMA followed by one LDS read and three decode instructions
-      // (two measured 2 % slower here: this decode has more VALU work per group)
+      // (two measured 2 % slower here: this decode has more VALU work per group); in
+      // group 3 the first twelve also carry one of the step's twelve vector-memory
+      // instructions (cycle stamps: issued back to back after the barrier, the four
+      // waves' copies queued at the address unit for about 750 cycles)
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
-        __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);  // VALU
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                            // MFMA
+        if (kk == 3 && i < 12) __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);  // VMEM
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                            // LDS read
+        __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);                            // VALU
       }
       __builtin_amdgcn_sched_barrier(0);
       if (kk == 2) {
-        wait_vm_lgkm(std::integral_constant<int, 2>{});
+        // every vector-memory operation of the previous step (this wave's copies of A
+        // stage kt + 1 and code stage kt + 4, the scale loads of stage kt + 3, issued
+        // in group 3 in an order the scheduler chooses), and this wave's a_hat stores
+        wait_vm_lgkm(std::integral_constant<int, 0>{});
         wbarrier();
-        dma_c(kt + 5, kt % kXStagesC);
-        __builtin_amdgcn_sched_barrier(0);
-        dma_a(kt + 2, (kt + 2) % kXStagesA);
-        __builtin_amdgcn_sched_barrier(0);
-        load_qs(kt + 4, Qcur);
         __builtin_amdgcn_sched_barrier(0);
       }
     }

@@ -293,7 +293,9 @@ def bench_attn_proj(args, torch, nf4, wl):
     torch.cuda.synchronize()
 
     ms_per_step = wall * 1e3 / args.steps
-    st_ms = {k: statistics.mean(e[i].elapsed_time(e[i + 1]) for e in evs) for i, k in enumerate(stages)}
+    # median over the steps: a host-side hiccup in one step of this untimed pass would
+    # otherwise dominate its stage
+    st_ms = {k: statistics.median(e[i].elapsed_time(e[i + 1]) for e in evs) for i, k in enumerate(stages)}
     gemm_fwd_ms = statistics.mean(hev.elapsed_ms(k[0], k[1]) for k, w in zip(kevs, timed) if w[0])
     gemm_dx_ms = statistics.mean(hev.elapsed_ms(k[2], k[3]) for k, w in zip(kevs, timed) if w[1])
     hev.close()
@@ -496,7 +498,7 @@ def bench_block(args, torch, nf4, wl, c):
     torch.cuda.synchronize()
     st_ms = {}
     for j in range(1, len(names)):
-        st_ms[names[j]] = statistics.mean(e[j - 1].elapsed_time(e[j]) for e in evs)
+        st_ms[names[j]] = statistics.median(e[j - 1].elapsed_time(e[j]) for e in evs)  # robust to one slow step
 
     ms_per_step = wall * 1e3 / steps
     fwd_f, bwd_f = block_flops(c)

@@ -10,6 +10,9 @@
 //                        chunk staged once in LDS); lora_rank_reduce_kernel
 //                        adds the K splits in order and rounds to bf16 with
 //                        the s-scaled copy the GEMM's rank-r step uses
+//   lora_rank16_kernel   the same products for r <= 16 in one pass: 8- or
+//                        16-row workgroups take the whole K, their eight
+//                        waves' sums added in LDS (no partials, no reduce)
 //   nf4_gemm_kernel      fused dequant-GEMM, MFMA 32x32x16: forward
 //                        (B = W_hat, K along h) and dX (B = W_hat^T, K
 //                        along o); the rank-r LoRA product is added as extra
@@ -28,7 +31,8 @@
 //                        split over tokens; lora_grad_reduce_kernel sums the
 //                        splits in order, scales by s and stores dL1 [h][r]
 //                        and dL2 [r][o]; both run before the dX GEMM on the
-//                        caller's stream
+//                        caller's stream (lora_grad16_kernel: r <= 16 in one
+//                        pass, 32- or 64-wide tiles over every token)
 
 #include "linear.h"
 #include "gemm.h"
@@ -82,7 +86,7 @@ QL_DEV __amdgpu_buffer_rsrc_t gv_rsrc(const void *base, int64_t bytes) {
 // lora_rank_kernel: a workgroup owns 64 rows and one K range (a multiple of 64
 // wide); its four waves take 16 rows each and every rank column, with 16x16x32
 // MFMAs.  A operand (X or dY, k-contiguous): lane (i, g) loads 16 bytes of row i
-// at k + 8g straight into registers, one 64-wide chunk ahead; rows past M read
+// at k + 8g straight into registers, three 64-wide chunks ahead; rows past M read
 // as zero.  B operand: L2 [r][o] (backward) is k-contiguous, so its fragments
 // are 16-byte loads of L2 rows; L1 [h][r] (forward) is r-contiguous, so each
 // 64 x r chunk of it goes into a double-buffered LDS tile with rows padded by
@@ -122,8 +126,25 @@ constexpr int kRankRows = 64;  // rows per workgroup: 16 per wave
 
 // The backward's extra duties, spread over a whole grid (gt: this thread's index,
 // gn: the grid's thread count).
+// Piece idx of L1p in 16-byte units (r a multiple of 8: L1 is 16-byte aligned and
+// ldp a multiple of 64, so every piece is whole): L1's or zero.
+QL_DEV u32x4 l1p_piece(const RankParams &p, int64_t idx) {
+  const int pp = p.ldp >> 3;
+  const int64_t a = idx / pp;
+  const int b = (int)(idx % pp);
+  return b < (p.r >> 3) ? *reinterpret_cast<const u32x4 *>(p.L1 + a * p.r + 8 * b) : u32x4{0, 0, 0, 0};
+}
+QL_DEV void l1p_store(const RankParams &p, int64_t idx, u32x4 v) {
+  const int pp = p.ldp >> 3;
+  *reinterpret_cast<u32x4 *>(p.L1p + (idx / pp) * p.ldp + 8 * (idx % pp)) = v;
+}
+
 QL_DEV void rank_extras(const RankParams &p, int64_t gt, int64_t gn) {
   if (!p.L1p) return;
+  if (p.r % 8 == 0) {
+    for (int64_t idx = gt; idx < p.h * (p.ldp >> 3); idx += gn) l1p_store(p, idx, l1p_piece(p, idx));
+    return;
+  }
   for (int64_t idx = gt; idx < p.h * p.ldp; idx += gn) {
     const int64_t a = idx / p.ldp, b = idx % p.ldp;
     p.L1p[idx] = b < p.r ? p.L1[a * p.r + b] : (uint16_t)0;
@@ -178,12 +199,17 @@ __global__ __launch_bounds__(256) void lora_rank_kernel(RankParams p) {
     u32x4 a[2];
     u32x4 b[BV];
   };
+  // a chunk past the split's end is loaded from an offset past every buffer view: the
+  // loads return zero without touching memory, and every step issues the same loads
+  // (so the compiler's wait counts stay exact)
+  constexpr int kPastEnd = 0x7FFF0000;
   auto load = [&](int c, Chunk &C) {
-    const int so = __builtin_amdgcn_readfirstlane(c * 128);  // bytes of 64 k
+    const bool live = c < nch;
+    const int so = __builtin_amdgcn_readfirstlane(live ? c * 128 : kPastEnd);  // bytes of 64 k
     C.a[0] = __builtin_amdgcn_raw_buffer_load_b128(rA, voffA, so, 0);
     C.a[1] = __builtin_amdgcn_raw_buffer_load_b128(rA, voffA + 64, so, 0);
     if (!KN || VEC) {
-      const int sb = KN ? __builtin_amdgcn_readfirstlane(c * 128 * r) : so;  // KN: 64 rows of r
+      const int sb = KN ? __builtin_amdgcn_readfirstlane(live ? c * 128 * r : kPastEnd) : so;  // KN: 64 rows of r
 #pragma unroll
       for (int j = 0; j < BV; ++j) C.b[j] = __builtin_amdgcn_raw_buffer_load_b128(rB, voffB[j], sb, 0);
     }
@@ -219,25 +245,27 @@ __global__ __launch_bounds__(256) void lora_rank_kernel(RankParams p) {
       }
   };
 
-  // Chunk c computes from LDS buffer c & 1 while chunk c + 1's loads are in flight;
-  // it is written to the other buffer after the computation (whose reads of that
-  // buffer ended at the previous barrier), then one barrier.
-  Chunk C0, C1;
-  load(0, C0);
-  put(0, 0, C0);
+  // Loads run kDepth chunks ahead in a ring of kDepth + 1 register stages (one
+  // chunk ahead left each workgroup waiting a memory latency per chunk).  Chunk c
+  // computes from LDS buffer c & 1; chunk c + 1's factor goes to the other buffer
+  // after that (whose reads ended at the previous barrier), then one barrier.  The
+  // loop runs whole rounds of kRing chunks with no early exit: chunks past the end
+  // load as zero and add nothing (the host makes the chunk count a multiple of
+  // kRing wherever K allows).
+  constexpr int kDepth = 3, kRing = kDepth + 1;
+  Chunk C[kRing];
+#pragma unroll
+  for (int j = 0; j < kDepth; ++j) load(j, C[j]);
+  put(0, 0, C[0]);
   __syncthreads();
-  for (int c = 0; c < nch; c += 2) {
-    if (c + 1 < nch) load(c + 1, C1);
-    __builtin_amdgcn_sched_barrier(0);
-    compute(0, C0);
-    if (c + 1 >= nch) break;
-    put(c + 1, 1, C1);
-    __syncthreads();
-    if (c + 2 < nch) load(c + 2, C0);
-    __builtin_amdgcn_sched_barrier(0);
-    compute(1, C1);
-    if (c + 2 < nch) {
-      put(c + 2, 0, C0);
+  for (int c0 = 0; c0 < nch; c0 += kRing) {
+#pragma unroll
+    for (int u = 0; u < kRing; ++u) {
+      const int c = c0 + u;
+      load(c + kDepth, C[(u + kDepth) % kRing]);
+      __builtin_amdgcn_sched_barrier(0);
+      compute(u & 1, C[u]);
+      put(c + 1, (u + 1) & 1, C[(u + 1) % kRing]);
       __syncthreads();
     }
   }
@@ -553,6 +581,293 @@ __global__ __launch_bounds__(256) void lora_grad_reduce_kernel(GradProblem pa, G
 }
 
 // ---------------------------------------------------------------------------
+// Ranks up to 16 in one pass ([MC] "The algebra", Eq. 3 and "One training step";
+// [TT] §4).  A rank-16 factor is small next to the activations it multiplies, so
+// a workgroup can take few rows (or few adapter-gradient columns) and the whole
+// reduction: no split partial sums, and no reduce launch, whose fixed cost of a
+// few microseconds per launch dominated these products on a 4096-wide
+// projection.  Eight waves split the reduction between them, each loading three
+// of its 64-wide pieces ahead into registers; the waves' sums are added in wave
+// order through LDS (deterministic).  Pieces past the end load from an offset
+// past every buffer view, so they read as zero and every wave issues the same
+// loads in each round.
+// ---------------------------------------------------------------------------
+constexpr int kP16Waves = 8;
+constexpr int kP16Threads = 64 * kP16Waves;
+constexpr int kP16PastEnd = 0x7FFF0000;
+
+// T = X·L1 (KN) or U = dY·L2^T for r <= 16: workgroup = ROWS rows (16, or 8 when
+// 16-row workgroups would leave compute units idle; the MFMA rows past them read
+// as zero), wave w takes the 64-wide K chunks w, w + 8, ...  The factor's chunk goes
+// through the wave's own LDS tile, loaded in whole 128-byte lines: an L1 chunk (64 x
+// r elements, 128 r contiguous bytes) into rows padded to 24 elements, read back with
+// transposing reads; an L2 chunk (16 rows of 64 k, rows past r reading as zero) into
+// rows padded to 72 elements, read back as each lane's 8 consecutive k.  Outputs as
+// lora_rank_kernel's.
+template <bool KN, bool VEC, int ROWS>
+__global__ __launch_bounds__(kP16Threads) void lora_rank16_kernel(RankParams p) {
+  constexpr int LDB = 24;  // KN tile [64 k][LDB]
+  constexpr int LDK = 72;  // L2 tile [16 q][LDK]
+  static_assert(16 * LDK <= 64 * LDB, "both tiles fit the wave's LDS area");
+  __shared__ __attribute__((aligned(16))) uint16_t Bs[kP16Waves][64 * LDB];
+  __shared__ float red[kP16Waves][16][16];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = lane >> 4, i16 = lane & 15;
+  const int r = p.r;
+  const int64_t m0 = (int64_t)blockIdx.x * ROWS;
+  const int64_t mrows = p.M - m0 < ROWS ? p.M - m0 : ROWS;
+  // backward: the first round of the padded L1 copy's pieces is loaded here and
+  // stored after the products, so its latency overlaps them
+  const int64_t gt = (int64_t)blockIdx.x * kP16Threads + tid, gn = (int64_t)gridDim.x * kP16Threads;
+  const bool l1vec = p.L1p && p.r % 8 == 0;
+  const int64_t l1n = l1vec ? p.h * (p.ldp >> 3) : 0;
+  const u32x4 l1first = gt < l1n ? l1p_piece(p, gt) : u32x4{0, 0, 0, 0};
+  const int kc = (int)(p.K >> 6);
+  const int nj = kc > wave ? (kc - wave + kP16Waves - 1) / kP16Waves : 0;
+  const auto rA = gv_rsrc(p.A + m0 * p.lda, mrows * p.lda * 2);
+  const int voffA = (int)((i16 * p.lda + 8 * g) * 2);
+  const auto rB = KN ? gv_rsrc(p.B, p.K * r * 2) : gv_rsrc(p.B, (int64_t)r * p.ldb * 2);
+  // KN: pieces `lane` and `lane + 64` of the chunk's 8 r pieces; otherwise rows
+  // lane / 8 and 8 + lane / 8 of L2, 16-byte piece lane % 8 of the chunk's 64 k
+  // (rows past r read as zero)
+  const int voffB0 = KN ? (lane < 8 * r ? lane * 16 : (int)0x80000000u)
+                        : (int)(((lane >> 3) * p.ldb + (lane & 7) * 8) * 2);
+  const int voffB1 = KN ? (lane + 64 < 8 * r ? (lane + 64) * 16 : (int)0x80000000u)
+                        : voffB0 + (int)(8 * p.ldb * 2);
+  uint16_t *bt = Bs[wave];
+  struct Chunk {
+    u32x4 a[2], b[2];
+  };
+  auto load = [&](int j, Chunk &C) {
+    const int c = wave + kP16Waves * j;
+    const bool live = j < nj;
+    const int so = __builtin_amdgcn_readfirstlane(live ? c * 128 : kP16PastEnd);
+    C.a[0] = __builtin_amdgcn_raw_buffer_load_b128(rA, voffA, so, 0);
+    C.a[1] = __builtin_amdgcn_raw_buffer_load_b128(rA, voffA + 64, so, 0);
+    const int sb = KN ? __builtin_amdgcn_readfirstlane(live ? c * 128 * r : kP16PastEnd) : so;
+    C.b[0] = __builtin_amdgcn_raw_buffer_load_b128(rB, voffB0, sb, 0);
+    C.b[1] = __builtin_amdgcn_raw_buffer_load_b128(rB, voffB1, sb, 0);
+  };
+  // the factor's chunk into the wave's tile.  KN: 64 x r elements (columns past r
+  // keep stale values; they only reach accumulator columns q >= r, which are never
+  // stored); otherwise 16 rows of 64 k.
+  auto put = [&](const Chunk &C) {
+    if constexpr (!KN) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+        *reinterpret_cast<u32x4 *>(bt + ((lane >> 3) + 8 * h) * LDK + (lane & 7) * 8) = C.b[h];
+      return;
+    }
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int pc = lane + 64 * h;
+      if (pc >= 8 * r) continue;
+      if (VEC) {
+        const int pr = r >> 3;
+        *reinterpret_cast<u32x4 *>(bt + (pc / pr) * LDB + (pc % pr) * 8) = C.b[h];
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int idx = 8 * pc + e;
+          bt[(idx / r) * LDB + idx % r] = (uint16_t)(C.b[h][e >> 1] >> (16 * (e & 1)));
+        }
+      }
+    }
+  };
+  const int trow = i16 >> 2, tcol = (i16 & 3) * 4;
+  f32x4 acc = f32x4{0, 0, 0, 0};
+  auto compute = [&](const Chunk &C) {
+#pragma unroll
+    for (int sub = 0; sub < 2; ++sub) {
+      u32x4 b;
+      if constexpr (KN) {
+        const uint16_t *lo = bt + (32 * sub + 8 * g + trow) * LDB + tcol;
+        b = tr_pair(lo, lo + 4 * LDB);
+      } else {
+        b = *reinterpret_cast<const u32x4 *>(bt + i16 * LDK + 32 * sub + 8 * g);
+      }
+      acc = mfma16(C.a[sub], b, acc);
+    }
+  };
+  // The wave's own LDS tile needs no barrier: a wave's LDS operations complete in
+  // order, and the compiler keeps the order of these may-alias accesses.
+  constexpr int kDepth = 3, kRing = kDepth + 1;
+  Chunk C[kRing];
+#pragma unroll
+  for (int j = 0; j < kDepth; ++j) load(j, C[j]);
+  for (int j0 = 0; j0 < nj; j0 += kRing) {
+#pragma unroll
+    for (int u = 0; u < kRing; ++u) {
+      load(j0 + u + kDepth, C[(u + kDepth) % kRing]);
+      put(C[u]);
+      compute(C[u]);
+    }
+  }
+
+  // C layout: lane (q = i16, g) holds rows 4g + v
+#pragma unroll
+  for (int v = 0; v < 4; ++v) red[wave][4 * g + v][i16] = acc[v];
+  __syncthreads();
+  if (tid < ROWS * 16) {
+    const int row = tid >> 4, q = tid & 15;
+    float sum = 0.0f;
+#pragma unroll
+    for (int w = 0; w < kP16Waves; ++w) sum += red[w][row][q];
+    if (row < mrows) {
+      const int64_t m = m0 + row;
+      if (p.out1 && q < p.ld1) p.out1[m * p.ld1 + q] = q < r ? to_bf16(sum) : (uint16_t)0;
+      if (p.out2 && q < p.ld2) p.out2[m * p.ld2 + q] = q < r ? to_bf16(p.s * sum) : (uint16_t)0;
+    }
+  }
+  const int W = p.ld1 > p.ld2 ? p.ld1 : p.ld2;
+  if (W > 16) {  // the outputs' columns past the rank tile: zero
+    const int pad = W - 16;
+    for (int idx = tid; idx < ROWS * pad; idx += kP16Threads) {
+      const int row = idx / pad, q = 16 + idx % pad;
+      if (row >= mrows) continue;
+      const int64_t m = m0 + row;
+      if (p.out1 && q < p.ld1) p.out1[m * p.ld1 + q] = 0;
+      if (p.out2 && q < p.ld2) p.out2[m * p.ld2 + q] = 0;
+    }
+  }
+  if (l1vec) {
+    for (int64_t idx = gt; idx < l1n; idx += gn) l1p_store(p, idx, idx == gt ? l1first : l1p_piece(p, idx));
+  } else {
+    rank_extras(p, gt, gn);
+  }
+}
+
+// dL1 = s·X^T·U and dL2 = s·T^T·dY for r <= 16: tiles [0, pa.tiles) are dL1's, the
+// rest dL2's, TI values of i each (pa.tiles, pb.tiles count TI-wide tiles here; TI =
+// 32 when 64-wide tiles would leave compute units idle).  With a tile count that is
+// a multiple of 8, consecutive tiles go to one XCD, whose L2 then serves the
+// neighbours' halves of each 128-byte line.  A workgroup takes every token; wave w
+// the 64-token slabs w, w + 8, ...  A slab of P (64 rows x 2 TI bytes) and of Q (64
+// rows of ldq elements, one contiguous run) go into the wave's own LDS tiles, P rows
+// padded to TI + 8 elements and Q rows to 24, and both come back through
+// transposing reads (8 consecutive tokens per lane).
+template <int TI>
+__global__ __launch_bounds__(kP16Threads) void lora_grad16_kernel(GradProblem pa, GradProblem pb, int rq, float s,
+                                                                  int64_t M) {
+  constexpr int LP = TI + 8, LQ = 24, PPR = TI / 8;  // P: 16-byte pieces per row
+  constexpr int NT = TI / 16;
+  constexpr int kTileElems = 64 * LP + 64 * LQ;
+  constexpr int kRedFloats = kP16Waves * TI * 16;
+  constexpr int kLdsBytes = kP16Waves * kTileElems * 2 > kRedFloats * 4 ? kP16Waves * kTileElems * 2 : kRedFloats * 4;
+  __shared__ __attribute__((aligned(16))) char lds[kLdsBytes];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = lane >> 4, c16 = lane & 15;
+  int64_t bid = blockIdx.x;
+  const int64_t ntiles = pa.tiles + pb.tiles;
+  if ((ntiles & 7) == 0) bid = (bid & 7) * (ntiles >> 3) + (bid >> 3);  // one XCD -> contiguous tiles
+  const bool second = bid >= pa.tiles;
+  const GradProblem &pr = second ? pb : pa;
+  const int64_t tile = second ? bid - pa.tiles : bid;
+  const int64_t i0 = tile * TI;
+  const int64_t ldp = pr.ldp, ldq = pr.ldq;
+  const bool qvec = (ldq & 7) == 0;  // wave-uniform: one problem per workgroup
+  const int nslab = (int)((M + 63) / 64);
+  const int nj = nslab > wave ? (nslab - wave + kP16Waves - 1) / kP16Waves : 0;
+  // rows [0, M) of P from column i0, and of Q; everything past them reads as zero
+  const auto rP = gv_rsrc(pr.P + i0, M * ldp * 2 - i0 * 2);
+  const auto rQ = gv_rsrc(pr.Q, M * ldq * 2);
+  int voffP[PPR], soffP[PPR];
+#pragma unroll
+  for (int u = 0; u < PPR; ++u) {
+    const int pc = lane + 64 * u, row = pc / PPR, c8 = pc % PPR;
+    voffP[u] = (int)((row * ldp + c8 * 8) * 2);
+    soffP[u] = row * LP + c8 * 8;
+  }
+  const int voffQ0 = lane < 8 * ldq ? lane * 16 : (int)0x80000000u;
+  const int voffQ1 = lane + 64 < 8 * ldq ? (lane + 64) * 16 : (int)0x80000000u;
+  uint16_t *ps = reinterpret_cast<uint16_t *>(lds) + wave * kTileElems;
+  uint16_t *qs = ps + 64 * LP;
+  struct Slab {
+    u32x4 p[PPR], q[2];
+  };
+  auto load = [&](int j, Slab &S) {
+    const int sl = wave + kP16Waves * j;
+    const bool live = j < nj;
+    const int sp = __builtin_amdgcn_readfirstlane(live ? (int)(sl * 64 * ldp * 2) : kP16PastEnd);
+    const int sq = __builtin_amdgcn_readfirstlane(live ? (int)(sl * 128 * ldq) : kP16PastEnd);
+#pragma unroll
+    for (int u = 0; u < PPR; ++u) S.p[u] = __builtin_amdgcn_raw_buffer_load_b128(rP, voffP[u], sp, 0);
+    S.q[0] = __builtin_amdgcn_raw_buffer_load_b128(rQ, voffQ0, sq, 0);
+    S.q[1] = __builtin_amdgcn_raw_buffer_load_b128(rQ, voffQ1, sq, 0);
+  };
+  // Q columns past ldq keep stale values; they only reach output columns q >= rq
+  auto put = [&](const Slab &S) {
+#pragma unroll
+    for (int u = 0; u < PPR; ++u) *reinterpret_cast<u32x4 *>(ps + soffP[u]) = S.p[u];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int pc = lane + 64 * h;
+      if (pc >= 8 * ldq) continue;
+      if (qvec) {
+        const int pq = (int)(ldq >> 3);
+        *reinterpret_cast<u32x4 *>(qs + (pc / pq) * LQ + (pc % pq) * 8) = S.q[h];
+      } else {
+        const int lq = (int)ldq;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int idx = 8 * pc + e;
+          qs[(idx / lq) * LQ + idx % lq] = (uint16_t)(S.q[h][e >> 1] >> (16 * (e & 1)));
+        }
+      }
+    }
+  };
+  const int trow = c16 >> 2, tcol = (c16 & 3) * 4;
+  f32x4 acc[NT];
+#pragma unroll
+  for (int a = 0; a < NT; ++a) acc[a] = f32x4{0, 0, 0, 0};
+  auto compute = [&]() {
+#pragma unroll
+    for (int sub = 0; sub < 2; ++sub) {
+      const uint16_t *lq = qs + (32 * sub + 8 * g + trow) * LQ + tcol;
+      const u32x4 bq = tr_pair(lq, lq + 4 * LQ);
+#pragma unroll
+      for (int a = 0; a < NT; ++a) {
+        const uint16_t *lp = ps + (32 * sub + 8 * g + trow) * LP + 16 * a + tcol;
+        acc[a] = mfma16(tr_pair(lp, lp + 4 * LP), bq, acc[a]);
+      }
+    }
+  };
+  constexpr int kDepth = 3, kRing = kDepth + 1;
+  Slab S[kRing];
+#pragma unroll
+  for (int j = 0; j < kDepth; ++j) load(j, S[j]);
+  for (int j0 = 0; j0 < nj; j0 += kRing) {
+#pragma unroll
+    for (int u = 0; u < kRing; ++u) {
+      load(j0 + u + kDepth, S[(u + kDepth) % kRing]);
+      put(S[u]);
+      compute();
+    }
+  }
+
+  // D layout: lane (q = c16, g) holds rows i = 16a + 4g + v; the sums of the eight
+  // waves are added in wave order
+  __syncthreads();  // every wave is done with its tiles, which the sums overwrite
+  float *red = reinterpret_cast<float *>(lds);
+#pragma unroll
+  for (int a = 0; a < NT; ++a)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) red[(wave * TI + 16 * a + 4 * g + v) * 16 + c16] = acc[a][v];
+  __syncthreads();
+  for (int idx = tid; idx < TI * 16; idx += kP16Threads) {
+    // dL2 ([r][I]) stores run along i, dL1 ([I][r]) stores along q
+    const int il = pr.trans ? idx % TI : idx / 16, q = pr.trans ? idx / TI : idx % 16;
+    float sum = 0.0f;
+#pragma unroll
+    for (int w = 0; w < kP16Waves; ++w) sum += red[(w * TI + il) * 16 + q];
+    const int64_t i = i0 + il;
+    if (i < pr.I && q < rq) pr.out[pr.trans ? (int64_t)q * pr.I + i : i * rq + q] = s * sum;
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Host side: split choices (shared by workspace sizing and launches), launches.
 // ---------------------------------------------------------------------------
 namespace {
@@ -582,6 +897,12 @@ Split grad_split(int64_t M, int64_t I, int64_t maxld) {
   return {(int)cdiv(M, chunk), chunk};
 }
 
+// Adapter gradients for r <= 16 in one pass (lora_grad16_kernel) when a slab's
+// 32-bit buffer offsets reach every token of the wider operand.
+bool grad_one_pass(int64_t M, int64_t h, int64_t o, int RP16) {
+  return RP16 == 16 && M * (h > o ? h : o) * 2 < (int64_t)0x7FFF0000;
+}
+
 // K split of a rank-r product over M rows and K (a multiple of 64): about 512
 // workgroups of 64 rows, each K range a multiple of 64 wide.
 struct RankSplit {
@@ -592,11 +913,14 @@ RankSplit rank_split(int64_t M, int64_t K) {
   const int64_t rb = cdiv(M, kRankRows), kc = K / 64;
   int64_t ks = cdiv(kTargetGroups, rb);
   ks = ks < 1 ? 1 : (ks > kc ? kc : ks);
-  const int64_t per = cdiv(kc, ks);
+  // chunks per K range: a multiple of the kernel's four-chunk rounds where K allows
+  int64_t per = rup(cdiv(kc, ks), 4);
+  per = per > kc ? kc : per;
   return {(int)cdiv(kc, per), (int)(per * 64)};
 }
 
 size_t rank_partial_bytes(int64_t M, int64_t K, int RP16) {
+  if (RP16 == 16) return 0;  // one pass (lora_rank16_kernel)
   const RankSplit rs = rank_split(M, K);
   return rs.ks > 1 ? (size_t)rs.ks * M * RP16 * 4 : 0;
 }
@@ -644,7 +968,7 @@ BwdLayout bwd_layout(int64_t M, int64_t h, int64_t o, int r) {
   L.off_u = take((size_t)M * L.RP16 * 2);
   L.off_su = take((size_t)M * L.RP64 * 2);
   L.off_l1p = take((size_t)h * L.RP64 * 2);
-  L.off_g = take((size_t)L.gs.S * (h + o) * L.RP16 * 4);
+  L.off_g = take(grad_one_pass(M, h, o, L.RP16) ? 0 : (size_t)L.gs.S * (h + o) * L.RP16 * 4);
   L.off_up = take(rank_partial_bytes(M, o, L.RP16));
   L.total = off;
   return L;
@@ -654,6 +978,19 @@ template <typename T>
 T *at(void *ws, size_t off) { return reinterpret_cast<T *>(reinterpret_cast<char *>(ws) + off); }
 
 hipError_t rank_r(RankParams &rp, bool kn, int RP16, float *part, hipStream_t st) {
+  if (RP16 == 16) {
+    // 8-row workgroups while 16-row ones would number fewer than the compute units
+    if (cdiv(rp.M, 16) < 256) {
+      const unsigned grid = (unsigned)cdiv(rp.M, 8);
+      if (!kn) return launch(lora_rank16_kernel<false, true, 8>, grid, kP16Threads, st, rp);
+      return rp.r % 8 == 0 ? launch(lora_rank16_kernel<true, true, 8>, grid, kP16Threads, st, rp)
+                           : launch(lora_rank16_kernel<true, false, 8>, grid, kP16Threads, st, rp);
+    }
+    const unsigned grid = (unsigned)cdiv(rp.M, 16);
+    if (!kn) return launch(lora_rank16_kernel<false, true, 16>, grid, kP16Threads, st, rp);
+    return rp.r % 8 == 0 ? launch(lora_rank16_kernel<true, true, 16>, grid, kP16Threads, st, rp)
+                         : launch(lora_rank16_kernel<true, false, 16>, grid, kP16Threads, st, rp);
+  }
   const RankSplit rs = rank_split(rp.M, rp.K);
   rp.ks = rs.ks;
   rp.kper = rs.kper;
@@ -681,6 +1018,16 @@ hipError_t rank_r(RankParams &rp, bool kn, int RP16, float *part, hipStream_t st
 
 hipError_t lora_grad(const GradProblem &pa, const GradProblem &pb, int r, float s, int64_t M, int RP16,
                      const Split &sp, float *part, hipStream_t st) {
+  if (grad_one_pass(M, pa.I, pb.I, RP16)) {
+    // 32-wide tiles while 64-wide ones would number fewer than the compute units
+    const bool narrow = cdiv(pa.I, 64) + cdiv(pb.I, 64) < 256;
+    GradProblem a = pa, b = pb;
+    a.tiles = cdiv(a.I, narrow ? 32 : 64);
+    b.tiles = cdiv(b.I, narrow ? 32 : 64);
+    const unsigned grid = (unsigned)(a.tiles + b.tiles);
+    return narrow ? launch(lora_grad16_kernel<32>, grid, kP16Threads, st, a, b, r, s, M)
+                  : launch(lora_grad16_kernel<64>, grid, kP16Threads, st, a, b, r, s, M);
+  }
   dim3 grid((unsigned)(pa.tiles + pb.tiles), (unsigned)sp.S);
   const int64_t prows = pa.I + pb.I;
   const unsigned rgrid = (unsigned)(prows / kGradRedRows);
@@ -1023,7 +1370,7 @@ size_t linear_bwd_workspace(int64_t M, int64_t h, int64_t o, int r) { return bwd
 
 bool linear_bwd_supported(int64_t M, int64_t h, int64_t o, int r) {
   // the adapter-gradient launch has one grid row per token split
-  return r == 0 || grad_split(M, h + o, h > o ? h : o).S <= 65535;
+  return r == 0 || grad_one_pass(M, h, o, (int)rup(r, 16)) || grad_split(M, h + o, h > o ? h : o).S <= 65535;
 }
 
 int64_t linear_bwd_token_splits(int64_t M, int64_t h, int64_t o) {

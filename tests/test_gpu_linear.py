@@ -67,6 +67,8 @@ SMALL = [  # (M, h, o, r, s)
     (4100, 192, 256, 100, 0.5),   # 16 rows per workgroup, ragged, r not a multiple of 8
     (33000, 128, 192, 8, 1.0),    # rank-r products in one K range (no split partials), ragged rows
     (32769, 64, 128, 100, 0.5),   # the same with r not a multiple of 8 (element-wise L1 copies)
+    (64, 8192, 8192, 16, 2.0),    # r <= 16 adapter gradients on 64-wide tiles (256 of them)
+    (40, 8192, 8448, 5, 1.0),     # the same with r not a multiple of 8, ragged token slab
 ]
 
 

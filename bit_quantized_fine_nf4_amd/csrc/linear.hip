@@ -31,7 +31,7 @@
 //                        split over tokens; lora_grad_reduce_kernel sums the
 //                        splits in order, scales by s and stores dL1 [h][r]
 //                        and dL2 [r][o]; both run before the dX GEMM on the
-//                        caller's stream (lora_grad16_kernel: r <= 16 in one
+//                        caller's stream (lora_gradp_kernel: r <= 16 in one
 //                        pass, 32- or 64-wide tiles over every token)
 
 #include "linear.h"
@@ -738,22 +738,25 @@ __global__ __launch_bounds__(kP16Threads) void lora_rank16_kernel(RankParams p) 
   }
 }
 
-// dL1 = s·X^T·U and dL2 = s·T^T·dY for r <= 16: tiles [0, pa.tiles) are dL1's, the
-// rest dL2's, TI values of i each (pa.tiles, pb.tiles count TI-wide tiles here; TI =
-// 32 when 64-wide tiles would leave compute units idle).  With a tile count that is
-// a multiple of 8, consecutive tiles go to one XCD, whose L2 then serves the
-// neighbours' halves of each 128-byte line.  A workgroup takes every token; wave w
-// the 64-token slabs w, w + 8, ...  A slab of P (64 rows x 2 TI bytes) and of Q (64
-// rows of ldq elements, one contiguous run) go into the wave's own LDS tiles, P rows
-// padded to TI + 8 elements and Q rows to 24, and both come back through
-// transposing reads (8 consecutive tokens per lane).
-template <int TI>
-__global__ __launch_bounds__(kP16Threads) void lora_grad16_kernel(GradProblem pa, GradProblem pb, int rq, float s,
-                                                                  int64_t M) {
-  constexpr int LP = TI + 8, LQ = 24, PPR = TI / 8;  // P: 16-byte pieces per row
-  constexpr int NT = TI / 16;
+// dL1 = s·X^T·U and dL2 = s·T^T·dY in one pass (launched for r <= 16, RP = 16; the
+// kernel takes RP up to 64): tiles [0, pa.tiles) are
+// dL1's, the rest dL2's, TI values of i by RP (r rounded up to 16) each (pa.tiles,
+// pb.tiles count TI-wide tiles here; TI = 32 when 64-wide tiles would leave compute
+// units idle).  With a tile count that is a multiple of 8, consecutive tiles go to
+// one XCD, whose L2 then serves the neighbours' halves of each 128-byte line.  A
+// workgroup takes every token; wave w the 64-token slabs w, w + 8, ...  A slab of P
+// (64 rows x 2 TI bytes) and of Q (64 rows of ldq elements, one contiguous run) go
+// into the wave's own LDS tiles, P rows padded to TI + 8 elements and Q rows to
+// RP + 8, and both come back through transposing reads (8 consecutive tokens per
+// lane).  The register ring holds 4, 3 or 2 slabs as RP grows.
+template <int TI, int RP>
+__global__ __launch_bounds__(kP16Threads) void lora_gradp_kernel(GradProblem pa, GradProblem pb, int rq, float s,
+                                                                 int64_t M) {
+  constexpr int LP = TI + 8, LQ = RP + 8, PPR = TI / 8;  // P: 16-byte pieces per row
+  constexpr int QPL = RP / 8;                            // Q: 16-byte pieces per lane (at most)
+  constexpr int NT = TI / 16, NQ = RP / 16;
   constexpr int kTileElems = 64 * LP + 64 * LQ;
-  constexpr int kRedFloats = kP16Waves * TI * 16;
+  constexpr int kRedFloats = kP16Waves * TI * RP;
   constexpr int kLdsBytes = kP16Waves * kTileElems * 2 > kRedFloats * 4 ? kP16Waves * kTileElems * 2 : kRedFloats * 4;
   __shared__ __attribute__((aligned(16))) char lds[kLdsBytes];
   const int tid = threadIdx.x, lane = tid & 63;
@@ -773,19 +776,19 @@ __global__ __launch_bounds__(kP16Threads) void lora_grad16_kernel(GradProblem pa
   // rows [0, M) of P from column i0, and of Q; everything past them reads as zero
   const auto rP = gv_rsrc(pr.P + i0, M * ldp * 2 - i0 * 2);
   const auto rQ = gv_rsrc(pr.Q, M * ldq * 2);
-  int voffP[PPR], soffP[PPR];
-#pragma unroll
-  for (int u = 0; u < PPR; ++u) {
-    const int pc = lane + 64 * u, row = pc / PPR, c8 = pc % PPR;
-    voffP[u] = (int)((row * ldp + c8 * 8) * 2);
-    soffP[u] = row * LP + c8 * 8;
-  }
-  const int voffQ0 = lane < 8 * ldq ? lane * 16 : (int)0x80000000u;
-  const int voffQ1 = lane + 64 < 8 * ldq ? (lane + 64) * 16 : (int)0x80000000u;
+  // P piece u of a lane: row lane / PPR + u * 64 / PPR, 16-byte column lane % PPR;
+  // Q piece u: bytes 16 (lane + 64 u) of the slab's 128 ldq contiguous bytes (pieces
+  // past them read the next slab's rows or zero, and are not stored).  One lane
+  // offset each; the pieces differ by scalar offsets.
+  constexpr int RPU = 64 / PPR;  // P rows per piece index
+  const int voffP = (int)(((lane / PPR) * ldp + (lane % PPR) * 8) * 2);
+  const int soffP = (lane / PPR) * LP + (lane % PPR) * 8;
+  const int pstep = (int)(RPU * ldp * 2);
+  const int voffQ = lane * 16;
   uint16_t *ps = reinterpret_cast<uint16_t *>(lds) + wave * kTileElems;
   uint16_t *qs = ps + 64 * LP;
   struct Slab {
-    u32x4 p[PPR], q[2];
+    u32x4 p[PPR], q[QPL];
   };
   auto load = [&](int j, Slab &S) {
     const int sl = wave + kP16Waves * j;
@@ -793,48 +796,59 @@ __global__ __launch_bounds__(kP16Threads) void lora_grad16_kernel(GradProblem pa
     const int sp = __builtin_amdgcn_readfirstlane(live ? (int)(sl * 64 * ldp * 2) : kP16PastEnd);
     const int sq = __builtin_amdgcn_readfirstlane(live ? (int)(sl * 128 * ldq) : kP16PastEnd);
 #pragma unroll
-    for (int u = 0; u < PPR; ++u) S.p[u] = __builtin_amdgcn_raw_buffer_load_b128(rP, voffP[u], sp, 0);
-    S.q[0] = __builtin_amdgcn_raw_buffer_load_b128(rQ, voffQ0, sq, 0);
-    S.q[1] = __builtin_amdgcn_raw_buffer_load_b128(rQ, voffQ1, sq, 0);
+    for (int u = 0; u < PPR; ++u)
+      S.p[u] = __builtin_amdgcn_raw_buffer_load_b128(rP, voffP, live ? (int)((unsigned)sp + (unsigned)(u * pstep))
+                                                                     : kP16PastEnd, 0);
+#pragma unroll
+    for (int u = 0; u < QPL; ++u)
+      S.q[u] = __builtin_amdgcn_raw_buffer_load_b128(rQ, voffQ, live ? sq + 1024 * u : kP16PastEnd, 0);
   };
-  // Q columns past ldq keep stale values; they only reach output columns q >= rq
-  auto put = [&](const Slab &S) {
+  // Q columns past ldq keep stale values; they only reach output columns q >= rq.
+  // With ldq not a multiple of 8 (T of a rank that is not), the slab's Q is copied
+  // element by element straight from memory instead (its loads not prefetched).
+  auto put = [&](int j, const Slab &S) {
 #pragma unroll
-    for (int u = 0; u < PPR; ++u) *reinterpret_cast<u32x4 *>(ps + soffP[u]) = S.p[u];
+    for (int u = 0; u < PPR; ++u) *reinterpret_cast<u32x4 *>(ps + soffP + u * RPU * LP) = S.p[u];
+    if (qvec) {
+      const int pq = (int)(ldq >> 3);
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int pc = lane + 64 * h;
-      if (pc >= 8 * ldq) continue;
-      if (qvec) {
-        const int pq = (int)(ldq >> 3);
-        *reinterpret_cast<u32x4 *>(qs + (pc / pq) * LQ + (pc % pq) * 8) = S.q[h];
-      } else {
-        const int lq = (int)ldq;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int idx = 8 * pc + e;
-          qs[(idx / lq) * LQ + idx % lq] = (uint16_t)(S.q[h][e >> 1] >> (16 * (e & 1)));
-        }
+      for (int u = 0; u < QPL; ++u) {
+        const int pc = lane + 64 * u;
+        if (pc < 8 * ldq) *reinterpret_cast<u32x4 *>(qs + (pc / pq) * LQ + (pc % pq) * 8) = S.q[u];
       }
+    } else {
+      const int lq = (int)ldq;
+      const int sl = wave + kP16Waves * j;
+      const int sq = __builtin_amdgcn_readfirstlane(j < nj ? (int)(sl * 128 * ldq) : kP16PastEnd);
+      for (int idx = lane; idx < 64 * lq; idx += 64)
+        qs[(idx / lq) * LQ + idx % lq] = (uint16_t)__builtin_amdgcn_raw_buffer_load_b16(rQ, idx * 2, sq, 0);
     }
   };
   const int trow = c16 >> 2, tcol = (c16 & 3) * 4;
-  f32x4 acc[NT];
+  f32x4 acc[NT][NQ];
 #pragma unroll
-  for (int a = 0; a < NT; ++a) acc[a] = f32x4{0, 0, 0, 0};
+  for (int a = 0; a < NT; ++a)
+#pragma unroll
+    for (int t = 0; t < NQ; ++t) acc[a][t] = f32x4{0, 0, 0, 0};
   auto compute = [&]() {
 #pragma unroll
     for (int sub = 0; sub < 2; ++sub) {
-      const uint16_t *lq = qs + (32 * sub + 8 * g + trow) * LQ + tcol;
-      const u32x4 bq = tr_pair(lq, lq + 4 * LQ);
+      u32x4 bq[NQ];
+#pragma unroll
+      for (int t = 0; t < NQ; ++t) {
+        const uint16_t *lq = qs + (32 * sub + 8 * g + trow) * LQ + 16 * t + tcol;
+        bq[t] = tr_pair(lq, lq + 4 * LQ);
+      }
 #pragma unroll
       for (int a = 0; a < NT; ++a) {
         const uint16_t *lp = ps + (32 * sub + 8 * g + trow) * LP + 16 * a + tcol;
-        acc[a] = mfma16(tr_pair(lp, lp + 4 * LP), bq, acc[a]);
+        const u32x4 af = tr_pair(lp, lp + 4 * LP);
+#pragma unroll
+        for (int t = 0; t < NQ; ++t) acc[a][t] = mfma16(af, bq[t], acc[a][t]);
       }
     }
   };
-  constexpr int kDepth = 3, kRing = kDepth + 1;
+  constexpr int kRing = RP <= 16 ? 4 : (RP <= 32 ? 3 : 2), kDepth = kRing - 1;
   Slab S[kRing];
 #pragma unroll
   for (int j = 0; j < kDepth; ++j) load(j, S[j]);
@@ -842,28 +856,31 @@ __global__ __launch_bounds__(kP16Threads) void lora_grad16_kernel(GradProblem pa
 #pragma unroll
     for (int u = 0; u < kRing; ++u) {
       load(j0 + u + kDepth, S[(u + kDepth) % kRing]);
-      put(S[u]);
+      put(j0 + u, S[u]);
       compute();
     }
   }
 
-  // D layout: lane (q = c16, g) holds rows i = 16a + 4g + v; the sums of the eight
-  // waves are added in wave order
+  // D layout: lane (q = 16t + c16, g) holds rows i = 16a + 4g + v; the sums of the
+  // eight waves are added in wave order
   __syncthreads();  // every wave is done with its tiles, which the sums overwrite
   float *red = reinterpret_cast<float *>(lds);
 #pragma unroll
   for (int a = 0; a < NT; ++a)
 #pragma unroll
-    for (int v = 0; v < 4; ++v) red[(wave * TI + 16 * a + 4 * g + v) * 16 + c16] = acc[a][v];
+    for (int t = 0; t < NQ; ++t)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) red[(wave * TI + 16 * a + 4 * g + v) * RP + 16 * t + c16] = acc[a][t][v];
   __syncthreads();
-  for (int idx = tid; idx < TI * 16; idx += kP16Threads) {
+  for (int idx = tid; idx < TI * RP; idx += kP16Threads) {
     // dL2 ([r][I]) stores run along i, dL1 ([I][r]) stores along q
-    const int il = pr.trans ? idx % TI : idx / 16, q = pr.trans ? idx / TI : idx % 16;
+    const int il = pr.trans ? idx % TI : idx / RP, q = pr.trans ? idx / TI : idx % RP;
+    if (q >= rq) continue;
     float sum = 0.0f;
 #pragma unroll
-    for (int w = 0; w < kP16Waves; ++w) sum += red[(w * TI + il) * 16 + q];
+    for (int w = 0; w < kP16Waves; ++w) sum += red[(w * TI + il) * RP + q];
     const int64_t i = i0 + il;
-    if (i < pr.I && q < rq) pr.out[pr.trans ? (int64_t)q * pr.I + i : i * rq + q] = s * sum;
+    if (i < pr.I) pr.out[pr.trans ? (int64_t)q * pr.I + i : i * rq + q] = s * sum;
   }
 }
 
@@ -897,8 +914,11 @@ Split grad_split(int64_t M, int64_t I, int64_t maxld) {
   return {(int)cdiv(M, chunk), chunk};
 }
 
-// Adapter gradients for r <= 16 in one pass (lora_grad16_kernel) when a slab's
-// 32-bit buffer offsets reach every token of the wider operand.
+// Adapter gradients for r <= 16 in one pass (lora_gradp_kernel) when a slab's 32-bit
+// buffer offsets reach every token of the wider operand.  (At r = 64 the one-pass
+// kernel measured slower than the split one on the 65B projections, 34 against 25
+// us and 63 against 40 us: every workgroup streams the whole 256 KB token-major U or
+// T from L2, and its 144 KB of LDS leaves one workgroup per compute unit.)
 bool grad_one_pass(int64_t M, int64_t h, int64_t o, int RP16) {
   return RP16 == 16 && M * (h > o ? h : o) * 2 < (int64_t)0x7FFF0000;
 }
@@ -1025,8 +1045,8 @@ hipError_t lora_grad(const GradProblem &pa, const GradProblem &pb, int r, float 
     a.tiles = cdiv(a.I, narrow ? 32 : 64);
     b.tiles = cdiv(b.I, narrow ? 32 : 64);
     const unsigned grid = (unsigned)(a.tiles + b.tiles);
-    return narrow ? launch(lora_grad16_kernel<32>, grid, kP16Threads, st, a, b, r, s, M)
-                  : launch(lora_grad16_kernel<64>, grid, kP16Threads, st, a, b, r, s, M);
+    return narrow ? launch(lora_gradp_kernel<32, 16>, grid, kP16Threads, st, a, b, r, s, M)
+                  : launch(lora_gradp_kernel<64, 16>, grid, kP16Threads, st, a, b, r, s, M);
   }
   dim3 grid((unsigned)(pa.tiles + pb.tiles), (unsigned)sp.S);
   const int64_t prows = pa.I + pb.I;

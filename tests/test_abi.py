@@ -225,17 +225,25 @@ def test_linear_bwd_token_split_bound():
     (chunk rows of max(h, o) bf16 values) stays below 2^31 bytes.  Observable on the host:
     the workspace holds one float32 partial tile per split, so its size grows with the
     number of splits once M passes the cap; a shape needing more than 65535 splits is
-    rejected before anything is launched."""
-    h, o, r = 22016, 8192, 64
+    rejected before anything is launched.  (r = 100 here: ranks up to 16 take the
+    one-pass kernel while every token's slab fits 32-bit offsets; checked below.)"""
+    h, o, r = 22016, 8192, 100
+    rp16, rp64 = 112, 128
     cap = (0x7FFFFFF0 // (2 * h)) // 64 * 64          # 48768 tokens per split
-    ws = lambda M: nf4.workspace_size(nf4.QLORA_OP_LINEAR_BWD, M, h, o, r)
-    part = (h + o) * 64 * 4        # one split's float32 partial tiles (r = 64)
-    per_token = (64 + 64) * 2      # U and s*U, bf16, r padded to 16 and to 64
+    ws = lambda M, r=r: nf4.workspace_size(nf4.QLORA_OP_LINEAR_BWD, M, h, o, r)
+    part = (h + o) * rp16 * 4      # one split's float32 partial tiles
+    per_token = (rp16 + rp64) * 2  # U and s*U, bf16, r padded to 16 and to 64
     for M in (cap, 5 * cap + 1, 40 * cap, 100 * cap):
         # without the cap about 3 splits would do (512 workgroups over 236 tiles)
         splits = -(-M // cap)
         assert ws(M) >= M * per_token + splits * part, M
     assert ws(cap) < cap * per_token + 4 * part
+    # r = 16: no partial tiles while M rows of the wider operand stay below 2^31 bytes
+    # (one pass over every token), split partials past that
+    one = (0x7FFF0000 - 1) // (2 * h)
+    fixed = h * 64 * 2                                # L1 padded to 64 columns
+    assert ws(one, 16) < one * (16 + 64) * 2 + fixed + 4096
+    assert ws(one + 1, 16) >= (one + 1) * (16 + 64) * 2 + (h + o) * 16 * 4
     big = weight(h=1 << 20, o=64)
     M = 1 << 31                                         # 1024-token chunks -> 2^21 splits: unsupported
     st = lib.qlora_linear_bwd(ctypes.byref(big), FAKE, FAKE, FAKE, M, FAKE, FAKE, 8, 1.0, FAKE, FAKE, FAKE, FAKE,

@@ -69,6 +69,10 @@ SMALL = [  # (M, h, o, r, s)
     (32769, 64, 128, 100, 0.5),   # the same with r not a multiple of 8 (element-wise L1 copies)
     (64, 8192, 8192, 16, 2.0),    # r <= 16 adapter gradients on 64-wide tiles (256 of them)
     (40, 8192, 8448, 5, 1.0),     # the same with r not a multiple of 8, ragged token slab
+    (200, 512, 768, 40, 1.0),     # split adapter gradients and rank products with 48 rank columns
+    (150, 640, 384, 27, 0.5),     # 32 rank columns, r not a multiple of 8
+    (96, 8192, 8192, 64, 0.25),   # 64 rank columns, 256 gradient tiles
+    (130, 512, 384, 13, 1.0),     # one pass, r not a multiple of 8: element-wise Q copies
 ]
 
 

@@ -586,9 +586,20 @@ __global__ __launch_bounds__(256) void dq_chunks_kernel(const float *__restrict_
   __syncthreads();
   constexpr int kLanesPerLimb = 256 / kLimbs;  // 21
   if (tid < kLanesPerLimb * kLimbs) {
+    // the slots were written by other workgroups (other L2s): eight loads in flight
+    // per step rather than one dependent load per slot
     const int j = tid % kLimbs;
     unsigned long long t = 0;
-    for (int p = tid / kLimbs; p < nparts; p += kLanesPerLimb) t += partial[(int64_t)p * kLimbs + j];
+    for (int p = tid / kLimbs; p < nparts; p += 8 * kLanesPerLimb) {
+      unsigned long long v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int pu = p + u * kLanesPerLimb;
+        v[u] = pu < nparts ? partial[(int64_t)pu * kLimbs + j] : 0ull;
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) t += v[u];
+    }
     if (t) atomicAdd(&csum[j], t);
   }
   __syncthreads();

@@ -79,10 +79,7 @@ QL_DEV void wbarrier() {
 // owns output columns [32 TN w, 32 TN (w + 1)): TN tiles of 32 columns.
 constexpr int kBM = 256, kBK = 64, kThreads = 256;
 constexpr int kTM = 8;                // 32x32 MFMA tiles per wave along M
-constexpr int kStages = 4;            // A ring depth
 constexpr int kStageElems = kBM * kBK;  // 256 rows x 64 k (bf16)
-constexpr int kLutCopies = 16;        // lane l reads copy l % 16 of the pair table
-constexpr int kLutBytes = 256 * 8 * kLutCopies;
 constexpr int wmax(int a, int b) { return a > b ? a : b; }
 
 // row r of an A stage keeps its 8 chunks of 16 bytes in the order c ^ swz(r)
@@ -93,21 +90,33 @@ QL_DEV int a_swz(int r) { return (r >> 1) & 7; }
 template <int TN>
 __global__ __launch_bounds__(kThreads) void nf4_gemm_wide_fwd_kernel(GemmParams p) {
   constexpr int kTN = TN, kBN = 128 * TN, kWC = 32 * TN;
+  // 256-wide tiles: a 3-stage A ring and a 64 KB pair table of 32 copies at a 256-byte
+  // entry stride, so a lookup's address is one v_perm_b32 and every lane of a 32-lane
+  // phase reads its own banks (41 fewer VALU instructions per step: the 65B block step
+  // 7.81 -> 7.68 ms); 128-wide tiles keep a 4-stage ring and 16 copies at 128 bytes
+  // (the 3-stage form measured 2 % slower there)
+  constexpr bool kPermLut = TN == 2;
+  constexpr int kStages = kPermLut ? 3 : 4;
+  constexpr int kLutCopies = kPermLut ? 32 : 16;  // lane l reads copy l % kLutCopies
+  constexpr int kLutStride = 8 * kLutCopies;       // bytes per table entry (level pair)
+  constexpr int kLutBytes = 256 * kLutStride;
   constexpr int kLdc = kBN + 8;    // epilogue staging row stride (elements)
   constexpr int kLdkn = kBN + 32;  // LoRA B2 tile [64 k][kLdkn] (transposing reads)
   constexpr int kLdsBytes = wmax(kLutBytes + kStages * kStageElems * 2, kBM * kLdc * 2);
   __shared__ __attribute__((aligned(16))) char lds[kLdsBytes];
-  // the A ring first, so the fragment reads of all four buffers reach their
-  // addresses from two base registers (16-bit offsets); the table after it
-  char *const tab = lds + kStages * kStageElems * 2;
-  uint16_t *ring = reinterpret_cast<uint16_t *>(lds);
+  // kPermLut: the pair table at offset 0, so a lookup's address is one byte
+  // permutation (the code byte above the lane's copy offset), the A ring after it;
+  // otherwise the A ring first, so the fragment reads of all four buffers reach their
+  // addresses from two base registers (16-bit offsets), the table after it
+  char *const tab = kPermLut ? lds : lds + kStages * kStageElems * 2;
+  uint16_t *ring = reinterpret_cast<uint16_t *>(kPermLut ? lds + kLutBytes : lds);
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 5, l32 = lane & 31;
 
   for (int i = tid; i < 256 * kLutCopies; i += kThreads) {
-    const int e = i / kLutCopies;
+    const int e = i / kLutCopies;  // word i at 8 i = entry e's stride + 8 x copy
     reinterpret_cast<f32x2 *>(tab)[i] = f32x2{p.level[e >> 4], p.level[e & 15]};
   }
 
@@ -169,6 +178,8 @@ __global__ __launch_bounds__(kThreads) void nf4_gemm_wide_fwd_kernel(GemmParams 
                                               rS2, (int)(((blk0[j] + kt) >> 8) * 4), 0, 0));
     }
   };
+  // kPermLut: lane l reads copy l % 32, so a 32-lane phase of 8-byte reads covers the
+  // 64 banks once whatever the code bytes
   const int lcopy8 = (lane % kLutCopies) * 8;
   // Decode of one part (4 code bytes of each of the lane's two rows = MFMA group
   // `part`) in two halves so the table reads can run ahead of their use:
@@ -181,8 +192,13 @@ __global__ __launch_bounds__(kThreads) void nf4_gemm_wide_fwd_kernel(GemmParams 
       const uint32_t w = R.c[j][part];
 #pragma unroll
       for (int b = 0; b < 4; ++b) {
-        const uint32_t byte = (w >> (8 * b)) & 0xFFu;
-        lv[j][b] = *reinterpret_cast<const f32x2 *>(tab + (byte << 7) + lcopy8);
+        if constexpr (kPermLut) {  // (byte b of w) << 8 | lcopy8
+          const uint32_t addr = __builtin_amdgcn_perm(w, (uint32_t)lcopy8, 0x0C0C0000u | ((4u + b) << 8));
+          lv[j][b] = *reinterpret_cast<const f32x2 *>(tab + addr);
+        } else {
+          const uint32_t byte = (w >> (8 * b)) & 0xFFu;
+          lv[j][b] = *reinterpret_cast<const f32x2 *>(tab + (byte << 7) + lcopy8);
+        }
       }
     }
   };
@@ -240,8 +256,10 @@ __global__ __launch_bounds__(kThreads) void nf4_gemm_wide_fwd_kernel(GemmParams 
   dma_a(1, 1);
   load_b(1, R1);
   __builtin_amdgcn_sched_barrier(0);
-  dma_a(2, 2);
-  __builtin_amdgcn_sched_barrier(0);
+  if constexpr (kStages == 4) {
+    dma_a(2, 2);
+    __builtin_amdgcn_sched_barrier(0);
+  }
   {
     float ah[kTN];
     scale_of(R0, ah);
@@ -252,9 +270,9 @@ __global__ __launch_bounds__(kThreads) void nf4_gemm_wide_fwd_kernel(GemmParams 
       lut_use(lv, ah, part, bcur);
     }
   }
-  // step 0's B loads and so stage 0 are done once the 16 + 3 TN younger operations
-  // (stage 1, step 1's B loads, stage 2) are all that may be outstanding
-  wait_vm(std::integral_constant<int, 16 + 3 * TN>{});
+  // step 0's B loads and so stage 0 are done once the younger operations (stage 1,
+  // step 1's B loads and, with four stages, stage 2) are all that may be outstanding
+  wait_vm(std::integral_constant<int, 8 * (kStages - 2) + 3 * TN>{});
   wbarrier();
   read_a(0, 0, af[0]);
   Lv lv[2];
@@ -262,8 +280,8 @@ __global__ __launch_bounds__(kThreads) void nf4_gemm_wide_fwd_kernel(GemmParams 
   lut_read(R1, 0, lv[0]);
   scale_of(R1, ahn);
 
-  // Step kt (ring buffer BUF = kt % 4, compile-time: the loop is unrolled four
-  // times; the two B register sets alternate).  On entry af[0] holds group 0's A
+  // Step kt (ring buffer BUF = kt % kStages, compile-time: the loop is unrolled six
+  // (three stages) or four times; the two B register sets alternate).  On entry af[0] holds group 0's A
   // fragments of step kt, bcur its decoded B, lv[0] and ahn the first table reads
   // and scales of step kt + 1's decode.  Issued between group 0's MFMAs: the B
   // loads of step kt + 2 (into the set step kt's own B came from).  The decode of
@@ -271,10 +289,10 @@ __global__ __launch_bounds__(kThreads) void nf4_gemm_wide_fwd_kernel(GemmParams 
   // fragments of group kk + 1 and the table reads of part kk + 1 are in flight and
   // part kk's levels are scaled and converted.  After group 2's MFMAs this wave's
   // copy of stage kt + 1 is awaited, one barrier makes every wave's copy visible
-  // and frees buffer (kt + 3) % 4 (last read in step kt - 1), and group 3 issues
-  // the copy of stage kt + 3 into it between its MFMAs, which also cover the reads
-  // of step kt + 1's group-0 fragments and of the first part of step kt + 2's
-  // decode.  Loads past the last step read harmless data that is never used.
+  // and frees buffer (kt - 1) % kStages (last read in step kt - 1), and group 3
+  // issues the copy of stage kt + kStages - 1 into it between its MFMAs, which also
+  // cover the reads of step kt + 1's group-0 fragments and of the first part of step
+  // kt + 2's decode.  Loads past the last step read harmless data that is never used.
   auto step = [&](auto bufc, int kt, BRegs &Rnext, BRegs &Rfree) {
     constexpr int BUF = decltype(bufc)::value;
     float ah[kTN];
@@ -288,7 +306,7 @@ __global__ __launch_bounds__(kThreads) void nf4_gemm_wide_fwd_kernel(GemmParams 
         read_a(BUF, kk + 1, af[(kk + 1) & 1]);
         lut_read(Rnext, kk + 1, lv[(kk + 1) & 1]);
       } else {
-        dma_a(kt + 3, (BUF + 3) % kStages);
+        dma_a(kt + kStages - 1, (BUF + kStages - 1) % kStages);
         read_a((BUF + 1) % kStages, 0, af[0]);
         lut_read(Rfree, 0, lv[0]);
         scale_of(Rfree, ahn);
@@ -303,7 +321,7 @@ __global__ __launch_bounds__(kThreads) void nf4_gemm_wide_fwd_kernel(GemmParams 
 #pragma unroll
       for (int i = 0; i < 8 * TN; ++i) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);           // MFMA
-        // the step's B loads ride on group 0, the copy of stage kt + 3 on group 3: issued
+        // the step's B loads ride on group 0, the copy of the next stage on group 3: issued
         // back to back by all four waves they queue at the compute unit's address unit
         // and stall the issuing wave, and the matrix core with it
         if ((kk == 0 && i < 3 * TN) || (kk == 3 && i < 8)) __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);  // VMEM
@@ -312,9 +330,10 @@ __global__ __launch_bounds__(kThreads) void nf4_gemm_wide_fwd_kernel(GemmParams 
       }
       __builtin_amdgcn_sched_barrier(0);
       if (kk == 2) {
-        // younger than this wave's copy of stage kt + 1: the B loads of step kt + 1,
-        // the copy of stage kt + 2, the B loads of step kt + 2 (3 TN + 8 + 3 TN)
-        wait_vm(std::integral_constant<int, 8 + 6 * TN>{});
+        // younger than this wave's copy of stage kt + 1: with three stages (issued in
+        // step kt - 1's last group) the B loads of step kt + 2 (3 TN); with four the B
+        // loads of step kt + 1, the copy of stage kt + 2 and the B loads of step kt + 2
+        wait_vm(std::integral_constant<int, kStages == 3 ? 3 * TN : 8 + 6 * TN>{});
         wbarrier();
         __builtin_amdgcn_sched_barrier(0);
       }
@@ -327,17 +346,33 @@ __global__ __launch_bounds__(kThreads) void nf4_gemm_wide_fwd_kernel(GemmParams 
   using I0 = std::integral_constant<int, 0>;
   using I1 = std::integral_constant<int, 1>;
   using I2 = std::integral_constant<int, 2>;
-  using I3 = std::integral_constant<int, 3>;
   int kt = 0;
-  for (; kt + 3 < nk; kt += 4) {
-    step(I0{}, kt, R1, R0);
-    step(I1{}, kt + 1, R0, R1);
-    step(I2{}, kt + 2, R1, R0);
-    step(I3{}, kt + 3, R0, R1);
+  if constexpr (kStages == 3) {
+    for (; kt + 5 < nk; kt += 6) {
+      step(I0{}, kt, R1, R0);
+      step(I1{}, kt + 1, R0, R1);
+      step(I2{}, kt + 2, R1, R0);
+      step(I0{}, kt + 3, R0, R1);
+      step(I1{}, kt + 4, R1, R0);
+      step(I2{}, kt + 5, R0, R1);
+    }
+    if (kt < nk) step(I0{}, kt, R1, R0);
+    if (kt + 1 < nk) step(I1{}, kt + 1, R0, R1);
+    if (kt + 2 < nk) step(I2{}, kt + 2, R1, R0);
+    if (kt + 3 < nk) step(I0{}, kt + 3, R0, R1);
+    if (kt + 4 < nk) step(I1{}, kt + 4, R1, R0);
+  } else {
+    using I3 = std::integral_constant<int, 3>;
+    for (; kt + 3 < nk; kt += 4) {
+      step(I0{}, kt, R1, R0);
+      step(I1{}, kt + 1, R0, R1);
+      step(I2{}, kt + 2, R1, R0);
+      step(I3{}, kt + 3, R0, R1);
+    }
+    if (kt < nk) step(I0{}, kt, R1, R0);
+    if (kt + 1 < nk) step(I1{}, kt + 1, R0, R1);
+    if (kt + 2 < nk) step(I2{}, kt + 2, R1, R0);
   }
-  if (kt < nk) step(I0{}, kt, R1, R0);
-  if (kt + 1 < nk) step(I1{}, kt + 1, R0, R1);
-  if (kt + 2 < nk) step(I2{}, kt + 2, R1, R0);
   __builtin_amdgcn_s_waitcnt(0);  // no copy of a stage past the end may still land in LDS
   __syncthreads();
 

@@ -448,7 +448,7 @@ __global__ __launch_bounds__(kThreads) void nf4_gemm_wide_fwd_kernel(GemmParams 
 // stored codes run along N, so a wave's B fragment (8 consecutive k of one
 // column) is a transpose of the stored rows:
 //  - each K step's 64 code rows x 256 columns (8 KB) go to LDS by direct-to-LDS
-//    loads, 16-byte chunks at chunk ^ ((row >> 1) & 7), in a 5-stage ring;
+//    loads, 16-byte chunks at chunk ^ ((row >> 1) & 7), in a 3-stage ring;
 //  - one 4-bit transposing read (ds_read_b64_tr_b4) gives lane i of a 16-lane
 //    group the nibbles of 16 consecutive rows of one column.  It returns a
 //    byte's low nibble first, and a stored byte keeps the even column in its
@@ -461,22 +461,25 @@ __global__ __launch_bounds__(kThreads) void nf4_gemm_wide_fwd_kernel(GemmParams 
 //    block), then one packed conversion gives the MFMA dword;
 //  - the 256 a_hat values of a stage (64 rows x the tile's 4 blocks) are
 //    rebuilt by the 256 threads, one each, two steps ahead, and published in a
-//    4-stage LDS ring; a lane reads its 8 values per MFMA group as two
+//    3-stage LDS ring; a lane reads its 8 values per MFMA group as two
 //    broadcast 16-byte reads.
-// A (dY) takes the forward's path through a 3-stage ring.  One barrier per K
+// A (dY) takes the forward's path through a 3-stage ring.  With all three rings
+// three stages deep, the K loop unrolled three times finds every slot at a
+// compile-time offset, and the LDS left over holds 16 copies of the pair table.  One barrier per K
 // step after the third MFMA group, as in the forward; the last group's MFMAs
 // cover the next step's first A fragments and the first part of the decode
 // after next.
 // ---------------------------------------------------------------------------
 namespace {
-constexpr int kXStagesA = 3;                  // A (dY) ring
-constexpr int kXStagesC = 5;                  // code ring
-constexpr int kXStagesS = 4;                  // a_hat ring
+constexpr int kXStages = 3;                   // A (dY), code and a_hat rings alike
+constexpr int kXStagesA = kXStages;
+constexpr int kXStagesC = kXStages;
+constexpr int kXStagesS = kXStages;
 constexpr int kXBN = 256, kXTN = 2;           // 256-wide tiles: two 32-column MFMA tiles per wave
 constexpr int kXLdc = kXBN + 8;               // epilogue staging row stride (elements)
 constexpr int kXCodeBytes = 64 * (kXBN / 2);  // 64 code rows x 256 columns
 constexpr int kXAhFloats = 4 * 64;            // [4 blocks][64 rows]
-constexpr int kXLutCopies = 8;                // lane l reads copy l % 8 of the pair table
+constexpr int kXLutCopies = 16;               // lane l reads copy l % 16 of the pair table
 constexpr int kXOffC = kXStagesA * kStageElems * 2;
 constexpr int kXOffS = kXOffC + kXStagesC * kXCodeBytes;
 constexpr int kXOffLut = kXOffS + kXStagesS * kXAhFloats * 4;
@@ -500,7 +503,7 @@ __global__ __launch_bounds__(kThreads) void nf4_gemm_wide_dx_kernel(GemmParams p
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 5, l32 = lane & 31, i16 = lane & 15, half = (lane >> 4) & 1;
 
-  // entry e of copy c (at 64 e + 8 c): (level[low nibble], level[high nibble]), the
+  // entry e of copy c (at 128 e + 8 c): (level[low nibble], level[high nibble]), the
   // levels of a byte's earlier and later row
   for (int i = tid; i < 256 * kXLutCopies; i += kThreads) {
     const int e = i / kXLutCopies;
@@ -598,7 +601,7 @@ __global__ __launch_bounds__(kThreads) void nf4_gemm_wide_dx_kernel(GemmParams p
 #pragma unroll
       for (int d = 0; d < 4; ++d) {
         const uint32_t byte = (w >> (8 * d)) & 0xFFu;
-        lv[j][d] = *reinterpret_cast<const f32x2 *>(tab + (byte << 6) + lcopy8);
+        lv[j][d] = *reinterpret_cast<const f32x2 *>(tab + byte * (8 * kXLutCopies) + lcopy8);
       }
     }
   };
@@ -633,34 +636,35 @@ __global__ __launch_bounds__(kThreads) void nf4_gemm_wide_dx_kernel(GemmParams p
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
 
   const int nk = p.ksteps;
-  QS Q0, Q1;
+  // stage s lives in slot s % 3 of every ring, and its int8 / second-level scales in
+  // register set Qs[s % 3] until they are published
+  QS Qs[kXStages];
   u32x4 bcur[kTN][4], bnext[kTN][4];
   u32x4 af[2][kTM];
   XLv lv[2];
   f32x4 sc[2][2];
   u32x2 tw0[kTN], tw1[kTN];
   __syncthreads();  // pair table ready
-  // Prologue: codes of stages 0-3, A of stage 0, scales of stages 0 and 1; then, in
-  // the order a step issues them, the scales of stage 2, the codes of stage 4, A of
-  // stage 1 and the scales of stage 3.
+  // Prologue: codes of stages 0-2, A of stages 0 and 1, the a_hat values of stages 0
+  // and 1 published, the scales of stages 2 and 3 loaded; then stage 0 decoded, the
+  // first reads of step 0 and of stage 1's decode, and, once every wave has read
+  // stage 0's codes, the codes of stage 3 into their slot.
 #pragma unroll
-  for (int s = 0; s < 4; ++s) dma_c(s, s);
+  for (int s = 0; s < 3; ++s) dma_c(s, s);
   dma_a(0, 0);
-  load_qs(0, Q0);
-  load_qs(1, Q1);
+  load_qs(0, Qs[0]);
+  load_qs(1, Qs[1]);
   __builtin_amdgcn_s_waitcnt(0);
-  put_ah(Q0, 0);
-  put_ah(Q1, 1);
+  put_ah(Qs[0], 0);
+  put_ah(Qs[1], 1);
   __builtin_amdgcn_sched_barrier(0);
-  load_qs(2, Q0);
-  __builtin_amdgcn_sched_barrier(0);
-  dma_c(4, 4);
+  load_qs(2, Qs[2]);
   __builtin_amdgcn_sched_barrier(0);
   dma_a(1, 1);
   __builtin_amdgcn_sched_barrier(0);
-  load_qs(3, Q1);
+  load_qs(3, Qs[0]);
   __builtin_amdgcn_sched_barrier(0);
-  __syncthreads();  // stage 0's A and codes, stages 0-3's codes, a_hat of stages 0 and 1
+  __syncthreads();  // stage 0's A, stages 0-2's codes, a_hat of stages 0 and 1
   {
     read_tr(0, 0, tw0);
     read_tr(0, 1, tw1);
@@ -677,45 +681,50 @@ __global__ __launch_bounds__(kThreads) void nf4_gemm_wide_dx_kernel(GemmParams p
   read_tr(1, 0, tw0);
   lut_read(tw0, 0, lv[0]);
   sc_read(1, 0, sc[0]);
+  __syncthreads();  // every wave's reads of code slot 0 are done
+  dma_c(3, 0);
 
-  // Step kt: A from ring buffer kt % 3, B from bcur; decodes stage kt + 1 into
-  // bnext (its part 0 read during step kt - 1).  On entry af[0] holds group 0's A
-  // fragments, tw0 the first transposing reads of stage kt + 1, lv[0] / sc[0] its
-  // part-0 table entries and scales.  At its start the a_hat values of stage
-  // kt + 2 are published.  After group 2: all of this wave's vector-memory
-  // operations (A stage kt + 1, code stage kt + 4, the scales of stage kt + 3) and
-  // its a_hat stores are awaited, one barrier publishes every wave's copies and
-  // a_hat values and frees A buffer (kt + 2) % 3 and code buffer kt % 5; group 3
-  // then issues the copies of code stage kt + 5 and A stage kt + 2 and the scale
-  // loads of stage kt + 4 between its MFMAs.
-  auto step = [&](int kt, QS &Qcur) {
-    const int bA = kt % kXStagesA, bC1 = (kt + 1) % kXStagesC, bC2 = (kt + 2) % kXStagesC;
-    const int bS1 = (kt + 1) % kXStagesS, bS2 = (kt + 2) % kXStagesS;
-    put_ah(Qcur, bS2);
+  // Step kt (BUF = kt % 3, compile-time: the loop is unrolled three times): A from
+  // slot BUF, B from bcur; decodes stage kt + 1 into bnext (its part 0 read during
+  // step kt - 1).  On entry af[0] holds group 0's A fragments, tw0 the first
+  // transposing reads of stage kt + 1, lv[0] / sc[0] its part-0 table entries and
+  // scales.  At its start the a_hat values of stage kt + 2 are published (slot
+  // (kt + 2) % 3, last read during step kt - 2).  After group 2: all of this wave's
+  // vector-memory operations (A stage kt + 1, code stage kt + 3, the scales of stage
+  // kt + 3) and its a_hat stores are awaited, and one barrier publishes every wave's
+  // copies and a_hat values and frees A slot (kt + 2) % 3 (last read in step kt - 1)
+  // and code slot (kt + 1) % 3 (stage kt + 1, last read in group 0); group 3 then
+  // issues the copies of code stage kt + 4 and A stage kt + 2 and the scale loads of
+  // stage kt + 4 between its MFMAs.  Copies and loads past the last stage read
+  // harmless data (zero past the buffers' ends) that is never used.
+  auto step = [&](auto bufc, int kt) {
+    constexpr int BUF = decltype(bufc)::value;
+    constexpr int B1 = (BUF + 1) % kXStages, B2 = (BUF + 2) % kXStages;
+    put_ah(Qs[B2], B2);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
       if (kk == 0) {
-        read_a(bA, 1, af[1]);
-        read_tr(bC1, 1, tw1);
+        read_a(BUF, 1, af[1]);
+        read_tr(B1, 1, tw1);
         lut_read(tw0, 1, lv[1]);
-        sc_read(bS1, 1, sc[1]);
+        sc_read(B1, 1, sc[1]);
       } else if (kk == 1) {
-        read_a(bA, 2, af[0]);
+        read_a(BUF, 2, af[0]);
         lut_read(tw1, 2, lv[0]);
-        sc_read(bS1, 2, sc[0]);
+        sc_read(B1, 2, sc[0]);
       } else if (kk == 2) {
-        read_a(bA, 3, af[1]);
+        read_a(BUF, 3, af[1]);
         lut_read(tw1, 3, lv[1]);
-        sc_read(bS1, 3, sc[1]);
-        read_tr(bC2, 0, tw0);
+        sc_read(B1, 3, sc[1]);
+        read_tr(B2, 0, tw0);
       } else {
-        dma_c(kt + 5, kt % kXStagesC);
-        dma_a(kt + 2, (kt + 2) % kXStagesA);
-        load_qs(kt + 4, Qcur);
-        read_a((kt + 1) % kXStagesA, 0, af[0]);
+        dma_c(kt + 4, B1);
+        dma_a(kt + 2, B2);
+        load_qs(kt + 4, Qs[B1]);
+        read_a(B1, 0, af[0]);
         lut_read(tw0, 0, lv[0]);
-        sc_read(bS2, 0, sc[0]);
+        sc_read(B2, 0, sc[0]);
       }
 #pragma unroll
       for (int i = 0; i < kTM; ++i)
@@ -737,7 +746,7 @@ __global__ __launch_bounds__(kThreads) void nf4_gemm_wide_dx_kernel(GemmParams p
       __builtin_amdgcn_sched_barrier(0);
       if (kk == 2) {
         // every vector-memory operation of the previous step (this wave's copies of A
-        // stage kt + 1 and code stage kt + 4, the scale loads of stage kt + 3, issued
+        // stage kt + 1 and code stage kt + 3, the scale loads of stage kt + 3, issued
         // in group 3 in an order the scheduler chooses), and this wave's a_hat stores
         wait_vm_lgkm(std::integral_constant<int, 0>{});
         wbarrier();
@@ -749,12 +758,17 @@ __global__ __launch_bounds__(kThreads) void nf4_gemm_wide_dx_kernel(GemmParams p
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) bcur[j][kk] = bnext[j][kk];
   };
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using I2 = std::integral_constant<int, 2>;
   int kt = 0;
-  for (; kt + 1 < nk; kt += 2) {
-    step(kt, Q0);
-    step(kt + 1, Q1);
+  for (; kt + 2 < nk; kt += 3) {
+    step(I0{}, kt);
+    step(I1{}, kt + 1);
+    step(I2{}, kt + 2);
   }
-  if (kt < nk) step(kt, Q0);
+  if (kt < nk) step(I0{}, kt);
+  if (kt + 1 < nk) step(I1{}, kt + 1);
   __builtin_amdgcn_s_waitcnt(0);  // no copy of a stage past the end may still land in LDS
   __syncthreads();
 

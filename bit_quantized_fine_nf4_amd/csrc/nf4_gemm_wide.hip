@@ -463,27 +463,31 @@ __global__ __launch_bounds__(kThreads) void nf4_gemm_wide_fwd_kernel(GemmParams 
 //    rebuilt by the 256 threads, one each, two steps ahead, and published in a
 //    3-stage LDS ring; a lane reads its 8 values per MFMA group as two
 //    broadcast 16-byte reads.
-// A (dY) takes the forward's path through a 3-stage ring.  With all three rings
-// three stages deep, the K loop unrolled three times finds every slot at a
-// compile-time offset, and the LDS left over holds 16 copies of the pair table.  One barrier per K
+// A (dY) takes the forward's path, through a 2-stage ring: a stage's slot is free
+// after the barrier of the step that reads it, which is where the copy two stages
+// ahead is issued.  The pair table sits at offset 0 in 32 copies at a 256-byte
+// entry stride: a lookup address is one v_perm_b32 of the code word and the lane's
+// copy offset, and each lane of a 32-lane phase reads its own two banks.  With rings
+// of two and three stages the K loop is unrolled six times, so every slot is a
+// compile-time offset.  One barrier per K
 // step after the third MFMA group, as in the forward; the last group's MFMAs
 // cover the next step's first A fragments and the first part of the decode
 // after next.
 // ---------------------------------------------------------------------------
 namespace {
-constexpr int kXStages = 3;                   // A (dY), code and a_hat rings alike
-constexpr int kXStagesA = kXStages;
-constexpr int kXStagesC = kXStages;
-constexpr int kXStagesS = kXStages;
+constexpr int kXStagesA = 2;                  // A (dY) ring
+constexpr int kXStages = 3;                   // code and a_hat rings
 constexpr int kXBN = 256, kXTN = 2;           // 256-wide tiles: two 32-column MFMA tiles per wave
 constexpr int kXLdc = kXBN + 8;               // epilogue staging row stride (elements)
 constexpr int kXCodeBytes = 64 * (kXBN / 2);  // 64 code rows x 256 columns
 constexpr int kXAhFloats = 4 * 64;            // [4 blocks][64 rows]
-constexpr int kXLutCopies = 16;               // lane l reads copy l % 16 of the pair table
-constexpr int kXOffC = kXStagesA * kStageElems * 2;
-constexpr int kXOffS = kXOffC + kXStagesC * kXCodeBytes;
-constexpr int kXOffLut = kXOffS + kXStagesS * kXAhFloats * 4;
-constexpr int kXLdsBytes = wmax(kXOffLut + 256 * 8 * kXLutCopies, kBM * kXLdc * 2);
+constexpr int kXLutCopies = 32;               // lane l reads copy l % 32 of the pair table
+constexpr int kXLutStride = 8 * kXLutCopies;  // bytes per table entry: a lookup address is
+                                              // (code byte) << 8 | 8 (lane % 32), one v_perm
+constexpr int kXOffA = 256 * kXLutStride;     // the table at offset 0, then the rings
+constexpr int kXOffC = kXOffA + kXStagesA * kStageElems * 2;
+constexpr int kXOffS = kXOffC + kXStages * kXCodeBytes;
+constexpr int kXLdsBytes = wmax(kXOffS + kXStages * kXAhFloats * 4, kBM * kXLdc * 2);
 typedef int wi32x2 __attribute__((ext_vector_type(2)));
 QL_DEV u32x2 wtr4(const uint8_t *ptr) {
   typedef __attribute__((address_space(3))) wi32x2 lds_i32x2;
@@ -494,16 +498,16 @@ QL_DEV u32x2 wtr4(const uint8_t *ptr) {
 __global__ __launch_bounds__(kThreads) void nf4_gemm_wide_dx_kernel(GemmParams p) {
   constexpr int kTN = kXTN, kBN = kXBN, kLdc = kXLdc;
   __shared__ __attribute__((aligned(16))) char lds[kXLdsBytes];
-  uint16_t *ring = reinterpret_cast<uint16_t *>(lds);
+  char *const tab = lds;
+  uint16_t *ring = reinterpret_cast<uint16_t *>(lds + kXOffA);
   uint8_t *cring = reinterpret_cast<uint8_t *>(lds + kXOffC);
   float *ahs = reinterpret_cast<float *>(lds + kXOffS);
-  char *const tab = lds + kXOffLut;
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 5, l32 = lane & 31, i16 = lane & 15, half = (lane >> 4) & 1;
 
-  // entry e of copy c (at 128 e + 8 c): (level[low nibble], level[high nibble]), the
+  // entry e of copy c (at 256 e + 8 c): (level[low nibble], level[high nibble]), the
   // levels of a byte's earlier and later row
   for (int i = tid; i < 256 * kXLutCopies; i += kThreads) {
     const int e = i / kXLutCopies;
@@ -600,8 +604,8 @@ __global__ __launch_bounds__(kThreads) void nf4_gemm_wide_dx_kernel(GemmParams p
       const uint32_t w = tw[j][kk & 1];
 #pragma unroll
       for (int d = 0; d < 4; ++d) {
-        const uint32_t byte = (w >> (8 * d)) & 0xFFu;
-        lv[j][d] = *reinterpret_cast<const f32x2 *>(tab + byte * (8 * kXLutCopies) + lcopy8);
+        const uint32_t addr = __builtin_amdgcn_perm(w, (uint32_t)lcopy8, 0x0C0C0000u | ((4u + d) << 8));
+        lv[j][d] = *reinterpret_cast<const f32x2 *>(tab + addr);
       }
     }
   };
@@ -636,8 +640,9 @@ __global__ __launch_bounds__(kThreads) void nf4_gemm_wide_dx_kernel(GemmParams p
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
 
   const int nk = p.ksteps;
-  // stage s lives in slot s % 3 of every ring, and its int8 / second-level scales in
-  // register set Qs[s % 3] until they are published
+  // stage s lives in slot s % 2 of the A ring, slot s % 3 of the code and a_hat
+  // rings, and its int8 / second-level scales in register set Qs[s % 3] until they
+  // are published
   QS Qs[kXStages];
   u32x4 bcur[kTN][4], bnext[kTN][4];
   u32x4 af[2][kTM];
@@ -684,22 +689,24 @@ __global__ __launch_bounds__(kThreads) void nf4_gemm_wide_dx_kernel(GemmParams p
   __syncthreads();  // every wave's reads of code slot 0 are done
   dma_c(3, 0);
 
-  // Step kt (BUF = kt % 3, compile-time: the loop is unrolled three times): A from
-  // slot BUF, B from bcur; decodes stage kt + 1 into bnext (its part 0 read during
-  // step kt - 1).  On entry af[0] holds group 0's A fragments, tw0 the first
-  // transposing reads of stage kt + 1, lv[0] / sc[0] its part-0 table entries and
-  // scales.  At its start the a_hat values of stage kt + 2 are published (slot
-  // (kt + 2) % 3, last read during step kt - 2).  After group 2: all of this wave's
-  // vector-memory operations (A stage kt + 1, code stage kt + 3, the scales of stage
-  // kt + 3) and its a_hat stores are awaited, and one barrier publishes every wave's
-  // copies and a_hat values and frees A slot (kt + 2) % 3 (last read in step kt - 1)
-  // and code slot (kt + 1) % 3 (stage kt + 1, last read in group 0); group 3 then
-  // issues the copies of code stage kt + 4 and A stage kt + 2 and the scale loads of
-  // stage kt + 4 between its MFMAs.  Copies and loads past the last stage read
-  // harmless data (zero past the buffers' ends) that is never used.
-  auto step = [&](auto bufc, int kt) {
-    constexpr int BUF = decltype(bufc)::value;
-    constexpr int B1 = (BUF + 1) % kXStages, B2 = (BUF + 2) % kXStages;
+  // Step kt (phase PH = kt % 6, compile-time: the loop is unrolled six times, so
+  // every slot is a compile-time offset): A from slot kt % 2, B from bcur; decodes
+  // stage kt + 1 into bnext (its part 0 read during step kt - 1).  On entry af[0]
+  // holds group 0's A fragments, tw0 the first transposing reads of stage kt + 1,
+  // lv[0] / sc[0] its part-0 table entries and scales.  At its start the a_hat values
+  // of stage kt + 2 are published (slot (kt + 2) % 3, last read during step kt - 2).
+  // After group 2: all of this wave's vector-memory operations (A stage kt + 1, code
+  // stage kt + 3, the scales of stage kt + 3) and its a_hat stores are awaited, and
+  // one barrier publishes every wave's copies and a_hat values and frees A slot
+  // kt % 2 (stage kt, last read in group 2) and code slot (kt + 1) % 3 (stage kt + 1,
+  // last read in group 0); group 3 then issues the copies of code stage kt + 4 and
+  // A stage kt + 2 and the scale loads of stage kt + 4 between its MFMAs.  Copies and
+  // loads past the last stage read harmless data (zero past the buffers' ends) that
+  // is never used.
+  auto step = [&](auto phc, int kt) {
+    constexpr int PH = decltype(phc)::value;
+    constexpr int BUF = PH % kXStagesA, BUF1 = (PH + 1) % kXStagesA;
+    constexpr int B1 = (PH + 1) % kXStages, B2 = (PH + 2) % kXStages;
     put_ah(Qs[B2], B2);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -720,9 +727,9 @@ __global__ __launch_bounds__(kThreads) void nf4_gemm_wide_dx_kernel(GemmParams p
         read_tr(B2, 0, tw0);
       } else {
         dma_c(kt + 4, B1);
-        dma_a(kt + 2, B2);
+        dma_a(kt + 2, BUF);
         load_qs(kt + 4, Qs[B1]);
-        read_a(B1, 0, af[0]);
+        read_a(BUF1, 0, af[0]);
         lut_read(tw0, 0, lv[0]);
         sc_read(B2, 0, sc[0]);
       }
@@ -761,14 +768,23 @@ __global__ __launch_bounds__(kThreads) void nf4_gemm_wide_dx_kernel(GemmParams p
   using I0 = std::integral_constant<int, 0>;
   using I1 = std::integral_constant<int, 1>;
   using I2 = std::integral_constant<int, 2>;
+  using I3 = std::integral_constant<int, 3>;
+  using I4 = std::integral_constant<int, 4>;
+  using I5 = std::integral_constant<int, 5>;
   int kt = 0;
-  for (; kt + 2 < nk; kt += 3) {
+  for (; kt + 5 < nk; kt += 6) {
     step(I0{}, kt);
     step(I1{}, kt + 1);
     step(I2{}, kt + 2);
+    step(I3{}, kt + 3);
+    step(I4{}, kt + 4);
+    step(I5{}, kt + 5);
   }
   if (kt < nk) step(I0{}, kt);
   if (kt + 1 < nk) step(I1{}, kt + 1);
+  if (kt + 2 < nk) step(I2{}, kt + 2);
+  if (kt + 3 < nk) step(I3{}, kt + 3);
+  if (kt + 4 < nk) step(I4{}, kt + 4);
   __builtin_amdgcn_s_waitcnt(0);  // no copy of a stage past the end may still land in LDS
   __syncthreads();
 

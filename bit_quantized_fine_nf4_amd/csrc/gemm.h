@@ -34,6 +34,25 @@ struct GemmParams {
   float level[16];
 };
 
+// Output tile (tm, tn) of workgroup `bid`.  The dispatcher deals workgroups to the
+// eight XCDs in turn (XCD = bid % 8) and each XCD has its own L2, so each XCD first
+// gets a contiguous range of a tile order, and that order walks bands of `band` tile
+// rows column by column: 32 tiles on one XCD then cover band x (32 / band) tiles.
+// An A tile-row holds 4 (256-wide tiles) or 8 (128-wide) times the bytes of a code
+// tile-column, so bands of 4 or 2 rows keep the fewest bytes per XCD; one row (a
+// whole row of tiles per XCD) makes every XCD fetch the whole weight (one LLaMA-65B
+// block at 2048 tokens: forward and dX GEMMs fetch 641 and 552 MB per launch with one
+// row, 385 and 380 MB with four).
+__device__ inline void gemm_tile_of(int bid, int tiles_m, int tiles_n, int band, int &tm, int &tn) {
+  const int ntiles = tiles_m * tiles_n;
+  if ((ntiles & 7) == 0) bid = (bid & 7) * (ntiles >> 3) + (bid >> 3);
+  const int b = bid / (band * tiles_n);
+  const int rows = tiles_m - b * band < band ? tiles_m - b * band : band;
+  const int rr = bid - b * band * tiles_n;
+  tn = rr / rows;
+  tm = b * band + rr % rows;
+}
+
 hipError_t launch_nf4_gemm(GemmParams &gp, bool trans, hipStream_t st);
 // 256 x bn tiles (bn = 256 or 128) with four waves that decode B in registers, both
 // directions (nf4_gemm_wide.hip)

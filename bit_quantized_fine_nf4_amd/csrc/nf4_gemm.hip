@@ -131,10 +131,8 @@ __global__ __launch_bounds__(512) void nf4_gemm_kernel(GemmParams p) {
     reinterpret_cast<f32x2 *>(lds)[i] = f32x2{p.level[e >> 4], p.level[e & 15]};
   }
 
-  int bid = blockIdx.x;
-  const int ntiles = p.tiles_m * p.tiles_n;
-  if ((ntiles & 7) == 0) bid = (bid & 7) * (ntiles >> 3) + (bid >> 3);  // one XCD -> contiguous tiles
-  const int tn = bid % p.tiles_n, tm = bid / p.tiles_n;
+  int tm, tn;
+  gemm_tile_of(blockIdx.x, p.tiles_m, p.tiles_n, 2, tm, tn);
   const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
   const int64_t mrows = p.M - m0 < BM ? p.M - m0 : BM;
   const int64_t nrows = p.N - n0 < BN ? p.N - n0 : BN;

@@ -120,10 +120,8 @@ __global__ __launch_bounds__(kThreads) void nf4_gemm_wide_fwd_kernel(GemmParams 
     reinterpret_cast<f32x2 *>(tab)[i] = f32x2{p.level[e >> 4], p.level[e & 15]};
   }
 
-  int bid = blockIdx.x;
-  const int ntiles = p.tiles_m * p.tiles_n;
-  if ((ntiles & 7) == 0) bid = (bid & 7) * (ntiles >> 3) + (bid >> 3);  // one XCD -> contiguous tiles
-  const int tn = bid % p.tiles_n, tm = bid / p.tiles_n;
+  int tm, tn;
+  gemm_tile_of(blockIdx.x, p.tiles_m, p.tiles_n, kTN == 2 ? 4 : 2, tm, tn);
   const int64_t m0 = (int64_t)tm * kBM, n0 = (int64_t)tn * kBN;
   const int64_t mrows = p.M - m0 < kBM ? p.M - m0 : kBM;
   const int64_t nrows = p.N - n0 < kBN ? p.N - n0 : kBN;
@@ -514,10 +512,8 @@ __global__ __launch_bounds__(kThreads) void nf4_gemm_wide_dx_kernel(GemmParams p
     reinterpret_cast<f32x2 *>(tab)[i] = f32x2{p.level[e & 15], p.level[e >> 4]};
   }
 
-  int bid = blockIdx.x;
-  const int ntiles = p.tiles_m * p.tiles_n;
-  if ((ntiles & 7) == 0) bid = (bid & 7) * (ntiles >> 3) + (bid >> 3);  // one XCD -> contiguous tiles
-  const int tn = bid % p.tiles_n, tm = bid / p.tiles_n;
+  int tm, tn;
+  gemm_tile_of(blockIdx.x, p.tiles_m, p.tiles_n, 4, tm, tn);
   const int64_t m0 = (int64_t)tm * kBM, n0 = (int64_t)tn * kBN;
   const int64_t mrows = p.M - m0 < kBM ? p.M - m0 : kBM;
   const int64_t nrows = p.N - n0 < kBN ? p.N - n0 : kBN;

@@ -50,10 +50,12 @@ __global__ __launch_bounds__(256) void adamw_kernel(AdamwParams a) {
   const int64_t n4 = a.n >> 2;
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
   for (int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; q < n4; q += stride) {
-    f32x4 p = reinterpret_cast<const f32x4 *>(a.p)[q];
-    const f32x4 g = reinterpret_cast<const f32x4 *>(a.g)[q];
-    f32x4 m = reinterpret_cast<const f32x4 *>(a.m)[q];
-    f32x4 v = reinterpret_cast<const f32x4 *>(a.v)[q];
+    // every value is read and written once per step: non-temporal accesses (the 65B
+    // block's 10.0 M adapter parameters: 62-64 -> 55 us)
+    f32x4 p = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(a.p) + q);
+    const f32x4 g = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(a.g) + q);
+    f32x4 m = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(a.m) + q);
+    f32x4 v = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(a.v) + q);
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       float pe = p[e], me = m[e], ve = v[e];
@@ -62,9 +64,9 @@ __global__ __launch_bounds__(256) void adamw_kernel(AdamwParams a) {
       m[e] = me;
       v[e] = ve;
     }
-    reinterpret_cast<f32x4 *>(a.p)[q] = p;
-    reinterpret_cast<f32x4 *>(a.m)[q] = m;
-    reinterpret_cast<f32x4 *>(a.v)[q] = v;
+    __builtin_nontemporal_store(p, reinterpret_cast<f32x4 *>(a.p) + q);
+    __builtin_nontemporal_store(m, reinterpret_cast<f32x4 *>(a.m) + q);
+    __builtin_nontemporal_store(v, reinterpret_cast<f32x4 *>(a.v) + q);
     if (a.pbf) reinterpret_cast<u32x2 *>(a.pbf)[q] = u32x2{pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3])};
   }
   // the last n % 4 elements

@@ -234,7 +234,7 @@ def test_linear_bwd_token_split_bound():
     part = (h + o) * rp16 * 4      # one split's float32 partial tiles
     per_token = (rp16 + rp64) * 2  # U and s*U, bf16, r padded to 16 and to 64
     for M in (cap, 5 * cap + 1, 40 * cap, 100 * cap):
-        # without the cap about 3 splits would do (512 workgroups over 236 tiles)
+        # without the cap about 2 splits would do (256 workgroups over 236 tiles)
         splits = -(-M // cap)
         assert ws(M) >= M * per_token + splits * part, M
     assert ws(cap) < cap * per_token + 4 * part

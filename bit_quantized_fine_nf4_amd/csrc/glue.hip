@@ -19,6 +19,10 @@ namespace ql {
 namespace {
 
 QL_DEV u32x4 ld16(const uint16_t *p) { return *reinterpret_cast<const u32x4 *>(p); }
+// Non-temporal: for inputs this step reads for the last time (the backward's G, U and
+// dH, the input-gradient parts; 65B block: SiLU-gate backward 75 -> 71 us, sum 38 ->
+// 36 us; the forward, whose G and U the backward reads again, measured 1 us slower)
+QL_DEV u32x4 ld16_last(const uint16_t *p) { return __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p)); }
 QL_DEV void st16(uint16_t *p, u32x4 v) { *reinterpret_cast<u32x4 *>(p) = v; }
 QL_DEV float bf(uint16_t v) { return __builtin_bit_cast(float, (uint32_t)v << 16); }
 QL_DEV uint16_t to_bf16(float v) { return (uint16_t)(pack_bf16x2(v, 0.0f) & 0xFFFFu); }
@@ -68,7 +72,7 @@ __global__ __launch_bounds__(kThreads) void silu_gate_bwd_kernel(const uint16_t 
   const int64_t nv = n >> 3, stride = (int64_t)gridDim.x * kThreads;
   const int64_t first = (int64_t)blockIdx.x * kThreads + threadIdx.x;
   for (int64_t i = first; i < nv; i += stride) {
-    const u32x4 g = ld16(G + 8 * i), u = ld16(U + 8 * i), d = ld16(dH + 8 * i);
+    const u32x4 g = ld16_last(G + 8 * i), u = ld16_last(U + 8 * i), d = ld16_last(dH + 8 * i);
     u32x4 og, ou;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -98,12 +102,12 @@ __global__ __launch_bounds__(kThreads) void grad_sum_kernel(SumParts parts, int6
   for (int64_t i = first; i < nv; i += stride) {
     float acc[8];
     {
-      const u32x4 v = ld16(parts.p[0] + 8 * i);
+      const u32x4 v = ld16_last(parts.p[0] + 8 * i);
 #pragma unroll
       for (int j = 0; j < 4; ++j) acc[2 * j] = bf16_lo(v[j]), acc[2 * j + 1] = bf16_hi(v[j]);
     }
     for (int q = 1; q < k; ++q) {
-      const u32x4 v = ld16(parts.p[q] + 8 * i);
+      const u32x4 v = ld16_last(parts.p[q] + 8 * i);
 #pragma unroll
       for (int j = 0; j < 4; ++j) acc[2 * j] += bf16_lo(v[j]), acc[2 * j + 1] += bf16_hi(v[j]);
     }

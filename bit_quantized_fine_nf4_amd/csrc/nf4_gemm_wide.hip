@@ -750,7 +750,10 @@ __global__ __launch_bounds__(kThreads) void nf4_gemm_wide_dx_kernel(GemmParams p
       if (kk == 2) {
         // every vector-memory operation of the previous step (this wave's copies of A
         // stage kt + 1 and code stage kt + 3, the scale loads of stage kt + 3, issued
-        // in group 3 in an order the scheduler chooses), and this wave's a_hat stores
+        // in group 3 in an order the scheduler chooses), this wave's a_hat stores, and
+        // all of its LDS reads: with them done in every wave, the barrier frees the A
+        // slot (stage kt, last read in group 2) and the code slot (stage kt + 1, last
+        // read in group 0) that group 3's copies overwrite
         wait_vm_lgkm(std::integral_constant<int, 0>{});
         wbarrier();
         __builtin_amdgcn_sched_barrier(0);
